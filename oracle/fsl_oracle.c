@@ -1,0 +1,389 @@
+/*
+ * Plain CPU oracle of the FreeSolo-Linear (FS-L) attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it. It shares no code with the HIP library.
+ *
+ * Everything here is deliberately slow and literal: one head at a time, one
+ * query at a time, floating point in fp64. Inputs arrive as float32 arrays
+ * whose values are exact copies of the fp32 or bf16 tensors the GPU reads, so
+ * the upcast to double is exact.
+ *
+ * Sources (the pages this follows):
+ *  [D]  "FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
+ *       Extrapolation" digest (paper.rainbus.top), sections "前置知识"
+ *       (RoPE, NoPE), "核心方法" (core method), "方法步骤详情" (six steps),
+ *       "局限与改进" (erf bound g_h >= erf(2)).
+ *  [S]  ai.info summary of the same paper, "Methodology in Plain English" and
+ *       "Why This Matters" (pool of P+W cells updated every B tokens, bounded
+ *       state O(((P+W)s + w + B + s)d)).
+ *
+ * Readings taken where the pages leave a step open (each repeated at its
+ * function): the long branch may use the cells that lie wholly before the
+ * window of the block's first query; the window holds w keys including the
+ * query itself; RoPE is the rotate-half pairing with base 10000 at absolute
+ * positions; the erf bias is lambda_h * a_c * erf(sigma_h (i - c s) / (2 s));
+ * the pool is the W most recent eligible cells plus the P best older ones under
+ * (a desc, index asc); top-K under (score desc, index asc); the mix is
+ * out = o_win + gamma_h * o_long / sqrt(mean(o_long^2) + eps).
+ *
+ * Cell statistics are stored as float32 (the rounding of the fp64 value), and
+ * every selection decision is taken in fp64 from those stored values.
+ *
+ * Parity pins: every function below is pinned by a CPU test against closed
+ * forms, library routines or brute force (the test module that exercises the
+ * oracle lists which pin covers which function).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int64_t N;       /* tokens */
+    int32_t d;       /* head dim (even) */
+    int32_t w;       /* window width, keys [i-w+1, i] */
+    int32_t s;       /* cell size */
+    int32_t P;       /* kept high-norm cells; -1 = no pruning (FS) */
+    int32_t W;       /* kept recent cells */
+    int32_t K;       /* cells read per query */
+    int32_t B;       /* query block */
+    int32_t pad_;
+    double scale;    /* softmax scale of both branches */
+    double rho;      /* weight of the content term in the cell score */
+    double rope_base;
+    double rms_eps;
+    double sigma;    /* per-head erf width */
+    double lambda;   /* per-head weight of the norm-weighted bias */
+    double gamma;    /* per-head mixing coefficient */
+} orc_head;
+
+/* ------------------------------------------------------------------------ */
+/* Cells and blocks ([D] core method: cells of s tokens, blocks of B queries) */
+
+int64_t orc_num_cells(const orc_head *p) { return p->N / p->s; }
+
+int64_t orc_num_blocks(const orc_head *p) { return (p->N + p->B - 1) / p->B; }
+
+/* Cells eligible for query block b: those wholly before the window of the
+ * block's first query t0 = b*B, i.e. floor((t0 - w + 1) / s), at least 0.
+ * ([D] core method: a block shares one available set; reading of where the
+ * long branch's cells end relative to the window.) */
+int64_t orc_eligible(int64_t b, const orc_head *p)
+{
+    int64_t x = b * (int64_t)p->B - (int64_t)p->w + 1;
+    if (x <= 0) return 0;
+    int64_t nb = x / p->s;
+    int64_t C = orc_num_cells(p);
+    return nb < C ? nb : C;
+}
+
+/* Mean key and max key norm of every complete cell ([D] core method and step
+ * 3; [S] methodology: mean key for routing, largest token-key norm as a
+ * query-independent priority). Sums run in fp64 in token order (mean) and in
+ * coordinate order with fused multiply-add (squared norm); the results are
+ * rounded once to float32. */
+void orc_cell_stats(const float *k, const orc_head *p, float *kbar, float *amax)
+{
+    const int64_t C = orc_num_cells(p);
+    const int d = p->d, s = p->s;
+    for (int64_t c = 0; c < C; ++c) {
+        const float *cell = k + c * s * (int64_t)d;
+        for (int x = 0; x < d; ++x) {
+            double acc = 0.0;
+            for (int j = 0; j < s; ++j) acc += (double)cell[(int64_t)j * d + x];
+            kbar[c * d + x] = (float)(acc / (double)s);
+        }
+        double best = 0.0;
+        for (int j = 0; j < s; ++j) {
+            double ss = 0.0;
+            for (int x = 0; x < d; ++x) {
+                double e = (double)cell[(int64_t)j * d + x];
+                ss = fma(e, e, ss);
+            }
+            if (ss > best) best = ss;
+        }
+        amax[c] = (float)sqrt(best);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Norm prune ([D] step 4 and core method; [S] methodology: the W most recent
+ * cells plus the P cells of highest max key norm, at most P+W, updated only at
+ * block boundaries). Reading: the P best are taken among the eligible cells
+ * that are not recent, ties by lower index. With P = -1 (FS) every eligible
+ * cell is kept. Returns the pool size; pool[] is ascending. */
+
+typedef struct { float a; int32_t idx; } orc_akey;
+
+static int cmp_akey(const void *pa, const void *pb)
+{
+    const orc_akey *a = (const orc_akey *)pa, *b = (const orc_akey *)pb;
+    if (a->a > b->a) return -1;
+    if (a->a < b->a) return 1;
+    return (a->idx < b->idx) ? -1 : (a->idx > b->idx);
+}
+
+static int cmp_i32(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+int32_t orc_pool(const float *amax, int64_t b, const orc_head *p, int32_t *pool)
+{
+    const int64_t nb = orc_eligible(b, p);
+    if (p->P < 0) {
+        for (int64_t c = 0; c < nb; ++c) pool[c] = (int32_t)c;
+        return (int32_t)nb;
+    }
+    const int64_t m = nb > p->W ? nb - p->W : 0; /* older cells: [0, m) */
+    int32_t n = 0;
+    if (m > 0 && p->P > 0) {
+        orc_akey *keys = (orc_akey *)malloc(sizeof(orc_akey) * (size_t)m);
+        for (int64_t c = 0; c < m; ++c) { keys[c].a = amax[c]; keys[c].idx = (int32_t)c; }
+        qsort(keys, (size_t)m, sizeof(orc_akey), cmp_akey);
+        int64_t take = m < p->P ? m : p->P;
+        for (int64_t t = 0; t < take; ++t) pool[n++] = keys[t].idx;
+        free(keys);
+        qsort(pool, (size_t)n, sizeof(int32_t), cmp_i32);
+    }
+    for (int64_t c = m; c < nb; ++c) pool[n++] = (int32_t)c;
+    return n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cell score and top-K ([D] core method and step 5: content match plus a
+ * norm-weighted erf relative-position bias, top K cells; [D] limits section:
+ * for available cells the erf factor is at least erf(2); [S] methodology: the
+ * bias grows with distance and is scaled by the cell norm).
+ * Reading: score = fma(rho, q.kbar_c, (lambda * a_c) * erf(sigma (i - c s) / (2 s))),
+ * the dot product a left-to-right fused multiply-add chain in fp64. The K best
+ * under (score desc, index asc) are kept (all of them if the pool is no larger
+ * than K) and reported ascending, padded with -1. *margin receives the gap
+ * between the K-th and (K+1)-th best score (+inf if no (K+1)-th). */
+
+double orc_cell_score(const float *q_i, int64_t i, const float *kbar_c, float a_c,
+                      int64_t c, const orc_head *p)
+{
+    double content = 0.0;
+    for (int x = 0; x < p->d; ++x) content = fma((double)q_i[x], (double)kbar_c[x], content);
+    double arg = (p->sigma * (double)(i - c * (int64_t)p->s)) / (2.0 * (double)p->s);
+    double bias = (p->lambda * (double)a_c) * erf(arg);
+    return fma(p->rho, content, bias);
+}
+
+typedef struct { double sc; int32_t idx; } orc_skey;
+
+static int cmp_skey(const void *pa, const void *pb)
+{
+    const orc_skey *a = (const orc_skey *)pa, *b = (const orc_skey *)pb;
+    if (a->sc > b->sc) return -1;
+    if (a->sc < b->sc) return 1;
+    return (a->idx < b->idx) ? -1 : (a->idx > b->idx);
+}
+
+int32_t orc_select(const float *q_i, int64_t i, const float *kbar, const float *amax,
+                   const int32_t *pool, int32_t npool, const orc_head *p,
+                   int32_t *sel, double *margin)
+{
+    const int d = p->d;
+    int32_t nsel = 0;
+    double gap = INFINITY;
+    if (npool > 0) {
+        orc_skey *sk = (orc_skey *)malloc(sizeof(orc_skey) * (size_t)npool);
+        for (int32_t t = 0; t < npool; ++t) {
+            int64_t c = pool[t];
+            sk[t].sc = orc_cell_score(q_i, i, kbar + c * d, amax[c], c, p);
+            sk[t].idx = (int32_t)c;
+        }
+        qsort(sk, (size_t)npool, sizeof(orc_skey), cmp_skey);
+        nsel = npool < p->K ? npool : p->K;
+        for (int32_t t = 0; t < nsel; ++t) sel[t] = sk[t].idx;
+        if (npool > p->K) gap = sk[p->K - 1].sc - sk[p->K].sc;
+        free(sk);
+        qsort(sel, (size_t)nsel, sizeof(int32_t), cmp_i32);
+    }
+    for (int32_t t = nsel; t < p->K; ++t) sel[t] = -1;
+    if (margin) *margin = gap;
+    return nsel;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RoPE ([D] prerequisites: rotate q_i and k_j by R(i), R(j) so that their dot
+ * product depends only on the offset; used only inside the local window).
+ * Reading: rotate-half pairing (x[m], x[m + d/2]), angle t * base^(-2m/d). */
+void orc_rope(const float *x, int64_t t, const orc_head *p, double *out)
+{
+    const int half = p->d / 2;
+    for (int m = 0; m < half; ++m) {
+        double theta = pow(p->rope_base, -2.0 * (double)m / (double)p->d);
+        double ang = (double)t * theta;
+        double cs = cos(ang), sn = sin(ang);
+        double a = (double)x[m], b = (double)x[m + half];
+        out[m] = a * cs - b * sn;
+        out[m + half] = b * cs + a * sn;
+    }
+}
+
+/* Local branch ([D] core method and step 2: standard RoPE attention in a
+ * window of width w). Reading: keys j in [max(0, i-w+1), i]. qrot is R(i)q_i;
+ * krot holds R(j)k_j for every j of the window (rows of a [N][d] array). */
+void orc_window(const double *qrot, const double *krot, const float *v, int64_t i,
+                const orc_head *p, double *o)
+{
+    const int d = p->d;
+    int64_t j0 = i - p->w + 1;
+    if (j0 < 0) j0 = 0;
+    const int64_t n = i - j0 + 1;
+    double *l = (double *)malloc(sizeof(double) * (size_t)n);
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < n; ++t) {
+        const double *kr = krot + (j0 + t) * d;
+        double dot = 0.0;
+        for (int x = 0; x < d; ++x) dot += qrot[x] * kr[x];
+        l[t] = p->scale * dot;
+        if (l[t] > mx) mx = l[t];
+    }
+    double sum = 0.0;
+    for (int64_t t = 0; t < n; ++t) { l[t] = exp(l[t] - mx); sum += l[t]; }
+    for (int x = 0; x < d; ++x) o[x] = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+        const float *vr = v + (j0 + t) * d;
+        for (int x = 0; x < d; ++x) o[x] += l[t] * (double)vr[x];
+    }
+    for (int x = 0; x < d; ++x) o[x] /= sum;
+    free(l);
+}
+
+/* Long branch readout ([D] core method and step 6; NoPE prerequisite: softmax
+ * attention over the raw, unrotated tokens of the selected cells, at most K*s
+ * tokens; the position bias takes no part in it). An empty selection gives 0. */
+void orc_readout(const float *q_i, const float *k, const float *v, const int32_t *sel,
+                 int32_t nsel, const orc_head *p, double *o)
+{
+    const int d = p->d, s = p->s;
+    for (int x = 0; x < d; ++x) o[x] = 0.0;
+    if (nsel <= 0) return;
+    const int64_t n = (int64_t)nsel * s;
+    double *l = (double *)malloc(sizeof(double) * (size_t)n);
+    double mx = -INFINITY;
+    for (int32_t u = 0; u < nsel; ++u)
+        for (int j = 0; j < s; ++j) {
+            const float *kr = k + ((int64_t)sel[u] * s + j) * d;
+            double dot = 0.0;
+            for (int x = 0; x < d; ++x) dot += (double)q_i[x] * (double)kr[x];
+            double val = p->scale * dot;
+            l[(int64_t)u * s + j] = val;
+            if (val > mx) mx = val;
+        }
+    double sum = 0.0;
+    for (int64_t t = 0; t < n; ++t) { l[t] = exp(l[t] - mx); sum += l[t]; }
+    for (int32_t u = 0; u < nsel; ++u)
+        for (int j = 0; j < s; ++j) {
+            const float *vr = v + ((int64_t)sel[u] * s + j) * d;
+            double pw = l[(int64_t)u * s + j];
+            for (int x = 0; x < d; ++x) o[x] += pw * (double)vr[x];
+        }
+    for (int x = 0; x < d; ++x) o[x] /= sum;
+    free(l);
+}
+
+/* Branch mix ([D] core method and step 6: the long output goes through
+ * RMSNorm and is added to the local branch with a per-head learned weight).
+ * Reading: RMSNorm over d without a gain vector, eps added to the mean square. */
+void orc_mix(const double *o_win, const double *o_long, const orc_head *p, double *out)
+{
+    const int d = p->d;
+    double ms = 0.0;
+    for (int x = 0; x < d; ++x) ms += o_long[x] * o_long[x];
+    ms /= (double)d;
+    double den = sqrt(ms + p->rms_eps);
+    for (int x = 0; x < d; ++x) out[x] = o_win[x] + p->gamma * (o_long[x] / den);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole forward for one head at a list of query rows. q, k, v are [N][d].
+ * Outputs per row r: out/o_win/o_long [nrows][d], sel [nrows][K], margin
+ * [nrows]; pool_out (nullable) receives the pool of every block as
+ * [nblk][pool_cap] padded with -1; kbar_out [C][d] and amax_out [C]
+ * (nullable) receive the cell statistics. Because the method is causal, the
+ * output at row i equals the output at the last row of the sequence cut
+ * after token i, which is also the definition of a decode step. */
+int orc_forward_head(const float *q, const float *k, const float *v, const orc_head *p,
+                     const int64_t *rows, int64_t nrows, double *out, double *o_win,
+                     double *o_long, int32_t *sel, double *margin, int32_t *pool_out,
+                     int32_t pool_cap, float *kbar_out, float *amax_out, int nthreads)
+{
+    const int d = p->d;
+    const int64_t N = p->N, C = orc_num_cells(p), nblk = orc_num_blocks(p);
+    if (d <= 0 || (d & 1) || p->s <= 0 || p->B <= 0 || p->w <= 0 || p->K <= 0 || N <= 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    float *kbar = (float *)malloc(sizeof(float) * (size_t)(C > 0 ? C : 1) * d);
+    float *amax = (float *)malloc(sizeof(float) * (size_t)(C > 0 ? C : 1));
+    orc_cell_stats(k, p, kbar, amax);
+    if (kbar_out) memcpy(kbar_out, kbar, sizeof(float) * (size_t)C * d);
+    if (amax_out) memcpy(amax_out, amax, sizeof(float) * (size_t)C);
+
+    const int64_t cap = p->P < 0 ? (C > 0 ? C : 1) : (int64_t)p->P + p->W;
+    /* pools of the blocks the rows fall in */
+    char *need_blk = (char *)calloc((size_t)nblk, 1);
+    char *need_tok = (char *)calloc((size_t)N, 1);
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows[r];
+        if (i < 0 || i >= N) { free(kbar); free(amax); free(need_blk); free(need_tok); return -2; }
+        need_blk[i / p->B] = 1;
+        int64_t j0 = i - p->w + 1;
+        if (j0 < 0) j0 = 0;
+        for (int64_t j = j0; j <= i; ++j) need_tok[j] = 1;
+    }
+    if (pool_out) for (int64_t b = 0; b < nblk; ++b) need_blk[b] = 1;
+    int32_t *pools = (int32_t *)malloc(sizeof(int32_t) * (size_t)nblk * (size_t)(cap > 0 ? cap : 1));
+    int32_t *npools = (int32_t *)calloc((size_t)nblk, sizeof(int32_t));
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < nblk; ++b)
+        if (need_blk[b]) npools[b] = orc_pool(amax, b, p, pools + b * cap);
+    if (pool_out) {
+        for (int64_t b = 0; b < nblk; ++b)
+            for (int64_t t = 0; t < pool_cap; ++t)
+                pool_out[b * pool_cap + t] = (t < npools[b] && t < cap) ? pools[b * cap + t] : -1;
+    }
+    /* rotated keys of every position some window needs */
+    double *krot = (double *)malloc(sizeof(double) * (size_t)N * d);
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j)
+        if (need_tok[j]) orc_rope(k + j * d, j, p, krot + j * d);
+
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows[r];
+        const int64_t b = i / p->B;
+        double *qrot = (double *)malloc(sizeof(double) * d);
+        double *ow = (double *)malloc(sizeof(double) * d);
+        double *ol = (double *)malloc(sizeof(double) * d);
+        int32_t *sl = (int32_t *)malloc(sizeof(int32_t) * (size_t)p->K);
+        double mg;
+        orc_rope(q + i * d, i, p, qrot);
+        orc_window(qrot, krot, v, i, p, ow);
+        int32_t nsel = orc_select(q + i * d, i, kbar, amax, pools + b * cap, npools[b], p, sl, &mg);
+        orc_readout(q + i * d, k, v, sl, nsel, p, ol);
+        orc_mix(ow, ol, p, out + r * d);
+        if (o_win) memcpy(o_win + r * d, ow, sizeof(double) * d);
+        if (o_long) memcpy(o_long + r * d, ol, sizeof(double) * d);
+        if (sel) memcpy(sel + r * p->K, sl, sizeof(int32_t) * (size_t)p->K);
+        if (margin) margin[r] = mg;
+        free(qrot); free(ow); free(ol); free(sl);
+    }
+    free(krot); free(pools); free(npools); free(need_blk); free(need_tok);
+    free(kbar); free(amax);
+    return 0;
+}
