@@ -1,0 +1,163 @@
+/*
+ * fsl.h: C ABI of the FS-L (FreeSolo-Linear) attention library for MI355X.
+ *
+ * FS-L is the linear-time variant of FreeSolo, a two-branch sparse attention
+ * ("FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
+ * Extrapolation"; digest at paper.rainbus.top, sections "核心方法" (core
+ * method) and "方法步骤详情" (method steps); ai.info summary, "Methodology in
+ * Plain English"). Per head and per block of B queries:
+ *   1. a RoPE sliding-window branch over the last w keys;
+ *   2. the prefix split into cells of s tokens, each summarised by its mean
+ *      key kbar_c and its largest token-key norm a_c;
+ *   3. a norm prune to the P cells of largest a_c plus the W most recent
+ *      cells, a cell score (content q.kbar_c plus an a_c-weighted erf
+ *      relative-position bias) and the top K cells per query;
+ *   4. an unrotated (NoPE) softmax readout over the K*s raw tokens of those
+ *      cells, RMSNorm, and a per-head weighted add to the window branch.
+ *
+ * Conventions of every entry point:
+ *  - Ownership: the caller owns every buffer (inputs, outputs, workspace,
+ *    decode state). The library allocates nothing on the device and keeps no
+ *    global state, so calls on different streams do not interact.
+ *  - Execution: work is enqueued on `stream` and returns without waiting;
+ *    results are ready when the stream reaches that point. Entry points do
+ *    not synchronise (fsl_decode_validate is the one exception, see there).
+ *  - Pointers named "device" must be device memory (hipMalloc or a torch
+ *    tensor on the GPU), 16-byte aligned, non-overlapping. Host pointers are
+ *    read before the call returns.
+ *  - Errors: every int-returning call returns FSL_OK (0) or a negative code.
+ *    Arguments are validated on the host before anything is launched, so an
+ *    error means nothing was enqueued. FSL_E_HIP reports a launch failure.
+ *  - Layouts: q, k, v, out are contiguous [H][N][d] (one sequence, head-major).
+ *    Element type is fp32 or bf16 (uint16 bit patterns) per fsl_params.dtype.
+ */
+#ifndef FSL_H
+#define FSL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSL_VERSION 1
+
+enum fsl_status {
+    FSL_OK = 0,
+    FSL_E_INVAL = -1,        /* bad size, parameter, null or misaligned pointer */
+    FSL_E_UNSUPPORTED = -2,  /* valid for the method, not implemented here (d, P, ...) */
+    FSL_E_WORKSPACE = -3,    /* workspace or state buffer too small */
+    FSL_E_STATE = -4,        /* decode state header does not match the parameters */
+    FSL_E_HIP = -5           /* a kernel launch failed */
+};
+
+enum fsl_dtype { FSL_F32 = 0, FSL_BF16 = 1 };
+
+/* Method parameters. Page defaults: w=512, s=32, P=64, W=8, K=4, B=128,
+ * sigma_h=4, lambda_h=1 (digest, core method; ai.info summary, methodology
+ * and training paragraph). Limits of this implementation: d in {64, 128};
+ * s in {16, 32, 64} with s dividing B; B a multiple of 16, at most 256;
+ * 0 <= P <= 64; 0 <= W <= 64; 1 <= K <= 8; w >= 1; H >= 1; 1 <= N < 2^31.
+ * P = -1 (no pruning, the plain FS variant) is defined by the method but not
+ * implemented here (FSL_E_UNSUPPORTED). */
+typedef struct fsl_params {
+    int64_t N;          /* tokens in the sequence (forward); ignored by decode */
+    int32_t H;          /* heads */
+    int32_t d;          /* head dimension */
+    int32_t w;          /* window width: query i sees keys [i-w+1, i] */
+    int32_t s;          /* cell size in tokens */
+    int32_t P;          /* high-norm cells kept per block */
+    int32_t W;          /* most recent eligible cells kept per block */
+    int32_t K;          /* cells read per query */
+    int32_t B;          /* query block size: the pool is shared by a block */
+    int32_t dtype;      /* fsl_dtype of q, k, v */
+    int32_t out_dtype;  /* fsl_dtype of out (the input dtype, or FSL_F32) */
+    float scale;        /* softmax scale of both branches; 0 selects 1/sqrt(d) */
+    float rho;          /* weight of the content term q.kbar_c in the cell score */
+    float rope_base;    /* RoPE base (10000) */
+    float rms_eps;      /* RMSNorm epsilon (1e-6) */
+    const float *sigma; /* device [H]: erf width sigma_h of the position bias */
+    const float *lambda;/* device [H]: weight lambda_h of the norm-weighted bias */
+    const float *gamma; /* device [H]: mixing coefficient gamma_h of the long branch */
+} fsl_params;
+
+/* Library version (FSL_VERSION) and a static message for a status code. */
+int fsl_version(void);
+const char *fsl_strerror(int status);
+
+/* Host-only check of a parameter block (no pointer is dereferenced).
+ * Returns FSL_OK, FSL_E_INVAL or FSL_E_UNSUPPORTED. */
+int fsl_check_params(const fsl_params *p);
+
+/* Bytes of device workspace fsl_prune_select and fsl_attn_fwd need for p
+ * (0 if p is invalid). The workspace holds the cell statistics, the per-block
+ * pools, the per-query selections, the RoPE table and the prune scan lists. */
+size_t fsl_workspace_bytes(const fsl_params *p);
+
+/* Cell statistics (digest, core method and step 3; ai.info summary,
+ * methodology: mean key for routing, largest token-key norm as a
+ * query-independent priority). For every complete cell c < C = floor(N/s):
+ *   kbar[h][c][x] = float(sum_j k[h][c*s+j][x] / s)     (fp64 sum in token order)
+ *   amax[h][c]    = float(sqrt(max_j sum_x k[h][c*s+j][x]^2))
+ * with the squared norm a left-to-right fp64 fused multiply-add chain.
+ * k: device [H][N][d] (dtype); kbar: device [H][C][d] float; amax: device [H][C] float. */
+int fsl_cell_stats(const void *k, float *kbar, float *amax, const fsl_params *p,
+                   hipStream_t stream);
+
+/* Norm prune and per-query top-K (digest, core method and steps 4-5; ai.info
+ * summary, methodology: pool of the W most recent eligible cells plus the P
+ * highest-norm older ones, updated once per query block).
+ * Block b (queries [bB, bB+B)) may use the n_b = max(0, floor((bB - w + 1)/s))
+ * cells that lie wholly before the window of its first query. Its pool is the
+ * W most recent of them plus the P best of the rest under (a desc, index asc).
+ * Each query i scores every pool cell in fp64:
+ *   score = fma(rho, q_i.kbar_c, (lambda_h * a_c) * erf(sigma_h (i - c s) / (2 s)))
+ * (dot product a left-to-right fma chain over x, inputs the float32 cell
+ * statistics) and keeps the K best under (score desc, index asc).
+ * q: device [H][N][d] (dtype); kbar/amax as produced by fsl_cell_stats;
+ * pool: device [H][ceil(N/B)][P+W] int32, ascending, padded with -1;
+ * sel: device [H][N][K] int32, ascending, padded with -1.
+ * ws: device workspace of at least fsl_workspace_bytes(p) bytes. */
+int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_t *pool,
+                     int32_t *sel, const fsl_params *p, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Whole FS-L forward (digest, core method and step 6: NoPE softmax over the
+ * selected tokens, RMSNorm, add to the RoPE window branch with a per-head
+ * weight):
+ *   o_win[i]  = softmax_j(scale R(i)q_i . R(j)k_j) v_j over j in [max(0,i-w+1), i]
+ *               (rotate-half RoPE, angle t * rope_base^(-2m/d))
+ *   o_long[i] = softmax_j(scale q_i . k_j) v_j over the tokens of sel[i] (0 if empty)
+ *   out[i]    = o_win[i] + gamma_h * o_long[i] / sqrt(mean_x(o_long[i]^2) + rms_eps)
+ * q, k, v: device [H][N][d] (dtype); out: device [H][N][d] (out_dtype).
+ * ws: device workspace of at least fsl_workspace_bytes(p) bytes; after the
+ * call it holds kbar, amax, pool and sel (see fsl_workspace_views).
+ * sel_out (device [H][N][K] int32), o_win_out and o_long_out (device
+ * [H][N][d] float) are optional copies for inspection; pass NULL to skip. */
+int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
+                 void *ws, size_t ws_bytes, int32_t *sel_out, float *o_win_out,
+                 float *o_long_out, hipStream_t stream);
+
+/* Byte offsets of the named arrays inside a forward workspace (host-only).
+ * Returns FSL_OK or the fsl_check_params error. */
+typedef struct fsl_workspace_layout {
+    size_t kbar;    /* float [H][C][d]            cell mean keys */
+    size_t amax;    /* float [H][C]               cell max key norms */
+    size_t pool;    /* int32 [H][ceil(N/B)][P+W]  per-block pools */
+    size_t sel;     /* int32 [H][N][K]            per-query selections */
+    size_t rope;    /* float2 table of (cos, sin) for relative offsets */
+    size_t scan_a;  /* float / int32 lists of the prune scan */
+    size_t scan_i;
+    size_t o_win;   /* float [H][N][d]            window-branch output */
+    size_t total;   /* bytes; equals fsl_workspace_bytes */
+} fsl_workspace_layout;
+int fsl_workspace_views(const fsl_params *p, fsl_workspace_layout *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSL_H */

@@ -1,0 +1,147 @@
+// Internal declarations shared by the FS-L HIP kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fsl.h"
+
+namespace fsl {
+
+// Everything a kernel needs to know about the problem, passed by value.
+struct KParams {
+    int64_t N;        // tokens
+    int64_t C;        // complete cells, floor(N / s)
+    int64_t nblk;     // query blocks, ceil(N / B)
+    int32_t H, d, w, s, P, W, K, B;
+    int32_t PW;       // pool capacity P + W
+    int32_t dtype, out_dtype;
+    float scale, rho, rope_base, rms_eps;
+    const float *sigma, *lambda, *gamma;  // device [H]
+    int32_t nchunk;   // prune scan: chunks of 64 cells, ceil(C / 64)
+    int32_t nsg;      // prune scan: groups of 16 chunks, nchunk / 16 + 1
+    int32_t rope_lo;  // first relative offset of the RoPE table (negative)
+    int32_t rope_n;   // rows of the RoPE table
+};
+
+// Device workspace carved by the host (see fsl_workspace_views).
+struct Work {
+    float *kbar;       // [H][C][d]
+    float *amax;       // [H][C]
+    int32_t *pool;     // [H][nblk][PW]
+    int32_t *sel;      // [H][N][K]
+    float2 *rope;      // [rope_n][d/2] (cos, sin)
+    float *scan_a;     // prune scan lists, (a, index) pairs of 64 entries:
+    int32_t *scan_i;   //   chunks [H][nchunk], local prefixes [H][nchunk+1],
+                       //   group totals [H][nsg], group prefixes [H][nsg]
+    float *o_win;      // [H][N][d] window-branch output
+};
+
+constexpr int kChunk = 64;    // cells per prune-scan chunk (one wave)
+constexpr int kGroup = 16;    // chunks per prune-scan group
+constexpr int kQTile = 128;   // queries per window workgroup
+constexpr int kKTile = 64;    // keys per window LDS tile
+
+// Offsets of the four prune-scan list families inside scan_a / scan_i, in lists of 64.
+__host__ __device__ inline int64_t scan_chunk(const KParams &p, int h, int64_t k) {
+    return (int64_t)h * p.nchunk + k;
+}
+__host__ __device__ inline int64_t scan_prefix(const KParams &p, int h, int64_t k) {
+    return (int64_t)p.H * p.nchunk + (int64_t)h * (p.nchunk + 1) + k;
+}
+__host__ __device__ inline int64_t scan_total(const KParams &p, int h, int64_t g) {
+    return (int64_t)p.H * (2 * (int64_t)p.nchunk + 1) + (int64_t)h * p.nsg + g;
+}
+__host__ __device__ inline int64_t scan_gprefix(const KParams &p, int h, int64_t g) {
+    return (int64_t)p.H * (2 * (int64_t)p.nchunk + 1 + p.nsg) + (int64_t)h * p.nsg + g;
+}
+__host__ __device__ inline int64_t scan_lists(const KParams &p) {
+    return (int64_t)p.H * (2 * (int64_t)p.nchunk + 1 + 2 * (int64_t)p.nsg);
+}
+
+// Cells eligible for block b: wholly before the window of its first query.
+__host__ __device__ inline int64_t eligible_cells(const KParams &p, int64_t b) {
+    int64_t x = b * p.B - p.w + 1;
+    if (x <= 0) return 0;
+    int64_t nb = x / p.s;
+    return nb < p.C ? nb : p.C;
+}
+
+// ---------------------------------------------------------------------------
+// element helpers (bf16 travels as raw uint16 bit patterns)
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+
+// ---------------------------------------------------------------------------
+// wave64 primitives over one (key, index) entry per lane.
+// Order "better": larger key first, then lower index. Sentinel: (-inf, INT32_MAX).
+
+__device__ __forceinline__ bool better(float a1, int i1, float a2, int i2) {
+    return a1 > a2 || (a1 == a2 && i1 < i2);
+}
+
+__device__ __forceinline__ bool better_d(double a1, int i1, double a2, int i2) {
+    return a1 > a2 || (a1 == a2 && i1 < i2);
+}
+
+// Sort the 64 entries of a wave best-first (lane 0 best). Bitonic network.
+__device__ __forceinline__ void wave_sort_best_first(float &a, int &idx) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            float pa = __shfl_xor(a, j);
+            int pi = __shfl_xor(idx, j);
+            bool lower = (lane & j) == 0;
+            bool dir = (lane & k) == 0;
+            bool pb = better(pa, pi, a, idx);
+            bool take = (lower == dir) ? pb : !pb;
+            if (take) { a = pa; idx = pi; }
+        }
+    }
+}
+
+// Given two best-first sorted lists (one entry per lane each), leave the 64
+// best of their union, best-first, in (a, idx).
+__device__ __forceinline__ void wave_merge_top(float &a, int &idx, float ba, int bi) {
+    const int lane = threadIdx.x & 63;
+    float ra = __shfl(ba, 63 - lane);
+    int ri = __shfl(bi, 63 - lane);
+    if (better(ra, ri, a, idx)) { a = ra; idx = ri; }
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) {
+        float pa = __shfl_xor(a, j);
+        int pi = __shfl_xor(idx, j);
+        bool lower = (lane & j) == 0;
+        bool pb = better(pa, pi, a, idx);
+        bool take = lower ? pb : !pb;
+        if (take) { a = pa; idx = pi; }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers (one per kernel family); each returns hipGetLastError()
+
+hipError_t launch_cell_stats(const void *k, float *kbar, float *amax, const KParams &p, hipStream_t st);
+hipError_t launch_prune(const float *amax, int32_t *pool, const Work &w, const KParams &p, hipStream_t st);
+hipError_t launch_select(const void *q, const float *kbar, const float *amax, const int32_t *pool,
+                         int32_t *sel, const KParams &p, hipStream_t st);
+hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st);
+hipError_t launch_window(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
+                         const KParams &p, hipStream_t st);
+hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const int32_t *sel,
+                              const float *o_win, void *out, float *o_long_out, const KParams &p,
+                              hipStream_t st);
+
+}  // namespace fsl

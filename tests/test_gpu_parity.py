@@ -1,0 +1,154 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Indices (pools, selections) and the cell statistics must be bit-exact;
+outputs must be within 1e-4 max-abs for fp32 inputs and 2e-2 max-abs /
+1e-2 mean-abs for bf16 inputs. Small shapes are compared at every query;
+the full workload shapes are compared on every pool and cell statistic and
+on sampled query rows (probes, block edges, random rows, the last row).
+"""
+import numpy as np
+import pytest
+import torch
+
+from fsl_testlib import GpuRun, check_out, host_f32, oracle_head_params
+from long_context_sparse_cell_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_sparse_cell_amd import fsl
+    fsl.lib()  # a missing library is an error here, not a skip
+
+
+def _print_case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=True):
+    """Compare one GPU run with the oracle, head by head."""
+    sh = inp.shape
+    over_oracle = over_oracle or {}
+    pools = run.views["pool"].cpu().numpy()
+    kbar = host_f32(run.views["kbar"]); amax = host_f32(run.views["amax"])
+    sel = run.sel.cpu().numpy()
+    out = host_f32(run.out)
+    o_win = host_f32(run.o_win); o_long = host_f32(run.o_long)
+    out_dtype = synth.F32 if run.p.out_dtype == 0 else synth.BF16
+    worst = 0.0
+    for h in range(sh.H):
+        p = oracle_head_params(oracle, sh, inp, h, **over_oracle)
+        r = oracle.forward_head(inp.q[h], inp.k[h], inp.v[h], p, rows=rows, want_pool=True, want_stats=True)
+        np.testing.assert_array_equal(kbar[h], r["kbar"], err_msg=f"kbar head {h}")
+        np.testing.assert_array_equal(amax[h], r["amax"], err_msg=f"amax head {h}")
+        np.testing.assert_array_equal(pools[h], r["pool"], err_msg=f"pool head {h}")
+        idx = r["rows"]
+        np.testing.assert_array_equal(sel[h][idx], r["sel"], err_msg=f"sel head {h}")
+        mx, _ = check_out(out[h][idx], r["out"], out_dtype, f"out head {h}")
+        worst = max(worst, mx)
+        if check_internals:
+            tol = 1e-4 if sh.dtype == synth.F32 else 1.5e-2
+            assert np.abs(o_win[h][idx] - r["o_win"]).max() <= tol, f"o_win head {h}"
+            assert np.abs(o_long[h][idx] - r["o_long"]).max() <= (1e-4 if sh.dtype == synth.F32 else 1e-3), \
+                f"o_long head {h}"
+    return worst
+
+
+SMALL = [
+    # name, shape overrides, kernel/oracle parameter overrides
+    ("bf16_d64_n8192_h2", dict(H=2, N=8192, d=64, dtype=synth.BF16), {}),
+    ("f32_d64_n4096_h1", dict(H=1, N=4096, d=64, dtype=synth.F32), {}),
+    ("bf16_d128_n5000_h2", dict(H=2, N=5000, d=128, dtype=synth.BF16), {}),
+    ("f32_d128_n3001_h2", dict(H=2, N=3001, d=128, dtype=synth.F32), {}),
+    ("bf16_d64_n700_h3", dict(H=3, N=700, d=64, dtype=synth.BF16), {}),
+    ("bf16_d64_n1_h1", dict(H=1, N=1, d=64, dtype=synth.BF16), {}),
+    ("bf16_d64_n130_h2", dict(H=2, N=130, d=64, dtype=synth.BF16), {}),
+    ("bf16_d64_n4100_sigma005", dict(H=2, N=4100, d=64, dtype=synth.BF16), dict(sigma=0.05)),
+    ("bf16_d64_n3000_small_window", dict(H=2, N=3000, d=64, dtype=synth.BF16, w=64, s=16, B=64, P=8, W=2, K=3), {}),
+    ("bf16_d64_n3000_p0", dict(H=2, N=3000, d=64, dtype=synth.BF16, w=64, s=16, B=64, P=0, W=3, K=1), {}),
+    ("bf16_d64_n4000_w0", dict(H=2, N=4000, d=64, dtype=synth.BF16, w=100, s=32, B=128, P=64, W=0, K=8), {}),
+    ("bf16_d64_n6000_s64", dict(H=1, N=6000, d=64, dtype=synth.BF16, s=64, P=5, W=1, K=2), {}),
+    ("bf16_d128_n5000_b256", dict(H=1, N=5000, d=128, dtype=synth.BF16, B=256, P=20, K=5), {}),
+    ("f32_d64_n2000_w1", dict(H=1, N=2000, d=64, dtype=synth.F32, w=1, s=16, B=16, P=4, W=1, K=2), {}),
+]
+
+
+@pytest.mark.parametrize("name,shape_over,par_over", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_every_query(oracle, name, shape_over, par_over):
+    _print_case(name)
+    sh = synth.Shape(name, seed=7, **shape_over)
+    inp = synth.random_inputs(sh)
+    inp.k[:, ::7] *= 2.5  # varied cell norms
+    inp.k = synth.to_dtype(inp.k, sh.dtype)
+    gpu_over, orc_over = {}, {}
+    if "sigma" in par_over:
+        inp.sigma[:] = par_over["sigma"]
+    run = GpuRun(inp, **gpu_over)
+    compare_full(oracle, inp, run, orc_over)
+
+
+def test_bf16_input_fp32_output(oracle):
+    _print_case("bf16_in_f32_out")
+    sh = synth.Shape("bf16_f32out", H=2, N=4096, d=64, dtype=synth.BF16, seed=8)
+    inp = synth.random_inputs(sh)
+    run = GpuRun(inp, out_dtype=0)
+    assert run.out.dtype == torch.float32
+    pools = run.views["pool"].cpu().numpy()
+    for h in range(sh.H):
+        p = oracle_head_params(oracle, sh, inp, h)
+        r = oracle.forward_head(inp.q[h], inp.k[h], inp.v[h], p)
+        # fp32 output: the error left is the bf16 window arithmetic alone
+        assert np.abs(host_f32(run.out)[h] - r["out"]).max() <= 1.5e-2
+        np.testing.assert_array_equal(run.sel.cpu().numpy()[h], r["sel"])
+
+
+def test_runs_are_bitwise_deterministic():
+    _print_case("determinism")
+    sh = synth.Shape("det", H=2, N=6000, d=128, dtype=synth.BF16, seed=9)
+    inp = synth.random_inputs(sh)
+    a = GpuRun(inp)
+    from long_context_sparse_cell_amd import fsl
+    out2 = fsl.attn_fwd(a.q, a.k, a.v, a.p, ws=torch.zeros_like(a.ws))
+    torch.cuda.synchronize()
+    assert torch.equal(a.out.view(torch.int16), out2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# full workload shapes
+
+def _sample_rows(sh, inp, n_random=160, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.integers(0, sh.N, size=n_random).tolist())
+    for b in rng.integers(0, (sh.N + sh.B - 1) // sh.B, size=16):
+        t0 = int(b) * sh.B
+        rows.update([t0, min(sh.N - 1, t0 + sh.B - 1)])
+    rows.update([0, sh.N - 1])
+    for pr in inp.probes:
+        rows.update(pr[:8])
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4"])
+def test_workload_parity_and_needles(oracle, cfg):
+    sh = synth.CONFIGS[cfg]
+    _print_case(f"workload {cfg} {sh.name}")
+    inp = synth.make_inputs(sh)
+    run = GpuRun(inp)
+    rows = None if cfg == "c1" else _sample_rows(sh, inp)
+    compare_full(oracle, inp, run, rows=rows, check_internals=(cfg == "c1"))
+    # needles: in the last block's pool and in their probe queries' selection (GPU values)
+    pools = run.views["pool"].cpu().numpy()
+    sel = run.sel.cpu().numpy()
+    last_blk = (sh.N - 1) // sh.B
+    for h in range(sh.H):
+        for m, pos in enumerate(inp.needles[h]):
+            cell = pos // sh.s
+            assert cell in pools[h][last_blk], (h, pos)
+            probes = inp.probes[h] if cfg == "c4" else [inp.probes[h][m]]
+            for row in probes:
+                assert cell in sel[h][row], (h, pos, row)
+    del run
+    torch.cuda.empty_cache()

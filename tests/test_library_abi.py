@@ -1,0 +1,109 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/fsl.h declares, and rejects bad arguments on the host before any
+launch (so no GPU is needed to exercise the error paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsl.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fsl_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def fsl():
+    from long_context_sparse_cell_amd import fsl as mod
+    if not os.path.exists(mod.LIB_PATH):
+        pytest.fail("libfsl.so is not built (run __graft_entry__.build())")
+    return mod
+
+
+def test_every_declared_symbol_is_exported(fsl):
+    names = declared_functions()
+    assert "fsl_attn_fwd" in names and "fsl_cell_stats" in names and "fsl_prune_select" in names
+    L = ctypes.CDLL(fsl.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_messages(fsl):
+    assert fsl.lib().fsl_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert fsl.strerror(code)
+    assert fsl.strerror(-99) == "unknown status"
+
+
+class FakeTensor:
+    """Stands in for a device tensor: only its address is used by the host checks."""
+
+    def __init__(self, addr=0x10000, n=1 << 20):
+        self._addr = addr
+        self._n = n
+
+    def data_ptr(self):
+        return self._addr
+
+
+def params(fsl, **kw):
+    base = dict(N=4096, H=2, d=64, w=512, s=32, P=64, W=8, K=4, B=128, dtype=1, out_dtype=1, scale=0.0, rho=1.0,
+                rope_base=10000.0, rms_eps=1e-6)
+    base.update(kw)
+    p = fsl.Params(**{k: v for k, v in base.items()})
+    p.sigma = p.lam = p.gamma = 0x20000
+    return p
+
+
+BAD = [
+    (dict(N=0), -1), (dict(H=0), -1), (dict(d=63), -1), (dict(s=0), -1), (dict(B=100, s=32), -1),
+    (dict(K=0), -1), (dict(W=-1), -1), (dict(P=-2), -1), (dict(dtype=7), -1), (dict(out_dtype=1, dtype=0), -1),
+    (dict(rms_eps=0.0), -1), (dict(rope_base=0.0), -1), (dict(w=0), -1), (dict(scale=-1.0), -1),
+    (dict(d=96), -2), (dict(s=8, B=128), -2), (dict(P=65), -2), (dict(P=-1), -2), (dict(K=9), -2),
+    (dict(W=65), -2), (dict(B=288, s=32), -2), (dict(B=24, s=8), -2),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_bad_parameters_are_rejected(fsl, over, code):
+    p = params(fsl, **over)
+    assert fsl.check_params(p) == code
+    assert fsl.workspace_bytes(p) == 0
+
+
+def test_good_parameters_and_workspace_size(fsl):
+    p = params(fsl)
+    assert fsl.check_params(p) == 0
+    n = fsl.workspace_bytes(p)
+    L = fsl.workspace_layout(p)
+    assert L.total == n
+    C, nblk = 4096 // 32, 4096 // 128
+    assert L.amax - L.kbar >= 2 * C * 64 * 4
+    assert L.sel - L.pool >= 2 * nblk * 72 * 4
+    assert all(getattr(L, f) % 256 == 0 for f in ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win"))
+
+
+def test_null_pointers_and_small_workspace_fail_before_launch(fsl):
+    L = fsl.lib()
+    p = params(fsl)
+    vp = ctypes.c_void_p
+    a = vp(0x100000)
+    n = fsl.workspace_bytes(p)
+    # null q
+    assert L.fsl_attn_fwd(None, a, a, a, ctypes.byref(p), a, n, None, None, None, None) == -1
+    # misaligned k
+    assert L.fsl_attn_fwd(a, vp(0x100004), a, a, ctypes.byref(p), a, n, None, None, None, None) == -1
+    # workspace one byte short
+    assert L.fsl_attn_fwd(a, a, a, a, ctypes.byref(p), a, n - 1, None, None, None, None) == -3
+    assert L.fsl_prune_select(a, a, a, a, a, ctypes.byref(p), a, n - 1, None) == -3
+    # missing per-head arrays
+    p2 = params(fsl)
+    p2.gamma = None
+    assert L.fsl_attn_fwd(a, a, a, a, ctypes.byref(p2), a, n, None, None, None, None) == -1
+    assert L.fsl_cell_stats(a, None, a, ctypes.byref(p), None) == -1
