@@ -1,0 +1,238 @@
+"""FS-L attention forward benchmark on one MI355X.
+
+One step = one fsl_attn_fwd call over the whole workload (cell statistics,
+norm prune, scoring + top-K, RoPE window attention, readout + RMSNorm + mix),
+inputs already resident in HBM. Prints one JSON line with whole-job tokens/s,
+per-stage kernel times measured with HIP events on the library's stream, the
+roofline of the dominant kernel and the oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload c4] [--no-cpu]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
+FP64_PEAK_TFLOPS = 78.6        # fp64 vector
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime's C API (torch's events only see torch's streams)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.arr[i] = h
+
+    def sub(self, start, n):
+        return ctypes.cast(ctypes.byref(self.arr, start * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[a], self.arr[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.arr:
+            self.hip.hipEventDestroy(h)
+
+
+def algorithmic_work(sh, sel_np=None):
+    """Per-launch algorithmic bytes / flops of each stage (roofline section)."""
+    H, N, d, s, w, B = sh.H, sh.N, sh.d, sh.s, sh.w, sh.B
+    e = 2 if sh.dtype == "bf16" else 4
+    C = N // s
+    i = np.arange(N, dtype=np.float64)
+    win_keys = np.minimum(i + 1, w).sum()
+    nblk = (N + B - 1) // B
+    nb = np.array([max(0, (b * B - w + 1) // s) for b in range(nblk)], dtype=np.int64)
+    npool = np.minimum(nb, sh.P + sh.W)
+    rows_per_blk = np.minimum(B, N - np.arange(nblk) * B)
+    work = {
+        "cell_stats": ("hbm", H * N * d * e + H * C * (d + 1) * 4),
+        "window": ("mfma", H * 4.0 * d * win_keys),
+        "select": ("alu", H * 2.0 * d * float((npool * rows_per_blk).sum())),
+        # compulsory streams: q read, o_win read, out written, plus the K/V rows of the
+        # distinct cells each block reads (measured union, counted once per block)
+        "readout_mix": ("hbm", H * N * d * (e + 4 + e)),
+    }
+    if sel_np is not None:
+        union_cells = 0
+        for h in range(H):
+            sh_sel = sel_np[h]
+            pad = (-N) % B
+            blocks = np.concatenate([sh_sel, np.full((pad, sh.K), -1, sh_sel.dtype)]).reshape(nblk, B * sh.K)
+            srt = np.sort(blocks, axis=1)
+            distinct = (np.diff(srt, axis=1) != 0).sum(axis=1) + 1 - (srt[:, 0] < 0)
+            union_cells += int(distinct.sum())
+        kind, base = work["readout_mix"]
+        work["readout_mix"] = (kind, base + union_cells * s * 2 * d * e)
+        work["_union_cells_per_block"] = union_cells / (H * nblk)
+    return work
+
+
+def cpu_baseline(inp, sample_rows):
+    """The oracle as it stands, on a bounded sample of the workload, scaled to tokens/s."""
+    from oracle import ref
+    sh = inp.shape
+    threads = len(os.sched_getaffinity(0))
+    rows = np.arange(sh.N - sample_rows, sh.N, dtype=np.int64)
+    t_fixed = 0.0
+    t_rows = 0.0
+    for h in range(sh.H):
+        p = ref.head_from_shape(sh, h, inp.sigma, inp.lam, inp.gamma)
+        t0 = time.perf_counter()
+        ref.forward_head(inp.q[h], inp.k[h], inp.v[h], p, rows=rows[-1:], nthreads=threads)
+        t1 = time.perf_counter()
+        ref.forward_head(inp.q[h], inp.k[h], inp.v[h], p, rows=rows, nthreads=threads)
+        t2 = time.perf_counter()
+        t_fixed += t1 - t0
+        t_rows += max(0.0, (t2 - t1) - (t1 - t0))
+    full = t_fixed + t_rows * sh.N / sample_rows
+    return {
+        "value": sh.N / full,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{sample_rows} query rows (the last {sample_rows // sh.B} blocks) x {sh.H} heads of the "
+                   f"{sh.name} workload, plus per-head cell statistics; rows time scaled by N/{sample_rows}; "
+                   f"measured {t_fixed + t_rows:.1f} s of oracle work"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4", help="c1..c4 (default c4: N=262144, H=8, d=128, bf16)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=131072)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "heads shard across GPUs with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_sparse_cell_amd import fsl, synth
+
+    sh = synth.CONFIGS[args.workload]
+    assert sh.kind == "fwd"
+    log(f"[bench] generating {sh.name}")
+    inp = synth.make_inputs(sh)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        if sh.dtype == synth.BF16:
+            return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in (inp.sigma, inp.lam, inp.gamma))
+    p = fsl.make_params(sh.N, sh.H, sh.d, q.dtype, sig, lam, gam, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
+    ws = fsl.new_workspace(p, dev)
+    out = torch.empty_like(q)
+    nst = fsl.NUM_STAGES + 1
+    ev = HipEvents(nst * max(args.steps, args.warmup, 1))
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(0, nst))
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(i * nst, nst))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * nst + j, i * nst + j + 1) for i in range(args.steps)]))
+                for j, name in enumerate(fsl.STAGES)}
+    gpu_ms = float(np.mean([ev.elapsed_ms(i * nst, i * nst + nst - 1) for i in range(args.steps)]))
+    log("[bench] stage ms: " + ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
+
+    sel_np = fsl.workspace_views(ws, p)["sel"].cpu().numpy()
+    work = algorithmic_work(sh, sel_np)
+    stages = {}
+    for name, t in stage_ms.items():
+        entry = {"ms": round(t, 4)}
+        if name in work:
+            kind, amount = work[name]
+            if kind == "hbm":
+                entry.update(bound="hbm", achieved=amount / (t * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+            elif kind == "mfma":
+                entry.update(bound="mfma", achieved=amount / (t * 1e-3) / 1e12, peak=MFMA_F16_PEAK_TFLOPS,
+                             unit="TFLOP/s")
+            else:
+                entry.update(bound="alu", achieved=amount / (t * 1e-3) / 1e12, peak=FP64_PEAK_TFLOPS,
+                             unit="TFLOP/s (fp64)")
+            entry["frac"] = entry["achieved"] / entry["peak"]
+            entry["achieved"] = round(entry["achieved"], 2)
+            entry["frac"] = round(entry["frac"], 4)
+        stages[name] = entry
+    dominant = max((n for n in stages if "bound" in stages[n]), key=lambda n: stage_ms[n])
+    dom = stages[dominant]
+    roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                "unit": dom["unit"], "frac": dom["frac"], "traffic": None}
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows")
+        cpu = cpu_baseline(inp, min(args.cpu_rows, sh.N))
+    ev.close()
+
+    tokens = sh.N
+    line = {
+        "metric": "FS-L attention fwd tokens/s at N=16k-256k; % of HBM/MFMA roofline",
+        "value": round(tokens * args.steps / (t1 - t0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sh.dtype,
+        "data": "synthetic (seeded q/k/v with planted needles; no dataset)",
+        "config": {"workload": sh.name, "H": sh.H, "N": sh.N, "d": sh.d, "w": sh.w, "s": sh.s, "P": sh.P,
+                   "W": sh.W, "K": sh.K, "B": sh.B, "batch": 1},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "union_cells_per_block": round(work.get("_union_cells_per_block", 0.0), 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

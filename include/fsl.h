@@ -141,6 +141,18 @@ int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const f
                  void *ws, size_t ws_bytes, int32_t *sel_out, float *o_win_out,
                  float *o_long_out, hipStream_t stream);
 
+/* fsl_attn_fwd with stage timing. stage_events must point to
+ * FSL_NUM_STAGES + 1 caller-created hipEvent_t handles; events[0] is recorded
+ * on `stream` before the first kernel and events[s + 1] after stage s, the
+ * stages being, in order: cell statistics, norm prune (4 kernels), scoring and
+ * top-K, RoPE table, window attention, readout + mix. Elapsed time between
+ * consecutive events is the duration of that stage's kernels. Same arguments,
+ * results and errors as fsl_attn_fwd otherwise (FSL_E_INVAL if stage_events
+ * is NULL). */
+#define FSL_NUM_STAGES 6
+int fsl_attn_fwd_timed(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
+                       void *ws, size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
+
 /* Byte offsets of the named arrays inside a forward workspace (host-only).
  * Returns FSL_OK or the fsl_check_params error. */
 typedef struct fsl_workspace_layout {

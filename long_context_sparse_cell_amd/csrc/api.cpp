@@ -143,8 +143,9 @@ int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_
     return hip_status(e);
 }
 
-int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const fsl_params *p, void *ws,
-                 size_t ws_bytes, int32_t *sel_out, float *o_win_out, float *o_long_out, hipStream_t stream) {
+static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out, const fsl_params *p, void *ws,
+                         size_t ws_bytes, int32_t *sel_out, float *o_win_out, float *o_long_out, hipEvent_t *ev,
+                         hipStream_t stream) {
     int rc = check(p);
     if (rc != FSL_OK) return rc;
     if (!q || !k || !v || !out || !ws) return FSL_E_INVAL;
@@ -156,12 +157,19 @@ int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const f
     const fsl_workspace_layout L = layout(kp);
     if (ws_bytes < L.total) return FSL_E_WORKSPACE;
     const Work w = carve(ws, L);
-    hipError_t e = launch_cell_stats(k, w.kbar, w.amax, kp, stream);
-    if (e == hipSuccess) e = launch_prune(w.amax, w.pool, w, kp, stream);
-    if (e == hipSuccess) e = launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream);
-    if (e == hipSuccess) e = launch_rope_table(w.rope, kp, stream);
-    if (e == hipSuccess) e = launch_window(q, k, v, w.rope, w.o_win, kp, stream);
-    if (e == hipSuccess) e = launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream);
+    int stage = 0;
+    auto mark = [&](hipError_t e) {
+        if (e == hipSuccess && ev) e = hipEventRecord(ev[stage], stream);
+        ++stage;
+        return e;
+    };
+    hipError_t e = mark(hipSuccess);
+    if (e == hipSuccess) e = mark(launch_cell_stats(k, w.kbar, w.amax, kp, stream));
+    if (e == hipSuccess) e = mark(launch_prune(w.amax, w.pool, w, kp, stream));
+    if (e == hipSuccess) e = mark(launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
+    if (e == hipSuccess) e = mark(launch_rope_table(w.rope, kp, stream));
+    if (e == hipSuccess) e = mark(launch_window(q, k, v, w.rope, w.o_win, kp, stream));
+    if (e == hipSuccess) e = mark(launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
     if (e == hipSuccess && sel_out)
         e = hipMemcpyAsync(sel_out, w.sel, (size_t)kp.H * kp.N * kp.K * sizeof(int32_t), hipMemcpyDeviceToDevice,
                            stream);
@@ -169,6 +177,17 @@ int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const f
         e = hipMemcpyAsync(o_win_out, w.o_win, (size_t)kp.H * kp.N * kp.d * sizeof(float), hipMemcpyDeviceToDevice,
                            stream);
     return hip_status(e);
+}
+
+int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const fsl_params *p, void *ws,
+                 size_t ws_bytes, int32_t *sel_out, float *o_win_out, float *o_long_out, hipStream_t stream) {
+    return attn_fwd_impl(q, k, v, out, p, ws, ws_bytes, sel_out, o_win_out, o_long_out, nullptr, stream);
+}
+
+int fsl_attn_fwd_timed(const void *q, const void *k, const void *v, void *out, const fsl_params *p, void *ws,
+                       size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream) {
+    if (!stage_events) return check(p) != FSL_OK ? check(p) : FSL_E_INVAL;
+    return attn_fwd_impl(q, k, v, out, p, ws, ws_bytes, nullptr, nullptr, nullptr, stage_events, stream);
 }
 
 }  // extern "C"

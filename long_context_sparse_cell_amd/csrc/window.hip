@@ -16,8 +16,13 @@
 //  - RoPE uses positions relative to the workgroup's first query q0: the
 //    score depends only on j - i, and |j - q0| < w + 128 keeps the fp64-built
 //    cos/sin table small and exact to fp32 rounding at any absolute position.
-//  - bf16 inputs: v_mfma_f32_16x16x32_bf16, P rounded to bf16 (the softmax
-//    denominator sums the rounded values). fp32 inputs: v_mfma_f32_16x16x4_f32.
+//  - bf16 inputs: the rotated q, k, the probabilities P and v enter
+//    v_mfma_f32_16x16x32_f16 as fp16 (fp32 accumulation). bf16 -> fp16 is
+//    exact in fp16's normal range, and fp16's 11-bit significand keeps the
+//    rounding of rotated q/k and of P about 8x below bf16's, which leaves
+//    room for the bf16 rounding of the output itself. Inputs are assumed to
+//    stay within fp16 range (|x| < 65504). The softmax denominator sums the
+//    rounded P. fp32 inputs: v_mfma_f32_16x16x4_f32 throughout.
 #include <cmath>
 #include <type_traits>
 
@@ -25,7 +30,7 @@
 
 namespace fsl {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __global__ void rope_table_kernel(float2 *__restrict__ tab, KParams p) {
@@ -47,8 +52,17 @@ hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st) {
 union Pack8 {
     uint4 u;
     uint16_t h[8];
-    bf16x8 v;
+    _Float16 f[8];
+    halfx8 v;
 };
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    union { _Float16 f; uint16_t u; } c;
+    c.f = (_Float16)x;
+    return c.u;
+}
+
+__device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x; }
 
 template <typename T, int D>
 struct WinLds;
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
 
     // ---- rotated queries as MFMA B operands (column = query, k-slot = dim)
     constexpr int QS = BF ? D / 32 : D / 4;  // k-steps over d
-    using QReg = typename std::conditional<BF, bf16x8, float>::type;
+    using QReg = typename std::conditional<BF, halfx8, float>::type;
     QReg qreg[2][QS];
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
             for (int ks = 0; ks < QS; ++ks) {
                 Pack8 pk;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) pk.h[r] = f32_to_bf16(x[ks][r]);
+                for (int r = 0; r < 8; ++r) pk.f[r] = (_Float16)x[ks][r];
                 qreg[qg][ks] = pk.v;
             }
         } else {
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
             if constexpr (BF) {
                 Pack8 pa, pb;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) { pa.h[r] = f32_to_bf16(a[r]); pb.h[r] = f32_to_bf16(b[r]); }
+                for (int r = 0; r < 8; ++r) { pa.f[r] = (_Float16)a[r]; pb.f[r] = (_Float16)b[r]; }
                 *reinterpret_cast<uint4 *>(&lds.k[jl * L::KLD + 8 * c]) = pa.u;
                 *reinterpret_cast<uint4 *>(&lds.k[jl * L::KLD + HALF + 8 * c]) = pb.u;
             } else {
@@ -194,18 +208,21 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
         }
         for (int it = tid; it < (kKTile / 4) * (D / 8); it += 256) {
             const int jq = it / (D / 8), c = it % (D / 8);
-            T e[4][8];
+            float e[4][8];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int64_t j = ks0 + 4 * jq + u;
                 const bool ok = j >= 0 && j < p.N;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) e[u][r] = ok ? vh[j * D + 8 * c + r] : (T)0;
+                for (int r = 0; r < 8; ++r) e[u][r] = ok ? to_f32<T>(vh[j * D + 8 * c + r]) : 0.0f;
             }
 #pragma unroll
             for (int r = 0; r < 8; ++r)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) lds.vt[(8 * c + r) * L::VLD + 4 * jq + u] = e[u][r];
+                for (int u = 0; u < 4; ++u) {
+                    if constexpr (BF) lds.vt[(8 * c + r) * L::VLD + 4 * jq + u] = f32_to_f16_bits(e[u][r]);
+                    else lds.vt[(8 * c + r) * L::VLD + 4 * jq + u] = e[u][r];
+                }
         }
         __syncthreads();
 
@@ -223,7 +240,7 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
                     for (int ks = 0; ks < QS; ++ks) {
                         Pack8 ka;
                         ka.u = *reinterpret_cast<const uint4 *>(&lds.k[(16 * kg + col) * L::KLD + 32 * ks + 8 * g]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qreg[qg][ks], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[qg][ks], acc, 0, 0, 0);
                     }
                 } else {
 #pragma unroll
@@ -262,7 +279,7 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float pv = exp2f(sacc[kg][qg][r] - m_use);
-                    if constexpr (BF) pv = bf16_to_f32(f32_to_bf16(pv));
+                    if constexpr (BF) pv = round_f16(pv);
                     sacc[kg][qg][r] = pv;
                     lsum += pv;
                 }
@@ -280,8 +297,8 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
                     Pack8 pb;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        pb.h[r] = f32_to_bf16(sacc[2 * kk][qg][r]);
-                        pb.h[4 + r] = f32_to_bf16(sacc[2 * kk + 1][qg][r]);
+                        pb.f[r] = (_Float16)sacc[2 * kk][qg][r];
+                        pb.f[4 + r] = (_Float16)sacc[2 * kk + 1][qg][r];
                     }
 #pragma unroll
                     for (int dt = 0; dt < D / 16; ++dt) {
@@ -290,7 +307,7 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
                         const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
                         const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
                         va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                        oacc[qg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb.v, oacc[qg][dt], 0, 0, 0);
+                        oacc[qg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb.v, oacc[qg][dt], 0, 0, 0);
                     }
                 }
             }

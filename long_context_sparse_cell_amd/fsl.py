@@ -65,6 +65,8 @@ def lib():
         L.fsl_prune_select.argtypes = [vp, vp, vp, vp, vp, pp, vp, sz, vp]
         L.fsl_attn_fwd.restype = i32
         L.fsl_attn_fwd.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, vp, vp, vp]
+        L.fsl_attn_fwd_timed.restype = i32
+        L.fsl_attn_fwd_timed.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, vp]
         _lib = L
     return _lib
 
@@ -166,6 +168,17 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, out: 
     ws = new_workspace(p, q.device) if ws is None else ws
     _check(lib().fsl_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(p), _ptr(ws), ws.numel(),
                               _ptr(sel_out), _ptr(o_win_out), _ptr(o_long_out), _stream(stream)), "fsl_attn_fwd")
+    return out
+
+
+NUM_STAGES = 6
+STAGES = ("cell_stats", "prune", "select", "rope_table", "window", "readout_mix")
+
+
+def attn_fwd_timed(q, k, v, p: Params, out: torch.Tensor, ws: torch.Tensor, events, stream=None):
+    """fsl_attn_fwd recording NUM_STAGES + 1 hipEvent_t handles (a ctypes array) between its stages."""
+    _check(lib().fsl_attn_fwd_timed(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(p), _ptr(ws), ws.numel(),
+                                    events, _stream(stream)), "fsl_attn_fwd_timed")
     return out
 
 

@@ -59,9 +59,11 @@ def oracle_head_params(oracle, sh, inp, h, **over):
 
 def check_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
     err = np.abs(got.astype(np.float64) - ref)
+    at = np.unravel_index(int(np.argmax(err)), err.shape)
+    info = f"{what}: max abs err {err.max():.3e} at {at} (oracle {ref[at]:.5f}, got {got[at]:.5f}), mean {err.mean():.3e}"
     if dtype == synth.BF16:
-        assert err.max() <= BF16_MAX_ABS, f"{what}: max abs err {err.max():.3e}"
-        assert err.mean() <= BF16_MEAN_ABS, f"{what}: mean abs err {err.mean():.3e}"
+        assert err.max() <= BF16_MAX_ABS, info
+        assert err.mean() <= BF16_MEAN_ABS, info
     else:
-        assert err.max() <= F32_MAX_ABS, f"{what}: max abs err {err.max():.3e}"
+        assert err.max() <= F32_MAX_ABS, info
     return float(err.max()), float(err.mean())

@@ -47,13 +47,14 @@ def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=
         np.testing.assert_array_equal(pools[h], r["pool"], err_msg=f"pool head {h}")
         idx = r["rows"]
         np.testing.assert_array_equal(sel[h][idx], r["sel"], err_msg=f"sel head {h}")
+        if check_internals:
+            ew = np.abs(o_win[h][idx] - r["o_win"]).max()
+            el = np.abs(o_long[h][idx] - r["o_long"]).max()
+            print(f"  head {h}: o_win max err {ew:.3e}, o_long max err {el:.3e}", flush=True)
+            assert ew <= (1e-4 if sh.dtype == synth.F32 else 4e-3), f"o_win head {h}: {ew:.3e}"
+            assert el <= 1e-4, f"o_long head {h}: {el:.3e}"
         mx, _ = check_out(out[h][idx], r["out"], out_dtype, f"out head {h}")
         worst = max(worst, mx)
-        if check_internals:
-            tol = 1e-4 if sh.dtype == synth.F32 else 1.5e-2
-            assert np.abs(o_win[h][idx] - r["o_win"]).max() <= tol, f"o_win head {h}"
-            assert np.abs(o_long[h][idx] - r["o_long"]).max() <= (1e-4 if sh.dtype == synth.F32 else 1e-3), \
-                f"o_long head {h}"
     return worst
 
 
