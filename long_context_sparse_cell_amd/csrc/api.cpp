@@ -139,7 +139,9 @@ int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_
     if (ws_bytes < L.total) return FSL_E_WORKSPACE;
     const Work w = carve(ws, L);
     hipError_t e = launch_prune(amax, pool, w, k, stream);
-    if (e == hipSuccess) e = launch_select(q, kbar, amax, pool, sel, k, stream);
+    if (e == hipSuccess)
+        e = k.dtype == FSL_BF16 ? launch_select_mfma(q, kbar, amax, pool, sel, k, stream)
+                                : launch_select(q, kbar, amax, pool, sel, k, stream);
     return hip_status(e);
 }
 
@@ -166,10 +168,17 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
     hipError_t e = mark(hipSuccess);
     if (e == hipSuccess) e = mark(launch_cell_stats(k, w.kbar, w.amax, kp, stream));
     if (e == hipSuccess) e = mark(launch_prune(w.amax, w.pool, w, kp, stream));
-    if (e == hipSuccess) e = mark(launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
+    if (e == hipSuccess)
+        e = mark(kp.dtype == FSL_BF16 ? launch_select_mfma(q, w.kbar, w.amax, w.pool, w.sel, kp, stream)
+                                      : launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
     if (e == hipSuccess) e = mark(launch_rope_table(w.rope, kp, stream));
-    if (e == hipSuccess) e = mark(launch_window(q, k, v, w.rope, w.o_win, kp, stream));
-    if (e == hipSuccess) e = mark(launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
+    if (e == hipSuccess)
+        e = mark(kp.dtype == FSL_BF16 ? launch_window_bf16(q, k, v, w.rope, w.o_win, kp, stream)
+                                      : launch_window(q, k, v, w.rope, w.o_win, kp, stream));
+    if (e == hipSuccess)
+        e = mark(kp.dtype == FSL_BF16
+                     ? launch_readout_cells(q, k, v, w.sel, w.pool, w.o_win, out, o_long_out, kp, stream)
+                     : launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
     if (e == hipSuccess && sel_out)
         e = hipMemcpyAsync(sel_out, w.sel, (size_t)kp.H * kp.N * kp.K * sizeof(int32_t), hipMemcpyDeviceToDevice,
                            stream);

@@ -137,9 +137,15 @@ hipError_t launch_cell_stats(const void *k, float *kbar, float *amax, const KPar
 hipError_t launch_prune(const float *amax, int32_t *pool, const Work &w, const KParams &p, hipStream_t st);
 hipError_t launch_select(const void *q, const float *kbar, const float *amax, const int32_t *pool,
                          int32_t *sel, const KParams &p, hipStream_t st);
+hipError_t launch_select_mfma(const void *q, const float *kbar, const float *amax, const int32_t *pool,
+                              int32_t *sel, const KParams &p, hipStream_t st);
 hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st);
 hipError_t launch_window(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
                          const KParams &p, hipStream_t st);
+hipError_t launch_window_bf16(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
+                              const KParams &p, hipStream_t st);
+hipError_t launch_readout_cells(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
+                                const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st);
 hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const int32_t *sel,
                               const float *o_win, void *out, float *o_long_out, const KParams &p,
                               hipStream_t st);

@@ -1,0 +1,252 @@
+// Cell scoring and top-K for bf16 inputs: an MFMA filter with a certified
+// error bound, then exact fp64 re-scoring of the few cells the bound cannot
+// separate (FreeSolo digest, core method and step 5: content match plus a
+// norm-weighted erf relative-position bias, top K cells).
+//
+// The exact score of the oracle and of the fp64 kernel is
+//   s = fma(rho, q.kbar_c, (lambda * a_c) * erf(sigma (i - c s) / (2 s)))
+// with the dot product a left-to-right fp64 fma chain. Here:
+//  1. content~ = q . (hi + lo) on v_mfma_f32_16x16x32_bf16, where hi and lo are
+//     the bf16 head and tail of the float32 kbar_c (q is bf16, so every
+//     product is exact in fp32). |kbar - hi - lo| <= 2^-18 |kbar| and the fp32
+//     accumulation of 2d exact products adds at most (2d+1) 2^-24 of their
+//     absolute sum, so
+//        |content - content~| <= ||q|| ||kbar_c|| (2^-17 + (4d+8) 2^-24)
+//     (Cauchy-Schwarz bounds the absolute sum). The fp32 bias and the final
+//     fp32 additions get their own rounding terms; the total is doubled.
+//  2. Per query, theta = the K-th largest lower bound s~ - eps. A cell whose
+//     upper bound s~ + eps is below theta is beaten by K cells for sure; every
+//     other cell ("contender") is re-scored exactly in fp64 and the K best
+//     contenders under (score desc, index asc) are the exact top-K.
+// One workgroup = up to 128 queries of one block, 8 waves x 16 queries.
+#include <climits>
+
+#include "fsl_internal.h"
+
+namespace fsl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kSelQ = 128;
+constexpr int kSelPool = 128;
+constexpr int kSelK = 8;
+
+union U16x8s {
+    uint4 u;
+    bf16x8 b;
+    uint16_t h[8];
+};
+
+// carry (v, i) down a list sorted by (v desc, i asc), dropping the last entry
+template <typename F>
+__device__ __forceinline__ void list_insert(F (&lv)[kSelK], int (&li)[kSelK], F v, int i, int K) {
+#pragma unroll
+    for (int r = 0; r < kSelK; ++r) {
+        if (r < K && (v > lv[r] || (v == lv[r] && i < li[r]))) {
+            F tv = lv[r]; int ti = li[r];
+            lv[r] = v; li[r] = i;
+            v = tv; i = ti;
+        }
+    }
+}
+
+template <typename F>
+__device__ __forceinline__ void list_merge_xor(F (&lv)[kSelK], int (&li)[kSelK], int K, int mask) {
+    F pv[kSelK];
+    int pi[kSelK];
+#pragma unroll
+    for (int r = 0; r < kSelK; ++r) { pv[r] = __shfl_xor(lv[r], mask); pi[r] = __shfl_xor(li[r], mask); }
+#pragma unroll
+    for (int r = 0; r < kSelK; ++r)
+        if (r < K) list_insert<F>(lv, li, pv[r], pi[r], K);
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__restrict__ q, const float *__restrict__ kbar,
+                                                          const float *__restrict__ amax,
+                                                          const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
+                                                          KParams p, int QW) {
+    constexpr int LD = D + 1;
+    __shared__ float s_kb[kSelPool * LD];
+    __shared__ float s_q[kSelQ * LD];
+    __shared__ int s_pool[kSelPool];
+    __shared__ float s_kn[kSelPool];
+    __shared__ float s_a[kSelPool];
+    __shared__ float s_qn[kSelQ];
+
+    const int h = blockIdx.y;
+    const int64_t q0 = (int64_t)blockIdx.x * QW;
+    const int64_t b = q0 / p.B;
+    const int nq = (int)min((int64_t)QW, p.N - q0);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, g = lane >> 4;
+    const int K = p.K;
+    const int npool = (int)min((int64_t)p.PW, eligible_cells(p, b));
+    const int64_t hN = (int64_t)h * p.N;
+
+    for (int t = tid; t < npool; t += 512) {
+        const int c = pool[((int64_t)h * p.nblk + b) * p.PW + t];
+        s_pool[t] = c;
+        s_a[t] = amax[(int64_t)h * p.C + c];
+    }
+    __syncthreads();
+    for (int e = tid; e < npool * D; e += 512) {
+        const int r = e / D, x = e % D;
+        s_kb[r * LD + x] = kbar[((int64_t)h * p.C + s_pool[r]) * D + x];
+    }
+    for (int e = tid; e < nq * D; e += 512) {
+        const int r = e / D, x = e % D;
+        s_q[r * LD + x] = bf16_to_f32(q[(hN + q0 + r) * D + x]);
+    }
+    __syncthreads();
+    for (int t = tid; t < npool + nq; t += 512) {
+        const float *row = t < npool ? &s_kb[t * LD] : &s_q[(t - npool) * LD];
+        float ss = 0.0f;
+        for (int x = 0; x < D; ++x) ss += row[x] * row[x];
+        if (t < npool) s_kn[t] = sqrtf(ss);
+        else s_qn[t - npool] = sqrtf(ss);
+    }
+    __syncthreads();
+
+    const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+    const float sigf = p.sigma[h], lamf = p.lambda[h], rhof = p.rho;
+    const float epsc = 1.001f * (7.62939453125e-06f + (float)(4 * D + 8) * 5.9604644775390625e-08f);
+    const int ntile = (npool + 15) / 16;
+
+    {  // 8 waves x 16 queries
+        const int ql = 16 * wave + col;
+        const bool qok = ql < nq;
+        const int qr = qok ? ql : 0;
+        const int64_t i = q0 + qr;
+        U16x8s bq[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qr) * D + 32 * ks + 8 * g);
+        const float qn = s_qn[qr];
+
+        float lowv[kSelK];
+        int lowi[kSelK];
+#pragma unroll
+        for (int r = 0; r < kSelK; ++r) { lowv[r] = -INFINITY; lowi[r] = INT_MAX; }
+        // approximate scores, 4 cells of each 16-cell tile per lane (cells 16*ct + 4*g + e)
+        float sapx[kSelPool / 16][4];
+        float seps[kSelPool / 16][4];
+#pragma unroll
+        for (int ct = 0; ct < kSelPool / 16; ++ct) {
+            if (ct >= ntile) break;
+            const int rowc = 16 * ct + col;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                U16x8s hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = rowc < npool ? s_kb[rowc * LD + 32 * ks + 8 * g + e] : 0.0f;
+                    const uint16_t hb = f32_to_bf16(x);
+                    hi.h[e] = hb;
+                    lo.h[e] = f32_to_bf16(x - bf16_to_f32(hb));
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi.b, bq[ks].b, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.b, bq[ks].b, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = 16 * ct + 4 * g + e;
+                sapx[ct][e] = -INFINITY;
+                seps[ct][e] = 0.0f;
+                if (pos < npool) {
+                    const int c = s_pool[pos];
+                    const float argf = sigf * (float)(i - (int64_t)c * p.s) / (2.0f * (float)p.s);
+                    const float gf = argf >= 6.0f ? 1.0f : erff(argf);
+                    const float la = lamf * s_a[pos];
+                    const float bf = la * gf;
+                    const float rc = rhof * acc[e];
+                    const float sv = rc + bf;
+                    float ev = fabsf(rhof) * qn * s_kn[pos] * epsc + fabsf(la) * 2e-6f +
+                               (fabsf(rc) + fabsf(bf)) * 2.384185791015625e-07f + 1e-30f;
+                    ev *= 2.0f;
+                    sapx[ct][e] = sv;
+                    seps[ct][e] = ev;
+                    list_insert<float>(lowv, lowi, sv - ev, pos, K);
+                }
+            }
+        }
+        list_merge_xor<float>(lowv, lowi, K, 16);
+        list_merge_xor<float>(lowv, lowi, K, 32);
+        float theta = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kSelK; ++r)
+            if (r == K - 1) theta = lowv[r];
+
+        // exact re-scoring of the contenders
+        double exv[kSelK];
+        int exi[kSelK];
+#pragma unroll
+        for (int r = 0; r < kSelK; ++r) { exv[r] = -INFINITY; exi[r] = INT_MAX; }
+        // this lane's contenders as a bitmask over its (tile, e) slots; the wave loops only as
+        // often as its busiest lane has contenders
+        uint32_t cmask = 0;
+#pragma unroll
+        for (int ct = 0; ct < kSelPool / 16; ++ct) {
+            if (ct >= ntile) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = 16 * ct + 4 * g + e;
+                if (pos < npool && sapx[ct][e] + seps[ct][e] >= theta) cmask |= 1u << (4 * ct + e);
+            }
+        }
+        int maxn = __popc(cmask);
+#pragma unroll
+        for (int m2 = 32; m2 > 0; m2 >>= 1) maxn = max(maxn, __shfl_xor(maxn, m2));
+        const float *qrow = &s_q[qr * LD];
+        for (int t = 0; t < maxn; ++t) {
+            if (cmask) {
+                const int slot = __ffs(cmask) - 1;
+                cmask &= cmask - 1;
+                const int pos = 16 * (slot >> 2) + 4 * g + (slot & 3);
+                const int c = s_pool[pos];
+                const float *krow = &s_kb[pos * LD];
+                double content = 0.0;
+#pragma unroll 8
+                for (int x = 0; x < D; ++x) content = __fma_rn((double)qrow[x], (double)krow[x], content);
+                const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
+                const double gg = arg >= 6.0 ? 1.0 : erf(arg);
+                const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[pos]), gg);
+                list_insert<double>(exv, exi, __fma_rn(rho, content, bias), c, K);
+            }
+        }
+        list_merge_xor<double>(exv, exi, K, 16);
+        list_merge_xor<double>(exv, exi, K, 32);
+        if (qok && g == 0) {
+#pragma unroll
+            for (int x = 0; x < kSelK; ++x)
+#pragma unroll
+                for (int y = 0; y + 1 < kSelK - x; ++y)
+                    if (exi[y] > exi[y + 1]) { int t2 = exi[y]; exi[y] = exi[y + 1]; exi[y + 1] = t2; }
+            int32_t *o = sel + (hN + i) * K;
+#pragma unroll
+            for (int r = 0; r < kSelK; ++r)
+                if (r < K) o[r] = exi[r] == INT_MAX ? -1 : exi[r];
+        }
+    }
+}
+
+hipError_t launch_select_mfma(const void *q, const float *kbar, const float *amax, const int32_t *pool,
+                              int32_t *sel, const KParams &p, hipStream_t st) {
+    const int QW = p.B <= kSelQ ? p.B : p.B / 2;
+    dim3 grid((unsigned)((p.N + QW - 1) / QW), (unsigned)p.H);
+    if (p.d == 64)
+        hipLaunchKernelGGL((select_mfma_kernel<64>), grid, dim3(512), 0, st, (const uint16_t *)q, kbar, amax, pool, sel,
+                           p, QW);
+    else
+        hipLaunchKernelGGL((select_mfma_kernel<128>), grid, dim3(512), 0, st, (const uint16_t *)q, kbar, amax, pool,
+                           sel, p, QW);
+    return hipGetLastError();
+}
+
+}  // namespace fsl

@@ -64,6 +64,23 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 
 __device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x; }
 
+// eight consecutive elements as float (one 16-byte load for bf16, two for fp32)
+__device__ __forceinline__ void load8(const uint16_t *ptr, float (&o)[8]) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(ptr);
+    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        o[2 * t] = __uint_as_float(w4[t] << 16);
+        o[2 * t + 1] = __uint_as_float(w4[t] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float *ptr, float (&o)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(ptr);
+    const float4 b = *reinterpret_cast<const float4 *>(ptr + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
 template <typename T, int D>
 struct WinLds;
 
@@ -175,22 +192,20 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
         for (int it = tid; it < kKTile * (D / 16); it += 256) {
             const int jl = it / (D / 16), c = it % (D / 16);
             const int64_t j = ks0 + jl;
+            // out-of-range keys read a clamped valid row and are zeroed (their scores are masked)
+            const bool ok = j >= 0 && j < p.N;
+            const int64_t jc = ok ? j : 0;
+            const T *kr = kh + jc * D;
             float a[8], b[8];
-            if (j >= 0 && j < p.N) {
-                const T *kr = kh + j * D;
+            load8(kr + 8 * c, a);
+            load8(kr + HALF + 8 * c, b);
+            const float2 *tr = rope + (int64_t)(j - q0 - p.rope_lo) * HALF + 8 * c;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) { a[r] = to_f32<T>(kr[8 * c + r]); b[r] = to_f32<T>(kr[HALF + 8 * c + r]); }
-                const float2 *tr = rope + (int64_t)(j - q0 - p.rope_lo) * HALF + 8 * c;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float2 cs = tr[r];
-                    const float x0 = a[r], y0 = b[r];
-                    a[r] = x0 * cs.x - y0 * cs.y;
-                    b[r] = y0 * cs.x + x0 * cs.y;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) { a[r] = 0.0f; b[r] = 0.0f; }
+            for (int r = 0; r < 8; ++r) {
+                const float2 cs = tr[r];
+                const float x0 = ok ? a[r] : 0.0f, y0 = ok ? b[r] : 0.0f;
+                a[r] = x0 * cs.x - y0 * cs.y;
+                b[r] = y0 * cs.x + x0 * cs.y;
             }
             if constexpr (BF) {
                 Pack8 pa, pb;
@@ -213,8 +228,9 @@ __global__ __launch_bounds__(256) void window_kernel(const T *__restrict__ q, co
             for (int u = 0; u < 4; ++u) {
                 const int64_t j = ks0 + 4 * jq + u;
                 const bool ok = j >= 0 && j < p.N;
+                load8(vh + (ok ? j : 0) * D + 8 * c, e[u]);
 #pragma unroll
-                for (int r = 0; r < 8; ++r) e[u][r] = ok ? to_f32<T>(vh[j * D + 8 * c + r]) : 0.0f;
+                for (int r = 0; r < 8; ++r) e[u][r] = ok ? e[u][r] : 0.0f;
             }
 #pragma unroll
             for (int r = 0; r < 8; ++r)

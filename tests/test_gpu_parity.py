@@ -49,11 +49,15 @@ def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=
         np.testing.assert_array_equal(sel[h][idx], r["sel"], err_msg=f"sel head {h}")
         if check_internals:
             ew = np.abs(o_win[h][idx] - r["o_win"]).max()
-            el = np.abs(o_long[h][idx] - r["o_long"]).max()
-            print(f"  head {h}: o_win max err {ew:.3e}, o_long max err {el:.3e}", flush=True)
+
+            def normed(o):
+                return o / np.sqrt((o.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6)
+            el = np.abs(normed(o_long[h][idx]) - normed(r["o_long"])).max()
+            print(f"  head {h}: o_win max err {ew:.3e}, RMSNorm(o_long) max err {el:.3e}", flush=True)
             assert ew <= (1e-4 if sh.dtype == synth.F32 else 4e-3), f"o_win head {h}: {ew:.3e}"
-            assert el <= 1e-4, f"o_long head {h}: {el:.3e}"
-        mx, _ = check_out(out[h][idx], r["out"], out_dtype, f"out head {h}")
+            assert el <= (1e-4 if sh.dtype == synth.F32 else 4e-3), f"RMSNorm(o_long) head {h}: {el:.3e}"
+        mx, mean = check_out(out[h][idx], r["out"], out_dtype, f"out head {h}")
+        print(f"  head {h}: out max err {mx:.3e}, mean {mean:.3e}", flush=True)
         worst = max(worst, mx)
     return worst
 
