@@ -124,6 +124,53 @@ def cpu_baseline(inp, sample_rows):
     }
 
 
+def decode_bench(fsl, synth, torch, dev, steps_override=None):
+    """Streaming decode workload: prefill every sequence, then time the steps."""
+    sh = synth.CONFIGS["c5"]
+    H, d, n, L = sh.H, sh.d, sh.n_seq, sh.prefix
+    steps = sh.steps if steps_override is None else steps_override
+    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in synth.head_scalars(H))
+    p = fsl.make_params(1, H, d, torch.bfloat16, sig, lam, gam, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
+    st = fsl.DecodeState(p, n, dev)
+    gen = torch.Generator(device=dev)
+    ws = None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(n):
+        gen.manual_seed(sh.seed * 1000 + r)
+        kp = torch.randn((H, L, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vp = torch.randn((H, L, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        ws = st.prefill(r, kp, vp, ws)
+        del kp, vp
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    gen.manual_seed(sh.seed * 1000 + 999)
+    qs = torch.randn((steps, n, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ks = torch.randn((steps, n, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vs = torch.randn((steps, n, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st.step(qs[i], ks[i], vs[i], out=out)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    e = 2
+    pool_cells = sh.P + sh.W
+    per_head = (sh.w * 2 * d * e) + pool_cells * (d + 1) * 4 + sh.K * sh.s * 2 * d * e + 4 * d * e
+    step_bytes = per_head * n * H
+    step_s = el / steps
+    return {
+        "workload": sh.name, "sequences": n, "steps": steps, "prefix": L,
+        "tokens_per_s": round(n * steps / el, 1), "ms_per_step": round(step_s * 1e3, 4),
+        "prefill_s_total": round(t_prefill, 3), "state_mib": round(st.nbytes / 2 ** 20, 1),
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / step_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes_per_step": step_bytes},
+        "data": "synthetic: k/v/q ~ N(0,1) from seeded device generators",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +179,7 @@ def main():
     ap.add_argument("--workload", default="c4", help="c1..c4 (default c4: N=262144, H=8, d=128, bf16)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-rows", type=int, default=131072)
+    ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -203,6 +251,14 @@ def main():
     roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                 "unit": dom["unit"], "frac": dom["frac"], "traffic": None}
 
+    dec = None
+    if not args.no_decode:
+        log("[bench] streaming decode workload")
+        del ws
+        torch.cuda.empty_cache()
+        dec = decode_bench(fsl, synth, torch, dev)
+        log(f"[bench] decode {dec['tokens_per_s']:.0f} tokens/s, {dec['ms_per_step']:.3f} ms/step")
+
     cpu = None
     if not args.no_cpu:
         log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows")
@@ -230,6 +286,7 @@ def main():
         "stages": stages,
         "gpu_ms_per_step": round(gpu_ms, 4),
         "union_cells_per_block": round(work.get("_union_cells_per_block", 0.0), 2),
+        "decode": dec,
     }
     print(json.dumps(line), flush=True)
 

@@ -168,6 +168,56 @@ typedef struct fsl_workspace_layout {
 } fsl_workspace_layout;
 int fsl_workspace_views(const fsl_params *p, fsl_workspace_layout *out);
 
+/* ------------------------------------------------------------------------
+ * Streaming decode (ai.info summary, "Why This Matters": a bounded streaming
+ * state of O(((P+W)s + w + B + s)d) per head; methodology: the pool changes
+ * only at block boundaries; digest, results: constant attention buffer from
+ * 4k to 256k context).
+ *
+ * One flat, versioned device buffer holds the state of n_seq independent
+ * sequences x H heads. Per (sequence, head): the next position t, a ring of
+ * the last w + B + s tokens' raw k/v (the window plus the tokens not yet in
+ * an eligible cell), and P + W pool slots, each holding one cell's raw k/v,
+ * mean key and max key norm. When t enters a new block, the cells that became
+ * eligible take free slots (copied once from the ring), the cells leaving the
+ * recent set compete for the P high-norm places, and losers free their slots;
+ * nothing else moves. The size does not depend on the prefix length.
+ * Output at position t equals the forward's output at row t of the whole
+ * sequence (selected cells bit-identical; window arithmetic in fp32 here).
+ * fp32 and bf16 (dtype) are supported; P = -1 is not (FSL_E_UNSUPPORTED). */
+
+/* Bytes of state for n_seq sequences under p (p->N is ignored); 0 if invalid. */
+size_t fsl_decode_state_bytes(const fsl_params *p, int32_t n_seq);
+
+/* Write the header and reset every sequence to position 0 with an empty pool.
+ * state: device buffer of at least fsl_decode_state_bytes(p, n_seq) bytes. */
+int fsl_decode_init(void *state, size_t state_bytes, int32_t n_seq, const fsl_params *p, hipStream_t stream);
+
+/* Workspace bytes fsl_decode_prefill needs for a prefix of prefix_len tokens. */
+size_t fsl_decode_prefill_workspace_bytes(const fsl_params *p, int64_t prefix_len);
+
+/* Load sequence `seq` with a prefix of prefix_len >= 1 tokens: cell statistics
+ * and the pool of the block holding position prefix_len are computed as in
+ * the forward, the pool cells' k/v are copied into slots and the ring gets
+ * the tokens since the first non-eligible cell. k_prefix, v_prefix: device
+ * [H][prefix_len][d] (dtype); they are not referenced after the call's work
+ * completes. The sequence's next position becomes prefix_len. */
+int fsl_decode_prefill(void *state, size_t state_bytes, int32_t seq, const void *k_prefix, const void *v_prefix,
+                       int64_t prefix_len, const fsl_params *p, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Advance every sequence by one token. q, k, v: device [n_seq][H][d] (dtype),
+ * the new token of each sequence; out: device [n_seq][H][d] (out_dtype), the
+ * attention output at that position. sel_out (nullable): device
+ * [n_seq][H][K] int32, the cells read, ascending, padded with -1. n_seq must
+ * equal the value the state was initialised with. */
+int fsl_decode_step(void *state, size_t state_bytes, const void *q, const void *k, const void *v, void *out,
+                    int32_t n_seq, const fsl_params *p, int32_t *sel_out, hipStream_t stream);
+
+/* Synchronous check of a state buffer's header against p and n_seq (copies
+ * the header to the host): FSL_OK, or FSL_E_STATE if the magic, version or
+ * any parameter differs. The only entry point that waits for the device. */
+int fsl_decode_validate(const void *state, size_t state_bytes, const fsl_params *p, int32_t n_seq);
+
 #ifdef __cplusplus
 }
 #endif

@@ -87,6 +87,50 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FSL_OK : FSL_E_HIP; }
 
+constexpr int32_t kDecodeMaxW = 65536;  // the decode RoPE table has w rows
+
+int check_decode(const fsl_params *p) {
+    if (!p) return FSL_E_INVAL;
+    fsl_params q = *p;
+    q.N = 1;
+    int rc = check(&q);
+    if (rc != FSL_OK) return rc;
+    if (p->w > kDecodeMaxW) return FSL_E_UNSUPPORTED;
+    return FSL_OK;
+}
+
+size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+
+DecodeLayout dlayout(const fsl_params *p) {
+    DecodeLayout L;
+    const size_t e = p->dtype == FSL_BF16 ? 2 : 4;
+    L.R = p->w + p->B + p->s;
+    L.PW = p->P + p->W;
+    L.off_rope = 256;
+    L.off_rec = (int64_t)align_up(256 + (size_t)p->w * (p->d / 2) * sizeof(float2));
+    size_t o = 16;  // int64 t, int64 block
+    L.o_cell = (int64_t)o; o = align16(o + 4 * (size_t)L.PW);
+    L.o_a = (int64_t)o; o = align16(o + 4 * (size_t)L.PW);
+    L.o_kbar = (int64_t)o; o = align16(o + 4 * (size_t)L.PW * p->d);
+    L.o_sk = (int64_t)o; o = align16(o + e * (size_t)L.PW * p->s * p->d);
+    L.o_sv = (int64_t)o; o = align16(o + e * (size_t)L.PW * p->s * p->d);
+    L.o_rk = (int64_t)o; o = align16(o + e * (size_t)L.R * p->d);
+    L.o_rv = (int64_t)o; o = align16(o + e * (size_t)L.R * p->d);
+    L.rec_bytes = (int64_t)align_up(o);
+    return L;
+}
+
+size_t decode_bytes(const fsl_params *p, int32_t n_seq) {
+    const DecodeLayout L = dlayout(p);
+    return (size_t)L.off_rec + (size_t)n_seq * p->H * (size_t)L.rec_bytes;
+}
+
+int32_t decode_capacity(const fsl_params *p, size_t state_bytes) {
+    const DecodeLayout L = dlayout(p);
+    if (state_bytes < (size_t)L.off_rec) return 0;
+    return (int32_t)((state_bytes - (size_t)L.off_rec) / ((size_t)p->H * (size_t)L.rec_bytes));
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,6 +241,82 @@ int fsl_attn_fwd_timed(const void *q, const void *k, const void *v, void *out, c
                        size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream) {
     if (!stage_events) return check(p) != FSL_OK ? check(p) : FSL_E_INVAL;
     return attn_fwd_impl(q, k, v, out, p, ws, ws_bytes, nullptr, nullptr, nullptr, stage_events, stream);
+}
+
+size_t fsl_decode_state_bytes(const fsl_params *p, int32_t n_seq) {
+    if (check_decode(p) != FSL_OK || n_seq < 1) return 0;
+    return decode_bytes(p, n_seq);
+}
+
+int fsl_decode_init(void *state, size_t state_bytes, int32_t n_seq, const fsl_params *p, hipStream_t stream) {
+    int rc = check_decode(p);
+    if (rc != FSL_OK) return rc;
+    if (!state || !aligned16(state) || n_seq < 1) return FSL_E_INVAL;
+    if (state_bytes < decode_bytes(p, n_seq)) return FSL_E_WORKSPACE;
+    fsl_params q = *p;
+    q.N = 1;
+    return hip_status(launch_decode_init(state, kparams(&q), dlayout(p), n_seq, stream));
+}
+
+size_t fsl_decode_prefill_workspace_bytes(const fsl_params *p, int64_t prefix_len) {
+    if (check_decode(p) != FSL_OK || prefix_len < 1 || prefix_len >= (int64_t(1) << 31) - p->B) return 0;
+    fsl_params q = *p;
+    q.N = prefix_len + p->B;
+    return layout(kparams(&q)).total;
+}
+
+int fsl_decode_prefill(void *state, size_t state_bytes, int32_t seq, const void *k_prefix, const void *v_prefix,
+                       int64_t prefix_len, const fsl_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_decode(p);
+    if (rc != FSL_OK) return rc;
+    if (!state || !k_prefix || !v_prefix || !ws || !aligned16(state) || !aligned16(k_prefix) ||
+        !aligned16(v_prefix) || !aligned16(ws))
+        return FSL_E_INVAL;
+    if (prefix_len < 1 || prefix_len >= (int64_t(1) << 31) - p->B || seq < 0) return FSL_E_INVAL;
+    if (seq >= decode_capacity(p, state_bytes)) return FSL_E_INVAL;
+    if (ws_bytes < fsl_decode_prefill_workspace_bytes(p, prefix_len)) return FSL_E_WORKSPACE;
+    fsl_params qa = *p;
+    qa.N = prefix_len + p->B;
+    const Work w = carve(ws, layout(kparams(&qa)));
+    fsl_params qs = *p;
+    qs.N = prefix_len;
+    KParams ks = kparams(&qs);            // statistics over the prefix's complete cells
+    KParams kpool = ks;
+    kpool.nblk = prefix_len / p->B + 1;   // pools up to the block holding position prefix_len
+    hipError_t e = launch_cell_stats(k_prefix, w.kbar, w.amax, ks, stream);
+    if (e == hipSuccess) e = launch_prune(w.amax, w.pool, w, kpool, stream);
+    if (e == hipSuccess) e = launch_decode_prefill(state, seq, k_prefix, v_prefix, prefix_len, w, kpool, dlayout(p), stream);
+    return hip_status(e);
+}
+
+int fsl_decode_step(void *state, size_t state_bytes, const void *q, const void *k, const void *v, void *out,
+                    int32_t n_seq, const fsl_params *p, int32_t *sel_out, hipStream_t stream) {
+    int rc = check_decode(p);
+    if (rc != FSL_OK) return rc;
+    if (!state || !q || !k || !v || !out || n_seq < 1) return FSL_E_INVAL;
+    if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (sel_out && !aligned4(sel_out)))
+        return FSL_E_INVAL;
+    if (n_seq > decode_capacity(p, state_bytes)) return FSL_E_WORKSPACE;
+    fsl_params qq = *p;
+    qq.N = 1;
+    return hip_status(launch_decode_step(state, q, k, v, out, sel_out, n_seq, kparams(&qq), dlayout(p), stream));
+}
+
+int fsl_decode_validate(const void *state, size_t state_bytes, const fsl_params *p, int32_t n_seq) {
+    int rc = check_decode(p);
+    if (rc != FSL_OK) return rc;
+    if (!state || n_seq < 1) return FSL_E_INVAL;
+    if (state_bytes < decode_bytes(p, n_seq)) return FSL_E_WORKSPACE;
+    DecodeHeader hd;
+    if (hipMemcpy(&hd, state, sizeof(hd), hipMemcpyDeviceToHost) != hipSuccess) return FSL_E_HIP;
+    const DecodeLayout L = dlayout(p);
+    if (hd.magic != kDecodeMagic || hd.version != kDecodeVersion) return FSL_E_STATE;
+    if (hd.H != p->H || hd.d != p->d || hd.w != p->w || hd.s != p->s || hd.P != p->P || hd.W != p->W ||
+        hd.K != p->K || hd.B != p->B || hd.dtype != p->dtype || hd.n_seq != n_seq || hd.R != L.R ||
+        hd.PW != L.PW || hd.rec_bytes != L.rec_bytes)
+        return FSL_E_STATE;
+    return FSL_OK;
 }
 
 }  // extern "C"

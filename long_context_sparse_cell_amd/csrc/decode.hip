@@ -1,0 +1,482 @@
+// Streaming decode with a bounded state (ai.info summary, "Why This Matters":
+// O(((P+W)s + w + B + s)d) per head; methodology: the pool of at most P+W
+// cells changes only at query-block boundaries; FreeSolo digest, core method
+// and steps 2-6 for what is computed per token).
+//
+// One workgroup per (sequence, head) and step. The state record of a
+// (sequence, head) holds the next position t, the block whose pool is loaded,
+// a ring of the last R = w + B + s tokens' raw k/v and P + W cell slots (cell
+// index, max key norm, mean key, raw k/v). A step:
+//  1. if t starts a new block, the cells that just became eligible get their
+//     statistics from the ring (fp64, same order as the forward), the cells
+//     leaving the recent set compete for the P high-norm places (keep the P
+//     best under (a desc, index asc); a loser's slot is freed), and every
+//     newly kept cell is copied once from the ring into a free slot;
+//  2. appends the new k/v to the ring;
+//  3. window attention over the ring (RoPE by the offset j - t, fp32);
+//  4. scores every occupied slot in fp64 exactly as the forward does, keeps
+//     the top K under (score desc, index asc);
+//  5. NoPE readout over the chosen cells' tokens, RMSNorm, mix, write.
+#include <climits>
+
+#include "fsl_internal.h"
+
+namespace fsl {
+
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecMaxPool = 128;
+constexpr int kDecMaxNew = 16;   // cells entering per block boundary: B/s <= 256/16
+
+__device__ __forceinline__ int64_t elig_nocap(const KParams &p, int64_t b) {
+    const int64_t x = b * p.B - p.w + 1;
+    return x <= 0 ? 0 : x / p.s;
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+
+__device__ float block_reduce(float v, float *scratch, bool is_max) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+        const float o = __shfl_xor(v, m);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    __syncthreads();
+    if (lane == 0) scratch[wave] = v;
+    __syncthreads();
+    float r = scratch[0];
+    for (int w2 = 1; w2 < kDecThreads / 64; ++w2) r = is_max ? fmaxf(r, scratch[w2]) : r + scratch[w2];
+    return r;
+}
+
+}  // namespace
+
+__global__ void decode_init_kernel(char *__restrict__ state, KParams p, DecodeLayout L, int n_seq, int dtype) {
+    const int rec_id = blockIdx.x;
+    if (rec_id == 0 && threadIdx.x == 0) {
+        DecodeHeader *hd = reinterpret_cast<DecodeHeader *>(state);
+        hd->magic = kDecodeMagic;
+        hd->version = kDecodeVersion;
+        hd->H = p.H; hd->d = p.d; hd->w = p.w; hd->s = p.s; hd->P = p.P; hd->W = p.W; hd->K = p.K; hd->B = p.B;
+        hd->dtype = dtype; hd->n_seq = n_seq; hd->R = L.R; hd->PW = L.PW;
+        hd->rec_bytes = L.rec_bytes;
+    }
+    // RoPE rows for offsets j - t in [-(w-1), 0]: row r <-> offset r - (w-1)
+    const int half = p.d / 2;
+    for (int64_t e = (int64_t)rec_id * blockDim.x + threadIdx.x; e < (int64_t)p.w * half;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int row = (int)(e / half), m = (int)(e % half);
+        const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)p.d);
+        const double ang = (double)(row - (p.w - 1)) * theta;
+        reinterpret_cast<float2 *>(state + L.off_rope)[e] = make_float2((float)cos(ang), (float)sin(ang));
+    }
+    char *rec = state + L.off_rec + (int64_t)rec_id * L.rec_bytes;
+    if (threadIdx.x == 0) {
+        reinterpret_cast<int64_t *>(rec)[0] = 0;  // t
+        reinterpret_cast<int64_t *>(rec)[1] = 0;  // block whose pool is loaded
+    }
+    int32_t *cell = reinterpret_cast<int32_t *>(rec + L.o_cell);
+    for (int i = threadIdx.x; i < L.PW; i += blockDim.x) cell[i] = -1;
+}
+
+template <typename T, int D>
+__global__ void decode_prefill_kernel(char *__restrict__ state, int seq, const T *__restrict__ kp,
+                                      const T *__restrict__ vp, int64_t Lp, const float *__restrict__ kbar,
+                                      const float *__restrict__ amax, const int32_t *__restrict__ pool, KParams p,
+                                      DecodeLayout L) {
+    const int h = blockIdx.x;
+    char *rec = state + L.off_rec + ((int64_t)seq * p.H + h) * L.rec_bytes;
+    const int64_t b = Lp / p.B;
+    const int64_t nb = elig_nocap(p, b);
+    const int npool = (int)min((int64_t)L.PW, nb);
+    int32_t *cell = reinterpret_cast<int32_t *>(rec + L.o_cell);
+    float *sa = reinterpret_cast<float *>(rec + L.o_a);
+    float *skb = reinterpret_cast<float *>(rec + L.o_kbar);
+    T *sk = reinterpret_cast<T *>(rec + L.o_sk);
+    T *sv = reinterpret_cast<T *>(rec + L.o_sv);
+    T *rk = reinterpret_cast<T *>(rec + L.o_rk);
+    T *rv = reinterpret_cast<T *>(rec + L.o_rv);
+    const int32_t *bp = pool + ((int64_t)h * p.nblk + b) * p.PW;
+    const T *kh = kp + (int64_t)h * Lp * D;
+    const T *vh = vp + (int64_t)h * Lp * D;
+    for (int i = threadIdx.x; i < L.PW; i += blockDim.x) {
+        const int c = i < npool ? bp[i] : -1;
+        cell[i] = c;
+        if (c >= 0) sa[i] = amax[(int64_t)h * p.C + c];
+    }
+    for (int64_t e = threadIdx.x; e < (int64_t)npool * D; e += blockDim.x) {
+        const int i = (int)(e / D), x = (int)(e % D);
+        skb[e] = kbar[((int64_t)h * p.C + bp[i]) * D + x];
+    }
+    for (int64_t e = threadIdx.x; e < (int64_t)npool * p.s * D; e += blockDim.x) {
+        const int64_t i = e / ((int64_t)p.s * D), rem = e % ((int64_t)p.s * D);
+        const int64_t src = (int64_t)bp[i] * p.s * D + rem;
+        sk[e] = kh[src];
+        sv[e] = vh[src];
+    }
+    const int64_t first = nb * p.s;
+    for (int64_t e = threadIdx.x; e < (Lp - first) * D; e += blockDim.x) {
+        const int64_t pos = first + e / D, x = e % D;
+        const int64_t slot = pos % L.R;
+        rk[slot * D + x] = kh[pos * D + x];
+        rv[slot * D + x] = vh[pos * D + x];
+    }
+    if (threadIdx.x == 0) {
+        reinterpret_cast<int64_t *>(rec)[0] = Lp;
+        reinterpret_cast<int64_t *>(rec)[1] = b;
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restrict__ state, const T *__restrict__ qn,
+                                                                  const T *__restrict__ kn, const T *__restrict__ vn,
+                                                                  void *__restrict__ out, int32_t *__restrict__ sel_out,
+                                                                  KParams p, DecodeLayout L) {
+    __shared__ float s_q[D];
+    __shared__ int s_cell[kDecMaxPool];
+    __shared__ float s_a[kDecMaxPool];
+    __shared__ double s_score[kDecMaxPool];
+    __shared__ int s_rank[kDecMaxPool];
+    __shared__ int s_sel[8];
+    __shared__ int s_selslot[8];
+    __shared__ float s_p[kDecThreads];
+    __shared__ float s_red[kDecThreads / 64];
+    __shared__ float s_o[kDecThreads];
+    __shared__ double s_ss[kDecMaxNew * 64];
+    __shared__ float s_newa[kDecMaxNew];
+    __shared__ int s_load_cell[kDecMaxNew], s_load_slot[kDecMaxNew], s_nload;
+
+    const int rid = blockIdx.x;  // seq * H + h
+    const int h = rid % p.H;
+    const int tid = threadIdx.x;
+    char *rec = state + L.off_rec + (int64_t)rid * L.rec_bytes;
+    int64_t *hdr = reinterpret_cast<int64_t *>(rec);
+    int32_t *cell = reinterpret_cast<int32_t *>(rec + L.o_cell);
+    float *sa = reinterpret_cast<float *>(rec + L.o_a);
+    float *skb = reinterpret_cast<float *>(rec + L.o_kbar);
+    T *sk = reinterpret_cast<T *>(rec + L.o_sk);
+    T *sv = reinterpret_cast<T *>(rec + L.o_sv);
+    T *rk = reinterpret_cast<T *>(rec + L.o_rk);
+    T *rv = reinterpret_cast<T *>(rec + L.o_rv);
+    const float2 *rope = reinterpret_cast<const float2 *>(state + L.off_rope);
+    const int s = p.s, PW = L.PW, R = L.R;
+
+    const int64_t t = hdr[0];
+    const int64_t blk = hdr[1];
+    const int64_t b = t / p.B;
+    for (int i = tid; i < PW; i += kDecThreads) {
+        s_cell[i] = cell[i];
+        s_a[i] = sa[i];
+    }
+    if (tid < D) s_q[tid] = to_f32<T>(qn[(int64_t)rid * D + tid]);
+    __syncthreads();
+
+    // ---- 1. block boundary: new eligible cells, recent -> high-norm competition
+    const int64_t n_old = elig_nocap(p, blk), n_new = elig_nocap(p, b);
+    if (b != blk && n_new > n_old) {
+        const int nnew = (int)(n_new - n_old);  // <= B/s <= kDecMaxNew
+        // max key norm of the new cells from the ring (fp64 fma chain in coordinate order)
+        for (int r = tid; r < nnew * s; r += kDecThreads) {
+            const int cn = r / s, j = r % s;
+            const int64_t pos = (n_old + cn) * s + j;
+            double acc = 0.0;
+            for (int x = 0; x < D; ++x) {
+                const double e = (double)to_f32<T>(rk[(pos % R) * D + x]);
+                acc = __fma_rn(e, e, acc);
+            }
+            s_ss[r] = acc;
+        }
+        __syncthreads();
+        if (tid < nnew) {
+            double best = 0.0;
+            for (int j = 0; j < s; ++j) {
+                const double v = s_ss[tid * s + j];
+                if (v > best) best = v;
+            }
+            s_newa[tid] = (float)__dsqrt_rn(best);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const int64_t m_old = n_old > p.W ? n_old - p.W : 0;
+            const int64_t m_new = n_new > p.W ? n_new - p.W : 0;
+            int top = 0;
+            for (int i = 0; i < PW; ++i) top += (s_cell[i] >= 0 && s_cell[i] < m_old) ? 1 : 0;
+            int nload = 0;
+            auto free_slot = [&]() {
+                for (int i = 0; i < PW; ++i)
+                    if (s_cell[i] < 0) return i;
+                return -1;
+            };
+            for (int64_t c = m_old; c < m_new; ++c) {
+                int sc = -1;
+                float ac;
+                if (c < n_old) {
+                    for (int i = 0; i < PW; ++i)
+                        if (s_cell[i] == c) sc = i;
+                    if (sc < 0) continue;  // cannot happen: every recent cell holds a slot
+                    ac = s_a[sc];
+                } else {
+                    ac = s_newa[c - n_old];
+                }
+                bool keep = false;
+                if (p.P > 0) {
+                    if (top < p.P) {
+                        keep = true;
+                    } else {
+                        // the high-norm set is every occupied cell below c (older ones kept earlier);
+                        // find its worst member: smallest a, then largest index
+                        int wsl = -1;
+                        for (int i = 0; i < PW; ++i) {
+                            if (s_cell[i] < 0 || s_cell[i] >= c) continue;
+                            if (wsl < 0 || better(s_a[wsl], s_cell[wsl], s_a[i], s_cell[i])) wsl = i;
+                        }
+                        if (wsl >= 0 && better(ac, (int)c, s_a[wsl], s_cell[wsl])) {
+                            s_cell[wsl] = -1;
+                            --top;
+                            keep = true;
+                        }
+                    }
+                }
+                if (keep) {
+                    if (sc < 0) {
+                        sc = free_slot();
+                        if (sc < 0) continue;  // cannot happen: at most P + W cells are ever held
+                        s_cell[sc] = (int)c;
+                        s_a[sc] = ac;
+                        s_load_cell[nload] = (int)c;
+                        s_load_slot[nload] = sc;
+                        ++nload;
+                    }
+                    ++top;
+                } else if (sc >= 0) {
+                    s_cell[sc] = -1;
+                }
+            }
+            for (int64_t c = (n_old > m_new ? n_old : m_new); c < n_new; ++c) {
+                const int sc = free_slot();
+                if (sc < 0) break;  // cannot happen: at most P + W cells are ever held
+                s_cell[sc] = (int)c;
+                s_a[sc] = s_newa[c - n_old];
+                s_load_cell[nload] = (int)c;
+                s_load_slot[nload] = sc;
+                ++nload;
+            }
+            s_nload = nload;
+        }
+        __syncthreads();
+        const int nload = s_nload;
+        for (int e = tid; e < nload * s * D; e += kDecThreads) {
+            const int li = e / (s * D), rem = e % (s * D);
+            const int64_t pos = (int64_t)s_load_cell[li] * s + rem / D;
+            const int64_t dst = ((int64_t)s_load_slot[li] * s) * D + rem;
+            sk[dst] = rk[(pos % R) * D + rem % D];
+            sv[dst] = rv[(pos % R) * D + rem % D];
+        }
+        for (int e = tid; e < nload * D; e += kDecThreads) {
+            const int li = e / D, x = e % D;
+            const int64_t c = s_load_cell[li];
+            double acc = 0.0;
+            for (int j = 0; j < s; ++j) acc += (double)to_f32<T>(rk[((c * s + j) % R) * D + x]);
+            skb[(int64_t)s_load_slot[li] * D + x] = (float)(acc / (double)s);
+        }
+        for (int i = tid; i < PW; i += kDecThreads) {
+            cell[i] = s_cell[i];
+            sa[i] = s_a[i];
+        }
+        __syncthreads();
+    }
+
+    // ---- 2. append the new token
+    const int64_t tslot = t % R;
+    if (tid < D) {
+        rk[tslot * D + tid] = kn[(int64_t)rid * D + tid];
+        rv[tslot * D + tid] = vn[(int64_t)rid * D + tid];
+    }
+    __syncthreads();
+
+    const float sl2 = p.scale * 1.4426950408889634f;
+    constexpr int PARTS = kDecThreads / D;  // threads per coordinate in the weighted sums
+    const int x_own = tid % D, part = tid / D;
+
+    // ---- 3. window over keys [max(0, t-w+1), t], RoPE by offset j - t, online softmax in chunks
+    float m_run = -INFINITY, l_run = 0.0f, o_acc = 0.0f;
+    const int64_t j_lo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
+    for (int64_t c0 = j_lo; c0 <= t; c0 += kDecThreads) {
+        const int64_t j = c0 + tid;
+        float sc = -INFINITY;
+        if (j <= t) {
+            const T *kr = rk + (j % R) * D;
+            const float2 *tr = rope + (j - t + p.w - 1) * (D / 2);
+            float dot = 0.0f;
+            for (int m = 0; m < D / 2; ++m) {
+                const float a = to_f32<T>(kr[m]), bb = to_f32<T>(kr[m + D / 2]);
+                const float2 cs = tr[m];
+                dot += s_q[m] * (a * cs.x - bb * cs.y) + s_q[m + D / 2] * (bb * cs.x + a * cs.y);
+            }
+            sc = dot * sl2;
+        }
+        const float cmax = block_reduce(sc, s_red, true);
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = exp2f(m_run - m_new);
+        const float pj = j <= t ? exp2f(sc - m_new) : 0.0f;
+        s_p[tid] = pj;
+        const float psum = block_reduce(pj, s_red, false);
+        l_run = l_run * alpha + psum;
+        o_acc *= alpha;
+        __syncthreads();
+        const int nk = (int)((t - c0 + 1) < kDecThreads ? (t - c0 + 1) : kDecThreads);
+        for (int u = part; u < nk; u += PARTS) o_acc += s_p[u] * to_f32<T>(rv[((c0 + u) % R) * D + x_own]);
+        m_run = m_new;
+        __syncthreads();
+    }
+    s_o[tid] = o_acc;
+    __syncthreads();
+    float o_win = 0.0f;
+    if (tid < D) {
+        for (int u = 0; u < PARTS; ++u) o_win += s_o[u * D + tid];
+        o_win /= l_run;
+    }
+    __syncthreads();
+
+    // ---- 4. exact fp64 cell scores and top-K over the occupied slots
+    const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+    for (int i = tid; i < PW; i += kDecThreads) {
+        double scv = -INFINITY;
+        const int c = s_cell[i];
+        if (c >= 0) {
+            double content = 0.0;
+            for (int x = 0; x < D; ++x) content = __fma_rn((double)s_q[x], (double)skb[(int64_t)i * D + x], content);
+            const double arg = __ddiv_rn(__dmul_rn(sig, (double)(t - (int64_t)c * s)), 2.0 * (double)s);
+            const double gg = arg >= 6.0 ? 1.0 : erf(arg);
+            const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[i]), gg);
+            scv = __fma_rn(rho, content, bias);
+        }
+        s_score[i] = scv;
+    }
+    if (tid < 8) { s_sel[tid] = INT_MAX; s_selslot[tid] = -1; }
+    __syncthreads();
+    for (int i = tid; i < PW; i += kDecThreads) {
+        const int c = s_cell[i];
+        int rank = INT_MAX;
+        if (c >= 0) {
+            rank = 0;
+            for (int o2 = 0; o2 < PW; ++o2) {
+                const int c2 = s_cell[o2];
+                if (c2 >= 0 && o2 != i && better_d(s_score[o2], c2, s_score[i], c)) ++rank;
+            }
+        }
+        s_rank[i] = rank;
+    }
+    __syncthreads();
+    for (int i = tid; i < PW; i += kDecThreads) {
+        const int c = s_cell[i];
+        if (c < 0 || s_rank[i] >= p.K) continue;
+        int below = 0;  // position among the selected cells in ascending index order
+        for (int o2 = 0; o2 < PW; ++o2)
+            if (s_cell[o2] >= 0 && s_rank[o2] < p.K && s_cell[o2] < c) ++below;
+        s_sel[below] = c;
+        s_selslot[below] = i;
+    }
+    __syncthreads();
+    int nsel = 0;
+    for (int r = 0; r < p.K; ++r) nsel += s_selslot[r] >= 0 ? 1 : 0;
+    if (sel_out && tid < p.K) sel_out[(int64_t)rid * p.K + tid] = s_selslot[tid] >= 0 ? s_sel[tid] : -1;
+
+    // ---- 5. NoPE readout over the chosen cells' tokens, RMSNorm, mix
+    const int ntok = nsel * s;
+    float o_long = 0.0f;
+    if (ntok > 0) {
+        float m2 = -INFINITY, l2 = 0.0f, acc2 = 0.0f;
+        for (int c0 = 0; c0 < ntok; c0 += kDecThreads) {
+            const int u = c0 + tid;
+            float sc = -INFINITY;
+            if (u < ntok) {
+                const T *kr = sk + ((int64_t)s_selslot[u / s] * s + u % s) * D;
+                float dot = 0.0f;
+                for (int x = 0; x < D; ++x) dot += s_q[x] * to_f32<T>(kr[x]);
+                sc = dot * sl2;
+            }
+            const float cmax = block_reduce(sc, s_red, true);
+            const float mn = fmaxf(m2, cmax);
+            const float alpha = exp2f(m2 - mn);
+            const float pj = u < ntok ? exp2f(sc - mn) : 0.0f;
+            s_p[tid] = pj;
+            const float psum = block_reduce(pj, s_red, false);
+            l2 = l2 * alpha + psum;
+            acc2 *= alpha;
+            __syncthreads();
+            const int nk = ntok - c0 < kDecThreads ? ntok - c0 : kDecThreads;
+            for (int uu = part; uu < nk; uu += PARTS) {
+                const int tok = c0 + uu;
+                acc2 += s_p[uu] * to_f32<T>(sv[((int64_t)s_selslot[tok / s] * s + tok % s) * D + x_own]);
+            }
+            m2 = mn;
+            __syncthreads();
+        }
+        s_o[tid] = acc2;
+        __syncthreads();
+        if (tid < D) {
+            for (int u = 0; u < PARTS; ++u) o_long += s_o[u * D + tid];
+            o_long /= l2;
+        }
+    }
+    const float ms = block_reduce(tid < D ? o_long * o_long : 0.0f, s_red, false) / (float)D;
+    if (tid < D) {
+        const float val = o_win + p.gamma[h] * (o_long / sqrtf(ms + p.rms_eps));
+        if (p.out_dtype == FSL_BF16) reinterpret_cast<uint16_t *>(out)[(int64_t)rid * D + tid] = f32_to_bf16(val);
+        else reinterpret_cast<float *>(out)[(int64_t)rid * D + tid] = val;
+    }
+    if (tid == 0) {
+        hdr[0] = t + 1;
+        hdr[1] = b;
+    }
+}
+
+hipError_t launch_decode_init(void *state, const KParams &p, const DecodeLayout &L, int n_seq, hipStream_t st) {
+    hipLaunchKernelGGL(decode_init_kernel, dim3((unsigned)(n_seq * p.H)), dim3(256), 0, st, (char *)state, p, L, n_seq,
+                       p.dtype);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t prefill_t(void *state, int seq, const void *kp, const void *vp, int64_t Lp, const Work &w,
+                            const KParams &p, const DecodeLayout &L, hipStream_t st) {
+    hipLaunchKernelGGL((decode_prefill_kernel<T, D>), dim3((unsigned)p.H), dim3(256), 0, st, (char *)state, seq,
+                       (const T *)kp, (const T *)vp, Lp, w.kbar, w.amax, w.pool, p, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_prefill(void *state, int seq, const void *kp, const void *vp, int64_t Lp, const Work &w,
+                                 const KParams &p, const DecodeLayout &L, hipStream_t st) {
+    if (p.dtype == FSL_BF16)
+        return p.d == 64 ? prefill_t<uint16_t, 64>(state, seq, kp, vp, Lp, w, p, L, st)
+                         : prefill_t<uint16_t, 128>(state, seq, kp, vp, Lp, w, p, L, st);
+    return p.d == 64 ? prefill_t<float, 64>(state, seq, kp, vp, Lp, w, p, L, st)
+                     : prefill_t<float, 128>(state, seq, kp, vp, Lp, w, p, L, st);
+}
+
+template <typename T, int D>
+static hipError_t step_t(void *state, const void *q, const void *k, const void *v, void *out, int32_t *sel_out,
+                         int n_seq, const KParams &p, const DecodeLayout &L, hipStream_t st) {
+    hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3((unsigned)(n_seq * p.H)), dim3(kDecThreads), 0, st,
+                       (char *)state, (const T *)q, (const T *)k, (const T *)v, out, sel_out, p, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_step(void *state, const void *q, const void *k, const void *v, void *out, int32_t *sel_out,
+                              int n_seq, const KParams &p, const DecodeLayout &L, hipStream_t st) {
+    if (p.dtype == FSL_BF16)
+        return p.d == 64 ? step_t<uint16_t, 64>(state, q, k, v, out, sel_out, n_seq, p, L, st)
+                         : step_t<uint16_t, 128>(state, q, k, v, out, sel_out, n_seq, p, L, st);
+    return p.d == 64 ? step_t<float, 64>(state, q, k, v, out, sel_out, n_seq, p, L, st)
+                     : step_t<float, 128>(state, q, k, v, out, sel_out, n_seq, p, L, st);
+}
+
+}  // namespace fsl

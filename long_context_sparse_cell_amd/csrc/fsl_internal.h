@@ -131,6 +131,29 @@ __device__ __forceinline__ void wave_merge_top(float &a, int &idx, float ba, int
 }
 
 // ---------------------------------------------------------------------------
+// decode state: a 256-byte header, a RoPE table for offsets [-(w-1), 0], then
+// one record per (sequence, head)
+
+constexpr uint32_t kDecodeMagic = 0x44534C46u;  // "FLSD"
+constexpr uint32_t kDecodeVersion = 1;
+
+struct DecodeHeader {
+    uint32_t magic, version;
+    int32_t H, d, w, s, P, W, K, B, dtype, n_seq, R, PW;
+    int64_t rec_bytes;
+};
+
+struct DecodeLayout {
+    int32_t R;          // ring tokens, w + B + s
+    int32_t PW;         // cell slots, P + W
+    int64_t off_rope;   // float2 [w][d/2]
+    int64_t off_rec;    // first record
+    int64_t rec_bytes;  // bytes per (sequence, head) record
+    // offsets inside a record (after int64 t and int64 block)
+    int64_t o_cell, o_a, o_kbar, o_sk, o_sv, o_rk, o_rv;
+};
+
+// ---------------------------------------------------------------------------
 // launchers (one per kernel family); each returns hipGetLastError()
 
 hipError_t launch_cell_stats(const void *k, float *kbar, float *amax, const KParams &p, hipStream_t st);
@@ -149,5 +172,11 @@ hipError_t launch_readout_cells(const void *q, const void *k, const void *v, con
 hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const int32_t *sel,
                               const float *o_win, void *out, float *o_long_out, const KParams &p,
                               hipStream_t st);
+
+hipError_t launch_decode_init(void *state, const KParams &p, const DecodeLayout &L, int n_seq, hipStream_t st);
+hipError_t launch_decode_prefill(void *state, int seq, const void *kp, const void *vp, int64_t Lp, const Work &w,
+                                 const KParams &p, const DecodeLayout &L, hipStream_t st);
+hipError_t launch_decode_step(void *state, const void *q, const void *k, const void *v, void *out, int32_t *sel_out,
+                              int n_seq, const KParams &p, const DecodeLayout &L, hipStream_t st);
 
 }  // namespace fsl

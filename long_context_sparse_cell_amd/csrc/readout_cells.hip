@@ -45,6 +45,16 @@ union H8 {
     _Float16 f[8];
 };
 
+// x * 2^32 as a two's-complement integer, exactly (|x| < 2^30): the integer
+// part and the fraction are converted separately with 32-bit conversions
+__device__ __forceinline__ unsigned long long to_fixed(float x) {
+    const float fl = floorf(x);
+    const float fr = x - fl;  // exact, in [0, 1)
+    const uint32_t lo = (uint32_t)(fr * kFix);
+    const int32_t hi = (int32_t)fl;
+    return ((unsigned long long)(uint32_t)hi << 32) + lo;
+}
+
 __device__ __forceinline__ int pack_item(int pos, int start, int cnt) { return pos | (start << 8) | (cnt << 20); }
 
 // exclusive scan of n <= 128 ints in LDS by one wave; returns the total
@@ -67,7 +77,7 @@ __device__ int wave_excl_scan(int *a, int n) {
 
 }  // namespace
 
-template <int D>
+template <int D, int S>
 __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__restrict__ q,
                                                             const uint16_t *__restrict__ k,
                                                             const uint16_t *__restrict__ v,
@@ -94,7 +104,8 @@ __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__re
     const int nq = (int)min((int64_t)QW, p.N - q0);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, g = lane >> 4;
-    const int K = p.K, s = p.s;
+    const int K = p.K;
+    constexpr int s = S;
     const int npool = (int)min((int64_t)p.PW, eligible_cells(p, b));
     const float sl2 = p.scale * 1.4426950408889634f;
     const int64_t hN = (int64_t)h * p.N;
@@ -155,7 +166,8 @@ __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__re
     }
     __syncthreads();
     const int nitems = s_nitems;
-    const int NT = s / 16;  // 16-token tiles per cell
+    constexpr int NT = S / 16;        // 16-token tiles per cell
+    constexpr int KK = (NT + 1) / 2;  // 32-token MFMA k-steps of P V
 
     // ---- pass 1: per (query, slot) max of the scaled scores
     for (int it = wave; it < nitems; it += kWaves) {
@@ -192,7 +204,8 @@ __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__re
     }
     __syncthreads();
 
-    // ---- pass 2: probabilities, partial sums, P V into the fixed-point accumulators
+    // ---- pass 2: probabilities, partial sums, P V into the fixed-point accumulators.
+    // Every load of an item (q columns, K rows, V rows) is issued before its math.
     for (int it = wave; it < nitems; it += kWaves) {
         const int item = s_item[it];
         const int pos = item & 0xFF, start = (item >> 8) & 0xFFF, cnt = item >> 20;
@@ -200,29 +213,43 @@ __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__re
         const int code = s_list[start + (col < cnt ? col : 0)];
         const int ql = code >> 3;
         const float m = s_m[ql];
+        const int64_t cell0 = hN + (int64_t)c * s;
         const uint16_t *qrow = q + (hN + q0 + ql) * D;
         U16x8 bq[D / 32];
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(qrow + 32 * ks + 8 * g);
+        U16x8 ka[2 * KK][D / 32];
+#pragma unroll
+        for (int tt = 0; tt < 2 * KK; ++tt) {
+            const uint16_t *krow = k + (cell0 + min(16 * tt + col, s - 1)) * D;  // rows past the cell: P = 0
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) ka[tt][ks].u = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
+        }
+        // V rows for tokens 32kk + {4g..4g+3, 16+4g..16+4g+3} (clamped to the cell)
+        uint16_t vraw[KK][D / 16][8];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tk = 32 * kk + ((e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4));
+                const uint16_t *vp = v + (cell0 + min(tk, s - 1)) * D + col;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) vraw[kk][dt][e] = vp[16 * dt];
+            }
         floatx4 oacc[D / 16];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
         float lsum = 0.0f;
-        for (int kk = 0; kk < (NT + 1) / 2; ++kk) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
             H8 pa;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int tt = 2 * kk + half;
                 floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
-                {
-                    const uint16_t *krow = k + (hN + (int64_t)c * s + min(16 * tt + col, s - 1)) * D;
 #pragma unroll
-                    for (int ks = 0; ks < D / 32; ++ks) {
-                        U16x8 ka;
-                        ka.u = *reinterpret_cast<const uint4 *>(krow + 32 * ks + 8 * g);
-                        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, bq[ks].b, sacc, 0, 0, 0);
-                    }
-                }
+                for (int ks = 0; ks < D / 32; ++ks)
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][ks].b, bq[ks].b, sacc, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const _Float16 ph = tt < NT ? (_Float16)exp2f(sacc[e] * sl2 - m) : (_Float16)0.0f;
@@ -230,25 +257,11 @@ __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__re
                     lsum += (float)ph;
                 }
             }
-            // B operand: V[token][dim] for tokens 32kk + {4g..4g+3, 16+4g..16+4g+3}; rows past the
-            // cell (s = 16) are clamped to a valid row, their P is zero
-            const int64_t cell0 = hN + (int64_t)c * s;
-            int64_t vrow[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tk = 32 * kk + ((e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4));
-                vrow[e] = (cell0 + min(tk, s - 1)) * D + col;
-            }
-            uint16_t vraw[D / 16][8];
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vraw[dt][e] = v[vrow[e] + 16 * dt];
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
                 H8 vb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vb.f[e] = (_Float16)bf16_to_f32(vraw[dt][e]);
+                for (int e = 0; e < 8; ++e) vb.f[e] = (_Float16)bf16_to_f32(vraw[kk][dt][e]);
                 oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.v, vb.v, oacc[dt], 0, 0, 0);
             }
         }
@@ -262,10 +275,7 @@ __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__re
             if (slot < cnt) {
                 const int qd = s_list[start + slot] >> 3;
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) {
-                    const long long fx = (long long)(oacc[dt][e] * kFix);
-                    atomicAdd(&acc[qd * D + 16 * dt + col], (unsigned long long)fx);
-                }
+                for (int dt = 0; dt < D / 16; ++dt) atomicAdd(&acc[qd * D + 16 * dt + col], to_fixed(oacc[dt][e]));
             }
         }
     }
@@ -316,16 +326,24 @@ __global__ __launch_bounds__(512) void readout_cells_kernel(const uint16_t *__re
     }
 }
 
+template <int D, int S>
+static void launch_rc(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, const int32_t *sel,
+                      const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p, int QW) {
+    hipLaunchKernelGGL((readout_cells_kernel<D, S>), grid, dim3(kThreads), 0, st, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, sel, pool, o_win, out, o_long_out, p, QW);
+}
+
 hipError_t launch_readout_cells(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
                                 const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st) {
     const int QW = p.B <= kMaxQ ? p.B : p.B / 2;
     dim3 grid((unsigned)((p.N + QW - 1) / QW), (unsigned)p.H);
-    if (p.d == 64)
-        hipLaunchKernelGGL((readout_cells_kernel<64>), grid, dim3(kThreads), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, sel, pool, o_win, out, o_long_out, p, QW);
-    else
-        hipLaunchKernelGGL((readout_cells_kernel<128>), grid, dim3(kThreads), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, sel, pool, o_win, out, o_long_out, p, QW);
+#define FSL_RC(DD, SS) launch_rc<DD, SS>(grid, st, q, k, v, sel, pool, o_win, out, o_long_out, p, QW)
+    if (p.d == 64) {
+        if (p.s == 16) FSL_RC(64, 16); else if (p.s == 32) FSL_RC(64, 32); else FSL_RC(64, 64);
+    } else {
+        if (p.s == 16) FSL_RC(128, 16); else if (p.s == 32) FSL_RC(128, 32); else FSL_RC(128, 64);
+    }
+#undef FSL_RC
     return hipGetLastError();
 }
 

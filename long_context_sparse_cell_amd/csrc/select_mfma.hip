@@ -14,10 +14,13 @@
 //        |content - content~| <= ||q|| ||kbar_c|| (2^-17 + (4d+8) 2^-24)
 //     (Cauchy-Schwarz bounds the absolute sum). The fp32 bias and the final
 //     fp32 additions get their own rounding terms; the total is doubled.
-//  2. Per query, theta = the K-th largest lower bound s~ - eps. A cell whose
-//     upper bound s~ + eps is below theta is beaten by K cells for sure; every
-//     other cell ("contender") is re-scored exactly in fp64 and the K best
-//     contenders under (score desc, index asc) are the exact top-K.
+//  2. Per query, each of its 4 lanes keeps its two largest lower bounds
+//     s~ - eps; theta is the K-th largest of those 8 values (they belong to 8
+//     distinct cells, so theta is at most the K-th largest lower bound over
+//     all cells). A cell whose upper bound s~ + eps is below theta is beaten
+//     by K cells for sure; every other cell ("contender") is re-scored exactly
+//     in fp64 and the K best contenders under (score desc, index asc) are the
+//     exact top-K.
 // One workgroup = up to 128 queries of one block, 8 waves x 16 queries.
 #include <climits>
 
@@ -129,10 +132,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
             bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qr) * D + 32 * ks + 8 * g);
         const float qn = s_qn[qr];
 
-        float lowv[kSelK];
-        int lowi[kSelK];
-#pragma unroll
-        for (int r = 0; r < kSelK; ++r) { lowv[r] = -INFINITY; lowi[r] = INT_MAX; }
+        float lb1 = -INFINITY, lb2 = -INFINITY;  // this lane's two largest lower bounds
         // approximate scores, 4 cells of each 16-cell tile per lane (cells 16*ct + 4*g + e)
         float sapx[kSelPool / 16][4];
         float seps[kSelPool / 16][4];
@@ -143,16 +143,16 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
-                U16x8s hi, lo;
+                bf16x8 hi, lo;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = rowc < npool ? s_kb[rowc * LD + 32 * ks + 8 * g + e] : 0.0f;
-                    const uint16_t hb = f32_to_bf16(x);
-                    hi.h[e] = hb;
-                    lo.h[e] = f32_to_bf16(x - bf16_to_f32(hb));
+                    const __bf16 hb = (__bf16)x;  // round to nearest even
+                    hi[e] = hb;
+                    lo[e] = (__bf16)(x - (float)hb);
                 }
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi.b, bq[ks].b, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.b, bq[ks].b, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq[ks].b, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq[ks].b, acc, 0, 0, 0);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -172,16 +172,29 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                     ev *= 2.0f;
                     sapx[ct][e] = sv;
                     seps[ct][e] = ev;
-                    list_insert<float>(lowv, lowi, sv - ev, pos, K);
+                    const float lb = sv - ev;
+                    lb2 = fmaxf(lb2, fminf(lb1, lb));
+                    lb1 = fmaxf(lb1, lb);
                 }
             }
         }
-        list_merge_xor<float>(lowv, lowi, K, 16);
-        list_merge_xor<float>(lowv, lowi, K, 32);
+        float lv8[8];
+        lv8[0] = lb1; lv8[1] = lb2;
+        lv8[2] = __shfl_xor(lb1, 16); lv8[3] = __shfl_xor(lb2, 16);
+        lv8[4] = __shfl_xor(lb1, 32); lv8[5] = __shfl_xor(lb2, 32);
+        lv8[6] = __shfl_xor(lb1, 48); lv8[7] = __shfl_xor(lb2, 48);
+        // sort descending (odd-even transposition, 8 rounds) and take the K-th
+#pragma unroll
+        for (int rnd = 0; rnd < 8; ++rnd)
+#pragma unroll
+            for (int a = rnd & 1; a + 1 < 8; a += 2) {
+                const float hi2 = fmaxf(lv8[a], lv8[a + 1]), lo2 = fminf(lv8[a], lv8[a + 1]);
+                lv8[a] = hi2; lv8[a + 1] = lo2;
+            }
         float theta = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < kSelK; ++r)
-            if (r == K - 1) theta = lowv[r];
+        for (int r = 0; r < 8; ++r)
+            if (r == K - 1) theta = lv8[r];
 
         // exact re-scoring of the contenders
         double exv[kSelK];

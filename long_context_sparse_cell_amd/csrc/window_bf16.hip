@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
             }
         }
         if (tid < VITEMS) {
-            const int jq = tid / (D / 8), c = tid % (D / 8);
+            const int jq = tid & 15, c = tid >> 4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t j = ks0 + 4 * jq + e;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
             *reinterpret_cast<uint4 *>(&ks_lds[buf][jl * KLD + HALF + 8 * c]) = rb.u;
         }
         if (tid < VITEMS) {
-            const int jq = tid / (D / 8), c = tid % (D / 8);
+            const int jq = tid & 15, c = tid >> 4;  // 16 lanes fill one V^T row segment: no bank conflicts
             float e4[4][8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -228,17 +228,23 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
                     sacc[kg][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[1][ks], sacc[kg][1], 0, 0, 0);
                 }
             }
+            // positions fit in int32 (N < 2^31, the window offset is bounded by w)
+            const int j0 = (int)ks0 + 4 * g;
+            const bool edge = !(ks0 + kKTile - 1 <= qw && ks0 > qw + 31 - p.w && ks0 >= 0);
+            P8 pb[2][2];
 #pragma unroll
             for (int qg = 0; qg < 2; ++qg) {
-                const int64_t i = qw + 16 * qg + col;
+                const int i = (int)qw + 16 * qg + col;
                 float mx = -INFINITY;
 #pragma unroll
                 for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int64_t j = ks0 + 16 * kg + 4 * g + r;
-                        const bool ok = j <= i && j > i - p.w && j >= 0;
-                        const float val = ok ? sacc[kg][qg][r] * sl2 : -INFINITY;
+                        float val = sacc[kg][qg][r] * sl2;
+                        if (edge) {
+                            const int j = j0 + 16 * kg + r;
+                            val = (j <= i && j > i - p.w && j >= 0) ? val : -INFINITY;
+                        }
                         sacc[kg][qg][r] = val;
                         mx = fmaxf(mx, val);
                     }
@@ -253,24 +259,18 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
                 for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float pv2 = (float)(_Float16)exp2f(sacc[kg][qg][r] - m_use);
-                        sacc[kg][qg][r] = pv2;
-                        lsum += pv2;
+                        const _Float16 ph = (_Float16)exp2f(sacc[kg][qg][r] - m_use);
+                        pb[kg >> 1][qg].f[4 * (kg & 1) + r] = ph;
+                        lsum += (float)ph;
                     }
                 l_part[qg] = l_part[qg] * alpha + lsum;
+                if (alpha != 1.0f) {
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) oacc[qg][dt] *= alpha;
+                    for (int dt = 0; dt < D / 16; ++dt) oacc[qg][dt] *= alpha;
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                P8 pb[2];
-#pragma unroll
-                for (int qg = 0; qg < 2; ++qg)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        pb[qg].f[r] = (_Float16)sacc[2 * kk][qg][r];
-                        pb[qg].f[4 + r] = (_Float16)sacc[2 * kk + 1][qg][r];
-                    }
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt) {
                     const uint16_t *vr = &vt[(16 * dt + col) * VLD + 32 * kk + 4 * g];
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
                     const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
                     P8 va;
                     va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[0].v, oacc[0][dt], 0, 0, 0);
-                    oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[1].v, oacc[1][dt], 0, 0, 0);
+                    oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][0].v, oacc[0][dt], 0, 0, 0);
+                    oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][1].v, oacc[1][dt], 0, 0, 0);
                 }
             }
         }

@@ -67,6 +67,17 @@ def lib():
         L.fsl_attn_fwd.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, vp, vp, vp]
         L.fsl_attn_fwd_timed.restype = i32
         L.fsl_attn_fwd_timed.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, vp]
+        i64 = ctypes.c_int64
+        L.fsl_decode_state_bytes.restype = sz; L.fsl_decode_state_bytes.argtypes = [pp, ctypes.c_int32]
+        L.fsl_decode_init.restype = i32; L.fsl_decode_init.argtypes = [vp, sz, ctypes.c_int32, pp, vp]
+        L.fsl_decode_prefill_workspace_bytes.restype = sz
+        L.fsl_decode_prefill_workspace_bytes.argtypes = [pp, i64]
+        L.fsl_decode_prefill.restype = i32
+        L.fsl_decode_prefill.argtypes = [vp, sz, ctypes.c_int32, vp, vp, i64, pp, vp, sz, vp]
+        L.fsl_decode_step.restype = i32
+        L.fsl_decode_step.argtypes = [vp, sz, vp, vp, vp, vp, ctypes.c_int32, pp, vp, vp]
+        L.fsl_decode_validate.restype = i32
+        L.fsl_decode_validate.argtypes = [vp, sz, pp, ctypes.c_int32]
         _lib = L
     return _lib
 
@@ -104,14 +115,16 @@ def dtype_code(t: torch.dtype) -> int:
 def make_params(N, H, d, dtype, sigma: torch.Tensor, lam: torch.Tensor, gamma: torch.Tensor, w=512, s=32,
                 P=64, W=8, K=4, B=128, out_dtype=None, scale=0.0, rho=1.0, rope_base=10000.0,
                 rms_eps=1e-6) -> Params:
-    """Parameter block; sigma/lam/gamma are device float32 tensors of shape [H] (kept alive by the caller)."""
+    """Parameter block; sigma/lam/gamma are device float32 tensors of shape [H], referenced by the block."""
     dt = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
     odt = dt if out_dtype is None else (dtype_code(out_dtype) if isinstance(out_dtype, torch.dtype) else int(out_dtype))
     for t in (sigma, lam, gamma):
         assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() >= H
-    return Params(N=N, H=H, d=d, w=w, s=s, P=P, W=W, K=K, B=B, dtype=dt, out_dtype=odt, scale=scale, rho=rho,
-                  rope_base=rope_base, rms_eps=rms_eps, sigma=sigma.data_ptr(), lam=lam.data_ptr(),
-                  gamma=gamma.data_ptr())
+    prm = Params(N=N, H=H, d=d, w=w, s=s, P=P, W=W, K=K, B=B, dtype=dt, out_dtype=odt, scale=scale, rho=rho,
+                 rope_base=rope_base, rms_eps=rms_eps, sigma=sigma.data_ptr(), lam=lam.data_ptr(),
+                 gamma=gamma.data_ptr())
+    prm._keep = (sigma, lam, gamma)  # the struct holds raw device pointers: keep the tensors alive with it
+    return prm
 
 
 def check_params(p: Params) -> int:
@@ -198,3 +211,46 @@ def workspace_views(ws: torch.Tensor, p: Params):
         pool=view(L.pool, p.H * nblk * (p.P + p.W), torch.int32, (p.H, nblk, p.P + p.W)),
         sel=view(L.sel, p.H * p.N * p.K, torch.int32, (p.H, p.N, p.K)),
     )
+
+
+# ---------------------------------------------------------------------------
+# streaming decode
+
+class DecodeState:
+    """A device state buffer for n_seq sequences (see fsl_decode_* in include/fsl.h)."""
+
+    def __init__(self, p: Params, n_seq: int, device="cuda", stream=None):
+        self.p = p
+        self.n_seq = n_seq
+        n = int(lib().fsl_decode_state_bytes(ctypes.byref(p), n_seq))
+        if n == 0:
+            _check(FSL_E_INVAL if n_seq < 1 else check_params(p), "fsl_decode_state_bytes")
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        _check(lib().fsl_decode_init(_ptr(self.buf), n, n_seq, ctypes.byref(p), _stream(stream)), "fsl_decode_init")
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+    def prefill(self, seq: int, k_prefix: torch.Tensor, v_prefix: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                stream=None):
+        L = k_prefix.shape[1]
+        need = int(lib().fsl_decode_prefill_workspace_bytes(ctypes.byref(self.p), L))
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.buf.device)
+        _check(lib().fsl_decode_prefill(_ptr(self.buf), self.nbytes, seq, _ptr(k_prefix), _ptr(v_prefix), L,
+                                        ctypes.byref(self.p), _ptr(ws), ws.numel(), _stream(stream)),
+               "fsl_decode_prefill")
+        return ws
+
+    def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
+             sel_out: Optional[torch.Tensor] = None, stream=None):
+        if out is None:
+            odt = torch.float32 if self.p.out_dtype == FSL_F32 else torch.bfloat16
+            out = torch.empty(q.shape, dtype=odt, device=q.device)
+        _check(lib().fsl_decode_step(_ptr(self.buf), self.nbytes, _ptr(q), _ptr(k), _ptr(v), _ptr(out), self.n_seq,
+                                     ctypes.byref(self.p), _ptr(sel_out), _stream(stream)), "fsl_decode_step")
+        return out
+
+    def validate(self) -> int:
+        return int(lib().fsl_decode_validate(_ptr(self.buf), self.nbytes, ctypes.byref(self.p), self.n_seq))

@@ -1,0 +1,159 @@
+"""Streaming decode through the C ABI, against the oracle and the forward.
+
+The output at position t must equal the forward at row t of the whole
+sequence (the oracle evaluates exactly that row): selected cells bit-exact,
+outputs within the dtype tolerance. Steps cross query-block boundaries so
+that cells enter the pool, leave the recent set and compete for the
+high-norm places.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fsl_testlib import check_out, device_tensor
+from long_context_sparse_cell_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_sparse_cell_amd import fsl
+    fsl.lib()
+
+
+def _case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def run_decode(sh, seqs, prefix, steps, sigma=None, check_every=1, save_at=None):
+    """Prefill each sequence, step through, return outputs/selections (host arrays)."""
+    from long_context_sparse_cell_amd import fsl
+    H, d = sh.H, sh.d
+    sig, lam, gam = synth.head_scalars(H)
+    if sigma is not None:
+        sig[:] = sigma
+    dev = "cuda"
+    sig_t, lam_t, gam_t = (torch.from_numpy(a).to(dev) for a in (sig, lam, gam))
+    tdt = torch.bfloat16 if sh.dtype == synth.BF16 else torch.float32
+    p = fsl.make_params(1, H, d, tdt, sig_t, lam_t, gam_t, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
+    st = fsl.DecodeState(p, len(seqs))
+    if prefix > 0:
+        for r, sq in enumerate(seqs):
+            st.prefill(r, device_tensor(np.ascontiguousarray(sq.k_prefix), sh.dtype),
+                       device_tensor(np.ascontiguousarray(sq.v_prefix), sh.dtype))
+    n = len(seqs)
+    outs = np.zeros((steps, n, H, d), np.float32)
+    sels = np.zeros((steps, n, H, sh.K), np.int32)
+    saved = None
+    sel_t = torch.empty((n, H, sh.K), dtype=torch.int32, device=dev)
+    for t in range(steps):
+        if save_at is not None and t == save_at:
+            saved = st.buf.clone()
+        q = device_tensor(np.stack([sq.q_steps[t] for sq in seqs]), sh.dtype)
+        k = device_tensor(np.stack([sq.k_steps[t] for sq in seqs]), sh.dtype)
+        v = device_tensor(np.stack([sq.v_steps[t] for sq in seqs]), sh.dtype)
+        out = st.step(q, k, v, sel_out=sel_t)
+        outs[t] = out.float().cpu().numpy()
+        sels[t] = sel_t.cpu().numpy()
+    torch.cuda.synchronize()
+    return dict(out=outs, sel=sels, sigma=sig, lam=lam, gamma=gam, state=st, saved=saved, params=p)
+
+
+def oracle_decode_rows(oracle, sh, seq, prefix, steps, sig, lam, gam, h):
+    q, k, v = synth.full_sequence(seq)
+    T = prefix + steps
+    p = oracle.head(N=T, d=sh.d, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B,
+                    scale=float(np.float32(1.0 / np.sqrt(sh.d))), sigma=float(sig[h]), lam=float(lam[h]),
+                    gamma=float(gam[h]))
+    return oracle.forward_head(q[h], k[h], v[h], p, rows=np.arange(prefix, T))
+
+
+DECODE_CASES = [
+    ("bf16_d64_prefix5000", dict(H=2, d=64, dtype=synth.BF16), 5000, 300, None),
+    ("bf16_d128_prefix4200", dict(H=2, d=128, dtype=synth.BF16), 4200, 200, None),
+    ("f32_d64_prefix3000_sigma005", dict(H=1, d=64, dtype=synth.F32), 3000, 260, 0.05),
+    ("bf16_d64_small_window_from_scratch", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=32, P=4, W=2, K=3), 0, 700,
+     None),
+    ("bf16_d64_w0_k8", dict(H=1, d=64, dtype=synth.BF16, w=100, s=32, B=64, P=16, W=0, K=8), 2500, 200, None),
+]
+
+
+@pytest.mark.parametrize("name,over,prefix,steps,sigma", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_matches_oracle_every_step(oracle, name, over, prefix, steps, sigma):
+    _case(name)
+    sh = synth.Shape(name, N=prefix + steps, seed=21, **over)
+    seqs = [synth.decode_sequence(sh, r, prefix=prefix, steps=steps) for r in range(2)]
+    res = run_decode(sh, seqs, prefix, steps, sigma=sigma)
+    for r, sq in enumerate(seqs):
+        for h in range(sh.H):
+            ref = oracle_decode_rows(oracle, sh, sq, prefix, steps, res["sigma"], res["lam"], res["gamma"], h)
+            np.testing.assert_array_equal(res["sel"][:, r, h], ref["sel"], err_msg=f"seq {r} head {h}")
+            mx, mean = check_out(res["out"][:, r, h], ref["out"], sh.dtype, f"decode seq {r} head {h}")
+            print(f"  seq {r} head {h}: out max err {mx:.3e} mean {mean:.3e}", flush=True)
+
+
+def test_decode_equals_forward_rows():
+    _case("decode_vs_forward")
+    from long_context_sparse_cell_amd import fsl
+    from fsl_testlib import GpuRun
+    sh = synth.Shape("dec_fwd", H=2, N=4500 + 200, d=64, dtype=synth.BF16, seed=22)
+    seq = synth.decode_sequence(sh, 0, prefix=4500, steps=200)
+    res = run_decode(sh, [seq], 4500, 200)
+    q, k, v = synth.full_sequence(seq)
+    inp = synth.Inputs(sh, q, k, v, res["sigma"], res["lam"], res["gamma"])
+    run = GpuRun(inp)
+    fwd_out = run.out.float().cpu().numpy()[:, 4500:]
+    fwd_sel = run.sel.cpu().numpy()[:, 4500:]
+    for h in range(sh.H):
+        np.testing.assert_array_equal(res["sel"][:, 0, h], fwd_sel[h])
+        # both sides round to bf16 once; their fp32 window arithmetic differs
+        assert np.abs(res["out"][:, 0, h] - fwd_out[h]).max() <= 2.5e-2
+
+
+def test_decode_state_save_restore_is_bit_identical():
+    _case("save_restore")
+    from long_context_sparse_cell_amd import fsl
+    sh = synth.Shape("dec_sr", H=2, N=3000 + 200, d=64, dtype=synth.BF16, seed=23)
+    seqs = [synth.decode_sequence(sh, r, prefix=3000, steps=200) for r in range(2)]
+    res = run_decode(sh, seqs, 3000, 200, save_at=100)
+    st = res["state"]
+    st.buf.copy_(res["saved"])  # restore the state saved before step 100
+    sel_t = torch.empty((2, sh.H, sh.K), dtype=torch.int32, device="cuda")
+    for t in range(100, 200):
+        q = device_tensor(np.stack([sq.q_steps[t] for sq in seqs]), sh.dtype)
+        k = device_tensor(np.stack([sq.k_steps[t] for sq in seqs]), sh.dtype)
+        v = device_tensor(np.stack([sq.v_steps[t] for sq in seqs]), sh.dtype)
+        out = st.step(q, k, v, sel_out=sel_t)
+        np.testing.assert_array_equal(out.float().cpu().numpy(), res["out"][t])
+        np.testing.assert_array_equal(sel_t.cpu().numpy(), res["sel"][t])
+
+
+def test_decode_validate_header():
+    _case("validate")
+    from long_context_sparse_cell_amd import fsl
+    sh = synth.Shape("dec_val", H=2, N=10, d=64, dtype=synth.BF16, seed=24)
+    sig, lam, gam = (torch.from_numpy(a).cuda() for a in synth.head_scalars(2))
+    p = fsl.make_params(1, 2, 64, torch.bfloat16, sig, lam, gam)
+    st = fsl.DecodeState(p, 3)
+    torch.cuda.synchronize()
+    assert st.validate() == 0
+    p2 = fsl.make_params(1, 2, 64, torch.bfloat16, sig, lam, gam, K=3)
+    import ctypes
+    assert int(fsl.lib().fsl_decode_validate(st.buf.data_ptr(), st.nbytes, ctypes.byref(p2), 3)) == fsl.FSL_E_STATE
+    st.buf[0] ^= 0xFF  # corrupt the magic
+    assert st.validate() == fsl.FSL_E_STATE
+
+
+def test_decode_workload_shape_sample(oracle):
+    """The decode workload's shape (prefix 131072, H=16, d=64, 256 steps), one sequence."""
+    sh = synth.CONFIGS["c5"]
+    _case(f"decode workload sample {sh.name}")
+    seq = synth.decode_sequence(sh, 0)
+    res = run_decode(sh, [seq], sh.prefix, sh.steps)
+    for h in range(sh.H):
+        ref = oracle_decode_rows(oracle, sh, seq, sh.prefix, sh.steps, res["sigma"], res["lam"], res["gamma"], h)
+        np.testing.assert_array_equal(res["sel"][:, 0, h], ref["sel"], err_msg=f"head {h}")
+        check_out(res["out"][:, 0, h], ref["out"], sh.dtype, f"decode head {h}")

@@ -107,3 +107,37 @@ def test_null_pointers_and_small_workspace_fail_before_launch(fsl):
     p2.gamma = None
     assert L.fsl_attn_fwd(a, a, a, a, ctypes.byref(p2), a, n, None, None, None, None) == -1
     assert L.fsl_cell_stats(a, None, a, ctypes.byref(p), None) == -1
+
+
+def test_decode_state_is_bounded_and_independent_of_prefix(fsl):
+    """State per (sequence, head): ring of w+B+s tokens + P+W cell slots, whatever the prefix
+    length (ai.info summary: bounded state O(((P+W)s + w + B + s)d))."""
+    L = fsl.lib()
+    sizes = []
+    for N in (1, 4096, 131072, 1 << 30):
+        p = params(fsl, N=N, H=16, d=64, dtype=1, out_dtype=1)
+        sizes.append(int(L.fsl_decode_state_bytes(ctypes.byref(p), 64)))
+    assert len(set(sizes)) == 1 and sizes[0] > 0
+    per_head = sizes[0] / (64 * 16)
+    tokens = (64 + 8) * 32 + 512 + 128 + 32  # (P+W)s + w + B + s
+    kv_bytes = tokens * 64 * 2 * 2           # raw k and v, bf16
+    assert kv_bytes <= per_head <= kv_bytes * 1.1  # plus cell means/norms and alignment
+    p = params(fsl, P=-1)
+    assert int(L.fsl_decode_state_bytes(ctypes.byref(p), 4)) == 0
+    p = params(fsl)
+    assert int(L.fsl_decode_state_bytes(ctypes.byref(p), 0)) == 0
+
+
+def test_decode_entry_points_reject_bad_arguments(fsl):
+    L = fsl.lib()
+    p = params(fsl)
+    n = int(L.fsl_decode_state_bytes(ctypes.byref(p), 2))
+    a = ctypes.c_void_p(0x100000)
+    assert L.fsl_decode_init(a, n - 1, 2, ctypes.byref(p), None) == -3
+    assert L.fsl_decode_init(None, n, 2, ctypes.byref(p), None) == -1
+    assert L.fsl_decode_step(a, n, a, a, a, a, 3, ctypes.byref(p), None, None) == -3   # more sequences than the state holds
+    assert L.fsl_decode_step(a, n, a, ctypes.c_void_p(0x100002), a, a, 2, ctypes.byref(p), None, None) == -1
+    assert L.fsl_decode_prefill(a, n, 2, a, a, 100, ctypes.byref(p), a, 1 << 30, None) == -1  # seq out of range
+    assert L.fsl_decode_prefill(a, n, 0, a, a, 100, ctypes.byref(p), a, 16, None) == -3      # workspace too small
+    pw = params(fsl, w=70000)
+    assert int(L.fsl_decode_state_bytes(ctypes.byref(pw), 1)) == 0
