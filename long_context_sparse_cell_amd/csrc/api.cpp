@@ -221,7 +221,7 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
                                       : launch_window(q, k, v, w.rope, w.o_win, kp, stream));
     if (e == hipSuccess)
         e = mark(kp.dtype == FSL_BF16
-                     ? launch_readout_cells(q, k, v, w.sel, w.pool, w.o_win, out, o_long_out, kp, stream)
+                     ? launch_readout_flash(q, k, v, w.sel, w.pool, w.o_win, out, o_long_out, kp, stream)
                      : launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
     if (e == hipSuccess && sel_out)
         e = hipMemcpyAsync(sel_out, w.sel, (size_t)kp.H * kp.N * kp.K * sizeof(int32_t), hipMemcpyDeviceToDevice,

@@ -167,6 +167,8 @@ hipError_t launch_window(const void *q, const void *k, const void *v, const floa
                          const KParams &p, hipStream_t st);
 hipError_t launch_window_bf16(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
                               const KParams &p, hipStream_t st);
+hipError_t launch_readout_flash(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
+                                const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st);
 hipError_t launch_readout_cells(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
                                 const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st);
 hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const int32_t *sel,

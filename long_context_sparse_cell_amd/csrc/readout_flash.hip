@@ -1,0 +1,317 @@
+// Long-branch readout + mix for bf16 inputs as one flash-attention sweep over
+// the cells a block selected (FreeSolo digest, core method and step 6: NoPE
+// softmax over the raw tokens of the selected cells, RMSNorm, add to the local
+// branch with a per-head weight).
+//
+// A workgroup takes up to 128 queries of one block (8 waves x 16 queries, each
+// wave's queries held in registers as MFMA operands). Every query's cells come
+// from the block's pool, so the workgroup walks the pool cells that at least
+// one of its queries selected, in ascending cell order, staging each cell's
+// keys (bf16, row-major) and values (fp16, transposed) in double-buffered LDS:
+// each selected cell is read from memory once per block. For every cell, each
+// wave whose queries include a selector computes S^T = K_c Q^T (bf16 MFMA,
+// exact products), masks the queries that did not select the cell, and
+// updates a per-query online softmax and O^T = V^T P^T (fp16 MFMA) held in
+// registers; the lane that owns a query column owns its statistics, so no
+// cross-lane traffic is needed. A query's result depends only on its own
+// cells in ascending order, so the output is deterministic.
+#include "fsl_internal.h"
+
+namespace fsl {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRfThreads = 512;     // 8 waves
+constexpr int kRfWaves = kRfThreads / 64;
+constexpr int kRfMaxQ = 128;
+constexpr int kRfMaxPool = 128;
+constexpr int kRfChunk = 2;         // cells per LDS stage
+
+union R8 {
+    uint4 u;
+    bf16x8 b;
+    halfx8 h;
+    _Float16 f[8];
+    uint16_t s[8];
+};
+
+// two floats to a packed fp16 pair (one v_cvt_pkrtz_f16_f32)
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    union { decltype(__builtin_amdgcn_cvt_pkrtz(0.0f, 0.0f)) h; uint32_t u; } c;
+    c.h = __builtin_amdgcn_cvt_pkrtz(a, b);
+    return c.u;
+}
+
+}  // namespace
+
+template <int D, int S>
+__global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ pool, const float *__restrict__ o_win,
+    void *__restrict__ out, float *__restrict__ o_long_out, KParams p, int QW) {
+    constexpr int KLD = D + 8;      // K row stride (elements)
+    constexpr int VLD = S + 8;      // V^T row stride
+    constexpr int NT = S / 16;      // 16-token tiles per cell
+    constexpr int KK = (NT + 1) / 2;
+    constexpr int QS = D / 32;
+    constexpr int KITEMS = kRfChunk * S * D / 8;           // 16-byte K loads per chunk
+    constexpr int VITEMS = kRfChunk * (S / 4) * (D / 8);   // (4 tokens x 8 dims) V items per chunk
+    constexpr int KPT = (KITEMS + kRfThreads - 1) / kRfThreads;
+    __shared__ uint16_t s_k[2][kRfChunk][S * KLD];
+    __shared__ uint16_t s_vt[2][kRfChunk][D * VLD];
+    __shared__ int s_pool[kRfMaxPool];
+    __shared__ uint32_t s_mask[kRfMaxPool][4];
+    __shared__ int s_act[kRfMaxPool];
+    __shared__ int s_nact;
+
+    const int h = blockIdx.y;
+    const int64_t q0 = (int64_t)blockIdx.x * QW;
+    const int64_t b = q0 / p.B;
+    const int nq = (int)min((int64_t)QW, p.N - q0);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, g = lane >> 4;
+    const int K = p.K;
+    const int npool = (int)min((int64_t)p.PW, eligible_cells(p, b));
+    const int64_t hN = (int64_t)h * p.N;
+    const float sl2 = p.scale * 1.4426950408889634f;
+
+    // ---- which queries selected which pool cell
+    for (int t = tid; t < npool; t += kRfThreads) {
+        s_pool[t] = pool[((int64_t)h * p.nblk + b) * p.PW + t];
+        s_mask[t][0] = s_mask[t][1] = s_mask[t][2] = s_mask[t][3] = 0u;
+    }
+    __syncthreads();
+    for (int pr = tid; pr < nq * K; pr += kRfThreads) {
+        const int c = sel[(hN + q0) * K + pr];
+        if (c < 0) continue;
+        int lo = 0, hi = npool - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pool[mid] < c) lo = mid + 1; else hi = mid;
+        }
+        const int ql = pr / K;
+        atomicOr(&s_mask[lo][ql >> 5], 1u << (ql & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // compact the selected positions in pool (= ascending cell) order
+        int base = 0;
+        for (int t0 = 0; t0 < npool; t0 += 64) {
+            const int t = t0 + lane;
+            const bool on = t < npool && (s_mask[t][0] | s_mask[t][1] | s_mask[t][2] | s_mask[t][3]) != 0u;
+            const uint64_t bal = __ballot(on);
+            if (on) s_act[base + __popcll(bal & ((1ull << lane) - 1ull))] = t;
+            base += __popcll(bal);
+        }
+        if (lane == 0) s_nact = base;
+    }
+    __syncthreads();
+    const int nact = s_nact;
+    const int nchunk = (nact + kRfChunk - 1) / kRfChunk;
+
+    // ---- this wave's 16 queries as bf16 MFMA B operands
+    const int qwl = 16 * wave;  // first query (local) of this wave
+    const int qrow = min(qwl + col, max(nq - 1, 0));
+    R8 bq[QS];
+#pragma unroll
+    for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qrow) * D + 32 * ks + 8 * g);
+
+    // ---- staging: K rows (bf16 copy) and V^T (fp16) of kRfChunk cells
+    static_assert(KPT <= 4, "K staging uses at most four prefetch registers per thread");
+    uint4 rk0 = make_uint4(0u, 0u, 0u, 0u), rk1 = rk0, rk2 = rk0, rk3 = rk0;  // named, never an array
+    uint4 rv0 = rk0, rv1 = rk0, rv2 = rk0, rv3 = rk0;
+    // every thread loads (item indices are clamped, duplicates are harmless) so that the
+    // prefetch registers are written unconditionally and stay in registers
+    auto kload = [&](int ch, int u) __attribute__((always_inline)) -> uint4 {
+        const int it = min(tid + kRfThreads * u, KITEMS - 1);
+        const int ci = it / (S * D / 8), rem = it % (S * D / 8);
+        const int ai = min(ch * kRfChunk + ci, nact - 1);
+        const int64_t row = hN + (int64_t)s_pool[s_act[ai]] * S + rem / (D / 8);
+        return *reinterpret_cast<const uint4 *>(k + row * D + 8 * (rem % (D / 8)));
+    };
+    auto kstore = [&](int buf, int u, uint4 val) __attribute__((always_inline)) {
+        const int it = min(tid + kRfThreads * u, KITEMS - 1);  // clamped items store the same data twice
+        const int ci = it / (S * D / 8), rem = it % (S * D / 8);
+        *reinterpret_cast<uint4 *>(&s_k[buf][ci][(rem / (D / 8)) * KLD + 8 * (rem % (D / 8))]) = val;
+    };
+    auto fetch = [&](int ch) __attribute__((always_inline)) {
+        rk0 = kload(ch, 0);
+        if constexpr (KPT > 1) rk1 = kload(ch, 1);
+        if constexpr (KPT > 2) rk2 = kload(ch, 2);
+        if constexpr (KPT > 3) rk3 = kload(ch, 3);
+        const int it = min(tid, VITEMS - 1);
+        const int ci = it / ((S / 4) * (D / 8)), rem = it % ((S / 4) * (D / 8));
+        const int jq = rem % (S / 4), c8 = rem / (S / 4);
+        const int ai = min(ch * kRfChunk + ci, nact - 1);
+        const uint16_t *vp = v + (hN + (int64_t)s_pool[s_act[ai]] * S + 4 * jq) * D + 8 * c8;
+        rv0 = *reinterpret_cast<const uint4 *>(vp);
+        rv1 = *reinterpret_cast<const uint4 *>(vp + D);
+        rv2 = *reinterpret_cast<const uint4 *>(vp + 2 * D);
+        rv3 = *reinterpret_cast<const uint4 *>(vp + 3 * D);
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+        kstore(buf, 0, rk0);
+        if constexpr (KPT > 1) kstore(buf, 1, rk1);
+        if constexpr (KPT > 2) kstore(buf, 2, rk2);
+        if constexpr (KPT > 3) kstore(buf, 3, rk3);
+        const int it = min(tid, VITEMS - 1);
+        const int ci = it / ((S / 4) * (D / 8)), rem = it % ((S / 4) * (D / 8));
+        const int jq = rem % (S / 4), c8 = rem / (S / 4);
+        R8 e0, e1, e2, e3;
+        e0.u = rv0; e1.u = rv1; e2.u = rv2; e3.u = rv3;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            // bf16 -> fp16 is exact in fp16's normal range, so the rounding mode of the packed convert is moot
+            const uint32_t lo = pk_f16(bf16_to_f32(e0.s[r]), bf16_to_f32(e1.s[r]));
+            const uint32_t hi = pk_f16(bf16_to_f32(e2.s[r]), bf16_to_f32(e3.s[r]));
+            *reinterpret_cast<uint2 *>(&s_vt[buf][ci][(8 * c8 + r) * VLD + 4 * jq]) = make_uint2(lo, hi);
+        }
+    };
+
+    float m_run = -INFINITY, l_part = 0.0f;
+    floatx4 oacc[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (nchunk > 0) {
+        fetch(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        const int buf = ch & 1;
+        const bool more = ch + 1 < nchunk;
+        if (more) fetch(ch + 1);
+#pragma unroll
+        for (int ci = 0; ci < kRfChunk; ++ci) {
+            const int ai = ch * kRfChunk + ci;
+            if (ai >= nact) break;
+            const int pos = s_act[ai];
+            const uint32_t m16 = (s_mask[pos][qwl >> 5] >> (qwl & 31)) & 0xFFFFu;
+            if (m16 == 0u) continue;  // none of this wave's queries selected the cell
+            const bool mine = (m16 >> col) & 1u;
+            const uint16_t *kt = s_k[buf][ci];
+            const uint16_t *vt = s_vt[buf][ci];
+            floatx4 sacc[2 * KK];
+#pragma unroll
+            for (int tt = 0; tt < 2 * KK; ++tt) {
+                sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (tt < NT) {
+#pragma unroll
+                    for (int ks = 0; ks < QS; ++ks) {
+                        R8 ka;
+                        ka.u = *reinterpret_cast<const uint4 *>(&kt[(16 * tt + col) * KLD + 32 * ks + 8 * g]);
+                        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, bq[ks].b, sacc[tt], 0, 0, 0);
+                    }
+                }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sacc[tt][r] *= sl2;
+                    mx = fmaxf(mx, sacc[tt][r]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = mine ? fmaxf(m_run, mx) : m_run;
+            const float alpha = mine ? exp2f(m_run - m_new) : 1.0f;
+            R8 pb[KK];
+            float lsum = 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < 2 * KK; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const _Float16 ph = (mine && tt < NT) ? (_Float16)exp2f(sacc[tt][r] - m_new) : (_Float16)0.0f;
+                    pb[tt >> 1].f[4 * (tt & 1) + r] = ph;
+                    lsum += (float)ph;
+                }
+            m_run = m_new;
+            l_part = l_part * alpha + lsum;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) {
+                    const uint16_t *vr = &vt[(16 * dt + col) * VLD + 32 * kk + 4 * g];
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
+                    const uint2 hi = (32 * kk + 16 < S) ? *reinterpret_cast<const uint2 *>(vr + 16) : make_uint2(0u, 0u);
+                    R8 va;
+                    va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, pb[kk].h, oacc[dt], 0, 0, 0);
+                }
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- normalise, RMSNorm over d, mix, write (lane: query col, dims 16*dt + 4*g + r)
+    float l = l_part;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float ss = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        oacc[dt] *= inv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ss += oacc[dt][r] * oacc[dt][r];
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float rs = 1.0f / sqrtf(ss / (float)D + p.rms_eps);
+    const int ql = qwl + col;
+    if (ql < nq) {
+        const float gam = p.gamma[h];
+        const int64_t row = hN + q0 + ql;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const int c0 = 16 * dt + 4 * g;
+            const float4 ow = *reinterpret_cast<const float4 *>(o_win + row * D + c0);
+            const float o4[4] = {ow.x, ow.y, ow.z, ow.w};
+            float val[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) val[r] = o4[r] + gam * (oacc[dt][r] * rs);
+            if (p.out_dtype == FSL_BF16) {
+                const uint32_t w0 = (uint32_t)f32_to_bf16(val[0]) | ((uint32_t)f32_to_bf16(val[1]) << 16);
+                const uint32_t w1 = (uint32_t)f32_to_bf16(val[2]) | ((uint32_t)f32_to_bf16(val[3]) << 16);
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + row * D + c0) = make_uint2(w0, w1);
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + row * D + c0) =
+                    make_float4(val[0], val[1], val[2], val[3]);
+            }
+            if (o_long_out)
+                *reinterpret_cast<float4 *>(o_long_out + row * D + c0) =
+                    make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
+        }
+    }
+}
+
+template <int D, int S>
+static void launch_rf(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, const int32_t *sel,
+                      const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p, int QW) {
+    hipLaunchKernelGGL((readout_flash_kernel<D, S>), grid, dim3(kRfThreads), 0, st, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, sel, pool, o_win, out, o_long_out, p, QW);
+}
+
+hipError_t launch_readout_flash(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
+                                const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st) {
+    const int QW = p.B <= kRfMaxQ ? p.B : p.B / 2;
+    dim3 grid((unsigned)((p.N + QW - 1) / QW), (unsigned)p.H);
+#define FSL_RF(DD, SS) launch_rf<DD, SS>(grid, st, q, k, v, sel, pool, o_win, out, o_long_out, p, QW)
+    if (p.d == 64) {
+        if (p.s == 16) FSL_RF(64, 16); else if (p.s == 32) FSL_RF(64, 32); else FSL_RF(64, 64);
+    } else {
+        if (p.s == 16) FSL_RF(128, 16); else if (p.s == 32) FSL_RF(128, 32); else FSL_RF(128, 64);
+    }
+#undef FSL_RF
+    return hipGetLastError();
+}
+
+}  // namespace fsl

@@ -74,13 +74,15 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                                                           const float *__restrict__ amax,
                                                           const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
                                                           KParams p, int QW) {
-    constexpr int LD = D + 1;
-    __shared__ float s_kb[kSelPool * LD];
-    __shared__ float s_q[kSelQ * LD];
+    constexpr int LD = D + 1;       // fp32 kbar row stride (odd: conflict-free row reads)
+    constexpr int QLD = D + 2;      // bf16 q row stride (odd number of words)
+    extern __shared__ float s_dyn[];                 // [PW][LD] kbar of the pool cells
+    __shared__ uint16_t s_q[kSelQ * QLD];            // the query tile, bf16 bits
     __shared__ int s_pool[kSelPool];
     __shared__ float s_kn[kSelPool];
     __shared__ float s_a[kSelPool];
     __shared__ float s_qn[kSelQ];
+    float *s_kb = s_dyn;
 
     const int h = blockIdx.y;
     const int64_t q0 = (int64_t)blockIdx.x * QW;
@@ -97,22 +99,41 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
         s_pool[t] = c;
         s_a[t] = amax[(int64_t)h * p.C + c];
     }
-    __syncthreads();
-    for (int e = tid; e < npool * D; e += 512) {
-        const int r = e / D, x = e % D;
-        s_kb[r * LD + x] = kbar[((int64_t)h * p.C + s_pool[r]) * D + x];
+    // query tile: 16-byte loads, 8 bf16 per thread per step
+    for (int e = tid; e < nq * (D / 8); e += 512) {
+        const int r = e / (D / 8), x = 8 * (e % (D / 8));
+        const uint4 raw = *reinterpret_cast<const uint4 *>(q + (hN + q0 + r) * D + x);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+            s_q[r * QLD + x + 2 * t2] = (uint16_t)(w4[t2] & 0xFFFFu);
+            s_q[r * QLD + x + 2 * t2 + 1] = (uint16_t)(w4[t2] >> 16);
+        }
     }
-    for (int e = tid; e < nq * D; e += 512) {
-        const int r = e / D, x = e % D;
-        s_q[r * LD + x] = bf16_to_f32(q[(hN + q0 + r) * D + x]);
+    __syncthreads();
+    // pool cell means: 16-byte loads, 4 floats per thread per step
+    for (int e = tid; e < npool * (D / 4); e += 512) {
+        const int r = e / (D / 4), x = 4 * (e % (D / 4));
+        const float4 f = *reinterpret_cast<const float4 *>(kbar + ((int64_t)h * p.C + s_pool[r]) * D + x);
+        s_kb[r * LD + x] = f.x;
+        s_kb[r * LD + x + 1] = f.y;
+        s_kb[r * LD + x + 2] = f.z;
+        s_kb[r * LD + x + 3] = f.w;
     }
     __syncthreads();
     for (int t = tid; t < npool + nq; t += 512) {
-        const float *row = t < npool ? &s_kb[t * LD] : &s_q[(t - npool) * LD];
         float ss = 0.0f;
-        for (int x = 0; x < D; ++x) ss += row[x] * row[x];
-        if (t < npool) s_kn[t] = sqrtf(ss);
-        else s_qn[t - npool] = sqrtf(ss);
+        if (t < npool) {
+            for (int x = 0; x < D; ++x) ss += s_kb[t * LD + x] * s_kb[t * LD + x];
+            s_kn[t] = sqrtf(ss);
+        } else {
+            const int r = t - npool;
+            for (int x = 0; x < D; ++x) {
+                const float f = bf16_to_f32(s_q[r * QLD + x]);
+                ss += f * f;
+            }
+            s_qn[r] = sqrtf(ss);
+        }
     }
     __syncthreads();
 
@@ -216,7 +237,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
         int maxn = __popc(cmask);
 #pragma unroll
         for (int m2 = 32; m2 > 0; m2 >>= 1) maxn = max(maxn, __shfl_xor(maxn, m2));
-        const float *qrow = &s_q[qr * LD];
+        const uint16_t *qrow = &s_q[qr * QLD];
         for (int t = 0; t < maxn; ++t) {
             if (cmask) {
                 const int slot = __ffs(cmask) - 1;
@@ -226,7 +247,8 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                 const float *krow = &s_kb[pos * LD];
                 double content = 0.0;
 #pragma unroll 8
-                for (int x = 0; x < D; ++x) content = __fma_rn((double)qrow[x], (double)krow[x], content);
+                for (int x = 0; x < D; ++x)
+                    content = __fma_rn((double)bf16_to_f32(qrow[x]), (double)krow[x], content);
                 const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
                 const double gg = arg >= 6.0 ? 1.0 : erf(arg);
                 const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[pos]), gg);
@@ -253,11 +275,12 @@ hipError_t launch_select_mfma(const void *q, const float *kbar, const float *ama
                               int32_t *sel, const KParams &p, hipStream_t st) {
     const int QW = p.B <= kSelQ ? p.B : p.B / 2;
     dim3 grid((unsigned)((p.N + QW - 1) / QW), (unsigned)p.H);
+    const size_t lds = (size_t)(p.PW > 0 ? p.PW : 1) * (p.d + 1) * sizeof(float);
     if (p.d == 64)
-        hipLaunchKernelGGL((select_mfma_kernel<64>), grid, dim3(512), 0, st, (const uint16_t *)q, kbar, amax, pool, sel,
-                           p, QW);
+        hipLaunchKernelGGL((select_mfma_kernel<64>), grid, dim3(512), lds, st, (const uint16_t *)q, kbar, amax, pool,
+                           sel, p, QW);
     else
-        hipLaunchKernelGGL((select_mfma_kernel<128>), grid, dim3(512), 0, st, (const uint16_t *)q, kbar, amax, pool,
+        hipLaunchKernelGGL((select_mfma_kernel<128>), grid, dim3(512), lds, st, (const uint16_t *)q, kbar, amax, pool,
                            sel, p, QW);
     return hipGetLastError();
 }

@@ -39,9 +39,10 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 raw, float (&o)[8]) {
     }
 }
 
-__device__ __forceinline__ uint16_t h_bits(float x) {
-    union { _Float16 f; uint16_t u; } c;
-    c.f = (_Float16)x;
+// two floats to a packed fp16 pair (one v_cvt_pkrtz_f16_f32)
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    union { decltype(__builtin_amdgcn_cvt_pkrtz(0.0f, 0.0f)) h; uint32_t u; } c;
+    c.h = __builtin_amdgcn_cvt_pkrtz(a, b);
     return c.u;
 }
 
@@ -155,8 +156,9 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
             }
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const uint32_t lo = (uint32_t)h_bits(e4[0][r]) | ((uint32_t)h_bits(e4[1][r]) << 16);
-                const uint32_t hi = (uint32_t)h_bits(e4[2][r]) | ((uint32_t)h_bits(e4[3][r]) << 16);
+                // bf16 -> fp16 is exact in fp16's normal range: the packed convert's rounding mode is moot
+                const uint32_t lo = pk_f16(e4[0][r], e4[1][r]);
+                const uint32_t hi = pk_f16(e4[2][r], e4[3][r]);
                 *reinterpret_cast<uint2 *>(&vt_lds[buf][(8 * c + r) * VLD + 4 * jq]) = make_uint2(lo, hi);
             }
         }
