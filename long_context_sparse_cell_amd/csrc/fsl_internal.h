@@ -78,6 +78,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 of a wave: the lanes that
+// hold one column of a 16x16 MFMA accumulator. Each step swaps register rows
+// between lane halves (v_permlane16_swap / v_permlane32_swap) and combines the
+// pair, so every lane of the column ends with the same value.
+__device__ __forceinline__ float colmax4(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float colsum4(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x with the hardware instruction alone (no denormal range scaling): softmax
+// weights below 2^-126 of the running maximum are flushed to zero.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online softmax with a lazily updated maximum: the reference value m only
+// moves when a new score exceeds it by more than kStaleLog2 (base-2 units), so
+// the weights 2^(s - m) stay within [0, 2^kStaleLog2] and the accumulators are
+// rescaled only on such rare jumps. The normalised result is the same softmax.
+constexpr float kStaleLog2 = 8.0f;
+
 template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }

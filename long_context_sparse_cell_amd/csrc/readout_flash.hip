@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
     __shared__ uint16_t s_vt[2][kRfChunk][D * VLD];
     __shared__ int s_pool[kRfMaxPool];
     __shared__ uint32_t s_mask[kRfMaxPool][4];
-    __shared__ int s_act[kRfMaxPool];
+    __shared__ uint32_t s_amask[kRfMaxPool][4];  // s_mask in compacted (ascending cell) order
+    __shared__ int s_acell[kRfMaxPool];          // the compacted cells
     __shared__ int s_nact;
 
     const int h = blockIdx.y;
@@ -104,7 +105,12 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
             const int t = t0 + lane;
             const bool on = t < npool && (s_mask[t][0] | s_mask[t][1] | s_mask[t][2] | s_mask[t][3]) != 0u;
             const uint64_t bal = __ballot(on);
-            if (on) s_act[base + __popcll(bal & ((1ull << lane) - 1ull))] = t;
+            if (on) {
+                const int a = base + __popcll(bal & ((1ull << lane) - 1ull));
+                s_acell[a] = s_pool[t];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) s_amask[a][x] = s_mask[t][x];
+            }
             base += __popcll(bal);
         }
         if (lane == 0) s_nact = base;
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
         const int it = min(tid + kRfThreads * u, KITEMS - 1);
         const int ci = it / (S * D / 8), rem = it % (S * D / 8);
         const int ai = min(ch * kRfChunk + ci, nact - 1);
-        const int64_t row = hN + (int64_t)s_pool[s_act[ai]] * S + rem / (D / 8);
+        const int64_t row = hN + (int64_t)s_acell[ai] * S + rem / (D / 8);
         return *reinterpret_cast<const uint4 *>(k + row * D + 8 * (rem % (D / 8)));
     };
     auto kstore = [&](int buf, int u, uint4 val) __attribute__((always_inline)) {
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
         const int ci = it / ((S / 4) * (D / 8)), rem = it % ((S / 4) * (D / 8));
         const int jq = rem % (S / 4), c8 = rem / (S / 4);
         const int ai = min(ch * kRfChunk + ci, nact - 1);
-        const uint16_t *vp = v + (hN + (int64_t)s_pool[s_act[ai]] * S + 4 * jq) * D + 8 * c8;
+        const uint16_t *vp = v + (hN + (int64_t)s_acell[ai] * S + 4 * jq) * D + 8 * c8;
         rv0 = *reinterpret_cast<const uint4 *>(vp);
         rv1 = *reinterpret_cast<const uint4 *>(vp + D);
         rv2 = *reinterpret_cast<const uint4 *>(vp + 2 * D);
@@ -190,8 +196,7 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
         for (int ci = 0; ci < kRfChunk; ++ci) {
             const int ai = ch * kRfChunk + ci;
             if (ai >= nact) break;
-            const int pos = s_act[ai];
-            const uint32_t m16 = (s_mask[pos][qwl >> 5] >> (qwl & 31)) & 0xFFFFu;
+            const uint32_t m16 = (s_amask[ai][qwl >> 5] >> (qwl & 31)) & 0xFFFFu;
             if (m16 == 0u) continue;  // none of this wave's queries selected the cell
             const bool mine = (m16 >> col) & 1u;
             const uint16_t *kt = s_k[buf][ci];
@@ -213,28 +218,46 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sacc[tt][r] *= sl2;
-                    mx = fmaxf(mx, sacc[tt][r]);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = mine ? fmaxf(m_run, mx) : m_run;
-            const float alpha = mine ? exp2f(m_run - m_new) : 1.0f;
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tt][r]);
+            const float cmx = colmax4(mx);  // every lane takes part in the cross-lane step
+            mx = mine ? cmx * sl2 : -INFINITY;
+            // lazily kept maximum: move it only on a jump past kStaleLog2; a query's first
+            // cell just sets it (its accumulators are still zero)
+            const bool grow = mx > m_run + kStaleLog2;
+            const bool resc = grow && m_run != -INFINITY;
+            if (__ballot(resc)) {
+                const float alpha = resc ? exp2_hw(m_run - mx) : 1.0f;
+                l_part *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+            }
+            if (grow) m_run = mx;
+            // queries that did not select the cell get weight 2^-inf = 0
+            const float msub = mine ? m_run : INFINITY;
             R8 pb[KK];
             float lsum = 0.0f;
 #pragma unroll
-            for (int tt = 0; tt < 2 * KK; ++tt)
+            for (int tt = 0; tt < 2 * KK; ++tt) {
+                uint32_t lo = 0u, hi = 0u;
+                if (tt < NT) {
+                    float e[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const _Float16 ph = (mine && tt < NT) ? (_Float16)exp2f(sacc[tt][r] - m_new) : (_Float16)0.0f;
-                    pb[tt >> 1].f[4 * (tt & 1) + r] = ph;
-                    lsum += (float)ph;
+                    for (int r = 0; r < 4; ++r) {
+                        e[r] = exp2_hw(fmaf(sacc[tt][r], sl2, -msub));
+                        lsum += e[r];
+                    }
+                    lo = pk_f16(e[0], e[1]);
+                    hi = pk_f16(e[2], e[3]);
                 }
-            m_run = m_new;
-            l_part = l_part * alpha + lsum;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+                if (tt & 1) {
+                    pb[tt >> 1].u.z = lo;
+                    pb[tt >> 1].u.w = hi;
+                } else {
+                    pb[tt >> 1].u.x = lo;
+                    pb[tt >> 1].u.y = hi;
+                }
+            }
+            l_part += lsum;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
@@ -252,9 +275,7 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
     }
 
     // ---- normalise, RMSNorm over d, mix, write (lane: query col, dims 16*dt + 4*g + r)
-    float l = l_part;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = colsum4(l_part);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     float ss = 0.0f;
 #pragma unroll
@@ -263,8 +284,7 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
 #pragma unroll
         for (int r = 0; r < 4; ++r) ss += oacc[dt][r] * oacc[dt][r];
     }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+    ss = colsum4(ss);
     const float rs = 1.0f / sqrtf(ss / (float)D + p.rms_eps);
     const int ql = qwl + col;
     if (ql < nq) {

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
                 for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float val = sacc[kg][qg][r] * sl2;
+                        float val = sacc[kg][qg][r];
                         if (edge) {
                             const int j = j0 + 16 * kg + r;
                             val = (j <= i && j > i - p.w && j >= 0) ? val : -INFINITY;
@@ -250,26 +250,38 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
                         sacc[kg][qg][r] = val;
                         mx = fmaxf(mx, val);
                     }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[qg], mx);
-                const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-                const float alpha = exp2f(m_run[qg] - m_use);
-                m_run[qg] = m_new;
-                float lsum = 0.0f;
-#pragma unroll
-                for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const _Float16 ph = (_Float16)exp2f(sacc[kg][qg][r] - m_use);
-                        pb[kg >> 1][qg].f[4 * (kg & 1) + r] = ph;
-                        lsum += (float)ph;
-                    }
-                l_part[qg] = l_part[qg] * alpha + lsum;
-                if (alpha != 1.0f) {
+                mx = colmax4(mx) * sl2;
+                const float mr = m_run[qg];
+                const bool grow = mx > mr + kStaleLog2;
+                const bool resc = grow && mr != -INFINITY;
+                if (__ballot(resc)) {  // rare: a score jumped past the lazily kept maximum
+                    const float alpha = resc ? exp2_hw(mr - mx) : 1.0f;
+                    l_part[qg] *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < D / 16; ++dt) oacc[qg][dt] *= alpha;
                 }
+                const float mn = grow ? mx : mr;
+                m_run[qg] = mn;
+                const float msub = mn == -INFINITY ? 0.0f : mn;
+                float lsum = 0.0f;
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) {
+                    float e[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        e[r] = exp2_hw(fmaf(sacc[kg][qg][r], sl2, -msub));
+                        lsum += e[r];
+                    }
+                    const uint32_t lo = pk_f16(e[0], e[1]), hi = pk_f16(e[2], e[3]);
+                    if (kg & 1) {
+                        pb[kg >> 1][qg].u.z = lo;
+                        pb[kg >> 1][qg].u.w = hi;
+                    } else {
+                        pb[kg >> 1][qg].u.x = lo;
+                        pb[kg >> 1][qg].u.y = hi;
+                    }
+                }
+                l_part[qg] += lsum;
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -291,9 +303,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
 
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
-        float l = l_part[qg];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = colsum4(l_part[qg]);
         const int64_t i = qw + 16 * qg + col;
         if (i >= p.N) continue;
         const float inv = 1.0f / l;
