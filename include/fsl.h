@@ -135,6 +135,10 @@ int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_
  * q, k, v: device [H][N][d] (dtype); out: device [H][N][d] (out_dtype).
  * ws: device workspace of at least fsl_workspace_bytes(p) bytes; after the
  * call it holds kbar, amax, pool and sel (see fsl_workspace_views).
+ * With bf16 inputs both attention branches multiply fp16 operands (keys
+ * rotated, values and softmax weights) with fp32 accumulation, so k and v
+ * must lie inside fp16's range (|x| < 65504); the selection path does not
+ * depend on this.
  * sel_out (device [H][N][K] int32), o_win_out and o_long_out (device
  * [H][N][d] float) are optional copies for inspection; pass NULL to skip. */
 int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
@@ -145,7 +149,8 @@ int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const f
  * FSL_NUM_STAGES + 1 caller-created hipEvent_t handles; events[0] is recorded
  * on `stream` before the first kernel and events[s + 1] after stage s, the
  * stages being, in order: cell statistics, norm prune (4 kernels), scoring and
- * top-K, RoPE table, window attention, readout + mix. Elapsed time between
+ * top-K, RoPE table (fp32) or RoPE table + key/value preparation (bf16),
+ * window attention, readout + mix. Elapsed time between
  * consecutive events is the duration of that stage's kernels. Same arguments,
  * results and errors as fsl_attn_fwd otherwise (FSL_E_INVAL if stage_events
  * is NULL). */
@@ -164,6 +169,9 @@ typedef struct fsl_workspace_layout {
     size_t scan_a;  /* float / int32 lists of the prune scan */
     size_t scan_i;
     size_t o_win;   /* float [H][N][d]            window-branch output */
+    size_t rope_abs;/* float2 (cos, sin) by absolute position, two levels (bf16 only) */
+    size_t kt;      /* fp16 [H][Np][d] RoPE-rotated keys, Np = 64 ceil(N/64) (bf16 only) */
+    size_t vt;      /* fp16 [H][Np/16][d][16] values transposed per 16 tokens (bf16 only) */
     size_t total;   /* bytes; equals fsl_workspace_bytes */
 } fsl_workspace_layout;
 int fsl_workspace_views(const fsl_params *p, fsl_workspace_layout *out);

@@ -67,6 +67,10 @@ fsl_workspace_layout layout(const KParams &k) {
     L.scan_a = take((size_t)scan_lists(k) * kChunk * sizeof(float));
     L.scan_i = take((size_t)scan_lists(k) * kChunk * sizeof(int32_t));
     L.o_win = take((size_t)k.H * k.N * k.d * sizeof(float));
+    const bool bf = k.dtype == FSL_BF16;  // the prepared fp16 keys/values serve the bf16 kernels only
+    L.rope_abs = take(bf ? (size_t)(rope_abs_rows_hi(k) + kRopeSpan) * (k.d / 2) * sizeof(float2) : 0);
+    L.kt = take(bf ? (size_t)k.H * kt_rows(k) * k.d * sizeof(uint16_t) : 0);
+    L.vt = take(bf ? (size_t)k.H * vt_groups(k) * 16 * k.d * sizeof(uint16_t) : 0);
     L.total = off;
     return L;
 }
@@ -82,6 +86,9 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
     w.scan_a = (float *)(b + L.scan_a);
     w.scan_i = (int32_t *)(b + L.scan_i);
     w.o_win = (float *)(b + L.o_win);
+    w.rope_abs = (float2 *)(b + L.rope_abs);
+    w.kt = (uint16_t *)(b + L.kt);
+    w.vt = (uint16_t *)(b + L.vt);
     return w;
 }
 
@@ -215,14 +222,15 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
     if (e == hipSuccess)
         e = mark(kp.dtype == FSL_BF16 ? launch_select_mfma(q, w.kbar, w.amax, w.pool, w.sel, kp, stream)
                                       : launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
-    if (e == hipSuccess) e = mark(launch_rope_table(w.rope, kp, stream));
+    const bool bf = kp.dtype == FSL_BF16;
     if (e == hipSuccess)
-        e = mark(kp.dtype == FSL_BF16 ? launch_window_bf16(q, k, v, w.rope, w.o_win, kp, stream)
-                                      : launch_window(q, k, v, w.rope, w.o_win, kp, stream));
+        e = mark(bf ? launch_kv_prep(k, v, w.kt, w.vt, w.rope_abs, kp, stream) : launch_rope_table(w.rope, kp, stream));
     if (e == hipSuccess)
-        e = mark(kp.dtype == FSL_BF16
-                     ? launch_readout_flash(q, k, v, w.sel, w.pool, w.o_win, out, o_long_out, kp, stream)
-                     : launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
+        e = mark(bf ? launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.o_win, kp, stream)
+                    : launch_window(q, k, v, w.rope, w.o_win, kp, stream));
+    if (e == hipSuccess)
+        e = mark(bf ? launch_readout_flash(q, k, w.vt, w.sel, w.pool, w.o_win, out, o_long_out, kp, stream)
+                    : launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
     if (e == hipSuccess && sel_out)
         e = hipMemcpyAsync(sel_out, w.sel, (size_t)kp.H * kp.N * kp.K * sizeof(int32_t), hipMemcpyDeviceToDevice,
                            stream);

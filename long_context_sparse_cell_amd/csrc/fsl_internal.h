@@ -35,12 +35,23 @@ struct Work {
     int32_t *scan_i;   //   chunks [H][nchunk], local prefixes [H][nchunk+1],
                        //   group totals [H][nsg], group prefixes [H][nsg]
     float *o_win;      // [H][N][d] window-branch output
+    // bf16 inputs only (null otherwise): what kv_prep writes
+    float2 *rope_abs;  // absolute-position (cos, sin): ceil(N/64) rows of 64a, then 64 rows of b
+    uint16_t *kt;      // fp16 [H][Np][d] rotated keys, Np = 64 ceil(N/64)
+    uint16_t *vt;      // fp16 [H][Np/16][d][16] values, transposed per 16-token group
 };
 
 constexpr int kChunk = 64;    // cells per prune-scan chunk (one wave)
 constexpr int kGroup = 16;    // chunks per prune-scan group
 constexpr int kQTile = 128;   // queries per window workgroup
 constexpr int kKTile = 64;    // keys per window LDS tile
+constexpr int kRopeSpan = 64; // positions per row of the coarse absolute RoPE table
+
+// rows of the coarse absolute RoPE table (one per 64 positions)
+__host__ __device__ inline int rope_abs_rows_hi(const KParams &p) { return (int)((p.N + kRopeSpan - 1) / kRopeSpan); }
+// kt and vt are padded per head to whole 64-token tiles (zeros past token N-1)
+__host__ __device__ inline int64_t kt_rows(const KParams &p) { return (int64_t)rope_abs_rows_hi(p) * kRopeSpan; }
+__host__ __device__ inline int64_t vt_groups(const KParams &p) { return kt_rows(p) / 16; }
 
 // Offsets of the four prune-scan list families inside scan_a / scan_i, in lists of 64.
 __host__ __device__ inline int64_t scan_chunk(const KParams &p, int h, int64_t k) {
@@ -98,6 +109,17 @@ __device__ __forceinline__ float colsum4(float x) {
     const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i of the wave writes lds_wave + 16 i, so lds_wave must be the same for the
+// whole wave; completion is counted by vmcnt like any global load.
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+typedef __attribute__((address_space(1))) void *global_void_ptr;
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_wave) {
+    __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)lds_wave, 16, 0, 0);
+}
+// wait for this wave's outstanding global loads, LDS copies included
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // 2^x with the hardware instruction alone (no denormal range scaling): softmax
 // weights below 2^-126 of the running maximum are flushed to zero.
@@ -196,12 +218,13 @@ hipError_t launch_select_mfma(const void *q, const float *kbar, const float *ama
 hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st);
 hipError_t launch_window(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
                          const KParams &p, hipStream_t st);
-hipError_t launch_window_bf16(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
+hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs,
+                          const KParams &p, hipStream_t st);
+hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs, float *o_win,
                               const KParams &p, hipStream_t st);
-hipError_t launch_readout_flash(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
-                                const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st);
-hipError_t launch_readout_cells(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
-                                const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st);
+hipError_t launch_readout_flash(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
+                                const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p,
+                                hipStream_t st);
 hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const int32_t *sel,
                               const float *o_win, void *out, float *o_long_out, const KParams &p,
                               hipStream_t st);

@@ -6,14 +6,19 @@
 // A workgroup takes up to 128 queries of one block (8 waves x 16 queries, each
 // wave's queries held in registers as MFMA operands). Every query's cells come
 // from the block's pool, so the workgroup walks the pool cells that at least
-// one of its queries selected, in ascending cell order, staging each cell's
-// keys (bf16, row-major) and values (fp16, transposed) in double-buffered LDS:
-// each selected cell is read from memory once per block. For every cell, each
-// wave whose queries include a selector computes S^T = K_c Q^T (bf16 MFMA,
-// exact products), masks the queries that did not select the cell, and
-// updates a per-query online softmax and O^T = V^T P^T (fp16 MFMA) held in
-// registers; the lane that owns a query column owns its statistics, so no
-// cross-lane traffic is needed. A query's result depends only on its own
+// one of its queries selected, in ascending cell order: each selected cell is
+// read from memory once per block. A cell's keys (raw bf16 rows) and values
+// (fp16, transposed per 16 tokens, from kv_prep.hip) are copied from global
+// memory straight into LDS (global_load_lds, 16 bytes per lane), the next
+// stage's cells while the current ones are multiplied, in two named buffers.
+// The copy picks which 16-byte piece each lane fetches so that key rows keep
+// chunk c of row r at c ^ (r mod d/8) and value rows swap their halves on bit 3
+// of the dimension, which spreads the MFMA operand reads over the LDS banks.
+// For every cell, each wave whose queries include a selector computes
+// S^T = K_c Q^T (bf16 MFMA, exact products), gives the queries that did not
+// select the cell weight zero, and updates a per-query online softmax (lazily
+// kept maximum) and O^T = V^T P^T (fp16 MFMA) held in registers; the lanes of
+// a query column own its statistics. A query's result depends only on its own
 // cells in ascending order, so the output is deterministic.
 #include "fsl_internal.h"
 
@@ -29,14 +34,12 @@ constexpr int kRfThreads = 512;     // 8 waves
 constexpr int kRfWaves = kRfThreads / 64;
 constexpr int kRfMaxQ = 128;
 constexpr int kRfMaxPool = 128;
-constexpr int kRfChunk = 2;         // cells per LDS stage
 
 union R8 {
     uint4 u;
+    uint2 d[2];
     bf16x8 b;
     halfx8 h;
-    _Float16 f[8];
-    uint16_t s[8];
 };
 
 // two floats to a packed fp16 pair (one v_cvt_pkrtz_f16_f32)
@@ -49,22 +52,25 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
 }  // namespace
 
 template <int D, int S>
-__global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+__global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ pool, const float *__restrict__ o_win,
     void *__restrict__ out, float *__restrict__ o_long_out, KParams p, int QW) {
-    constexpr int KLD = D + 8;      // K row stride (elements)
-    constexpr int VLD = S + 8;      // V^T row stride
-    constexpr int NT = S / 16;      // 16-token tiles per cell
+    constexpr int CH = S == 64 ? 1 : 2;              // cells per LDS stage
+    constexpr int CELL = S * D;                      // elements of one cell's keys (and of its values)
+    constexpr int UNITS = 2 * CH * CELL * 2 / 1024;  // 1 KB copy units per stage, keys then values
+    constexpr int UPW = UNITS / kRfWaves;            // units per wave
+    constexpr int CPR = D / 8;                       // 16-byte chunks per key row
+    constexpr int NT = S / 16;                       // 16-token tiles per cell
     constexpr int KK = (NT + 1) / 2;
     constexpr int QS = D / 32;
-    constexpr int KITEMS = kRfChunk * S * D / 8;           // 16-byte K loads per chunk
-    constexpr int VITEMS = kRfChunk * (S / 4) * (D / 8);   // (4 tokens x 8 dims) V items per chunk
-    constexpr int KPT = (KITEMS + kRfThreads - 1) / kRfThreads;
-    __shared__ uint16_t s_k[2][kRfChunk][S * KLD];
-    __shared__ uint16_t s_vt[2][kRfChunk][D * VLD];
+    static_assert(UNITS % kRfWaves == 0 && UPW >= 1, "copy units must split evenly over the waves");
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k0[CH * CELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k1[CH * CELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v0[CH * CELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v1[CH * CELL];
     __shared__ int s_pool[kRfMaxPool];
-    __shared__ uint32_t s_mask[kRfMaxPool][4];
+    __shared__ uint32_t s_mask[kRfMaxPool][4];   // which local queries selected pool position t
     __shared__ uint32_t s_amask[kRfMaxPool][4];  // s_mask in compacted (ascending cell) order
     __shared__ int s_acell[kRfMaxPool];          // the compacted cells
     __shared__ int s_nact;
@@ -73,11 +79,13 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
     const int64_t q0 = (int64_t)blockIdx.x * QW;
     const int64_t b = q0 / p.B;
     const int nq = (int)min((int64_t)QW, p.N - q0);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
     const int K = p.K;
     const int npool = (int)min((int64_t)p.PW, eligible_cells(p, b));
     const int64_t hN = (int64_t)h * p.N;
+    const int64_t G = vt_groups(p);
     const float sl2 = p.scale * 1.4426950408889634f;
 
     // ---- which queries selected which pool cell
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
     }
     __syncthreads();
     const int nact = s_nact;
-    const int nchunk = (nact + kRfChunk - 1) / kRfChunk;
+    const int nchunk = (nact + CH - 1) / CH;
 
     // ---- this wave's 16 queries as bf16 MFMA B operands
     const int qwl = 16 * wave;  // first query (local) of this wave
@@ -126,55 +134,35 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
 #pragma unroll
     for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qrow) * D + 32 * ks + 8 * g);
 
-    // ---- staging: K rows (bf16 copy) and V^T (fp16) of kRfChunk cells
-    static_assert(KPT <= 4, "K staging uses at most four prefetch registers per thread");
-    uint4 rk0 = make_uint4(0u, 0u, 0u, 0u), rk1 = rk0, rk2 = rk0, rk3 = rk0;  // named, never an array
-    uint4 rv0 = rk0, rv1 = rk0, rv2 = rk0, rv3 = rk0;
-    // every thread loads (item indices are clamped, duplicates are harmless) so that the
-    // prefetch registers are written unconditionally and stay in registers
-    auto kload = [&](int ch, int u) __attribute__((always_inline)) -> uint4 {
-        const int it = min(tid + kRfThreads * u, KITEMS - 1);
-        const int ci = it / (S * D / 8), rem = it % (S * D / 8);
-        const int ai = min(ch * kRfChunk + ci, nact - 1);
-        const int64_t row = hN + (int64_t)s_acell[ai] * S + rem / (D / 8);
-        return *reinterpret_cast<const uint4 *>(k + row * D + 8 * (rem % (D / 8)));
-    };
-    auto kstore = [&](int buf, int u, uint4 val) __attribute__((always_inline)) {
-        const int it = min(tid + kRfThreads * u, KITEMS - 1);  // clamped items store the same data twice
-        const int ci = it / (S * D / 8), rem = it % (S * D / 8);
-        *reinterpret_cast<uint4 *>(&s_k[buf][ci][(rem / (D / 8)) * KLD + 8 * (rem % (D / 8))]) = val;
-    };
-    auto fetch = [&](int ch) __attribute__((always_inline)) {
-        rk0 = kload(ch, 0);
-        if constexpr (KPT > 1) rk1 = kload(ch, 1);
-        if constexpr (KPT > 2) rk2 = kload(ch, 2);
-        if constexpr (KPT > 3) rk3 = kload(ch, 3);
-        const int it = min(tid, VITEMS - 1);
-        const int ci = it / ((S / 4) * (D / 8)), rem = it % ((S / 4) * (D / 8));
-        const int jq = rem % (S / 4), c8 = rem / (S / 4);
-        const int ai = min(ch * kRfChunk + ci, nact - 1);
-        const uint16_t *vp = v + (hN + (int64_t)s_acell[ai] * S + 4 * jq) * D + 8 * c8;
-        rv0 = *reinterpret_cast<const uint4 *>(vp);
-        rv1 = *reinterpret_cast<const uint4 *>(vp + D);
-        rv2 = *reinterpret_cast<const uint4 *>(vp + 2 * D);
-        rv3 = *reinterpret_cast<const uint4 *>(vp + 3 * D);
-    };
-    auto store = [&](int buf) __attribute__((always_inline)) {
-        kstore(buf, 0, rk0);
-        if constexpr (KPT > 1) kstore(buf, 1, rk1);
-        if constexpr (KPT > 2) kstore(buf, 2, rk2);
-        if constexpr (KPT > 3) kstore(buf, 3, rk3);
-        const int it = min(tid, VITEMS - 1);
-        const int ci = it / ((S / 4) * (D / 8)), rem = it % ((S / 4) * (D / 8));
-        const int jq = rem % (S / 4), c8 = rem / (S / 4);
-        R8 e0, e1, e2, e3;
-        e0.u = rv0; e1.u = rv1; e2.u = rv2; e3.u = rv3;
+    // ---- copy plan: unit wave + 8 i of a stage, fixed per lane
+    int c_off[UPW], c_cell[UPW], c_dst[UPW];
+    bool c_key[UPW];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            // bf16 -> fp16 is exact in fp16's normal range, so the rounding mode of the packed convert is moot
-            const uint32_t lo = pk_f16(bf16_to_f32(e0.s[r]), bf16_to_f32(e1.s[r]));
-            const uint32_t hi = pk_f16(bf16_to_f32(e2.s[r]), bf16_to_f32(e3.s[r]));
-            *reinterpret_cast<uint2 *>(&s_vt[buf][ci][(8 * c8 + r) * VLD + 4 * jq]) = make_uint2(lo, hi);
+    for (int i = 0; i < UPW; ++i) {
+        const int u = wave + kRfWaves * i;
+        c_key[i] = u < UNITS / 2;
+        const int e0 = (c_key[i] ? u : u - UNITS / 2) * 512;  // first element of the unit in its region
+        c_cell[i] = e0 / CELL;
+        c_dst[i] = e0;
+        const int s = (e0 % CELL) / 8 + lane;                   // 16-byte slot within the cell
+        if (c_key[i]) {
+            const int row = s / CPR, pc = s % CPR;
+            c_off[i] = row * D + 8 * (pc ^ (row & (CPR - 1)));
+        } else {
+            const int r = s >> 1, hf = s & 1;  // r = group * D + dim
+            c_off[i] = r * 16 + 8 * (hf ^ (((r % D) >> 3) & 1));
+        }
+    }
+    const uint16_t *vth = vt + (int64_t)h * G * D * 16;
+    auto issue = [&](int ch, uint16_t *kbuf, uint16_t *vbuf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < UPW; ++i) {
+            const int ai = min(ch * CH + c_cell[i], nact - 1);  // a short last stage repeats its last cell
+            const int64_t cell = __builtin_amdgcn_readfirstlane(s_acell[ai]);
+            if (c_key[i])
+                lds_dma16(k + (hN + cell * S) * D + c_off[i], kbuf + c_dst[i]);
+            else
+                lds_dma16(vth + cell * CELL + c_off[i], vbuf + c_dst[i]);
         }
     };
 
@@ -182,34 +170,28 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
     floatx4 oacc[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int vsw = 8 * ((g >> 1) ^ ((col >> 3) & 1)) + 4 * (g & 1);  // value operand: tokens 4g..4g+3
 
-    if (nchunk > 0) {
-        fetch(0);
-        store(0);
-    }
-    __syncthreads();
-    for (int ch = 0; ch < nchunk; ++ch) {
-        const int buf = ch & 1;
-        const bool more = ch + 1 < nchunk;
-        if (more) fetch(ch + 1);
+    auto process = [&](int ch, const uint16_t *kbuf, const uint16_t *vbuf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ci = 0; ci < kRfChunk; ++ci) {
-            const int ai = ch * kRfChunk + ci;
+        for (int ci = 0; ci < CH; ++ci) {
+            const int ai = ch * CH + ci;
             if (ai >= nact) break;
             const uint32_t m16 = (s_amask[ai][qwl >> 5] >> (qwl & 31)) & 0xFFFFu;
             if (m16 == 0u) continue;  // none of this wave's queries selected the cell
             const bool mine = (m16 >> col) & 1u;
-            const uint16_t *kt = s_k[buf][ci];
-            const uint16_t *vt = s_vt[buf][ci];
+            const uint16_t *kc = kbuf + ci * CELL;
+            const uint16_t *vc = vbuf + ci * CELL;
             floatx4 sacc[2 * KK];
 #pragma unroll
             for (int tt = 0; tt < 2 * KK; ++tt) {
                 sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
                 if (tt < NT) {
+                    const int row = 16 * tt + col;
 #pragma unroll
                     for (int ks = 0; ks < QS; ++ks) {
                         R8 ka;
-                        ka.u = *reinterpret_cast<const uint4 *>(&kt[(16 * tt + col) * KLD + 32 * ks + 8 * g]);
+                        ka.u = *reinterpret_cast<const uint4 *>(&kc[row * D + 8 * ((4 * ks + g) ^ (row & (CPR - 1)))]);
                         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, bq[ks].b, sacc[tt], 0, 0, 0);
                     }
                 }
@@ -249,28 +231,34 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
                     lo = pk_f16(e[0], e[1]);
                     hi = pk_f16(e[2], e[3]);
                 }
-                if (tt & 1) {
-                    pb[tt >> 1].u.z = lo;
-                    pb[tt >> 1].u.w = hi;
-                } else {
-                    pb[tt >> 1].u.x = lo;
-                    pb[tt >> 1].u.y = hi;
-                }
+                pb[tt >> 1].d[tt & 1] = make_uint2(lo, hi);
             }
             l_part += lsum;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt) {
-                    const uint16_t *vr = &vt[(16 * dt + col) * VLD + 32 * kk + 4 * g];
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-                    const uint2 hi = (32 * kk + 16 < S) ? *reinterpret_cast<const uint2 *>(vr + 16) : make_uint2(0u, 0u);
+                    const uint16_t *vr = &vc[((2 * kk) * D + 16 * dt + col) * 16 + vsw];
                     R8 va;
-                    va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    va.d[0] = *reinterpret_cast<const uint2 *>(vr);
+                    va.d[1] = (32 * kk + 16 < S) ? *reinterpret_cast<const uint2 *>(vr + D * 16) : make_uint2(0u, 0u);
                     oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, pb[kk].h, oacc[dt], 0, 0, 0);
                 }
         }
-        if (more) store(buf ^ 1);
+    };
+
+    if (nchunk > 0) issue(0, s_k0, s_v0);
+    wait_vmem();
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ch += 2) {
+        if (ch + 1 < nchunk) issue(ch + 1, s_k1, s_v1);
+        process(ch, s_k0, s_v0);
+        wait_vmem();
+        __syncthreads();
+        if (ch + 1 >= nchunk) break;
+        if (ch + 2 < nchunk) issue(ch + 2, s_k0, s_v0);
+        process(ch + 1, s_k1, s_v1);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -314,17 +302,18 @@ __global__ __launch_bounds__(kRfThreads, (S <= 32 ? 4 : 2)) void readout_flash_k
 }
 
 template <int D, int S>
-static void launch_rf(dim3 grid, hipStream_t st, const void *q, const void *k, const void *v, const int32_t *sel,
+static void launch_rf(dim3 grid, hipStream_t st, const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
                       const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p, int QW) {
     hipLaunchKernelGGL((readout_flash_kernel<D, S>), grid, dim3(kRfThreads), 0, st, (const uint16_t *)q,
-                       (const uint16_t *)k, (const uint16_t *)v, sel, pool, o_win, out, o_long_out, p, QW);
+                       (const uint16_t *)k, vt, sel, pool, o_win, out, o_long_out, p, QW);
 }
 
-hipError_t launch_readout_flash(const void *q, const void *k, const void *v, const int32_t *sel, const int32_t *pool,
-                                const float *o_win, void *out, float *o_long_out, const KParams &p, hipStream_t st) {
+hipError_t launch_readout_flash(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
+                                const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p,
+                                hipStream_t st) {
     const int QW = p.B <= kRfMaxQ ? p.B : p.B / 2;
     dim3 grid((unsigned)((p.N + QW - 1) / QW), (unsigned)p.H);
-#define FSL_RF(DD, SS) launch_rf<DD, SS>(grid, st, q, k, v, sel, pool, o_win, out, o_long_out, p, QW)
+#define FSL_RF(DD, SS) launch_rf<DD, SS>(grid, st, q, k, vt, sel, pool, o_win, out, o_long_out, p, QW)
     if (p.d == 64) {
         if (p.s == 16) FSL_RF(64, 16); else if (p.s == 32) FSL_RF(64, 32); else FSL_RF(64, 64);
     } else {

@@ -2,18 +2,20 @@
 // (FreeSolo digest, core method and step 2; prerequisites: RoPE rotates q_i
 // and k_j so that their product depends only on the offset j - i).
 //
-// Same tiling and operand layout as the generic window kernel (window.hip):
-// 128 queries per workgroup, 4 waves x 32 queries, keys through LDS in tiles
-// of 64, S^T = K Q^T so that P^T feeds O^T = V^T P^T from the accumulator
-// registers, RoPE from a relative-offset table, fp16 operands with fp32
-// accumulation. What this version adds for throughput:
-//  - LDS is double-buffered, and the next tile's global loads (keys, values,
-//    cos/sin rows) are issued into registers before the current tile's MFMAs,
-//    so their latency overlaps the math; one barrier per tile.
-//  - the register budget targets two waves per SIMD.
-//  - only the key tiles that intersect the workgroup's window range are visited.
-#include <cmath>
-
+// Tiling and operands as in the generic window kernel (window.hip): 128
+// queries per workgroup, 4 waves x 32 queries, keys in tiles of 64,
+// S^T = K Q^T so that P^T feeds O^T = V^T P^T from the accumulator registers,
+// fp16 operands with fp32 accumulation. The keys arrive rotated and the values
+// transposed, both in fp16 (kv_prep.hip), so each tile is copied from global
+// memory straight into LDS (global_load_lds, 16 bytes per lane) with no
+// register staging: the LDS layout is set by which 16-byte piece each lane
+// fetches. Key rows keep 16-byte chunk c of row r at position c ^ (r mod
+// D/8), and each 32-byte value row (16 tokens of one dimension) swaps its two
+// halves when bit 3 of the dimension is set; both spread the MFMA operand reads
+// of a wave over the LDS banks. The next tile is copied while the current one
+// is multiplied (two named LDS buffers, so the compiler can tell the copies
+// from the reads), and the online softmax keeps a lazily updated maximum.
+// Queries are rotated in registers with the same absolute-position table.
 #include "fsl_internal.h"
 
 namespace fsl {
@@ -25,19 +27,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 union P8 {
     uint4 u;
-    uint16_t h[8];
+    uint2 d[2];
     _Float16 f[8];
     halfx8 v;
 };
-
-__device__ __forceinline__ void unpack_bf16x8(const uint4 raw, float (&o)[8]) {
-    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        o[2 * t] = __uint_as_float(w4[t] << 16);
-        o[2 * t + 1] = __uint_as_float(w4[t] & 0xFFFF0000u);
-    }
-}
 
 // two floats to a packed fp16 pair (one v_cvt_pkrtz_f16_f32)
 __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
@@ -50,150 +43,101 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__restrict__ q,
-                                                             const uint16_t *__restrict__ k,
-                                                             const uint16_t *__restrict__ v,
+                                                             const uint16_t *__restrict__ kt,
+                                                             const uint16_t *__restrict__ vt,
                                                              const float2 *__restrict__ rope,
                                                              float *__restrict__ o_win, KParams p) {
     constexpr int HALF = D / 2;
-    constexpr int KLD = D + 8;         // K tile row stride (fp16 elements)
-    constexpr int VLD = kKTile + 8;    // V^T tile row stride
-    constexpr int KIT = D / 64;        // K staging items per thread (64 keys x D/16 chunk pairs)
-    constexpr int VITEMS = 2 * D;      // V staging items (16 key quads x D/8 chunks)
-    constexpr int QS = D / 32;         // MFMA k-steps over d
-    __shared__ uint16_t ks_lds[2][kKTile * KLD];
-    __shared__ uint16_t vt_lds[2][D * VLD];
+    constexpr int QS = D / 32;                  // MFMA k-steps over d
+    constexpr int CPR = D / 8;                  // 16-byte chunks per key row
+    constexpr int TILE = kKTile * D;            // fp16 elements of a key tile (and of a value tile)
+    constexpr int UNITS = TILE * 2 / 1024;      // 1 KB copy units per tile
+    constexpr int UPW = UNITS / 4;              // key (and value) units per wave
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
     const int h = blockIdx.y;
     const int64_t q0 = (int64_t)blockIdx.x * kQTile;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
     const int64_t qw = q0 + 32 * wave;
-    const uint16_t *kh = k + (int64_t)h * p.N * D;
-    const uint16_t *vh = v + (int64_t)h * p.N * D;
+    const int64_t npad = (int64_t)rope_abs_rows_hi(p) * kRopeSpan;
+    const int64_t G = vt_groups(p);
     const float sl2 = p.scale * 1.4426950408889634f;
 
     // key tiles that intersect [max(0, q0-w+1), min(N, q0+128) - 1]
-    const int64_t base = q0 + p.rope_lo;
     const int64_t kmin = max((int64_t)0, q0 - p.w + 1);
     const int64_t kmax = min(p.N, q0 + kQTile) - 1;
-    const int t_first = (int)((kmin - base) / kKTile);
-    const int t_last = (int)((kmax - base) / kKTile);
+    const int t_first = (int)(kmin / kKTile);
+    const int t_last = (int)(kmax / kKTile);
 
-    // ---- staging registers
-    constexpr bool PRE_CS = D <= 64;   // prefetch cos/sin rows too when registers allow
-    uint4 pk_a[KIT], pk_b[KIT];
-    float4 pcs[PRE_CS ? KIT : 1][4];
-    uint4 pv[4];
-    auto fetch = [&](int t) {
-        const int64_t ks0 = base + (int64_t)t * kKTile;
+    // ---- this lane's copy offsets (elements within a tile), for units wave + 4 i
+    int koff[UPW], voff[UPW];
 #pragma unroll
-        for (int u = 0; u < KIT; ++u) {
-            const int it = tid + 256 * u;
-            const int jl = it / (D / 16), c = it % (D / 16);
-            const int64_t j = ks0 + jl;
-            const int64_t jc = (j >= 0 && j < p.N) ? j : 0;
-            pk_a[u] = *reinterpret_cast<const uint4 *>(kh + jc * D + 8 * c);
-            pk_b[u] = *reinterpret_cast<const uint4 *>(kh + jc * D + HALF + 8 * c);
-            if constexpr (PRE_CS) {
-                const float4 *tr = reinterpret_cast<const float4 *>(rope + (j - q0 - p.rope_lo) * HALF + 8 * c);
+    for (int i = 0; i < UPW; ++i) {
+        const int s = 64 * (wave + 4 * i) + lane;  // 16-byte slot within the tile
+        const int row = s / CPR, pc = s % CPR;
+        koff[i] = row * D + 8 * (pc ^ (row & (CPR - 1)));
+        const int r = s >> 1, hf = s & 1;       // r = group * D + dim
+        const int dim = r % D;
+        voff[i] = r * 16 + 8 * (hf ^ ((dim >> 3) & 1));
+    }
+    const uint16_t *kth = kt + (int64_t)h * npad * D;
+    const uint16_t *vth = vt + (int64_t)h * G * D * 16;
+    auto issue = [&](int t, uint16_t *kbuf, uint16_t *vbuf) __attribute__((always_inline)) {
+        const uint16_t *kb = kth + (int64_t)t * TILE;  // tiles are contiguous in both arrays
+        const uint16_t *vb = vth + (int64_t)t * TILE;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pcs[u][r] = tr[r];
-            }
-        }
-        if (tid < VITEMS) {
-            const int jq = tid & 15, c = tid >> 4;
+        for (int i = 0; i < UPW; ++i) lds_dma16(kb + koff[i], kbuf + 512 * (wave + 4 * i));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t j = ks0 + 4 * jq + e;
-                const int64_t jc = (j >= 0 && j < p.N) ? j : 0;
-                pv[e] = *reinterpret_cast<const uint4 *>(vh + jc * D + 8 * c);
-            }
-        }
-    };
-    auto store = [&](int t, int buf) {
-        const int64_t ks0 = base + (int64_t)t * kKTile;
-#pragma unroll
-        for (int u = 0; u < KIT; ++u) {
-            const int it = tid + 256 * u;
-            const int jl = it / (D / 16), c = it % (D / 16);
-            const int64_t j = ks0 + jl;
-            const bool ok = j >= 0 && j < p.N;
-            float a[8], b[8];
-            unpack_bf16x8(pk_a[u], a);
-            unpack_bf16x8(pk_b[u], b);
-            float4 c4[4];
-            if constexpr (PRE_CS) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) c4[r] = pcs[u][r];
-            } else {
-                const float4 *tr = reinterpret_cast<const float4 *>(rope + (j - q0 - p.rope_lo) * HALF + 8 * c);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) c4[r] = tr[r];
-            }
-            const float cs[16] = {c4[0].x, c4[0].y, c4[0].z, c4[0].w, c4[1].x, c4[1].y, c4[1].z, c4[1].w,
-                                  c4[2].x, c4[2].y, c4[2].z, c4[2].w, c4[3].x, c4[3].y, c4[3].z, c4[3].w};
-            P8 ra, rb;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float x0 = ok ? a[r] : 0.0f, y0 = ok ? b[r] : 0.0f;
-                const float co = cs[2 * r], si = cs[2 * r + 1];
-                ra.f[r] = (_Float16)(x0 * co - y0 * si);
-                rb.f[r] = (_Float16)(y0 * co + x0 * si);
-            }
-            *reinterpret_cast<uint4 *>(&ks_lds[buf][jl * KLD + 8 * c]) = ra.u;
-            *reinterpret_cast<uint4 *>(&ks_lds[buf][jl * KLD + HALF + 8 * c]) = rb.u;
-        }
-        if (tid < VITEMS) {
-            const int jq = tid & 15, c = tid >> 4;  // 16 lanes fill one V^T row segment: no bank conflicts
-            float e4[4][8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t j = ks0 + 4 * jq + e;
-                const bool ok = j >= 0 && j < p.N;
-                unpack_bf16x8(pv[e], e4[e]);
-#pragma unroll
-                for (int r = 0; r < 8; ++r) e4[e][r] = ok ? e4[e][r] : 0.0f;
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                // bf16 -> fp16 is exact in fp16's normal range: the packed convert's rounding mode is moot
-                const uint32_t lo = pk_f16(e4[0][r], e4[1][r]);
-                const uint32_t hi = pk_f16(e4[2][r], e4[3][r]);
-                *reinterpret_cast<uint2 *>(&vt_lds[buf][(8 * c + r) * VLD + 4 * jq]) = make_uint2(lo, hi);
-            }
-        }
+        for (int i = 0; i < UPW; ++i) lds_dma16(vb + voff[i], vbuf + 512 * (wave + 4 * i));
     };
 
     // ---- rotated queries as fp16 MFMA B operands (column = query, k-slots = dims 32ks + 8g + r)
     halfx8 qreg[2][QS];
+    {
+        const int nhi = rope_abs_rows_hi(p);
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        const int64_t i = qw + 16 * qg + col;
-        const bool ok = i < p.N;
-        const uint16_t *qi = q + ((int64_t)h * p.N + (ok ? i : 0)) * D;
-        const float2 *tr = rope + (int64_t)(i - q0 - p.rope_lo) * HALF;
-        float x[QS][8];
+        for (int qg = 0; qg < 2; ++qg) {
+            const int64_t i = qw + 16 * qg + col;
+            const bool ok = i < p.N;
+            const int64_t ic = ok ? i : p.N - 1;
+            const uint16_t *qi = q + ((int64_t)h * p.N + ic) * D;
+            const float2 *th = rope + (ic / kRopeSpan) * HALF;
+            const float2 *tl = rope + (int64_t)(nhi + (int)(ic % kRopeSpan)) * HALF;
+            float x[QS][8];
 #pragma unroll
-        for (int ks = 0; ks < QS; ++ks) {
-            unpack_bf16x8(*reinterpret_cast<const uint4 *>(qi + 32 * ks + 8 * g), x[ks]);
+            for (int ks = 0; ks < QS; ++ks) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(qi + 32 * ks + 8 * g);
+                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-            for (int r = 0; r < 8; ++r) x[ks][r] = ok ? x[ks][r] : 0.0f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < QS / 2; ++ks)
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float2 cs = tr[32 * ks + 8 * g + r];
-                const float a = x[ks][r], b = x[ks + QS / 2][r];
-                x[ks][r] = a * cs.x - b * cs.y;
-                x[ks + QS / 2][r] = b * cs.x + a * cs.y;
+                for (int t = 0; t < 4; ++t) {
+                    x[ks][2 * t] = ok ? __uint_as_float(w4[t] << 16) : 0.0f;
+                    x[ks][2 * t + 1] = ok ? __uint_as_float(w4[t] & 0xFFFF0000u) : 0.0f;
+                }
             }
 #pragma unroll
-        for (int ks = 0; ks < QS; ++ks) {
-            P8 pk;
+            for (int ks = 0; ks < QS / 2; ++ks)
 #pragma unroll
-            for (int r = 0; r < 8; ++r) pk.f[r] = (_Float16)x[ks][r];
-            qreg[qg][ks] = pk.v;
+                for (int r = 0; r < 8; ++r) {
+                    const int m = 32 * ks + 8 * g + r;
+                    const float2 a2 = th[m], b2 = tl[m];
+                    const float c = a2.x * b2.x - a2.y * b2.y;
+                    const float sn = a2.y * b2.x + a2.x * b2.y;
+                    const float a = x[ks][r], b = x[ks + QS / 2][r];
+                    x[ks][r] = a * c - b * sn;
+                    x[ks + QS / 2][r] = b * c + a * sn;
+                }
+#pragma unroll
+            for (int ks = 0; ks < QS; ++ks) {
+                P8 pk;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) pk.f[r] = (_Float16)x[ks][r];
+                qreg[qg][ks] = pk.v;
+            }
         }
     }
 
@@ -205,99 +149,98 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) oacc[qg][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    fetch(t_first);
-    store(t_first, 0);
-    __syncthreads();
-    for (int t = t_first; t <= t_last; ++t) {
-        const int buf = (t - t_first) & 1;
-        const bool more = t < t_last;
-        if (more) fetch(t + 1);
-        const int64_t ks0 = base + (int64_t)t * kKTile;
+    auto compute = [&](int t, const uint16_t *kbuf, const uint16_t *vbuf) __attribute__((always_inline)) {
+        const int64_t ks0 = (int64_t)t * kKTile;
         const bool active = qw < p.N && ks0 <= qw + 31 && ks0 + kKTile - 1 >= qw - p.w + 1;
-        if (active) {
-            const uint16_t *kt = ks_lds[buf];
-            const uint16_t *vt = vt_lds[buf];
-            floatx4 sacc[4][2];
+        if (!active) return;
+        floatx4 sacc[4][2];
 #pragma unroll
-            for (int kg = 0; kg < 4; ++kg) {
-                sacc[kg][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-                sacc[kg][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int kg = 0; kg < 4; ++kg) {
+            sacc[kg][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+            sacc[kg][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const int row = 16 * kg + col;
 #pragma unroll
-                for (int ks = 0; ks < QS; ++ks) {
-                    P8 ka;
-                    ka.u = *reinterpret_cast<const uint4 *>(&kt[(16 * kg + col) * KLD + 32 * ks + 8 * g]);
-                    sacc[kg][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[0][ks], sacc[kg][0], 0, 0, 0);
-                    sacc[kg][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[1][ks], sacc[kg][1], 0, 0, 0);
-                }
-            }
-            // positions fit in int32 (N < 2^31, the window offset is bounded by w)
-            const int j0 = (int)ks0 + 4 * g;
-            const bool edge = !(ks0 + kKTile - 1 <= qw && ks0 > qw + 31 - p.w && ks0 >= 0);
-            P8 pb[2][2];
-#pragma unroll
-            for (int qg = 0; qg < 2; ++qg) {
-                const int i = (int)qw + 16 * qg + col;
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float val = sacc[kg][qg][r];
-                        if (edge) {
-                            const int j = j0 + 16 * kg + r;
-                            val = (j <= i && j > i - p.w && j >= 0) ? val : -INFINITY;
-                        }
-                        sacc[kg][qg][r] = val;
-                        mx = fmaxf(mx, val);
-                    }
-                mx = colmax4(mx) * sl2;
-                const float mr = m_run[qg];
-                const bool grow = mx > mr + kStaleLog2;
-                const bool resc = grow && mr != -INFINITY;
-                if (__ballot(resc)) {  // rare: a score jumped past the lazily kept maximum
-                    const float alpha = resc ? exp2_hw(mr - mx) : 1.0f;
-                    l_part[qg] *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < D / 16; ++dt) oacc[qg][dt] *= alpha;
-                }
-                const float mn = grow ? mx : mr;
-                m_run[qg] = mn;
-                const float msub = mn == -INFINITY ? 0.0f : mn;
-                float lsum = 0.0f;
-#pragma unroll
-                for (int kg = 0; kg < 4; ++kg) {
-                    float e[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        e[r] = exp2_hw(fmaf(sacc[kg][qg][r], sl2, -msub));
-                        lsum += e[r];
-                    }
-                    const uint32_t lo = pk_f16(e[0], e[1]), hi = pk_f16(e[2], e[3]);
-                    if (kg & 1) {
-                        pb[kg >> 1][qg].u.z = lo;
-                        pb[kg >> 1][qg].u.w = hi;
-                    } else {
-                        pb[kg >> 1][qg].u.x = lo;
-                        pb[kg >> 1][qg].u.y = hi;
-                    }
-                }
-                l_part[qg] += lsum;
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) {
-                    const uint16_t *vr = &vt[(16 * dt + col) * VLD + 32 * kk + 4 * g];
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
-                    P8 va;
-                    va.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][0].v, oacc[0][dt], 0, 0, 0);
-                    oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][1].v, oacc[1][dt], 0, 0, 0);
-                }
+            for (int ks = 0; ks < QS; ++ks) {
+                P8 ka;
+                ka.u = *reinterpret_cast<const uint4 *>(&kbuf[row * D + 8 * ((4 * ks + g) ^ (row & (CPR - 1)))]);
+                sacc[kg][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[0][ks], sacc[kg][0], 0, 0, 0);
+                sacc[kg][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[1][ks], sacc[kg][1], 0, 0, 0);
             }
         }
-        if (more) store(t + 1, buf ^ 1);
+        // positions fit in int32 (N < 2^31)
+        const int j0 = (int)ks0 + 4 * g;
+        const bool edge = !(ks0 + kKTile - 1 <= qw && ks0 > qw + 31 - p.w);
+        P8 pb[2][2];
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+            const int i = (int)qw + 16 * qg + col;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float val = sacc[kg][qg][r];
+                    if (edge) {
+                        const int j = j0 + 16 * kg + r;
+                        val = (j <= i && j > i - p.w) ? val : -INFINITY;
+                    }
+                    sacc[kg][qg][r] = val;
+                    mx = fmaxf(mx, val);
+                }
+            mx = colmax4(mx) * sl2;
+            const float mr = m_run[qg];
+            const bool grow = mx > mr + kStaleLog2;
+            const bool resc = grow && mr != -INFINITY;
+            if (__ballot(resc)) {  // rare: a score jumped past the lazily kept maximum
+                const float alpha = resc ? exp2_hw(mr - mx) : 1.0f;
+                l_part[qg] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) oacc[qg][dt] *= alpha;
+            }
+            const float mn = grow ? mx : mr;
+            m_run[qg] = mn;
+            const float msub = mn == -INFINITY ? 0.0f : mn;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) {
+                float e[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    e[r] = exp2_hw(fmaf(sacc[kg][qg][r], sl2, -msub));
+                    lsum += e[r];
+                }
+                pb[kg >> 1][qg].d[kg & 1] = make_uint2(pk_f16(e[0], e[1]), pk_f16(e[2], e[3]));
+            }
+            l_part[qg] += lsum;
+        }
+        // value operand: dimension 16 dt + col, tokens 4g..4g+3 of groups 2kk and 2kk+1
+        const int vsw = 8 * ((g >> 1) ^ ((col >> 3) & 1)) + 4 * (g & 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const uint16_t *vr = &vbuf[((2 * kk) * D + 16 * dt + col) * 16 + vsw];
+                P8 va;
+                va.d[0] = *reinterpret_cast<const uint2 *>(vr);
+                va.d[1] = *reinterpret_cast<const uint2 *>(vr + D * 16);
+                oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][0].v, oacc[0][dt], 0, 0, 0);
+                oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][1].v, oacc[1][dt], 0, 0, 0);
+            }
+        }
+    };
+
+    issue(t_first, k_lds0, v_lds0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = t_first; t <= t_last; t += 2) {
+        if (t + 1 <= t_last) issue(t + 1, k_lds1, v_lds1);
+        compute(t, k_lds0, v_lds0);
+        wait_vmem();
+        __syncthreads();
+        if (t + 1 > t_last) break;
+        if (t + 2 <= t_last) issue(t + 2, k_lds0, v_lds0);
+        compute(t + 1, k_lds1, v_lds1);
+        wait_vmem();
         __syncthreads();
     }
 
@@ -316,15 +259,15 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
     }
 }
 
-hipError_t launch_window_bf16(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
-                              const KParams &p, hipStream_t st) {
+hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs,
+                              float *o_win, const KParams &p, hipStream_t st) {
     dim3 grid((unsigned)((p.N + kQTile - 1) / kQTile), (unsigned)p.H);
     if (p.d == 64)
-        hipLaunchKernelGGL((window_bf16_kernel<64>), grid, dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
-                           (const uint16_t *)v, rope, o_win, p);
+        hipLaunchKernelGGL((window_bf16_kernel<64>), grid, dim3(256), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
+                           o_win, p);
     else
-        hipLaunchKernelGGL((window_bf16_kernel<128>), grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, rope, o_win, p);
+        hipLaunchKernelGGL((window_bf16_kernel<128>), grid, dim3(256), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
+                           o_win, p);
     return hipGetLastError();
 }
 

@@ -39,7 +39,8 @@ class Params(ctypes.Structure):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win", "total")]
+                ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win", "rope_abs", "kt", "vt",
+                                      "total")]
 
 
 _lib = None
@@ -185,7 +186,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, out: 
 
 
 NUM_STAGES = 6
-STAGES = ("cell_stats", "prune", "select", "rope_table", "window", "readout_mix")
+STAGES = ("cell_stats", "prune", "select", "kv_prep", "window", "readout_mix")
 
 
 def attn_fwd_timed(q, k, v, p: Params, out: torch.Tensor, ws: torch.Tensor, events, stream=None):

@@ -28,6 +28,14 @@ def _print_case(name):
     print(f"\n[case] {name}", flush=True)
 
 
+# Branch-level diagnostics (the parity bar itself is on `out`, checked below).
+# With bf16 inputs both branches multiply fp16 operands: softmax weights rounded
+# toward zero carry up to 2^-10 relative error, which moves an output by up to
+# 2^-10 of the weighted spread |v_j - o_i| (about 4 for N(0,1) values, so
+# ~4e-3), on top of the fp16 rounding of the rotated q and k inside the scores.
+BRANCH_TOL_BF16 = 6e-3
+
+
 def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=True):
     """Compare one GPU run with the oracle, head by head."""
     sh = inp.shape
@@ -54,8 +62,9 @@ def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=
                 return o / np.sqrt((o.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6)
             el = np.abs(normed(o_long[h][idx]) - normed(r["o_long"])).max()
             print(f"  head {h}: o_win max err {ew:.3e}, RMSNorm(o_long) max err {el:.3e}", flush=True)
-            assert ew <= (1e-4 if sh.dtype == synth.F32 else 4e-3), f"o_win head {h}: {ew:.3e}"
-            assert el <= (1e-4 if sh.dtype == synth.F32 else 4e-3), f"RMSNorm(o_long) head {h}: {el:.3e}"
+            tol = 1e-4 if sh.dtype == synth.F32 else BRANCH_TOL_BF16
+            assert ew <= tol, f"o_win head {h}: {ew:.3e}"
+            assert el <= tol, f"RMSNorm(o_long) head {h}: {el:.3e}"
         mx, mean = check_out(out[h][idx], r["out"], out_dtype, f"out head {h}")
         print(f"  head {h}: out max err {mx:.3e}, mean {mean:.3e}", flush=True)
         worst = max(worst, mx)
