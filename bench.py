@@ -80,6 +80,9 @@ def algorithmic_work(sh, sel_np=None):
         # distinct cells each block reads (measured union, counted once per block)
         "readout_mix": ("hbm", H * N * d * (e + 4 + e)),
     }
+    if sh.dtype == "bf16":
+        # k and v read once, fp16 rotated keys and transposed values written once
+        work["kv_prep"] = ("hbm", H * N * d * (2 * e + 2 * 2))
     if sel_np is not None:
         union_cells = 0
         for h in range(H):
@@ -180,6 +183,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-rows", type=int, default=131072)
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB, the reference kernel for scaling "
+                         "profiler byte counters (FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -189,6 +195,16 @@ def main():
 
     import torch
     from long_context_sparse_cell_amd import fsl, synth
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read, {args.calib_copy_mib} MiB written")
+        del src, dst
 
     sh = synth.CONFIGS[args.workload]
     assert sh.kind == "fwd"

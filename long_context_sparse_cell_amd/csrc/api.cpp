@@ -32,6 +32,8 @@ int check(const fsl_params *p) {
     if (p->s != 16 && p->s != 32 && p->s != 64) return FSL_E_UNSUPPORTED;
     if (p->B % 16 != 0 || p->B > 256) return FSL_E_UNSUPPORTED;
     if (p->P < 0 || p->P > 64 || p->W > 64 || p->K > 8) return FSL_E_UNSUPPORTED;
+    // work-group ids over (head, 64-token tile) must fit one 32-bit grid dimension
+    if ((p->N / 64 + 1) * (int64_t)p->H >= (int64_t(1) << 31)) return FSL_E_UNSUPPORTED;
     return FSL_OK;
 }
 
@@ -69,8 +71,8 @@ fsl_workspace_layout layout(const KParams &k) {
     L.o_win = take((size_t)k.H * k.N * k.d * sizeof(float));
     const bool bf = k.dtype == FSL_BF16;  // the prepared fp16 keys/values serve the bf16 kernels only
     L.rope_abs = take(bf ? (size_t)(rope_abs_rows_hi(k) + kRopeSpan) * (k.d / 2) * sizeof(float2) : 0);
-    L.kt = take(bf ? (size_t)k.H * kt_rows(k) * k.d * sizeof(uint16_t) : 0);
-    L.vt = take(bf ? (size_t)k.H * vt_groups(k) * 16 * k.d * sizeof(uint16_t) : 0);
+    L.kt = take(bf ? (size_t)k.H * kt_head_elems(k) * sizeof(uint16_t) : 0);
+    L.vt = take(bf ? (size_t)k.H * vt_head_elems(k) * sizeof(uint16_t) : 0);
     L.total = off;
     return L;
 }

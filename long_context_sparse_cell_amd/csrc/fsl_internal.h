@@ -38,7 +38,7 @@ struct Work {
     // bf16 inputs only (null otherwise): what kv_prep writes
     float2 *rope_abs;  // absolute-position (cos, sin): ceil(N/64) rows of 64a, then 64 rows of b
     uint16_t *kt;      // fp16 [H][Np][d] rotated keys, Np = 64 ceil(N/64)
-    uint16_t *vt;      // fp16 [H][Np/16][d][16] values, transposed per 16-token group
+    uint16_t *vt;      // fp16 [H][Np/32][d][32] values, transposed per 32-token group (vt_pos order)
 };
 
 constexpr int kChunk = 64;    // cells per prune-scan chunk (one wave)
@@ -51,7 +51,34 @@ constexpr int kRopeSpan = 64; // positions per row of the coarse absolute RoPE t
 __host__ __device__ inline int rope_abs_rows_hi(const KParams &p) { return (int)((p.N + kRopeSpan - 1) / kRopeSpan); }
 // kt and vt are padded per head to whole 64-token tiles (zeros past token N-1)
 __host__ __device__ inline int64_t kt_rows(const KParams &p) { return (int64_t)rope_abs_rows_hi(p) * kRopeSpan; }
-__host__ __device__ inline int64_t vt_groups(const KParams &p) { return kt_rows(p) / 16; }
+// vt holds groups of 32 tokens: [H][Np/32][d][32], tokens permuted inside a group
+__host__ __device__ inline int64_t vt_groups(const KParams &p) { return kt_rows(p) / 32; }
+// elements per head of kt and of vt (the same count: Np tokens x d); the
+// workspace sizes and every kernel's per-head offsets derive from these
+__host__ __device__ inline int64_t kt_head_elems(const KParams &p) { return kt_rows(p) * p.d; }
+__host__ __device__ inline int64_t vt_head_elems(const KParams &p) { return vt_groups(p) * 32 * p.d; }
+// Position of token t (0..31) inside a vt group row. An MFMA P^T operand built
+// from the accumulators of two 16-token score tiles gives lane group g (lanes
+// 16g..16g+15) tokens 4g..4g+3 of the first tile and 4g..4g+3 of the second as
+// its k-slots 0..7; storing them at 8g..8g+7 makes each lane's value operand
+// one contiguous 16-byte piece.
+__host__ __device__ inline int vt_pos(int t) { return 8 * ((t & 15) >> 2) + (t & 3) + 4 * (t >> 4); }
+// LDS swizzles applied by the tile copies (16-byte pieces) and undone by the
+// operand reads, chosen so that the 16 lanes of one MFMA operand read hit
+// distinct banks: key rows (d/8 chunks) and value rows (4 pieces).
+__host__ __device__ inline int swz_key(int row, int d) {
+    return d == 128 ? (row & 15) : ((row ^ (row >> 3)) & 7);
+}
+__host__ __device__ inline int swz_val(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
+
+// Work-group order for L2 reuse. The dispatcher deals consecutive work-group ids
+// to the eight XCDs in turn, and each XCD has its own L2; this bijection of
+// [0, T) gives XCD x a contiguous range of the logical order, so neighbouring
+// logical work-groups (which share key/value tiles) run under the same L2.
+__device__ __forceinline__ int xcd_remap(int L, int T) {
+    const int q = T >> 3, r = T & 7, x = L & 7, i = L >> 3;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
 
 // Offsets of the four prune-scan list families inside scan_a / scan_i, in lists of 64.
 __host__ __device__ inline int64_t scan_chunk(const KParams &p, int h, int64_t k) {

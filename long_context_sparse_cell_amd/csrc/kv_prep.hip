@@ -3,8 +3,9 @@
 //  - kt: RoPE-rotated keys R(j) k_j at their absolute positions, fp16, [H][Np][d]
 //    (FreeSolo digest, core method and step 2: the window branch uses standard
 //    rotate-half RoPE with base 10000, frequencies base^(-2m/d));
-//  - vt: values as fp16, transposed per group of 16 tokens, [H][Np/16][d][16],
-//    the A-operand layout of the O^T = V^T P^T products in both branches.
+//  - vt: values as fp16, transposed per group of 32 tokens, [H][Np/32][d][32],
+//    tokens inside a group in vt_pos order: the A-operand layout of the
+//    O^T = V^T P^T products in both branches, one 16-byte piece per lane.
 // Np = 64 ceil(N/64): both arrays are padded to whole 64-token tiles with zeros.
 // fp16 holds bf16 values exactly inside fp16's range (|x| < 65504); the
 // fp16-operand products of both branches assume inputs in that range.
@@ -54,32 +55,46 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ kt, uint16_t *__restrict__ vt,
                                                       const float2 *__restrict__ rope, int nhi, KParams p) {
     constexpr int HALF = D / 2;
-    constexpr int PG = HALF / 8;       // groups of 8 rotation pairs per row
-    constexpr int TLD = kRopeSpan + 8; // transposed tile row stride
-    __shared__ uint16_t s_t[D * TLD];  // fp16 bits, [dim][token]
+    constexpr int PG = HALF / 8;               // groups of 8 rotation pairs per row
+    constexpr int KIT = kRopeSpan * PG / 256;  // key items per thread
+    constexpr int VIT = kRopeSpan * D / 8 / 2 / 256;  // value items (token pair x 8 dims) per thread
+    constexpr int TLD = kRopeSpan + 8;         // transposed tile row stride
+    static_assert(KIT >= 1 && VIT >= 1, "tile work must cover every thread");
+    __shared__ uint16_t s_t[D * TLD];          // fp16 bits, [dim][token]
 
     const int h = blockIdx.y;
     const int64_t j0 = (int64_t)blockIdx.x * kRopeSpan;
     const int tid = threadIdx.x;
     const int64_t hN = (int64_t)h * p.N;
-    const int64_t G = vt_groups(p);
-    const int64_t hNp = (int64_t)h * kt_rows(p);
+
+    // ---- issue every global load of this thread first
+    uint4 ka[KIT], kb[KIT], va[VIT], vb[VIT];
+#pragma unroll
+    for (int u = 0; u < KIT; ++u) {
+        const int it = tid + 256 * u, jl = it / PG, pg = it % PG;
+        const int64_t j = min(j0 + jl, p.N - 1);  // rows past the end are replaced by zeros below
+        const uint16_t *kr = k + (hN + j) * D;
+        ka[u] = *reinterpret_cast<const uint4 *>(kr + 8 * pg);
+        kb[u] = *reinterpret_cast<const uint4 *>(kr + HALF + 8 * pg);
+    }
+#pragma unroll
+    for (int u = 0; u < VIT; ++u) {
+        const int it = tid + 256 * u, jp = it % (kRopeSpan / 2), c8 = it / (kRopeSpan / 2);
+        const int64_t j = j0 + 2 * jp;
+        va[u] = *reinterpret_cast<const uint4 *>(v + (hN + min(j, p.N - 1)) * D + 8 * c8);
+        vb[u] = *reinterpret_cast<const uint4 *>(v + (hN + min(j + 1, p.N - 1)) * D + 8 * c8);
+    }
 
     // ---- rotated keys
     const float2 *hi = rope + (int64_t)blockIdx.x * HALF;
-    for (int it = tid; it < kRopeSpan * PG; it += 256) {
-        const int jl = it / PG, pg = it % PG;
+#pragma unroll
+    for (int u = 0; u < KIT; ++u) {
+        const int it = tid + 256 * u, jl = it / PG, pg = it % PG;
         const int64_t j = j0 + jl;
-        uint16_t *o = kt + (hNp + j) * D;
-        if (j >= p.N) {
-            *reinterpret_cast<uint4 *>(o + 8 * pg) = make_uint4(0u, 0u, 0u, 0u);
-            *reinterpret_cast<uint4 *>(o + HALF + 8 * pg) = make_uint4(0u, 0u, 0u, 0u);
-            continue;
-        }
-        const uint16_t *kr = k + (hN + j) * D;
+        const bool ok = j < p.N;
         float a[8], b[8];
-        bf16x8_to_f32(*reinterpret_cast<const uint4 *>(kr + 8 * pg), a);
-        bf16x8_to_f32(*reinterpret_cast<const uint4 *>(kr + HALF + 8 * pg), b);
+        bf16x8_to_f32(ka[u], a);
+        bf16x8_to_f32(kb[u], b);
         const float2 *lo = rope + (int64_t)(nhi + jl) * HALF;
         H8 ra, rb;
 #pragma unroll
@@ -87,39 +102,45 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
             const float2 th = hi[8 * pg + r], tl = lo[8 * pg + r];
             const float c = th.x * tl.x - th.y * tl.y;
             const float s = th.y * tl.x + th.x * tl.y;
-            ra.f[r] = (_Float16)(a[r] * c - b[r] * s);
-            rb.f[r] = (_Float16)(b[r] * c + a[r] * s);
+            ra.f[r] = ok ? (_Float16)(a[r] * c - b[r] * s) : (_Float16)0.0f;
+            rb.f[r] = ok ? (_Float16)(b[r] * c + a[r] * s) : (_Float16)0.0f;
         }
+        uint16_t *o = kt + h * kt_head_elems(p) + j * D;
         *reinterpret_cast<uint4 *>(o + 8 * pg) = ra.u;
         *reinterpret_cast<uint4 *>(o + HALF + 8 * pg) = rb.u;
     }
 
     // ---- values: fp16, transposed through LDS (token pairs per 32-bit store)
-    for (int it = tid; it < (kRopeSpan / 2) * (D / 8); it += 256) {
-        const int jp = it % (kRopeSpan / 2), c8 = it / (kRopeSpan / 2);
+#pragma unroll
+    for (int u = 0; u < VIT; ++u) {
+        const int it = tid + 256 * u, jp = it % (kRopeSpan / 2), c8 = it / (kRopeSpan / 2);
         const int64_t j = j0 + 2 * jp;
         float e0[8], e1[8];
-        if (j < p.N) bf16x8_to_f32(*reinterpret_cast<const uint4 *>(v + (hN + j) * D + 8 * c8), e0);
-        else for (int r = 0; r < 8; ++r) e0[r] = 0.0f;
-        if (j + 1 < p.N) bf16x8_to_f32(*reinterpret_cast<const uint4 *>(v + (hN + j + 1) * D + 8 * c8), e1);
-        else for (int r = 0; r < 8; ++r) e1[r] = 0.0f;
+        bf16x8_to_f32(va[u], e0);
+        bf16x8_to_f32(vb[u], e1);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             union { _Float16 f[2]; uint32_t u; } pr;
-            pr.f[0] = (_Float16)e0[r];
-            pr.f[1] = (_Float16)e1[r];
+            pr.f[0] = j < p.N ? (_Float16)e0[r] : (_Float16)0.0f;
+            pr.f[1] = j + 1 < p.N ? (_Float16)e1[r] : (_Float16)0.0f;
             *reinterpret_cast<uint32_t *>(&s_t[(8 * c8 + r) * TLD + 2 * jp]) = pr.u;
         }
     }
     __syncthreads();
-    // [group][dim][16] rows of 32 bytes, two 16-byte pieces each; consecutive pieces
-    // are consecutive in memory
-    const int64_t g0 = j0 / 16;
-    for (int pi = tid; pi < (kRopeSpan / 16) * D * 2; pi += 256) {
-        const int grp = pi / (2 * D), rem = pi % (2 * D);
-        const int dim = rem >> 1, hf = rem & 1;
-        const uint4 val = *reinterpret_cast<const uint4 *>(&s_t[dim * TLD + 16 * grp + 8 * hf]);
-        *reinterpret_cast<uint4 *>(vt + ((h * G + g0 + grp) * D + dim) * 16 + 8 * hf) = val;
+    // rows of 32 tokens in vt_pos order: piece g of (group, dim) holds tokens
+    // 4g..4g+3 and 16+4g..16+4g+3 of the group; consecutive pieces are consecutive
+    // in memory
+    constexpr int PIECES = (kRopeSpan / 32) * D * 4;
+#pragma unroll
+    for (int u = 0; u < PIECES / 256; ++u) {
+        const int pi = tid + 256 * u;
+        const int grp = pi / (4 * D), rem = pi % (4 * D);
+        const int dim = rem >> 2, pg = rem & 3;
+        const uint16_t *src = &s_t[dim * TLD + 32 * grp + 4 * pg];
+        const uint2 lo = *reinterpret_cast<const uint2 *>(src);
+        const uint2 hi2 = *reinterpret_cast<const uint2 *>(src + 16);
+        *reinterpret_cast<uint4 *>(vt + h * vt_head_elems(p) + ((2 * (int64_t)blockIdx.x + grp) * D + dim) * 32 + 8 * pg) =
+            make_uint4(lo.x, lo.y, hi2.x, hi2.y);
     }
 }
 

@@ -8,12 +8,14 @@
 // from the block's pool, so the workgroup walks the pool cells that at least
 // one of its queries selected, in ascending cell order: each selected cell is
 // read from memory once per block. A cell's keys (raw bf16 rows) and values
-// (fp16, transposed per 16 tokens, from kv_prep.hip) are copied from global
-// memory straight into LDS (global_load_lds, 16 bytes per lane), the next
-// stage's cells while the current ones are multiplied, in two named buffers.
-// The copy picks which 16-byte piece each lane fetches so that key rows keep
-// chunk c of row r at c ^ (r mod d/8) and value rows swap their halves on bit 3
-// of the dimension, which spreads the MFMA operand reads over the LDS banks.
+// (fp16, transposed per 32-token group in vt_pos order, from kv_prep.hip; a
+// 16-token cell brings its whole group) are copied from global memory straight
+// into LDS (global_load_lds, 16 bytes per lane), the next stage's cells while
+// the current ones are multiplied, in two named buffers. The copy picks which
+// 16-byte piece each lane fetches so that key rows keep chunk c at
+// c ^ swz_key(row) and value rows keep piece g at g ^ swz_val(dim), which
+// spreads the MFMA operand reads over the LDS banks. Work-groups run in an
+// XCD-aware order so that consecutive blocks, whose pools overlap, share an L2.
 // For every cell, each wave whose queries include a selector computes
 // S^T = K_c Q^T (bf16 MFMA, exact products), gives the queries that did not
 // select the cell weight zero, and updates a per-query online softmax (lazily
@@ -57,26 +59,29 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     const int32_t *__restrict__ sel, const int32_t *__restrict__ pool, const float *__restrict__ o_win,
     void *__restrict__ out, float *__restrict__ o_long_out, KParams p, int QW) {
     constexpr int CH = S == 64 ? 1 : 2;              // cells per LDS stage
-    constexpr int CELL = S * D;                      // elements of one cell's keys (and of its values)
-    constexpr int UNITS = 2 * CH * CELL * 2 / 1024;  // 1 KB copy units per stage, keys then values
-    constexpr int UPW = UNITS / kRfWaves;            // units per wave
+    constexpr int CELL = S * D;                      // elements of one cell's keys
+    constexpr int VCELL = (S < 32 ? 32 : S) * D;     // elements of the value groups holding a cell
+    constexpr int KUNITS = CH * CELL * 2 / 1024;     // 1 KB copy units per stage: keys,
+    constexpr int UNITS = KUNITS + CH * VCELL * 2 / 1024;  // then values
+    constexpr int UPW = (UNITS + kRfWaves - 1) / kRfWaves;  // units per wave (the last may be idle)
     constexpr int CPR = D / 8;                       // 16-byte chunks per key row
     constexpr int NT = S / 16;                       // 16-token tiles per cell
     constexpr int KK = (NT + 1) / 2;
     constexpr int QS = D / 32;
-    static_assert(UNITS % kRfWaves == 0 && UPW >= 1, "copy units must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) uint16_t s_k0[CH * CELL];
     __shared__ __attribute__((aligned(1024))) uint16_t s_k1[CH * CELL];
-    __shared__ __attribute__((aligned(1024))) uint16_t s_v0[CH * CELL];
-    __shared__ __attribute__((aligned(1024))) uint16_t s_v1[CH * CELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v0[CH * VCELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v1[CH * VCELL];
     __shared__ int s_pool[kRfMaxPool];
     __shared__ uint32_t s_mask[kRfMaxPool][4];   // which local queries selected pool position t
     __shared__ uint32_t s_amask[kRfMaxPool][4];  // s_mask in compacted (ascending cell) order
     __shared__ int s_acell[kRfMaxPool];          // the compacted cells
     __shared__ int s_nact;
 
-    const int h = blockIdx.y;
-    const int64_t q0 = (int64_t)blockIdx.x * QW;
+    const int nqb = (int)((p.N + QW - 1) / QW);
+    const int logical = xcd_remap((int)blockIdx.x, nqb * p.H);
+    const int h = logical / nqb;
+    const int64_t q0 = (int64_t)(logical % nqb) * QW;
     const int64_t b = q0 / p.B;
     const int nq = (int)min((int64_t)QW, p.N - q0);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -85,7 +90,6 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     const int K = p.K;
     const int npool = (int)min((int64_t)p.PW, eligible_cells(p, b));
     const int64_t hN = (int64_t)h * p.N;
-    const int64_t G = vt_groups(p);
     const float sl2 = p.scale * 1.4426950408889634f;
 
     // ---- which queries selected which pool cell
@@ -136,33 +140,36 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
 
     // ---- copy plan: unit wave + 8 i of a stage, fixed per lane
     int c_off[UPW], c_cell[UPW], c_dst[UPW];
-    bool c_key[UPW];
+    bool c_key[UPW], c_on[UPW];
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
         const int u = wave + kRfWaves * i;
-        c_key[i] = u < UNITS / 2;
-        const int e0 = (c_key[i] ? u : u - UNITS / 2) * 512;  // first element of the unit in its region
-        c_cell[i] = e0 / CELL;
+        c_on[i] = u < UNITS;
+        c_key[i] = u < KUNITS;
+        const int e0 = (c_key[i] ? u : u - KUNITS) * 512;  // first element of the unit in its region
+        const int per = c_key[i] ? CELL : VCELL;
+        c_cell[i] = e0 / per;
         c_dst[i] = e0;
-        const int s = (e0 % CELL) / 8 + lane;                   // 16-byte slot within the cell
+        const int s = (e0 % per) / 8 + lane;                 // 16-byte slot within the cell's region
         if (c_key[i]) {
             const int row = s / CPR, pc = s % CPR;
-            c_off[i] = row * D + 8 * (pc ^ (row & (CPR - 1)));
+            c_off[i] = row * D + 8 * (pc ^ swz_key(row, D));
         } else {
-            const int r = s >> 1, hf = s & 1;  // r = group * D + dim
-            c_off[i] = r * 16 + 8 * (hf ^ (((r % D) >> 3) & 1));
+            const int r = s >> 2, pg = s & 3;  // r = group * D + dim
+            c_off[i] = r * 32 + 8 * (pg ^ swz_val(r % D));
         }
     }
-    const uint16_t *vth = vt + (int64_t)h * G * D * 16;
+    const uint16_t *vth = vt + h * vt_head_elems(p);
     auto issue = [&](int ch, uint16_t *kbuf, uint16_t *vbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < UPW; ++i) {
+            if (!c_on[i]) continue;
             const int ai = min(ch * CH + c_cell[i], nact - 1);  // a short last stage repeats its last cell
             const int64_t cell = __builtin_amdgcn_readfirstlane(s_acell[ai]);
             if (c_key[i])
                 lds_dma16(k + (hN + cell * S) * D + c_off[i], kbuf + c_dst[i]);
             else
-                lds_dma16(vth + cell * CELL + c_off[i], vbuf + c_dst[i]);
+                lds_dma16(vth + (cell * S / 32) * (32 * D) + c_off[i], vbuf + c_dst[i]);
         }
     };
 
@@ -170,7 +177,6 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     floatx4 oacc[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int vsw = 8 * ((g >> 1) ^ ((col >> 3) & 1)) + 4 * (g & 1);  // value operand: tokens 4g..4g+3
 
     auto process = [&](int ch, const uint16_t *kbuf, const uint16_t *vbuf) __attribute__((always_inline)) {
 #pragma unroll
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
             if (m16 == 0u) continue;  // none of this wave's queries selected the cell
             const bool mine = (m16 >> col) & 1u;
             const uint16_t *kc = kbuf + ci * CELL;
-            const uint16_t *vc = vbuf + ci * CELL;
+            const uint16_t *vc = vbuf + ci * VCELL;
             floatx4 sacc[2 * KK];
 #pragma unroll
             for (int tt = 0; tt < 2 * KK; ++tt) {
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
 #pragma unroll
                     for (int ks = 0; ks < QS; ++ks) {
                         R8 ka;
-                        ka.u = *reinterpret_cast<const uint4 *>(&kc[row * D + 8 * ((4 * ks + g) ^ (row & (CPR - 1)))]);
+                        ka.u = *reinterpret_cast<const uint4 *>(&kc[row * D + 8 * ((4 * ks + g) ^ swz_key(row, D))]);
                         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, bq[ks].b, sacc[tt], 0, 0, 0);
                     }
                 }
@@ -233,15 +239,22 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
                 }
                 pb[tt >> 1].d[tt & 1] = make_uint2(lo, hi);
             }
+            if constexpr (S == 16) {
+                // a 16-token cell is one half of its value group: move its weights to the
+                // k-slots of that half (slots 4..7 for an odd cell)
+                if (s_acell[ai] & 1) {
+                    pb[0].d[1] = pb[0].d[0];
+                    pb[0].d[0] = make_uint2(0u, 0u);
+                }
+            }
             l_part += lsum;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt) {
-                    const uint16_t *vr = &vc[((2 * kk) * D + 16 * dt + col) * 16 + vsw];
+                    const int dim = 16 * dt + col;
                     R8 va;
-                    va.d[0] = *reinterpret_cast<const uint2 *>(vr);
-                    va.d[1] = (32 * kk + 16 < S) ? *reinterpret_cast<const uint2 *>(vr + D * 16) : make_uint2(0u, 0u);
+                    va.u = *reinterpret_cast<const uint4 *>(&vc[((kk * D + dim) * 4 + (g ^ swz_val(dim))) * 8]);
                     oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, pb[kk].h, oacc[dt], 0, 0, 0);
                 }
         }
@@ -312,7 +325,7 @@ hipError_t launch_readout_flash(const void *q, const void *k, const uint16_t *vt
                                 const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p,
                                 hipStream_t st) {
     const int QW = p.B <= kRfMaxQ ? p.B : p.B / 2;
-    dim3 grid((unsigned)((p.N + QW - 1) / QW), (unsigned)p.H);
+    dim3 grid((unsigned)(((p.N + QW - 1) / QW) * p.H));
 #define FSL_RF(DD, SS) launch_rf<DD, SS>(grid, st, q, k, vt, sel, pool, o_win, out, o_long_out, p, QW)
     if (p.d == 64) {
         if (p.s == 16) FSL_RF(64, 16); else if (p.s == 32) FSL_RF(64, 32); else FSL_RF(64, 64);

@@ -9,10 +9,12 @@
 // transposed, both in fp16 (kv_prep.hip), so each tile is copied from global
 // memory straight into LDS (global_load_lds, 16 bytes per lane) with no
 // register staging: the LDS layout is set by which 16-byte piece each lane
-// fetches. Key rows keep 16-byte chunk c of row r at position c ^ (r mod
-// D/8), and each 32-byte value row (16 tokens of one dimension) swaps its two
-// halves when bit 3 of the dimension is set; both spread the MFMA operand reads
-// of a wave over the LDS banks. The next tile is copied while the current one
+// fetches. Key rows keep 16-byte chunk c at position c ^ swz_key(row), and
+// each 64-byte value row (32 tokens of one dimension in vt_pos order, four
+// 16-byte pieces, one per MFMA lane group) keeps piece g at g ^ swz_val(dim);
+// both spread the operand reads of a wave over the LDS banks. Work-groups run
+// in an XCD-aware order so that the ~10 query tiles sharing a key tile meet in
+// one L2. The next tile is copied while the current one
 // is multiplied (two named LDS buffers, so the compiler can tell the copies
 // from the reads), and the online softmax keeps a lazily updated maximum.
 // Queries are rotated in registers with the same absolute-position table.
@@ -58,14 +60,14 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
-    const int h = blockIdx.y;
-    const int64_t q0 = (int64_t)blockIdx.x * kQTile;
+    const int ntile = (int)((p.N + kQTile - 1) / kQTile);
+    const int logical = xcd_remap((int)blockIdx.x, ntile * p.H);
+    const int h = logical / ntile;
+    const int64_t q0 = (int64_t)(logical % ntile) * kQTile;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
     const int64_t qw = q0 + 32 * wave;
-    const int64_t npad = (int64_t)rope_abs_rows_hi(p) * kRopeSpan;
-    const int64_t G = vt_groups(p);
     const float sl2 = p.scale * 1.4426950408889634f;
 
     // key tiles that intersect [max(0, q0-w+1), min(N, q0+128) - 1]
@@ -80,13 +82,12 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
     for (int i = 0; i < UPW; ++i) {
         const int s = 64 * (wave + 4 * i) + lane;  // 16-byte slot within the tile
         const int row = s / CPR, pc = s % CPR;
-        koff[i] = row * D + 8 * (pc ^ (row & (CPR - 1)));
-        const int r = s >> 1, hf = s & 1;       // r = group * D + dim
-        const int dim = r % D;
-        voff[i] = r * 16 + 8 * (hf ^ ((dim >> 3) & 1));
+        koff[i] = row * D + 8 * (pc ^ swz_key(row, D));
+        const int r = s >> 2, pg = s & 3;       // r = group * D + dim
+        voff[i] = r * 32 + 8 * (pg ^ swz_val(r % D));
     }
-    const uint16_t *kth = kt + (int64_t)h * npad * D;
-    const uint16_t *vth = vt + (int64_t)h * G * D * 16;
+    const uint16_t *kth = kt + h * kt_head_elems(p);
+    const uint16_t *vth = vt + h * vt_head_elems(p);
     auto issue = [&](int t, uint16_t *kbuf, uint16_t *vbuf) __attribute__((always_inline)) {
         const uint16_t *kb = kth + (int64_t)t * TILE;  // tiles are contiguous in both arrays
         const uint16_t *vb = vth + (int64_t)t * TILE;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
 #pragma unroll
             for (int ks = 0; ks < QS; ++ks) {
                 P8 ka;
-                ka.u = *reinterpret_cast<const uint4 *>(&kbuf[row * D + 8 * ((4 * ks + g) ^ (row & (CPR - 1)))]);
+                ka.u = *reinterpret_cast<const uint4 *>(&kbuf[row * D + 8 * ((4 * ks + g) ^ swz_key(row, D))]);
                 sacc[kg][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[0][ks], sacc[kg][0], 0, 0, 0);
                 sacc[kg][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[1][ks], sacc[kg][1], 0, 0, 0);
             }
@@ -213,16 +214,14 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
             }
             l_part[qg] += lsum;
         }
-        // value operand: dimension 16 dt + col, tokens 4g..4g+3 of groups 2kk and 2kk+1
-        const int vsw = 8 * ((g >> 1) ^ ((col >> 3) & 1)) + 4 * (g & 1);
+        // value operand: dimension 16 dt + col, piece g of 32-token group kk
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
-                const uint16_t *vr = &vbuf[((2 * kk) * D + 16 * dt + col) * 16 + vsw];
+                const int dim = 16 * dt + col;
                 P8 va;
-                va.d[0] = *reinterpret_cast<const uint2 *>(vr);
-                va.d[1] = *reinterpret_cast<const uint2 *>(vr + D * 16);
+                va.u = *reinterpret_cast<const uint4 *>(&vbuf[((kk * D + dim) * 4 + (g ^ swz_val(dim))) * 8]);
                 oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][0].v, oacc[0][dt], 0, 0, 0);
                 oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][1].v, oacc[1][dt], 0, 0, 0);
             }
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
 
 hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs,
                               float *o_win, const KParams &p, hipStream_t st) {
-    dim3 grid((unsigned)((p.N + kQTile - 1) / kQTile), (unsigned)p.H);
+    dim3 grid((unsigned)(((p.N + kQTile - 1) / kQTile) * p.H));
     if (p.d == 64)
         hipLaunchKernelGGL((window_bf16_kernel<64>), grid, dim3(256), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
                            o_win, p);

@@ -89,6 +89,24 @@ def test_good_parameters_and_workspace_size(fsl):
     assert all(getattr(L, f) % 256 == 0 for f in ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win"))
 
 
+@pytest.mark.parametrize("N,d", [(5000, 128), (4096, 64), (64, 64), (1, 128), (262144, 128)])
+def test_prepared_key_value_arrays_cover_whole_tiles(fsl, N, d):
+    """With bf16 inputs the workspace holds the rotated fp16 keys and transposed fp16
+    values that the window and readout kernels copy in whole 64-token tiles: each
+    needs H x Np x d fp16 elements, Np = 64 ceil(N/64), per-head extents back to back."""
+    H = 3
+    p = params(fsl, N=N, d=d, H=H, dtype=1, out_dtype=1)
+    L = fsl.workspace_layout(p)
+    need = H * (64 * ((N + 63) // 64)) * d * 2
+    assert L.vt - L.kt >= need
+    assert L.total - L.vt >= need
+    assert L.kt % 256 == 0 and L.vt % 256 == 0
+    # the fp32 path does not prepare them
+    p32 = params(fsl, N=N, d=d, H=H, dtype=0, out_dtype=0)
+    L32 = fsl.workspace_layout(p32)
+    assert L32.total == L32.vt == L32.kt
+
+
 def test_null_pointers_and_small_workspace_fail_before_launch(fsl):
     L = fsl.lib()
     p = params(fsl)
