@@ -147,6 +147,43 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds_wave) {
 }
 // wait for this wave's outstanding global loads, LDS copies included
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N of this wave's global loads / LDS copies are outstanding
+// (they complete in issue order, so everything older than the last N is done)
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// 16-byte LDS reads issued as one inline-asm block that also waits for them:
+// for ring buffers whose refills and reads are ordered explicitly (vmcnt wait +
+// barrier), this keeps the compiler from adding its own conservative wait for
+// every copy in flight. The results are complete when the block ends.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void lds_read16x2(uint4 &a, uint4 &b, const void *pa, const void *pb) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b)
+                 : "v"(lds_addr(pa)), "v"(lds_addr(pb))
+                 : "memory");
+}
+__device__ __forceinline__ void lds_read16x4(uint4 &a, uint4 &b, uint4 &c, uint4 &d, const void *pa, const void *pb,
+                                             const void *pc, const void *pd) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+        : "v"(lds_addr(pa)), "v"(lds_addr(pb)), "v"(lds_addr(pc)), "v"(lds_addr(pd))
+        : "memory");
+}
+
+// Work-group barrier without the memory fence of __syncthreads, whose release
+// would also drain every LDS copy still in flight. The caller has already
+// waited (vmcnt) for the copies the other waves are about to read; this wave's
+// own LDS reads are completed here so that a copy issued after the barrier
+// cannot overwrite a slot that is still being read.
+__device__ __forceinline__ void barrier_no_fence() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // 2^x with the hardware instruction alone (no denormal range scaling): softmax
 // weights below 2^-126 of the running maximum are flushed to zero.

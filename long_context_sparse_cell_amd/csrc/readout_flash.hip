@@ -10,8 +10,9 @@
 // read from memory once per block. A cell's keys (raw bf16 rows) and values
 // (fp16, transposed per 32-token group in vt_pos order, from kv_prep.hip; a
 // 16-token cell brings its whole group) are copied from global memory straight
-// into LDS (global_load_lds, 16 bytes per lane), the next stage's cells while
-// the current ones are multiplied, in two named buffers. The copy picks which
+// into LDS (global_load_lds, 16 bytes per lane) through a ring of one-cell
+// stages (named arrays, so the compiler can tell copies from reads), several
+// cells ahead of the one being multiplied. The copy picks which
 // 16-byte piece each lane fetches so that key rows keep chunk c at
 // c ^ swz_key(row) and value rows keep piece g at g ^ swz_val(dim), which
 // spreads the MFMA operand reads over the LDS banks. Work-groups run in an
@@ -58,20 +59,25 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ pool, const float *__restrict__ o_win,
     void *__restrict__ out, float *__restrict__ o_long_out, KParams p, int QW) {
-    constexpr int CH = S == 64 ? 1 : 2;              // cells per LDS stage
     constexpr int CELL = S * D;                      // elements of one cell's keys
     constexpr int VCELL = (S < 32 ? 32 : S) * D;     // elements of the value groups holding a cell
-    constexpr int KUNITS = CH * CELL * 2 / 1024;     // 1 KB copy units per stage: keys,
-    constexpr int UNITS = KUNITS + CH * VCELL * 2 / 1024;  // then values
-    constexpr int UPW = (UNITS + kRfWaves - 1) / kRfWaves;  // units per wave (the last may be idle)
+    constexpr int KUNITS = CELL * 2 / 1024;          // 1 KB copy units per cell: keys,
+    constexpr int UNITS = KUNITS + VCELL * 2 / 1024; // then values
+    constexpr int UPW = (UNITS + kRfWaves - 1) / kRfWaves;  // copies per wave per cell
+    constexpr int NS = (CELL + VCELL) * 2 <= 16384 ? 4 : 2;  // ring stages (LDS <= 64 KB)
     constexpr int CPR = D / 8;                       // 16-byte chunks per key row
     constexpr int NT = S / 16;                       // 16-token tiles per cell
     constexpr int KK = (NT + 1) / 2;
     constexpr int QS = D / 32;
-    __shared__ __attribute__((aligned(1024))) uint16_t s_k0[CH * CELL];
-    __shared__ __attribute__((aligned(1024))) uint16_t s_k1[CH * CELL];
-    __shared__ __attribute__((aligned(1024))) uint16_t s_v0[CH * VCELL];
-    __shared__ __attribute__((aligned(1024))) uint16_t s_v1[CH * VCELL];
+    static_assert(UPW * (NS - 2) < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k0[CELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k1[CELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k2[NS > 2 ? CELL : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_k3[NS > 2 ? CELL : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v0[VCELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v1[VCELL];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v2[NS > 2 ? VCELL : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_v3[NS > 2 ? VCELL : 8];
     __shared__ int s_pool[kRfMaxPool];
     __shared__ uint32_t s_mask[kRfMaxPool][4];   // which local queries selected pool position t
     __shared__ uint32_t s_amask[kRfMaxPool][4];  // s_mask in compacted (ascending cell) order
@@ -129,7 +135,6 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     }
     __syncthreads();
     const int nact = s_nact;
-    const int nchunk = (nact + CH - 1) / CH;
 
     // ---- this wave's 16 queries as bf16 MFMA B operands
     const int qwl = 16 * wave;  // first query (local) of this wave
@@ -138,19 +143,18 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
 #pragma unroll
     for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qrow) * D + 32 * ks + 8 * g);
 
-    // ---- copy plan: unit wave + 8 i of a stage, fixed per lane
-    int c_off[UPW], c_cell[UPW], c_dst[UPW];
-    bool c_key[UPW], c_on[UPW];
+    // ---- copy plan: a cell's keys then its values in 1 KB units; this wave copies
+    // units wave + 8 i. Every wave issues exactly UPW copies per cell (spare units
+    // repeat the last one, writing the same bytes) so that vmcnt counts whole cells.
+    int c_off[UPW], c_dst[UPW];
+    bool c_key[UPW];
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
-        const int u = wave + kRfWaves * i;
-        c_on[i] = u < UNITS;
+        const int u = min(wave + kRfWaves * i, UNITS - 1);
         c_key[i] = u < KUNITS;
         const int e0 = (c_key[i] ? u : u - KUNITS) * 512;  // first element of the unit in its region
-        const int per = c_key[i] ? CELL : VCELL;
-        c_cell[i] = e0 / per;
         c_dst[i] = e0;
-        const int s = (e0 % per) / 8 + lane;                 // 16-byte slot within the cell's region
+        const int s = e0 / 8 + lane;                       // 16-byte slot within the region
         if (c_key[i]) {
             const int row = s / CPR, pc = s % CPR;
             c_off[i] = row * D + 8 * (pc ^ swz_key(row, D));
@@ -160,12 +164,10 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
         }
     }
     const uint16_t *vth = vt + h * vt_head_elems(p);
-    auto issue = [&](int ch, uint16_t *kbuf, uint16_t *vbuf) __attribute__((always_inline)) {
+    auto issue = [&](int ai, uint16_t *kbuf, uint16_t *vbuf) __attribute__((always_inline)) {
+        const int64_t cell = __builtin_amdgcn_readfirstlane(s_acell[ai]);
 #pragma unroll
         for (int i = 0; i < UPW; ++i) {
-            if (!c_on[i]) continue;
-            const int ai = min(ch * CH + c_cell[i], nact - 1);  // a short last stage repeats its last cell
-            const int64_t cell = __builtin_amdgcn_readfirstlane(s_acell[ai]);
             if (c_key[i])
                 lds_dma16(k + (hN + cell * S) * D + c_off[i], kbuf + c_dst[i]);
             else
@@ -178,102 +180,126 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto process = [&](int ch, const uint16_t *kbuf, const uint16_t *vbuf) __attribute__((always_inline)) {
+    auto process = [&](int ai, const uint16_t *kc, const uint16_t *vc) __attribute__((always_inline)) {
+        const uint32_t m16 = (s_amask[ai][qwl >> 5] >> (qwl & 31)) & 0xFFFFu;
+        if (m16 == 0u) return;  // none of this wave's queries selected the cell
+        const bool mine = (m16 >> col) & 1u;
+        floatx4 sacc[2 * KK];
 #pragma unroll
-        for (int ci = 0; ci < CH; ++ci) {
-            const int ai = ch * CH + ci;
-            if (ai >= nact) break;
-            const uint32_t m16 = (s_amask[ai][qwl >> 5] >> (qwl & 31)) & 0xFFFFu;
-            if (m16 == 0u) continue;  // none of this wave's queries selected the cell
-            const bool mine = (m16 >> col) & 1u;
-            const uint16_t *kc = kbuf + ci * CELL;
-            const uint16_t *vc = vbuf + ci * VCELL;
-            floatx4 sacc[2 * KK];
+        for (int tt = 0; tt < 2 * KK; ++tt) {
+            sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (tt < NT) {
+                const int row = 16 * tt + col;
 #pragma unroll
-            for (int tt = 0; tt < 2 * KK; ++tt) {
-                sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                if (tt < NT) {
-                    const int row = 16 * tt + col;
-#pragma unroll
-                    for (int ks = 0; ks < QS; ++ks) {
-                        R8 ka;
-                        ka.u = *reinterpret_cast<const uint4 *>(&kc[row * D + 8 * ((4 * ks + g) ^ swz_key(row, D))]);
-                        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, bq[ks].b, sacc[tt], 0, 0, 0);
-                    }
+                for (int ks = 0; ks < QS; ++ks) {
+                    R8 ka;
+                    ka.u = *reinterpret_cast<const uint4 *>(&kc[row * D + 8 * ((4 * ks + g) ^ swz_key(row, D))]);
+                    sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, bq[ks].b, sacc[tt], 0, 0, 0);
                 }
             }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tt][r]);
-            const float cmx = colmax4(mx);  // every lane takes part in the cross-lane step
-            mx = mine ? cmx * sl2 : -INFINITY;
-            // lazily kept maximum: move it only on a jump past kStaleLog2; a query's first
-            // cell just sets it (its accumulators are still zero)
-            const bool grow = mx > m_run + kStaleLog2;
-            const bool resc = grow && m_run != -INFINITY;
-            if (__ballot(resc)) {
-                const float alpha = resc ? exp2_hw(m_run - mx) : 1.0f;
-                l_part *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
-            }
-            if (grow) m_run = mx;
-            // queries that did not select the cell get weight 2^-inf = 0
-            const float msub = mine ? m_run : INFINITY;
-            R8 pb[KK];
-            float lsum = 0.0f;
-#pragma unroll
-            for (int tt = 0; tt < 2 * KK; ++tt) {
-                uint32_t lo = 0u, hi = 0u;
-                if (tt < NT) {
-                    float e[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        e[r] = exp2_hw(fmaf(sacc[tt][r], sl2, -msub));
-                        lsum += e[r];
-                    }
-                    lo = pk_f16(e[0], e[1]);
-                    hi = pk_f16(e[2], e[3]);
-                }
-                pb[tt >> 1].d[tt & 1] = make_uint2(lo, hi);
-            }
-            if constexpr (S == 16) {
-                // a 16-token cell is one half of its value group: move its weights to the
-                // k-slots of that half (slots 4..7 for an odd cell)
-                if (s_acell[ai] & 1) {
-                    pb[0].d[1] = pb[0].d[0];
-                    pb[0].d[0] = make_uint2(0u, 0u);
-                }
-            }
-            l_part += lsum;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) {
-                    const int dim = 16 * dt + col;
-                    R8 va;
-                    va.u = *reinterpret_cast<const uint4 *>(&vc[((kk * D + dim) * 4 + (g ^ swz_val(dim))) * 8]);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.h, pb[kk].h, oacc[dt], 0, 0, 0);
-                }
         }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tt][r]);
+        const float cmx = colmax4(mx);  // every lane takes part in the cross-lane step
+        mx = mine ? cmx * sl2 : -INFINITY;
+        // lazily kept maximum: move it only on a jump past kStaleLog2; a query's first
+        // cell just sets it (its accumulators are still zero)
+        const bool grow = mx > m_run + kStaleLog2;
+        const bool resc = grow && m_run != -INFINITY;
+        if (__ballot(resc)) {
+            const float alpha = resc ? exp2_hw(m_run - mx) : 1.0f;
+            l_part *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+        }
+        if (grow) m_run = mx;
+        // queries that did not select the cell get weight 2^-inf = 0
+        const float msub = mine ? m_run : INFINITY;
+        R8 pb[KK];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int tt = 0; tt < 2 * KK; ++tt) {
+            uint32_t lo = 0u, hi = 0u;
+            if (tt < NT) {
+                float e[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    e[r] = exp2_hw(fmaf(sacc[tt][r], sl2, -msub));
+                    lsum += e[r];
+                }
+                lo = pk_f16(e[0], e[1]);
+                hi = pk_f16(e[2], e[3]);
+            }
+            pb[tt >> 1].d[tt & 1] = make_uint2(lo, hi);
+        }
+        if constexpr (S == 16) {
+            // a 16-token cell is one half of its value group: move its weights to the
+            // k-slots of that half (slots 4..7 for an odd cell)
+            if (s_acell[ai] & 1) {
+                pb[0].d[1] = pb[0].d[0];
+                pb[0].d[0] = make_uint2(0u, 0u);
+            }
+        }
+        l_part += lsum;
+        // value operands two or four at a time (one inline-asm block, see lds_read16x4)
+        constexpr int VB = KK > 1 ? 2 : 4;
+        auto vaddr = [&](int kk, int dt) __attribute__((always_inline)) {
+            const int dim = 16 * dt + col;
+            return &vc[((kk * D + dim) * 4 + (g ^ swz_val(dim))) * 8];
+        };
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int d0 = 0; d0 < D / 16; d0 += VB) {
+                R8 va[VB];
+                if constexpr (VB == 4)
+                    lds_read16x4(va[0].u, va[1].u, va[2].u, va[3].u, vaddr(kk, d0), vaddr(kk, d0 + 1),
+                                 vaddr(kk, d0 + 2), vaddr(kk, d0 + 3));
+                else
+                    lds_read16x2(va[0].u, va[1].u, vaddr(kk, d0), vaddr(kk, d0 + 1));
+#pragma unroll
+                for (int x = 0; x < VB; ++x)
+                    oacc[d0 + x] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[x].h, pb[kk].h, oacc[d0 + x], 0, 0, 0);
+            }
     };
 
-    if (nchunk > 0) issue(0, s_k0, s_v0);
-    wait_vmem();
-    __syncthreads();
-    for (int ch = 0; ch < nchunk; ch += 2) {
-        if (ch + 1 < nchunk) issue(ch + 1, s_k1, s_v1);
-        process(ch, s_k0, s_v0);
-        wait_vmem();
-        __syncthreads();
-        if (ch + 1 >= nchunk) break;
-        if (ch + 2 < nchunk) issue(ch + 2, s_k0, s_v0);
-        process(ch + 1, s_k1, s_v1);
-        wait_vmem();
-        __syncthreads();
+    // ---- ring of NS one-cell stages: while cell a is multiplied, cells a+1 .. a+NS-1
+    // are in flight. Before cell a: this wave's copies of it are done once at most
+    // the NS-2 younger cells' copies are outstanding; the barrier then makes every
+    // wave's copies visible, and the slot of cell a-1 (processed by all) is refilled.
+    auto step = [&](int a, const uint16_t *kc, const uint16_t *vc, uint16_t *kpf, uint16_t *vpf)
+        __attribute__((always_inline)) {
+        wait_vmem_le<UPW * (NS - 2)>();
+        barrier_no_fence();
+        issue(min(a + NS - 1, nact - 1), kpf, vpf);  // past the end: harmless repeats of the last cell
+        process(a, kc, vc);
+    };
+    if (nact > 0) {
+        issue(0, s_k0, s_v0);
+        issue(min(1, nact - 1), s_k1, s_v1);
+        if constexpr (NS > 2) {
+            issue(min(2, nact - 1), s_k2, s_v2);
+        }
     }
+    for (int a = 0; a < nact; a += NS) {
+        if constexpr (NS > 2) {
+            step(a, s_k0, s_v0, s_k3, s_v3);
+            if (a + 1 >= nact) break;
+            step(a + 1, s_k1, s_v1, s_k0, s_v0);
+            if (a + 2 >= nact) break;
+            step(a + 2, s_k2, s_v2, s_k1, s_v1);
+            if (a + 3 >= nact) break;
+            step(a + 3, s_k3, s_v3, s_k2, s_v2);
+        } else {
+            step(a, s_k0, s_v0, s_k1, s_v1);
+            if (a + 1 >= nact) break;
+            step(a + 1, s_k1, s_v1, s_k0, s_v0);
+        }
+    }
+    wait_vmem();  // no copy into LDS may outlive the work-group
 
     // ---- normalise, RMSNorm over d, mix, write (lane: query col, dims 16*dt + 4*g + r)
     const float l = colsum4(l_part);
