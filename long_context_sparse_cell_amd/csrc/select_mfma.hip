@@ -21,7 +21,11 @@
 //     by K cells for sure; every other cell ("contender") is re-scored exactly
 //     in fp64 and the K best contenders under (score desc, index asc) are the
 //     exact top-K.
-// One workgroup = up to 128 queries of one block, 8 waves x 16 queries.
+// When a query has no more than K contenders, they are its top-K set and no
+// exact score is needed; near-ties (more than K contenders) are re-scored with
+// q and kbar read from global memory. The bf16 split of the pool means is made
+// once per work-group. One workgroup = up to 128 queries of one block, 8 waves
+// x 16 queries, in an XCD-aware order.
 #include <climits>
 
 #include "fsl_internal.h"
@@ -43,16 +47,21 @@ union U16x8s {
     uint16_t h[8];
 };
 
-// carry (v, i) down a list sorted by (v desc, i asc), dropping the last entry
+// carry (v, i) down a list sorted by (v desc, i asc), dropping the last entry.
+// Written with selects rather than a conditional swap: the branchy form with
+// double keys was compiled into wrong code (equal keys lost the index
+// tie-break) by this toolchain at -O3, while this form is exact.
 template <typename F>
 __device__ __forceinline__ void list_insert(F (&lv)[kSelK], int (&li)[kSelK], F v, int i, int K) {
 #pragma unroll
     for (int r = 0; r < kSelK; ++r) {
-        if (r < K && (v > lv[r] || (v == lv[r] && i < li[r]))) {
-            F tv = lv[r]; int ti = li[r];
-            lv[r] = v; li[r] = i;
-            v = tv; i = ti;
-        }
+        const bool sw = r < K && (v > lv[r] || (v == lv[r] && i < li[r]));
+        const F nv = sw ? lv[r] : v;
+        const int ni = sw ? li[r] : i;
+        lv[r] = sw ? v : lv[r];
+        li[r] = sw ? i : li[r];
+        v = nv;
+        i = ni;
     }
 }
 
@@ -74,73 +83,73 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                                                           const float *__restrict__ amax,
                                                           const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
                                                           KParams p, int QW) {
-    constexpr int LD = D + 1;       // fp32 kbar row stride (odd: conflict-free row reads)
-    constexpr int QLD = D + 2;      // bf16 q row stride (odd number of words)
-    extern __shared__ float s_dyn[];                 // [PW][LD] kbar of the pool cells
-    __shared__ uint16_t s_q[kSelQ * QLD];            // the query tile, bf16 bits
+    constexpr int HLD = D + 8;  // bf16 row stride of the split pool means (272 B for d = 128: conflict-free rows)
+    extern __shared__ uint16_t s_dyn[];  // hi rows [ntile*16][HLD], then lo rows
     __shared__ int s_pool[kSelPool];
     __shared__ float s_kn[kSelPool];
     __shared__ float s_a[kSelPool];
-    __shared__ float s_qn[kSelQ];
-    float *s_kb = s_dyn;
 
-    const int h = blockIdx.y;
-    const int64_t q0 = (int64_t)blockIdx.x * QW;
+    const int nqb = (int)((p.N + QW - 1) / QW);
+    const int logical = xcd_remap((int)blockIdx.x, nqb * p.H);
+    const int h = logical / nqb;
+    const int64_t q0 = (int64_t)(logical % nqb) * QW;
     const int64_t b = q0 / p.B;
     const int nq = (int)min((int64_t)QW, p.N - q0);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, g = lane >> 4;
     const int K = p.K;
     const int npool = (int)min((int64_t)p.PW, eligible_cells(p, b));
+    const int ntile = (npool + 15) / 16;
     const int64_t hN = (int64_t)h * p.N;
+    const int64_t hC = (int64_t)h * p.C;
+    uint16_t *s_hi = s_dyn;
+    uint16_t *s_lo = s_dyn + ntile * 16 * HLD;
 
     for (int t = tid; t < npool; t += 512) {
         const int c = pool[((int64_t)h * p.nblk + b) * p.PW + t];
         s_pool[t] = c;
-        s_a[t] = amax[(int64_t)h * p.C + c];
-    }
-    // query tile: 16-byte loads, 8 bf16 per thread per step
-    for (int e = tid; e < nq * (D / 8); e += 512) {
-        const int r = e / (D / 8), x = 8 * (e % (D / 8));
-        const uint4 raw = *reinterpret_cast<const uint4 *>(q + (hN + q0 + r) * D + x);
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) {
-            s_q[r * QLD + x + 2 * t2] = (uint16_t)(w4[t2] & 0xFFFFu);
-            s_q[r * QLD + x + 2 * t2 + 1] = (uint16_t)(w4[t2] >> 16);
-        }
+        s_a[t] = amax[hC + c];
     }
     __syncthreads();
-    // pool cell means: 16-byte loads, 4 floats per thread per step
-    for (int e = tid; e < npool * (D / 4); e += 512) {
+    // pool cell means split once into bf16 head + tail (round to nearest even; rows
+    // past the pool are zero), 4 floats per thread per step
+    for (int e = tid; e < ntile * 16 * (D / 4); e += 512) {
         const int r = e / (D / 4), x = 4 * (e % (D / 4));
-        const float4 f = *reinterpret_cast<const float4 *>(kbar + ((int64_t)h * p.C + s_pool[r]) * D + x);
-        s_kb[r * LD + x] = f.x;
-        s_kb[r * LD + x + 1] = f.y;
-        s_kb[r * LD + x + 2] = f.z;
-        s_kb[r * LD + x + 3] = f.w;
-    }
-    __syncthreads();
-    for (int t = tid; t < npool + nq; t += 512) {
-        float ss = 0.0f;
-        if (t < npool) {
-            for (int x = 0; x < D; ++x) ss += s_kb[t * LD + x] * s_kb[t * LD + x];
-            s_kn[t] = sqrtf(ss);
-        } else {
-            const int r = t - npool;
-            for (int x = 0; x < D; ++x) {
-                const float f = bf16_to_f32(s_q[r * QLD + x]);
-                ss += f * f;
-            }
-            s_qn[r] = sqrtf(ss);
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < npool) f = *reinterpret_cast<const float4 *>(kbar + (hC + s_pool[r]) * D + x);
+        const float fx[4] = {f.x, f.y, f.z, f.w};
+        union { __bf16 b[4]; uint2 u; } hi4, lo4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const __bf16 hb = (__bf16)fx[t];
+            hi4.b[t] = hb;
+            lo4.b[t] = (__bf16)(fx[t] - (float)hb);
         }
+        *reinterpret_cast<uint2 *>(&s_hi[r * HLD + x]) = hi4.u;
+        *reinterpret_cast<uint2 *>(&s_lo[r * HLD + x]) = lo4.u;
+    }
+    // ||kbar_c||: 8 lanes per cell, D/8 elements each
+    for (int e = tid; e < ((npool + 63) / 64) * 512; e += 512) {
+        const int r = e >> 3, part = e & 7;
+        float ss = 0.0f;
+        if (r < npool) {
+            const float *kr = kbar + (hC + s_pool[r]) * D + part * (D / 8);
+#pragma unroll
+            for (int x = 0; x < D / 8; x += 4) {
+                const float4 f = *reinterpret_cast<const float4 *>(kr + x);
+                ss += f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
+            }
+        }
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        if (r < npool && part == 0) s_kn[r] = sqrtf(ss);
     }
     __syncthreads();
 
     const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
     const float sigf = p.sigma[h], lamf = p.lambda[h], rhof = p.rho;
     const float epsc = 1.001f * (7.62939453125e-06f + (float)(4 * D + 8) * 5.9604644775390625e-08f);
-    const int ntile = (npool + 15) / 16;
 
     {  // 8 waves x 16 queries
         const int ql = 16 * wave + col;
@@ -148,10 +157,17 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
         const int qr = qok ? ql : 0;
         const int64_t i = q0 + qr;
         U16x8s bq[D / 32];
+        float qss = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qr) * D + 32 * ks + 8 * g);
-        const float qn = s_qn[qr];
+        for (int ks = 0; ks < D / 32; ++ks) {
+            bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + i) * D + 32 * ks + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = bf16_to_f32(bq[ks].h[e]);
+                qss += f * f;
+            }
+        }
+        const float qn = sqrtf(colsum4(qss));  // the four lanes of a query hold all its d elements
 
         float lb1 = -INFINITY, lb2 = -INFINITY;  // this lane's two largest lower bounds
         // approximate scores, 4 cells of each 16-cell tile per lane (cells 16*ct + 4*g + e)
@@ -164,16 +180,11 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
-                bf16x8 hi, lo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = rowc < npool ? s_kb[rowc * LD + 32 * ks + 8 * g + e] : 0.0f;
-                    const __bf16 hb = (__bf16)x;  // round to nearest even
-                    hi[e] = hb;
-                    lo[e] = (__bf16)(x - (float)hb);
-                }
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq[ks].b, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq[ks].b, acc, 0, 0, 0);
+                U16x8s hi, lo;
+                hi.u = *reinterpret_cast<const uint4 *>(&s_hi[rowc * HLD + 32 * ks + 8 * g]);
+                lo.u = *reinterpret_cast<const uint4 *>(&s_lo[rowc * HLD + 32 * ks + 8 * g]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi.b, bq[ks].b, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.b, bq[ks].b, acc, 0, 0, 0);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -183,7 +194,8 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                 if (pos < npool) {
                     const int c = s_pool[pos];
                     const float argf = sigf * (float)(i - (int64_t)c * p.s) / (2.0f * (float)p.s);
-                    const float gf = argf >= 6.0f ? 1.0f : erff(argf);
+                    float gf = 1.0f;
+                    if (argf < 6.0f) gf = erff(argf);
                     const float la = lamf * s_a[pos];
                     const float bf = la * gf;
                     const float rc = rhof * acc[e];
@@ -217,13 +229,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
         for (int r = 0; r < 8; ++r)
             if (r == K - 1) theta = lv8[r];
 
-        // exact re-scoring of the contenders
-        double exv[kSelK];
-        int exi[kSelK];
-#pragma unroll
-        for (int r = 0; r < kSelK; ++r) { exv[r] = -INFINITY; exi[r] = INT_MAX; }
-        // this lane's contenders as a bitmask over its (tile, e) slots; the wave loops only as
-        // often as its busiest lane has contenders
+        // this lane's contenders as a bitmask over its (tile, e) slots
         uint32_t cmask = 0;
 #pragma unroll
         for (int ct = 0; ct < kSelPool / 16; ++ct) {
@@ -234,25 +240,49 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                 if (pos < npool && sapx[ct][e] + seps[ct][e] >= theta) cmask |= 1u << (4 * ct + e);
             }
         }
+        // At least min(K, pool) cells are contenders. With no more than K of them
+        // the top-K set is certified without exact scores (the output lists the
+        // cells by index); otherwise the contenders are re-scored exactly in fp64.
+        const int ncont = (int)colsum4((float)__popc(cmask));
+        const bool exact = ncont > K;
+        double exv[kSelK];
+        int exi[kSelK];
+#pragma unroll
+        for (int r = 0; r < kSelK; ++r) { exv[r] = -INFINITY; exi[r] = INT_MAX; }
         int maxn = __popc(cmask);
 #pragma unroll
         for (int m2 = 32; m2 > 0; m2 >>= 1) maxn = max(maxn, __shfl_xor(maxn, m2));
-        const uint16_t *qrow = &s_q[qr * QLD];
+        const uint16_t *qg = q + (hN + i) * D;
         for (int t = 0; t < maxn; ++t) {
             if (cmask) {
                 const int slot = __ffs(cmask) - 1;
                 cmask &= cmask - 1;
                 const int pos = 16 * (slot >> 2) + 4 * g + (slot & 3);
                 const int c = s_pool[pos];
-                const float *krow = &s_kb[pos * LD];
-                double content = 0.0;
-#pragma unroll 8
-                for (int x = 0; x < D; ++x)
-                    content = __fma_rn((double)bf16_to_f32(qrow[x]), (double)krow[x], content);
-                const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
-                const double gg = arg >= 6.0 ? 1.0 : erf(arg);
-                const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[pos]), gg);
-                list_insert<double>(exv, exi, __fma_rn(rho, content, bias), c, K);
+                double v = 0.0;  // certified set: equal keys list the cells by index
+                if (exact) {
+                    const float *krow = kbar + (hC + c) * D;
+                    double content = 0.0;
+#pragma unroll 2
+                    for (int x = 0; x < D; x += 8) {
+                        const uint4 qv = *reinterpret_cast<const uint4 *>(qg + x);
+                        const float4 k0 = *reinterpret_cast<const float4 *>(krow + x);
+                        const float4 k1 = *reinterpret_cast<const float4 *>(krow + x + 4);
+                        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+                        const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float qf = __uint_as_float(e & 1 ? (qw[e >> 1] & 0xFFFF0000u) : (qw[e >> 1] << 16));
+                            content = __fma_rn((double)qf, (double)kf[e], content);
+                        }
+                    }
+                    const double arg =
+                        __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
+                    const double gg = arg >= 6.0 ? 1.0 : erf(arg);
+                    const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[pos]), gg);
+                    v = __fma_rn(rho, content, bias);
+                }
+                list_insert<double>(exv, exi, v, c, K);
             }
         }
         list_merge_xor<double>(exv, exi, K, 16);
@@ -274,8 +304,9 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
 hipError_t launch_select_mfma(const void *q, const float *kbar, const float *amax, const int32_t *pool,
                               int32_t *sel, const KParams &p, hipStream_t st) {
     const int QW = p.B <= kSelQ ? p.B : p.B / 2;
-    dim3 grid((unsigned)((p.N + QW - 1) / QW), (unsigned)p.H);
-    const size_t lds = (size_t)(p.PW > 0 ? p.PW : 1) * (p.d + 1) * sizeof(float);
+    dim3 grid((unsigned)(((p.N + QW - 1) / QW) * p.H));
+    const int rows = (p.PW + 15) / 16 * 16;
+    const size_t lds = (size_t)(rows > 0 ? rows : 16) * (p.d + 8) * sizeof(uint16_t) * 2;
     if (p.d == 64)
         hipLaunchKernelGGL((select_mfma_kernel<64>), grid, dim3(512), lds, st, (const uint16_t *)q, kbar, amax, pool,
                            sel, p, QW);
