@@ -171,7 +171,8 @@ typedef struct fsl_workspace_layout {
     size_t o_win;   /* float [H][N][d]            window-branch output */
     size_t rope_abs;/* float2 (cos, sin) by absolute position, two levels (bf16 only) */
     size_t kt;      /* fp16 [H][Np][d] RoPE-rotated keys, Np = 64 ceil(N/64) (bf16 only) */
-    size_t vt;      /* fp16 [H][Np/16][d][16] values transposed per 16 tokens (bf16 only) */
+    size_t vt;      /* fp16 [H][Np/32][d][32] values transposed per 32 tokens (bf16 only) */
+    size_t fixups;  /* uint32 near-tie query list of the bf16 scoring (bf16 only) */
     size_t total;   /* bytes; equals fsl_workspace_bytes */
 } fsl_workspace_layout;
 int fsl_workspace_views(const fsl_params *p, fsl_workspace_layout *out);

@@ -57,25 +57,30 @@ KParams kparams(const fsl_params *p) {
     return k;
 }
 
-fsl_workspace_layout layout(const KParams &k) {
+// full: the forward's arrays; otherwise only what the decode prefill uses (cell
+// statistics, pools and the prune-scan lists)
+fsl_workspace_layout layout(const KParams &k, bool full = true) {
     fsl_workspace_layout L;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
     L.kbar = take((size_t)k.H * k.C * k.d * sizeof(float));
     L.amax = take((size_t)k.H * k.C * sizeof(float));
     L.pool = take((size_t)k.H * k.nblk * k.PW * sizeof(int32_t));
-    L.sel = take((size_t)k.H * k.N * k.K * sizeof(int32_t));
-    L.rope = take((size_t)k.rope_n * (k.d / 2) * sizeof(float2));
+    L.sel = take(full ? (size_t)k.H * k.N * k.K * sizeof(int32_t) : 0);
+    L.rope = take(full ? (size_t)k.rope_n * (k.d / 2) * sizeof(float2) : 0);
     L.scan_a = take((size_t)scan_lists(k) * kChunk * sizeof(float));
     L.scan_i = take((size_t)scan_lists(k) * kChunk * sizeof(int32_t));
-    L.o_win = take((size_t)k.H * k.N * k.d * sizeof(float));
-    const bool bf = k.dtype == FSL_BF16;  // the prepared fp16 keys/values serve the bf16 kernels only
+    L.o_win = take(full ? (size_t)k.H * k.N * k.d * sizeof(float) : 0);
+    const bool bf = full && k.dtype == FSL_BF16;  // prepared fp16 keys/values, near-tie list: bf16 forward only
     L.rope_abs = take(bf ? (size_t)(rope_abs_rows_hi(k) + kRopeSpan) * (k.d / 2) * sizeof(float2) : 0);
     L.kt = take(bf ? (size_t)k.H * kt_head_elems(k) * sizeof(uint16_t) : 0);
     L.vt = take(bf ? (size_t)k.H * vt_head_elems(k) * sizeof(uint16_t) : 0);
+    L.fixups = take(bf ? (size_t)fix_words(k) * sizeof(uint32_t) : 0);
     L.total = off;
     return L;
 }
+
+bool k_has_fix(const fsl_workspace_layout &L) { return L.total > L.fixups; }
 
 Work carve(void *ws, const fsl_workspace_layout &L) {
     char *b = (char *)ws;
@@ -91,6 +96,7 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
     w.rope_abs = (float2 *)(b + L.rope_abs);
     w.kt = (uint16_t *)(b + L.kt);
     w.vt = (uint16_t *)(b + L.vt);
+    w.fix = k_has_fix(L) ? (uint32_t *)(b + L.fixups) : nullptr;
     return w;
 }
 
@@ -193,8 +199,9 @@ int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_
     const Work w = carve(ws, L);
     hipError_t e = launch_prune(amax, pool, w, k, stream);
     if (e == hipSuccess)
-        e = k.dtype == FSL_BF16 ? launch_select_mfma(q, kbar, amax, pool, sel, k, stream)
+        e = k.dtype == FSL_BF16 ? launch_select_mfma(q, kbar, amax, pool, sel, w.fix, k, stream)
                                 : launch_select(q, kbar, amax, pool, sel, k, stream);
+    if (e == hipSuccess && k.dtype == FSL_BF16) e = launch_select_fixup(q, kbar, amax, pool, sel, w.fix, k, stream);
     return hip_status(e);
 }
 
@@ -222,8 +229,11 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
     if (e == hipSuccess) e = mark(launch_cell_stats(k, w.kbar, w.amax, kp, stream));
     if (e == hipSuccess) e = mark(launch_prune(w.amax, w.pool, w, kp, stream));
     if (e == hipSuccess)
-        e = mark(kp.dtype == FSL_BF16 ? launch_select_mfma(q, w.kbar, w.amax, w.pool, w.sel, kp, stream)
-                                      : launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
+        e = mark(kp.dtype == FSL_BF16
+                     ? (launch_select_mfma(q, w.kbar, w.amax, w.pool, w.sel, w.fix, kp, stream) == hipSuccess
+                            ? launch_select_fixup(q, w.kbar, w.amax, w.pool, w.sel, w.fix, kp, stream)
+                            : hipErrorLaunchFailure)
+                     : launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
     const bool bf = kp.dtype == FSL_BF16;
     if (e == hipSuccess)
         e = mark(bf ? launch_kv_prep(k, v, w.kt, w.vt, w.rope_abs, kp, stream) : launch_rope_table(w.rope, kp, stream));
@@ -272,7 +282,7 @@ size_t fsl_decode_prefill_workspace_bytes(const fsl_params *p, int64_t prefix_le
     if (check_decode(p) != FSL_OK || prefix_len < 1 || prefix_len >= (int64_t(1) << 31) - p->B) return 0;
     fsl_params q = *p;
     q.N = prefix_len + p->B;
-    return layout(kparams(&q)).total;
+    return layout(kparams(&q), false).total;
 }
 
 int fsl_decode_prefill(void *state, size_t state_bytes, int32_t seq, const void *k_prefix, const void *v_prefix,
@@ -287,7 +297,7 @@ int fsl_decode_prefill(void *state, size_t state_bytes, int32_t seq, const void 
     if (ws_bytes < fsl_decode_prefill_workspace_bytes(p, prefix_len)) return FSL_E_WORKSPACE;
     fsl_params qa = *p;
     qa.N = prefix_len + p->B;
-    const Work w = carve(ws, layout(kparams(&qa)));
+    const Work w = carve(ws, layout(kparams(&qa), false));
     fsl_params qs = *p;
     qs.N = prefix_len;
     KParams ks = kparams(&qs);            // statistics over the prefix's complete cells

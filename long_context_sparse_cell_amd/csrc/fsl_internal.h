@@ -39,7 +39,28 @@ struct Work {
     float2 *rope_abs;  // absolute-position (cos, sin): ceil(N/64) rows of 64a, then 64 rows of b
     uint16_t *kt;      // fp16 [H][Np][d] rotated keys, Np = 64 ceil(N/64)
     uint16_t *vt;      // fp16 [H][Np/32][d][32] values, transposed per 32-token group (vt_pos order)
+    // queries whose certified filter left more than K contenders (bf16 scoring):
+    // one region of kFixRegion entries per scoring work-group (fix_region), and
+    // the number of entries each region holds at fix[0 .. fix_regions)
+    uint32_t *fix;
 };
+
+constexpr int kFixRegion = 128;  // entries per region (queries per scoring work-group)
+constexpr int kFixWords = 6;     // head, row, then the contender masks of lane groups 0..3
+// scoring work-groups: (head, up to 128 queries of one block)
+__host__ __device__ inline int64_t fix_regions(const KParams &p) {
+    const int qw = p.B <= kFixRegion ? p.B : p.B / 2;
+    return (int64_t)p.H * ((p.N + qw - 1) / qw);
+}
+__host__ __device__ inline int64_t fix_words(const KParams &p) {
+    return (fix_regions(p) + 63) / 64 * 64 + fix_regions(p) * kFixRegion * kFixWords;
+}
+__host__ __device__ inline uint32_t *fix_region(uint32_t *fix, const KParams &p, int64_t r) {
+    return fix + (fix_regions(p) + 63) / 64 * 64 + r * kFixRegion * kFixWords;
+}
+__host__ __device__ inline const uint32_t *fix_region(const uint32_t *fix, const KParams &p, int64_t r) {
+    return fix + (fix_regions(p) + 63) / 64 * 64 + r * kFixRegion * kFixWords;
+}
 
 constexpr int kChunk = 64;    // cells per prune-scan chunk (one wave)
 constexpr int kGroup = 16;    // chunks per prune-scan group
@@ -278,7 +299,9 @@ hipError_t launch_prune(const float *amax, int32_t *pool, const Work &w, const K
 hipError_t launch_select(const void *q, const float *kbar, const float *amax, const int32_t *pool,
                          int32_t *sel, const KParams &p, hipStream_t st);
 hipError_t launch_select_mfma(const void *q, const float *kbar, const float *amax, const int32_t *pool,
-                              int32_t *sel, const KParams &p, hipStream_t st);
+                              int32_t *sel, uint32_t *fix, const KParams &p, hipStream_t st);
+hipError_t launch_select_fixup(const void *q, const float *kbar, const float *amax, const int32_t *pool,
+                               int32_t *sel, const uint32_t *fix, const KParams &p, hipStream_t st);
 hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st);
 hipError_t launch_window(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
                          const KParams &p, hipStream_t st);

@@ -14,13 +14,11 @@
 //        |content - content~| <= ||q|| ||kbar_c|| (2^-17 + (4d+8) 2^-24)
 //     (Cauchy-Schwarz bounds the absolute sum). The fp32 bias and the final
 //     fp32 additions get their own rounding terms; the total is doubled.
-//  2. Per query, each of its 4 lanes keeps its two largest lower bounds
-//     s~ - eps; theta is the K-th largest of those 8 values (they belong to 8
-//     distinct cells, so theta is at most the K-th largest lower bound over
-//     all cells). A cell whose upper bound s~ + eps is below theta is beaten
-//     by K cells for sure; every other cell ("contender") is re-scored exactly
-//     in fp64 and the K best contenders under (score desc, index asc) are the
-//     exact top-K.
+//  2. Per query, each of its 4 lanes keeps its KL >= K largest lower bounds
+//     s~ - eps and the lanes merge them, so theta is exactly the K-th largest
+//     lower bound over all cells. A cell whose upper bound s~ + eps is below
+//     theta is beaten by K cells for sure; every other cell is a contender, and
+//     the K best contenders under (score desc, index asc) are the exact top-K.
 // When a query has no more than K contenders, they are its top-K set and no
 // exact score is needed; near-ties (more than K contenders) are re-scored with
 // q and kbar read from global memory. The bf16 split of the pool means is made
@@ -47,47 +45,19 @@ union U16x8s {
     uint16_t h[8];
 };
 
-// carry (v, i) down a list sorted by (v desc, i asc), dropping the last entry.
-// Written with selects rather than a conditional swap: the branchy form with
-// double keys was compiled into wrong code (equal keys lost the index
-// tie-break) by this toolchain at -O3, while this form is exact.
-template <typename F>
-__device__ __forceinline__ void list_insert(F (&lv)[kSelK], int (&li)[kSelK], F v, int i, int K) {
-#pragma unroll
-    for (int r = 0; r < kSelK; ++r) {
-        const bool sw = r < K && (v > lv[r] || (v == lv[r] && i < li[r]));
-        const F nv = sw ? lv[r] : v;
-        const int ni = sw ? li[r] : i;
-        lv[r] = sw ? v : lv[r];
-        li[r] = sw ? i : li[r];
-        v = nv;
-        i = ni;
-    }
-}
-
-template <typename F>
-__device__ __forceinline__ void list_merge_xor(F (&lv)[kSelK], int (&li)[kSelK], int K, int mask) {
-    F pv[kSelK];
-    int pi[kSelK];
-#pragma unroll
-    for (int r = 0; r < kSelK; ++r) { pv[r] = __shfl_xor(lv[r], mask); pi[r] = __shfl_xor(li[r], mask); }
-#pragma unroll
-    for (int r = 0; r < kSelK; ++r)
-        if (r < K) list_insert<F>(lv, li, pv[r], pi[r], K);
-}
-
 }  // namespace
 
-template <int D>
+template <int D, int KL>
 __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__restrict__ q, const float *__restrict__ kbar,
                                                           const float *__restrict__ amax,
                                                           const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
-                                                          KParams p, int QW) {
+                                                          uint32_t *__restrict__ fix, KParams p, int QW) {
     constexpr int HLD = D + 8;  // bf16 row stride of the split pool means (272 B for d = 128: conflict-free rows)
     extern __shared__ uint16_t s_dyn[];  // hi rows [ntile*16][HLD], then lo rows
     __shared__ int s_pool[kSelPool];
-    __shared__ float s_kn[kSelPool];
-    __shared__ float s_a[kSelPool];
+    // per pool cell: lambda a_c, |rho| ||kbar_c|| epsc, |lambda a_c| 2e-6, and c s (int bits)
+    __shared__ float4 s_cf[kSelPool];
+    __shared__ int s_nfix;  // near-tie queries of this work-group
 
     const int nqb = (int)((p.N + QW - 1) / QW);
     const int logical = xcd_remap((int)blockIdx.x, nqb * p.H);
@@ -105,18 +75,29 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
     uint16_t *s_hi = s_dyn;
     uint16_t *s_lo = s_dyn + ntile * 16 * HLD;
 
-    for (int t = tid; t < npool; t += 512) {
-        const int c = pool[((int64_t)h * p.nblk + b) * p.PW + t];
-        s_pool[t] = c;
-        s_a[t] = amax[hC + c];
-    }
-    __syncthreads();
-    // pool cell means split once into bf16 head + tail (round to nearest even; rows
-    // past the pool are zero), 4 floats per thread per step
+    const float sigf = p.sigma[h], lamf = p.lambda[h], rhof = p.rho;
+    const float epsc = 1.001f * (7.62939453125e-06f + (float)(4 * D + 8) * 5.9604644775390625e-08f);
+    const float karg = sigf / (2.0f * (float)p.s);  // erf argument per token of distance
+
+    // this wave's 16 queries, loaded first so that their latency overlaps the setup
+    const int ql = 16 * wave + col;
+    const bool qok = ql < nq;
+    const int qr = qok ? ql : 0;
+    const int64_t i = q0 + qr;
+    U16x8s bq[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + i) * D + 32 * ks + 8 * g);
+
+    // ---- setup, one pass: pool row r by D/4 consecutive threads (4 floats each): its
+    // mean split into bf16 head + tail (round to nearest even; rows past the pool are
+    // zero), its norm, and the per-cell constants of the bound
+    if (tid == 0) s_nfix = 0;
     for (int e = tid; e < ntile * 16 * (D / 4); e += 512) {
         const int r = e / (D / 4), x = 4 * (e % (D / 4));
+        const bool ok = r < npool;
+        const int c = ok ? pool[((int64_t)h * p.nblk + b) * p.PW + r] : 0;
         float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < npool) f = *reinterpret_cast<const float4 *>(kbar + (hC + s_pool[r]) * D + x);
+        if (ok) f = *reinterpret_cast<const float4 *>(kbar + (hC + c) * D + x);
         const float fx[4] = {f.x, f.y, f.z, f.w};
         union { __bf16 b[4]; uint2 u; } hi4, lo4;
 #pragma unroll
@@ -127,49 +108,35 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
         }
         *reinterpret_cast<uint2 *>(&s_hi[r * HLD + x]) = hi4.u;
         *reinterpret_cast<uint2 *>(&s_lo[r * HLD + x]) = lo4.u;
-    }
-    // ||kbar_c||: 8 lanes per cell, D/8 elements each
-    for (int e = tid; e < ((npool + 63) / 64) * 512; e += 512) {
-        const int r = e >> 3, part = e & 7;
-        float ss = 0.0f;
-        if (r < npool) {
-            const float *kr = kbar + (hC + s_pool[r]) * D + part * (D / 8);
+        float ss = f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
 #pragma unroll
-            for (int x = 0; x < D / 8; x += 4) {
-                const float4 f = *reinterpret_cast<const float4 *>(kr + x);
-                ss += f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
-            }
+        for (int m2 = 1; m2 < D / 4; m2 <<= 1) ss += __shfl_xor(ss, m2);
+        if (ok && x == 0) {
+            const float la = lamf * amax[hC + c];
+            s_pool[r] = c;
+            s_cf[r] = make_float4(la, fabsf(rhof) * sqrtf(ss) * epsc, fabsf(la) * 2e-6f, __int_as_float(c * p.s));
         }
-        ss += __shfl_xor(ss, 1);
-        ss += __shfl_xor(ss, 2);
-        ss += __shfl_xor(ss, 4);
-        if (r < npool && part == 0) s_kn[r] = sqrtf(ss);
     }
     __syncthreads();
-
-    const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
-    const float sigf = p.sigma[h], lamf = p.lambda[h], rhof = p.rho;
-    const float epsc = 1.001f * (7.62939453125e-06f + (float)(4 * D + 8) * 5.9604644775390625e-08f);
+    // The erf factor is 1 (to fp32 and fp64 rounding) once its argument reaches 6. The
+    // pool is ascending and every query of the work-group is at or after q0, so if the
+    // last pool cell is that far from q0 no query needs erf at all.
+    const bool need_erf = npool > 0 && !((float)((int)q0 - s_pool[npool - 1] * p.s) * karg >= 6.0f);
 
     {  // 8 waves x 16 queries
-        const int ql = 16 * wave + col;
-        const bool qok = ql < nq;
-        const int qr = qok ? ql : 0;
-        const int64_t i = q0 + qr;
-        U16x8s bq[D / 32];
         float qss = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + i) * D + 32 * ks + 8 * g);
+        for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float f = bf16_to_f32(bq[ks].h[e]);
                 qss += f * f;
             }
-        }
         const float qn = sqrtf(colsum4(qss));  // the four lanes of a query hold all its d elements
 
-        float lb1 = -INFINITY, lb2 = -INFINITY;  // this lane's two largest lower bounds
+        float lbk[KL];  // this lane's KL largest lower bounds, descending
+#pragma unroll
+        for (int r = 0; r < KL; ++r) lbk[r] = -INFINITY;
         // approximate scores, 4 cells of each 16-cell tile per lane (cells 16*ct + 4*g + e)
         float sapx[kSelPool / 16][4];
         float seps[kSelPool / 16][4];
@@ -192,42 +159,52 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                 sapx[ct][e] = -INFINITY;
                 seps[ct][e] = 0.0f;
                 if (pos < npool) {
-                    const int c = s_pool[pos];
-                    const float argf = sigf * (float)(i - (int64_t)c * p.s) / (2.0f * (float)p.s);
-                    float gf = 1.0f;
-                    if (argf < 6.0f) gf = erff(argf);
-                    const float la = lamf * s_a[pos];
-                    const float bf = la * gf;
+                    const float4 cf = s_cf[pos];
+                    float bf = cf.x;  // lambda a_c times the erf factor 1
+                    if (need_erf) {
+                        const float argf = (float)((int)i - __float_as_int(cf.w)) * karg;
+                        if (argf < 6.0f) bf = cf.x * erff(argf);
+                    }
                     const float rc = rhof * acc[e];
                     const float sv = rc + bf;
-                    float ev = fabsf(rhof) * qn * s_kn[pos] * epsc + fabsf(la) * 2e-6f +
-                               (fabsf(rc) + fabsf(bf)) * 2.384185791015625e-07f + 1e-30f;
-                    ev *= 2.0f;
+                    const float ev =
+                        2.0f * (fmaf(qn, cf.y, cf.z) + (fabsf(rc) + fabsf(bf)) * 2.384185791015625e-07f + 1e-30f);
                     sapx[ct][e] = sv;
                     seps[ct][e] = ev;
-                    const float lb = sv - ev;
-                    lb2 = fmaxf(lb2, fminf(lb1, lb));
-                    lb1 = fmaxf(lb1, lb);
+                    float x = sv - ev;
+#pragma unroll
+                    for (int r = 0; r < KL; ++r) {
+                        const float hi = fmaxf(lbk[r], x);
+                        x = fminf(lbk[r], x);
+                        lbk[r] = hi;
+                    }
                 }
             }
         }
-        float lv8[8];
-        lv8[0] = lb1; lv8[1] = lb2;
-        lv8[2] = __shfl_xor(lb1, 16); lv8[3] = __shfl_xor(lb2, 16);
-        lv8[4] = __shfl_xor(lb1, 32); lv8[5] = __shfl_xor(lb2, 32);
-        lv8[6] = __shfl_xor(lb1, 48); lv8[7] = __shfl_xor(lb2, 48);
-        // sort descending (odd-even transposition, 8 rounds) and take the K-th
+        // merge with the lanes of the same query column: reversing the partner's list
+        // and taking elementwise maxima keeps the KL largest of both as a bitonic
+        // sequence, which a half-cleaner network sorts back to descending order
 #pragma unroll
-        for (int rnd = 0; rnd < 8; ++rnd)
+        for (int m2 = 16; m2 <= 32; m2 <<= 1) {
+            float pl[KL];
 #pragma unroll
-            for (int a = rnd & 1; a + 1 < 8; a += 2) {
-                const float hi2 = fmaxf(lv8[a], lv8[a + 1]), lo2 = fminf(lv8[a], lv8[a + 1]);
-                lv8[a] = hi2; lv8[a + 1] = lo2;
-            }
+            for (int r = 0; r < KL; ++r) pl[r] = __shfl_xor(lbk[r], m2);
+#pragma unroll
+            for (int r = 0; r < KL; ++r) lbk[r] = fmaxf(lbk[r], pl[KL - 1 - r]);
+#pragma unroll
+            for (int st = KL / 2; st > 0; st >>= 1)
+#pragma unroll
+                for (int r = 0; r < KL; ++r)
+                    if ((r & st) == 0) {
+                        const float hi = fmaxf(lbk[r], lbk[r + st]), lo = fminf(lbk[r], lbk[r + st]);
+                        lbk[r] = hi;
+                        lbk[r + st] = lo;
+                    }
+        }
         float theta = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            if (r == K - 1) theta = lv8[r];
+        for (int r = 0; r < KL; ++r)
+            if (r == K - 1) theta = lbk[r];
 
         // this lane's contenders as a bitmask over its (tile, e) slots
         uint32_t cmask = 0;
@@ -241,78 +218,195 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
             }
         }
         // At least min(K, pool) cells are contenders. With no more than K of them
-        // the top-K set is certified without exact scores (the output lists the
-        // cells by index); otherwise the contenders are re-scored exactly in fp64.
+        // the top-K set is certified without exact scores: the output lists the
+        // contenders in pool (= ascending cell) order. Otherwise (a near-tie) the
+        // query and its contender masks go to the fix-up list, which re-scores the
+        // contenders exactly in fp64 (select_fixup_kernel).
         const int ncont = (int)colsum4((float)__popc(cmask));
-        const bool exact = ncont > K;
-        double exv[kSelK];
-        int exi[kSelK];
+        uint32_t m[4];
 #pragma unroll
-        for (int r = 0; r < kSelK; ++r) { exv[r] = -INFINITY; exi[r] = INT_MAX; }
-        int maxn = __popc(cmask);
+        for (int gg = 0; gg < 4; ++gg) m[gg] = (uint32_t)__shfl((int)cmask, col + 16 * gg);
+        if (qok && g == 0) {
+            if (ncont > K) {
+                const int slot = atomicAdd(&s_nfix, 1);
+                uint32_t *e = fix_region(fix, p, logical) + (size_t)slot * kFixWords;
+                e[0] = (uint32_t)h;
+                e[1] = (uint32_t)i;
 #pragma unroll
-        for (int m2 = 32; m2 > 0; m2 >>= 1) maxn = max(maxn, __shfl_xor(maxn, m2));
-        const uint16_t *qg = q + (hN + i) * D;
-        for (int t = 0; t < maxn; ++t) {
-            if (cmask) {
-                const int slot = __ffs(cmask) - 1;
-                cmask &= cmask - 1;
-                const int pos = 16 * (slot >> 2) + 4 * g + (slot & 3);
-                const int c = s_pool[pos];
-                double v = 0.0;  // certified set: equal keys list the cells by index
-                if (exact) {
-                    const float *krow = kbar + (hC + c) * D;
-                    double content = 0.0;
-#pragma unroll 2
-                    for (int x = 0; x < D; x += 8) {
-                        const uint4 qv = *reinterpret_cast<const uint4 *>(qg + x);
-                        const float4 k0 = *reinterpret_cast<const float4 *>(krow + x);
-                        const float4 k1 = *reinterpret_cast<const float4 *>(krow + x + 4);
-                        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-                        const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                for (int gg = 0; gg < 4; ++gg) e[2 + gg] = m[gg];
+            } else {
+                // contender bitmap over pool positions 16 ct + 4 g + e
+                uint64_t bm_lo = 0, bm_hi = 0;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float qf = __uint_as_float(e & 1 ? (qw[e >> 1] & 0xFFFF0000u) : (qw[e >> 1] << 16));
-                            content = __fma_rn((double)qf, (double)kf[e], content);
-                        }
+                for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+                    for (int ct = 0; ct < kSelPool / 16; ++ct) {
+                        const uint64_t nib = (uint64_t)((m[gg] >> (4 * ct)) & 15u);
+                        const int at = 16 * ct + 4 * gg;
+                        if (at < 64) bm_lo |= nib << at;
+                        else bm_hi |= nib << (at - 64);
                     }
-                    const double arg =
-                        __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
-                    const double gg = arg >= 6.0 ? 1.0 : erf(arg);
-                    const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[pos]), gg);
-                    v = __fma_rn(rho, content, bias);
+                int32_t *o = sel + (hN + i) * K;
+#pragma unroll
+                for (int r = 0; r < kSelK; ++r) {
+                    if (r >= K) break;
+                    int pos = -1;
+                    if (bm_lo) {
+                        pos = __ffsll((unsigned long long)bm_lo) - 1;
+                        bm_lo &= bm_lo - 1;
+                    } else if (bm_hi) {
+                        pos = 64 + __ffsll((unsigned long long)bm_hi) - 1;
+                        bm_hi &= bm_hi - 1;
+                    }
+                    o[r] = pos >= 0 ? s_pool[pos] : -1;
                 }
-                list_insert<double>(exv, exi, v, c, K);
             }
         }
-        list_merge_xor<double>(exv, exi, K, 16);
-        list_merge_xor<double>(exv, exi, K, 32);
-        if (qok && g == 0) {
+    }
+    __syncthreads();
+    if (tid == 0) fix[logical] = (uint32_t)s_nfix;
+}
+
+// Exact re-scoring of the near-tie queries listed by select_mfma_kernel: one
+// wave per scoring work-group's region, one query at a time; lane l scores the contenders at
+// pool positions l and 64 + l with the fp64 fma chain of the oracle, then the
+// wave picks the K best by (score desc, cell asc) and lists them by cell.
+// Comparisons are written as selects: a conditional-swap list insert with
+// double keys was compiled into wrong code (equal keys lost the index
+// tie-break) by this toolchain at -O3.
+template <int D>
+__global__ __launch_bounds__(64) void select_fixup_kernel(const uint16_t *__restrict__ q,
+                                                           const float *__restrict__ kbar,
+                                                           const float *__restrict__ amax,
+                                                           const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
+                                                           const uint32_t *__restrict__ fix, KParams p) {
+    const int64_t region = blockIdx.x;
+    const uint32_t n = fix[region];
+    const int lane = threadIdx.x & 63;
+    for (uint32_t j = 0; j < n; ++j) {
+        const uint32_t *e = fix_region(fix, p, region) + (size_t)j * kFixWords;
+        const int h = (int)e[0];
+        const int64_t i = (int64_t)e[1];
+        uint64_t bm_lo = 0, bm_hi = 0;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            const uint32_t m = e[2 + gg];
+#pragma unroll
+            for (int ct = 0; ct < kSelPool / 16; ++ct) {
+                const uint64_t nib = (uint64_t)((m >> (4 * ct)) & 15u);
+                const int at = 16 * ct + 4 * gg;
+                if (at < 64) bm_lo |= nib << at;
+                else bm_hi |= nib << (at - 64);
+            }
+        }
+        const int64_t b = i / p.B;
+        const int32_t *prow = pool + ((int64_t)h * p.nblk + b) * p.PW;
+        const uint16_t *qg = q + ((int64_t)h * p.N + i) * D;
+        const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+        // this lane's (up to two) contenders, best first
+        double v0 = -INFINITY, v1 = -INFINITY;
+        int c0 = INT_MAX, c1 = INT_MAX;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint64_t bm = half ? bm_hi : bm_lo;
+            if (!((bm >> lane) & 1ull)) continue;
+            const int c = prow[64 * half + lane];
+            const float *krow = kbar + ((int64_t)h * p.C + c) * D;
+            double content = 0.0;
+            // 32 elements per step, all loads of a step issued before its fma chain
+            for (int x0 = 0; x0 < D; x0 += 32) {
+                uint4 qv[4];
+                float4 kv[8];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) qv[u] = *reinterpret_cast<const uint4 *>(qg + x0 + 8 * u);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) kv[u] = *reinterpret_cast<const float4 *>(krow + x0 + 4 * u);
+#pragma unroll
+                for (int t = 0; t < 32; ++t) {
+                    const uint4 w4 = qv[t >> 3];
+                    const uint32_t wd = (t & 7) < 2 ? w4.x : (t & 7) < 4 ? w4.y : (t & 7) < 6 ? w4.z : w4.w;
+                    const float qf = __uint_as_float(t & 1 ? (wd & 0xFFFF0000u) : (wd << 16));
+                    const float4 k4 = kv[t >> 2];
+                    const float kf = (t & 3) == 0 ? k4.x : (t & 3) == 1 ? k4.y : (t & 3) == 2 ? k4.z : k4.w;
+                    content = __fma_rn((double)qf, (double)kf, content);
+                }
+            }
+            const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
+            const double gg = arg >= 6.0 ? 1.0 : erf(arg);
+            const double bias = __dmul_rn(__dmul_rn(lam, (double)amax[(int64_t)h * p.C + c]), gg);
+            const double v = __fma_rn(rho, content, bias);
+            // pool positions ascend with the cell, so the second candidate has the larger cell
+            const bool first = v > v0 || (v == v0 && c < c0);
+            v1 = first ? v0 : v;
+            c1 = first ? c0 : c;
+            v0 = first ? v : v0;
+            c0 = first ? c : c0;
+        }
+        int res[kSelK];
+#pragma unroll
+        for (int r = 0; r < kSelK; ++r) {
+            double bv = v0;
+            int bc = c0;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ov = __shfl_xor(bv, off);
+                const int oc = __shfl_xor(bc, off);
+                const bool take = ov > bv || (ov == bv && oc < bc);
+                bv = take ? ov : bv;
+                bc = take ? oc : bc;
+            }
+            res[r] = (r < p.K && bc != INT_MAX) ? bc : INT_MAX;
+            const bool pop = bc != INT_MAX && c0 == bc;
+            v0 = pop ? v1 : v0;
+            c0 = pop ? c1 : c0;
+            v1 = pop ? -INFINITY : v1;
+            c1 = pop ? INT_MAX : c1;
+        }
+        if (lane == 0) {
 #pragma unroll
             for (int x = 0; x < kSelK; ++x)
 #pragma unroll
-                for (int y = 0; y + 1 < kSelK - x; ++y)
-                    if (exi[y] > exi[y + 1]) { int t2 = exi[y]; exi[y] = exi[y + 1]; exi[y + 1] = t2; }
-            int32_t *o = sel + (hN + i) * K;
+                for (int y = 0; y + 1 < kSelK - x; ++y) {
+                    const bool sw = res[y] > res[y + 1];
+                    const int lo2 = sw ? res[y + 1] : res[y], hi2 = sw ? res[y] : res[y + 1];
+                    res[y] = lo2;
+                    res[y + 1] = hi2;
+                }
+            int32_t *o = sel + ((int64_t)h * p.N + i) * p.K;
 #pragma unroll
             for (int r = 0; r < kSelK; ++r)
-                if (r < K) o[r] = exi[r] == INT_MAX ? -1 : exi[r];
+                if (r < p.K) o[r] = res[r] == INT_MAX ? -1 : res[r];
         }
     }
 }
 
+hipError_t launch_select_fixup(const void *q, const float *kbar, const float *amax, const int32_t *pool,
+                               int32_t *sel, const uint32_t *fix, const KParams &p, hipStream_t st) {
+    const dim3 grid((unsigned)fix_regions(p)), block(64);
+    if (p.d == 64)
+        hipLaunchKernelGGL((select_fixup_kernel<64>), grid, block, 0, st, (const uint16_t *)q, kbar, amax, pool, sel,
+                           fix, p);
+    else
+        hipLaunchKernelGGL((select_fixup_kernel<128>), grid, block, 0, st, (const uint16_t *)q, kbar, amax, pool,
+                           sel, fix, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_select_mfma(const void *q, const float *kbar, const float *amax, const int32_t *pool,
-                              int32_t *sel, const KParams &p, hipStream_t st) {
+                              int32_t *sel, uint32_t *fix, const KParams &p, hipStream_t st) {
     const int QW = p.B <= kSelQ ? p.B : p.B / 2;
     dim3 grid((unsigned)(((p.N + QW - 1) / QW) * p.H));
     const int rows = (p.PW + 15) / 16 * 16;
     const size_t lds = (size_t)(rows > 0 ? rows : 16) * (p.d + 8) * sizeof(uint16_t) * 2;
-    if (p.d == 64)
-        hipLaunchKernelGGL((select_mfma_kernel<64>), grid, dim3(512), lds, st, (const uint16_t *)q, kbar, amax, pool,
-                           sel, p, QW);
-    else
-        hipLaunchKernelGGL((select_mfma_kernel<128>), grid, dim3(512), lds, st, (const uint16_t *)q, kbar, amax, pool,
-                           sel, p, QW);
+#define FSL_SEL(DD, KK)                                                                                           \
+    hipLaunchKernelGGL((select_mfma_kernel<DD, KK>), grid, dim3(512), lds, st, (const uint16_t *)q, kbar, amax, pool, \
+                       sel, fix, p, QW)
+    if (p.d == 64) {
+        if (p.K <= 4) FSL_SEL(64, 4); else FSL_SEL(64, 8);
+    } else {
+        if (p.K <= 4) FSL_SEL(128, 4); else FSL_SEL(128, 8);
+    }
+#undef FSL_SEL
     return hipGetLastError();
 }
 

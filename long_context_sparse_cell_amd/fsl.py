@@ -40,7 +40,7 @@ class Params(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win", "rope_abs", "kt", "vt",
-                                      "total")]
+                                      "fixups", "total")]
 
 
 _lib = None
