@@ -11,8 +11,9 @@
 // (fp16, transposed per 32-token group in vt_pos order, from kv_prep.hip; a
 // 16-token cell brings its whole group) are copied from global memory straight
 // into LDS (global_load_lds, 16 bytes per lane) through a ring of one-cell
-// stages (named arrays, so the compiler can tell copies from reads), several
-// cells ahead of the one being multiplied. The copy picks which
+// slots (named arrays, so the compiler can tell copies from reads) used two
+// cells per barrier, the next pair in flight while one pair is multiplied. The
+// copy picks which
 // 16-byte piece each lane fetches so that key rows keep chunk c at
 // c ^ swz_key(row) and value rows keep piece g at g ^ swz_val(dim), which
 // spreads the MFMA operand reads over the LDS banks. Work-groups run in an
@@ -266,34 +267,40 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
             }
     };
 
-    // ---- ring of NS one-cell stages: while cell a is multiplied, cells a+1 .. a+NS-1
-    // are in flight. Before cell a: this wave's copies of it are done once at most
-    // the NS-2 younger cells' copies are outstanding; the barrier then makes every
-    // wave's copies visible, and the slot of cell a-1 (processed by all) is refilled.
-    auto step = [&](int a, const uint16_t *kc, const uint16_t *vc, uint16_t *kpf, uint16_t *vpf)
-        __attribute__((always_inline)) {
-        wait_vmem_le<UPW * (NS - 2)>();
-        barrier_no_fence();
-        issue(min(a + NS - 1, nact - 1), kpf, vpf);  // past the end: harmless repeats of the last cell
-        process(a, kc, vc);
-    };
-    if (nact > 0) {
-        issue(0, s_k0, s_v0);
-        issue(min(1, nact - 1), s_k1, s_v1);
-        if constexpr (NS > 2) {
-            issue(min(2, nact - 1), s_k2, s_v2);
+    // ---- ring of NS one-cell slots, used two cells at a time: while cells a, a+1 are
+    // multiplied, a+2 and a+3 are in flight. Before a pair, this wave's copies of it
+    // are done once nothing younger is outstanding; the barrier then makes every
+    // wave's copies visible, and the pair of slots processed before is refilled.
+    static_assert(NS == 4 || NS == 2, "ring of 4 slots (pairs) or 2 slots (single cells)");
+    if constexpr (NS == 4) {
+        auto pair = [&](int a, const uint16_t *kc0, const uint16_t *vc0, const uint16_t *kc1, const uint16_t *vc1,
+                        uint16_t *kp0, uint16_t *vp0, uint16_t *kp1, uint16_t *vp1) __attribute__((always_inline)) {
+            wait_vmem_le<0>();
+            barrier_no_fence();
+            issue(min(a + 2, nact - 1), kp0, vp0);  // past the end: harmless repeats of the last cell
+            issue(min(a + 3, nact - 1), kp1, vp1);
+            process(a, kc0, vc0);
+            if (a + 1 < nact) process(a + 1, kc1, vc1);
+        };
+        if (nact > 0) {
+            issue(0, s_k0, s_v0);
+            issue(min(1, nact - 1), s_k1, s_v1);
         }
-    }
-    for (int a = 0; a < nact; a += NS) {
-        if constexpr (NS > 2) {
-            step(a, s_k0, s_v0, s_k3, s_v3);
-            if (a + 1 >= nact) break;
-            step(a + 1, s_k1, s_v1, s_k0, s_v0);
+        for (int a = 0; a < nact; a += 4) {
+            pair(a, s_k0, s_v0, s_k1, s_v1, s_k2, s_v2, s_k3, s_v3);
             if (a + 2 >= nact) break;
-            step(a + 2, s_k2, s_v2, s_k1, s_v1);
-            if (a + 3 >= nact) break;
-            step(a + 3, s_k3, s_v3, s_k2, s_v2);
-        } else {
+            pair(a + 2, s_k2, s_v2, s_k3, s_v3, s_k0, s_v0, s_k1, s_v1);
+        }
+    } else {
+        auto step = [&](int a, const uint16_t *kc, const uint16_t *vc, uint16_t *kpf, uint16_t *vpf)
+            __attribute__((always_inline)) {
+            wait_vmem_le<0>();
+            barrier_no_fence();
+            issue(min(a + 1, nact - 1), kpf, vpf);
+            process(a, kc, vc);
+        };
+        if (nact > 0) issue(0, s_k0, s_v0);
+        for (int a = 0; a < nact; a += 2) {
             step(a, s_k0, s_v0, s_k1, s_v1);
             if (a + 1 >= nact) break;
             step(a + 1, s_k1, s_v1, s_k0, s_v0);
