@@ -9,6 +9,7 @@ roofline of the dominant kernel and the oracle timed on a bounded sample.
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload c4] [--no-cpu]
 """
 import argparse
+import hashlib
 import ctypes
 import json
 import os
@@ -22,7 +23,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
-FP64_PEAK_TFLOPS = 78.6        # fp64 vector
 
 
 def log(msg):
@@ -62,8 +62,9 @@ class HipEvents:
 
 
 def algorithmic_work(sh, sel_np=None):
-    """Per-launch algorithmic bytes / flops of each stage (roofline section)."""
-    H, N, d, s, w, B = sh.H, sh.N, sh.d, sh.s, sh.w, sh.B
+    """Per-launch algorithmic bytes / flops of each stage: what the method must move or compute,
+    each input read once and each output written once."""
+    H, N, d, s, w, B, K = sh.H, sh.N, sh.d, sh.s, sh.w, sh.B, sh.K
     e = 2 if sh.dtype == "bf16" else 4
     C = N // s
     i = np.arange(N, dtype=np.float64)
@@ -71,31 +72,56 @@ def algorithmic_work(sh, sel_np=None):
     nblk = (N + B - 1) // B
     nb = np.array([max(0, (b * B - w + 1) // s) for b in range(nblk)], dtype=np.int64)
     npool = np.minimum(nb, sh.P + sh.W)
-    rows_per_blk = np.minimum(B, N - np.arange(nblk) * B)
     work = {
+        # k read once; kbar and amax written once
         "cell_stats": ("hbm", H * N * d * e + H * C * (d + 1) * 4),
+        # q and kbar/amax read once, the pools and selections written once
+        "select": ("hbm", H * N * d * e + H * C * (d + 1) * 4 + H * nblk * (sh.P + sh.W) * 4 + H * N * K * 4),
         "window": ("mfma", H * 4.0 * d * win_keys),
-        "select": ("alu", H * 2.0 * d * float((npool * rows_per_blk).sum())),
-        # compulsory streams: q read, o_win read, out written, plus the K/V rows of the
-        # distinct cells each block reads (measured union, counted once per block)
-        "readout_mix": ("hbm", H * N * d * (e + 4 + e)),
     }
     if sh.dtype == "bf16":
         # k and v read once, fp16 rotated keys and transposed values written once
         work["kv_prep"] = ("hbm", H * N * d * (2 * e + 2 * 2))
+    # q and o_win read, out written, plus the keys and values of every selected cell once
+    # per head (keys in the input dtype; values fp16 on the bf16 path, fp32 otherwise)
+    readout = H * N * d * (e + 4 + e)
     if sel_np is not None:
         union_cells = 0
+        distinct = 0
         for h in range(H):
             sh_sel = sel_np[h]
+            distinct += int(np.unique(sh_sel[sh_sel >= 0]).size)
             pad = (-N) % B
-            blocks = np.concatenate([sh_sel, np.full((pad, sh.K), -1, sh_sel.dtype)]).reshape(nblk, B * sh.K)
+            blocks = np.concatenate([sh_sel, np.full((pad, K), -1, sh_sel.dtype)]).reshape(nblk, B * K)
             srt = np.sort(blocks, axis=1)
-            distinct = (np.diff(srt, axis=1) != 0).sum(axis=1) + 1 - (srt[:, 0] < 0)
-            union_cells += int(distinct.sum())
-        kind, base = work["readout_mix"]
-        work["readout_mix"] = (kind, base + union_cells * s * 2 * d * e)
+            union_cells += int(((np.diff(srt, axis=1) != 0).sum(axis=1) + 1 - (srt[:, 0] < 0)).sum())
+        readout += distinct * s * d * (e + (2 if sh.dtype == "bf16" else 4))
         work["_union_cells_per_block"] = union_cells / (H * nblk)
+        work["_distinct_cells"] = distinct
+    work["readout_mix"] = ("hbm", readout)
     return work
+
+
+# HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00, the
+# factors read off a plain 1 GiB device copy in the same run), for the kernel source they were taken
+# on; reported only while that source is unchanged.
+TRAFFIC = {
+    "readout_mix": {"bytes": 3197506426, "source": "long_context_sparse_cell_amd/csrc/readout_flash.hip",
+                    "sha256": "6a5cd7611db70f3b235789b82e0b9df2b1122098200f8bed4de6228d1c6a9eca",
+                    "profile": "profiles/fwd_c4_hbm_traffic.md"},
+}
+
+
+def measured_traffic(stage):
+    rec = TRAFFIC.get(stage)
+    if rec is None:
+        return None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"])
+    try:
+        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return rec["bytes"] if digest == rec["sha256"] else None
 
 
 def cpu_baseline(inp, sample_rows):
@@ -252,12 +278,9 @@ def main():
             kind, amount = work[name]
             if kind == "hbm":
                 entry.update(bound="hbm", achieved=amount / (t * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
-            elif kind == "mfma":
+            else:
                 entry.update(bound="mfma", achieved=amount / (t * 1e-3) / 1e12, peak=MFMA_F16_PEAK_TFLOPS,
                              unit="TFLOP/s")
-            else:
-                entry.update(bound="alu", achieved=amount / (t * 1e-3) / 1e12, peak=FP64_PEAK_TFLOPS,
-                             unit="TFLOP/s (fp64)")
             entry["frac"] = entry["achieved"] / entry["peak"]
             entry["achieved"] = round(entry["achieved"], 2)
             entry["frac"] = round(entry["frac"], 4)
@@ -265,7 +288,7 @@ def main():
     dominant = max((n for n in stages if "bound" in stages[n]), key=lambda n: stage_ms[n])
     dom = stages[dominant]
     roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
-                "unit": dom["unit"], "frac": dom["frac"], "traffic": None}
+                "unit": dom["unit"], "frac": dom["frac"], "traffic": measured_traffic(dominant)}
 
     dec = None
     if not args.no_decode:
@@ -302,6 +325,7 @@ def main():
         "stages": stages,
         "gpu_ms_per_step": round(gpu_ms, 4),
         "union_cells_per_block": round(work.get("_union_cells_per_block", 0.0), 2),
+        "distinct_selected_cells": work.get("_distinct_cells"),
         "decode": dec,
     }
     print(json.dumps(line), flush=True)
