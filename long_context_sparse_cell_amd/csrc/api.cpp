@@ -102,7 +102,7 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FSL_OK : FSL_E_HIP; }
 
-constexpr int32_t kDecodeMaxW = 65536;  // the decode RoPE table has w rows
+constexpr int32_t kDecodeMaxW = 65536;  // bounds the ring of w + B + s tokens per (sequence, head)
 
 int check_decode(const fsl_params *p) {
     if (!p) return FSL_E_INVAL;
@@ -121,8 +121,7 @@ DecodeLayout dlayout(const fsl_params *p) {
     const size_t e = p->dtype == FSL_BF16 ? 2 : 4;
     L.R = p->w + p->B + p->s;
     L.PW = p->P + p->W;
-    L.off_rope = 256;
-    L.off_rec = (int64_t)align_up(256 + (size_t)p->w * (p->d / 2) * sizeof(float2));
+    L.off_rec = 256;
     size_t o = 16;  // int64 t, int64 block
     L.o_cell = (int64_t)o; o = align16(o + 4 * (size_t)L.PW);
     L.o_a = (int64_t)o; o = align16(o + 4 * (size_t)L.PW);
@@ -131,6 +130,7 @@ DecodeLayout dlayout(const fsl_params *p) {
     L.o_sv = (int64_t)o; o = align16(o + e * (size_t)L.PW * p->s * p->d);
     L.o_rk = (int64_t)o; o = align16(o + e * (size_t)L.R * p->d);
     L.o_rv = (int64_t)o; o = align16(o + e * (size_t)L.R * p->d);
+    L.o_rkr = (int64_t)o; o = align16(o + e * (size_t)L.R * p->d);  // fp16 for bf16 inputs, else fp32
     L.rec_bytes = (int64_t)align_up(o);
     return L;
 }

@@ -5,19 +5,25 @@
 //
 // One workgroup per (sequence, head) and step. The state record of a
 // (sequence, head) holds the next position t, the block whose pool is loaded,
-// a ring of the last R = w + B + s tokens' raw k/v and P + W cell slots (cell
-// index, max key norm, mean key, raw k/v). A step:
+// a ring of the last R = w + B + s tokens' raw k/v plus their keys rotated at
+// their absolute positions (fp16 for bf16 inputs, fp32 otherwise), and P + W
+// cell slots (cell index, max key norm, mean key, raw k/v). A step:
 //  1. if t starts a new block, the cells that just became eligible get their
 //     statistics from the ring (fp64, same order as the forward), the cells
 //     leaving the recent set compete for the P high-norm places (keep the P
 //     best under (a desc, index asc); a loser's slot is freed), and every
 //     newly kept cell is copied once from the ring into a free slot;
-//  2. appends the new k/v to the ring;
-//  3. window attention over the ring (RoPE by the offset j - t, fp32);
+//  2. appends the new k/v to the ring and its key rotated at t (angles in fp64);
+//  3. window attention over the ring: R(t)q against the rotated keys;
 //  4. scores every occupied slot in fp64 exactly as the forward does, keeps
 //     the top K under (score desc, index asc);
 //  5. NoPE readout over the chosen cells' tokens, RMSNorm, mix, write.
+// Both attention steps spread the keys over the lanes of 4 waves, 64 keys per
+// chunk (16-byte row loads), then turn the lanes to dimensions for the P.V sum
+// (each key's weight broadcast from its lane, value rows read coalesced); the
+// four waves' partial softmax states are merged at the end.
 #include <climits>
+#include <type_traits>
 
 #include "fsl_internal.h"
 
@@ -26,6 +32,7 @@ namespace fsl {
 namespace {
 
 constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDecMaxPool = 128;
 constexpr int kDecMaxNew = 16;   // cells entering per block boundary: B/s <= 256/16
 
@@ -40,6 +47,44 @@ template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+
+// element type of the rotated-key ring: fp16 bits for bf16 inputs, fp32 otherwise
+template <typename T> struct RotKey { typedef float type; };
+template <> struct RotKey<uint16_t> { typedef uint16_t type; };
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    union { _Float16 f; uint16_t u; } c;
+    c.f = (_Float16)x;  // round to nearest even
+    return c.u;
+}
+template <typename RT> __device__ __forceinline__ RT rot_store(float x);
+template <> __device__ __forceinline__ float rot_store<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t rot_store<uint16_t>(float x) { return f32_to_f16_bits(x); }
+
+// eight consecutive elements of a key row as float: 16-bit elements are either
+// bf16 (raw keys) or fp16 (rotated keys)
+template <typename E, bool F16>
+__device__ __forceinline__ void load8f(const E *ptr, float (&o)[8]) {
+    if constexpr (sizeof(E) == 2) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(ptr);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (F16) {
+                union { uint32_t u; _Float16 h[2]; } c;
+                c.u = w4[t];
+                o[2 * t] = (float)c.h[0];
+                o[2 * t + 1] = (float)c.h[1];
+            } else {
+                o[2 * t] = __uint_as_float(w4[t] << 16);
+                o[2 * t + 1] = __uint_as_float(w4[t] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(ptr);
+        const float4 b = *reinterpret_cast<const float4 *>(ptr + 4);
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+}
 
 __device__ float block_reduce(float v, float *scratch, bool is_max) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -67,15 +112,6 @@ __global__ void decode_init_kernel(char *__restrict__ state, KParams p, DecodeLa
         hd->H = p.H; hd->d = p.d; hd->w = p.w; hd->s = p.s; hd->P = p.P; hd->W = p.W; hd->K = p.K; hd->B = p.B;
         hd->dtype = dtype; hd->n_seq = n_seq; hd->R = L.R; hd->PW = L.PW;
         hd->rec_bytes = L.rec_bytes;
-    }
-    // RoPE rows for offsets j - t in [-(w-1), 0]: row r <-> offset r - (w-1)
-    const int half = p.d / 2;
-    for (int64_t e = (int64_t)rec_id * blockDim.x + threadIdx.x; e < (int64_t)p.w * half;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int row = (int)(e / half), m = (int)(e % half);
-        const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)p.d);
-        const double ang = (double)(row - (p.w - 1)) * theta;
-        reinterpret_cast<float2 *>(state + L.off_rope)[e] = make_float2((float)cos(ang), (float)sin(ang));
     }
     char *rec = state + L.off_rec + (int64_t)rec_id * L.rec_bytes;
     if (threadIdx.x == 0) {
@@ -128,6 +164,20 @@ __global__ void decode_prefill_kernel(char *__restrict__ state, int seq, const T
         rk[slot * D + x] = kh[pos * D + x];
         rv[slot * D + x] = vh[pos * D + x];
     }
+    // the same tokens' keys rotated at their positions (angle pos * base^(-2m/d) in fp64)
+    typedef typename RotKey<T>::type RT;
+    RT *rkr = reinterpret_cast<RT *>(rec + L.o_rkr);
+    for (int64_t e = threadIdx.x; e < (Lp - first) * (D / 2); e += blockDim.x) {
+        const int64_t pos = first + e / (D / 2);
+        const int m = (int)(e % (D / 2));
+        const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
+        const double ang = (double)pos * theta;
+        const float c = (float)cos(ang), sn = (float)sin(ang);
+        const float a = to_f32<T>(kh[pos * D + m]), bb = to_f32<T>(kh[pos * D + m + D / 2]);
+        const int64_t slot = pos % L.R;
+        rkr[slot * D + m] = rot_store<RT>(a * c - bb * sn);
+        rkr[slot * D + m + D / 2] = rot_store<RT>(bb * c + a * sn);
+    }
     if (threadIdx.x == 0) {
         reinterpret_cast<int64_t *>(rec)[0] = Lp;
         reinterpret_cast<int64_t *>(rec)[1] = b;
@@ -135,20 +185,21 @@ __global__ void decode_prefill_kernel(char *__restrict__ state, int seq, const T
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restrict__ state, const T *__restrict__ qn,
+__global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__restrict__ state, const T *__restrict__ qn,
                                                                   const T *__restrict__ kn, const T *__restrict__ vn,
                                                                   void *__restrict__ out, int32_t *__restrict__ sel_out,
                                                                   KParams p, DecodeLayout L) {
-    __shared__ float s_q[D];
+    __shared__ __attribute__((aligned(16))) float s_q[D];
     __shared__ int s_cell[kDecMaxPool];
     __shared__ float s_a[kDecMaxPool];
     __shared__ double s_score[kDecMaxPool];
     __shared__ int s_rank[kDecMaxPool];
     __shared__ int s_sel[8];
     __shared__ int s_selslot[8];
-    __shared__ float s_p[kDecThreads];
     __shared__ float s_red[kDecThreads / 64];
-    __shared__ float s_o[kDecThreads];
+    __shared__ __attribute__((aligned(16))) float s_qr[D];  // R(t) q
+    __shared__ float s_wm[kDecWaves], s_wl[kDecWaves];     // per-wave softmax state
+    __shared__ float s_wo[kDecWaves][D];                    // per-wave partial outputs
     __shared__ double s_ss[kDecMaxNew * 64];
     __shared__ float s_newa[kDecMaxNew];
     __shared__ int s_load_cell[kDecMaxNew], s_load_slot[kDecMaxNew], s_nload;
@@ -165,8 +216,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restri
     T *sv = reinterpret_cast<T *>(rec + L.o_sv);
     T *rk = reinterpret_cast<T *>(rec + L.o_rk);
     T *rv = reinterpret_cast<T *>(rec + L.o_rv);
-    const float2 *rope = reinterpret_cast<const float2 *>(state + L.off_rope);
+    typedef typename RotKey<T>::type RT;
+    RT *rkr = reinterpret_cast<RT *>(rec + L.o_rkr);
     const int s = p.s, PW = L.PW, R = L.R;
+    const int lane = tid & 63, wave = tid >> 6;
 
     const int64_t t = hdr[0];
     const int64_t blk = hdr[1];
@@ -187,6 +240,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restri
             const int cn = r / s, j = r % s;
             const int64_t pos = (n_old + cn) * s + j;
             double acc = 0.0;
+#pragma unroll 8
             for (int x = 0; x < D; ++x) {
                 const double e = (double)to_f32<T>(rk[(pos % R) * D + x]);
                 acc = __fma_rn(e, e, acc);
@@ -293,8 +347,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restri
         __syncthreads();
     }
 
-    // ---- 2. append the new token
+    // ---- 2. append the new token: raw k/v, and the key rotated at t
     const int64_t tslot = t % R;
+    if (tid < D / 2) {
+        const int m = tid;
+        const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
+        const double ang = (double)t * theta;
+        const float c = (float)cos(ang), sn = (float)sin(ang);
+        const float qa = s_q[m], qb = s_q[m + D / 2];
+        s_qr[m] = qa * c - qb * sn;
+        s_qr[m + D / 2] = qb * c + qa * sn;
+        const float ka = to_f32<T>(kn[(int64_t)rid * D + m]), kb = to_f32<T>(kn[(int64_t)rid * D + m + D / 2]);
+        rkr[tslot * D + m] = rot_store<RT>(ka * c - kb * sn);
+        rkr[tslot * D + m + D / 2] = rot_store<RT>(kb * c + ka * sn);
+    }
     if (tid < D) {
         rk[tslot * D + tid] = kn[(int64_t)rid * D + tid];
         rv[tslot * D + tid] = vn[(int64_t)rid * D + tid];
@@ -302,48 +368,105 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restri
     __syncthreads();
 
     const float sl2 = p.scale * 1.4426950408889634f;
-    constexpr int PARTS = kDecThreads / D;  // threads per coordinate in the weighted sums
-    const int x_own = tid % D, part = tid / D;
+    constexpr int DPL = D / 64;  // dimensions per lane in the P.V sums
 
-    // ---- 3. window over keys [max(0, t-w+1), t], RoPE by offset j - t, online softmax in chunks
-    float m_run = -INFINITY, l_run = 0.0f, o_acc = 0.0f;
-    const int64_t j_lo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
-    for (int64_t c0 = j_lo; c0 <= t; c0 += kDecThreads) {
-        const int64_t j = c0 + tid;
-        float sc = -INFINITY;
-        if (j <= t) {
-            const T *kr = rk + (j % R) * D;
-            const float2 *tr = rope + (j - t + p.w - 1) * (D / 2);
-            float dot = 0.0f;
-            for (int m = 0; m < D / 2; ++m) {
-                const float a = to_f32<T>(kr[m]), bb = to_f32<T>(kr[m + D / 2]);
-                const float2 cs = tr[m];
-                dot += s_q[m] * (a * cs.x - bb * cs.y) + s_q[m + D / 2] * (bb * cs.x + a * cs.y);
+    // Softmax attention of one query (qs in LDS) over nkeys keys: key u's row at krow(u)
+    // (fp16 bits if kf16, else the input type), its value row at vrow(u). Keys go to lanes in
+    // chunks of 64 (chunk c to wave c mod 4); each wave keeps its own (max, sum, o),
+    // merged over the waves into res[x] for x < D by threads tid < D.
+    auto attend = [&](int nkeys, const float *qs, auto krow, auto vrow, auto kf16, float &res)
+        __attribute__((always_inline)) {
+        typedef typename std::remove_cv<typename std::remove_pointer<decltype(krow(0))>::type>::type KE;
+        constexpr bool KF16 = decltype(kf16)::value;  // 16-bit keys: fp16 (rotated ring) or bf16 (raw)
+        float m_run = -INFINITY, l_run = 0.0f;
+        float o[DPL];
+#pragma unroll
+        for (int d2 = 0; d2 < DPL; ++d2) o[d2] = 0.0f;
+        for (int c0 = 64 * wave; c0 < nkeys; c0 += 64 * kDecWaves) {
+            const int u = c0 + lane;
+            float sc = -INFINITY;
+            if (u < nkeys) {
+                const KE *kr = krow(u);
+                float dot = 0.0f;
+#pragma unroll 4
+                for (int x0 = 0; x0 < D; x0 += 8) {
+                    float kf[8];
+                    load8f<KE, KF16>(kr + x0, kf);
+                    const float4 qa = *reinterpret_cast<const float4 *>(qs + x0);
+                    const float4 qb = *reinterpret_cast<const float4 *>(qs + x0 + 4);
+                    dot += qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] + qb.x * kf[4] + qb.y * kf[5] +
+                           qb.z * kf[6] + qb.w * kf[7];
+                }
+                sc = dot * sl2;
             }
-            sc = dot * sl2;
+            float cm = sc;
+#pragma unroll
+            for (int m2 = 32; m2 > 0; m2 >>= 1) cm = fmaxf(cm, __shfl_xor(cm, m2));
+            const float m_new = fmaxf(m_run, cm);
+            const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+            const float pj = u < nkeys ? exp2f(sc - m_new) : 0.0f;
+            float ps = pj;
+#pragma unroll
+            for (int m2 = 32; m2 > 0; m2 >>= 1) ps += __shfl_xor(ps, m2);
+            l_run = l_run * alpha + ps;
+#pragma unroll
+            for (int d2 = 0; d2 < DPL; ++d2) o[d2] *= alpha;
+            m_run = m_new;
+            // lanes as dimensions: o[lane*DPL + d2] += p_u v_u, the weight taken from lane u
+            const int nk = min(64, nkeys - c0);
+#pragma unroll 1
+            for (int k0 = 0; k0 < nk; k0 += 8) {
+                float vv[8][DPL];
+#pragma unroll
+                for (int j2 = 0; j2 < 8; ++j2) {
+                    const T *vr = vrow(c0 + min(k0 + j2, nk - 1)) + lane * DPL;
+#pragma unroll
+                    for (int d2 = 0; d2 < DPL; ++d2) vv[j2][d2] = to_f32<T>(vr[d2]);
+                }
+#pragma unroll
+                for (int j2 = 0; j2 < 8; ++j2) {
+                    // weight of key k0 + j2, broadcast from its lane (zero past the chunk's end)
+                    const float pk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), k0 + j2));
+#pragma unroll
+                    for (int d2 = 0; d2 < DPL; ++d2) o[d2] += (k0 + j2 < nk ? pk : 0.0f) * vv[j2][d2];
+                }
+            }
         }
-        const float cmax = block_reduce(sc, s_red, true);
-        const float m_new = fmaxf(m_run, cmax);
-        const float alpha = exp2f(m_run - m_new);
-        const float pj = j <= t ? exp2f(sc - m_new) : 0.0f;
-        s_p[tid] = pj;
-        const float psum = block_reduce(pj, s_red, false);
-        l_run = l_run * alpha + psum;
-        o_acc *= alpha;
+        if (lane == 0) {
+            s_wm[wave] = m_run;
+            s_wl[wave] = l_run;
+        }
+#pragma unroll
+        for (int d2 = 0; d2 < DPL; ++d2) s_wo[wave][lane * DPL + d2] = o[d2];
         __syncthreads();
-        const int nk = (int)((t - c0 + 1) < kDecThreads ? (t - c0 + 1) : kDecThreads);
-        for (int u = part; u < nk; u += PARTS) o_acc += s_p[u] * to_f32<T>(rv[((c0 + u) % R) * D + x_own]);
-        m_run = m_new;
+        if (tid < D) {
+            float mm = -INFINITY;
+#pragma unroll
+            for (int w2 = 0; w2 < kDecWaves; ++w2) mm = fmaxf(mm, s_wm[w2]);
+            float num = 0.0f, den = 0.0f;
+#pragma unroll
+            for (int w2 = 0; w2 < kDecWaves; ++w2) {
+                const float f = s_wm[w2] == -INFINITY ? 0.0f : exp2f(s_wm[w2] - mm);
+                num += f * s_wo[w2][tid];
+                den += f * s_wl[w2];
+            }
+            res = den > 0.0f ? num / den : 0.0f;
+        }
         __syncthreads();
-    }
-    s_o[tid] = o_acc;
-    __syncthreads();
+    };
+
+    // ---- 3. window over keys [max(0, t-w+1), t]: R(t)q against the rotated keys
     float o_win = 0.0f;
-    if (tid < D) {
-        for (int u = 0; u < PARTS; ++u) o_win += s_o[u * D + tid];
-        o_win /= l_run;
+    {
+        const int64_t j_lo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
+        const int nwin = (int)(t - j_lo + 1);
+        const int r0 = (int)(j_lo % R);  // ring row of key j_lo; keys j_lo + u stay below j_lo + R
+        auto ring = [=](int u) { const int r = r0 + u; return (r >= R ? r - R : r) * D; };
+        attend(
+            nwin, s_qr, [&](int u) { return (const RT *)(rkr + ring(u)); },
+            [&](int u) { return (const T *)(rv + ring(u)); },
+            std::integral_constant<bool, sizeof(RT) == 2>{}, o_win);
     }
-    __syncthreads();
 
     // ---- 4. exact fp64 cell scores and top-K over the occupied slots
     const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
@@ -351,8 +474,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restri
         double scv = -INFINITY;
         const int c = s_cell[i];
         if (c >= 0) {
+            const float *kr = skb + (int64_t)i * D;
             double content = 0.0;
-            for (int x = 0; x < D; ++x) content = __fma_rn((double)s_q[x], (double)skb[(int64_t)i * D + x], content);
+#pragma unroll 4
+            for (int x0 = 0; x0 < D; x0 += 4) {
+                const float4 k4 = *reinterpret_cast<const float4 *>(kr + x0);
+                content = __fma_rn((double)s_q[x0], (double)k4.x, content);
+                content = __fma_rn((double)s_q[x0 + 1], (double)k4.y, content);
+                content = __fma_rn((double)s_q[x0 + 2], (double)k4.z, content);
+                content = __fma_rn((double)s_q[x0 + 3], (double)k4.w, content);
+            }
             const double arg = __ddiv_rn(__dmul_rn(sig, (double)(t - (int64_t)c * s)), 2.0 * (double)s);
             const double gg = arg >= 6.0 ? 1.0 : erf(arg);
             const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[i]), gg);
@@ -390,42 +521,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(char *__restri
     if (sel_out && tid < p.K) sel_out[(int64_t)rid * p.K + tid] = s_selslot[tid] >= 0 ? s_sel[tid] : -1;
 
     // ---- 5. NoPE readout over the chosen cells' tokens, RMSNorm, mix
-    const int ntok = nsel * s;
     float o_long = 0.0f;
+    const int ntok = nsel * s;
     if (ntok > 0) {
-        float m2 = -INFINITY, l2 = 0.0f, acc2 = 0.0f;
-        for (int c0 = 0; c0 < ntok; c0 += kDecThreads) {
-            const int u = c0 + tid;
-            float sc = -INFINITY;
-            if (u < ntok) {
-                const T *kr = sk + ((int64_t)s_selslot[u / s] * s + u % s) * D;
-                float dot = 0.0f;
-                for (int x = 0; x < D; ++x) dot += s_q[x] * to_f32<T>(kr[x]);
-                sc = dot * sl2;
-            }
-            const float cmax = block_reduce(sc, s_red, true);
-            const float mn = fmaxf(m2, cmax);
-            const float alpha = exp2f(m2 - mn);
-            const float pj = u < ntok ? exp2f(sc - mn) : 0.0f;
-            s_p[tid] = pj;
-            const float psum = block_reduce(pj, s_red, false);
-            l2 = l2 * alpha + psum;
-            acc2 *= alpha;
-            __syncthreads();
-            const int nk = ntok - c0 < kDecThreads ? ntok - c0 : kDecThreads;
-            for (int uu = part; uu < nk; uu += PARTS) {
-                const int tok = c0 + uu;
-                acc2 += s_p[uu] * to_f32<T>(sv[((int64_t)s_selslot[tok / s] * s + tok % s) * D + x_own]);
-            }
-            m2 = mn;
-            __syncthreads();
-        }
-        s_o[tid] = acc2;
-        __syncthreads();
-        if (tid < D) {
-            for (int u = 0; u < PARTS; ++u) o_long += s_o[u * D + tid];
-            o_long /= l2;
-        }
+        const int ls = __builtin_ctz((unsigned)s);  // s is a power of two
+        auto slot_row = [=](int u) { return ((s_selslot[u >> ls] << ls) + (u & (s - 1))) * D; };
+        attend(
+            ntok, s_q, [&](int u) { return (const T *)(sk + slot_row(u)); },
+            [&](int u) { return (const T *)(sv + slot_row(u)); }, std::false_type{}, o_long);
     }
     const float ms = block_reduce(tid < D ? o_long * o_long : 0.0f, s_red, false) / (float)D;
     if (tid < D) {

@@ -273,7 +273,7 @@ __device__ __forceinline__ void wave_merge_top(float &a, int &idx, float ba, int
 // one record per (sequence, head)
 
 constexpr uint32_t kDecodeMagic = 0x44534C46u;  // "FLSD"
-constexpr uint32_t kDecodeVersion = 1;
+constexpr uint32_t kDecodeVersion = 2;
 
 struct DecodeHeader {
     uint32_t magic, version;
@@ -284,11 +284,11 @@ struct DecodeHeader {
 struct DecodeLayout {
     int32_t R;          // ring tokens, w + B + s
     int32_t PW;         // cell slots, P + W
-    int64_t off_rope;   // float2 [w][d/2]
     int64_t off_rec;    // first record
     int64_t rec_bytes;  // bytes per (sequence, head) record
     // offsets inside a record (after int64 t and int64 block)
     int64_t o_cell, o_a, o_kbar, o_sk, o_sv, o_rk, o_rv;
+    int64_t o_rkr;      // ring of keys rotated at their positions: fp16 (bf16 inputs) or fp32 [R][d]
 };
 
 // ---------------------------------------------------------------------------

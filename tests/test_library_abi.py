@@ -139,7 +139,9 @@ def test_decode_state_is_bounded_and_independent_of_prefix(fsl):
     per_head = sizes[0] / (64 * 16)
     tokens = (64 + 8) * 32 + 512 + 128 + 32  # (P+W)s + w + B + s
     kv_bytes = tokens * 64 * 2 * 2           # raw k and v, bf16
-    assert kv_bytes <= per_head <= kv_bytes * 1.1  # plus cell means/norms and alignment
+    rot_bytes = (512 + 128 + 32) * 64 * 2    # the ring's keys rotated at their positions, fp16
+    need = kv_bytes + rot_bytes
+    assert need <= per_head <= need * 1.1    # plus cell means/norms and alignment
     p = params(fsl, P=-1)
     assert int(L.fsl_decode_state_bytes(ctypes.byref(p), 4)) == 0
     p = params(fsl)
