@@ -45,6 +45,16 @@ union U16x8s {
     uint16_t h[8];
 };
 
+// Sum over the aligned group of 8 lanes that holds lane l (lanes 8 (l / 8) ..
+// 8 (l / 8) + 7) with three DPP moves: swap neighbours, swap pairs, mirror the
+// halves of the group. Every lane of the group ends with the same sum.
+__device__ __forceinline__ float sum8_dpp(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    return x;
+}
+
 }  // namespace
 
 template <int D, int KL>
@@ -53,7 +63,9 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                                                           const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
                                                           uint32_t *__restrict__ fix, KParams p, int QW) {
     constexpr int HLD = D + 8;  // bf16 row stride of the split pool means (272 B for d = 128: conflict-free rows)
-    extern __shared__ uint16_t s_dyn[];  // hi rows [ntile*16][HLD], then lo rows
+    // hi rows [ntile*16][HLD], then lo rows; 16-byte aligned for the 16-byte operand
+    // reads (after the static arrays below, whose size is not a multiple of 16)
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
     __shared__ int s_pool[kSelPool];
     // per pool cell: lambda a_c, |rho| ||kbar_c|| epsc, |lambda a_c| 2e-6, and c s (int bits)
     __shared__ float4 s_cf[kSelPool];
@@ -88,33 +100,59 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + i) * D + 32 * ks + 8 * g);
 
-    // ---- setup, one pass: pool row r by D/4 consecutive threads (4 floats each): its
-    // mean split into bf16 head + tail (round to nearest even; rows past the pool are
-    // zero), its norm, and the per-cell constants of the bound
-    if (tid == 0) s_nfix = 0;
-    for (int e = tid; e < ntile * 16 * (D / 4); e += 512) {
-        const int r = e / (D / 4), x = 4 * (e % (D / 4));
-        const bool ok = r < npool;
-        const int c = ok ? pool[((int64_t)h * p.nblk + b) * p.PW + r] : 0;
-        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (ok) f = *reinterpret_cast<const float4 *>(kbar + (hC + c) * D + x);
-        const float fx[4] = {f.x, f.y, f.z, f.w};
-        union { __bf16 b[4]; uint2 u; } hi4, lo4;
+    // ---- setup: pool row r by 8 consecutive threads (D/8 floats each): its mean split
+    // into bf16 head + tail (round to nearest even; rows past the pool are zero), its
+    // norm, and the per-cell constants of the bound. Every global load of the setup is
+    // issued before the first one is used: the pool indices, then the rows and norms.
+    constexpr int RPP = 512 / 8;                  // rows per pass
+    constexpr int NPASS = kSelPool / RPP;         // passes over the largest pool
+    constexpr int FPT = D / 8;                    // floats per thread
+    const int part = tid & 7;
+    int crow[NPASS];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const __bf16 hb = (__bf16)fx[t];
-            hi4.b[t] = hb;
-            lo4.b[t] = (__bf16)(fx[t] - (float)hb);
+    for (int j = 0; j < NPASS; ++j) {
+        const int r = RPP * j + (tid >> 3);
+        crow[j] = r < npool ? pool[((int64_t)h * p.nblk + b) * p.PW + r] : -1;
+    }
+    float4 f[NPASS][FPT / 4];
+    float am[NPASS];
+#pragma unroll
+    for (int j = 0; j < NPASS; ++j) {
+        am[j] = 0.0f;
+#pragma unroll
+        for (int x = 0; x < FPT / 4; ++x) f[j][x] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (crow[j] >= 0) {
+            const float *src = kbar + (hC + crow[j]) * D + FPT * part;
+#pragma unroll
+            for (int x = 0; x < FPT / 4; ++x) f[j][x] = *reinterpret_cast<const float4 *>(src + 4 * x);
+            if (part == 0) am[j] = amax[hC + crow[j]];
         }
-        *reinterpret_cast<uint2 *>(&s_hi[r * HLD + x]) = hi4.u;
-        *reinterpret_cast<uint2 *>(&s_lo[r * HLD + x]) = lo4.u;
-        float ss = f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
+    }
+    if (tid == 0) s_nfix = 0;
 #pragma unroll
-        for (int m2 = 1; m2 < D / 4; m2 <<= 1) ss += __shfl_xor(ss, m2);
-        if (ok && x == 0) {
-            const float la = lamf * amax[hC + c];
-            s_pool[r] = c;
-            s_cf[r] = make_float4(la, fabsf(rhof) * sqrtf(ss) * epsc, fabsf(la) * 2e-6f, __int_as_float(c * p.s));
+    for (int j = 0; j < NPASS; ++j) {
+        const int r = RPP * j + (tid >> 3);
+        if (r >= ntile * 16) continue;  // rows of the last tile past the pool are written as zeros
+        float ss = 0.0f;
+#pragma unroll
+        for (int x = 0; x < FPT / 4; ++x) {
+            const float fx[4] = {f[j][x].x, f[j][x].y, f[j][x].z, f[j][x].w};
+            union { __bf16 b[4]; uint2 u; } hi4, lo4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const __bf16 hb = (__bf16)fx[t];
+                hi4.b[t] = hb;
+                lo4.b[t] = (__bf16)(fx[t] - (float)hb);
+                ss += fx[t] * fx[t];
+            }
+            *reinterpret_cast<uint2 *>(&s_hi[r * HLD + FPT * part + 4 * x]) = hi4.u;
+            *reinterpret_cast<uint2 *>(&s_lo[r * HLD + FPT * part + 4 * x]) = lo4.u;
+        }
+        ss = sum8_dpp(ss);  // the row's 8 threads are one aligned group of 8 lanes
+        if (crow[j] >= 0 && part == 0) {
+            const float la = lamf * am[j];
+            s_pool[r] = crow[j];
+            s_cf[r] = make_float4(la, fabsf(rhof) * sqrtf(ss) * epsc, fabsf(la) * 2e-6f, __int_as_float(crow[j] * p.s));
         }
     }
     __syncthreads();
@@ -138,8 +176,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
 #pragma unroll
         for (int r = 0; r < KL; ++r) lbk[r] = -INFINITY;
         // approximate scores, 4 cells of each 16-cell tile per lane (cells 16*ct + 4*g + e)
-        float sapx[kSelPool / 16][4];
-        float seps[kSelPool / 16][4];
+        float sub[kSelPool / 16][4];  // upper bounds s~ + eps
 #pragma unroll
         for (int ct = 0; ct < kSelPool / 16; ++ct) {
             if (ct >= ntile) break;
@@ -156,8 +193,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int pos = 16 * ct + 4 * g + e;
-                sapx[ct][e] = -INFINITY;
-                seps[ct][e] = 0.0f;
+                sub[ct][e] = -INFINITY;
                 if (pos < npool) {
                     const float4 cf = s_cf[pos];
                     float bf = cf.x;  // lambda a_c times the erf factor 1
@@ -169,8 +205,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                     const float sv = rc + bf;
                     const float ev =
                         2.0f * (fmaf(qn, cf.y, cf.z) + (fabsf(rc) + fabsf(bf)) * 2.384185791015625e-07f + 1e-30f);
-                    sapx[ct][e] = sv;
-                    seps[ct][e] = ev;
+                    sub[ct][e] = sv + ev;
                     float x = sv - ev;
 #pragma unroll
                     for (int r = 0; r < KL; ++r) {
@@ -214,7 +249,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int pos = 16 * ct + 4 * g + e;
-                if (pos < npool && sapx[ct][e] + seps[ct][e] >= theta) cmask |= 1u << (4 * ct + e);
+                if (pos < npool && sub[ct][e] >= theta) cmask |= 1u << (4 * ct + e);
             }
         }
         // At least min(K, pool) cells are contenders. With no more than K of them
