@@ -85,12 +85,14 @@ __host__ __device__ inline int64_t vt_head_elems(const KParams &p) { return vt_g
 // one contiguous 16-byte piece.
 __host__ __device__ inline int vt_pos(int t) { return 8 * ((t & 15) >> 2) + (t & 3) + 4 * (t >> 4); }
 // LDS swizzles applied by the tile copies (16-byte pieces) and undone by the
-// operand reads, chosen so that the 16 lanes of one MFMA operand read hit
-// distinct banks: key rows (d/8 chunks) and value rows (4 pieces).
+// operand reads: key rows (d/8 chunks) and value rows (4 pieces). Both were
+// measured with a bank-conflict probe on gfx950: a 16-byte operand read of
+// either kind takes 4 LDS cycles per wave, the conflict-free minimum (the
+// value swizzle ((dim >> 1) ^ (dim >> 3)) & 3 took 8).
 __host__ __device__ inline int swz_key(int row, int d) {
     return d == 128 ? (row & 15) : ((row ^ (row >> 3)) & 7);
 }
-__host__ __device__ inline int swz_val(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
+__host__ __device__ inline int swz_val(int dim) { return (dim >> 1) & 3; }
 
 // Work-group order for L2 reuse. The dispatcher deals consecutive work-group ids
 // to the eight XCDs in turn, and each XCD has its own L2; this bijection of

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
     constexpr int VIT = kRopeSpan * D / 8 / 2 / 256;  // value items (token pair x 8 dims) per thread
     constexpr int TLD = kRopeSpan + 8;         // transposed tile row stride
     static_assert(KIT >= 1 && VIT >= 1, "tile work must cover every thread");
-    __shared__ uint16_t s_t[D * TLD];          // fp16 bits, [dim][token]
+    __shared__ __attribute__((aligned(16))) uint16_t s_t[D * TLD];  // fp16 bits, [dim][token]
 
     const int h = blockIdx.y;
     const int64_t j0 = (int64_t)blockIdx.x * kRopeSpan;
