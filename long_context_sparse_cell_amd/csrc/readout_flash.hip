@@ -99,6 +99,13 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     const int64_t hN = (int64_t)h * p.N;
     const float sl2 = p.scale * 1.4426950408889634f;
 
+    // this wave's 16 queries as bf16 MFMA B operands, requested before the setup
+    const int qwl = 16 * wave;  // first query (local) of this wave
+    const int qrow = min(qwl + col, max(nq - 1, 0));
+    R8 bq[QS];
+#pragma unroll
+    for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qrow) * D + 32 * ks + 8 * g);
+
     // ---- which queries selected which pool cell
     for (int t = tid; t < npool; t += kRfThreads) {
         s_pool[t] = pool[((int64_t)h * p.nblk + b) * p.PW + t];
@@ -137,12 +144,6 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     __syncthreads();
     const int nact = s_nact;
 
-    // ---- this wave's 16 queries as bf16 MFMA B operands
-    const int qwl = 16 * wave;  // first query (local) of this wave
-    const int qrow = min(qwl + col, max(nq - 1, 0));
-    R8 bq[QS];
-#pragma unroll
-    for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qrow) * D + 32 * ks + 8 * g);
 
     // ---- copy plan: a cell's keys then its values in 1 KB units; this wave copies
     // units wave + 8 i. Every wave issues exactly UPW copies per cell (spare units
