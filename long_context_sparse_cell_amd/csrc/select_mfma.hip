@@ -303,14 +303,16 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
 }
 
 // Exact re-scoring of the near-tie queries listed by select_mfma_kernel: one
-// wave per scoring work-group's region, one query at a time; lane l scores the contenders at
-// pool positions l and 64 + l with the fp64 fma chain of the oracle, then the
-// wave picks the K best by (score desc, cell asc) and lists them by cell.
+// work-group of four waves per scoring work-group's region, wave w taking its
+// near-ties w, w + 4, ...; lane l scores the contenders at pool positions l and
+// 64 + l with the fp64 fma chain of the oracle, then ranks each of its
+// contenders against all of the query's contenders (read lane by lane), keeps
+// the K best by (score desc, cell asc) and writes them in cell order.
 // Comparisons are written as selects: a conditional-swap list insert with
 // double keys was compiled into wrong code (equal keys lost the index
 // tie-break) by this toolchain at -O3.
 template <int D>
-__global__ __launch_bounds__(64) void select_fixup_kernel(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(256) void select_fixup_kernel(const uint16_t *__restrict__ q,
                                                            const float *__restrict__ kbar,
                                                            const float *__restrict__ amax,
                                                            const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
@@ -318,7 +320,8 @@ __global__ __launch_bounds__(64) void select_fixup_kernel(const uint16_t *__rest
     const int64_t region = blockIdx.x;
     const uint32_t n = fix[region];
     const int lane = threadIdx.x & 63;
-    for (uint32_t j = 0; j < n; ++j) {
+    const uint32_t wave = threadIdx.x >> 6;
+    for (uint32_t j = wave; j < n; j += 4) {
         const uint32_t *e = fix_region(fix, p, region) + (size_t)j * kFixWords;
         const int h = (int)e[0];
         const int64_t i = (int64_t)e[1];
@@ -338,17 +341,19 @@ __global__ __launch_bounds__(64) void select_fixup_kernel(const uint16_t *__rest
         const int32_t *prow = pool + ((int64_t)h * p.nblk + b) * p.PW;
         const uint16_t *qg = q + ((int64_t)h * p.N + i) * D;
         const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
-        // this lane's (up to two) contenders, best first
-        double v0 = -INFINITY, v1 = -INFINITY;
-        int c0 = INT_MAX, c1 = INT_MAX;
-#pragma unroll
+        // this lane's contenders: pool positions lane (half 0) and 64 + lane (half 1)
+        double vh[2] = {-INFINITY, -INFINITY};
+        int ch[2] = {INT_MAX, INT_MAX};
+#pragma unroll 1
         for (int half = 0; half < 2; ++half) {
             const uint64_t bm = half ? bm_hi : bm_lo;
             if (!((bm >> lane) & 1ull)) continue;
             const int c = prow[64 * half + lane];
             const float *krow = kbar + ((int64_t)h * p.C + c) * D;
+            const float am = amax[(int64_t)h * p.C + c];
             double content = 0.0;
-            // 32 elements per step, all loads of a step issued before its fma chain
+            // 32 elements per step, two steps' loads issued before their fma chain
+#pragma unroll 2
             for (int x0 = 0; x0 < D; x0 += 32) {
                 uint4 qv[4];
                 float4 kv[8];
@@ -368,56 +373,41 @@ __global__ __launch_bounds__(64) void select_fixup_kernel(const uint16_t *__rest
             }
             const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
             const double gg = arg >= 6.0 ? 1.0 : erf(arg);
-            const double bias = __dmul_rn(__dmul_rn(lam, (double)amax[(int64_t)h * p.C + c]), gg);
-            const double v = __fma_rn(rho, content, bias);
-            // pool positions ascend with the cell, so the second candidate has the larger cell
-            const bool first = v > v0 || (v == v0 && c < c0);
-            v1 = first ? v0 : v;
-            c1 = first ? c0 : c;
-            v0 = first ? v : v0;
-            c0 = first ? c : c0;
+            const double bias = __dmul_rn(__dmul_rn(lam, (double)am), gg);
+            vh[half] = __fma_rn(rho, content, bias);
+            ch[half] = c;
         }
-        int res[kSelK];
+        // rank every contender against all of them: (score desc, cell asc); the K best
+        // are selected, and pool order is cell order, so a selected contender's output
+        // slot is the number of selected contenders at lower pool positions
+        int rank[2] = {0, 0};
 #pragma unroll
-        for (int r = 0; r < kSelK; ++r) {
-            double bv = v0;
-            int bc = c0;
+        for (int half = 0; half < 2; ++half) {
+            uint64_t bm = half ? bm_hi : bm_lo;
+            while (bm) {
+                const int src = __ffsll((unsigned long long)bm) - 1;
+                bm &= bm - 1;
+                const double vy = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(vh[half]), src),
+                                                   __builtin_amdgcn_readlane(__double2loint(vh[half]), src));
+                const int cy = __builtin_amdgcn_readlane(ch[half], src);
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const double ov = __shfl_xor(bv, off);
-                const int oc = __shfl_xor(bc, off);
-                const bool take = ov > bv || (ov == bv && oc < bc);
-                bv = take ? ov : bv;
-                bc = take ? oc : bc;
+                for (int x = 0; x < 2; ++x)
+                    rank[x] += (vy > vh[x] || (vy == vh[x] && cy < ch[x])) ? 1 : 0;
             }
-            res[r] = (r < p.K && bc != INT_MAX) ? bc : INT_MAX;
-            const bool pop = bc != INT_MAX && c0 == bc;
-            v0 = pop ? v1 : v0;
-            c0 = pop ? c1 : c0;
-            v1 = pop ? -INFINITY : v1;
-            c1 = pop ? INT_MAX : c1;
         }
-        if (lane == 0) {
-#pragma unroll
-            for (int x = 0; x < kSelK; ++x)
-#pragma unroll
-                for (int y = 0; y + 1 < kSelK - x; ++y) {
-                    const bool sw = res[y] > res[y + 1];
-                    const int lo2 = sw ? res[y + 1] : res[y], hi2 = sw ? res[y] : res[y + 1];
-                    res[y] = lo2;
-                    res[y + 1] = hi2;
-                }
-            int32_t *o = sel + ((int64_t)h * p.N + i) * p.K;
-#pragma unroll
-            for (int r = 0; r < kSelK; ++r)
-                if (r < p.K) o[r] = res[r] == INT_MAX ? -1 : res[r];
-        }
+        const bool s0 = ch[0] != INT_MAX && rank[0] < p.K;
+        const bool s1 = ch[1] != INT_MAX && rank[1] < p.K;
+        const uint64_t b0 = __ballot(s0), b1 = __ballot(s1);
+        const uint64_t below = (1ull << lane) - 1ull;
+        int32_t *o = sel + ((int64_t)h * p.N + i) * p.K;
+        if (s0) o[__popcll(b0 & below)] = ch[0];
+        if (s1) o[__popcll(b0) + __popcll(b1 & below)] = ch[1];
     }
 }
 
 hipError_t launch_select_fixup(const void *q, const float *kbar, const float *amax, const int32_t *pool,
                                int32_t *sel, const uint32_t *fix, const KParams &p, hipStream_t st) {
-    const dim3 grid((unsigned)fix_regions(p)), block(64);
+    const dim3 grid((unsigned)fix_regions(p)), block(256);
     if (p.d == 64)
         hipLaunchKernelGGL((select_fixup_kernel<64>), grid, block, 0, st, (const uint16_t *)q, kbar, amax, pool, sel,
                            fix, p);
