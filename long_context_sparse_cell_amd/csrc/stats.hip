@@ -28,23 +28,41 @@ __global__ __launch_bounds__(256) void cell_stats_kernel(const T *__restrict__ k
     const int nrows = ncell * s;
     const T *src = k + ((int64_t)h * p.N + c0 * s) * D;
 
+    // a tile holds at most 8192 elements (the launcher checks cpb * s * D <= 8192), so at
+    // most 8192 / VEC 16-byte vectors: a fixed number per thread, all issued before any
+    // is stored
+    constexpr int VPT = 8192 / VEC / 256;
     const int nvec = nrows * (D / VEC);
-    for (int e = threadIdx.x; e < nvec; e += 256) {
+    uint4 raw[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        // vectors past the tile read its last row again (every load is issued, so the
+        // waits below cover them all at once) and are not stored
+        const int e = min((int)threadIdx.x + 256 * u, nvec - 1);
+        const int r = e / (D / VEC), x = (e % (D / VEC)) * VEC;
+        raw[u] = *reinterpret_cast<const uint4 *>(src + (int64_t)r * D + x);
+    }
+    // consume every loaded register here, so that no load is moved into the guarded
+    // stores below (and waited for one at a time)
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) asm volatile("" ::"v"(raw[u].x), "v"(raw[u].y), "v"(raw[u].z), "v"(raw[u].w));
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int e = (int)threadIdx.x + 256 * u;
+        if (e >= nvec) continue;
         const int r = e / (D / VEC), x = (e % (D / VEC)) * VEC;
         if constexpr (sizeof(T) == 2) {
-            uint4 raw = *reinterpret_cast<const uint4 *>(src + (int64_t)r * D + x);
-            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+            const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 tile[r * LD + x + 2 * t] = __uint_as_float(w4[t] << 16);
                 tile[r * LD + x + 2 * t + 1] = __uint_as_float(w4[t] & 0xFFFF0000u);
             }
         } else {
-            float4 raw = *reinterpret_cast<const float4 *>(src + (int64_t)r * D + x);
-            tile[r * LD + x + 0] = raw.x;
-            tile[r * LD + x + 1] = raw.y;
-            tile[r * LD + x + 2] = raw.z;
-            tile[r * LD + x + 3] = raw.w;
+            tile[r * LD + x + 0] = __uint_as_float(raw[u].x);
+            tile[r * LD + x + 1] = __uint_as_float(raw[u].y);
+            tile[r * LD + x + 2] = __uint_as_float(raw[u].z);
+            tile[r * LD + x + 3] = __uint_as_float(raw[u].w);
         }
     }
     __syncthreads();
@@ -81,6 +99,7 @@ template <typename T, int D>
 static hipError_t launch_stats_t(const void *k, float *kbar, float *amax, const KParams &p, hipStream_t st) {
     int cpb = 256 / D;
     while (cpb > 1 && (size_t)cpb * p.s * (D + 1) * sizeof(float) > 48 * 1024) cpb /= 2;
+    if ((size_t)cpb * p.s * D > 8192) return hipErrorInvalidValue;  // the kernel's per-thread load count
     dim3 grid((unsigned)((p.C + cpb - 1) / cpb), (unsigned)p.H);
     size_t lds = (size_t)cpb * p.s * (D + 1) * sizeof(float);
     hipLaunchKernelGGL((cell_stats_kernel<T, D>), grid, dim3(256), lds, st, (const T *)k, kbar, amax, p, cpb);
