@@ -104,6 +104,28 @@ def test_small_shapes_every_query(oracle, name, shape_over, par_over):
     compare_full(oracle, inp, run, orc_over)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_exact_score_ties_resolve_by_cell_index(oracle, d):
+    """Copies of one high-norm key block in several cells give those cells identical
+    means, norms and (far from the query, where the erf factor is 1) identical scores.
+    The pool must keep the lowest indices among equal norms and the top-K the lowest
+    indices among equal scores, bit-exactly: on the GPU the certified filter cannot
+    separate the copies, so every one of them goes through the exact re-scoring."""
+    _print_case(f"exact_ties_d{d}")
+    sh = synth.Shape(f"ties_d{d}", H=1, N=4096, d=d, dtype=synth.BF16, seed=11, s=32, B=128, w=512, P=8, W=2, K=4)
+    inp = synth.random_inputs(sh)
+    dup = [5, 9, 14, 20, 33, 41, 52, 60]
+    blk = inp.k[0, 0:sh.s].copy() * 3.0
+    for c in dup:
+        inp.k[0, c * sh.s:(c + 1) * sh.s] = blk
+    inp.k = synth.to_dtype(inp.k, sh.dtype)
+    run = GpuRun(inp)
+    compare_full(oracle, inp, run)
+    # the ties decided the result: late queries see all copies and take the four lowest
+    sel = run.sel.cpu().numpy()[0]
+    np.testing.assert_array_equal(sel[sh.N - 1], dup[:4])
+
+
 def test_bf16_input_fp32_output(oracle):
     _print_case("bf16_in_f32_out")
     sh = synth.Shape("bf16_f32out", H=2, N=4096, d=64, dtype=synth.BF16, seed=8)
