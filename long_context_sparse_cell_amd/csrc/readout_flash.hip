@@ -325,10 +325,19 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     if (ql < nq) {
         const float gam = p.gamma[h];
         const int64_t row = hN + q0 + ql;
+        // every local-branch load first (consumed by an empty asm, so none of them is
+        // moved past a store and waited for one at a time)
+        float4 owv[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            owv[dt] = *reinterpret_cast<const float4 *>(o_win + row * D + 16 * dt + 4 * g);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            asm volatile("" ::"v"(owv[dt].x), "v"(owv[dt].y), "v"(owv[dt].z), "v"(owv[dt].w));
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
             const int c0 = 16 * dt + 4 * g;
-            const float4 ow = *reinterpret_cast<const float4 *>(o_win + row * D + c0);
+            const float4 ow = owv[dt];
             const float o4[4] = {ow.x, ow.y, ow.z, ow.w};
             float val[4];
 #pragma unroll
