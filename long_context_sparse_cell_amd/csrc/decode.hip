@@ -413,18 +413,20 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
             for (int d2 = 0; d2 < DPL; ++d2) o[d2] *= alpha;
             m_run = m_new;
             // lanes as dimensions: o[lane*DPL + d2] += p_u v_u, the weight taken from lane u
+            // value rows in batches of KB keys, each batch's loads issued together
+            constexpr int KB = 16;
             const int nk = min(64, nkeys - c0);
 #pragma unroll 1
-            for (int k0 = 0; k0 < nk; k0 += 8) {
-                float vv[8][DPL];
+            for (int k0 = 0; k0 < nk; k0 += KB) {
+                float vv[KB][DPL];
 #pragma unroll
-                for (int j2 = 0; j2 < 8; ++j2) {
+                for (int j2 = 0; j2 < KB; ++j2) {
                     const T *vr = vrow(c0 + min(k0 + j2, nk - 1)) + lane * DPL;
 #pragma unroll
                     for (int d2 = 0; d2 < DPL; ++d2) vv[j2][d2] = to_f32<T>(vr[d2]);
                 }
 #pragma unroll
-                for (int j2 = 0; j2 < 8; ++j2) {
+                for (int j2 = 0; j2 < KB; ++j2) {
                     // weight of key k0 + j2, broadcast from its lane (zero past the chunk's end)
                     const float pk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), k0 + j2));
 #pragma unroll
