@@ -191,13 +191,17 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
         for (int tt = 0; tt < 2 * KK; ++tt) {
             sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
             if (tt < NT) {
+                // the tile's key operands in one inline-asm block (one wait for all of them)
                 const int row = 16 * tt + col;
+                auto kaddr = [&](int ks) { return &kc[row * D + 8 * ((4 * ks + g) ^ swz_key(row, D))]; };
+                R8 ka[QS];
+                if constexpr (QS == 4)
+                    lds_read16x4(ka[0].u, ka[1].u, ka[2].u, ka[3].u, kaddr(0), kaddr(1), kaddr(2), kaddr(3));
+                else
+                    lds_read16x2(ka[0].u, ka[1].u, kaddr(0), kaddr(1));
 #pragma unroll
-                for (int ks = 0; ks < QS; ++ks) {
-                    R8 ka;
-                    ka.u = *reinterpret_cast<const uint4 *>(&kc[row * D + 8 * ((4 * ks + g) ^ swz_key(row, D))]);
-                    sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.b, bq[ks].b, sacc[tt], 0, 0, 0);
-                }
+                for (int ks = 0; ks < QS; ++ks)
+                    sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks].b, bq[ks].b, sacc[tt], 0, 0, 0);
             }
         }
         float mx = -INFINITY;
