@@ -60,9 +60,12 @@ enum fsl_dtype { FSL_F32 = 0, FSL_BF16 = 1 };
  * sigma_h=4, lambda_h=1 (digest, core method; ai.info summary, methodology
  * and training paragraph). Limits of this implementation: d in {64, 128};
  * s in {16, 32, 64} with s dividing B; B a multiple of 16, at most 256;
- * 0 <= P <= 64; 0 <= W <= 64; 1 <= K <= 8; w >= 1; H >= 1; 1 <= N < 2^31.
- * P = -1 (no pruning, the plain FS variant) is defined by the method but not
- * implemented here (FSL_E_UNSUPPORTED). */
+ * -1 <= P <= 64; 0 <= W <= 64; 1 <= K <= 8; w >= 1; H >= 1; 1 <= N < 2^31.
+ * P = -1 selects the plain FS variant (digest, core method: FS-L is FS with the
+ * norm prune added): every query of block b scores all n_b eligible cells, no
+ * pool is formed and W is unused. The streaming decode needs P >= 0 (its
+ * bounded state holds P + W pool cells) and returns FSL_E_UNSUPPORTED for
+ * P = -1. */
 typedef struct fsl_params {
     int64_t N;          /* tokens in the sequence (forward); ignored by decode */
     int32_t H;          /* heads */
@@ -118,7 +121,8 @@ int fsl_cell_stats(const void *k, float *kbar, float *amax, const fsl_params *p,
  * (dot product a left-to-right fma chain over x, inputs the float32 cell
  * statistics) and keeps the K best under (score desc, index asc).
  * q: device [H][N][d] (dtype); kbar/amax as produced by fsl_cell_stats;
- * pool: device [H][ceil(N/B)][P+W] int32, ascending, padded with -1;
+ * pool: device [H][ceil(N/B)][P+W] int32, ascending, padded with -1 (with
+ * P = -1 the pool is every eligible cell and is not written: pool may be NULL);
  * sel: device [H][N][K] int32, ascending, padded with -1.
  * ws: device workspace of at least fsl_workspace_bytes(p) bytes. */
 int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_t *pool,
@@ -173,6 +177,9 @@ typedef struct fsl_workspace_layout {
     size_t kt;      /* fp16 [H][Np][d] RoPE-rotated keys, Np = 64 ceil(N/64) (bf16 only) */
     size_t vt;      /* fp16 [H][Np/32][d][32] values transposed per 32 tokens (bf16 only) */
     size_t fixups;  /* uint32 near-tie query list of the bf16 scoring (bf16 only) */
+    size_t khi;     /* bf16 [H][C][d] head of every kbar_c (bf16 with P = -1 only) */
+    size_t klo;     /* bf16 [H][C][d] tail kbar_c - khi (bf16 with P = -1 only) */
+    size_t kcf;     /* float4 [H][C] per-cell constants of the scoring bound (bf16 with P = -1 only) */
     size_t total;   /* bytes; equals fsl_workspace_bytes */
 } fsl_workspace_layout;
 int fsl_workspace_views(const fsl_params *p, fsl_workspace_layout *out);

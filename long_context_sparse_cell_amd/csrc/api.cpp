@@ -31,7 +31,7 @@ int check(const fsl_params *p) {
     if (p->d != 64 && p->d != 128) return FSL_E_UNSUPPORTED;
     if (p->s != 16 && p->s != 32 && p->s != 64) return FSL_E_UNSUPPORTED;
     if (p->B % 16 != 0 || p->B > 256) return FSL_E_UNSUPPORTED;
-    if (p->P < 0 || p->P > 64 || p->W > 64 || p->K > 8) return FSL_E_UNSUPPORTED;
+    if (p->P > 64 || p->W > 64 || p->K > 8) return FSL_E_UNSUPPORTED;
     // work-group ids over (head, 64-token tile) must fit one 32-bit grid dimension
     if ((p->N / 64 + 1) * (int64_t)p->H >= (int64_t(1) << 31)) return FSL_E_UNSUPPORTED;
     return FSL_OK;
@@ -44,7 +44,7 @@ KParams kparams(const fsl_params *p) {
     k.C = p->N / p->s;
     k.nblk = (p->N + p->B - 1) / p->B;
     k.H = p->H; k.d = p->d; k.w = p->w; k.s = p->s; k.P = p->P; k.W = p->W; k.K = p->K; k.B = p->B;
-    k.PW = p->P + p->W;
+    k.PW = p->P < 0 ? 0 : p->P + p->W;  // no pool table without pruning
     k.dtype = p->dtype; k.out_dtype = p->out_dtype;
     k.scale = p->scale > 0.0f ? p->scale : (float)(1.0 / std::sqrt((double)p->d));
     k.rho = p->rho; k.rope_base = p->rope_base; k.rms_eps = p->rms_eps;
@@ -75,12 +75,14 @@ fsl_workspace_layout layout(const KParams &k, bool full = true) {
     L.rope_abs = take(bf ? (size_t)(rope_abs_rows_hi(k) + kRopeSpan) * (k.d / 2) * sizeof(float2) : 0);
     L.kt = take(bf ? (size_t)k.H * kt_head_elems(k) * sizeof(uint16_t) : 0);
     L.vt = take(bf ? (size_t)k.H * vt_head_elems(k) * sizeof(uint16_t) : 0);
-    L.fixups = take(bf ? (size_t)fix_words(k) * sizeof(uint32_t) : 0);
+    const bool fs = k.P < 0;  // no pruning: a contender list per near-tie, and the split cell means
+    L.fixups = take(bf ? (size_t)(fs ? fix_words_fs(k) : fix_words(k)) * sizeof(uint32_t) : 0);
+    L.khi = take(bf && fs ? (size_t)k.H * k.C * k.d * sizeof(uint16_t) : 0);
+    L.klo = take(bf && fs ? (size_t)k.H * k.C * k.d * sizeof(uint16_t) : 0);
+    L.kcf = take(bf && fs ? (size_t)k.H * k.C * sizeof(float4) : 0);
     L.total = off;
     return L;
 }
-
-bool k_has_fix(const fsl_workspace_layout &L) { return L.total > L.fixups; }
 
 Work carve(void *ws, const fsl_workspace_layout &L) {
     char *b = (char *)ws;
@@ -96,7 +98,10 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
     w.rope_abs = (float2 *)(b + L.rope_abs);
     w.kt = (uint16_t *)(b + L.kt);
     w.vt = (uint16_t *)(b + L.vt);
-    w.fix = k_has_fix(L) ? (uint32_t *)(b + L.fixups) : nullptr;
+    w.fix = L.khi > L.fixups ? (uint32_t *)(b + L.fixups) : nullptr;  // present iff it has bytes
+    w.khi = L.klo > L.khi ? (uint16_t *)(b + L.khi) : nullptr;
+    w.klo = L.kcf > L.klo ? (uint16_t *)(b + L.klo) : nullptr;
+    w.kcf = L.total > L.kcf ? (float4 *)(b + L.kcf) : nullptr;
     return w;
 }
 
@@ -110,7 +115,8 @@ int check_decode(const fsl_params *p) {
     q.N = 1;
     int rc = check(&q);
     if (rc != FSL_OK) return rc;
-    if (p->w > kDecodeMaxW) return FSL_E_UNSUPPORTED;
+    // the bounded state holds P + W pool cells: the unpruned variant has no such bound
+    if (p->P < 0 || p->w > kDecodeMaxW) return FSL_E_UNSUPPORTED;
     return FSL_OK;
 }
 
@@ -190,14 +196,21 @@ int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_
                      const fsl_params *p, void *ws, size_t ws_bytes, hipStream_t stream) {
     int rc = check(p);
     if (rc != FSL_OK) return rc;
-    if (!q || !kbar || !amax || !pool || !sel || !ws) return FSL_E_INVAL;
+    const bool fs = p->P < 0;  // no pruning: no pool is written and pool may be NULL
+    if (!q || !kbar || !amax || (!pool && !fs) || !sel || !ws) return FSL_E_INVAL;
     if (!aligned16(q) || !aligned4(kbar) || !aligned4(amax) || !aligned4(pool) || !aligned4(sel) || !aligned16(ws))
         return FSL_E_INVAL;
     const KParams k = kparams(p);
     const fsl_workspace_layout L = layout(k);
     if (ws_bytes < L.total) return FSL_E_WORKSPACE;
     const Work w = carve(ws, L);
-    hipError_t e = launch_prune(amax, pool, w, k, stream);
+    hipError_t e = hipSuccess;
+    if (fs) {
+        e = k.dtype == FSL_BF16 ? launch_select_fs(q, kbar, amax, sel, w, k, stream)
+                                : launch_select(q, kbar, amax, nullptr, sel, k, stream);
+        return hip_status(e);
+    }
+    e = launch_prune(amax, pool, w, k, stream);
     if (e == hipSuccess)
         e = k.dtype == FSL_BF16 ? launch_select_mfma(q, kbar, amax, pool, sel, w.fix, k, stream)
                                 : launch_select(q, kbar, amax, pool, sel, k, stream);
@@ -227,9 +240,12 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
     };
     hipError_t e = mark(hipSuccess);
     if (e == hipSuccess) e = mark(launch_cell_stats(k, w.kbar, w.amax, kp, stream));
-    if (e == hipSuccess) e = mark(launch_prune(w.amax, w.pool, w, kp, stream));
+    const bool fs = kp.P < 0;  // no pruning: the prune stage is empty
+    if (e == hipSuccess) e = mark(fs ? hipSuccess : launch_prune(w.amax, w.pool, w, kp, stream));
     if (e == hipSuccess)
-        e = mark(kp.dtype == FSL_BF16
+        e = mark(fs ? (kp.dtype == FSL_BF16 ? launch_select_fs(q, w.kbar, w.amax, w.sel, w, kp, stream)
+                                            : launch_select(q, w.kbar, w.amax, nullptr, w.sel, kp, stream))
+                 : kp.dtype == FSL_BF16
                      ? (launch_select_mfma(q, w.kbar, w.amax, w.pool, w.sel, w.fix, kp, stream) == hipSuccess
                             ? launch_select_fixup(q, w.kbar, w.amax, w.pool, w.sel, w.fix, kp, stream)
                             : hipErrorLaunchFailure)

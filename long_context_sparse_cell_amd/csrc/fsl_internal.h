@@ -43,6 +43,10 @@ struct Work {
     // one region of kFixRegion entries per scoring work-group (fix_region), and
     // the number of entries each region holds at fix[0 .. fix_regions)
     uint32_t *fix;
+    // bf16 scoring without pruning (P = -1) only: the bf16 head and tail of every
+    // kbar_c, [H][C][d] each, and the per-cell constants of the error bound [H][C]
+    uint16_t *khi, *klo;
+    float4 *kcf;
 };
 
 constexpr int kFixRegion = 128;  // entries per region (queries per scoring work-group)
@@ -60,6 +64,21 @@ __host__ __device__ inline uint32_t *fix_region(uint32_t *fix, const KParams &p,
 }
 __host__ __device__ inline const uint32_t *fix_region(const uint32_t *fix, const KParams &p, int64_t r) {
     return fix + (fix_regions(p) + 63) / 64 * 64 + r * kFixRegion * kFixWords;
+}
+
+// Without pruning (P = -1) a near-tie entry lists its contender cells instead of a
+// pool mask: head, row, the count (kFsOverflow: re-score every eligible cell), an
+// unused word and up to 32 cell indices.
+constexpr int kFixWordsFs = 36;
+constexpr uint32_t kFsOverflow = 0xFFFFFFFFu;
+__host__ __device__ inline int64_t fix_words_fs(const KParams &p) {
+    return (fix_regions(p) + 63) / 64 * 64 + fix_regions(p) * kFixRegion * kFixWordsFs;
+}
+__host__ __device__ inline uint32_t *fix_region_fs(uint32_t *fix, const KParams &p, int64_t r) {
+    return fix + (fix_regions(p) + 63) / 64 * 64 + r * kFixRegion * kFixWordsFs;
+}
+__host__ __device__ inline const uint32_t *fix_region_fs(const uint32_t *fix, const KParams &p, int64_t r) {
+    return fix + (fix_regions(p) + 63) / 64 * 64 + r * kFixRegion * kFixWordsFs;
 }
 
 constexpr int kChunk = 64;    // cells per prune-scan chunk (one wave)
@@ -208,6 +227,16 @@ __device__ __forceinline__ void barrier_no_fence() {
     asm volatile("" ::: "memory");
 }
 
+// Sum over the aligned group of 8 lanes that holds lane l (lanes 8 (l / 8) ..
+// 8 (l / 8) + 7) with three DPP moves: swap neighbours, swap pairs, mirror the
+// halves of the group. Every lane of the group ends with the same sum.
+__device__ __forceinline__ float sum8_dpp(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    return x;
+}
+
 // 2^x with the hardware instruction alone (no denormal range scaling): softmax
 // weights below 2^-126 of the running maximum are flushed to zero.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -304,6 +333,8 @@ hipError_t launch_select_mfma(const void *q, const float *kbar, const float *ama
                               int32_t *sel, uint32_t *fix, const KParams &p, hipStream_t st);
 hipError_t launch_select_fixup(const void *q, const float *kbar, const float *amax, const int32_t *pool,
                                int32_t *sel, const uint32_t *fix, const KParams &p, hipStream_t st);
+hipError_t launch_select_fs(const void *q, const float *kbar, const float *amax, int32_t *sel, const Work &w,
+                            const KParams &p, hipStream_t st);
 hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st);
 hipError_t launch_window(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
                          const KParams &p, hipStream_t st);

@@ -7,7 +7,9 @@
 // wave's queries held in registers as MFMA operands). Every query's cells come
 // from the block's pool, so the workgroup walks the pool cells that at least
 // one of its queries selected, in ascending cell order: each selected cell is
-// read from memory once per block. A cell's keys (raw bf16 rows) and values
+// read from memory once per block. Without pruning (P = -1) there is no pool
+// table: the workgroup sorts its queries' selections (at most 512 entries, so
+// 64 queries per workgroup when K > 4) and walks the distinct cells. A cell's keys (raw bf16 rows) and values
 // (fp16, transposed per 32-token group in vt_pos order, from kv_prep.hip; a
 // 16-token cell brings its whole group) are copied from global memory straight
 // into LDS (global_load_lds, 16 bytes per lane) through a ring of one-cell
@@ -24,6 +26,8 @@
 // kept maximum) and O^T = V^T P^T (fp16 MFMA) held in registers; the lanes of
 // a query column own its statistics. A query's result depends only on its own
 // cells in ascending order, so the output is deterministic.
+#include <climits>
+
 #include "fsl_internal.h"
 
 namespace fsl {
@@ -38,6 +42,7 @@ constexpr int kRfThreads = 512;     // 8 waves
 constexpr int kRfWaves = kRfThreads / 64;
 constexpr int kRfMaxQ = 128;
 constexpr int kRfMaxPool = 128;
+constexpr int kRfMaxSel = 512;  // selections of one work-group without pruning
 
 union R8 {
     uint4 u;
@@ -55,7 +60,7 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
 
 }  // namespace
 
-template <int D, int S>
+template <int D, int S, bool FS>
 __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ sel, const int32_t *__restrict__ pool, const float *__restrict__ o_win,
@@ -79,10 +84,11 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t s_v1[VCELL];
     __shared__ __attribute__((aligned(1024))) uint16_t s_v2[NS > 2 ? VCELL : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t s_v3[NS > 2 ? VCELL : 8];
-    __shared__ int s_pool[kRfMaxPool];
-    __shared__ uint32_t s_mask[kRfMaxPool][4];   // which local queries selected pool position t
-    __shared__ uint32_t s_amask[kRfMaxPool][4];  // s_mask in compacted (ascending cell) order
-    __shared__ int s_acell[kRfMaxPool];          // the compacted cells
+    constexpr int MAXA = FS ? kRfMaxSel : kRfMaxPool;  // distinct cells a work-group can walk
+    __shared__ int s_pool[FS ? 1 : kRfMaxPool];
+    __shared__ uint32_t s_mask[FS ? 1 : kRfMaxPool][4];  // which local queries selected pool position t
+    __shared__ uint32_t s_amask[MAXA][4];  // which local queries selected the a-th walked cell
+    __shared__ int s_acell[MAXA];          // the walked cells, ascending
     __shared__ int s_nact;
 
     const int nqb = (int)((p.N + QW - 1) / QW);
@@ -106,42 +112,95 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
 #pragma unroll
     for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + q0 + qrow) * D + 32 * ks + 8 * g);
 
-    // ---- which queries selected which pool cell
-    for (int t = tid; t < npool; t += kRfThreads) {
-        s_pool[t] = pool[((int64_t)h * p.nblk + b) * p.PW + t];
-        s_mask[t][0] = s_mask[t][1] = s_mask[t][2] = s_mask[t][3] = 0u;
-    }
-    __syncthreads();
-    for (int pr = tid; pr < nq * K; pr += kRfThreads) {
-        const int c = sel[(hN + q0) * K + pr];
-        if (c < 0) continue;
-        int lo = 0, hi = npool - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (s_pool[mid] < c) lo = mid + 1; else hi = mid;
+    if constexpr (FS) {
+        // ---- the distinct selected cells: sort the work-group's selections (bitonic,
+        // in the first value slot, which the ring fills only later), keep the first of
+        // each run, then mark which queries selected each
+        int *s_sort = reinterpret_cast<int *>(s_v0);
+        static_assert(VCELL * 2 >= kRfMaxSel * 4, "sort scratch fits a value slot");
+        const int nent = nq * K;
+        for (int t = tid; t < kRfMaxSel; t += kRfThreads) {
+            const int c = t < nent ? sel[(hN + q0) * K + t] : -1;
+            s_sort[t] = c < 0 ? INT_MAX : c;
         }
-        const int ql = pr / K;
-        atomicOr(&s_mask[lo][ql >> 5], 1u << (ql & 31));
-    }
-    __syncthreads();
-    if (wave == 0) {
-        // compact the selected positions in pool (= ascending cell) order
-        int base = 0;
-        for (int t0 = 0; t0 < npool; t0 += 64) {
-            const int t = t0 + lane;
-            const bool on = t < npool && (s_mask[t][0] | s_mask[t][1] | s_mask[t][2] | s_mask[t][3]) != 0u;
-            const uint64_t bal = __ballot(on);
-            if (on) {
-                const int a = base + __popcll(bal & ((1ull << lane) - 1ull));
-                s_acell[a] = s_pool[t];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) s_amask[a][x] = s_mask[t][x];
+        __syncthreads();
+        for (int len = 2; len <= kRfMaxSel; len <<= 1)
+            for (int st = len >> 1; st > 0; st >>= 1) {
+                for (int t = tid; t < kRfMaxSel / 2; t += kRfThreads) {
+                    const int lo = 2 * st * (t / st) + (t % st), hi = lo + st;
+                    const bool up = (lo & len) == 0;
+                    const int a = s_sort[lo], c = s_sort[hi];
+                    s_sort[lo] = up ? min(a, c) : max(a, c);
+                    s_sort[hi] = up ? max(a, c) : min(a, c);
+                }
+                __syncthreads();
             }
-            base += __popcll(bal);
+        if (wave == 0) {
+            int base = 0;
+            for (int t0 = 0; t0 < kRfMaxSel; t0 += 64) {
+                const int t = t0 + lane;
+                const int c = s_sort[t];
+                const bool on = c != INT_MAX && (t == 0 || s_sort[t - 1] != c);
+                const uint64_t bal = __ballot(on);
+                if (on) s_acell[base + __popcll(bal & ((1ull << lane) - 1ull))] = c;
+                base += __popcll(bal);
+            }
+            if (lane == 0) s_nact = base;
         }
-        if (lane == 0) s_nact = base;
+        __syncthreads();
+        const int na = s_nact;
+        for (int t = tid; t < na; t += kRfThreads) s_amask[t][0] = s_amask[t][1] = s_amask[t][2] = s_amask[t][3] = 0u;
+        __syncthreads();
+        for (int pr = tid; pr < nent; pr += kRfThreads) {
+            const int c = sel[(hN + q0) * K + pr];
+            if (c < 0) continue;
+            int lo = 0, hi = na - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_acell[mid] < c) lo = mid + 1; else hi = mid;
+            }
+            const int ql = pr / K;
+            atomicOr(&s_amask[lo][ql >> 5], 1u << (ql & 31));
+        }
+        __syncthreads();
+    } else {
+        // ---- which queries selected which pool cell
+        for (int t = tid; t < npool; t += kRfThreads) {
+            s_pool[t] = pool[((int64_t)h * p.nblk + b) * p.PW + t];
+            s_mask[t][0] = s_mask[t][1] = s_mask[t][2] = s_mask[t][3] = 0u;
+        }
+        __syncthreads();
+        for (int pr = tid; pr < nq * K; pr += kRfThreads) {
+            const int c = sel[(hN + q0) * K + pr];
+            if (c < 0) continue;
+            int lo = 0, hi = npool - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_pool[mid] < c) lo = mid + 1; else hi = mid;
+            }
+            const int ql = pr / K;
+            atomicOr(&s_mask[lo][ql >> 5], 1u << (ql & 31));
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // compact the selected positions in pool (= ascending cell) order
+            int base = 0;
+            for (int t0 = 0; t0 < npool; t0 += 64) {
+                const int t = t0 + lane;
+                const bool on = t < npool && (s_mask[t][0] | s_mask[t][1] | s_mask[t][2] | s_mask[t][3]) != 0u;
+                const uint64_t bal = __ballot(on);
+                if (on) {
+                    const int a = base + __popcll(bal & ((1ull << lane) - 1ull));
+                    s_acell[a] = s_pool[t];
+    #pragma unroll
+                    for (int x = 0; x < 4; ++x) s_amask[a][x] = s_mask[t][x];
+                }
+                base += __popcll(bal);
+            }
+            if (lane == 0) s_nact = base;
+        }
+        __syncthreads();
     }
-    __syncthreads();
     const int nact = s_nact;
 
 
@@ -364,14 +423,21 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
 template <int D, int S>
 static void launch_rf(dim3 grid, hipStream_t st, const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
                       const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p, int QW) {
-    hipLaunchKernelGGL((readout_flash_kernel<D, S>), grid, dim3(kRfThreads), 0, st, (const uint16_t *)q,
-                       (const uint16_t *)k, vt, sel, pool, o_win, out, o_long_out, p, QW);
+    if (p.P < 0)
+        hipLaunchKernelGGL((readout_flash_kernel<D, S, true>), grid, dim3(kRfThreads), 0, st, (const uint16_t *)q,
+                           (const uint16_t *)k, vt, sel, pool, o_win, out, o_long_out, p, QW);
+    else
+        hipLaunchKernelGGL((readout_flash_kernel<D, S, false>), grid, dim3(kRfThreads), 0, st, (const uint16_t *)q,
+                           (const uint16_t *)k, vt, sel, pool, o_win, out, o_long_out, p, QW);
 }
 
 hipError_t launch_readout_flash(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
                                 const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p,
                                 hipStream_t st) {
-    const int QW = p.B <= kRfMaxQ ? p.B : p.B / 2;
+    // queries per work-group: half a block when B > 128; without pruning also at most
+    // kRfMaxSel / K, so that the work-group's selections fit the sort
+    const int qmax = p.P < 0 && p.K > 4 ? kRfMaxSel / 8 : kRfMaxQ;
+    const int QW = p.B <= qmax ? p.B : (p.B / 2 <= qmax ? p.B / 2 : p.B / 4);
     dim3 grid((unsigned)(((p.N + QW - 1) / QW) * p.H));
 #define FSL_RF(DD, SS) launch_rf<DD, SS>(grid, st, q, k, vt, sel, pool, o_win, out, o_long_out, p, QW)
     if (p.d == 64) {

@@ -33,8 +33,9 @@ __global__ __launch_bounds__(256) void select_kernel(const T *__restrict__ q, co
     const int64_t i = b * p.B + tid;
     const bool active = tid < p.B && i < p.N;
     const int64_t nb = eligible_cells(p, b);
-    const int npool = (int)min((int64_t)p.PW, nb);
-    const int32_t *bp = pool + ((int64_t)h * p.nblk + b) * p.PW;
+    const bool fs = p.P < 0;  // no pruning: every eligible cell, no pool table
+    const int npool = fs ? (int)nb : (int)min((int64_t)p.PW, nb);
+    const int32_t *bp = fs ? nullptr : pool + ((int64_t)h * p.nblk + b) * p.PW;
 
     float qf[D];
     const T *qi = q + ((int64_t)h * p.N + (active ? i : 0)) * D;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void select_kernel(const T *__restrict__ q, co
     for (int r = 0; r < kMaxK; ++r) { bs[r] = -INFINITY; bi[r] = INT_MAX; }
 
     for (int t = 0; t < npool; ++t) {
-        const int c = bp[t];
+        const int c = fs ? t : bp[t];
         const float *kb = kbar + ((int64_t)h * p.C + c) * D;
         double content = 0.0;
 #pragma unroll

@@ -1,0 +1,503 @@
+// Cell scoring and top-K without pruning: the plain FreeSolo (FS) variant, in
+// which every query of block b scores all n_b cells that lie wholly before the
+// window of the block's first query (FreeSolo digest, core method: the long
+// branch's candidates are the available cells, FS-L differs only by the norm
+// prune; method steps 4 and 5: score = content match plus a norm-weighted erf
+// relative-position bias, top K cells per query).
+//
+// The exact score is the one of select.hip and of the oracle:
+//   s = fma(rho, q.kbar_c, (lambda * a_c) * erf(sigma (i - c s) / (2 s)))
+// in fp64 with the dot product a left-to-right fma chain. The bf16 path
+// certifies an MFMA approximation and re-scores only what it cannot separate:
+//
+//  1. fs_prep_kernel splits every float32 kbar_c once into bf16 head + tail
+//     (hi, lo) and stores the per-cell constants of the error bound.
+//  2. select_fs_kernel streams the block's cells through LDS in chunks of 64
+//     (double buffered) and computes content~ = q.(hi + lo) on
+//     v_mfma_f32_16x16x32_bf16, with the bound |s - s~| <= eps of the pool
+//     scoring kernel (select_mfma.hip). Each lane (one query, four cells of
+//     every 16-cell tile) keeps the kFsCap cells of largest upper bound
+//     ub = s~ + eps, with lb = s~ - eps. A cell whose ub is below the smallest
+//     lb of the list's K leading entries is beaten by those K cells and is not
+//     inserted. At the end theta = the K-th largest lb over the query's four
+//     lists; the contenders are the listed cells with ub >= theta. Every true
+//     top-K cell has ub >= its score >= theta, so it is a contender unless a
+//     full list dropped it, which needs that list's smallest ub to reach theta
+//     (an overflow). Without overflow, at most K contenders are the top-K set.
+//  3. Near-ties (more than K contenders) and overflows go to a per-work-group
+//     list; select_fs_fixup_kernel re-scores the contenders (or, after an
+//     overflow, every eligible cell) exactly as the oracle does.
+#include <climits>
+
+#include "fsl_internal.h"
+
+namespace fsl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kFsChunk = 64;  // cells per LDS chunk
+constexpr int kFsCap = 8;     // listed cells per lane
+constexpr int kFsK = 8;       // largest K
+
+union U16x8f {
+    uint4 u;
+    bf16x8 b;
+    uint16_t h[8];
+};
+
+// the bound's constant for a dot product over d coordinates (select_mfma.hip)
+__host__ __device__ constexpr float fs_eps_content(int d) {
+    return 1.001f * (7.62939453125e-06f + (float)(4 * d + 8) * 5.9604644775390625e-08f);
+}
+
+// One 16-byte piece u (row u / (D/8), piece u % (D/8)) of a chunk's split means:
+// rows past the block's last cell read that cell again (they are never scored).
+template <int D>
+__device__ __forceinline__ void fs_load_piece(const uint16_t *__restrict__ khi, const uint16_t *__restrict__ klo,
+                                              int64_t hC, int64_t c0, int64_t clast, int u, uint4 &h, uint4 &l) {
+    const int64_t c = min(c0 + u / (D / 8), clast);
+    const int64_t off = (hC + c) * D + 8 * (u % (D / 8));
+    h = *reinterpret_cast<const uint4 *>(khi + off);
+    l = *reinterpret_cast<const uint4 *>(klo + off);
+}
+template <int D, int HLD>
+__device__ __forceinline__ void fs_store_piece(uint16_t *s_hi, uint16_t *s_lo, int u, const uint4 &h, const uint4 &l) {
+    *reinterpret_cast<uint4 *>(&s_hi[(u / (D / 8)) * HLD + 8 * (u % (D / 8))]) = h;
+    *reinterpret_cast<uint4 *>(&s_lo[(u / (D / 8)) * HLD + 8 * (u % (D / 8))]) = l;
+}
+
+}  // namespace
+
+// kbar -> khi, klo (bf16 head and tail, round to nearest even) and
+// kcf = (lambda a_c, |rho| ||kbar_c|| eps, |lambda a_c| 2e-6, c s as int bits).
+// Row r by 8 consecutive threads, 64 rows per work-group.
+template <int D>
+__global__ __launch_bounds__(512) void fs_prep_kernel(const float *__restrict__ kbar, const float *__restrict__ amax,
+                                                      uint16_t *__restrict__ khi, uint16_t *__restrict__ klo,
+                                                      float4 *__restrict__ kcf, KParams p) {
+    constexpr int FPT = D / 8;
+    const int h = blockIdx.y;
+    const int64_t r = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 3);
+    const int part = threadIdx.x & 7;
+    const bool ok = r < p.C;
+    const int64_t rr = ok ? r : p.C - 1;
+    const float *src = kbar + ((int64_t)h * p.C + rr) * D + FPT * part;
+    float4 f[FPT / 4];
+#pragma unroll
+    for (int x = 0; x < FPT / 4; ++x) f[x] = *reinterpret_cast<const float4 *>(src + 4 * x);
+    float ss = 0.0f;
+    uint16_t *dh = khi + ((int64_t)h * p.C + rr) * D + FPT * part;
+    uint16_t *dl = klo + ((int64_t)h * p.C + rr) * D + FPT * part;
+#pragma unroll
+    for (int x = 0; x < FPT / 4; ++x) {
+        const float fx[4] = {f[x].x, f[x].y, f[x].z, f[x].w};
+        union { __bf16 b[4]; uint2 u; } hi4, lo4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const __bf16 hb = (__bf16)fx[t];
+            hi4.b[t] = hb;
+            lo4.b[t] = (__bf16)(fx[t] - (float)hb);
+            ss += fx[t] * fx[t];
+        }
+        if (ok) {
+            *reinterpret_cast<uint2 *>(dh + 4 * x) = hi4.u;
+            *reinterpret_cast<uint2 *>(dl + 4 * x) = lo4.u;
+        }
+    }
+    ss = sum8_dpp(ss);  // all 8 threads of the row take part
+    if (ok && part == 0) {
+        const float la = p.lambda[h] * amax[(int64_t)h * p.C + r];
+        kcf[(int64_t)h * p.C + r] = make_float4(la, fabsf(p.rho) * sqrtf(ss) * fs_eps_content(D), fabsf(la) * 2e-6f,
+                                                __int_as_float((int)(r * p.s)));
+    }
+}
+
+template <int D, int KL>
+__global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ khi,
+                                                        const uint16_t *__restrict__ klo,
+                                                        const float4 *__restrict__ kcf, int32_t *__restrict__ sel,
+                                                        uint32_t *__restrict__ fix, KParams p, int QW) {
+    constexpr int HLD = D + 8;     // bf16 row stride in LDS (272 B for d = 128)
+    constexpr int QS = D / 32;
+    constexpr int CH = kFsChunk;
+    constexpr int VPR = D / 8;     // 16-byte pieces per row
+    constexpr int VPT = CH * VPR / 512;  // pieces per thread per array and chunk
+    __shared__ __attribute__((aligned(16))) uint16_t s_hi[2][CH * HLD];
+    __shared__ __attribute__((aligned(16))) uint16_t s_lo[2][CH * HLD];
+    __shared__ float4 s_cf[2][CH];
+    __shared__ int s_nfix;
+
+    const int nqb = (int)((p.N + QW - 1) / QW);
+    const int logical = xcd_remap((int)blockIdx.x, nqb * p.H);
+    const int h = logical / nqb;
+    const int64_t q0 = (int64_t)(logical % nqb) * QW;
+    const int64_t b = q0 / p.B;
+    const int nq = (int)min((int64_t)QW, p.N - q0);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, g = lane >> 4;
+    const int K = p.K;
+    const int n = (int)eligible_cells(p, b);
+    const int nch = (n + CH - 1) / CH;
+    const int64_t hN = (int64_t)h * p.N;
+    const int64_t hC = (int64_t)h * p.C;
+    const float sigf = p.sigma[h], rhof = p.rho;
+    const float karg = sigf / (2.0f * (float)p.s);
+
+    const int ql = 16 * wave + col;
+    const bool qok = ql < nq;
+    const int64_t i = q0 + (qok ? ql : 0);
+    U16x8f bq[QS];
+#pragma unroll
+    for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + i) * D + 32 * ks + 8 * g);
+    if (tid == 0) s_nfix = 0;
+
+    // ---- chunk staging in registers: every load of a chunk is issued before any is
+    // stored. Plain variables, not arrays, so that nothing of it lives in scratch.
+    static_assert(VPT == 1 || VPT == 2, "one or two 16-byte pieces per thread and array");
+    uint4 rh0, rl0, rh1, rl1;
+    float4 rcf = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t nlast = (int64_t)n - 1;
+    auto load = [&](int t) __attribute__((always_inline)) {
+        fs_load_piece<D>(khi, klo, hC, (int64_t)t * CH, nlast, tid, rh0, rl0);
+        if constexpr (VPT > 1) fs_load_piece<D>(khi, klo, hC, (int64_t)t * CH, nlast, tid + 512, rh1, rl1);
+        if (tid < CH) rcf = kcf[hC + min((int64_t)t * CH + tid, nlast)];
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+        fs_store_piece<D, HLD>(s_hi[buf], s_lo[buf], tid, rh0, rl0);
+        if constexpr (VPT > 1) fs_store_piece<D, HLD>(s_hi[buf], s_lo[buf], tid + 512, rh1, rl1);
+        if (tid < CH) s_cf[buf][tid] = rcf;
+    };
+
+    float qss = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < QS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float f = bf16_to_f32(bq[ks].h[e]);
+            qss += f * f;
+        }
+    const float qn = sqrtf(colsum4(qss));  // the four lanes of a query hold all its d elements
+
+    // this lane's list: the kFsCap cells of largest upper bound, descending
+    float lu[kFsCap], ll[kFsCap];
+    int li[kFsCap];
+#pragma unroll
+    for (int r = 0; r < kFsCap; ++r) { lu[r] = -INFINITY; ll[r] = -INFINITY; li[r] = INT_MAX; }
+    float thr = -INFINITY;  // smallest lb among the K leading entries
+
+    if (nch > 0) {
+        load(0);
+        store(0);
+        if (nch > 1) load(1);
+    }
+    __syncthreads();
+    for (int t = 0; t < nch; ++t) {
+        const int buf = t & 1;
+        const int c0 = t * CH;
+        // erf is 1 (in fp32 and fp64) once its argument reaches 6; cells are ascending
+        // and every query is at or after q0, so the chunk's last cell decides for all
+        const int clast = min(c0 + CH, n) - 1;
+        const bool need_erf = !((float)((int)q0 - clast * p.s) * karg >= 6.0f);
+#pragma unroll
+        for (int ct = 0; ct < CH / 16; ++ct) {
+            const int rowc = 16 * ct + col;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < QS; ++ks) {
+                U16x8f hi, lo;
+                hi.u = *reinterpret_cast<const uint4 *>(&s_hi[buf][rowc * HLD + 32 * ks + 8 * g]);
+                lo.u = *reinterpret_cast<const uint4 *>(&s_lo[buf][rowc * HLD + 32 * ks + 8 * g]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi.b, bq[ks].b, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.b, bq[ks].b, acc, 0, 0, 0);
+            }
+            // read the accumulators in straight-line code right after the MFMAs, where the
+            // compiler pads the MFMA-to-VALU dependency with wait states; the empty asm keeps
+            // these reads here, ahead of the branches below (a read placed after a branch
+            // was seen taking the accumulator before the MFMA had written it)
+            float rcv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rcv[e] = rhof * acc[e];
+            asm volatile("" : "+v"(rcv[0]), "+v"(rcv[1]), "+v"(rcv[2]), "+v"(rcv[3]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int loc = 16 * ct + 4 * g + e;
+                const int c = c0 + loc;
+                const float4 cf = s_cf[buf][loc];
+                float bf = cf.x;  // lambda a_c times the erf factor 1
+                if (need_erf) {
+                    const float argf = (float)((int)i - __float_as_int(cf.w)) * karg;
+                    if (argf < 6.0f) bf = cf.x * erff(argf);
+                }
+                const float rc = rcv[e];
+                const float sv = rc + bf;
+                const float ev =
+                    2.0f * (fmaf(qn, cf.y, cf.z) + (fabsf(rc) + fabsf(bf)) * 2.384185791015625e-07f + 1e-30f);
+                float cu = c < n ? sv + ev : -INFINITY;
+                if (cu >= thr && cu > lu[kFsCap - 1]) {
+                    float cl = sv - ev;
+                    int ci = c;
+                    // carry the cell down the list (selects only)
+#pragma unroll
+                    for (int r = 0; r < kFsCap; ++r) {
+                        const bool bt = cu > lu[r];
+                        const float tu = lu[r], tl = ll[r];
+                        const int ti = li[r];
+                        lu[r] = bt ? cu : tu;
+                        ll[r] = bt ? cl : tl;
+                        li[r] = bt ? ci : ti;
+                        cu = bt ? tu : cu;
+                        cl = bt ? tl : cl;
+                        ci = bt ? ti : ci;
+                    }
+                    float m = INFINITY;
+#pragma unroll
+                    for (int r = 0; r < kFsK; ++r)
+                        if (r < K) m = fminf(m, ll[r]);
+                    thr = m;
+                }
+            }
+        }
+        if (t + 1 < nch) {
+            store(buf ^ 1);
+            if (t + 2 < nch) load(t + 2);
+        }
+        __syncthreads();
+    }
+
+    // ---- theta = K-th largest lb over the query's four lists: each lane sorts its
+    // lbs (descending, KL kept), then the lists of the query column are merged
+    float lbk[KL];
+#pragma unroll
+    for (int r = 0; r < KL; ++r) lbk[r] = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < kFsCap; ++s2) {
+        float x = ll[s2];
+#pragma unroll
+        for (int r = 0; r < KL; ++r) {
+            const float hi = fmaxf(lbk[r], x);
+            x = fminf(lbk[r], x);
+            lbk[r] = hi;
+        }
+    }
+#pragma unroll
+    for (int m2 = 16; m2 <= 32; m2 <<= 1) {
+        float pl[KL];
+#pragma unroll
+        for (int r = 0; r < KL; ++r) pl[r] = __shfl_xor(lbk[r], m2);
+#pragma unroll
+        for (int r = 0; r < KL; ++r) lbk[r] = fmaxf(lbk[r], pl[KL - 1 - r]);
+#pragma unroll
+        for (int st = KL / 2; st > 0; st >>= 1)
+#pragma unroll
+            for (int r = 0; r < KL; ++r)
+                if ((r & st) == 0) {
+                    const float hi = fmaxf(lbk[r], lbk[r + st]), lo = fminf(lbk[r], lbk[r + st]);
+                    lbk[r] = hi;
+                    lbk[r + st] = lo;
+                }
+    }
+    float theta = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < KL; ++r)
+        if (r == K - 1) theta = lbk[r];
+
+    // contenders of this lane; an overflow if a full list's smallest ub reaches theta
+    int cid[kFsCap];
+    int mycnt = 0;
+#pragma unroll
+    for (int r = 0; r < kFsCap; ++r) {
+        const bool on = li[r] != INT_MAX && lu[r] >= theta;
+        cid[r] = on ? li[r] : INT_MAX;
+        mycnt += on ? 1 : 0;
+    }
+    const bool over_l = li[kFsCap - 1] != INT_MAX && lu[kFsCap - 1] >= theta;
+    const int ncont = (int)colsum4((float)mycnt);
+    const bool over = colmax4(over_l ? 1.0f : 0.0f) > 0.0f;
+
+    // lane g == 0 of each query column gathers the column's contenders (all lanes
+    // take part in the shuffles)
+    int gath[kFsCap * 4];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int r = 0; r < kFsCap; ++r) gath[gg * kFsCap + r] = __shfl(cid[r], col + 16 * gg);
+    if (qok && g == 0) {
+        if (over || ncont > K) {
+            const int slot = atomicAdd(&s_nfix, 1);
+            uint32_t *e = fix_region_fs(fix, p, logical) + (size_t)slot * kFixWordsFs;
+            e[0] = (uint32_t)h;
+            e[1] = (uint32_t)i;
+            e[2] = over ? kFsOverflow : (uint32_t)ncont;
+            e[3] = 0u;
+            int k2 = 0;
+#pragma unroll
+            for (int x = 0; x < kFsCap * 4; ++x) {
+                if (gath[x] != INT_MAX) {
+                    e[4 + k2] = (uint32_t)gath[x];
+                    ++k2;
+                }
+            }
+        } else {
+            // at most K contenders: the top-K set, written in ascending cell order
+            int best[kFsK];
+#pragma unroll
+            for (int r = 0; r < kFsK; ++r) best[r] = INT_MAX;
+#pragma unroll
+            for (int x = 0; x < kFsCap * 4; ++x) {
+                int c = gath[x];
+#pragma unroll
+                for (int r = 0; r < kFsK; ++r) {
+                    const int lo = min(best[r], c), hi = max(best[r], c);
+                    best[r] = lo;
+                    c = hi;
+                }
+            }
+            int32_t *o = sel + (hN + i) * K;
+#pragma unroll
+            for (int r = 0; r < kFsK; ++r)
+                if (r < K) o[r] = best[r] == INT_MAX ? -1 : best[r];
+        }
+    }
+    __syncthreads();
+    if (tid == 0) fix[logical] = (uint32_t)s_nfix;
+}
+
+// Exact re-scoring of the near-tie and overflow queries listed by
+// select_fs_kernel: one work-group of four waves per scoring work-group's
+// region, wave w taking entries w, w + 4, ... Each lane scores its share of the
+// candidates (the listed contenders, or every eligible cell after an overflow)
+// with the oracle's fp64 fma chain and keeps its K best under (score desc,
+// cell asc); K rounds of a wave-wide maximum then take the K best overall,
+// written in ascending cell order. Comparisons are written as selects.
+template <int D>
+__global__ __launch_bounds__(256) void select_fs_fixup_kernel(const uint16_t *__restrict__ q,
+                                                              const float *__restrict__ kbar,
+                                                              const float *__restrict__ amax,
+                                                              int32_t *__restrict__ sel,
+                                                              const uint32_t *__restrict__ fix, KParams p) {
+    const int64_t region = blockIdx.x;
+    const uint32_t nfix = fix[region];
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = threadIdx.x >> 6;
+    const int K = p.K;
+    for (uint32_t j = wave; j < nfix; j += 4) {
+        const uint32_t *e = fix_region_fs(fix, p, region) + (size_t)j * kFixWordsFs;
+        const int h = (int)e[0];
+        const int64_t i = (int64_t)e[1];
+        const bool over = e[2] == kFsOverflow;
+        const int64_t ncand = over ? eligible_cells(p, i / p.B) : (int64_t)e[2];
+        const uint16_t *qg = q + ((int64_t)h * p.N + i) * D;
+        const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+        double bs[kFsK];
+        int bi[kFsK];
+#pragma unroll
+        for (int r = 0; r < kFsK; ++r) { bs[r] = -INFINITY; bi[r] = INT_MAX; }
+        for (int64_t t = lane; t < ncand; t += 64) {
+            const int c = over ? (int)t : (int)e[4 + t];
+            const float *krow = kbar + ((int64_t)h * p.C + c) * D;
+            double content = 0.0;
+            for (int x0 = 0; x0 < D; x0 += 8) {
+                const uint4 qv = *reinterpret_cast<const uint4 *>(qg + x0);
+                const float4 k0 = *reinterpret_cast<const float4 *>(krow + x0);
+                const float4 k1 = *reinterpret_cast<const float4 *>(krow + x0 + 4);
+                const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
+                const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float qf = __uint_as_float(u & 1 ? (w4[u >> 1] & 0xFFFF0000u) : (w4[u >> 1] << 16));
+                    content = __fma_rn((double)qf, (double)kf[u], content);
+                }
+            }
+            const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
+            const double gg = arg >= 6.0 ? 1.0 : erf(arg);
+            const double bias = __dmul_rn(__dmul_rn(lam, (double)amax[(int64_t)h * p.C + c]), gg);
+            double sc = __fma_rn(rho, content, bias);
+            int ci = c;
+#pragma unroll
+            for (int r = 0; r < kFsK; ++r) {
+                const bool bt = r < K && better_d(sc, ci, bs[r], bi[r]);
+                const double ts = bs[r];
+                const int ti = bi[r];
+                bs[r] = bt ? sc : ts;
+                bi[r] = bt ? ci : ti;
+                sc = bt ? ts : sc;
+                ci = bt ? ti : ci;
+            }
+        }
+        // K rounds of the wave-wide best head; the winning lane drops its head
+        int win[kFsK];
+#pragma unroll
+        for (int r = 0; r < kFsK; ++r) {
+            win[r] = INT_MAX;
+            if (r >= K) continue;
+            double vs = bs[0];
+            int vi = bi[0];
+#pragma unroll
+            for (int m = 32; m > 0; m >>= 1) {
+                const double ps = __hiloint2double(__shfl_xor(__double2hiint(vs), m), __shfl_xor(__double2loint(vs), m));
+                const int pi = __shfl_xor(vi, m);
+                const bool bt = better_d(ps, pi, vs, vi);
+                vs = bt ? ps : vs;
+                vi = bt ? pi : vi;
+            }
+            win[r] = vi;
+            if (vi != INT_MAX && bi[0] == vi) {
+#pragma unroll
+                for (int x = 0; x + 1 < kFsK; ++x) { bs[x] = bs[x + 1]; bi[x] = bi[x + 1]; }
+                bs[kFsK - 1] = -INFINITY;
+                bi[kFsK - 1] = INT_MAX;
+            }
+        }
+        if (lane == 0) {
+            // ascending cell order, -1 padding
+#pragma unroll
+            for (int x = 0; x < kFsK; ++x)
+#pragma unroll
+                for (int y = 0; y + 1 < kFsK - x; ++y) {
+                    const int lo = min(win[y], win[y + 1]), hi = max(win[y], win[y + 1]);
+                    win[y] = lo;
+                    win[y + 1] = hi;
+                }
+            int32_t *o = sel + ((int64_t)h * p.N + i) * K;
+            for (int r = 0; r < K; ++r) o[r] = win[r] == INT_MAX ? -1 : win[r];
+        }
+    }
+}
+
+hipError_t launch_select_fs(const void *q, const float *kbar, const float *amax, int32_t *sel, const Work &w,
+                            const KParams &p, hipStream_t st) {
+    if (p.C > 0) {
+        const dim3 pg((unsigned)((p.C + 63) / 64), (unsigned)p.H);
+        if (p.d == 64)
+            hipLaunchKernelGGL((fs_prep_kernel<64>), pg, dim3(512), 0, st, kbar, amax, w.khi, w.klo, w.kcf, p);
+        else
+            hipLaunchKernelGGL((fs_prep_kernel<128>), pg, dim3(512), 0, st, kbar, amax, w.khi, w.klo, w.kcf, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int QW = p.B <= kFixRegion ? p.B : p.B / 2;
+    const dim3 grid((unsigned)(((p.N + QW - 1) / QW) * p.H));
+#define FSL_SFS(DD, KK)                                                                                            \
+    hipLaunchKernelGGL((select_fs_kernel<DD, KK>), grid, dim3(512), 0, st, (const uint16_t *)q, w.khi, w.klo, w.kcf, \
+                       sel, w.fix, p, QW)
+    if (p.d == 64) {
+        if (p.K <= 4) FSL_SFS(64, 4); else FSL_SFS(64, 8);
+    } else {
+        if (p.K <= 4) FSL_SFS(128, 4); else FSL_SFS(128, 8);
+    }
+#undef FSL_SFS
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.d == 64)
+        hipLaunchKernelGGL((select_fs_fixup_kernel<64>), grid, dim3(256), 0, st, (const uint16_t *)q, kbar, amax, sel,
+                           w.fix, p);
+    else
+        hipLaunchKernelGGL((select_fs_fixup_kernel<128>), grid, dim3(256), 0, st, (const uint16_t *)q, kbar, amax, sel,
+                           w.fix, p);
+    return hipGetLastError();
+}
+
+}  // namespace fsl

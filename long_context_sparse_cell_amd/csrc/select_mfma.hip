@@ -45,16 +45,6 @@ union U16x8s {
     uint16_t h[8];
 };
 
-// Sum over the aligned group of 8 lanes that holds lane l (lanes 8 (l / 8) ..
-// 8 (l / 8) + 7) with three DPP moves: swap neighbours, swap pairs, mirror the
-// halves of the group. Every lane of the group ends with the same sum.
-__device__ __forceinline__ float sum8_dpp(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
-    return x;
-}
-
 }  // namespace
 
 template <int D, int KL>

@@ -40,7 +40,7 @@ class Params(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win", "rope_abs", "kt", "vt",
-                                      "fixups", "total")]
+                                      "fixups", "khi", "klo", "kcf", "total")]
 
 
 _lib = None
@@ -163,8 +163,9 @@ def cell_stats(k: torch.Tensor, p: Params, kbar: Optional[torch.Tensor] = None,
 
 def prune_select(q: torch.Tensor, kbar: torch.Tensor, amax: torch.Tensor, p: Params,
                  ws: Optional[torch.Tensor] = None, stream=None):
+    """Pools and per-query selections; without pruning (P = -1) no pool is formed and None is returned for it."""
     nblk = (p.N + p.B - 1) // p.B
-    pool = torch.empty((p.H, nblk, p.P + p.W), dtype=torch.int32, device=q.device)
+    pool = torch.empty((p.H, nblk, p.P + p.W), dtype=torch.int32, device=q.device) if p.P >= 0 else None
     sel = torch.empty((p.H, p.N, p.K), dtype=torch.int32, device=q.device)
     ws = new_workspace(p, q.device) if ws is None else ws
     _check(lib().fsl_prune_select(_ptr(q), _ptr(kbar), _ptr(amax), _ptr(pool), _ptr(sel), ctypes.byref(p),
@@ -209,7 +210,8 @@ def workspace_views(ws: torch.Tensor, p: Params):
     return dict(
         kbar=view(L.kbar, p.H * C * p.d, torch.float32, (p.H, C, p.d)),
         amax=view(L.amax, p.H * C, torch.float32, (p.H, C)),
-        pool=view(L.pool, p.H * nblk * (p.P + p.W), torch.int32, (p.H, nblk, p.P + p.W)),
+        pool=view(L.pool, p.H * nblk * max(p.P + p.W, 0), torch.int32, (p.H, nblk, max(p.P + p.W, 0))) if p.P >= 0
+        else None,
         sel=view(L.sel, p.H * p.N * p.K, torch.int32, (p.H, p.N, p.K)),
     )
 

@@ -1,0 +1,132 @@
+"""Parity of the unpruned FS variant (P = -1) of the HIP path with the oracle.
+
+Every query scores all cells that lie wholly before its block's window (no
+pool), so the bf16 scoring streams thousands of cells per query through the
+certified MFMA filter; near-ties and full candidate lists go to the exact fp64
+fix-up. Selections must be bit-exact, outputs within the bf16 / fp32 bars.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fsl_testlib import GpuRun, check_out, host_f32, oracle_head_params
+from long_context_sparse_cell_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_sparse_cell_amd import fsl
+    fsl.lib()  # a missing library is an error here, not a skip
+
+
+def _print_case(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def compare_fs(oracle, inp, run, rows=None):
+    sh = inp.shape
+    assert run.views["pool"] is None  # no pool table without pruning
+    kbar = host_f32(run.views["kbar"]); amax = host_f32(run.views["amax"])
+    sel = run.sel.cpu().numpy()
+    out = host_f32(run.out)
+    out_dtype = synth.F32 if run.p.out_dtype == 0 else synth.BF16
+    for h in range(sh.H):
+        p = oracle_head_params(oracle, sh, inp, h)
+        assert p.P == -1
+        r = oracle.forward_head(inp.q[h], inp.k[h], inp.v[h], p, rows=rows, want_stats=True)
+        np.testing.assert_array_equal(kbar[h], r["kbar"], err_msg=f"kbar head {h}")
+        np.testing.assert_array_equal(amax[h], r["amax"], err_msg=f"amax head {h}")
+        idx = r["rows"]
+        np.testing.assert_array_equal(sel[h][idx], r["sel"], err_msg=f"sel head {h}")
+        mx, mean = check_out(out[h][idx], r["out"], out_dtype, f"out head {h}")
+        print(f"  head {h}: out max err {mx:.3e}, mean {mean:.3e}, min top-K margin {r['margin'].min():.3e}",
+              flush=True)
+    return sel
+
+
+SMALL_FS = [
+    ("fs_bf16_d64_n8192_h2", dict(H=2, N=8192, d=64, dtype=synth.BF16), {}),
+    ("fs_bf16_d128_n5000_h2", dict(H=2, N=5000, d=128, dtype=synth.BF16), {}),
+    ("fs_f32_d64_n4096_h1", dict(H=1, N=4096, d=64, dtype=synth.F32), {}),
+    ("fs_f32_d128_n2100_h2", dict(H=2, N=2100, d=128, dtype=synth.F32), {}),
+    ("fs_bf16_d64_n3000_k8", dict(H=2, N=3000, d=64, dtype=synth.BF16, K=8), {}),
+    ("fs_bf16_d64_n4100_sigma005", dict(H=2, N=4100, d=64, dtype=synth.BF16), dict(sigma=0.05)),
+    ("fs_bf16_d128_n5000_b256_k5", dict(H=1, N=5000, d=128, dtype=synth.BF16, B=256, K=5), {}),
+    ("fs_bf16_d64_n3000_small_window", dict(H=2, N=3000, d=64, dtype=synth.BF16, w=64, s=16, B=64, K=3), {}),
+    ("fs_bf16_d64_n700_h3", dict(H=3, N=700, d=64, dtype=synth.BF16), {}),
+    ("fs_bf16_d64_n1_h1", dict(H=1, N=1, d=64, dtype=synth.BF16), {}),
+    ("fs_bf16_d128_n6000_s64_k2", dict(H=1, N=6000, d=128, dtype=synth.BF16, s=64, K=2), {}),
+]
+
+
+@pytest.mark.parametrize("name,shape_over,par_over", SMALL_FS, ids=[c[0] for c in SMALL_FS])
+def test_fs_small_shapes_every_query(oracle, name, shape_over, par_over):
+    _print_case(name)
+    sh = synth.Shape(name, seed=17, P=-1, **shape_over)
+    inp = synth.random_inputs(sh)
+    inp.k[:, ::7] *= 2.5  # varied cell norms
+    inp.k = synth.to_dtype(inp.k, sh.dtype)
+    if "sigma" in par_over:
+        inp.sigma[:] = par_over["sigma"]
+    run = GpuRun(inp)
+    compare_fs(oracle, inp, run)
+
+
+@pytest.mark.parametrize("dup,name", [
+    # one copy per 16-cell tile position spread over the four lane groups: a near-tie
+    # with more than K contenders, re-scored from the contender list
+    ([5, 9, 14, 20, 33, 41, 52, 60], "near_tie"),
+    # nine copies in cells that one lane group scores (positions 0..3 of each 16-cell
+    # tile): that lane's candidate list fills with equal bounds, and the query is
+    # re-scored over every eligible cell
+    ([0, 1, 2, 3, 16, 17, 18, 19, 32, 33], "overflow"),
+])
+def test_fs_exact_ties_resolve_by_cell_index(oracle, dup, name):
+    _print_case(f"fs_exact_ties_{name}")
+    sh = synth.Shape(f"fs_ties_{name}", H=1, N=4096, d=128, dtype=synth.BF16, seed=11, P=-1, K=4)
+    inp = synth.random_inputs(sh)
+    blk = inp.k[0, 40 * sh.s:41 * sh.s].copy() * 3.0
+    for c in dup:
+        inp.k[0, c * sh.s:(c + 1) * sh.s] = blk
+    inp.k = synth.to_dtype(inp.k, sh.dtype)
+    run = GpuRun(inp)
+    sel = compare_fs(oracle, inp, run)
+    np.testing.assert_array_equal(sel[0][sh.N - 1], sorted(dup)[:4])
+
+
+def _sample_rows(sh, n_random=96, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.integers(0, sh.N, size=n_random).tolist())
+    for b in rng.integers(0, (sh.N + sh.B - 1) // sh.B, size=12):
+        t0 = int(b) * sh.B
+        rows.update([t0, min(sh.N - 1, t0 + sh.B - 1)])
+    rows.update([0, sh.N - 1])
+    return rows
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c4"])
+def test_fs_workload_parity_and_needles(oracle, cfg):
+    """The workload shapes with pruning off: every cell is a candidate; sampled rows
+    (random rows, block edges, needle probes) against the oracle, and every needle in
+    its probe queries' selection."""
+    sh = synth.CONFIGS[cfg].replace(P=-1)
+    _print_case(f"fs workload {cfg} {sh.name}")
+    inp = synth.make_inputs(synth.CONFIGS[cfg])
+    inp.shape = sh
+    run = GpuRun(inp)
+    rows = _sample_rows(sh)
+    for pr in inp.probes:
+        rows.update(pr[:8])
+    rows = np.array(sorted(rows), dtype=np.int64)
+    sel = compare_fs(oracle, inp, run, rows=rows)
+    for h in range(sh.H):
+        for m, pos in enumerate(inp.needles[h]):
+            probes = inp.probes[h] if cfg == "c4" else [inp.probes[h][m]]
+            for row in probes:
+                assert pos // sh.s in sel[h][row], (h, pos, row)
+    del run
+    torch.cuda.empty_cache()

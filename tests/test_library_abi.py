@@ -65,7 +65,7 @@ BAD = [
     (dict(N=0), -1), (dict(H=0), -1), (dict(d=63), -1), (dict(s=0), -1), (dict(B=100, s=32), -1),
     (dict(K=0), -1), (dict(W=-1), -1), (dict(P=-2), -1), (dict(dtype=7), -1), (dict(out_dtype=1, dtype=0), -1),
     (dict(rms_eps=0.0), -1), (dict(rope_base=0.0), -1), (dict(w=0), -1), (dict(scale=-1.0), -1),
-    (dict(d=96), -2), (dict(s=8, B=128), -2), (dict(P=65), -2), (dict(P=-1), -2), (dict(K=9), -2),
+    (dict(d=96), -2), (dict(s=8, B=128), -2), (dict(P=65), -2), (dict(K=9), -2),
     (dict(W=65), -2), (dict(B=288, s=32), -2), (dict(B=24, s=8), -2),
 ]
 
@@ -105,6 +105,37 @@ def test_prepared_key_value_arrays_cover_whole_tiles(fsl, N, d):
     p32 = params(fsl, N=N, d=d, H=H, dtype=0, out_dtype=0)
     L32 = fsl.workspace_layout(p32)
     assert L32.total == L32.vt == L32.kt
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_unpruned_variant_workspace(fsl, dtype):
+    """P = -1 (plain FS): no pool table; with bf16 inputs the workspace holds the split cell
+    means (two bf16 [H][C][d] arrays), the per-cell bound constants (float4 [H][C]) and a
+    near-tie list of 36-word entries (head, row, count, unused, 32 cell indices) per query."""
+    H, N, d = 3, 5000, 128
+    p = params(fsl, N=N, H=H, d=d, P=-1, W=8, dtype=dtype, out_dtype=dtype)
+    assert fsl.check_params(p) == 0
+    L = fsl.workspace_layout(p)
+    assert L.sel == L.pool  # zero pool bytes
+    C = N // 32
+    if dtype == 1:
+        regions = H * ((N + 127) // 128)
+        assert L.khi - L.fixups >= 4 * ((regions + 63) // 64 * 64 + regions * 128 * 36)
+        assert L.klo - L.khi >= H * C * d * 2 and L.kcf - L.klo >= H * C * d * 2
+        assert L.total - L.kcf >= H * C * 16
+        assert all(getattr(L, f) % 256 == 0 for f in ("fixups", "khi", "klo", "kcf"))
+    else:
+        assert L.total == L.kcf == L.klo == L.khi
+    # the pruned variant has none of the split arrays
+    Lp = fsl.workspace_layout(params(fsl, N=N, H=H, d=d, dtype=dtype, out_dtype=dtype))
+    assert Lp.total == Lp.kcf == Lp.klo == Lp.khi
+    # pool may be NULL without pruning, not with it
+    lib = fsl.lib()
+    a = ctypes.c_void_p(0x100000)
+    n = fsl.workspace_bytes(p)
+    assert lib.fsl_prune_select(a, a, a, None, a, ctypes.byref(p), a, n - 1, None) == -3
+    pp = params(fsl, N=N, H=H, d=d, dtype=dtype, out_dtype=dtype)
+    assert lib.fsl_prune_select(a, a, a, None, a, ctypes.byref(pp), a, fsl.workspace_bytes(pp), None) == -1
 
 
 def test_null_pointers_and_small_workspace_fail_before_launch(fsl):
