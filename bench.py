@@ -200,6 +200,47 @@ def decode_bench(fsl, synth, torch, dev, steps_override=None):
     }
 
 
+def fs_bench(fsl, synth, torch, inp, q, k, v, dev, steps, warmup):
+    """The same workload without pruning (P = -1, the plain FS variant): every query scores all
+    eligible cells. Stage times from HIP events; the scoring stage's roofline counts the content
+    dot products, 2 d flops per (query, eligible cell), against the bf16 MFMA peak."""
+    sh = inp.shape
+    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in (inp.sigma, inp.lam, inp.gamma))
+    p = fsl.make_params(sh.N, sh.H, sh.d, q.dtype, sig, lam, gam, w=sh.w, s=sh.s, P=-1, W=sh.W, K=sh.K, B=sh.B)
+    ws = fsl.new_workspace(p, dev)
+    out = torch.empty_like(q)
+    nst = fsl.NUM_STAGES + 1
+    ev = HipEvents(nst * max(steps, warmup, 1))
+    for i in range(warmup):
+        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(0, nst))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(i * nst, nst))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    stage_ms = {name: round(float(np.mean([ev.elapsed_ms(i * nst + j, i * nst + j + 1) for i in range(steps)])), 4)
+                for j, name in enumerate(fsl.STAGES)}
+    ev.close()
+    nblk = (sh.N + sh.B - 1) // sh.B
+    pairs = 0
+    for b in range(nblk):
+        nb = max(0, (b * sh.B - sh.w + 1) // sh.s)
+        pairs += nb * (min(sh.N, (b + 1) * sh.B) - b * sh.B)
+    flops = sh.H * 2.0 * sh.d * pairs
+    sel_tf = flops / (stage_ms["select"] * 1e-3) / 1e12
+    del ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": sh.name + "_noprune", "P": -1,
+        "tokens_per_s": round(sh.N * steps / el, 1), "ms_per_step": round(el * 1e3 / steps, 4),
+        "stages": stage_ms,
+        "select_roofline": {"bound": "mfma", "achieved": round(sel_tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(sel_tf / MFMA_F16_PEAK_TFLOPS, 4),
+                            "flops_per_launch": flops},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +250,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-rows", type=int, default=131072)
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
+    ap.add_argument("--no-fs", action="store_true", help="skip the unpruned (P = -1) forward measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, the reference kernel for scaling "
                          "profiler byte counters (FETCH_SIZE / WRITE_SIZE)")
@@ -290,10 +332,19 @@ def main():
     roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                 "unit": dom["unit"], "frac": dom["frac"], "traffic": measured_traffic(dominant)}
 
+    fs = None
+    if not args.no_fs and sh.dtype == synth.BF16:
+        log("[bench] unpruned (P = -1) forward")
+        del ws
+        torch.cuda.empty_cache()
+        fs = fs_bench(fsl, synth, torch, inp, q, k, v, dev, args.steps, args.warmup)
+        ws = None
+        log(f"[bench] unpruned forward {fs['ms_per_step']:.3f} ms/step, stages {fs['stages']}")
+
     dec = None
     if not args.no_decode:
         log("[bench] streaming decode workload")
-        del ws
+        ws = None
         torch.cuda.empty_cache()
         dec = decode_bench(fsl, synth, torch, dev)
         log(f"[bench] decode {dec['tokens_per_s']:.0f} tokens/s, {dec['ms_per_step']:.3f} ms/step")
@@ -327,6 +378,7 @@ def main():
         "union_cells_per_block": round(work.get("_union_cells_per_block", 0.0), 2),
         "distinct_selected_cells": work.get("_distinct_cells"),
         "decode": dec,
+        "noprune": fs,
     }
     print(json.dumps(line), flush=True)
 
