@@ -382,13 +382,26 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
         float o[DPL];
 #pragma unroll
         for (int d2 = 0; d2 < DPL; ++d2) o[d2] = 0.0f;
+        // 16-bit values at d = 64: each half of the wave takes 32 of the chunk's keys and each
+        // lane two adjacent dimensions, so a lane's 32 value pairs (one dword each) are all
+        // requested with the chunk's keys; the halves are added at the end
+        constexpr bool HALF_PV = sizeof(T) == 2 && D == 64;
+        float o2[2] = {0.0f, 0.0f};
+        const int hf = lane >> 5, dp = 2 * (lane & 31);
         for (int c0 = 64 * wave; c0 < nkeys; c0 += 64 * kDecWaves) {
             const int u = c0 + lane;
+            const int nkc = min(64, nkeys - c0);
+            uint32_t vpair[HALF_PV ? 32 : 1];
+            if constexpr (HALF_PV) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    vpair[j] = *reinterpret_cast<const uint32_t *>(vrow(c0 + min(32 * hf + j, nkc - 1)) + dp);
+            }
             float sc = -INFINITY;
             if (u < nkeys) {
                 const KE *kr = krow(u);
                 float dot = 0.0f;
-#pragma unroll 4
+#pragma unroll 2
                 for (int x0 = 0; x0 < D; x0 += 8) {
                     float kf[8];
                     load8f<KE, KF16>(kr + x0, kf);
@@ -411,11 +424,25 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
             l_run = l_run * alpha + ps;
 #pragma unroll
             for (int d2 = 0; d2 < DPL; ++d2) o[d2] *= alpha;
+            o2[0] *= alpha;
+            o2[1] *= alpha;
             m_run = m_new;
+            if constexpr (HALF_PV) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    // weight of key 32 hf + j, from its lane (zero past the chunk's end)
+                    const float p0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), j));
+                    const float p1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), 32 + j));
+                    const float pk = 32 * hf + j < nkc ? (hf ? p1 : p0) : 0.0f;
+                    o2[0] = fmaf(pk, __uint_as_float(vpair[j] << 16), o2[0]);
+                    o2[1] = fmaf(pk, __uint_as_float(vpair[j] & 0xFFFF0000u), o2[1]);
+                }
+                continue;
+            }
             // lanes as dimensions: o[lane*DPL + d2] += p_u v_u, the weight taken from lane u
             // value rows in batches of KB keys, each batch's loads issued together
             constexpr int KB = 16;
-            const int nk = min(64, nkeys - c0);
+            const int nk = nkc;
 #pragma unroll 1
             for (int k0 = 0; k0 < nk; k0 += KB) {
                 float vv[KB][DPL];
@@ -438,8 +465,17 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
             s_wm[wave] = m_run;
             s_wl[wave] = l_run;
         }
+        if constexpr (HALF_PV) {
+            o2[0] += __shfl_xor(o2[0], 32);
+            o2[1] += __shfl_xor(o2[1], 32);
+            if (lane < 32) {
+                s_wo[wave][dp] = o2[0];
+                s_wo[wave][dp + 1] = o2[1];
+            }
+        } else {
 #pragma unroll
-        for (int d2 = 0; d2 < DPL; ++d2) s_wo[wave][lane * DPL + d2] = o[d2];
+            for (int d2 = 0; d2 < DPL; ++d2) s_wo[wave][lane * DPL + d2] = o[d2];
+        }
         __syncthreads();
         if (tid < D) {
             float mm = -INFINITY;
