@@ -80,8 +80,9 @@ def algorithmic_work(sh, sel_np=None):
         "window": ("mfma", H * 4.0 * d * win_keys),
     }
     if sh.dtype == "bf16":
-        # k and v read once, fp16 rotated keys and transposed values written once
-        work["kv_prep"] = ("hbm", H * N * d * (2 * e + 2 * 2))
+        # one fused pass: k and v read once, the cell statistics, the fp16 rotated keys and
+        # the transposed fp16 values written once (the key/value preparation stage is empty)
+        work["cell_stats"] = ("hbm", H * N * d * (2 * e + 2 * 2) + H * C * (d + 1) * 4)
     # q and o_win read, out written, plus the keys and values of every selected cell once
     # per head (keys in the input dtype; values fp16 on the bf16 path, fp32 otherwise)
     readout = H * N * d * (e + 4 + e)

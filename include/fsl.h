@@ -152,8 +152,9 @@ int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const f
 /* fsl_attn_fwd with stage timing. stage_events must point to
  * FSL_NUM_STAGES + 1 caller-created hipEvent_t handles; events[0] is recorded
  * on `stream` before the first kernel and events[s + 1] after stage s, the
- * stages being, in order: cell statistics, norm prune (4 kernels), scoring and
- * top-K, RoPE table (fp32) or RoPE table + key/value preparation (bf16),
+ * stages being, in order: cell statistics (bf16: fused with the RoPE table and
+ * the key/value preparation, one pass over k and v), norm prune (4 kernels;
+ * empty with P = -1), scoring and top-K, RoPE table (fp32; empty for bf16),
  * window attention, readout + mix. Elapsed time between
  * consecutive events is the duration of that stage's kernels. Same arguments,
  * results and errors as fsl_attn_fwd otherwise (FSL_E_INVAL if stage_events

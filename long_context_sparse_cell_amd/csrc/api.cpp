@@ -239,7 +239,12 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
         return e;
     };
     hipError_t e = mark(hipSuccess);
-    if (e == hipSuccess) e = mark(launch_cell_stats(k, w.kbar, w.amax, kp, stream));
+    const bool bf = kp.dtype == FSL_BF16;
+    // bf16: one pass over k and v gives the cell statistics, the rotated fp16 keys and the
+    // transposed fp16 values (recorded as the statistics stage; the preparation stage is empty)
+    if (e == hipSuccess)
+        e = mark(bf ? launch_kv_prep(k, v, w.kt, w.vt, w.rope_abs, w.kbar, w.amax, kp, stream)
+                    : launch_cell_stats(k, w.kbar, w.amax, kp, stream));
     const bool fs = kp.P < 0;  // no pruning: the prune stage is empty
     if (e == hipSuccess) e = mark(fs ? hipSuccess : launch_prune(w.amax, w.pool, w, kp, stream));
     if (e == hipSuccess)
@@ -250,9 +255,7 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
                             ? launch_select_fixup(q, w.kbar, w.amax, w.pool, w.sel, w.fix, kp, stream)
                             : hipErrorLaunchFailure)
                      : launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
-    const bool bf = kp.dtype == FSL_BF16;
-    if (e == hipSuccess)
-        e = mark(bf ? launch_kv_prep(k, v, w.kt, w.vt, w.rope_abs, kp, stream) : launch_rope_table(w.rope, kp, stream));
+    if (e == hipSuccess) e = mark(bf ? hipSuccess : launch_rope_table(w.rope, kp, stream));
     if (e == hipSuccess)
         e = mark(bf ? launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.o_win, kp, stream)
                     : launch_window(q, k, v, w.rope, w.o_win, kp, stream));

@@ -338,8 +338,8 @@ hipError_t launch_select_fs(const void *q, const float *kbar, const float *amax,
 hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st);
 hipError_t launch_window(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
                          const KParams &p, hipStream_t st);
-hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs,
-                          const KParams &p, hipStream_t st);
+hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs, float *kbar,
+                          float *amax, const KParams &p, hipStream_t st);
 hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs, float *o_win,
                               const KParams &p, hipStream_t st);
 hipError_t launch_readout_flash(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,

@@ -10,6 +10,13 @@
 // fp16 holds bf16 values exactly inside fp16's range (|x| < 65504); the
 // fp16-operand products of both branches assume inputs in that range.
 //
+// With kbar/amax given, the same pass also produces the cell statistics of the
+// tile's complete cells (FreeSolo digest, core method and step 3: the mean key
+// and the largest token-key norm of every cell), so k is read from memory once
+// per forward: the raw key rows are kept in LDS, each coordinate's mean is an
+// fp64 sum in token order and each row's squared norm an fp64 fma chain in
+// coordinate order, the orders of cell_stats_kernel (bit-identical results).
+//
 // Angles at large positions are formed from a two-level table built in fp64:
 // pos = 64a + b, (cos, sin)(pos theta) = rotation by (64a theta) composed with
 // rotation by (b theta), so every table entry is a correctly rounded fp32 value
@@ -50,10 +57,11 @@ __global__ void rope_abs_kernel(float2 *__restrict__ tab, int nhi, KParams p) {
     tab[e] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-template <int D>
+template <int D, bool STATS>
 __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
                                                       uint16_t *__restrict__ kt, uint16_t *__restrict__ vt,
-                                                      const float2 *__restrict__ rope, int nhi, KParams p) {
+                                                      const float2 *__restrict__ rope, int nhi, float *__restrict__ kbar,
+                                                      float *__restrict__ amax, KParams p) {
     constexpr int HALF = D / 2;
     constexpr int PG = HALF / 8;               // groups of 8 rotation pairs per row
     constexpr int KIT = kRopeSpan * PG / 256;  // key items per thread
@@ -61,6 +69,11 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
     constexpr int TLD = kRopeSpan + 8;         // transposed tile row stride
     static_assert(KIT >= 1 && VIT >= 1, "tile work must cover every thread");
     __shared__ __attribute__((aligned(16))) uint16_t s_t[D * TLD];  // fp16 bits, [dim][token]
+    // raw key rows for the statistics: a row stride of D + 2 bf16 (an odd number of
+    // dwords) keeps the row-norm threads, one row each, on distinct banks
+    constexpr int KLD = D + 2;
+    __shared__ __attribute__((aligned(16))) uint16_t s_kr[STATS ? kRopeSpan * KLD : 2];
+    __shared__ double s_ss[STATS ? kRopeSpan : 1];
 
     const int h = blockIdx.y;
     const int64_t j0 = (int64_t)blockIdx.x * kRopeSpan;
@@ -83,6 +96,19 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
         const int64_t j = j0 + 2 * jp;
         va[u] = *reinterpret_cast<const uint4 *>(v + (hN + min(j, p.N - 1)) * D + 8 * c8);
         vb[u] = *reinterpret_cast<const uint4 *>(v + (hN + min(j + 1, p.N - 1)) * D + 8 * c8);
+    }
+
+    if constexpr (STATS) {
+        // raw key rows into LDS (rows past the end hold the last row; they belong to no
+        // complete cell)
+#pragma unroll
+        for (int u = 0; u < KIT; ++u) {
+            const int it = tid + 256 * u, jl = it / PG, pg = it % PG;
+            uint32_t *ra = reinterpret_cast<uint32_t *>(&s_kr[jl * KLD + 8 * pg]);
+            uint32_t *rb = reinterpret_cast<uint32_t *>(&s_kr[jl * KLD + HALF + 8 * pg]);
+            ra[0] = ka[u].x; ra[1] = ka[u].y; ra[2] = ka[u].z; ra[3] = ka[u].w;
+            rb[0] = kb[u].x; rb[1] = kb[u].y; rb[2] = kb[u].z; rb[3] = kb[u].w;
+        }
     }
 
     // ---- rotated keys
@@ -127,6 +153,31 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
         }
     }
     __syncthreads();
+    if constexpr (STATS) {
+        // cell statistics of the tile's complete cells (cells of s tokens, s | 64)
+        const int s = p.s;
+        const int cpt = kRopeSpan / s;
+        const int64_t c0 = (int64_t)blockIdx.x * cpt;
+        for (int idx = tid; idx < cpt * D; idx += 256) {
+            const int cl = idx / D, x = idx % D;
+            if (c0 + cl >= p.C) continue;
+            double acc = 0.0;
+            for (int j = 0; j < s; ++j) acc += (double)bf16_to_f32(s_kr[(cl * s + j) * KLD + x]);
+            kbar[((int64_t)h * p.C + c0 + cl) * D + x] = (float)(acc / (double)s);
+        }
+        if (tid < kRopeSpan) {
+            double acc = 0.0;
+            const uint32_t *row = reinterpret_cast<const uint32_t *>(&s_kr[tid * KLD]);
+#pragma unroll 8
+            for (int x2 = 0; x2 < D / 2; ++x2) {
+                const uint32_t w = row[x2];
+                const double e0 = (double)__uint_as_float(w << 16), e1 = (double)__uint_as_float(w & 0xFFFF0000u);
+                acc = __fma_rn(e0, e0, acc);
+                acc = __fma_rn(e1, e1, acc);
+            }
+            s_ss[tid] = acc;
+        }
+    }
     // rows of 32 tokens in vt_pos order: piece g of (group, dim) holds tokens
     // 4g..4g+3 and 16+4g..16+4g+3 of the group; consecutive pieces are consecutive
     // in memory
@@ -142,22 +193,40 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
         *reinterpret_cast<uint4 *>(vt + h * vt_head_elems(p) + ((2 * (int64_t)blockIdx.x + grp) * D + dim) * 32 + 8 * pg) =
             make_uint4(lo.x, lo.y, hi2.x, hi2.y);
     }
+    if constexpr (STATS) {
+        __syncthreads();
+        const int s = p.s;
+        const int cpt = kRopeSpan / s;
+        const int64_t c = (int64_t)blockIdx.x * cpt + tid;
+        if (tid < cpt && c < p.C) {
+            double best = 0.0;
+            for (int j = 0; j < s; ++j) {
+                const double vv = s_ss[tid * s + j];
+                if (vv > best) best = vv;
+            }
+            amax[(int64_t)h * p.C + c] = (float)__dsqrt_rn(best);
+        }
+    }
 }
 
-hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs,
-                          const KParams &p, hipStream_t st) {
+hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs, float *kbar,
+                          float *amax, const KParams &p, hipStream_t st) {
     const int nhi = rope_abs_rows_hi(p);
     const int64_t n = (int64_t)(nhi + kRopeSpan) * (p.d / 2);
     hipLaunchKernelGGL(rope_abs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, rope_abs, nhi, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)nhi, (unsigned)p.H);
-    if (p.d == 64)
-        hipLaunchKernelGGL((kv_prep_kernel<64>), grid, dim3(256), 0, st, (const uint16_t *)k, (const uint16_t *)v, kt,
-                           vt, rope_abs, nhi, p);
-    else
-        hipLaunchKernelGGL((kv_prep_kernel<128>), grid, dim3(256), 0, st, (const uint16_t *)k, (const uint16_t *)v,
-                           kt, vt, rope_abs, nhi, p);
+    const bool stats = kbar && amax;
+#define FSL_KVP(DD, SS)                                                                                            \
+    hipLaunchKernelGGL((kv_prep_kernel<DD, SS>), grid, dim3(256), 0, st, (const uint16_t *)k, (const uint16_t *)v, kt, \
+                       vt, rope_abs, nhi, kbar, amax, p)
+    if (p.d == 64) {
+        if (stats) FSL_KVP(64, true); else FSL_KVP(64, false);
+    } else {
+        if (stats) FSL_KVP(128, true); else FSL_KVP(128, false);
+    }
+#undef FSL_KVP
     return hipGetLastError();
 }
 
