@@ -16,10 +16,12 @@
 //     (double buffered) and computes content~ = q.(hi + lo) on
 //     v_mfma_f32_16x16x32_bf16, with the bound |s - s~| <= eps of the pool
 //     scoring kernel (select_mfma.hip). Each lane (one query, four cells of
-//     every 16-cell tile) keeps the kFsCap cells of largest upper bound
+//     every 16-cell tile) keeps the K_L + 1 cells of largest upper bound (K_L =
+//     4 or 8, at least K)
 //     ub = s~ + eps, with lb = s~ - eps. A cell whose ub is below the smallest
-//     lb of the list's K leading entries is beaten by those K cells and is not
-//     inserted. At the end theta = the K-th largest lb over the query's four
+//     lb of some lane's K leading entries (at any earlier time, shared by the
+//     query's four lanes) is beaten by those K cells and is not inserted. At
+//     the end theta = the K-th largest lb over the query's four
 //     lists; the contenders are the listed cells with ub >= theta. Every true
 //     top-K cell has ub >= its score >= theta, so it is a contender unless a
 //     full list dropped it, which needs that list's smallest ub to reach theta
@@ -39,8 +41,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kFsChunk = 64;  // cells per LDS chunk
-constexpr int kFsCap = 8;     // listed cells per lane
 constexpr int kFsK = 8;       // largest K
+constexpr int kFsMaxCont = kFixWordsFs - 4;  // contender cells a near-tie entry lists
 
 union U16x8f {
     uint4 u;
@@ -125,6 +127,9 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
     constexpr int CH = kFsChunk;
     constexpr int VPR = D / 8;     // 16-byte pieces per row
     constexpr int VPT = CH * VPR / 512;  // pieces per thread per array and chunk
+    // listed cells per lane: one more than the largest K of this instance, so a list
+    // overflows only when a single lane holds K + 1 cells whose bounds reach theta
+    constexpr int kFsCap = KL + 1;
     __shared__ __attribute__((aligned(16))) uint16_t s_hi[2][CH * HLD];
     __shared__ __attribute__((aligned(16))) uint16_t s_lo[2][CH * HLD];
     __shared__ float4 s_cf[2][CH];
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
     int li[kFsCap];
 #pragma unroll
     for (int r = 0; r < kFsCap; ++r) { lu[r] = -INFINITY; ll[r] = -INFINITY; li[r] = INT_MAX; }
-    float thr = -INFINITY;  // smallest lb among the K leading entries
+    float thr = -INFINITY;  // a score that K cells are known to beat: skip cells whose ub is below it
 
     if (nch > 0) {
         load(0);
@@ -256,9 +261,13 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
 #pragma unroll
                     for (int r = 0; r < kFsK; ++r)
                         if (r < K) m = fminf(m, ll[r]);
-                    thr = m;
+                    thr = fmaxf(thr, m);
                 }
             }
+            // a lane's threshold holds for the whole query (K cells beat anything below it),
+            // so the four lanes of the query column take the largest; thresholds stay valid
+            // when the entries that certified them are evicted later
+            thr = colmax4(thr);
         }
         if (t + 1 < nch) {
             store(buf ^ 1);
@@ -315,7 +324,8 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
     }
     const bool over_l = li[kFsCap - 1] != INT_MAX && lu[kFsCap - 1] >= theta;
     const int ncont = (int)colsum4((float)mycnt);
-    const bool over = colmax4(over_l ? 1.0f : 0.0f) > 0.0f;
+    // more contenders than a near-tie entry holds: re-score every eligible cell instead
+    const bool over = colmax4(over_l ? 1.0f : 0.0f) > 0.0f || ncont > kFsMaxCont;
 
     // lane g == 0 of each query column gathers the column's contenders (all lanes
     // take part in the shuffles)
@@ -335,7 +345,7 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
             int k2 = 0;
 #pragma unroll
             for (int x = 0; x < kFsCap * 4; ++x) {
-                if (gath[x] != INT_MAX) {
+                if (gath[x] != INT_MAX && k2 < kFsMaxCont) {
                     e[4 + k2] = (uint32_t)gath[x];
                     ++k2;
                 }
