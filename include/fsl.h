@@ -222,6 +222,24 @@ size_t fsl_decode_prefill_workspace_bytes(const fsl_params *p, int64_t prefix_le
 int fsl_decode_prefill(void *state, size_t state_bytes, int32_t seq, const void *k_prefix, const void *v_prefix,
                        int64_t prefix_len, const fsl_params *p, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Append len tokens to each of the sequences seq0 .. seq0+n-1 without queries:
+ * the streamed (chunked) prefill (ai.info summary, "Why This Matters" and future
+ * directions: a bounded state fed in chunks, so that the prefix's O(N d) keys
+ * and values need not be resident at once). k, v: device [n][H][len][d]
+ * (dtype), for each sequence the tokens at positions t .. t+len-1 where t is
+ * that sequence's current position (0 after fsl_decode_init; the sequences may
+ * be at different positions). One work-group per (sequence, head) walks the
+ * chunk block by block. At every query-block boundary the state's pool is updated
+ * exactly as fsl_decode_step does it, so any split of a prefix into appends, or
+ * a prefill followed by appends, gives the state a single fsl_decode_prefill of
+ * the whole prefix gives (decode results are bit-identical). k and v are not
+ * referenced after the call's work completes; no workspace is needed.
+ * Positions must stay below 2^31 - B. Returns FSL_E_INVAL for a null or
+ * misaligned pointer, len < 1, n < 1 or sequences outside the state's
+ * capacity. */
+int fsl_decode_append(void *state, size_t state_bytes, int32_t seq0, int32_t n, const void *k, const void *v,
+                      int64_t len, const fsl_params *p, hipStream_t stream);
+
 /* Advance every sequence by one token. q, k, v: device [n_seq][H][d] (dtype),
  * the new token of each sequence; out: device [n_seq][H][d] (out_dtype), the
  * attention output at that position. sel_out (nullable): device

@@ -328,6 +328,19 @@ int fsl_decode_prefill(void *state, size_t state_bytes, int32_t seq, const void 
     return hip_status(e);
 }
 
+int fsl_decode_append(void *state, size_t state_bytes, int32_t seq0, int32_t n, const void *k, const void *v,
+                      int64_t len, const fsl_params *p, hipStream_t stream) {
+    int rc = check_decode(p);
+    if (rc != FSL_OK) return rc;
+    if (!state || !k || !v || !aligned16(state) || !aligned16(k) || !aligned16(v)) return FSL_E_INVAL;
+    if (len < 1 || len >= (int64_t(1) << 31) - p->B || seq0 < 0 || n < 1) return FSL_E_INVAL;
+    if ((int64_t)seq0 + n > decode_capacity(p, state_bytes)) return FSL_E_INVAL;
+    if ((int64_t)n * p->H >= (int64_t(1) << 31)) return FSL_E_UNSUPPORTED;
+    fsl_params qq = *p;
+    qq.N = 1;
+    return hip_status(launch_decode_append(state, seq0, n, k, v, len, kparams(&qq), dlayout(p), stream));
+}
+
 int fsl_decode_step(void *state, size_t state_bytes, const void *q, const void *k, const void *v, void *out,
                     int32_t n_seq, const fsl_params *p, int32_t *sel_out, hipStream_t stream) {
     int rc = check_decode(p);

@@ -184,54 +184,19 @@ __global__ void decode_prefill_kernel(char *__restrict__ state, int seq, const T
     }
 }
 
+// Block boundary of a (sequence, head) record, shared by the decode step and the
+// append: when position b B starts a block with new eligible cells (blk is the
+// block of the previous token), the new cells' norms come from the ring, the cells
+// leaving the recent set compete for the P high-norm places, and every newly kept
+// cell's tokens and mean key are copied from the ring into a free slot. s_cell /
+// s_a mirror the record's slot table in LDS and are written back. All threads of
+// the work-group call it (it synchronises).
 template <typename T, int D>
-__global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__restrict__ state, const T *__restrict__ qn,
-                                                                  const T *__restrict__ kn, const T *__restrict__ vn,
-                                                                  void *__restrict__ out, int32_t *__restrict__ sel_out,
-                                                                  KParams p, DecodeLayout L) {
-    __shared__ __attribute__((aligned(16))) float s_q[D];
-    __shared__ int s_cell[kDecMaxPool];
-    __shared__ float s_a[kDecMaxPool];
-    __shared__ double s_score[kDecMaxPool];
-    __shared__ int s_rank[kDecMaxPool];
-    __shared__ int s_sel[8];
-    __shared__ int s_selslot[8];
-    __shared__ float s_red[kDecThreads / 64];
-    __shared__ __attribute__((aligned(16))) float s_qr[D];  // R(t) q
-    __shared__ float s_wm[kDecWaves], s_wl[kDecWaves];     // per-wave softmax state
-    __shared__ float s_wo[kDecWaves][D];                    // per-wave partial outputs
-    __shared__ double s_ss[kDecMaxNew * 64];
-    __shared__ float s_newa[kDecMaxNew];
-    __shared__ int s_load_cell[kDecMaxNew], s_load_slot[kDecMaxNew], s_nload;
-
-    const int rid = blockIdx.x;  // seq * H + h
-    const int h = rid % p.H;
-    const int tid = threadIdx.x;
-    char *rec = state + L.off_rec + (int64_t)rid * L.rec_bytes;
-    int64_t *hdr = reinterpret_cast<int64_t *>(rec);
-    int32_t *cell = reinterpret_cast<int32_t *>(rec + L.o_cell);
-    float *sa = reinterpret_cast<float *>(rec + L.o_a);
-    float *skb = reinterpret_cast<float *>(rec + L.o_kbar);
-    T *sk = reinterpret_cast<T *>(rec + L.o_sk);
-    T *sv = reinterpret_cast<T *>(rec + L.o_sv);
-    T *rk = reinterpret_cast<T *>(rec + L.o_rk);
-    T *rv = reinterpret_cast<T *>(rec + L.o_rv);
-    typedef typename RotKey<T>::type RT;
-    RT *rkr = reinterpret_cast<RT *>(rec + L.o_rkr);
-    const int s = p.s, PW = L.PW, R = L.R;
-    const int lane = tid & 63, wave = tid >> 6;
-
-    const int64_t t = hdr[0];
-    const int64_t blk = hdr[1];
-    const int64_t b = t / p.B;
-    for (int i = tid; i < PW; i += kDecThreads) {
-        s_cell[i] = cell[i];
-        s_a[i] = sa[i];
-    }
-    if (tid < D) s_q[tid] = to_f32<T>(qn[(int64_t)rid * D + tid]);
-    __syncthreads();
-
-    // ---- 1. block boundary: new eligible cells, recent -> high-norm competition
+__device__ void decode_boundary(const KParams &p, int64_t blk, int64_t b, int PW, int R, int tid, int *s_cell,
+                                float *s_a, double *s_ss, float *s_newa, int *s_load_cell, int *s_load_slot,
+                                int *s_nload, const T *rk, const T *rv, T *sk, T *sv, float *skb, int32_t *cell,
+                                float *sa) {
+    const int s = p.s;
     const int64_t n_old = elig_nocap(p, blk), n_new = elig_nocap(p, b);
     if (b != blk && n_new > n_old) {
         const int nnew = (int)(n_new - n_old);  // <= B/s <= kDecMaxNew
@@ -322,10 +287,10 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
                 s_load_slot[nload] = sc;
                 ++nload;
             }
-            s_nload = nload;
+            *s_nload = nload;
         }
         __syncthreads();
-        const int nload = s_nload;
+        const int nload = *s_nload;
         for (int e = tid; e < nload * s * D; e += kDecThreads) {
             const int li = e / (s * D), rem = e % (s * D);
             const int64_t pos = (int64_t)s_load_cell[li] * s + rem / D;
@@ -346,6 +311,59 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
         }
         __syncthreads();
     }
+
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__restrict__ state, const T *__restrict__ qn,
+                                                                  const T *__restrict__ kn, const T *__restrict__ vn,
+                                                                  void *__restrict__ out, int32_t *__restrict__ sel_out,
+                                                                  KParams p, DecodeLayout L) {
+    __shared__ __attribute__((aligned(16))) float s_q[D];
+    __shared__ int s_cell[kDecMaxPool];
+    __shared__ float s_a[kDecMaxPool];
+    __shared__ double s_score[kDecMaxPool];
+    __shared__ int s_rank[kDecMaxPool];
+    __shared__ int s_sel[8];
+    __shared__ int s_selslot[8];
+    __shared__ float s_red[kDecThreads / 64];
+    __shared__ __attribute__((aligned(16))) float s_qr[D];  // R(t) q
+    __shared__ float s_wm[kDecWaves], s_wl[kDecWaves];     // per-wave softmax state
+    __shared__ float s_wo[kDecWaves][D];                    // per-wave partial outputs
+    __shared__ double s_ss[kDecMaxNew * 64];
+    __shared__ float s_newa[kDecMaxNew];
+    __shared__ int s_load_cell[kDecMaxNew], s_load_slot[kDecMaxNew], s_nload;
+
+    const int rid = blockIdx.x;  // seq * H + h
+    const int h = rid % p.H;
+    const int tid = threadIdx.x;
+    char *rec = state + L.off_rec + (int64_t)rid * L.rec_bytes;
+    int64_t *hdr = reinterpret_cast<int64_t *>(rec);
+    int32_t *cell = reinterpret_cast<int32_t *>(rec + L.o_cell);
+    float *sa = reinterpret_cast<float *>(rec + L.o_a);
+    float *skb = reinterpret_cast<float *>(rec + L.o_kbar);
+    T *sk = reinterpret_cast<T *>(rec + L.o_sk);
+    T *sv = reinterpret_cast<T *>(rec + L.o_sv);
+    T *rk = reinterpret_cast<T *>(rec + L.o_rk);
+    T *rv = reinterpret_cast<T *>(rec + L.o_rv);
+    typedef typename RotKey<T>::type RT;
+    RT *rkr = reinterpret_cast<RT *>(rec + L.o_rkr);
+    const int s = p.s, PW = L.PW, R = L.R;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    const int64_t t = hdr[0];
+    const int64_t blk = hdr[1];
+    const int64_t b = t / p.B;
+    for (int i = tid; i < PW; i += kDecThreads) {
+        s_cell[i] = cell[i];
+        s_a[i] = sa[i];
+    }
+    if (tid < D) s_q[tid] = to_f32<T>(qn[(int64_t)rid * D + tid]);
+    __syncthreads();
+
+    // ---- 1. block boundary: new eligible cells, recent -> high-norm competition
+    decode_boundary<T, D>(p, blk, b, PW, R, tid, s_cell, s_a, s_ss, s_newa, s_load_cell, s_load_slot, &s_nload, rk, rv,
+                          sk, sv, skb, cell, sa);
 
     // ---- 2. append the new token: raw k/v, and the key rotated at t
     const int64_t tslot = t % R;
@@ -580,6 +598,80 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     }
 }
 
+// Append len tokens of one sequence (all heads) to its records without queries: the
+// state then equals the one a prefill of the whole prefix would give, without the
+// prefix's O(N d) keys and values or a workspace (ai.info summary, "Why This
+// Matters" and future directions: bounded streaming state, fed in chunks). One
+// work-group per head. Block by block: the block boundary as in the decode step,
+// then the block's tokens go into the ring in parallel (raw k/v, and keys rotated at
+// their positions with fp64 angles). A launch covers sequences seq0 .. seq0 + n - 1
+// (one work-group per (sequence, head)), k/v [n][H][len][d].
+template <typename T, int D>
+__global__ __launch_bounds__(kDecThreads) void decode_append_kernel(char *__restrict__ state, int seq0,
+                                                                    const T *__restrict__ kc, const T *__restrict__ vc,
+                                                                    int64_t len, KParams p, DecodeLayout L) {
+    __shared__ int s_cell[kDecMaxPool];
+    __shared__ float s_a[kDecMaxPool];
+    __shared__ double s_ss[kDecMaxNew * 64];
+    __shared__ float s_newa[kDecMaxNew];
+    __shared__ int s_load_cell[kDecMaxNew], s_load_slot[kDecMaxNew], s_nload;
+    const int rl = blockIdx.x;  // (sequence - seq0) * H + head
+    const int tid = threadIdx.x;
+    char *rec = state + L.off_rec + ((int64_t)seq0 * p.H + rl) * L.rec_bytes;
+    int64_t *hdr = reinterpret_cast<int64_t *>(rec);
+    int32_t *cell = reinterpret_cast<int32_t *>(rec + L.o_cell);
+    float *sa = reinterpret_cast<float *>(rec + L.o_a);
+    float *skb = reinterpret_cast<float *>(rec + L.o_kbar);
+    T *sk = reinterpret_cast<T *>(rec + L.o_sk);
+    T *sv = reinterpret_cast<T *>(rec + L.o_sv);
+    T *rk = reinterpret_cast<T *>(rec + L.o_rk);
+    T *rv = reinterpret_cast<T *>(rec + L.o_rv);
+    typedef typename RotKey<T>::type RT;
+    RT *rkr = reinterpret_cast<RT *>(rec + L.o_rkr);
+    const int PW = L.PW, R = L.R;
+    const int64_t t0 = hdr[0];
+    int64_t blk = hdr[1];
+    for (int i = tid; i < PW; i += kDecThreads) {
+        s_cell[i] = cell[i];
+        s_a[i] = sa[i];
+    }
+    __syncthreads();
+    const T *kh = kc + (int64_t)rl * len * D;
+    const T *vh = vc + (int64_t)rl * len * D;
+    for (int64_t j = 0; j < len;) {
+        const int64_t b = (t0 + j) / p.B;
+        decode_boundary<T, D>(p, blk, b, PW, R, tid, s_cell, s_a, s_ss, s_newa, s_load_cell, s_load_slot, &s_nload, rk,
+                              rv, sk, sv, skb, cell, sa);
+        blk = b;
+        const int64_t jend = min(len, (b + 1) * p.B - t0);  // this block's tokens within the chunk
+        const int64_t n = jend - j;
+        for (int64_t e = tid; e < n * D; e += kDecThreads) {
+            const int64_t u = j + e / D;
+            const int x = (int)(e % D);
+            const int64_t slot = (t0 + u) % R;
+            rk[slot * D + x] = kh[u * D + x];
+            rv[slot * D + x] = vh[u * D + x];
+        }
+        for (int64_t e = tid; e < n * (D / 2); e += kDecThreads) {
+            const int64_t u = j + e / (D / 2);
+            const int m = (int)(e % (D / 2));
+            const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
+            const double ang = (double)(t0 + u) * theta;
+            const float c = (float)cos(ang), sn = (float)sin(ang);
+            const float a = to_f32<T>(kh[u * D + m]), bb = to_f32<T>(kh[u * D + m + D / 2]);
+            const int64_t slot = (t0 + u) % R;
+            rkr[slot * D + m] = rot_store<RT>(a * c - bb * sn);
+            rkr[slot * D + m + D / 2] = rot_store<RT>(bb * c + a * sn);
+        }
+        __syncthreads();  // the next boundary reads these ring rows
+        j = jend;
+    }
+    if (tid == 0) {
+        hdr[0] = t0 + len;
+        hdr[1] = blk;
+    }
+}
+
 hipError_t launch_decode_init(void *state, const KParams &p, const DecodeLayout &L, int n_seq, hipStream_t st) {
     hipLaunchKernelGGL(decode_init_kernel, dim3((unsigned)(n_seq * p.H)), dim3(256), 0, st, (char *)state, p, L, n_seq,
                        p.dtype);
@@ -618,6 +710,23 @@ hipError_t launch_decode_step(void *state, const void *q, const void *k, const v
                          : step_t<uint16_t, 128>(state, q, k, v, out, sel_out, n_seq, p, L, st);
     return p.d == 64 ? step_t<float, 64>(state, q, k, v, out, sel_out, n_seq, p, L, st)
                      : step_t<float, 128>(state, q, k, v, out, sel_out, n_seq, p, L, st);
+}
+
+template <typename T, int D>
+static hipError_t append_t(void *state, int seq0, int n, const void *k, const void *v, int64_t len, const KParams &p,
+                           const DecodeLayout &L, hipStream_t st) {
+    hipLaunchKernelGGL((decode_append_kernel<T, D>), dim3((unsigned)(n * p.H)), dim3(kDecThreads), 0, st,
+                       (char *)state, seq0, (const T *)k, (const T *)v, len, p, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_append(void *state, int seq0, int n, const void *k, const void *v, int64_t len,
+                                const KParams &p, const DecodeLayout &L, hipStream_t st) {
+    if (p.dtype == FSL_BF16)
+        return p.d == 64 ? append_t<uint16_t, 64>(state, seq0, n, k, v, len, p, L, st)
+                         : append_t<uint16_t, 128>(state, seq0, n, k, v, len, p, L, st);
+    return p.d == 64 ? append_t<float, 64>(state, seq0, n, k, v, len, p, L, st)
+                     : append_t<float, 128>(state, seq0, n, k, v, len, p, L, st);
 }
 
 }  // namespace fsl

@@ -352,6 +352,8 @@ hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const
 hipError_t launch_decode_init(void *state, const KParams &p, const DecodeLayout &L, int n_seq, hipStream_t st);
 hipError_t launch_decode_prefill(void *state, int seq, const void *kp, const void *vp, int64_t Lp, const Work &w,
                                  const KParams &p, const DecodeLayout &L, hipStream_t st);
+hipError_t launch_decode_append(void *state, int seq0, int n, const void *k, const void *v, int64_t len,
+                                const KParams &p, const DecodeLayout &L, hipStream_t st);
 hipError_t launch_decode_step(void *state, const void *q, const void *k, const void *v, void *out, int32_t *sel_out,
                               int n_seq, const KParams &p, const DecodeLayout &L, hipStream_t st);
 

@@ -75,6 +75,8 @@ def lib():
         L.fsl_decode_prefill_workspace_bytes.argtypes = [pp, i64]
         L.fsl_decode_prefill.restype = i32
         L.fsl_decode_prefill.argtypes = [vp, sz, ctypes.c_int32, vp, vp, i64, pp, vp, sz, vp]
+        L.fsl_decode_append.restype = i32
+        L.fsl_decode_append.argtypes = [vp, sz, ctypes.c_int32, ctypes.c_int32, vp, vp, i64, pp, vp]
         L.fsl_decode_step.restype = i32
         L.fsl_decode_step.argtypes = [vp, sz, vp, vp, vp, vp, ctypes.c_int32, pp, vp, vp]
         L.fsl_decode_validate.restype = i32
@@ -245,6 +247,14 @@ class DecodeState:
                                         ctypes.byref(self.p), _ptr(ws), ws.numel(), _stream(stream)),
                "fsl_decode_prefill")
         return ws
+
+    def append(self, seq: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+        """Append tokens without queries (streamed prefill): k, v [H][len][d] for sequence seq, or
+        [n][H][len][d] for sequences seq .. seq + n - 1."""
+        n = 1 if k.dim() == 3 else int(k.shape[0])
+        L = int(k.shape[-2])
+        _check(lib().fsl_decode_append(_ptr(self.buf), self.nbytes, seq, n, _ptr(k), _ptr(v), L,
+                                       ctypes.byref(self.p), _stream(stream)), "fsl_decode_append")
 
     def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, stream=None):

@@ -28,8 +28,10 @@ def _case(name):
     print(f"\n[case] {name}", flush=True)
 
 
-def run_decode(sh, seqs, prefix, steps, sigma=None, check_every=1, save_at=None):
-    """Prefill each sequence, step through, return outputs/selections (host arrays)."""
+def run_decode(sh, seqs, prefix, steps, sigma=None, check_every=1, save_at=None, chunks=None, prefill_first=False):
+    """Prefill each sequence, step through, return outputs/selections (host arrays). With chunks (a
+    list of lengths summing to prefix) the prefix is streamed through fsl_decode_append instead,
+    after a one-shot prefill of the first chunk if prefill_first."""
     from long_context_sparse_cell_amd import fsl
     H, d = sh.H, sh.d
     sig, lam, gam = synth.head_scalars(H)
@@ -40,10 +42,29 @@ def run_decode(sh, seqs, prefix, steps, sigma=None, check_every=1, save_at=None)
     tdt = torch.bfloat16 if sh.dtype == synth.BF16 else torch.float32
     p = fsl.make_params(1, H, d, tdt, sig_t, lam_t, gam_t, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
     st = fsl.DecodeState(p, len(seqs))
-    if prefix > 0:
+    if prefix > 0 and chunks is None:
         for r, sq in enumerate(seqs):
             st.prefill(r, device_tensor(np.ascontiguousarray(sq.k_prefix), sh.dtype),
                        device_tensor(np.ascontiguousarray(sq.v_prefix), sh.dtype))
+    elif chunks is not None:
+        assert sum(chunks) == prefix
+        a = 0
+        for ci, n in enumerate(chunks):
+            if ci == 0 and prefill_first:
+                for r, sq in enumerate(seqs):
+                    st.prefill(r, device_tensor(np.ascontiguousarray(sq.k_prefix[:, a:a + n]), sh.dtype),
+                               device_tensor(np.ascontiguousarray(sq.v_prefix[:, a:a + n]), sh.dtype))
+            elif ci % 2 == 0:
+                # every sequence's chunk in one call ([n_seq][H][len][d])
+                st.append(0, device_tensor(np.ascontiguousarray(np.stack([sq.k_prefix[:, a:a + n] for sq in seqs])),
+                                           sh.dtype),
+                          device_tensor(np.ascontiguousarray(np.stack([sq.v_prefix[:, a:a + n] for sq in seqs])),
+                                        sh.dtype))
+            else:
+                for r, sq in enumerate(seqs):
+                    st.append(r, device_tensor(np.ascontiguousarray(sq.k_prefix[:, a:a + n]), sh.dtype),
+                              device_tensor(np.ascontiguousarray(sq.v_prefix[:, a:a + n]), sh.dtype))
+            a += n
     n = len(seqs)
     outs = np.zeros((steps, n, H, d), np.float32)
     sels = np.zeros((steps, n, H, sh.K), np.int32)
@@ -93,6 +114,42 @@ def test_decode_matches_oracle_every_step(oracle, name, over, prefix, steps, sig
             np.testing.assert_array_equal(res["sel"][:, r, h], ref["sel"], err_msg=f"seq {r} head {h}")
             mx, mean = check_out(res["out"][:, r, h], ref["out"], sh.dtype, f"decode seq {r} head {h}")
             print(f"  seq {r} head {h}: out max err {mx:.3e} mean {mean:.3e}", flush=True)
+
+
+APPEND_CASES = [
+    # name, shape overrides, prefix, steps, chunk lengths, prefill the first chunk
+    ("bf16_d64_three_uneven_chunks", dict(H=2, d=64, dtype=synth.BF16), 5000, 150, [1000, 1, 3999], False),
+    ("bf16_d64_prefill_then_appends", dict(H=2, d=64, dtype=synth.BF16), 5000, 150, [2048, 1536, 1416], True),
+    ("f32_d128_block_aligned_chunks", dict(H=1, d=128, dtype=synth.F32), 3072, 140, [1024, 1024, 1024], False),
+    ("bf16_d64_small_window_tiny_chunks", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=32, P=4, W=2, K=3), 700,
+     120, [1, 31, 32, 33, 300, 303], False),
+]
+
+
+@pytest.mark.parametrize("name,over,prefix,steps,chunks,first", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_streamed_prefill_equals_one_shot_prefill(name, over, prefix, steps, chunks, first):
+    """A prefix streamed through fsl_decode_append in chunks (crossing query-block boundaries inside
+    chunks, single-token chunks, after a one-shot prefill or from an empty state) leaves the state a
+    one-shot prefill of the whole prefix leaves: every later decode step is bit-identical."""
+    _case(f"append {name}")
+    sh = synth.Shape(name, N=prefix + steps, seed=31, **over)
+    seqs = [synth.decode_sequence(sh, r, prefix=prefix, steps=steps) for r in range(2)]
+    ref = run_decode(sh, seqs, prefix, steps)
+    got = run_decode(sh, seqs, prefix, steps, chunks=chunks, prefill_first=first)
+    np.testing.assert_array_equal(got["sel"], ref["sel"])
+    np.testing.assert_array_equal(got["out"], ref["out"])
+
+
+def test_streamed_prefill_matches_oracle(oracle):
+    _case("append vs oracle")
+    sh = synth.Shape("append_oracle", N=2600 + 180, H=2, d=64, dtype=synth.BF16, seed=32)
+    seqs = [synth.decode_sequence(sh, r, prefix=2600, steps=180) for r in range(2)]
+    res = run_decode(sh, seqs, 2600, 180, chunks=[700, 1300, 600])
+    for r, sq in enumerate(seqs):
+        for h in range(sh.H):
+            ref = oracle_decode_rows(oracle, sh, sq, 2600, 180, res["sigma"], res["lam"], res["gamma"], h)
+            np.testing.assert_array_equal(res["sel"][:, r, h], ref["sel"], err_msg=f"seq {r} head {h}")
+            check_out(res["out"][:, r, h], ref["out"], sh.dtype, f"append seq {r} head {h}")
 
 
 def test_decode_equals_forward_rows():

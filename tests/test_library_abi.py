@@ -192,3 +192,12 @@ def test_decode_entry_points_reject_bad_arguments(fsl):
     assert L.fsl_decode_prefill(a, n, 0, a, a, 100, ctypes.byref(p), a, 16, None) == -3      # workspace too small
     pw = params(fsl, w=70000)
     assert int(L.fsl_decode_state_bytes(ctypes.byref(pw), 1)) == 0
+    # streamed prefill: pointers, length and sequence checked before any launch
+    assert L.fsl_decode_append(a, n, 0, 1, None, a, 10, ctypes.byref(p), None) == -1
+    assert L.fsl_decode_append(a, n, 0, 1, a, ctypes.c_void_p(0x100008), 10, ctypes.byref(p), None) == -1
+    assert L.fsl_decode_append(a, n, 0, 1, a, a, 0, ctypes.byref(p), None) == -1
+    assert L.fsl_decode_append(a, n, 2, 1, a, a, 10, ctypes.byref(p), None) == -1   # state holds sequences 0, 1
+    assert L.fsl_decode_append(a, n, 1, 2, a, a, 10, ctypes.byref(p), None) == -1   # 1 .. 2 is past the end
+    assert L.fsl_decode_append(a, n, 0, 0, a, a, 10, ctypes.byref(p), None) == -1
+    assert L.fsl_decode_append(a, n, -1, 1, a, a, 10, ctypes.byref(p), None) == -1
+    assert L.fsl_decode_append(a, n, 0, 1, a, a, 10, ctypes.byref(params(fsl, P=-1)), None) == -2
