@@ -2,8 +2,11 @@
 // (FreeSolo digest, core method and step 2; prerequisites: RoPE rotates q_i
 // and k_j so that their product depends only on the offset j - i).
 //
-// Tiling and operands as in the generic window kernel (window.hip): 128
-// queries per workgroup, 4 waves x 32 queries, keys in tiles of 64,
+// Tiling and operands as in the generic window kernel (window.hip), but 128
+// queries per workgroup as 8 waves x 16 queries (one MFMA query tile per wave:
+// 123 VGPRs, so two work-groups fill a CU with 16 waves to hide the tile
+// copies; two query tiles per wave needed 202 VGPRs and ran 10% slower), keys
+// in tiles of 64,
 // S^T = K Q^T so that P^T feeds O^T = V^T P^T from the accumulator registers,
 // fp16 operands with fp32 accumulation. The keys arrive rotated and the values
 // transposed, both in fp16 (kv_prep.hip), so each tile is copied from global
@@ -44,7 +47,7 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ kt,
                                                              const uint16_t *__restrict__ vt,
                                                              const float2 *__restrict__ rope,
@@ -54,7 +57,9 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
     constexpr int CPR = D / 8;                  // 16-byte chunks per key row
     constexpr int TILE = kKTile * D;            // fp16 elements of a key tile (and of a value tile)
     constexpr int UNITS = TILE * 2 / 1024;      // 1 KB copy units per tile
-    constexpr int UPW = UNITS / 4;              // key (and value) units per wave
+    constexpr int NW = 8;                       // waves
+    constexpr int QT = 1;                       // 16-query MFMA tiles per wave
+    constexpr int UPW = UNITS / NW;             // key (and value) units per wave
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
-    const int64_t qw = q0 + 32 * wave;
+    const int64_t qw = q0 + 16 * QT * wave;
     const float sl2 = p.scale * 1.4426950408889634f;
 
     // key tiles that intersect [max(0, q0-w+1), min(N, q0+128) - 1]
@@ -76,11 +81,11 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
     const int t_first = (int)(kmin / kKTile);
     const int t_last = (int)(kmax / kKTile);
 
-    // ---- this lane's copy offsets (elements within a tile), for units wave + 4 i
+    // ---- this lane's copy offsets (elements within a tile), for units wave + 8 i
     int koff[UPW], voff[UPW];
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
-        const int s = 64 * (wave + 4 * i) + lane;  // 16-byte slot within the tile
+        const int s = 64 * (wave + NW * i) + lane;  // 16-byte slot within the tile
         const int row = s / CPR, pc = s % CPR;
         koff[i] = row * D + 8 * (pc ^ swz_key(row, D));
         const int r = s >> 2, pg = s & 3;       // r = group * D + dim
@@ -92,17 +97,17 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
         const uint16_t *kb = kth + (int64_t)t * TILE;  // tiles are contiguous in both arrays
         const uint16_t *vb = vth + (int64_t)t * TILE;
 #pragma unroll
-        for (int i = 0; i < UPW; ++i) lds_dma16(kb + koff[i], kbuf + 512 * (wave + 4 * i));
+        for (int i = 0; i < UPW; ++i) lds_dma16(kb + koff[i], kbuf + 512 * (wave + NW * i));
 #pragma unroll
-        for (int i = 0; i < UPW; ++i) lds_dma16(vb + voff[i], vbuf + 512 * (wave + 4 * i));
+        for (int i = 0; i < UPW; ++i) lds_dma16(vb + voff[i], vbuf + 512 * (wave + NW * i));
     };
 
     // ---- rotated queries as fp16 MFMA B operands (column = query, k-slots = dims 32ks + 8g + r)
-    halfx8 qreg[2][QS];
+    halfx8 qreg[QT][QS];
     {
         const int nhi = rope_abs_rows_hi(p);
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QT; ++qg) {
             const int64_t i = qw + 16 * qg + col;
             const bool ok = i < p.N;
             const int64_t ic = ok ? i : p.N - 1;
@@ -142,38 +147,42 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
         }
     }
 
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_part[2] = {0.0f, 0.0f};
-    floatx4 oacc[2][D / 16];
+    float m_run[QT];
+    float l_part[QT];
+    floatx4 oacc[QT][D / 16];
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg)
+    for (int qg = 0; qg < QT; ++qg) {
+        m_run[qg] = -INFINITY;
+        l_part[qg] = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) oacc[qg][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 
     auto compute = [&](int t, const uint16_t *kbuf, const uint16_t *vbuf) __attribute__((always_inline)) {
         const int64_t ks0 = (int64_t)t * kKTile;
-        const bool active = qw < p.N && ks0 <= qw + 31 && ks0 + kKTile - 1 >= qw - p.w + 1;
+        const bool active = qw < p.N && ks0 <= qw + 16 * QT - 1 && ks0 + kKTile - 1 >= qw - p.w + 1;
         if (!active) return;
-        floatx4 sacc[4][2];
+        floatx4 sacc[4][QT];
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
-            sacc[kg][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-            sacc[kg][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qg = 0; qg < QT; ++qg) sacc[kg][qg] = floatx4{0.f, 0.f, 0.f, 0.f};
             const int row = 16 * kg + col;
 #pragma unroll
             for (int ks = 0; ks < QS; ++ks) {
                 P8 ka;
                 ka.u = *reinterpret_cast<const uint4 *>(&kbuf[row * D + 8 * ((4 * ks + g) ^ swz_key(row, D))]);
-                sacc[kg][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[0][ks], sacc[kg][0], 0, 0, 0);
-                sacc[kg][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[1][ks], sacc[kg][1], 0, 0, 0);
+#pragma unroll
+                for (int qg = 0; qg < QT; ++qg)
+                    sacc[kg][qg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[qg][ks], sacc[kg][qg], 0, 0, 0);
             }
         }
         // positions fit in int32 (N < 2^31)
         const int j0 = (int)ks0 + 4 * g;
-        const bool edge = !(ks0 + kKTile - 1 <= qw && ks0 > qw + 31 - p.w);
-        P8 pb[2][2];
+        const bool edge = !(ks0 + kKTile - 1 <= qw && ks0 > qw + 16 * QT - 1 - p.w);
+        P8 pb[2][QT];
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QT; ++qg) {
             const int i = (int)qw + 16 * qg + col;
             float mx = -INFINITY;
 #pragma unroll
@@ -222,8 +231,9 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
                 const int dim = 16 * dt + col;
                 P8 va;
                 va.u = *reinterpret_cast<const uint4 *>(&vbuf[((kk * D + dim) * 4 + (g ^ swz_val(dim))) * 8]);
-                oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][0].v, oacc[0][dt], 0, 0, 0);
-                oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][1].v, oacc[1][dt], 0, 0, 0);
+#pragma unroll
+                for (int qg = 0; qg < QT; ++qg)
+                    oacc[qg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][qg].v, oacc[qg][dt], 0, 0, 0);
             }
         }
     };
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void window_bf16_kernel(const uint16_t *__r
     }
 
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
+    for (int qg = 0; qg < QT; ++qg) {
         const float l = colsum4(l_part[qg]);
         const int64_t i = qw + 16 * qg + col;
         if (i >= p.N) continue;
@@ -262,10 +272,10 @@ hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t 
                               float *o_win, const KParams &p, hipStream_t st) {
     dim3 grid((unsigned)(((p.N + kQTile - 1) / kQTile) * p.H));
     if (p.d == 64)
-        hipLaunchKernelGGL((window_bf16_kernel<64>), grid, dim3(256), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
+        hipLaunchKernelGGL((window_bf16_kernel<64>), grid, dim3(512), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
                            o_win, p);
     else
-        hipLaunchKernelGGL((window_bf16_kernel<128>), grid, dim3(256), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
+        hipLaunchKernelGGL((window_bf16_kernel<128>), grid, dim3(512), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
                            o_win, p);
     return hipGetLastError();
 }
