@@ -108,7 +108,7 @@ def _sample_rows(sh, n_random=96, seed=0):
     return rows
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c4"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4"])
 def test_fs_workload_parity_and_needles(oracle, cfg):
     """The workload shapes with pruning off: every cell is a candidate; sampled rows
     (random rows, block edges, needle probes) against the oracle, and every needle in
@@ -121,7 +121,7 @@ def test_fs_workload_parity_and_needles(oracle, cfg):
     rows = _sample_rows(sh)
     for pr in inp.probes:
         rows.update(pr[:8])
-    rows = np.array(sorted(rows), dtype=np.int64)
+    rows = None if cfg == "c1" else np.array(sorted(rows), dtype=np.int64)
     sel = compare_fs(oracle, inp, run, rows=rows)
     for h in range(sh.H):
         for m, pos in enumerate(inp.needles[h]):
