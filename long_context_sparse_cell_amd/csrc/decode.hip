@@ -323,7 +323,6 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     __shared__ int s_cell[kDecMaxPool];
     __shared__ float s_a[kDecMaxPool];
     __shared__ double s_score[kDecMaxPool];
-    __shared__ int s_rank[kDecMaxPool];
     __shared__ int s_sel[8];
     __shared__ int s_selslot[8];
     __shared__ float s_red[kDecThreads / 64];
@@ -549,27 +548,55 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     }
     if (tid < 8) { s_sel[tid] = INT_MAX; s_selslot[tid] = -1; }
     __syncthreads();
-    for (int i = tid; i < PW; i += kDecThreads) {
-        const int c = s_cell[i];
-        int rank = INT_MAX;
-        if (c >= 0) {
-            rank = 0;
-            for (int o2 = 0; o2 < PW; ++o2) {
-                const int c2 = s_cell[o2];
-                if (c2 >= 0 && o2 != i && better_d(s_score[o2], c2, s_score[i], c)) ++rank;
+    // top K under (score desc, cell asc) on wave 0: each lane holds slots lane and 64 + lane;
+    // K rounds of a wave-wide maximum, the winner's lane drops it; then the K winners are
+    // put in ascending cell order. Comparisons are written as selects.
+    static_assert(kDecMaxPool <= 128, "two slots per lane of one wave");
+    if (wave == 0) {
+        double v0 = -INFINITY, v1 = -INFINITY;
+        int c0 = INT_MAX, c1 = INT_MAX;
+        if (lane < PW && s_cell[lane] >= 0) { v0 = s_score[lane]; c0 = s_cell[lane]; }
+        if (lane + 64 < PW && s_cell[lane + 64] >= 0) { v1 = s_score[lane + 64]; c1 = s_cell[lane + 64]; }
+        int wc[8], ws[8];
+        for (int r = 0; r < p.K; ++r) {
+            const bool first = better_d(v0, c0, v1, c1) || c1 == INT_MAX;
+            double vb = first ? v0 : v1;
+            int cb = first ? c0 : c1;
+            int sb = first ? lane : lane + 64;
+#pragma unroll
+            for (int m = 32; m > 0; m >>= 1) {
+                const double ov = __hiloint2double(__shfl_xor(__double2hiint(vb), m), __shfl_xor(__double2loint(vb), m));
+                const int oc = __shfl_xor(cb, m), os = __shfl_xor(sb, m);
+                const bool bt = better_d(ov, oc, vb, cb);
+                vb = bt ? ov : vb;
+                cb = bt ? oc : cb;
+                sb = bt ? os : sb;
+            }
+            wc[r] = cb;
+            ws[r] = cb == INT_MAX ? -1 : sb;
+            // the lane that held the winner drops it (cells are distinct)
+            const bool d0 = cb != INT_MAX && c0 == cb, d1 = cb != INT_MAX && c1 == cb;
+            v0 = d0 ? -INFINITY : v0;
+            c0 = d0 ? INT_MAX : c0;
+            v1 = d1 ? -INFINITY : v1;
+            c1 = d1 ? INT_MAX : c1;
+        }
+        if (lane == 0) {
+            // ascending cell order (K <= 8), empty picks (INT_MAX) last
+            for (int x = 0; x < p.K; ++x)
+                for (int y = 0; y + 1 < p.K - x; ++y) {
+                    const bool sw = wc[y] > wc[y + 1];
+                    const int a = wc[y], bb = wc[y + 1], sa2 = ws[y], sb2 = ws[y + 1];
+                    wc[y] = sw ? bb : a;
+                    wc[y + 1] = sw ? a : bb;
+                    ws[y] = sw ? sb2 : sa2;
+                    ws[y + 1] = sw ? sa2 : sb2;
+                }
+            for (int r = 0; r < p.K; ++r) {
+                s_sel[r] = wc[r];
+                s_selslot[r] = ws[r];
             }
         }
-        s_rank[i] = rank;
-    }
-    __syncthreads();
-    for (int i = tid; i < PW; i += kDecThreads) {
-        const int c = s_cell[i];
-        if (c < 0 || s_rank[i] >= p.K) continue;
-        int below = 0;  // position among the selected cells in ascending index order
-        for (int o2 = 0; o2 < PW; ++o2)
-            if (s_cell[o2] >= 0 && s_rank[o2] < p.K && s_cell[o2] < c) ++below;
-        s_sel[below] = c;
-        s_selslot[below] = i;
     }
     __syncthreads();
     int nsel = 0;
