@@ -332,6 +332,9 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     __shared__ double s_ss[kDecMaxNew * 64];
     __shared__ float s_newa[kDecMaxNew];
     __shared__ int s_load_cell[kDecMaxNew], s_load_slot[kDecMaxNew], s_nload;
+    // d = 64: the slot means, copied in before the window so that scoring reads LDS
+    extern __shared__ __attribute__((aligned(16))) float s_kbl[];
+    constexpr bool KB_LDS = D == 64;
 
     const int rid = blockIdx.x;  // seq * H + h
     const int h = rid % p.H;
@@ -363,6 +366,17 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     // ---- 1. block boundary: new eligible cells, recent -> high-norm competition
     decode_boundary<T, D>(p, blk, b, PW, R, tid, s_cell, s_a, s_ss, s_newa, s_load_cell, s_load_slot, &s_nload, rk, rv,
                           sk, sv, skb, cell, sa);
+
+    // the slot means are final now: start their copy into LDS (1 KB per wave instruction, the
+    // source clamped to the array), so that it is queued ahead of the window's loads
+    if constexpr (KB_LDS) {
+        const int nbytes = PW * D * 4, npiece = (nbytes + 1023) >> 10;
+        const char *src = reinterpret_cast<const char *>(skb);
+        for (int k = wave; k < npiece; k += kDecWaves) {
+            const int off = min(k * 1024 + 16 * lane, nbytes - 16);
+            lds_dma16(src + off, reinterpret_cast<char *>(s_kbl) + k * 1024);
+        }
+    }
 
     // ---- 2. append the new token: raw k/v, and the key rotated at t
     const int64_t tslot = t % R;
@@ -525,11 +539,15 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
 
     // ---- 4. exact fp64 cell scores and top-K over the occupied slots
     const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+    if constexpr (KB_LDS) {
+        wait_vmem();
+        __syncthreads();
+    }
     for (int i = tid; i < PW; i += kDecThreads) {
         double scv = -INFINITY;
         const int c = s_cell[i];
         if (c >= 0) {
-            const float *kr = skb + (int64_t)i * D;
+            const float *kr = (KB_LDS ? s_kbl : skb) + (int64_t)i * D;
             double content = 0.0;
 #pragma unroll 4
             for (int x0 = 0; x0 < D; x0 += 4) {
@@ -549,8 +567,9 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     if (tid < 8) { s_sel[tid] = INT_MAX; s_selslot[tid] = -1; }
     __syncthreads();
     // top K under (score desc, cell asc) on wave 0: each lane holds slots lane and 64 + lane;
-    // K rounds of a wave-wide maximum, the winner's lane drops it; then the K winners are
-    // put in ascending cell order. Comparisons are written as selects.
+    // K rounds of a wave-wide maximum, the lane that held the winner drops it (cells are
+    // distinct); lanes r < K then put winner r at the count of smaller cells (empty picks,
+    // INT_MAX with slot -1, after the others). Comparisons are written as selects.
     static_assert(kDecMaxPool <= 128, "two slots per lane of one wave");
     if (wave == 0) {
         double v0 = -INFINITY, v1 = -INFINITY;
@@ -558,44 +577,36 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
         if (lane < PW && s_cell[lane] >= 0) { v0 = s_score[lane]; c0 = s_cell[lane]; }
         if (lane + 64 < PW && s_cell[lane + 64] >= 0) { v1 = s_score[lane + 64]; c1 = s_cell[lane + 64]; }
         int wc[8], ws[8];
-        for (int r = 0; r < p.K; ++r) {
-            const bool first = better_d(v0, c0, v1, c1) || c1 == INT_MAX;
-            double vb = first ? v0 : v1;
-            int cb = first ? c0 : c1;
-            int sb = first ? lane : lane + 64;
 #pragma unroll
-            for (int m = 32; m > 0; m >>= 1) {
-                const double ov = __hiloint2double(__shfl_xor(__double2hiint(vb), m), __shfl_xor(__double2loint(vb), m));
-                const int oc = __shfl_xor(cb, m), os = __shfl_xor(sb, m);
-                const bool bt = better_d(ov, oc, vb, cb);
-                vb = bt ? ov : vb;
-                cb = bt ? oc : cb;
-                sb = bt ? os : sb;
+        for (int r = 0; r < 8; ++r) {
+            wc[r] = INT_MAX;
+            ws[r] = -1;
+            if (r < p.K) {
+                const bool first = better_d(v0, c0, v1, c1) || c1 == INT_MAX;
+                double vb = first ? v0 : v1;
+                int cb = first ? c0 : c1;
+                int sb = first ? lane : lane + 64;
+                wave_best_d(vb, cb, sb);
+                wc[r] = cb;
+                ws[r] = cb == INT_MAX ? -1 : sb;
+                const bool d0 = cb != INT_MAX && c0 == cb, d1 = cb != INT_MAX && c1 == cb;
+                v0 = d0 ? -INFINITY : v0;
+                c0 = d0 ? INT_MAX : c0;
+                v1 = d1 ? -INFINITY : v1;
+                c1 = d1 ? INT_MAX : c1;
             }
-            wc[r] = cb;
-            ws[r] = cb == INT_MAX ? -1 : sb;
-            // the lane that held the winner drops it (cells are distinct)
-            const bool d0 = cb != INT_MAX && c0 == cb, d1 = cb != INT_MAX && c1 == cb;
-            v0 = d0 ? -INFINITY : v0;
-            c0 = d0 ? INT_MAX : c0;
-            v1 = d1 ? -INFINITY : v1;
-            c1 = d1 ? INT_MAX : c1;
         }
-        if (lane == 0) {
-            // ascending cell order (K <= 8), empty picks (INT_MAX) last
-            for (int x = 0; x < p.K; ++x)
-                for (int y = 0; y + 1 < p.K - x; ++y) {
-                    const bool sw = wc[y] > wc[y + 1];
-                    const int a = wc[y], bb = wc[y + 1], sa2 = ws[y], sb2 = ws[y + 1];
-                    wc[y] = sw ? bb : a;
-                    wc[y + 1] = sw ? a : bb;
-                    ws[y] = sw ? sb2 : sa2;
-                    ws[y + 1] = sw ? sa2 : sb2;
-                }
-            for (int r = 0; r < p.K; ++r) {
-                s_sel[r] = wc[r];
-                s_selslot[r] = ws[r];
-            }
+        int mc = wc[0], msl = ws[0], below = 0;
+#pragma unroll
+        for (int r = 1; r < 8; ++r) {
+            mc = lane == r ? wc[r] : mc;
+            msl = lane == r ? ws[r] : msl;
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) below += wc[r] < mc ? 1 : 0;
+        if (lane < p.K) {
+            s_sel[below] = mc;
+            s_selslot[below] = msl;
         }
     }
     __syncthreads();
@@ -725,7 +736,8 @@ hipError_t launch_decode_prefill(void *state, int seq, const void *kp, const voi
 template <typename T, int D>
 static hipError_t step_t(void *state, const void *q, const void *k, const void *v, void *out, int32_t *sel_out,
                          int n_seq, const KParams &p, const DecodeLayout &L, hipStream_t st) {
-    hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3((unsigned)(n_seq * p.H)), dim3(kDecThreads), 0, st,
+    const size_t kb_lds = D == 64 ? ((size_t)L.PW * D * 4 + 1023) / 1024 * 1024 : 0;
+    hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3((unsigned)(n_seq * p.H)), dim3(kDecThreads), kb_lds, st,
                        (char *)state, (const T *)q, (const T *)k, (const T *)v, out, sel_out, p, L);
     return hipGetLastError();
 }

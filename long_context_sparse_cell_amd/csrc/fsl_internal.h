@@ -263,6 +263,50 @@ __device__ __forceinline__ bool better_d(double a1, int i1, double a2, int i2) {
     return a1 > a2 || (a1 == a2 && i1 < i2);
 }
 
+// Wave-wide best (better_d order) of one (key, index, tag) entry per lane, left in every lane.
+// Lanes pair up as i ^ 1, i ^ 2 (quad permutes), mirrored half rows and rows, then i ^ 16 and
+// i ^ 32 (lane swaps); each step keeps the better of a lane's entry and its partner's, so both
+// lanes of a pair agree. The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ void best_step_dpp(double &v, int &c, int &tag) {
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int oc = __builtin_amdgcn_mov_dpp(c, CTRL, 0xF, 0xF, false);
+    const int ot = __builtin_amdgcn_mov_dpp(tag, CTRL, 0xF, 0xF, false);
+    const double ov = __hiloint2double(hi, lo);
+    const bool bt = better_d(ov, oc, v, c);
+    v = bt ? ov : v;
+    c = bt ? oc : c;
+    tag = bt ? ot : tag;
+}
+// the pair (a[0], a[1]) of a lane swap holds the lane's own value and its partner's
+template <bool S32>
+__device__ __forceinline__ void best_step_swap(double &v, int &c, int &tag) {
+    const uint32_t hi = (uint32_t)__double2hiint(v), lo = (uint32_t)__double2loint(v);
+    const uint32_t uc = (uint32_t)c, ut = (uint32_t)tag;
+    const auto h = S32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                       : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto l = S32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                       : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto cc = S32 ? __builtin_amdgcn_permlane32_swap(uc, uc, false, false)
+                        : __builtin_amdgcn_permlane16_swap(uc, uc, false, false);
+    const auto tt = S32 ? __builtin_amdgcn_permlane32_swap(ut, ut, false, false)
+                        : __builtin_amdgcn_permlane16_swap(ut, ut, false, false);
+    const double x = __hiloint2double((int)h[0], (int)l[0]), y = __hiloint2double((int)h[1], (int)l[1]);
+    const bool by = better_d(y, (int)cc[1], x, (int)cc[0]);
+    v = by ? y : x;
+    c = by ? (int)cc[1] : (int)cc[0];
+    tag = by ? (int)tt[1] : (int)tt[0];
+}
+__device__ __forceinline__ void wave_best_d(double &v, int &c, int &tag) {
+    best_step_dpp<0xB1>(v, c, tag);   // quad_perm [1, 0, 3, 2]
+    best_step_dpp<0x4E>(v, c, tag);   // quad_perm [2, 3, 0, 1]
+    best_step_dpp<0x141>(v, c, tag);  // row_half_mirror
+    best_step_dpp<0x140>(v, c, tag);  // row_mirror
+    best_step_swap<false>(v, c, tag);
+    best_step_swap<true>(v, c, tag);
+}
+
 // Sort the 64 entries of a wave best-first (lane 0 best). Bitonic network.
 __device__ __forceinline__ void wave_sort_best_first(float &a, int &idx) {
     const int lane = threadIdx.x & 63;
