@@ -314,6 +314,31 @@ __device__ void decode_boundary(const KParams &p, int64_t blk, int64_t b, int PW
 
 }
 
+// Keys of 16-bit types are read coalesced: a 64-key chunk of rows (PPR 16-byte pieces each)
+// is loaded RPI = 64 / PPR rows per wave instruction, lane l holding piece l % PPR of row
+// l / PPR, so instruction i gives the lane a partial dot of key i * RPI + l / PPR. Summing the
+// PPR pieces of a row is a reduce-scatter over the PPR lanes of a row group (recursive halving,
+// highest index bit first): after it, part[0] of the lane with piece pc is the dot of its
+// group's key with instruction index pc. Partners: the mirrored row or half row for the first
+// halving (either flips the bit being split), then i ^ 2 and i ^ 1 (quad permutes); each later
+// partner agrees on the bits already split. The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int H, int PPR>
+__device__ __forceinline__ void halve_pieces(float (&a)[PPR], int pc) {
+    constexpr int CTRL = H == PPR / 2 ? (PPR == 16 ? 0x140 : 0x141) : H == 4 ? 0x141 : H == 2 ? 0x4E : 0xB1;
+    const bool hi = (pc & H) != 0;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+        const float send = hi ? a[j] : a[j + H];
+        const float keep = hi ? a[j + H] : a[j];
+        a[j] = keep + dpp_f<CTRL>(send);
+    }
+    if constexpr (H > 1) halve_pieces<H / 2, PPR>(a, pc);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__restrict__ state, const T *__restrict__ qn,
                                                                   const T *__restrict__ kn, const T *__restrict__ vn,
@@ -419,8 +444,20 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
         constexpr bool HALF_PV = sizeof(T) == 2 && D == 64;
         float o2[2] = {0.0f, 0.0f};
         const int hf = lane >> 5, dp = 2 * (lane & 31);
+        // 16-bit keys: coalesced rows and a reduce-scatter of the pieces (see halve_pieces);
+        // lane l then scores key kl of the chunk, and key j's weight sits in lane key_lane(j)
+        constexpr bool CO = sizeof(KE) == 2;
+        constexpr int PPR = CO ? D / 8 : 1, RPI = 64 / PPR;
+        const int pc = lane % PPR, ri = lane / PPR;
+        const int kl = CO ? pc * RPI + ri : lane;
+        auto key_lane = [](int j) { return CO ? (j % RPI) * PPR + j / RPI : j; };
+        float qv[8];
+        if constexpr (CO) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = qs[pc * 8 + e];
+        }
         for (int c0 = 64 * wave; c0 < nkeys; c0 += 64 * kDecWaves) {
-            const int u = c0 + lane;
+            const int u = c0 + kl;
             const int nkc = min(64, nkeys - c0);
             uint32_t vpair[HALF_PV ? 32 : 1];
             if constexpr (HALF_PV) {
@@ -429,7 +466,18 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
                     vpair[j] = *reinterpret_cast<const uint32_t *>(vrow(c0 + min(32 * hf + j, nkc - 1)) + dp);
             }
             float sc = -INFINITY;
-            if (u < nkeys) {
+            if constexpr (CO) {
+                float part[PPR];
+#pragma unroll
+                for (int i = 0; i < PPR; ++i) {
+                    float kf[8];
+                    load8f<KE, KF16>(krow(c0 + min(i * RPI + ri, nkc - 1)) + pc * 8, kf);
+                    part[i] = qv[0] * kf[0] + qv[1] * kf[1] + qv[2] * kf[2] + qv[3] * kf[3] + qv[4] * kf[4] +
+                              qv[5] * kf[5] + qv[6] * kf[6] + qv[7] * kf[7];
+                }
+                halve_pieces<PPR / 2, PPR>(part, pc);
+                sc = u < nkeys ? part[0] * sl2 : -INFINITY;
+            } else if (u < nkeys) {
                 const KE *kr = krow(u);
                 float dot = 0.0f;
 #pragma unroll 2
@@ -462,8 +510,9 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
 #pragma unroll
                 for (int j = 0; j < 32; ++j) {
                     // weight of key 32 hf + j, from its lane (zero past the chunk's end)
-                    const float p0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), j));
-                    const float p1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), 32 + j));
+                    const float p0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), key_lane(j)));
+                    const float p1 =
+                        __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), key_lane(32 + j)));
                     const float pk = 32 * hf + j < nkc ? (hf ? p1 : p0) : 0.0f;
                     o2[0] = fmaf(pk, __uint_as_float(vpair[j] << 16), o2[0]);
                     o2[1] = fmaf(pk, __uint_as_float(vpair[j] & 0xFFFF0000u), o2[1]);
@@ -486,7 +535,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
 #pragma unroll
                 for (int j2 = 0; j2 < KB; ++j2) {
                     // weight of key k0 + j2, broadcast from its lane (zero past the chunk's end)
-                    const float pk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), k0 + j2));
+                    const float pk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pj), key_lane(k0 + j2)));
 #pragma unroll
                     for (int d2 = 0; d2 < DPL; ++d2) o[d2] += (k0 + j2 < nk ? pk : 0.0f) * vv[j2][d2];
                 }
