@@ -18,10 +18,14 @@
 //  4. scores every occupied slot in fp64 exactly as the forward does, keeps
 //     the top K under (score desc, index asc);
 //  5. NoPE readout over the chosen cells' tokens, RMSNorm, mix, write.
-// Both attention steps spread the keys over the lanes of 4 waves, 64 keys per
-// chunk (16-byte row loads), then turn the lanes to dimensions for the P.V sum
-// (each key's weight broadcast from its lane, value rows read coalesced); the
-// four waves' partial softmax states are merged at the end.
+// Both attention steps give each of the 4 waves chunks of 64 keys. 16-bit key
+// rows are read coalesced (a wave instruction covers 1 KB of consecutive rows)
+// and each row's pieces are summed across its lanes; fp32 rows are read one per
+// lane. The lanes then turn to dimensions for the P.V sum (each key's weight
+// broadcast from its lane, value rows read coalesced); the four waves' partial
+// softmax states are merged at the end. The slot means are copied into LDS
+// before the window so that step 4 reads no global memory, and the top K is K
+// rounds of a wave-wide maximum.
 #include <climits>
 #include <type_traits>
 
