@@ -18,10 +18,10 @@
 //  4. scores every occupied slot in fp64 exactly as the forward does, keeps
 //     the top K under (score desc, index asc);
 //  5. NoPE readout over the chosen cells' tokens, RMSNorm, mix, write.
-// Both attention steps give each of the 4 waves chunks of 64 keys. 16-bit key
-// rows are read coalesced (a wave instruction covers 1 KB of consecutive rows)
-// and each row's pieces are summed across its lanes; fp32 rows are read one per
-// lane. The lanes then turn to dimensions for the P.V sum (each key's weight
+// Both attention steps give each of the 4 waves chunks of 64 keys. The window's
+// fp16 key rows are read coalesced (a wave instruction covers 1 KB of
+// consecutive rows) and each row's pieces are summed across its lanes; other
+// key rows are read one per lane. The lanes then turn to dimensions for the P.V sum (each key's weight
 // broadcast from its lane, value rows read coalesced); the four waves' partial
 // softmax states are merged at the end. The slot means are copied into LDS
 // before the window so that step 4 reads no global memory, and the top K is K
@@ -448,9 +448,11 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
         constexpr bool HALF_PV = sizeof(T) == 2 && D == 64;
         float o2[2] = {0.0f, 0.0f};
         const int hf = lane >> 5, dp = 2 * (lane & 31);
-        // 16-bit keys: coalesced rows and a reduce-scatter of the pieces (see halve_pieces);
-        // lane l then scores key kl of the chunk, and key j's weight sits in lane key_lane(j)
-        constexpr bool CO = sizeof(KE) == 2;
+        // the window's fp16 keys: coalesced rows and a reduce-scatter of the pieces (see
+        // halve_pieces); lane l then scores key kl of the chunk, and key j's weight sits in lane
+        // key_lane(j). The readout keeps one row per lane: its rows are found through the slot
+        // table, one lookup per lane instead of one per row and instruction (measured faster).
+        constexpr bool CO = sizeof(KE) == 2 && KF16;
         constexpr int PPR = CO ? D / 8 : 1, RPI = 64 / PPR;
         const int pc = lane % PPR, ri = lane / PPR;
         const int kl = CO ? pc * RPI + ri : lane;
