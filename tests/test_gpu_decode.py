@@ -99,6 +99,9 @@ DECODE_CASES = [
     ("bf16_d64_small_window_from_scratch", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=32, P=4, W=2, K=3), 0, 700,
      None),
     ("bf16_d64_w0_k8", dict(H=1, d=64, dtype=synth.BF16, w=100, s=32, B=64, P=16, W=0, K=8), 2500, 200, None),
+    # the largest slot table (P + W = 128: two slots per lane in the top K) with K = 8
+    ("bf16_d64_pool128_k8", dict(H=1, d=64, dtype=synth.BF16, w=256, s=16, B=64, P=64, W=64, K=8), 3000, 200, None),
+    ("f32_d128_pool128_k5", dict(H=1, d=128, dtype=synth.F32, w=200, s=16, B=32, P=64, W=64, K=5), 2600, 120, None),
 ]
 
 
