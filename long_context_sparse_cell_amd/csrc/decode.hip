@@ -14,18 +14,20 @@
 //     best under (a desc, index asc); a loser's slot is freed), and every
 //     newly kept cell is copied once from the ring into a free slot;
 //  2. appends the new k/v to the ring and its key rotated at t (angles in fp64);
-//  3. window attention over the ring: R(t)q against the rotated keys;
-//  4. scores every occupied slot in fp64 exactly as the forward does, keeps
-//     the top K under (score desc, index asc);
-//  5. NoPE readout over the chosen cells' tokens, RMSNorm, mix, write.
-// Both attention steps give each of the 4 waves chunks of 64 keys. The window's
-// fp16 key rows are read coalesced (a wave instruction covers 1 KB of
-// consecutive rows) and each row's pieces are summed across its lanes; other
-// key rows are read one per lane. The lanes then turn to dimensions for the P.V sum (each key's weight
-// broadcast from its lane, value rows read coalesced); the four waves' partial
-// softmax states are merged at the end. The slot means are copied into LDS
-// before the window so that step 4 reads no global memory, and the top K is K
-// rounds of a wave-wide maximum.
+//  3. wave 0 scores every occupied slot in fp64 exactly as the forward does,
+//     keeps the top K under (score desc, index asc) and reads the chosen
+//     cells' tokens out (NoPE), while
+//  4. waves 1-3 attend over the window in the ring: R(t)q against the rotated
+//     keys, whose loads keep HBM busy during wave 0's latency-bound chain;
+//  5. merges the partial softmax states, RMSNorm, mix, write.
+// Each attention gives its waves chunks of 64 keys. The window's fp16 key rows
+// are read coalesced (a wave instruction covers 1 KB of consecutive rows) and
+// each row's pieces are summed across its lanes; other key rows are read one
+// per lane. The lanes then turn to dimensions for the P.V sum (each key's
+// weight broadcast from its lane, value rows read coalesced). The slot means
+// are copied into LDS (d = 64) while the new token is appended, so that
+// scoring reads no global memory, and the top K is K rounds of a wave-wide
+// maximum.
 #include <climits>
 #include <type_traits>
 
@@ -351,7 +353,6 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     __shared__ __attribute__((aligned(16))) float s_q[D];
     __shared__ int s_cell[kDecMaxPool];
     __shared__ float s_a[kDecMaxPool];
-    __shared__ double s_score[kDecMaxPool];
     __shared__ int s_sel[8];
     __shared__ int s_selslot[8];
     __shared__ float s_red[kDecThreads / 64];
@@ -431,10 +432,10 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
     constexpr int DPL = D / 64;  // dimensions per lane in the P.V sums
 
     // Softmax attention of one query (qs in LDS) over nkeys keys: key u's row at krow(u)
-    // (fp16 bits if kf16, else the input type), its value row at vrow(u). Keys go to lanes in
-    // chunks of 64 (chunk c to wave c mod 4); each wave keeps its own (max, sum, o),
-    // merged over the waves into res[x] for x < D by threads tid < D.
-    auto attend = [&](int nkeys, const float *qs, auto krow, auto vrow, auto kf16, float &res)
+    // (fp16 bits if kf16, else the input type), its value row at vrow(u), run by the waves
+    // w0 .. w0 + nw - 1. Keys go to lanes in chunks of 64 (chunk c to wave w0 + c mod nw); each
+    // wave leaves its own (max, sum, o) in s_wm / s_wl / s_wo, combined by merge() below.
+    auto attend = [&](int nkeys, const float *qs, auto krow, auto vrow, auto kf16, int w0, int nw)
         __attribute__((always_inline)) {
         typedef typename std::remove_cv<typename std::remove_pointer<decltype(krow(0))>::type>::type KE;
         constexpr bool KF16 = decltype(kf16)::value;  // 16-bit keys: fp16 (rotated ring) or bf16 (raw)
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
 #pragma unroll
             for (int e = 0; e < 8; ++e) qv[e] = qs[pc * 8 + e];
         }
-        for (int c0 = 64 * wave; c0 < nkeys; c0 += 64 * kDecWaves) {
+        for (int c0 = 64 * (wave - w0); c0 < nkeys; c0 += 64 * nw) {
             const int u = c0 + kl;
             const int nkc = min(64, nkeys - c0);
             uint32_t vpair[HALF_PV ? 32 : 1];
@@ -562,75 +563,68 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
 #pragma unroll
             for (int d2 = 0; d2 < DPL; ++d2) s_wo[wave][lane * DPL + d2] = o[d2];
         }
-        __syncthreads();
-        if (tid < D) {
-            float mm = -INFINITY;
-#pragma unroll
-            for (int w2 = 0; w2 < kDecWaves; ++w2) mm = fmaxf(mm, s_wm[w2]);
-            float num = 0.0f, den = 0.0f;
-#pragma unroll
-            for (int w2 = 0; w2 < kDecWaves; ++w2) {
-                const float f = s_wm[w2] == -INFINITY ? 0.0f : exp2f(s_wm[w2] - mm);
-                num += f * s_wo[w2][tid];
-                den += f * s_wl[w2];
-            }
-            res = den > 0.0f ? num / den : 0.0f;
+    };
+    // softmax merge of the partials of waves w0 .. w0 + nw - 1, for dimension x = tid < D
+    auto merge = [&](int w0, int nw) __attribute__((always_inline)) {
+        float mm = -INFINITY;
+        for (int w2 = w0; w2 < w0 + nw; ++w2) mm = fmaxf(mm, s_wm[w2]);
+        float num = 0.0f, den = 0.0f;
+        for (int w2 = w0; w2 < w0 + nw; ++w2) {
+            const float f = s_wm[w2] == -INFINITY ? 0.0f : exp2f(s_wm[w2] - mm);
+            num += f * s_wo[w2][tid];
+            den += f * s_wl[w2];
         }
-        __syncthreads();
+        return den > 0.0f ? num / den : 0.0f;
     };
 
-    // ---- 3. window over keys [max(0, t-w+1), t]: R(t)q against the rotated keys
-    float o_win = 0.0f;
-    {
-        const int64_t j_lo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
-        const int nwin = (int)(t - j_lo + 1);
-        const int r0 = (int)(j_lo % R);  // ring row of key j_lo; keys j_lo + u stay below j_lo + R
-        auto ring = [=](int u) { const int r = r0 + u; return (r >= R ? r - R : r) * D; };
-        attend(
-            nwin, s_qr, [&](int u) { return (const RT *)(rkr + ring(u)); },
-            [&](int u) { return (const T *)(rv + ring(u)); },
-            std::integral_constant<bool, sizeof(RT) == 2>{}, o_win);
-    }
-
-    // ---- 4. exact fp64 cell scores and top-K over the occupied slots
-    const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+    // ---- 3. the long-range branch on wave 0: exact fp64 cell scores, top K, readout.
+    // ---- 4. at the same time, waves 1 .. 3: the window over keys [max(0, t-w+1), t], R(t)q
+    //         against the rotated keys. The window's loads keep HBM busy while wave 0 works
+    //         through its latency-bound chain.
     if constexpr (KB_LDS) {
-        wait_vmem();
+        wait_vmem();  // this wave's slot-mean copies have landed; the barrier publishes them
         __syncthreads();
     }
-    for (int i = tid; i < PW; i += kDecThreads) {
-        double scv = -INFINITY;
-        const int c = s_cell[i];
-        if (c >= 0) {
-            const float *kr = (KB_LDS ? s_kbl : skb) + (int64_t)i * D;
-            double content = 0.0;
+    if (wave == 0) {
+        const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+        // lane takes slots lane and lane + 64: two independent fma chains over the dimensions,
+        // each in ascending order
+        const int i0 = lane, i1 = lane + 64;
+        const bool ok0 = i0 < PW && s_cell[i0] >= 0, ok1 = i1 < PW && s_cell[i1] >= 0;
+        const float *kbase = KB_LDS ? s_kbl : skb;
+        const float *kr0 = kbase + (int64_t)(i0 < PW ? i0 : 0) * D;
+        const float *kr1 = kbase + (int64_t)(i1 < PW ? i1 : 0) * D;
+        double ct0 = 0.0, ct1 = 0.0;
+        const bool two = PW > 64;
 #pragma unroll 4
-            for (int x0 = 0; x0 < D; x0 += 4) {
-                const float4 k4 = *reinterpret_cast<const float4 *>(kr + x0);
-                content = __fma_rn((double)s_q[x0], (double)k4.x, content);
-                content = __fma_rn((double)s_q[x0 + 1], (double)k4.y, content);
-                content = __fma_rn((double)s_q[x0 + 2], (double)k4.z, content);
-                content = __fma_rn((double)s_q[x0 + 3], (double)k4.w, content);
-            }
+        for (int x0 = 0; x0 < D; x0 += 4) {
+            const float4 ka = *reinterpret_cast<const float4 *>(kr0 + x0);
+            const float4 kb4 = two ? *reinterpret_cast<const float4 *>(kr1 + x0) : ka;
+            const double q0 = s_q[x0], q1 = s_q[x0 + 1], q2 = s_q[x0 + 2], q3 = s_q[x0 + 3];
+            ct0 = __fma_rn(q0, (double)ka.x, ct0);
+            ct1 = __fma_rn(q0, (double)kb4.x, ct1);
+            ct0 = __fma_rn(q1, (double)ka.y, ct0);
+            ct1 = __fma_rn(q1, (double)kb4.y, ct1);
+            ct0 = __fma_rn(q2, (double)ka.z, ct0);
+            ct1 = __fma_rn(q2, (double)kb4.z, ct1);
+            ct0 = __fma_rn(q3, (double)ka.w, ct0);
+            ct1 = __fma_rn(q3, (double)kb4.w, ct1);
+        }
+        auto finish = [&](int i, double content) __attribute__((always_inline)) {
+            const int c = s_cell[i];
             const double arg = __ddiv_rn(__dmul_rn(sig, (double)(t - (int64_t)c * s)), 2.0 * (double)s);
             const double gg = arg >= 6.0 ? 1.0 : erf(arg);
             const double bias = __dmul_rn(__dmul_rn(lam, (double)s_a[i]), gg);
-            scv = __fma_rn(rho, content, bias);
-        }
-        s_score[i] = scv;
-    }
-    if (tid < 8) { s_sel[tid] = INT_MAX; s_selslot[tid] = -1; }
-    __syncthreads();
-    // top K under (score desc, cell asc) on wave 0: each lane holds slots lane and 64 + lane;
-    // K rounds of a wave-wide maximum, the lane that held the winner drops it (cells are
-    // distinct); lanes r < K then put winner r at the count of smaller cells (empty picks,
-    // INT_MAX with slot -1, after the others). Comparisons are written as selects.
-    static_assert(kDecMaxPool <= 128, "two slots per lane of one wave");
-    if (wave == 0) {
+            return __fma_rn(rho, content, bias);
+        };
         double v0 = -INFINITY, v1 = -INFINITY;
         int c0 = INT_MAX, c1 = INT_MAX;
-        if (lane < PW && s_cell[lane] >= 0) { v0 = s_score[lane]; c0 = s_cell[lane]; }
-        if (lane + 64 < PW && s_cell[lane + 64] >= 0) { v1 = s_score[lane + 64]; c1 = s_cell[lane + 64]; }
+        if (ok0) { v0 = finish(i0, ct0); c0 = s_cell[i0]; }
+        if (ok1) { v1 = finish(i1, ct1); c1 = s_cell[i1]; }
+
+        // top K under (score desc, cell asc): K rounds of a wave-wide maximum, the lane that held
+        // the winner drops it (cells are distinct); comparisons are written as selects
+        static_assert(kDecMaxPool <= 128, "two slots per lane of one wave");
         int wc[8], ws[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -640,7 +634,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
                 const bool first = better_d(v0, c0, v1, c1) || c1 == INT_MAX;
                 double vb = first ? v0 : v1;
                 int cb = first ? c0 : c1;
-                int sb = first ? lane : lane + 64;
+                int sb = first ? i0 : i1;
                 wave_best_d(vb, cb, sb);
                 wc[r] = cb;
                 ws[r] = cb == INT_MAX ? -1 : sb;
@@ -651,33 +645,54 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_step_kernel(char *__res
                 c1 = d1 ? INT_MAX : c1;
             }
         }
-        int mc = wc[0], msl = ws[0], below = 0;
+        // the winners in ascending cell order: lane r < K puts winner r at the count of smaller
+        // cells (empty picks, INT_MAX with slot -1, land after the others)
+        if (lane < 8) {
+            s_sel[lane] = INT_MAX;
+            s_selslot[lane] = -1;
+        }
+        int mc = wc[0], msl = ws[0], nsel = 0, below = 0;
 #pragma unroll
         for (int r = 1; r < 8; ++r) {
             mc = lane == r ? wc[r] : mc;
             msl = lane == r ? ws[r] : msl;
         }
 #pragma unroll
-        for (int r = 0; r < 8; ++r) below += wc[r] < mc ? 1 : 0;
+        for (int r = 0; r < 8; ++r) {
+            below += wc[r] < mc ? 1 : 0;
+            nsel += ws[r] >= 0 ? 1 : 0;
+        }
         if (lane < p.K) {
             s_sel[below] = mc;
             s_selslot[below] = msl;
         }
-    }
-    __syncthreads();
-    int nsel = 0;
-    for (int r = 0; r < p.K; ++r) nsel += s_selslot[r] >= 0 ? 1 : 0;
-    if (sel_out && tid < p.K) sel_out[(int64_t)rid * p.K + tid] = s_selslot[tid] >= 0 ? s_sel[tid] : -1;
+        // a wave's LDS operations complete in issue order: the reads below see these writes
+        if (sel_out && lane < p.K) sel_out[(int64_t)rid * p.K + lane] = s_selslot[lane] >= 0 ? s_sel[lane] : -1;
 
-    // ---- 5. NoPE readout over the chosen cells' tokens, RMSNorm, mix
-    float o_long = 0.0f;
-    const int ntok = nsel * s;
-    if (ntok > 0) {
+        // NoPE readout over the chosen cells' tokens, in ascending cell order
+        const int ntok = nsel * s;
         const int ls = __builtin_ctz((unsigned)s);  // s is a power of two
         auto slot_row = [=](int u) { return ((s_selslot[u >> ls] << ls) + (u & (s - 1))) * D; };
         attend(
             ntok, s_q, [&](int u) { return (const T *)(sk + slot_row(u)); },
-            [&](int u) { return (const T *)(sv + slot_row(u)); }, std::false_type{}, o_long);
+            [&](int u) { return (const T *)(sv + slot_row(u)); }, std::false_type{}, 0, 1);
+    } else {
+        const int64_t j_lo = t - p.w + 1 > 0 ? t - p.w + 1 : 0;
+        const int nwin = (int)(t - j_lo + 1);
+        const int r0 = (int)(j_lo % R);  // ring row of key j_lo; keys j_lo + u stay below j_lo + R
+        auto ring = [=](int u) { const int r = r0 + u; return (r >= R ? r - R : r) * D; };
+        attend(
+            nwin, s_qr, [&](int u) { return (const RT *)(rkr + ring(u)); },
+            [&](int u) { return (const T *)(rv + ring(u)); },
+            std::integral_constant<bool, sizeof(RT) == 2>{}, 1, kDecWaves - 1);
+    }
+    __syncthreads();
+
+    // ---- 5. RMSNorm of the long-range output, mix
+    float o_win = 0.0f, o_long = 0.0f;
+    if (tid < D) {
+        o_win = merge(1, kDecWaves - 1);
+        o_long = merge(0, 1);
     }
     const float ms = block_reduce(tid < D ? o_long * o_long : 0.0f, s_red, false) / (float)D;
     if (tid < D) {
