@@ -210,11 +210,17 @@ __device__ void decode_boundary(const KParams &p, int64_t blk, int64_t b, int PW
         for (int r = tid; r < nnew * s; r += kDecThreads) {
             const int cn = r / s, j = r % s;
             const int64_t pos = (n_old + cn) * s + j;
+            const T *row = rk + (pos % R) * D;
             double acc = 0.0;
-#pragma unroll 8
-            for (int x = 0; x < D; ++x) {
-                const double e = (double)to_f32<T>(rk[(pos % R) * D + x]);
-                acc = __fma_rn(e, e, acc);
+#pragma unroll 2
+            for (int x0 = 0; x0 < D; x0 += 16) {
+                float fa[8], fb[8];
+                load8f<T, false>(row + x0, fa);
+                load8f<T, false>(row + x0 + 8, fb);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc = __fma_rn((double)fa[u], (double)fa[u], acc);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc = __fma_rn((double)fb[u], (double)fb[u], acc);
             }
             s_ss[r] = acc;
         }
@@ -297,18 +303,45 @@ __device__ void decode_boundary(const KParams &p, int64_t blk, int64_t b, int PW
         }
         __syncthreads();
         const int nload = *s_nload;
-        for (int e = tid; e < nload * s * D; e += kDecThreads) {
-            const int li = e / (s * D), rem = e % (s * D);
-            const int64_t pos = (int64_t)s_load_cell[li] * s + rem / D;
-            const int64_t dst = ((int64_t)s_load_slot[li] * s) * D + rem;
-            sk[dst] = rk[(pos % R) * D + rem % D];
-            sv[dst] = rv[(pos % R) * D + rem % D];
+        // the kept cells' tokens, ring -> slot, in 16-byte pieces with a batch of loads per thread
+        // (addresses clamped, stores guarded)
+        constexpr int EPP = 16 / (int)sizeof(T), PPRW = D / EPP;
+        const int ls = __builtin_ctz((unsigned)s);  // s is a power of two
+        const int npc = nload * s * PPRW;
+        auto piece = [&](int e, int64_t &src, int64_t &dst) __attribute__((always_inline)) {
+            const int rr = e / PPRW, pc = e % PPRW, li = rr >> ls, tok = rr & (s - 1);
+            src = ((((int64_t)s_load_cell[li] << ls) + tok) % R) * D + pc * EPP;
+            dst = (((int64_t)s_load_slot[li] << ls) + tok) * D + pc * EPP;
+        };
+        for (int e0 = 0; e0 < npc; e0 += 2 * kDecThreads) {
+            const int ea = e0 + tid, eb = e0 + kDecThreads + tid;
+            int64_t sa0, da0, sb0, db0;
+            piece(min(ea, npc - 1), sa0, da0);
+            piece(min(eb, npc - 1), sb0, db0);
+            const uint4 ka = *reinterpret_cast<const uint4 *>(rk + sa0), va = *reinterpret_cast<const uint4 *>(rv + sa0);
+            const uint4 kb = *reinterpret_cast<const uint4 *>(rk + sb0), vb = *reinterpret_cast<const uint4 *>(rv + sb0);
+            if (ea < npc) {
+                *reinterpret_cast<uint4 *>(sk + da0) = ka;
+                *reinterpret_cast<uint4 *>(sv + da0) = va;
+            }
+            if (eb < npc) {
+                *reinterpret_cast<uint4 *>(sk + db0) = kb;
+                *reinterpret_cast<uint4 *>(sv + db0) = vb;
+            }
         }
+        // their mean keys: fp64 sums in token order, each batch of 16 tokens' loads issued together
         for (int e = tid; e < nload * D; e += kDecThreads) {
             const int li = e / D, x = e % D;
             const int64_t c = s_load_cell[li];
             double acc = 0.0;
-            for (int j = 0; j < s; ++j) acc += (double)to_f32<T>(rk[((c * s + j) % R) * D + x]);
+            constexpr int TB = sizeof(T) == 2 ? 16 : 8;  // tokens per batch
+            for (int j0 = 0; j0 < s; j0 += TB) {
+                float f[TB];
+#pragma unroll
+                for (int u = 0; u < TB; ++u) f[u] = to_f32<T>(rk[((c * s + min(j0 + u, s - 1)) % R) * D + x]);
+#pragma unroll
+                for (int u = 0; u < TB; ++u) acc += j0 + u < s ? (double)f[u] : 0.0;
+            }
             skb[(int64_t)s_load_slot[li] * D + x] = (float)(acc / (double)s);
         }
         for (int i = tid; i < PW; i += kDecThreads) {
@@ -753,23 +786,57 @@ __global__ __launch_bounds__(kDecThreads) void decode_append_kernel(char *__rest
         blk = b;
         const int64_t jend = min(len, (b + 1) * p.B - t0);  // this block's tokens within the chunk
         const int64_t n = jend - j;
-        for (int64_t e = tid; e < n * D; e += kDecThreads) {
-            const int64_t u = j + e / D;
-            const int x = (int)(e % D);
-            const int64_t slot = (t0 + u) % R;
-            rk[slot * D + x] = kh[u * D + x];
-            rv[slot * D + x] = vh[u * D + x];
+        // raw rows into the ring in 16-byte pieces, a batch of pieces per thread with its loads
+        // issued together (addresses clamped to the block, stores guarded)
+        constexpr int EPP = 16 / (int)sizeof(T), PPRW = D / EPP, BAT = 4;
+        const int64_t npc = n * PPRW;
+        for (int64_t e0 = 0; e0 < npc; e0 += (int64_t)kDecThreads * BAT) {
+            uint4 kk[BAT], vv[BAT];
+#pragma unroll
+            for (int q = 0; q < BAT; ++q) {
+                const int64_t e = min(e0 + tid + (int64_t)kDecThreads * q, npc - 1);
+                const int64_t off = (j + e / PPRW) * D + (e % PPRW) * EPP;
+                kk[q] = *reinterpret_cast<const uint4 *>(kh + off);
+                vv[q] = *reinterpret_cast<const uint4 *>(vh + off);
+            }
+#pragma unroll
+            for (int q = 0; q < BAT; ++q) {
+                const int64_t e = e0 + tid + (int64_t)kDecThreads * q;
+                if (e < npc) {
+                    const int64_t u = j + e / PPRW;
+                    const int64_t dst = ((t0 + u) % R) * D + (e % PPRW) * EPP;
+                    *reinterpret_cast<uint4 *>(rk + dst) = kk[q];
+                    *reinterpret_cast<uint4 *>(rv + dst) = vv[q];
+                }
+            }
         }
-        for (int64_t e = tid; e < n * (D / 2); e += kDecThreads) {
-            const int64_t u = j + e / (D / 2);
-            const int m = (int)(e % (D / 2));
-            const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
-            const double ang = (double)(t0 + u) * theta;
-            const float c = (float)cos(ang), sn = (float)sin(ang);
-            const float a = to_f32<T>(kh[u * D + m]), bb = to_f32<T>(kh[u * D + m + D / 2]);
-            const int64_t slot = (t0 + u) % R;
-            rkr[slot * D + m] = rot_store<RT>(a * c - bb * sn);
-            rkr[slot * D + m + D / 2] = rot_store<RT>(bb * c + a * sn);
+        // keys rotated at their positions (angles in fp64), a batch of pairs per thread
+        constexpr int RB = 8;
+        const int64_t npr = n * (D / 2);
+        for (int64_t e0 = 0; e0 < npr; e0 += (int64_t)kDecThreads * RB) {
+            float ka[RB], kb[RB];
+#pragma unroll
+            for (int q = 0; q < RB; ++q) {
+                const int64_t e = min(e0 + tid + (int64_t)kDecThreads * q, npr - 1);
+                const int64_t u = j + e / (D / 2);
+                const int m = (int)(e % (D / 2));
+                ka[q] = to_f32<T>(kh[u * D + m]);
+                kb[q] = to_f32<T>(kh[u * D + m + D / 2]);
+            }
+#pragma unroll
+            for (int q = 0; q < RB; ++q) {
+                const int64_t e = e0 + tid + (int64_t)kDecThreads * q;
+                if (e < npr) {
+                    const int64_t u = j + e / (D / 2);
+                    const int m = (int)(e % (D / 2));
+                    const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
+                    const double ang = (double)(t0 + u) * theta;
+                    const float c = (float)cos(ang), sn = (float)sin(ang);
+                    const int64_t slot = (t0 + u) % R;
+                    rkr[slot * D + m] = rot_store<RT>(ka[q] * c - kb[q] * sn);
+                    rkr[slot * D + m + D / 2] = rot_store<RT>(kb[q] * c + ka[q] * sn);
+                }
+            }
         }
         __syncthreads();  // the next boundary reads these ring rows
         j = jend;
