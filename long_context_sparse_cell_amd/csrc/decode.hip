@@ -129,11 +129,15 @@ __global__ void decode_init_kernel(char *__restrict__ state, KParams p, DecodeLa
 }
 
 template <typename T, int D>
-__global__ void decode_prefill_kernel(char *__restrict__ state, int seq, const T *__restrict__ kp,
-                                      const T *__restrict__ vp, int64_t Lp, const float *__restrict__ kbar,
-                                      const float *__restrict__ amax, const int32_t *__restrict__ pool, KParams p,
-                                      DecodeLayout L) {
-    const int h = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_prefill_kernel(char *__restrict__ state, int seq,
+                                                             const T *__restrict__ kp, const T *__restrict__ vp,
+                                                             int64_t Lp, const float *__restrict__ kbar,
+                                                             const float *__restrict__ amax,
+                                                             const int32_t *__restrict__ pool, KParams p,
+                                                             DecodeLayout L) {
+    // grid (parts, heads): every loop strides over the threads of all parts of its head
+    const int h = blockIdx.y;
+    const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, gn = (int64_t)gridDim.x * blockDim.x;
     char *rec = state + L.off_rec + ((int64_t)seq * p.H + h) * L.rec_bytes;
     const int64_t b = Lp / p.B;
     const int64_t nb = elig_nocap(p, b);
@@ -148,32 +152,62 @@ __global__ void decode_prefill_kernel(char *__restrict__ state, int seq, const T
     const int32_t *bp = pool + ((int64_t)h * p.nblk + b) * p.PW;
     const T *kh = kp + (int64_t)h * Lp * D;
     const T *vh = vp + (int64_t)h * Lp * D;
-    for (int i = threadIdx.x; i < L.PW; i += blockDim.x) {
+    for (int64_t i = gt; i < L.PW; i += gn) {
         const int c = i < npool ? bp[i] : -1;
         cell[i] = c;
         if (c >= 0) sa[i] = amax[(int64_t)h * p.C + c];
     }
-    for (int64_t e = threadIdx.x; e < (int64_t)npool * D; e += blockDim.x) {
-        const int i = (int)(e / D), x = (int)(e % D);
-        skb[e] = kbar[((int64_t)h * p.C + bp[i]) * D + x];
+    // the pool cells' mean keys, 16-byte pieces
+    for (int64_t e = gt; e < (int64_t)npool * (D / 4); e += gn) {
+        const int i = (int)(e / (D / 4)), x4 = (int)(e % (D / 4)) * 4;
+        *reinterpret_cast<float4 *>(skb + (int64_t)i * D + x4) =
+            *reinterpret_cast<const float4 *>(kbar + ((int64_t)h * p.C + bp[i]) * D + x4);
     }
-    for (int64_t e = threadIdx.x; e < (int64_t)npool * p.s * D; e += blockDim.x) {
-        const int64_t i = e / ((int64_t)p.s * D), rem = e % ((int64_t)p.s * D);
-        const int64_t src = (int64_t)bp[i] * p.s * D + rem;
-        sk[e] = kh[src];
-        sv[e] = vh[src];
+    // the pool cells' raw tokens, then the ring's rows: 16-byte pieces, two per thread and
+    // round with the loads issued first (addresses clamped, stores guarded)
+    constexpr int EPP = 16 / (int)sizeof(T), PPRW = D / EPP;
+    const int64_t spc = (int64_t)p.s * PPRW;  // pieces per cell
+    const int64_t ncp = npool * spc;
+    for (int64_t e0 = 0; e0 < ncp; e0 += 2 * gn) {
+        const int64_t ea = e0 + gt, eb = e0 + gn + gt;
+        const int64_t ca = min(ea, ncp - 1), cb = min(eb, ncp - 1);
+        const int64_t sa0 = (int64_t)bp[ca / spc] * p.s * D + (ca % spc) * EPP;
+        const int64_t sb0 = (int64_t)bp[cb / spc] * p.s * D + (cb % spc) * EPP;
+        const uint4 ka = *reinterpret_cast<const uint4 *>(kh + sa0), va = *reinterpret_cast<const uint4 *>(vh + sa0);
+        const uint4 kb = *reinterpret_cast<const uint4 *>(kh + sb0), vb = *reinterpret_cast<const uint4 *>(vh + sb0);
+        if (ea < ncp) {
+            *reinterpret_cast<uint4 *>(sk + ea * EPP) = ka;
+            *reinterpret_cast<uint4 *>(sv + ea * EPP) = va;
+        }
+        if (eb < ncp) {
+            *reinterpret_cast<uint4 *>(sk + eb * EPP) = kb;
+            *reinterpret_cast<uint4 *>(sv + eb * EPP) = vb;
+        }
     }
     const int64_t first = nb * p.s;
-    for (int64_t e = threadIdx.x; e < (Lp - first) * D; e += blockDim.x) {
-        const int64_t pos = first + e / D, x = e % D;
-        const int64_t slot = pos % L.R;
-        rk[slot * D + x] = kh[pos * D + x];
-        rv[slot * D + x] = vh[pos * D + x];
+    const int64_t nrp = (Lp - first) * PPRW;
+    for (int64_t e0 = 0; e0 < nrp; e0 += 2 * gn) {
+        const int64_t ea = e0 + gt, eb = e0 + gn + gt;
+        const int64_t ra = min(ea, nrp - 1), rb = min(eb, nrp - 1);
+        const int64_t sa0 = (first + ra / PPRW) * D + (ra % PPRW) * EPP;
+        const int64_t sb0 = (first + rb / PPRW) * D + (rb % PPRW) * EPP;
+        const uint4 ka = *reinterpret_cast<const uint4 *>(kh + sa0), va = *reinterpret_cast<const uint4 *>(vh + sa0);
+        const uint4 kb = *reinterpret_cast<const uint4 *>(kh + sb0), vb = *reinterpret_cast<const uint4 *>(vh + sb0);
+        if (ea < nrp) {
+            const int64_t d = ((first + ea / PPRW) % L.R) * D + (ea % PPRW) * EPP;
+            *reinterpret_cast<uint4 *>(rk + d) = ka;
+            *reinterpret_cast<uint4 *>(rv + d) = va;
+        }
+        if (eb < nrp) {
+            const int64_t d = ((first + eb / PPRW) % L.R) * D + (eb % PPRW) * EPP;
+            *reinterpret_cast<uint4 *>(rk + d) = kb;
+            *reinterpret_cast<uint4 *>(rv + d) = vb;
+        }
     }
     // the same tokens' keys rotated at their positions (angle pos * base^(-2m/d) in fp64)
     typedef typename RotKey<T>::type RT;
     RT *rkr = reinterpret_cast<RT *>(rec + L.o_rkr);
-    for (int64_t e = threadIdx.x; e < (Lp - first) * (D / 2); e += blockDim.x) {
+    for (int64_t e = gt; e < (Lp - first) * (D / 2); e += gn) {
         const int64_t pos = first + e / (D / 2);
         const int m = (int)(e % (D / 2));
         const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
@@ -184,7 +218,7 @@ __global__ void decode_prefill_kernel(char *__restrict__ state, int seq, const T
         rkr[slot * D + m] = rot_store<RT>(a * c - bb * sn);
         rkr[slot * D + m + D / 2] = rot_store<RT>(bb * c + a * sn);
     }
-    if (threadIdx.x == 0) {
+    if (gt == 0) {
         reinterpret_cast<int64_t *>(rec)[0] = Lp;
         reinterpret_cast<int64_t *>(rec)[1] = b;
     }
@@ -856,7 +890,8 @@ hipError_t launch_decode_init(void *state, const KParams &p, const DecodeLayout 
 template <typename T, int D>
 static hipError_t prefill_t(void *state, int seq, const void *kp, const void *vp, int64_t Lp, const Work &w,
                             const KParams &p, const DecodeLayout &L, hipStream_t st) {
-    hipLaunchKernelGGL((decode_prefill_kernel<T, D>), dim3((unsigned)p.H), dim3(256), 0, st, (char *)state, seq,
+    // 32 parts per head: the record's copies spread over 32 H work-groups
+    hipLaunchKernelGGL((decode_prefill_kernel<T, D>), dim3(32u, (unsigned)p.H), dim3(256), 0, st, (char *)state, seq,
                        (const T *)kp, (const T *)vp, Lp, w.kbar, w.amax, w.pool, p, L);
     return hipGetLastError();
 }
