@@ -844,36 +844,39 @@ __global__ __launch_bounds__(kDecThreads) void decode_append_kernel(char *__rest
                 }
             }
         }
-        // keys rotated at their positions (angles in fp64), a batch of pairs per thread
-        constexpr int RB = 8;
-        const int64_t npr = n * (D / 2);
-        for (int64_t e0 = 0; e0 < npr; e0 += (int64_t)kDecThreads * RB) {
-            float ka[RB], kb[RB];
-#pragma unroll
-            for (int q = 0; q < RB; ++q) {
-                const int64_t e = min(e0 + tid + (int64_t)kDecThreads * q, npr - 1);
-                const int64_t u = j + e / (D / 2);
-                const int m = (int)(e % (D / 2));
-                ka[q] = to_f32<T>(kh[u * D + m]);
-                kb[q] = to_f32<T>(kh[u * D + m + D / 2]);
-            }
-#pragma unroll
-            for (int q = 0; q < RB; ++q) {
-                const int64_t e = e0 + tid + (int64_t)kDecThreads * q;
-                if (e < npr) {
-                    const int64_t u = j + e / (D / 2);
-                    const int m = (int)(e % (D / 2));
-                    const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
-                    const double ang = (double)(t0 + u) * theta;
-                    const float c = (float)cos(ang), sn = (float)sin(ang);
-                    const int64_t slot = (t0 + u) % R;
-                    rkr[slot * D + m] = rot_store<RT>(ka[q] * c - kb[q] * sn);
-                    rkr[slot * D + m + D / 2] = rot_store<RT>(kb[q] * c + ka[q] * sn);
-                }
-            }
-        }
         __syncthreads();  // the next boundary reads these ring rows
         j = jend;
+    }
+    // keys rotated at their positions (angles in fp64), a batch of pairs per thread. Only the
+    // chunk's last R tokens stay in the ring, and the boundary updates read the raw rows only,
+    // so the rotation covers those tokens alone.
+    const int64_t u0 = len > R ? len - R : 0;
+    constexpr int RB = 8;
+    const int64_t npr = (len - u0) * (D / 2);
+    for (int64_t e0 = 0; e0 < npr; e0 += (int64_t)kDecThreads * RB) {
+        float ka[RB], kb[RB];
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+            const int64_t e = min(e0 + tid + (int64_t)kDecThreads * q, npr - 1);
+            const int64_t u = u0 + e / (D / 2);
+            const int m = (int)(e % (D / 2));
+            ka[q] = to_f32<T>(kh[u * D + m]);
+            kb[q] = to_f32<T>(kh[u * D + m + D / 2]);
+        }
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+            const int64_t e = e0 + tid + (int64_t)kDecThreads * q;
+            if (e < npr) {
+                const int64_t u = u0 + e / (D / 2);
+                const int m = (int)(e % (D / 2));
+                const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)D);
+                const double ang = (double)(t0 + u) * theta;
+                const float c = (float)cos(ang), sn = (float)sin(ang);
+                const int64_t slot = (t0 + u) % R;
+                rkr[slot * D + m] = rot_store<RT>(ka[q] * c - kb[q] * sn);
+                rkr[slot * D + m + D / 2] = rot_store<RT>(kb[q] * c + ka[q] * sn);
+            }
+        }
     }
     if (tid == 0) {
         hdr[0] = t0 + len;
