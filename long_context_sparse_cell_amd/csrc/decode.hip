@@ -268,25 +268,39 @@ __device__ void decode_boundary(const KParams &p, int64_t blk, int64_t b, int PW
             s_newa[tid] = (float)__dsqrt_rn(best);
         }
         __syncthreads();
-        if (tid == 0) {
+        if (tid < 64) {
+            // wave 0: lane l holds slots l and 64 + l (cell -2 marks a slot past PW). The cells
+            // leaving the recent set are taken in index order, as one thread would: each either
+            // keeps its slot (fewer than P high-norm cells, or it beats their worst member, which
+            // is freed), or is freed; then the new cells take the lowest free slots.
+            const int lane = tid;
+            const int i0 = lane, i1 = lane + 64;
+            int cl0 = i0 < PW ? s_cell[i0] : -2, cl1 = i1 < PW ? s_cell[i1] : -2;
+            float al0 = i0 < PW ? s_a[i0] : 0.0f, al1 = i1 < PW ? s_a[i1] : 0.0f;
             const int64_t m_old = n_old > p.W ? n_old - p.W : 0;
             const int64_t m_new = n_new > p.W ? n_new - p.W : 0;
-            int top = 0;
-            for (int i = 0; i < PW; ++i) top += (s_cell[i] >= 0 && s_cell[i] < m_old) ? 1 : 0;
-            int nload = 0;
-            auto free_slot = [&]() {
-                for (int i = 0; i < PW; ++i)
-                    if (s_cell[i] < 0) return i;
-                return -1;
+            auto count = [&](bool x0, bool x1) { return __popcll(__ballot(x0)) + __popcll(__ballot(x1)); };
+            auto first = [&](bool x0, bool x1) {  // lowest slot index with the property, or -1
+                const uint64_t b0 = __ballot(x0), b1 = __ballot(x1);
+                return b0 ? __ffsll((unsigned long long)b0) - 1 : b1 ? 64 + __ffsll((unsigned long long)b1) - 1 : -1;
             };
+            auto set_slot = [&](int sc, int c, float a) {
+                if (sc == i0) { cl0 = c; al0 = a; }
+                if (sc == i1) { cl1 = c; al1 = a; }
+            };
+            auto a_of = [&](int sc) {
+                return __uint_as_float(sc < 64 ? __builtin_amdgcn_readlane(__float_as_uint(al0), sc)
+                                               : __builtin_amdgcn_readlane(__float_as_uint(al1), sc - 64));
+            };
+            int top = count(cl0 >= 0 && cl0 < m_old, cl1 >= 0 && cl1 < m_old);
+            int nload = 0;
             for (int64_t c = m_old; c < m_new; ++c) {
                 int sc = -1;
                 float ac;
                 if (c < n_old) {
-                    for (int i = 0; i < PW; ++i)
-                        if (s_cell[i] == c) sc = i;
+                    sc = first(cl0 == c, cl1 == c);
                     if (sc < 0) continue;  // cannot happen: every recent cell holds a slot
-                    ac = s_a[sc];
+                    ac = a_of(sc);
                 } else {
                     ac = s_newa[c - n_old];
                 }
@@ -295,15 +309,17 @@ __device__ void decode_boundary(const KParams &p, int64_t blk, int64_t b, int PW
                     if (top < p.P) {
                         keep = true;
                     } else {
-                        // the high-norm set is every occupied cell below c (older ones kept earlier);
-                        // find its worst member: smallest a, then largest index
-                        int wsl = -1;
-                        for (int i = 0; i < PW; ++i) {
-                            if (s_cell[i] < 0 || s_cell[i] >= c) continue;
-                            if (wsl < 0 || better(s_a[wsl], s_cell[wsl], s_a[i], s_cell[i])) wsl = i;
-                        }
-                        if (wsl >= 0 && better(ac, (int)c, s_a[wsl], s_cell[wsl])) {
-                            s_cell[wsl] = -1;
+                        // the high-norm set is every occupied cell below c; its worst member
+                        // (smallest a, then largest index) is the best under (-a, -index)
+                        const bool m0 = cl0 >= 0 && cl0 < c, m1 = cl1 >= 0 && cl1 < c;
+                        const double k0 = m0 ? -(double)al0 : -INFINITY, k1 = m1 ? -(double)al1 : -INFINITY;
+                        const int x0 = m0 ? -cl0 : INT_MAX, x1 = m1 ? -cl1 : INT_MAX;
+                        const bool pick0 = better_d(k0, x0, k1, x1) || !m1;
+                        double wk = pick0 ? k0 : k1;
+                        int wx = pick0 ? x0 : x1, wsl = pick0 ? i0 : i1;
+                        wave_best_d(wk, wx, wsl);
+                        if (wk != -INFINITY && better(ac, (int)c, (float)(-wk), -wx)) {
+                            set_slot(wsl, -1, a_of(wsl));
                             --top;
                             keep = true;
                         }
@@ -311,29 +327,33 @@ __device__ void decode_boundary(const KParams &p, int64_t blk, int64_t b, int PW
                 }
                 if (keep) {
                     if (sc < 0) {
-                        sc = free_slot();
+                        sc = first(i0 < PW && cl0 < 0 && cl0 != -2, i1 < PW && cl1 < 0 && cl1 != -2);
                         if (sc < 0) continue;  // cannot happen: at most P + W cells are ever held
-                        s_cell[sc] = (int)c;
-                        s_a[sc] = ac;
-                        s_load_cell[nload] = (int)c;
-                        s_load_slot[nload] = sc;
+                        set_slot(sc, (int)c, ac);
+                        if (lane == 0) {
+                            s_load_cell[nload] = (int)c;
+                            s_load_slot[nload] = sc;
+                        }
                         ++nload;
                     }
                     ++top;
                 } else if (sc >= 0) {
-                    s_cell[sc] = -1;
+                    set_slot(sc, -1, a_of(sc));
                 }
             }
             for (int64_t c = (n_old > m_new ? n_old : m_new); c < n_new; ++c) {
-                const int sc = free_slot();
+                const int sc = first(i0 < PW && cl0 < 0 && cl0 != -2, i1 < PW && cl1 < 0 && cl1 != -2);
                 if (sc < 0) break;  // cannot happen: at most P + W cells are ever held
-                s_cell[sc] = (int)c;
-                s_a[sc] = s_newa[c - n_old];
-                s_load_cell[nload] = (int)c;
-                s_load_slot[nload] = sc;
+                set_slot(sc, (int)c, s_newa[c - n_old]);
+                if (lane == 0) {
+                    s_load_cell[nload] = (int)c;
+                    s_load_slot[nload] = sc;
+                }
                 ++nload;
             }
-            *s_nload = nload;
+            if (i0 < PW) { s_cell[i0] = cl0; s_a[i0] = al0; }
+            if (i1 < PW) { s_cell[i1] = cl1; s_a[i1] = al1; }
+            if (lane == 0) *s_nload = nload;
         }
         __syncthreads();
         const int nload = *s_nload;
