@@ -6,7 +6,7 @@ inputs already resident in HBM. Prints one JSON line with whole-job tokens/s,
 per-stage kernel times measured with HIP events on the library's stream, the
 roofline of the dominant kernel and the oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload c4] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload fwd_bf16_n262144] [--no-cpu]
 """
 import argparse
 import hashlib
@@ -63,7 +63,7 @@ class HipEvents:
 
 def algorithmic_work(sh, sel_np=None):
     """Per-launch algorithmic bytes / flops of each stage: what the method must move or compute,
-    each input read once and each output written once (DESIGN.md, section 7)."""
+    each input read once and each output written once."""
     H, N, d, s, w, B, K = sh.H, sh.N, sh.d, sh.s, sh.w, sh.B, sh.K
     e = 2 if sh.dtype == "bf16" else 4
     C = N // s
@@ -105,17 +105,18 @@ def algorithmic_work(sh, sel_np=None):
 
 # HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00, the
 # factors read off a plain 1 GiB device copy in the same run), for the kernel source they were taken
-# on; reported only while that source is unchanged.
+# on and the workload they were taken at; reported only for that workload while that source is unchanged.
 TRAFFIC = {
-    "readout_mix": {"bytes": 3188487861, "source": "long_context_sparse_cell_amd/csrc/readout_flash.hip",
+    "readout_mix": {"bytes": 3188487861, "workload": "fwd_bf16_h8_n262144_d128",
+                    "source": "long_context_sparse_cell_amd/csrc/readout_flash.hip",
                     "sha256": "db24c4bf584dee7774454ab46329c9d0fe7e22655b98ab2a622791ee6efd826f",
-                    "profile": "profiles/fwd_c4_hbm_traffic.md"},
+                    "profile": "profiles/fwd_n262144_hbm_traffic.md"},
 }
 
 
-def measured_traffic(stage):
+def measured_traffic(stage, workload):
     rec = TRAFFIC.get(stage)
-    if rec is None:
+    if rec is None or rec["workload"] != workload:
         return None
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"])
     try:
@@ -156,7 +157,7 @@ def cpu_baseline(inp, sample_rows):
 
 def decode_bench(fsl, synth, torch, dev, steps_override=None):
     """Streaming decode workload: prefill every sequence, then time the steps."""
-    sh = synth.CONFIGS["c5"]
+    sh = synth.CONFIGS["decode_64seq"]
     H, d, n, L = sh.H, sh.d, sh.n_seq, sh.prefix
     steps = sh.steps if steps_override is None else steps_override
     sig, lam, gam = (torch.from_numpy(a).to(dev) for a in synth.head_scalars(H))
@@ -267,7 +268,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", help="c1..c4 (default c4: N=262144, H=8, d=128, bf16)")
+    ap.add_argument("--workload", default="fwd_bf16_n262144", help="a forward workload of synth.CONFIGS (default fwd_bf16_n262144: N=262144, H=8, d=128, bf16)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-rows", type=int, default=131072)
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
@@ -279,7 +280,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "heads shard across GPUs with no exchange, see DESIGN.md", file=sys.stderr)
+              "the path would shard heads and sequences across GPUs with no exchange", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -351,7 +352,7 @@ def main():
     dominant = max((n for n in stages if "bound" in stages[n]), key=lambda n: stage_ms[n])
     dom = stages[dominant]
     roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
-                "unit": dom["unit"], "frac": dom["frac"], "traffic": measured_traffic(dominant)}
+                "unit": dom["unit"], "frac": dom["frac"], "traffic": measured_traffic(dominant, sh.name)}
 
     fs = None
     if not args.no_fs and sh.dtype == synth.BF16:

@@ -57,11 +57,11 @@ class Shape:
 
 # The five workloads: four forward shapes and one streaming-decode shape.
 CONFIGS: Dict[str, Shape] = {
-    "c1": Shape("fwd_f32_h1_n4096_d64", H=1, N=4096, d=64, dtype=F32, seed=1),
-    "c2": Shape("fwd_bf16_h16_n16384_d64", H=16, N=16384, d=64, dtype=BF16, seed=2),
-    "c3": Shape("fwd_bf16_h16_n65536_d64", H=16, N=65536, d=64, dtype=BF16, seed=3),
-    "c4": Shape("fwd_bf16_h8_n262144_d128", H=8, N=262144, d=128, dtype=BF16, seed=4),
-    "c5": Shape("decode_bf16_64seq_h16_d64_prefix131072", H=16, N=131072 + 256, d=64,
+    "fwd_f32_n4096": Shape("fwd_f32_h1_n4096_d64", H=1, N=4096, d=64, dtype=F32, seed=1),
+    "fwd_bf16_n16384": Shape("fwd_bf16_h16_n16384_d64", H=16, N=16384, d=64, dtype=BF16, seed=2),
+    "fwd_bf16_n65536": Shape("fwd_bf16_h16_n65536_d64", H=16, N=65536, d=64, dtype=BF16, seed=3),
+    "fwd_bf16_n262144": Shape("fwd_bf16_h8_n262144_d128", H=8, N=262144, d=128, dtype=BF16, seed=4),
+    "decode_64seq": Shape("decode_bf16_64seq_h16_d64_prefix131072", H=16, N=131072 + 256, d=64,
                 dtype=BF16, seed=5, n_seq=64, prefix=131072, steps=256, kind="decode"),
 }
 

@@ -210,7 +210,7 @@ def test_decode_validate_header():
 
 def test_decode_workload_shape_sample(oracle):
     """The decode workload's shape (prefix 131072, H=16, d=64, 256 steps), one sequence."""
-    sh = synth.CONFIGS["c5"]
+    sh = synth.CONFIGS["decode_64seq"]
     _case(f"decode workload sample {sh.name}")
     seq = synth.decode_sequence(sh, 0)
     res = run_decode(sh, [seq], sh.prefix, sh.steps)

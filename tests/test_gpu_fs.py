@@ -108,7 +108,7 @@ def _sample_rows(sh, n_random=96, seed=0):
     return rows
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("cfg", ["fwd_f32_n4096", "fwd_bf16_n16384", "fwd_bf16_n65536", "fwd_bf16_n262144"])
 def test_fs_workload_parity_and_needles(oracle, cfg):
     """The workload shapes with pruning off: every cell is a candidate; sampled rows
     (random rows, block edges, needle probes) against the oracle, and every needle in
@@ -121,11 +121,11 @@ def test_fs_workload_parity_and_needles(oracle, cfg):
     rows = _sample_rows(sh)
     for pr in inp.probes:
         rows.update(pr[:8])
-    rows = None if cfg == "c1" else np.array(sorted(rows), dtype=np.int64)
+    rows = None if cfg == "fwd_f32_n4096" else np.array(sorted(rows), dtype=np.int64)
     sel = compare_fs(oracle, inp, run, rows=rows)
     for h in range(sh.H):
         for m, pos in enumerate(inp.needles[h]):
-            probes = inp.probes[h] if cfg == "c4" else [inp.probes[h][m]]
+            probes = inp.probes[h] if cfg == "fwd_bf16_n262144" else [inp.probes[h][m]]
             for row in probes:
                 assert pos // sh.s in sel[h][row], (h, pos, row)
     del run

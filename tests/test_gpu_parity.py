@@ -167,14 +167,14 @@ def _sample_rows(sh, inp, n_random=160, seed=0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("cfg", ["fwd_f32_n4096", "fwd_bf16_n16384", "fwd_bf16_n65536", "fwd_bf16_n262144"])
 def test_workload_parity_and_needles(oracle, cfg):
     sh = synth.CONFIGS[cfg]
     _print_case(f"workload {cfg} {sh.name}")
     inp = synth.make_inputs(sh)
     run = GpuRun(inp)
-    rows = None if cfg == "c1" else _sample_rows(sh, inp)
-    compare_full(oracle, inp, run, rows=rows, check_internals=(cfg == "c1"))
+    rows = None if cfg == "fwd_f32_n4096" else _sample_rows(sh, inp)
+    compare_full(oracle, inp, run, rows=rows, check_internals=(cfg == "fwd_f32_n4096"))
     # needles: in the last block's pool and in their probe queries' selection (GPU values)
     pools = run.views["pool"].cpu().numpy()
     sel = run.sel.cpu().numpy()
@@ -183,7 +183,7 @@ def test_workload_parity_and_needles(oracle, cfg):
         for m, pos in enumerate(inp.needles[h]):
             cell = pos // sh.s
             assert cell in pools[h][last_blk], (h, pos)
-            probes = inp.probes[h] if cfg == "c4" else [inp.probes[h][m]]
+            probes = inp.probes[h] if cfg == "fwd_bf16_n262144" else [inp.probes[h][m]]
             for row in probes:
                 assert cell in sel[h][row], (h, pos, row)
     del run

@@ -62,7 +62,7 @@ def rand(shape, seed, dtype=synth.F32):
 
 def test_page_constants_match_defaults():
     g = json.load(open(GOLDEN))
-    sh = synth.CONFIGS["c2"]
+    sh = synth.CONFIGS["fwd_bf16_n16384"]
     for key in ("w", "s", "K", "P", "W", "B"):
         assert getattr(sh, key) == g[key]["value"], key
     assert sh.K * sh.s == g["read_budget_tokens"]["value"]
@@ -367,7 +367,7 @@ def test_mix_zero_long_branch(oracle):
 # whole forward
 
 def test_needle_survives_pruning_and_is_selected_c1(oracle):
-    inp = synth.make_inputs(synth.CONFIGS["c1"])
+    inp = synth.make_inputs(synth.CONFIGS["fwd_f32_n4096"])
     (res,) = oracle.forward(inp, rows=inp.probes[0], want_pool=True)
     cell = inp.needles[0][0] // inp.shape.s
     last_blk = (inp.shape.N - 1) // inp.shape.B
@@ -376,7 +376,7 @@ def test_needle_survives_pruning_and_is_selected_c1(oracle):
 
 
 def test_needles_survive_pruning_and_are_selected_c2(oracle):
-    inp = synth.make_inputs(synth.CONFIGS["c2"])
+    inp = synth.make_inputs(synth.CONFIGS["fwd_bf16_n16384"])
     sh = inp.shape
     for h in (0, 7, 15):
         p = oracle.head_from_shape(sh, h, inp.sigma, inp.lam, inp.gamma)
