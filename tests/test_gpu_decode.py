@@ -125,6 +125,9 @@ APPEND_CASES = [
     ("bf16_d64_prefill_then_appends", dict(H=2, d=64, dtype=synth.BF16), 5000, 150, [2048, 1536, 1416], True),
     ("f32_d128_block_aligned_chunks", dict(H=1, d=128, dtype=synth.F32), 3072, 140, [1024, 1024, 1024], False),
     ("bf16_d128_prefill_then_appends", dict(H=2, d=128, dtype=synth.BF16), 4200, 130, [3000, 700, 500], True),
+    # the largest slot table (P + W = 128): the boundary competition uses both slots of every lane
+    ("bf16_d64_pool128_chunks", dict(H=1, d=64, dtype=synth.BF16, w=256, s=16, B=64, P=64, W=64, K=8), 3000, 120,
+     [1000, 999, 1001], False),
     ("bf16_d64_small_window_tiny_chunks", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=32, P=4, W=2, K=3), 700,
      120, [1, 31, 32, 33, 300, 303], False),
 ]
