@@ -388,6 +388,9 @@ __global__ __launch_bounds__(256) void select_fs_fixup_kernel(const uint16_t *__
                                                               const float *__restrict__ amax,
                                                               int32_t *__restrict__ sel,
                                                               const uint32_t *__restrict__ fix, KParams p) {
+    // each wave's current query row in fp32 (written and read by that wave only: a wave's LDS
+    // operations complete in issue order)
+    __shared__ __attribute__((aligned(16))) float s_qf[4][D];
     const int64_t region = blockIdx.x;
     const uint32_t nfix = fix[region];
     const int lane = threadIdx.x & 63;
@@ -400,6 +403,7 @@ __global__ __launch_bounds__(256) void select_fs_fixup_kernel(const uint16_t *__
         const bool over = e[2] == kFsOverflow;
         const int64_t ncand = over ? eligible_cells(p, i / p.B) : (int64_t)e[2];
         const uint16_t *qg = q + ((int64_t)h * p.N + i) * D;
+        for (int x = lane; x < D; x += 64) s_qf[wave][x] = __uint_as_float((uint32_t)qg[x] << 16);
         const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
         double bs[kFsK];
         int bi[kFsK];
@@ -409,16 +413,19 @@ __global__ __launch_bounds__(256) void select_fs_fixup_kernel(const uint16_t *__
             const int c = over ? (int)t : (int)e[4 + t];
             const float *krow = kbar + ((int64_t)h * p.C + c) * D;
             double content = 0.0;
-            for (int x0 = 0; x0 < D; x0 += 8) {
-                const uint4 qv = *reinterpret_cast<const uint4 *>(qg + x0);
-                const float4 k0 = *reinterpret_cast<const float4 *>(krow + x0);
-                const float4 k1 = *reinterpret_cast<const float4 *>(krow + x0 + 4);
-                const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
-                const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            // 64 coordinates' loads per round, then their fma chain in coordinate order
+#pragma unroll 1
+            for (int x0 = 0; x0 < D; x0 += 64) {
+                float4 kv[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float qf = __uint_as_float(u & 1 ? (w4[u >> 1] & 0xFFFF0000u) : (w4[u >> 1] << 16));
-                    content = __fma_rn((double)qf, (double)kf[u], content);
+                for (int u = 0; u < 16; ++u) kv[u] = *reinterpret_cast<const float4 *>(krow + x0 + 4 * u);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const float4 q4 = *reinterpret_cast<const float4 *>(&s_qf[wave][x0 + 4 * u]);
+                    content = __fma_rn((double)q4.x, (double)kv[u].x, content);
+                    content = __fma_rn((double)q4.y, (double)kv[u].y, content);
+                    content = __fma_rn((double)q4.z, (double)kv[u].z, content);
+                    content = __fma_rn((double)q4.w, (double)kv[u].w, content);
                 }
             }
             const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)c * p.s)), 2.0 * (double)p.s);
