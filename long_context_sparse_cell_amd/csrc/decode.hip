@@ -47,13 +47,6 @@ __device__ __forceinline__ int64_t elig_nocap(const KParams &p, int64_t b) {
     return x <= 0 ? 0 : x / p.s;
 }
 
-template <typename T>
-__device__ __forceinline__ T from_f32(float x);
-template <>
-__device__ __forceinline__ float from_f32<float>(float x) { return x; }
-template <>
-__device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
-
 // element type of the rotated-key ring: fp16 bits for bf16 inputs, fp32 otherwise
 template <typename T> struct RotKey { typedef float type; };
 template <> struct RotKey<uint16_t> { typedef uint16_t type; };
