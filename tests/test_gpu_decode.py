@@ -102,6 +102,8 @@ DECODE_CASES = [
     # the largest slot table (P + W = 128: two slots per lane in the top K) with K = 8
     ("bf16_d64_pool128_k8", dict(H=1, d=64, dtype=synth.BF16, w=256, s=16, B=64, P=64, W=64, K=8), 3000, 200, None),
     ("f32_d128_pool128_k5", dict(H=1, d=128, dtype=synth.F32, w=200, s=16, B=32, P=64, W=64, K=5), 2600, 120, None),
+    # no high-norm places (P = 0): every cell leaving the recent set is freed
+    ("bf16_d64_p0_w3", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=64, P=0, W=3, K=2), 1500, 300, None),
 ]
 
 
@@ -128,6 +130,8 @@ APPEND_CASES = [
     # the largest slot table (P + W = 128): the boundary competition uses both slots of every lane
     ("bf16_d64_pool128_chunks", dict(H=1, d=64, dtype=synth.BF16, w=256, s=16, B=64, P=64, W=64, K=8), 3000, 120,
      [1000, 999, 1001], False),
+    ("bf16_d64_p0_w3_chunks", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=64, P=0, W=3, K=2), 1500, 200,
+     [700, 333, 467], False),
     ("bf16_d64_small_window_tiny_chunks", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=32, P=4, W=2, K=3), 700,
      120, [1, 31, 32, 33, 300, 303], False),
 ]
