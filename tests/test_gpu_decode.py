@@ -104,6 +104,8 @@ DECODE_CASES = [
     ("f32_d128_pool128_k5", dict(H=1, d=128, dtype=synth.F32, w=200, s=16, B=32, P=64, W=64, K=5), 2600, 120, None),
     # no high-norm places (P = 0): every cell leaving the recent set is freed
     ("bf16_d64_p0_w3", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=64, P=0, W=3, K=2), 1500, 300, None),
+    # 64-token cells: two cells enter per 128-token block
+    ("bf16_d128_s64", dict(H=1, d=128, dtype=synth.BF16, w=256, s=64, B=128, P=16, W=4, K=3), 2600, 300, None),
 ]
 
 
@@ -132,6 +134,8 @@ APPEND_CASES = [
      [1000, 999, 1001], False),
     ("bf16_d64_p0_w3_chunks", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=64, P=0, W=3, K=2), 1500, 200,
      [700, 333, 467], False),
+    ("f32_d64_s64_chunks", dict(H=1, d=64, dtype=synth.F32, w=256, s=64, B=128, P=16, W=4, K=3), 2600, 150,
+     [1111, 1489], False),
     ("bf16_d64_small_window_tiny_chunks", dict(H=2, d=64, dtype=synth.BF16, w=64, s=16, B=32, P=4, W=2, K=3), 700,
      120, [1, 31, 32, 33, 300, 303], False),
 ]
