@@ -141,8 +141,9 @@ int fsl_prune_select(const void *q, const float *kbar, const float *amax, int32_
  * call it holds kbar, amax, pool and sel (see fsl_workspace_views).
  * With bf16 inputs both attention branches multiply fp16 operands (keys
  * rotated, values and softmax weights) with fp32 accumulation, so k and v
- * must lie inside fp16's range (|x| < 65504); the selection path does not
- * depend on this.
+ * must lie inside fp16's range (|x| < 65504, a precondition); a call that
+ * breaks it sets FSL_STATUS_F16_RANGE in the workspace's status word. The
+ * selection path does not depend on this.
  * sel_out (device [H][N][K] int32), o_win_out and o_long_out (device
  * [H][N][d] float) are optional copies for inspection; pass NULL to skip. */
 int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
@@ -181,9 +182,19 @@ typedef struct fsl_workspace_layout {
     size_t khi;     /* bf16 [H][C][d] head of every kbar_c (bf16 with P = -1 only) */
     size_t klo;     /* bf16 [H][C][d] tail kbar_c - khi (bf16 with P = -1 only) */
     size_t kcf;     /* float4 [H][C] per-cell constants of the scoring bound (bf16 with P = -1 only) */
+    size_t status;  /* uint32 input check word, set by every forward (see FSL_STATUS_F16_RANGE) */
     size_t total;   /* bytes; equals fsl_workspace_bytes */
 } fsl_workspace_layout;
 int fsl_workspace_views(const fsl_params *p, fsl_workspace_layout *out);
+
+/* Bits of the workspace's status word after a forward (0 for fp32 inputs).
+ * FSL_STATUS_F16_RANGE: with bf16 inputs, an element of k or v, or a
+ * RoPE-rotated key, was not finite or had magnitude >= 65504, outside fp16's
+ * finite range. Both attention branches multiply fp16 operands, so the
+ * outputs of such a call are undefined (typically inf or NaN); selections
+ * and cell statistics do not depend on it. Reading the word is optional
+ * (it costs a device-to-host copy after the call completes). */
+#define FSL_STATUS_F16_RANGE 1u
 
 /* ------------------------------------------------------------------------
  * Streaming decode (ai.info summary, "Why This Matters": a bounded streaming

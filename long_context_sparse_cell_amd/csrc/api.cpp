@@ -80,6 +80,7 @@ fsl_workspace_layout layout(const KParams &k, bool full = true) {
     L.khi = take(bf && fs ? (size_t)k.H * k.C * k.d * sizeof(uint16_t) : 0);
     L.klo = take(bf && fs ? (size_t)k.H * k.C * k.d * sizeof(uint16_t) : 0);
     L.kcf = take(bf && fs ? (size_t)k.H * k.C * sizeof(float4) : 0);
+    L.status = take(sizeof(uint32_t));
     L.total = off;
     return L;
 }
@@ -101,7 +102,8 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
     w.fix = L.khi > L.fixups ? (uint32_t *)(b + L.fixups) : nullptr;  // present iff it has bytes
     w.khi = L.klo > L.khi ? (uint16_t *)(b + L.khi) : nullptr;
     w.klo = L.kcf > L.klo ? (uint16_t *)(b + L.klo) : nullptr;
-    w.kcf = L.total > L.kcf ? (float4 *)(b + L.kcf) : nullptr;
+    w.kcf = L.status > L.kcf ? (float4 *)(b + L.kcf) : nullptr;
+    w.status = (uint32_t *)(b + L.status);
     return w;
 }
 
@@ -243,7 +245,7 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
     // bf16: one pass over k and v gives the cell statistics, the rotated fp16 keys and the
     // transposed fp16 values (recorded as the statistics stage; the preparation stage is empty)
     if (e == hipSuccess)
-        e = mark(bf ? launch_kv_prep(k, v, w.kt, w.vt, w.rope_abs, w.kbar, w.amax, kp, stream)
+        e = mark(bf ? launch_kv_prep(k, v, w.kt, w.vt, w.rope_abs, w.kbar, w.amax, w.status, kp, stream)
                     : launch_cell_stats(k, w.kbar, w.amax, kp, stream));
     const bool fs = kp.P < 0;  // no pruning: the prune stage is empty
     if (e == hipSuccess) e = mark(fs ? hipSuccess : launch_prune(w.amax, w.pool, w, kp, stream));
@@ -255,7 +257,7 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
                             ? launch_select_fixup(q, w.kbar, w.amax, w.pool, w.sel, w.fix, kp, stream)
                             : hipErrorLaunchFailure)
                      : launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
-    if (e == hipSuccess) e = mark(bf ? hipSuccess : launch_rope_table(w.rope, kp, stream));
+    if (e == hipSuccess) e = mark(bf ? hipSuccess : launch_rope_table(w.rope, w.status, kp, stream));
     if (e == hipSuccess)
         e = mark(bf ? launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.o_win, kp, stream)
                     : launch_window(q, k, v, w.rope, w.o_win, kp, stream));

@@ -47,6 +47,7 @@ struct Work {
     // kbar_c, [H][C][d] each, and the per-cell constants of the error bound [H][C]
     uint16_t *khi, *klo;
     float4 *kcf;
+    uint32_t *status;  // input check word (FSL_STATUS_* bits), cleared by each forward's first kernel
 };
 
 constexpr int kFixRegion = 128;  // entries per region (queries per scoring work-group)
@@ -241,6 +242,23 @@ __device__ __forceinline__ float sum8_dpp(float x) {
 // weights below 2^-126 of the running maximum are flushed to zero.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two softmax weights as one packed fp16 pair for a P.V MFMA operand, rounded to
+// nearest even (v_cvt_pk_f16_f32), with the two rounded weights added to the fp32
+// running denominator (v_dot2c_f32_f16 against a pair of ones). The denominator then
+// sums exactly the weights the product multiplies, so weight rounding errors are
+// unbiased and do not accumulate into a one-sided output scale.
+typedef _Float16 fsl_half2 __attribute__((ext_vector_type(2)));
+typedef float fsl_float2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_f16_rne_acc(float a, float b, float &sum) {
+    const fsl_float2 f = {a, b};
+    const fsl_half2 h = __builtin_convertvector(f, fsl_half2);
+    const fsl_half2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    sum = __builtin_amdgcn_fdot2(h, ones, sum, false);
+    union { fsl_half2 h; uint32_t u; } c;
+    c.h = h;
+    return c.u;
+}
+
 // Online softmax with a lazily updated maximum: the reference value m only
 // moves when a new score exceeds it by more than kStaleLog2 (base-2 units), so
 // the weights 2^(s - m) stay within [0, 2^kStaleLog2] and the accumulators are
@@ -379,11 +397,11 @@ hipError_t launch_select_fixup(const void *q, const float *kbar, const float *am
                                int32_t *sel, const uint32_t *fix, const KParams &p, hipStream_t st);
 hipError_t launch_select_fs(const void *q, const float *kbar, const float *amax, int32_t *sel, const Work &w,
                             const KParams &p, hipStream_t st);
-hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st);
+hipError_t launch_rope_table(float2 *tab, uint32_t *status, const KParams &p, hipStream_t st);
 hipError_t launch_window(const void *q, const void *k, const void *v, const float2 *rope, float *o_win,
                          const KParams &p, hipStream_t st);
 hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs, float *kbar,
-                          float *amax, const KParams &p, hipStream_t st);
+                          float *amax, uint32_t *status, const KParams &p, hipStream_t st);
 hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs, float *o_win,
                               const KParams &p, hipStream_t st);
 hipError_t launch_readout_flash(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,

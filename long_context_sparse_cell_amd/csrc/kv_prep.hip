@@ -8,7 +8,10 @@
 //    O^T = V^T P^T products in both branches, one 16-byte piece per lane.
 // Np = 64 ceil(N/64): both arrays are padded to whole 64-token tiles with zeros.
 // fp16 holds bf16 values exactly inside fp16's range (|x| < 65504); the
-// fp16-operand products of both branches assume inputs in that range.
+// fp16-operand products of both branches assume inputs in that range, and an
+// element of k or v, or a rotated key, outside it (or not finite) sets
+// FSL_STATUS_F16_RANGE in the status word (cleared by rope_abs_kernel, which
+// runs first on the same stream).
 //
 // With kbar/amax given, the same pass also produces the cell statistics of the
 // tile's complete cells (FreeSolo digest, core method and step 3: the mean key
@@ -46,9 +49,10 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 raw, float (&o)[8]) {
 }  // namespace
 
 // rows [0, nhi): angle (64 a) theta_m; rows [nhi, nhi + 64): angle b theta_m
-__global__ void rope_abs_kernel(float2 *__restrict__ tab, int nhi, KParams p) {
+__global__ void rope_abs_kernel(float2 *__restrict__ tab, int nhi, uint32_t *__restrict__ status, KParams p) {
     const int half = p.d / 2;
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e == 0) *status = 0u;
     if (e >= (int64_t)(nhi + kRopeSpan) * half) return;
     const int row = (int)(e / half), m = (int)(e % half);
     const double pos = row < nhi ? (double)row * kRopeSpan : (double)(row - nhi);
@@ -61,7 +65,8 @@ template <int D, bool STATS>
 __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
                                                       uint16_t *__restrict__ kt, uint16_t *__restrict__ vt,
                                                       const float2 *__restrict__ rope, int nhi, float *__restrict__ kbar,
-                                                      float *__restrict__ amax, KParams p) {
+                                                      float *__restrict__ amax, uint32_t *__restrict__ status,
+                                                      KParams p) {
     constexpr int HALF = D / 2;
     constexpr int PG = HALF / 8;               // groups of 8 rotation pairs per row
     constexpr int KIT = kRopeSpan * PG / 256;  // key items per thread
@@ -112,6 +117,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
     }
 
     // ---- rotated keys
+    bool out_of_range = false;  // an fp16 operand would not hold this thread's value
     const float2 *hi = rope + (int64_t)blockIdx.x * HALF;
 #pragma unroll
     for (int u = 0; u < KIT; ++u) {
@@ -128,8 +134,10 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
             const float2 th = hi[8 * pg + r], tl = lo[8 * pg + r];
             const float c = th.x * tl.x - th.y * tl.y;
             const float s = th.y * tl.x + th.x * tl.y;
-            ra.f[r] = ok ? (_Float16)(a[r] * c - b[r] * s) : (_Float16)0.0f;
-            rb.f[r] = ok ? (_Float16)(b[r] * c + a[r] * s) : (_Float16)0.0f;
+            const float xa = a[r] * c - b[r] * s, xb = b[r] * c + a[r] * s;
+            out_of_range |= ok && !(fabsf(xa) < 65504.0f && fabsf(xb) < 65504.0f);
+            ra.f[r] = ok ? (_Float16)xa : (_Float16)0.0f;
+            rb.f[r] = ok ? (_Float16)xb : (_Float16)0.0f;
         }
         uint16_t *o = kt + h * kt_head_elems(p) + j * D;
         *reinterpret_cast<uint4 *>(o + 8 * pg) = ra.u;
@@ -147,11 +155,24 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             union { _Float16 f[2]; uint32_t u; } pr;
+            out_of_range |= (j < p.N && !(fabsf(e0[r]) < 65504.0f)) || (j + 1 < p.N && !(fabsf(e1[r]) < 65504.0f));
             pr.f[0] = j < p.N ? (_Float16)e0[r] : (_Float16)0.0f;
             pr.f[1] = j + 1 < p.N ? (_Float16)e1[r] : (_Float16)0.0f;
             *reinterpret_cast<uint32_t *>(&s_t[(8 * c8 + r) * TLD + 2 * jp]) = pr.u;
         }
     }
+    // raw keys past fp16's range are caught too (a rotation can shrink a coordinate)
+#pragma unroll
+    for (int u = 0; u < KIT; ++u) {
+        const int jl = (tid + 256 * u) / PG;
+        float a[8], b[8];
+        bf16x8_to_f32(ka[u], a);
+        bf16x8_to_f32(kb[u], b);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            out_of_range |= j0 + jl < p.N && !(fabsf(a[r]) < 65504.0f && fabsf(b[r]) < 65504.0f);
+    }
+    if (__ballot(out_of_range) != 0ull && (tid & 63) == 0) atomicOr(status, FSL_STATUS_F16_RANGE);
     __syncthreads();
     if constexpr (STATS) {
         // cell statistics of the tile's complete cells (cells of s tokens, s | 64)
@@ -210,17 +231,18 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
 }
 
 hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs, float *kbar,
-                          float *amax, const KParams &p, hipStream_t st) {
+                          float *amax, uint32_t *status, const KParams &p, hipStream_t st) {
     const int nhi = rope_abs_rows_hi(p);
     const int64_t n = (int64_t)(nhi + kRopeSpan) * (p.d / 2);
-    hipLaunchKernelGGL(rope_abs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, rope_abs, nhi, p);
+    hipLaunchKernelGGL(rope_abs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, rope_abs, nhi, status,
+                       p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)nhi, (unsigned)p.H);
     const bool stats = kbar && amax;
 #define FSL_KVP(DD, SS)                                                                                            \
     hipLaunchKernelGGL((kv_prep_kernel<DD, SS>), grid, dim3(256), 0, st, (const uint16_t *)k, (const uint16_t *)v, kt, \
-                       vt, rope_abs, nhi, kbar, amax, p)
+                       vt, rope_abs, nhi, kbar, amax, status, p)
     if (p.d == 64) {
         if (stats) FSL_KVP(64, true); else FSL_KVP(64, false);
     } else {

@@ -51,13 +51,6 @@ union R8 {
     halfx8 h;
 };
 
-// two floats to a packed fp16 pair (one v_cvt_pkrtz_f16_f32)
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-    union { decltype(__builtin_amdgcn_cvt_pkrtz(0.0f, 0.0f)) h; uint32_t u; } c;
-    c.h = __builtin_amdgcn_cvt_pkrtz(a, b);
-    return c.u;
-}
-
 }  // namespace
 
 template <int D, int S, bool FS>
@@ -291,12 +284,9 @@ __global__ __launch_bounds__(kRfThreads, 4) void readout_flash_kernel(
             if (tt < NT) {
                 float e[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    e[r] = exp2_hw(fmaf(sacc[tt][r], sl2, -msub));
-                    lsum += e[r];
-                }
-                lo = pk_f16(e[0], e[1]);
-                hi = pk_f16(e[2], e[3]);
+                for (int r = 0; r < 4; ++r) e[r] = exp2_hw(fmaf(sacc[tt][r], sl2, -msub));
+                lo = pk_f16_rne_acc(e[0], e[1], lsum);
+                hi = pk_f16_rne_acc(e[2], e[3], lsum);
             }
             pb[tt >> 1].d[tt & 1] = make_uint2(lo, hi);
         }

@@ -33,9 +33,10 @@ namespace fsl {
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-__global__ void rope_table_kernel(float2 *__restrict__ tab, KParams p) {
+__global__ void rope_table_kernel(float2 *__restrict__ tab, uint32_t *__restrict__ status, KParams p) {
     const int half = p.d / 2;
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e == 0) *status = 0u;  // fp32 inputs take no fp16 conversion: nothing to flag
     if (e >= (int64_t)p.rope_n * half) return;
     const int row = (int)(e / half), m = (int)(e % half);
     const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)p.d);
@@ -43,9 +44,9 @@ __global__ void rope_table_kernel(float2 *__restrict__ tab, KParams p) {
     tab[e] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-hipError_t launch_rope_table(float2 *tab, const KParams &p, hipStream_t st) {
+hipError_t launch_rope_table(float2 *tab, uint32_t *status, const KParams &p, hipStream_t st) {
     const int64_t n = (int64_t)p.rope_n * (p.d / 2);
-    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, p);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, status, p);
     return hipGetLastError();
 }
 

@@ -37,13 +37,6 @@ union P8 {
     halfx8 v;
 };
 
-// two floats to a packed fp16 pair (one v_cvt_pkrtz_f16_f32)
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-    union { decltype(__builtin_amdgcn_cvt_pkrtz(0.0f, 0.0f)) h; uint32_t u; } c;
-    c.h = __builtin_amdgcn_cvt_pkrtz(a, b);
-    return c.u;
-}
-
 }  // namespace
 
 template <int D>
@@ -215,11 +208,10 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
             for (int kg = 0; kg < 4; ++kg) {
                 float e[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    e[r] = exp2_hw(fmaf(sacc[kg][qg][r], sl2, -msub));
-                    lsum += e[r];
-                }
-                pb[kg >> 1][qg].d[kg & 1] = make_uint2(pk_f16(e[0], e[1]), pk_f16(e[2], e[3]));
+                for (int r = 0; r < 4; ++r) e[r] = exp2_hw(fmaf(sacc[kg][qg][r], sl2, -msub));
+                const uint32_t w01 = pk_f16_rne_acc(e[0], e[1], lsum);
+                const uint32_t w23 = pk_f16_rne_acc(e[2], e[3], lsum);
+                pb[kg >> 1][qg].d[kg & 1] = make_uint2(w01, w23);
             }
             l_part[qg] += lsum;
         }

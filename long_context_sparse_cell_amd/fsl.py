@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from contextlib import nullcontext as _nullcontext
 from typing import Optional
 
 import torch
@@ -40,7 +41,7 @@ class Params(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win", "rope_abs", "kt", "vt",
-                                      "fixups", "khi", "klo", "kcf", "total")]
+                                      "fixups", "khi", "klo", "kcf", "status", "total")]
 
 
 _lib = None
@@ -107,6 +108,61 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.float32 if code == FSL_F32 else torch.bfloat16
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype, optional=False):
+    """Reject a tensor whose shape or dtype does not match what the library will read or
+    write through its pointer: a mismatch would become an out-of-bounds access on the
+    device, so it is caught here, before any launch (devices are checked by _on_gpu)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: a tensor is required")
+    shape = tuple(int(x) for x in shape)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {shape}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensors passed to the FS-L library must be contiguous")
+
+
+def _on_gpu(**named):
+    """Every given tensor (None entries skipped) must be GPU memory on one device; returns it."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: tensor on {t.device}, the library needs GPU memory")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name}: tensor on {t.device}, other operands on {dev}")
+    return dev
+
+
+def _expect_ws(ws: torch.Tensor, need: int, device, name="ws"):
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError(f"{name}: a 1-D uint8 tensor is expected, got {ws.dtype} with shape {tuple(ws.shape)}")
+    if ws.numel() < need:
+        raise ValueError(f"{name}: {ws.numel()} bytes, the call needs {need}")
+    if ws.device.type != "cuda" or ws.device != device:
+        raise ValueError(f"{name}: tensor on {ws.device}, other operands on {device}")
+
+
+def _empty(shape, dtype, device, stream):
+    """A new tensor from torch's caching allocator, associated with the stream the library
+    launches on, so that its memory is not handed to other work while the kernels still
+    use it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def dtype_code(t: torch.dtype) -> int:
     if t == torch.float32:
         return FSL_F32
@@ -144,47 +200,100 @@ def workspace_layout(p: Params) -> WorkspaceLayout:
     return L
 
 
-def new_workspace(p: Params, device="cuda") -> torch.Tensor:
+def new_workspace(p: Params, device="cuda", stream=None) -> torch.Tensor:
     n = workspace_bytes(p)
     if n == 0:
         _check(check_params(p), "fsl_workspace_bytes")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return _empty(n, torch.uint8, device, stream)
+
+
+def _qkv_shape(p: Params):
+    return (p.H, p.N, p.d)
 
 
 def cell_stats(k: torch.Tensor, p: Params, kbar: Optional[torch.Tensor] = None,
                amax: Optional[torch.Tensor] = None, stream=None):
     C = p.N // p.s
+    _expect(k, "k", _qkv_shape(p), _torch_dtype(p.dtype))
+    _expect(kbar, "kbar", (p.H, C, p.d), torch.float32, optional=True)
+    _expect(amax, "amax", (p.H, C), torch.float32, optional=True)
+    dev = _on_gpu(k=k, kbar=kbar, amax=amax)
     if kbar is None:
-        kbar = torch.empty((p.H, C, p.d), dtype=torch.float32, device=k.device)
+        kbar = _empty((p.H, C, p.d), torch.float32, dev, stream)
     if amax is None:
-        amax = torch.empty((p.H, C), dtype=torch.float32, device=k.device)
+        amax = _empty((p.H, C), torch.float32, dev, stream)
     _check(lib().fsl_cell_stats(_ptr(k), _ptr(kbar), _ptr(amax), ctypes.byref(p), _stream(stream)),
            "fsl_cell_stats")
     return kbar, amax
 
 
 def prune_select(q: torch.Tensor, kbar: torch.Tensor, amax: torch.Tensor, p: Params,
-                 ws: Optional[torch.Tensor] = None, stream=None):
+                 ws: Optional[torch.Tensor] = None, pool: Optional[torch.Tensor] = None,
+                 sel: Optional[torch.Tensor] = None, stream=None):
     """Pools and per-query selections; without pruning (P = -1) no pool is formed and None is returned for it."""
+    C = p.N // p.s
     nblk = (p.N + p.B - 1) // p.B
-    pool = torch.empty((p.H, nblk, p.P + p.W), dtype=torch.int32, device=q.device) if p.P >= 0 else None
-    sel = torch.empty((p.H, p.N, p.K), dtype=torch.int32, device=q.device)
-    ws = new_workspace(p, q.device) if ws is None else ws
+    _expect(q, "q", _qkv_shape(p), _torch_dtype(p.dtype))
+    _expect(kbar, "kbar", (p.H, C, p.d), torch.float32)
+    _expect(amax, "amax", (p.H, C), torch.float32)
+    if p.P < 0:
+        pool = None
+    _expect(pool, "pool", (p.H, nblk, p.P + p.W), torch.int32, optional=True)
+    _expect(sel, "sel", (p.H, p.N, p.K), torch.int32, optional=True)
+    dev = _on_gpu(q=q, kbar=kbar, amax=amax, pool=pool, sel=sel, ws=ws)
+    if p.P >= 0 and pool is None:
+        pool = _empty((p.H, nblk, p.P + p.W), torch.int32, dev, stream)
+    if sel is None:
+        sel = _empty((p.H, p.N, p.K), torch.int32, dev, stream)
+    ws = new_workspace(p, dev, stream) if ws is None else ws
+    _expect_ws(ws, workspace_bytes(p), dev)
     _check(lib().fsl_prune_select(_ptr(q), _ptr(kbar), _ptr(amax), _ptr(pool), _ptr(sel), ctypes.byref(p),
                                   _ptr(ws), ws.numel(), _stream(stream)), "fsl_prune_select")
     return pool, sel
 
 
+def _check_fwd_operands(q, k, v, out, p: Params, sel_out=None, o_win_out=None, o_long_out=None, ws=None):
+    shp = _qkv_shape(p)
+    _expect(q, "q", shp, _torch_dtype(p.dtype))
+    _expect(k, "k", shp, _torch_dtype(p.dtype))
+    _expect(v, "v", shp, _torch_dtype(p.dtype))
+    _expect(out, "out", shp, _torch_dtype(p.out_dtype), optional=True)
+    _expect(sel_out, "sel_out", (p.H, p.N, p.K), torch.int32, optional=True)
+    _expect(o_win_out, "o_win_out", shp, torch.float32, optional=True)
+    _expect(o_long_out, "o_long_out", shp, torch.float32, optional=True)
+    return _on_gpu(q=q, k=k, v=v, out=out, sel_out=sel_out, o_win_out=o_win_out, o_long_out=o_long_out, ws=ws)
+
+
+FSL_STATUS_F16_RANGE = 1
+
+
+def range_status(ws: torch.Tensor, p: Params) -> int:
+    """The status word a forward left in its workspace (FSL_STATUS_* bits); waits for the stream."""
+    L = workspace_layout(p)
+    return int(ws[L.status: L.status + 4].view(torch.int32).item())
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, out: Optional[torch.Tensor] = None,
              ws: Optional[torch.Tensor] = None, sel_out: Optional[torch.Tensor] = None,
-             o_win_out: Optional[torch.Tensor] = None, o_long_out: Optional[torch.Tensor] = None, stream=None):
-    """FS-L forward. q, k, v: [H][N][d] device tensors (float32 or bfloat16)."""
+             o_win_out: Optional[torch.Tensor] = None, o_long_out: Optional[torch.Tensor] = None, stream=None,
+             check_range: bool = False):
+    """FS-L forward. q, k, v: [H][N][d] device tensors (float32 or bfloat16).
+
+    check_range: after the call, read the workspace's status word and raise ValueError if a bf16
+    input (or a rotated key) was outside fp16's finite range, which both attention branches need."""
+    dev = _check_fwd_operands(q, k, v, out, p, sel_out, o_win_out, o_long_out, ws)
     if out is None:
-        odt = torch.float32 if p.out_dtype == FSL_F32 else torch.bfloat16
-        out = torch.empty(q.shape, dtype=odt, device=q.device)
-    ws = new_workspace(p, q.device) if ws is None else ws
+        out = _empty(q.shape, _torch_dtype(p.out_dtype), dev, stream)
+    ws = new_workspace(p, dev, stream) if ws is None else ws
+    _expect_ws(ws, workspace_bytes(p), dev)
     _check(lib().fsl_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(p), _ptr(ws), ws.numel(),
                               _ptr(sel_out), _ptr(o_win_out), _ptr(o_long_out), _stream(stream)), "fsl_attn_fwd")
+    if check_range:
+        with torch.cuda.stream(stream) if stream is not None else _nullcontext():
+            st = range_status(ws, p)
+        if st & FSL_STATUS_F16_RANGE:
+            raise ValueError("fsl_attn_fwd: an element of k or v, or a rotated key, lies outside fp16's finite "
+                             "range (|x| >= 65504 or not finite); the outputs of this call are undefined")
     return out
 
 
@@ -194,6 +303,11 @@ STAGES = ("cell_stats", "prune", "select", "kv_prep", "window", "readout_mix")
 
 def attn_fwd_timed(q, k, v, p: Params, out: torch.Tensor, ws: torch.Tensor, events, stream=None):
     """fsl_attn_fwd recording NUM_STAGES + 1 hipEvent_t handles (a ctypes array) between its stages."""
+    _expect(out, "out", _qkv_shape(p), _torch_dtype(p.out_dtype))
+    dev = _check_fwd_operands(q, k, v, out, p, ws=ws)
+    _expect_ws(ws, workspace_bytes(p), dev)
+    if events is None:
+        raise ValueError(f"events: a pointer to {NUM_STAGES + 1} hipEvent_t handles is required")
     _check(lib().fsl_attn_fwd_timed(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(p), _ptr(ws), ws.numel(),
                                     events, _stream(stream)), "fsl_attn_fwd_timed")
     return out
@@ -204,6 +318,7 @@ def workspace_views(ws: torch.Tensor, p: Params):
     L = workspace_layout(p)
     C = p.N // p.s
     nblk = (p.N + p.B - 1) // p.B
+    _expect_ws(ws, L.total, ws.device)
 
     def view(off, n, dt, shape):
         esz = torch.tensor([], dtype=dt).element_size()
@@ -230,7 +345,7 @@ class DecodeState:
         n = int(lib().fsl_decode_state_bytes(ctypes.byref(p), n_seq))
         if n == 0:
             _check(FSL_E_INVAL if n_seq < 1 else check_params(p), "fsl_decode_state_bytes")
-        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        self.buf = _empty(n, torch.uint8, device, stream)
         _check(lib().fsl_decode_init(_ptr(self.buf), n, n_seq, ctypes.byref(p), _stream(stream)), "fsl_decode_init")
 
     @property
@@ -239,10 +354,22 @@ class DecodeState:
 
     def prefill(self, seq: int, k_prefix: torch.Tensor, v_prefix: torch.Tensor, ws: Optional[torch.Tensor] = None,
                 stream=None):
-        L = k_prefix.shape[1]
+        """Load sequence seq from a prefix k_prefix, v_prefix [H][L][d]. Returns the workspace used; it must
+        stay allocated until the stream has run the call's work (a workspace made here is tied to
+        `stream`)."""
+        if k_prefix.dim() != 3:
+            raise ValueError(f"k_prefix: shape {tuple(k_prefix.shape)}, expected [H][L][d]")
+        L = int(k_prefix.shape[1])
+        dt = _torch_dtype(self.p.dtype)
+        _expect(k_prefix, "k_prefix", (self.p.H, L, self.p.d), dt)
+        _expect(v_prefix, "v_prefix", (self.p.H, L, self.p.d), dt)
+        _on_gpu(state=self.buf, k_prefix=k_prefix, v_prefix=v_prefix, ws=ws)
+        if not 0 <= seq < self.n_seq:
+            raise ValueError(f"seq {seq} outside [0, {self.n_seq})")
         need = int(lib().fsl_decode_prefill_workspace_bytes(ctypes.byref(self.p), L))
         if ws is None or ws.numel() < need:
-            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.buf.device)
+            ws = _empty(max(need, 1), torch.uint8, self.buf.device, stream)
+        _expect_ws(ws, need, self.buf.device)
         _check(lib().fsl_decode_prefill(_ptr(self.buf), self.nbytes, seq, _ptr(k_prefix), _ptr(v_prefix), L,
                                         ctypes.byref(self.p), _ptr(ws), ws.numel(), _stream(stream)),
                "fsl_decode_prefill")
@@ -251,16 +378,33 @@ class DecodeState:
     def append(self, seq: int, k: torch.Tensor, v: torch.Tensor, stream=None):
         """Append tokens without queries (streamed prefill): k, v [H][len][d] for sequence seq, or
         [n][H][len][d] for sequences seq .. seq + n - 1."""
+        if k.dim() not in (3, 4):
+            raise ValueError(f"k: shape {tuple(k.shape)}, expected [H][len][d] or [n][H][len][d]")
         n = 1 if k.dim() == 3 else int(k.shape[0])
         L = int(k.shape[-2])
+        shp = (self.p.H, L, self.p.d) if k.dim() == 3 else (n, self.p.H, L, self.p.d)
+        dt = _torch_dtype(self.p.dtype)
+        _expect(k, "k", shp, dt)
+        _expect(v, "v", shp, dt)
+        _on_gpu(state=self.buf, k=k, v=v)
+        if seq < 0 or seq + n > self.n_seq:
+            raise ValueError(f"sequences {seq} .. {seq + n - 1} outside [0, {self.n_seq})")
         _check(lib().fsl_decode_append(_ptr(self.buf), self.nbytes, seq, n, _ptr(k), _ptr(v), L,
                                        ctypes.byref(self.p), _stream(stream)), "fsl_decode_append")
 
     def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, stream=None):
+        """Advance every sequence by one token: q, k, v [n_seq][H][d]."""
+        shp = (self.n_seq, self.p.H, self.p.d)
+        dt = _torch_dtype(self.p.dtype)
+        _expect(q, "q", shp, dt)
+        _expect(k, "k", shp, dt)
+        _expect(v, "v", shp, dt)
+        _expect(out, "out", shp, _torch_dtype(self.p.out_dtype), optional=True)
+        _expect(sel_out, "sel_out", (self.n_seq, self.p.H, self.p.K), torch.int32, optional=True)
+        dev = _on_gpu(state=self.buf, q=q, k=k, v=v, out=out, sel_out=sel_out)
         if out is None:
-            odt = torch.float32 if self.p.out_dtype == FSL_F32 else torch.bfloat16
-            out = torch.empty(q.shape, dtype=odt, device=q.device)
+            out = _empty(shp, _torch_dtype(self.p.out_dtype), dev, stream)
         _check(lib().fsl_decode_step(_ptr(self.buf), self.nbytes, _ptr(q), _ptr(k), _ptr(v), _ptr(out), self.n_seq,
                                      ctypes.byref(self.p), _ptr(sel_out), _stream(stream)), "fsl_decode_step")
         return out

@@ -67,3 +67,23 @@ def check_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
     else:
         assert err.max() <= F32_MAX_ABS, info
     return float(err.max()), float(err.mean())
+
+
+def near_tie_rows(run, fs: bool):
+    """(head, row) of every query the bf16 scoring passed to its exact fp64 fix-up: the
+    queries whose certified MFMA filter left more than K contenders. Read from the
+    workspace's near-tie list (a count per scoring region, then 128 entries of 6 words,
+    or 36 without pruning, each starting with head and row)."""
+    from long_context_sparse_cell_amd import fsl
+    p = run.p
+    L = fsl.workspace_layout(p)
+    qw = p.B if p.B <= 128 else p.B // 2
+    regions = p.H * ((p.N + qw - 1) // qw)
+    words = 36 if fs else 6
+    base = (regions + 63) // 64 * 64
+    raw = run.ws[L.fixups: L.fixups + (base + regions * 128 * words) * 4].view(torch.int32).cpu().numpy()
+    counts = raw[:regions]
+    assert counts.min() >= 0 and counts.max() <= 128, "near-tie list counts out of range"
+    ent = raw[base:].reshape(regions, 128, words)
+    rows = [(int(ent[r, j, 0]), int(ent[r, j, 1])) for r in np.nonzero(counts)[0] for j in range(counts[r])]
+    return rows

@@ -2,9 +2,11 @@
 
 Indices (pools, selections) and the cell statistics must be bit-exact;
 outputs must be within 1e-4 max-abs for fp32 inputs and 2e-2 max-abs /
-1e-2 mean-abs for bf16 inputs. Small shapes are compared at every query;
-the full workload shapes are compared on every pool and cell statistic and
-on sampled query rows (probes, block edges, random rows, the last row).
+1e-2 mean-abs for bf16 inputs. Every shape, the four workloads up to
+N=262144 included, is compared on every pool, cell statistic, selection and
+output row; the branch outputs (o_win, RMSNorm(o_long)) are compared on every
+row up to N=16384 and on sampled rows (probes, block edges, random rows, the
+last row) beyond.
 """
 import numpy as np
 import pytest
@@ -30,14 +32,32 @@ def _print_case(name):
 
 # Branch-level diagnostics (the parity bar itself is on `out`, checked below).
 # With bf16 inputs both branches multiply fp16 operands: softmax weights rounded
-# toward zero carry up to 2^-10 relative error, which moves an output by up to
-# 2^-10 of the weighted spread |v_j - o_i| (about 4 for N(0,1) values, so
-# ~4e-3), on top of the fp16 rounding of the rotated q and k inside the scores.
-BRANCH_TOL_BF16 = 6e-3
+# to nearest carry up to 2^-11 relative error each, unbiased, and the softmax
+# denominator sums the same rounded weights, so an output moves by a signed sum
+# of those errors times the spread |v_j - o_i| (about 4 for N(0,1) values). The
+# fp16 rounding of the rotated query and keys inside the window's scores moves a
+# score by up to scale * 2^-10 * |q_i| |k_j|: it grows with the key norms, so a
+# window holding a planted key of large norm (the needles of the N=16384 workload,
+# about 110 against 8-16 for N(0,1) keys) sees proportionally larger errors. The
+# window bound is BRANCH_TOL_BF16 * max(1, kappa_i / KAPPA_REF), kappa_i the
+# largest key norm in row i's window.
+BRANCH_TOL_BF16 = 4e-3
+KAPPA_REF = 32.0
 
 
-def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=True):
-    """Compare one GPU run with the oracle, head by head."""
+def window_key_norm_max(k_h, rows, w):
+    """Largest key norm over each row's window [i - w + 1, i]."""
+    norms = np.linalg.norm(k_h.astype(np.float64), axis=1)
+    out = np.empty(len(rows))
+    for t, i in enumerate(rows):
+        out[t] = norms[max(0, i - w + 1): i + 1].max()
+    return out
+
+
+def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=True, internal_rows=None):
+    """Compare one GPU run with the oracle, head by head: statistics and pools in full,
+    selections and outputs on `rows` (default every row), the branch outputs on
+    `internal_rows` (a subset of `rows`; default all of them) when check_internals."""
     sh = inp.shape
     over_oracle = over_oracle or {}
     pools = run.views["pool"].cpu().numpy()
@@ -56,18 +76,32 @@ def compare_full(oracle, inp, run, over_oracle=None, rows=None, check_internals=
         idx = r["rows"]
         np.testing.assert_array_equal(sel[h][idx], r["sel"], err_msg=f"sel head {h}")
         if check_internals:
-            ew = np.abs(o_win[h][idx] - r["o_win"]).max()
+            pos = np.arange(len(idx)) if internal_rows is None else np.searchsorted(idx, internal_rows)
+            if internal_rows is not None:
+                assert np.array_equal(idx[pos], internal_rows)
+            sub = idx[pos]
+            ew = np.abs(o_win[h][sub] - r["o_win"][pos]).max()
 
             def normed(o):
                 return o / np.sqrt((o.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6)
-            el = np.abs(normed(o_long[h][idx]) - normed(r["o_long"])).max()
+            el = np.abs(normed(o_long[h][sub]) - normed(r["o_long"][pos])).max()
             print(f"  head {h}: o_win max err {ew:.3e}, RMSNorm(o_long) max err {el:.3e}", flush=True)
-            tol = 1e-4 if sh.dtype == synth.F32 else BRANCH_TOL_BF16
-            assert ew <= tol, f"o_win head {h}: {ew:.3e}"
-            assert el <= tol, f"RMSNorm(o_long) head {h}: {el:.3e}"
+            if sh.dtype == synth.F32:
+                assert ew <= 1e-4, f"o_win head {h}: {ew:.3e}"
+                assert el <= 1e-4, f"RMSNorm(o_long) head {h}: {el:.3e}"
+            else:
+                kappa = window_key_norm_max(inp.k[h], sub, sh.w)
+                tol_w = BRANCH_TOL_BF16 * np.maximum(1.0, kappa / KAPPA_REF)
+                err_w = np.abs(o_win[h][sub] - r["o_win"][pos]).max(axis=1)
+                bad = np.nonzero(err_w > tol_w)[0]
+                assert bad.size == 0, (f"o_win head {h}: row {sub[bad[0]]} error {err_w[bad[0]]:.3e} "
+                                       f"> {tol_w[bad[0]]:.3e} (largest key norm in its window {kappa[bad[0]]:.1f})")
+                assert el <= BRANCH_TOL_BF16, f"RMSNorm(o_long) head {h}: {el:.3e}"
         mx, mean = check_out(out[h][idx], r["out"], out_dtype, f"out head {h}")
-        print(f"  head {h}: out max err {mx:.3e}, mean {mean:.3e}", flush=True)
+        print(f"  head {h}: out max err {mx:.3e}, mean {mean:.3e}, rows {len(idx)}, "
+              f"min top-K margin {r['margin'].min():.3e}", flush=True)
         worst = max(worst, mx)
+        del r
     return worst
 
 
@@ -169,12 +203,15 @@ def _sample_rows(sh, inp, n_random=160, seed=0):
 
 @pytest.mark.parametrize("cfg", ["fwd_f32_n4096", "fwd_bf16_n16384", "fwd_bf16_n65536", "fwd_bf16_n262144"])
 def test_workload_parity_and_needles(oracle, cfg):
+    """Every row of every workload: selections bit-exact and outputs within tolerance,
+    pools and cell statistics bit-exact; the branch outputs on every row up to
+    N=16384 and on sampled rows beyond."""
     sh = synth.CONFIGS[cfg]
     _print_case(f"workload {cfg} {sh.name}")
     inp = synth.make_inputs(sh)
     run = GpuRun(inp)
-    rows = None if cfg == "fwd_f32_n4096" else _sample_rows(sh, inp)
-    compare_full(oracle, inp, run, rows=rows, check_internals=(cfg == "fwd_f32_n4096"))
+    small = sh.N * sh.H <= 16 * 16384
+    compare_full(oracle, inp, run, rows=None, internal_rows=None if small else _sample_rows(sh, inp))
     # needles: in the last block's pool and in their probe queries' selection (GPU values)
     pools = run.views["pool"].cpu().numpy()
     sel = run.sel.cpu().numpy()
@@ -188,3 +225,34 @@ def test_workload_parity_and_needles(oracle, cfg):
                 assert cell in sel[h][row], (h, pos, row)
     del run
     torch.cuda.empty_cache()
+
+
+def test_fp16_range_precondition_is_flagged():
+    """bf16 inputs feed fp16 operands: an element of k or v at or beyond fp16's finite
+    range sets the status bit (and attn_fwd(check_range=True) raises); the largest bf16
+    value inside the range does not."""
+    from long_context_sparse_cell_amd import fsl
+    _print_case("fp16 range flag")
+    sh = synth.Shape("range_flag", H=2, N=3000, d=64, dtype=synth.BF16, seed=12)
+    base = synth.random_inputs(sh)
+
+    def run_with(plant):
+        inp = synth.random_inputs(sh)
+        plant(inp)
+        r = GpuRun(inp, want_internals=False)
+        return r, fsl.range_status(r.ws, r.p)
+
+    r, st = run_with(lambda i: i.v.__setitem__((1, 100, 5), 65280.0))  # largest bf16 below 65504
+    assert st == 0
+    assert bool(torch.isfinite(r.out.float()).all())
+    fsl.attn_fwd(r.q, r.k, r.v, r.p, ws=r.ws, check_range=True)  # no error
+    for where, val in [("k", 70144.0), ("v", -1.0e6)]:  # finite: non-finite inputs are outside the contract
+        r, st = run_with(lambda i: getattr(i, where).__setitem__((0, 2000, 7), val))
+        assert st & fsl.FSL_STATUS_F16_RANGE, (where, val)
+        with pytest.raises(ValueError, match="fp16"):
+            fsl.attn_fwd(r.q, r.k, r.v, r.p, ws=r.ws, check_range=True)
+    # a clean run after a flagged one clears the word
+    r2 = GpuRun(base, want_internals=False)
+    assert fsl.range_status(r2.ws, r2.p) == 0
+    r2.out = fsl.attn_fwd(r2.q, r2.k, r2.v, r2.p, ws=r.ws)
+    assert fsl.range_status(r.ws, r2.p) == 0

@@ -86,7 +86,9 @@ def test_good_parameters_and_workspace_size(fsl):
     C, nblk = 4096 // 32, 4096 // 128
     assert L.amax - L.kbar >= 2 * C * 64 * 4
     assert L.sel - L.pool >= 2 * nblk * 72 * 4
-    assert all(getattr(L, f) % 256 == 0 for f in ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win"))
+    assert all(getattr(L, f) % 256 == 0 for f in ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win",
+                                                  "status"))
+    assert L.total - L.status >= 4  # the status word is the last array
 
 
 @pytest.mark.parametrize("N,d", [(5000, 128), (4096, 64), (64, 64), (1, 128), (262144, 128)])
@@ -99,12 +101,12 @@ def test_prepared_key_value_arrays_cover_whole_tiles(fsl, N, d):
     L = fsl.workspace_layout(p)
     need = H * (64 * ((N + 63) // 64)) * d * 2
     assert L.vt - L.kt >= need
-    assert L.total - L.vt >= need
+    assert L.status - L.vt >= need
     assert L.kt % 256 == 0 and L.vt % 256 == 0
     # the fp32 path does not prepare them
     p32 = params(fsl, N=N, d=d, H=H, dtype=0, out_dtype=0)
     L32 = fsl.workspace_layout(p32)
-    assert L32.total == L32.vt == L32.kt
+    assert L32.status == L32.vt == L32.kt
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
@@ -122,13 +124,13 @@ def test_unpruned_variant_workspace(fsl, dtype):
         regions = H * ((N + 127) // 128)
         assert L.khi - L.fixups >= 4 * ((regions + 63) // 64 * 64 + regions * 128 * 36)
         assert L.klo - L.khi >= H * C * d * 2 and L.kcf - L.klo >= H * C * d * 2
-        assert L.total - L.kcf >= H * C * 16
+        assert L.status - L.kcf >= H * C * 16
         assert all(getattr(L, f) % 256 == 0 for f in ("fixups", "khi", "klo", "kcf"))
     else:
-        assert L.total == L.kcf == L.klo == L.khi
+        assert L.status == L.kcf == L.klo == L.khi
     # the pruned variant has none of the split arrays
     Lp = fsl.workspace_layout(params(fsl, N=N, H=H, d=d, dtype=dtype, out_dtype=dtype))
-    assert Lp.total == Lp.kcf == Lp.klo == Lp.khi
+    assert Lp.status == Lp.kcf == Lp.klo == Lp.khi
     # pool may be NULL without pruning, not with it
     lib = fsl.lib()
     a = ctypes.c_void_p(0x100000)
@@ -201,3 +203,74 @@ def test_decode_entry_points_reject_bad_arguments(fsl):
     assert L.fsl_decode_append(a, n, 0, 0, a, a, 10, ctypes.byref(p), None) == -1
     assert L.fsl_decode_append(a, n, -1, 1, a, a, 10, ctypes.byref(p), None) == -1
     assert L.fsl_decode_append(a, n, 0, 1, a, a, 10, ctypes.byref(params(fsl, P=-1)), None) == -2
+
+
+# ---------------------------------------------------------------------------
+# the Python binding checks every tensor against the parameter block before any
+# launch (a mismatch would otherwise be an out-of-bounds access on the device)
+
+def _cpu_params(fsl, torch, **kw):
+    H = kw.pop("H", 2)
+    N = kw.pop("N", 512)
+    d = kw.pop("d", 64)
+    dt = kw.pop("dtype", torch.bfloat16)
+    sig = torch.full((H,), 4.0)
+    lam = torch.ones(H)
+    gam = torch.ones(H)
+    return fsl.make_params(N, H, d, dt, sig, lam, gam, **kw)
+
+
+def test_binding_rejects_mismatched_tensors(fsl):
+    import torch
+    p = _cpu_params(fsl, torch)
+    H, N, d = p.H, p.N, p.d
+    good = torch.zeros((H, N, d), dtype=torch.bfloat16)
+    cases = [
+        (dict(q=torch.zeros((H, N + 1, d), dtype=torch.bfloat16)), "shape"),
+        (dict(k=torch.zeros((H, N, d), dtype=torch.float32)), "dtype"),
+        (dict(v=torch.zeros((H * N * d,), dtype=torch.bfloat16)), "shape"),
+        (dict(out=torch.zeros((H, N, d), dtype=torch.float32)), "dtype"),
+        (dict(sel_out=torch.zeros((H, N, p.K + 1), dtype=torch.int32)), "shape"),
+        (dict(o_win_out=torch.zeros((H, N, d), dtype=torch.bfloat16)), "dtype"),
+        (dict(o_long_out=torch.zeros((H, N - 1, d), dtype=torch.float32)), "shape"),
+        (dict(q=good.t() if good.dim() == 2 else good.transpose(0, 1)), "shape"),
+        (dict(), "GPU memory"),  # right shapes and dtypes, but host tensors
+    ]
+    for over, msg in cases:
+        args = dict(q=good, k=good, v=good, out=torch.zeros((H, N, d), dtype=torch.bfloat16))
+        args.update(over)
+        with pytest.raises(ValueError, match=msg):
+            fsl.attn_fwd(args["q"], args["k"], args["v"], p, out=args["out"], ws=torch.zeros(16, dtype=torch.uint8),
+                         sel_out=args.get("sel_out"), o_win_out=args.get("o_win_out"),
+                         o_long_out=args.get("o_long_out"))
+
+
+def test_binding_rejects_bad_statistics_and_selection_buffers(fsl):
+    import torch
+    p = _cpu_params(fsl, torch, N=1024)
+    H, N, d = p.H, p.N, p.d
+    C = N // p.s
+    nblk = (N + p.B - 1) // p.B
+    k = torch.zeros((H, N, d), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        fsl.cell_stats(k, p, kbar=torch.zeros((H, C + 1, d)), amax=torch.zeros((H, C)))
+    with pytest.raises(ValueError, match="dtype"):
+        fsl.cell_stats(k, p, kbar=torch.zeros((H, C, d)), amax=torch.zeros((H, C), dtype=torch.float64))
+    with pytest.raises(ValueError, match="shape"):
+        fsl.cell_stats(k[:, :-1], p)
+    kbar, amax = torch.zeros((H, C, d)), torch.zeros((H, C))
+    with pytest.raises(ValueError, match="shape"):
+        fsl.prune_select(k, kbar, amax, p, pool=torch.zeros((H, nblk, p.P + p.W - 1), dtype=torch.int32))
+    with pytest.raises(ValueError, match="dtype"):
+        fsl.prune_select(k, kbar, amax, p, sel=torch.zeros((H, N, p.K), dtype=torch.int64))
+    with pytest.raises(ValueError, match="GPU memory"):
+        fsl.prune_select(k, kbar, amax, p)
+
+
+def test_binding_rejects_small_or_foreign_workspace(fsl):
+    import torch
+    p = _cpu_params(fsl, torch)
+    with pytest.raises(ValueError, match="uint8"):
+        fsl._expect_ws(torch.zeros(16, dtype=torch.int32), 8, torch.device("cpu"))
+    with pytest.raises(ValueError, match="needs"):
+        fsl._expect_ws(torch.zeros(16, dtype=torch.uint8), fsl.workspace_bytes(p), torch.device("cpu"))
