@@ -164,6 +164,20 @@ int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const f
 int fsl_attn_fwd_timed(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
                        void *ws, size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
 
+/* fsl_attn_fwd for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, hosts that forbid allocation calls):
+ * the same arguments and results without ws / ws_bytes. The workspace is a
+ * device array of FSL_NOALLOC_WORKSPACE_MAX bytes held by the library, one
+ * per GPU it runs on, from the first call on that GPU until the process ends;
+ * this call allocates and frees nothing. Returns FSL_E_WORKSPACE, before any
+ * device work, when fsl_workspace_bytes(p) exceeds that size (256 MiB: the
+ * bf16 forward of 16 heads x 16384 tokens x d=64 needs 141 MB). Every call on
+ * one GPU uses that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race and give undefined results. */
+#define FSL_NOALLOC_WORKSPACE_MAX (256u << 20)
+int fsl_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
+                         int32_t *sel_out, float *o_win_out, float *o_long_out, hipStream_t stream);
+
 /* Byte offsets of the named arrays inside a forward workspace (host-only).
  * Returns FSL_OK or the fsl_check_params error. */
 typedef struct fsl_workspace_layout {

@@ -67,6 +67,8 @@ def lib():
         L.fsl_prune_select.argtypes = [vp, vp, vp, vp, vp, pp, vp, sz, vp]
         L.fsl_attn_fwd.restype = i32
         L.fsl_attn_fwd.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, vp, vp, vp]
+        L.fsl_attn_fwd_noalloc.restype = i32
+        L.fsl_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, pp, vp, vp, vp, vp]
         L.fsl_attn_fwd_timed.restype = i32
         L.fsl_attn_fwd_timed.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, vp]
         i64 = ctypes.c_int64
@@ -294,6 +296,21 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, out: 
         if st & FSL_STATUS_F16_RANGE:
             raise ValueError("fsl_attn_fwd: an element of k or v, or a rotated key, lies outside fp16's finite "
                              "range (|x| >= 65504 or not finite); the outputs of this call are undefined")
+    return out
+
+
+NOALLOC_WORKSPACE_MAX = 256 << 20  # FSL_NOALLOC_WORKSPACE_MAX
+
+
+def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, out: torch.Tensor,
+                     sel_out: Optional[torch.Tensor] = None, o_win_out: Optional[torch.Tensor] = None,
+                     o_long_out: Optional[torch.Tensor] = None, stream=None):
+    """fsl_attn_fwd_noalloc: the forward with the library's own workspace array (no allocation, so the
+    caller passes `out`). Overlapping calls on one GPU share that array and race."""
+    _expect(out, "out", _qkv_shape(p), _torch_dtype(p.out_dtype))
+    _check_fwd_operands(q, k, v, out, p, sel_out, o_win_out, o_long_out)
+    _check(lib().fsl_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(p), _ptr(sel_out),
+                                      _ptr(o_win_out), _ptr(o_long_out), _stream(stream)), "fsl_attn_fwd_noalloc")
     return out
 
 

@@ -274,3 +274,17 @@ def test_binding_rejects_small_or_foreign_workspace(fsl):
         fsl._expect_ws(torch.zeros(16, dtype=torch.int32), 8, torch.device("cpu"))
     with pytest.raises(ValueError, match="needs"):
         fsl._expect_ws(torch.zeros(16, dtype=torch.uint8), fsl.workspace_bytes(p), torch.device("cpu"))
+
+
+def test_noalloc_size_and_pointer_checks_on_the_host(fsl):
+    """fsl_attn_fwd_noalloc rejects a workspace beyond its array, and null pointers,
+    before touching the device."""
+    L = fsl.lib()
+    a = ctypes.c_void_p(0x10000)
+    big = params(fsl, N=65536, H=16, d=64)
+    assert fsl.workspace_bytes(big) > fsl.NOALLOC_WORKSPACE_MAX
+    assert L.fsl_attn_fwd_noalloc(a, a, a, a, ctypes.byref(big), None, None, None, None) == -3
+    ok = params(fsl, N=4096, H=2, d=64)
+    assert fsl.workspace_bytes(ok) <= fsl.NOALLOC_WORKSPACE_MAX
+    assert L.fsl_attn_fwd_noalloc(None, a, a, a, ctypes.byref(ok), None, None, None, None) == -1
+    assert L.fsl_attn_fwd_noalloc(a, a, a, a, ctypes.byref(params(fsl, K=0)), None, None, None, None) == -1
