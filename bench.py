@@ -80,9 +80,11 @@ def algorithmic_work(sh, sel_np=None):
         "window": ("mfma", H * 4.0 * d * win_keys),
     }
     if sh.dtype == "bf16":
-        # one fused pass: k and v read once, the cell statistics, the fp16 rotated keys and
-        # the transposed fp16 values written once (the key/value preparation stage is empty)
-        work["cell_stats"] = ("hbm", H * N * d * (2 * e + 2 * 2) + H * C * (d + 1) * 4)
+        # the bf16 statistics are fused into one pass that also reads v and writes the fp16
+        # rotated keys and transposed fp16 values (the key/value preparation stage is empty):
+        # the statistics roofline counts the statistics' own bytes (k read, kbar/amax written),
+        # the fused pass's whole traffic is reported beside it
+        work["_cell_stats_fused_pass"] = H * N * d * (2 * e + 2 * 2) + H * C * (d + 1) * 4
     # q and o_win read, out written, plus the keys and values of every selected cell once
     # per head (keys in the input dtype; values fp16 on the bf16 path, fp32 otherwise)
     readout = H * N * d * (e + 4 + e)
@@ -111,6 +113,10 @@ TRAFFIC = {
                     "source": "long_context_sparse_cell_amd/csrc/readout_flash.hip",
                     "sha256": "db24c4bf584dee7774454ab46329c9d0fe7e22655b98ab2a622791ee6efd826f",
                     "profile": "profiles/fwd_n262144_hbm_traffic.md"},
+    "decode_step": {"bytes": 191697316, "workload": "decode_bf16_64seq_h16_d64_prefix131072",
+                    "source": "long_context_sparse_cell_amd/csrc/decode.hip",
+                    "sha256": "f18958cf685d90b25e9ab85b33099e375a5c0adf61f23c1441ebe0535fa3f4b9",
+                    "profile": "profiles/decode_64seq_hbm_traffic.md"},
 }
 
 
@@ -217,7 +223,7 @@ def decode_bench(fsl, synth, torch, dev, steps_override=None):
                              "note": "fsl_decode_append of every sequence's prefix in chunks, no O(N d) workspace"},
         "roofline": {"bound": "hbm", "achieved": round(step_bytes / step_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes_per_step": step_bytes},
+                     "bytes_per_step": step_bytes, "traffic": measured_traffic("decode_step", sh.name)},
         "data": "synthetic: k/v/q ~ N(0,1) from seeded device generators",
     }
 
@@ -263,6 +269,115 @@ def fs_bench(fsl, synth, torch, inp, q, k, v, dev, steps, warmup):
     }
 
 
+def upload(inp, dev):
+    import torch
+    from long_context_sparse_cell_amd import synth
+
+    def up(x):
+        if inp.shape.dtype == synth.BF16:
+            return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+    return up(inp.q), up(inp.k), up(inp.v)
+
+
+def time_forward(fsl, torch, sh, inp, q, k, v, dev, steps, warmup, with_work=False):
+    """Time `steps` forwards of one workload (after `warmup`), with per-stage HIP events."""
+    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in (inp.sigma, inp.lam, inp.gamma))
+    p = fsl.make_params(sh.N, sh.H, sh.d, q.dtype, sig, lam, gam, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
+    ws = fsl.new_workspace(p, dev)
+    out = torch.empty_like(q)
+    nst = fsl.NUM_STAGES + 1
+    ev = HipEvents(nst * max(steps, warmup, 1))
+    for i in range(warmup):
+        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(0, nst))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(i * nst, nst))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * nst + j, i * nst + j + 1) for i in range(steps)]))
+                for j, name in enumerate(fsl.STAGES)}
+    gpu_ms = float(np.mean([ev.elapsed_ms(i * nst, i * nst + nst - 1) for i in range(steps)]))
+    ev.close()
+    res = {"workload": sh.name, "tokens_per_s": round(sh.N * steps / el, 1), "ms_per_step": round(el * 1e3 / steps, 4),
+           "ns_per_token": round(el * 1e9 / steps / sh.N, 3), "gpu_ms_per_step": round(gpu_ms, 4),
+           "stage_ms": {n: round(t, 4) for n, t in stage_ms.items()}, "elapsed_s": el}
+    if with_work:
+        sel_np = fsl.workspace_views(ws, p)["sel"].cpu().numpy()
+        work = algorithmic_work(sh, sel_np)
+        stages = {}
+        for name, t in stage_ms.items():
+            entry = {"ms": round(t, 4)}
+            if name in work:
+                kind, amount = work[name]
+                if kind == "hbm":
+                    entry.update(bound="hbm", achieved=amount / (t * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+                else:
+                    entry.update(bound="mfma", achieved=amount / (t * 1e-3) / 1e12, peak=MFMA_F16_PEAK_TFLOPS,
+                                 unit="TFLOP/s")
+                entry["frac"] = round(entry["achieved"] / entry["peak"], 4)
+                entry["achieved"] = round(entry["achieved"], 2)
+            stages[name] = entry
+        if "_cell_stats_fused_pass" in work:
+            gbs = work["_cell_stats_fused_pass"] / (stage_ms["cell_stats"] * 1e-3) / 1e9
+            stages["cell_stats"]["fused_pass"] = {
+                "note": "the bf16 statistics pass also reads v and writes the fp16 rotated keys and values",
+                "bytes": work["_cell_stats_fused_pass"], "achieved": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        dominant = max((n for n in stages if "bound" in stages[n]), key=lambda n: stage_ms[n])
+        dom = stages[dominant]
+        res["stages"] = stages
+        res["work"] = work
+        res["roofline"] = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                           "unit": dom["unit"], "frac": dom["frac"], "traffic": measured_traffic(dominant, sh.name)}
+    del ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def other_workloads(fsl, synth, torch, dev, steps, warmup, skip):
+    """The other forward workloads (4k fp32, 16k and 64k bf16), each timed on its own seeded inputs."""
+    res = {}
+    for name in ("fwd_f32_n4096", "fwd_bf16_n16384", "fwd_bf16_n65536"):
+        if name == skip:
+            continue
+        sh = synth.CONFIGS[name]
+        log(f"[bench] workload {sh.name}")
+        inp = synth.make_inputs(sh)
+        q, k, v = upload(inp, dev)
+        r = time_forward(fsl, torch, sh, inp, q, k, v, dev, steps, warmup)
+        r.pop("elapsed_s")
+        res[sh.name] = r
+        del q, k, v, inp
+    torch.cuda.empty_cache()
+    return res
+
+
+def linearity_check(fsl, synth, torch, dev, steps, warmup):
+    """The pages' O(N) cost claim: the 16-head, d=64 bf16 shape at N = 16384, 65536 and 262144
+    (q, k, v ~ N(0,1) drawn on the device), time per token at each N; flat within ~20% is linear."""
+    H, d = 16, 64
+    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in synth.head_scalars(H))
+    gen = torch.Generator(device=dev)
+    pts = []
+    for N in (16384, 65536, 262144):
+        gen.manual_seed(7000 + N)
+        q, k, v = (torch.randn((H, N, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(3))
+        sh = synth.Shape(f"linear_bf16_h{H}_n{N}_d{d}", H=H, N=N, d=d, dtype=synth.BF16, seed=0)
+        inp = synth.Inputs(sh, None, None, None, *synth.head_scalars(H))
+        r = time_forward(fsl, torch, sh, inp, q, k, v, dev, steps, warmup)
+        log(f"[bench] O(N) check N={N}: {r['ns_per_token']:.3f} ns/token")
+        pts.append({"N": N, "ms_per_step": r["ms_per_step"], "ns_per_token": r["ns_per_token"],
+                    "stage_ms": r["stage_ms"]})
+        del q, k, v
+    torch.cuda.empty_cache()
+    per = [x["ns_per_token"] for x in pts]
+    return {"shape": f"H={H}, d={d}, bf16, q/k/v ~ N(0,1), pruned FS-L", "points": pts,
+            "max_over_min_ns_per_token": round(max(per) / min(per), 3),
+            "claim": "FS-L attention cost O(N) (FreeSolo digest, motivation; ai.info summary, Key Contributions)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +388,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=131072)
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     ap.add_argument("--no-fs", action="store_true", help="skip the unpruned (P = -1) forward measurement")
+    ap.add_argument("--no-others", action="store_true", help="skip the 4k/16k/64k workloads and the O(N) check")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, the reference kernel for scaling "
                          "profiler byte counters (FETCH_SIZE / WRITE_SIZE)")
@@ -301,72 +417,25 @@ def main():
     log(f"[bench] generating {sh.name}")
     inp = synth.make_inputs(sh)
     dev = torch.device("cuda:0")
-
-    def up(x):
-        if sh.dtype == synth.BF16:
-            return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(x).to(dev)
-
-    q, k, v = up(inp.q), up(inp.k), up(inp.v)
-    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in (inp.sigma, inp.lam, inp.gamma))
-    p = fsl.make_params(sh.N, sh.H, sh.d, q.dtype, sig, lam, gam, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
-    ws = fsl.new_workspace(p, dev)
-    out = torch.empty_like(q)
-    nst = fsl.NUM_STAGES + 1
-    ev = HipEvents(nst * max(args.steps, args.warmup, 1))
-
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(0, nst))
-    torch.cuda.synchronize()
-
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        fsl.attn_fwd_timed(q, k, v, p, out, ws, ev.sub(i * nst, nst))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * nst + j, i * nst + j + 1) for i in range(args.steps)]))
-                for j, name in enumerate(fsl.STAGES)}
-    gpu_ms = float(np.mean([ev.elapsed_ms(i * nst, i * nst + nst - 1) for i in range(args.steps)]))
-    log("[bench] stage ms: " + ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
-
-    sel_np = fsl.workspace_views(ws, p)["sel"].cpu().numpy()
-    work = algorithmic_work(sh, sel_np)
-    stages = {}
-    for name, t in stage_ms.items():
-        entry = {"ms": round(t, 4)}
-        if name in work:
-            kind, amount = work[name]
-            if kind == "hbm":
-                entry.update(bound="hbm", achieved=amount / (t * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
-            else:
-                entry.update(bound="mfma", achieved=amount / (t * 1e-3) / 1e12, peak=MFMA_F16_PEAK_TFLOPS,
-                             unit="TFLOP/s")
-            entry["frac"] = entry["achieved"] / entry["peak"]
-            entry["achieved"] = round(entry["achieved"], 2)
-            entry["frac"] = round(entry["frac"], 4)
-        stages[name] = entry
-    dominant = max((n for n in stages if "bound" in stages[n]), key=lambda n: stage_ms[n])
-    dom = stages[dominant]
-    roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
-                "unit": dom["unit"], "frac": dom["frac"], "traffic": measured_traffic(dominant, sh.name)}
+    q, k, v = upload(inp, dev)
+    head = time_forward(fsl, torch, sh, inp, q, k, v, dev, args.steps, args.warmup, with_work=True)
+    stages, roofline, work = head["stages"], head["roofline"], head["work"]
+    t0, t1 = 0.0, head["elapsed_s"]
+    others = lin = None
+    if not args.no_others:
+        others = other_workloads(fsl, synth, torch, dev, args.steps, args.warmup, args.workload)
+        lin = linearity_check(fsl, synth, torch, dev, args.steps, args.warmup)
 
     fs = None
     if not args.no_fs and sh.dtype == synth.BF16:
         log("[bench] unpruned (P = -1) forward")
-        del ws
         torch.cuda.empty_cache()
         fs = fs_bench(fsl, synth, torch, inp, q, k, v, dev, args.steps, args.warmup)
-        ws = None
         log(f"[bench] unpruned forward {fs['ms_per_step']:.3f} ms/step, stages {fs['stages']}")
 
     dec = None
     if not args.no_decode:
         log("[bench] streaming decode workload")
-        ws = None
         torch.cuda.empty_cache()
         dec = decode_bench(fsl, synth, torch, dev)
         log(f"[bench] decode {dec['tokens_per_s']:.0f} tokens/s, {dec['ms_per_step']:.3f} ms/step")
@@ -375,7 +444,6 @@ def main():
     if not args.no_cpu:
         log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows")
         cpu = cpu_baseline(inp, min(args.cpu_rows, sh.N))
-    ev.close()
 
     tokens = sh.N
     line = {
@@ -385,7 +453,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -396,9 +464,12 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
-        "gpu_ms_per_step": round(gpu_ms, 4),
+        "gpu_ms_per_step": head["gpu_ms_per_step"],
+        "ns_per_token": head["ns_per_token"],
         "union_cells_per_block": round(work.get("_union_cells_per_block", 0.0), 2),
         "distinct_selected_cells": work.get("_distinct_cells"),
+        "other_workloads": others,
+        "linearity": lin,
         "decode": dec,
         "noprune": fs,
     }
