@@ -387,3 +387,175 @@ int orc_forward_head(const float *q, const float *k, const float *v, const orc_h
     free(kbar); free(amax);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of one head, for training ([D] method steps, training paragraph:
+ * the hard top-P / top-K indices receive no gradient; [S] "Methodology in
+ * Plain English", training paragraph: the routing scalars sigma_h, lambda_h
+ * stay fixed while the per-head mixing weight is learned).
+ *
+ * With the forward's selection sel [N][K] (ascending, -1 padded) held fixed,
+ * out is a differentiable function of q, k, v and gamma. Given
+ * dout = dL/dout [N][d] this accumulates dq, dk, dv [N][d] (zeroed here) and
+ * returns dgamma in *dgamma. Per query i, for each branch with output o and
+ * upstream gradient dO, and D = dO . o:
+ *   P_j = softmax_j(l_j), dS_j = P_j (dO . v_j - D), dv_j += P_j dO,
+ *   and the gradient of l_j = scale a . b_j goes to a (scale dS_j b_j) and to
+ *   b_j (scale dS_j a).
+ * Window: a = R(i) q_i, b_j = R(j) k_j, dO = dout_i; the rotated gradients are
+ * turned back with R(t)^T = R(-t). Long branch: a = q_i, b_j = k_j over the
+ * tokens of the selected cells; with r = sqrt(mean(o^2) + eps) and y = o / r,
+ * dgamma += dout_i . y, dy = gamma dout_i and dO = (dy - y (dy . y) / d) / r
+ * (RMSNorm's backward). An empty selection contributes nothing. fp64
+ * throughout, queries in order. Returns 0, or -1 for bad parameters. */
+
+/* R(t)^T x = R(-t) x for the rotate-half pairing, angle t * base^(-2m/d) */
+static void orc_rope_back(const double *x, int64_t t, const orc_head *p, double *out)
+{
+    const int half = p->d / 2;
+    for (int m = 0; m < half; ++m) {
+        double theta = pow(p->rope_base, -2.0 * (double)m / (double)p->d);
+        double ang = (double)t * theta;
+        double cs = cos(ang), sn = sin(ang);
+        double a = x[m], b = x[m + half];
+        out[m] = a * cs + b * sn;
+        out[m + half] = b * cs - a * sn;
+    }
+}
+
+/* softmax backward over n keys for one query: a [d] the query-side operand,
+ * brow(t) / vrow(t) the key-side operand and value of key t; accumulates
+ * da [d], db_t and dv_t (through the callbacks' destinations) */
+typedef struct {
+    const double *b;  /* key-side operands, rows of d (or NULL: use bf) */
+    const float *bf;
+    const float *v;
+    const int64_t *idx; /* key t -> row index */
+    double *db;        /* gradient rows of the key-side operand */
+    double *dv;        /* gradient rows of v */
+} orc_keys;
+
+static void orc_softmax_back(const double *a, const orc_keys *K, int64_t n, const double *dO,
+                             const orc_head *p, double *da, double *o_out)
+{
+    const int d = p->d;
+    double *l = (double *)malloc(sizeof(double) * (size_t)n);
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t j = K->idx[t];
+        double dot = 0.0;
+        for (int x = 0; x < d; ++x) dot += a[x] * (K->b ? K->b[j * d + x] : (double)K->bf[j * d + x]);
+        l[t] = p->scale * dot;
+        if (l[t] > mx) mx = l[t];
+    }
+    double sum = 0.0;
+    for (int64_t t = 0; t < n; ++t) { l[t] = exp(l[t] - mx); sum += l[t]; }
+    for (int64_t t = 0; t < n; ++t) l[t] /= sum; /* P_t */
+    double *o = (double *)calloc((size_t)d, sizeof(double));
+    for (int64_t t = 0; t < n; ++t) {
+        const float *vr = K->v + K->idx[t] * d;
+        for (int x = 0; x < d; ++x) o[x] += l[t] * (double)vr[x];
+    }
+    if (o_out) memcpy(o_out, o, sizeof(double) * d);
+    double D = 0.0;
+    for (int x = 0; x < d; ++x) D += dO[x] * o[x];
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t j = K->idx[t];
+        const float *vr = K->v + j * d;
+        double dP = 0.0;
+        for (int x = 0; x < d; ++x) dP += dO[x] * (double)vr[x];
+        const double dS = l[t] * (dP - D);
+        for (int x = 0; x < d; ++x) {
+            const double bx = K->b ? K->b[j * d + x] : (double)K->bf[j * d + x];
+            da[x] += p->scale * dS * bx;
+            K->db[j * d + x] += p->scale * dS * a[x];
+            K->dv[j * d + x] += l[t] * dO[x];
+        }
+    }
+    free(o);
+    free(l);
+}
+
+int orc_backward_head(const float *q, const float *k, const float *v, const float *dout,
+                      const int32_t *sel, const orc_head *p, double *dq, double *dk,
+                      double *dv, double *dgamma)
+{
+    const int d = p->d, s = p->s;
+    const int64_t N = p->N;
+    if (d <= 0 || (d & 1) || s <= 0 || p->w <= 0 || p->K <= 0 || N <= 0) return -1;
+    memset(dq, 0, sizeof(double) * (size_t)N * d);
+    memset(dk, 0, sizeof(double) * (size_t)N * d);
+    memset(dv, 0, sizeof(double) * (size_t)N * d);
+    double *krot = (double *)malloc(sizeof(double) * (size_t)N * d);
+    double *dkrot = (double *)calloc((size_t)N * d, sizeof(double));
+    for (int64_t j = 0; j < N; ++j) orc_rope(k + j * d, j, p, krot + j * d);
+    double *qrot = (double *)malloc(sizeof(double) * d);
+    double *dqrot = (double *)malloc(sizeof(double) * d);
+    double *back = (double *)malloc(sizeof(double) * d);
+    double *dO = (double *)malloc(sizeof(double) * d);
+    double *o = (double *)malloc(sizeof(double) * d);
+    double *qd = (double *)malloc(sizeof(double) * d);
+    int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)(p->w > (int64_t)p->K * s ? p->w : (int64_t)p->K * s));
+    double dg = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+        /* local branch */
+        int64_t j0 = i - p->w + 1;
+        if (j0 < 0) j0 = 0;
+        const int64_t nw = i - j0 + 1;
+        for (int64_t t = 0; t < nw; ++t) idx[t] = j0 + t;
+        orc_rope(q + i * d, i, p, qrot);
+        for (int x = 0; x < d; ++x) { dqrot[x] = 0.0; dO[x] = (double)dout[i * d + x]; }
+        orc_keys kw = {krot, NULL, v, idx, dkrot, dv};
+        orc_softmax_back(qrot, &kw, nw, dO, p, dqrot, NULL);
+        orc_rope_back(dqrot, i, p, back);
+        for (int x = 0; x < d; ++x) dq[i * d + x] += back[x];
+        /* long branch over the selected cells' tokens */
+        int64_t nl = 0;
+        for (int u = 0; u < p->K; ++u) {
+            const int32_t c = sel[i * p->K + u];
+            if (c < 0) continue;
+            for (int j = 0; j < s; ++j) idx[nl++] = (int64_t)c * s + j;
+        }
+        if (nl == 0) continue;
+        /* forward of the branch for y, then RMSNorm's backward for dO */
+        {
+            double *l = (double *)malloc(sizeof(double) * (size_t)nl);
+            double mx = -INFINITY, sum = 0.0;
+            for (int64_t t = 0; t < nl; ++t) {
+                double dot = 0.0;
+                for (int x = 0; x < d; ++x) dot += (double)q[i * d + x] * (double)k[idx[t] * d + x];
+                l[t] = p->scale * dot;
+                if (l[t] > mx) mx = l[t];
+            }
+            for (int64_t t = 0; t < nl; ++t) { l[t] = exp(l[t] - mx); sum += l[t]; }
+            for (int x = 0; x < d; ++x) o[x] = 0.0;
+            for (int64_t t = 0; t < nl; ++t)
+                for (int x = 0; x < d; ++x) o[x] += (l[t] / sum) * (double)v[idx[t] * d + x];
+            free(l);
+        }
+        double ms = 0.0;
+        for (int x = 0; x < d; ++x) ms += o[x] * o[x];
+        const double r = sqrt(ms / (double)d + p->rms_eps);
+        double dyy = 0.0;
+        for (int x = 0; x < d; ++x) {
+            const double y = o[x] / r;
+            dg += (double)dout[i * d + x] * y;
+            dyy += p->gamma * (double)dout[i * d + x] * y;
+        }
+        for (int x = 0; x < d; ++x) {
+            const double y = o[x] / r;
+            dO[x] = (p->gamma * (double)dout[i * d + x] - y * dyy / (double)d) / r;
+        }
+        for (int x = 0; x < d; ++x) { qd[x] = (double)q[i * d + x]; dqrot[x] = 0.0; }
+        orc_keys kl = {NULL, k, v, idx, dk, dv};
+        orc_softmax_back(qd, &kl, nl, dO, p, dqrot, NULL);
+        for (int x = 0; x < d; ++x) dq[i * d + x] += dqrot[x];
+    }
+    for (int64_t j = 0; j < N; ++j) {
+        orc_rope_back(dkrot + j * d, j, p, back);
+        for (int x = 0; x < d; ++x) dk[j * d + x] += back[x];
+    }
+    *dgamma = dg;
+    free(krot); free(dkrot); free(qrot); free(dqrot); free(back); free(dO); free(o); free(qd); free(idx);
+    return 0;
+}

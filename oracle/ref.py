@@ -71,6 +71,8 @@ def lib():
         L.orc_window.restype = None; L.orc_window.argtypes = [f64p, f64p, f32p, ctypes.c_int64, hp, f64p]
         L.orc_readout.restype = None; L.orc_readout.argtypes = [f32p, f32p, f32p, i32p, ctypes.c_int32, hp, f64p]
         L.orc_mix.restype = None; L.orc_mix.argtypes = [f64p, f64p, hp, f64p]
+        L.orc_backward_head.restype = ctypes.c_int
+        L.orc_backward_head.argtypes = [f32p, f32p, f32p, f32p, i32p, hp, f64p, f64p, f64p, f64p]
         L.orc_forward_head.restype = ctypes.c_int
         L.orc_forward_head.argtypes = [f32p, f32p, f32p, hp, i64p, ctypes.c_int64, f64p, f64p, f64p,
                                        i32p, f64p, i32p, ctypes.c_int32, f32p, f32p, ctypes.c_int]
@@ -237,3 +239,43 @@ def forward(inputs, rows: Optional[Sequence[int]] = None, heads: Optional[Sequen
         res.append(forward_head(inputs.q[h], inputs.k[h], inputs.v[h], p, rows, want_pool,
                                 want_stats, nthreads))
     return res
+
+
+# ---------------------------------------------------------------------------
+# backward (training): gradients with the forward's selection held fixed
+
+def backward_head(q, k, v, dout, sel, p: Head):
+    """dq, dk, dv ([N][d] fp64) and dgamma of one head, for upstream gradient dout [N][d] and the
+    forward's selection sel [N][K] (held fixed: the hard indices receive no gradient)."""
+    q = _f32(q); k = _f32(k); v = _f32(v); dout = _f32(dout)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    N, d = p.N, p.d
+    assert q.shape == (N, d) and k.shape == (N, d) and v.shape == (N, d) and dout.shape == (N, d)
+    assert sel.shape == (N, p.K)
+    dq = np.zeros((N, d), np.float64); dk = np.zeros((N, d), np.float64); dv = np.zeros((N, d), np.float64)
+    dg = np.zeros(1, np.float64)
+    rc = lib().orc_backward_head(_p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
+                                 _p(dout, ctypes.c_float), _p(sel, ctypes.c_int32), ctypes.byref(p),
+                                 _p(dq, ctypes.c_double), _p(dk, ctypes.c_double), _p(dv, ctypes.c_double),
+                                 _p(dg, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the parameters (code {rc})")
+    return dict(dq=dq, dk=dk, dv=dv, dgamma=float(dg[0]))
+
+
+def backward(inputs, dout, sels, heads=None, workers: int = 0, **overrides):
+    """Backward of a synth.Inputs workload: one result per head, heads run in parallel threads
+    (the oracle call releases the GIL); sels[h] is head h's forward selection [N][K]."""
+    from concurrent.futures import ThreadPoolExecutor
+    shape = inputs.shape
+    heads = list(range(shape.H)) if heads is None else list(heads)
+
+    def one(h):
+        p = head_from_shape(shape, h, inputs.sigma, inputs.lam, inputs.gamma)
+        for key, val in overrides.items():
+            setattr(p, key, val)
+        return backward_head(inputs.q[h], inputs.k[h], inputs.v[h], dout[h], sels[h], p)
+
+    n = workers or min(len(heads), len(os.sched_getaffinity(0)), 16)
+    with ThreadPoolExecutor(max_workers=max(1, n)) as ex:
+        return list(ex.map(one, heads))

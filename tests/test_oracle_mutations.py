@@ -2,7 +2,8 @@
 
 Every mutation below edits one line of fsl_oracle.c (a dropped term, a wrong
 sign, an off-by-one, a transposed index), builds the copy into a temporary
-directory, and runs the pin module against it in a subprocess. The real oracle
+directory, and runs the pin modules (forward and backward) against it in a
+subprocess. The real oracle
 is never touched.
 """
 import os
@@ -36,7 +37,16 @@ MUTATIONS = {
                            "((int64_t)sel[u] * s + j + 1) * d;\n            double dot"),
     "mix_mean": ("ms /= (double)d;", "ms /= (double)(d - 1);"),
     "mix_gamma": ("out[x] = o_win[x] + p->gamma * (o_long[x] / den);", "out[x] = o_win[x] + (o_long[x] / den);"),
+    # the backward
+    "bwd_rotate_back": ("out[m + half] = b * cs - a * sn;", "out[m + half] = b * cs + a * sn;"),
+    "bwd_softmax_D": ("const double dS = l[t] * (dP - D);", "const double dS = l[t] * dP;"),
+    "bwd_rmsnorm_projection": ("dO[x] = (p->gamma * (double)dout[i * d + x] - y * dyy / (double)d) / r;",
+                               "dO[x] = (p->gamma * (double)dout[i * d + x]) / r;"),
+    "bwd_dgamma": ("dg += (double)dout[i * d + x] * y;", "dg += (double)dout[i * d + x] * o[x];"),
+    "bwd_scale": ("da[x] += p->scale * dS * bx;", "da[x] += dS * bx;"),
+    "bwd_dv_weight": ("K->dv[j * d + x] += l[t] * dO[x];", "K->dv[j * d + x] += dO[x];"),
 }
+PIN_MODULES = ("test_oracle_pins.py", "test_oracle_backward_pins.py")
 
 
 @pytest.mark.slow
@@ -51,7 +61,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
                     "-o", str(lib), str(mut), "-lm"], check=True)
     env = dict(os.environ, FSL_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                       [os.path.join(ROOT, "tests", m) for m in PIN_MODULES],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"no pin failed for mutation {name}:\n{r.stdout[-2000:]}"
