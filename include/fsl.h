@@ -164,6 +164,27 @@ int fsl_attn_fwd(const void *q, const void *k, const void *v, void *out, const f
 int fsl_attn_fwd_timed(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
                        void *ws, size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream);
 
+/* Backward of the forward, for training (digest, method steps: the hard
+ * top-P / top-K indices receive no gradient; ai.info summary, training
+ * paragraph: sigma_h and lambda_h stay fixed, the mixing weight gamma_h is
+ * learned). With the forward's selections held fixed, out is differentiable
+ * in q, k, v and gamma; given dout = dL/dout this computes
+ *   dq, dk, dv: device [H][N][d] float (written, not accumulated),
+ *   dgamma:     device [H] float,
+ * through both attention branches (window: RoPE'd softmax backward, gradients
+ * turned back through R(t)^T; long branch: RMSNorm's backward, then the softmax
+ * backward over the selected cells' tokens). q, k, v: the forward's inputs;
+ * dout: device [H][N][d] in out_dtype. fwd_ws: the workspace of a completed
+ * fsl_attn_fwd call on the same q, k, v and p (its selections and pools are
+ * read, nothing is written). ws: device workspace of at
+ * least fsl_attn_bwd_workspace_bytes(p) bytes. Arithmetic is fp32; the sums
+ * run in a fixed order (no atomics), so results are reproducible. Errors as
+ * fsl_attn_fwd (FSL_E_WORKSPACE if either workspace is too small). */
+size_t fsl_attn_bwd_workspace_bytes(const fsl_params *p);
+int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, const fsl_params *p,
+                 const void *fwd_ws, size_t fwd_ws_bytes, void *ws, size_t ws_bytes, float *dq, float *dk,
+                 float *dv, float *dgamma, hipStream_t stream);
+
 /* fsl_attn_fwd for callers that cannot allocate device memory (code under
  * stream capture, tight serving loops, hosts that forbid allocation calls):
  * the same arguments and results without ws / ws_bytes. The workspace is a
@@ -202,9 +223,10 @@ typedef struct fsl_workspace_layout {
 int fsl_workspace_views(const fsl_params *p, fsl_workspace_layout *out);
 
 /* Bits of the workspace's status word after a forward (0 for fp32 inputs).
- * FSL_STATUS_F16_RANGE: with bf16 inputs, an element of k or v, or a
- * RoPE-rotated key, was not finite or had magnitude >= 65504, outside fp16's
- * finite range. Both attention branches multiply fp16 operands, so the
+ * FSL_STATUS_F16_RANGE: with bf16 inputs, an element of k or v was not
+ * finite or had magnitude >= 65504, past fp16's largest finite value (the
+ * first such bf16 value is 65536), or a RoPE-rotated key rounded to an fp16
+ * infinity. Both attention branches multiply fp16 operands, so the
  * outputs of such a call are undefined (typically inf or NaN); selections
  * and cell statistics do not depend on it. Reading the word is optional
  * (it costs a device-to-host copy after the call completes). */

@@ -148,6 +148,33 @@ size_t decode_bytes(const fsl_params *p, int32_t n_seq) {
     return (size_t)L.off_rec + (size_t)n_seq * p->H * (size_t)L.rec_bytes;
 }
 
+// backward workspace: the rotated q and k, the upstream gradient, the long branch's
+// softmax-output gradient, five row statistics and the cells' block ranges
+struct BwdLayout {
+    size_t rope, qr, kr, dO, do_l, lse_w, D_w, lse_l, D_l, dg, crange, status, total;
+};
+
+BwdLayout bwd_layout(const KParams &k) {
+    BwdLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+    const size_t rows = (size_t)k.H * k.N, elems = rows * k.d;
+    L.rope = take((size_t)(rope_abs_rows_hi(k) + kRopeSpan) * (k.d / 2) * sizeof(float2));
+    L.qr = take(elems * sizeof(float));
+    L.kr = take(elems * sizeof(float));
+    L.dO = take(elems * sizeof(float));
+    L.do_l = take(elems * sizeof(float));
+    L.lse_w = take(rows * sizeof(float));
+    L.D_w = take(rows * sizeof(float));
+    L.lse_l = take(rows * sizeof(float));
+    L.D_l = take(rows * sizeof(float));
+    L.dg = take(rows * sizeof(float));
+    L.crange = take((size_t)k.H * k.C * 2 * sizeof(int32_t));
+    L.status = take(sizeof(uint32_t));
+    L.total = off;
+    return L;
+}
+
 int32_t decode_capacity(const fsl_params *p, size_t state_bytes) {
     const DecodeLayout L = dlayout(p);
     if (state_bytes < (size_t)L.off_rec) return 0;
@@ -282,6 +309,42 @@ int fsl_attn_fwd_timed(const void *q, const void *k, const void *v, void *out, c
                        size_t ws_bytes, hipEvent_t *stage_events, hipStream_t stream) {
     if (!stage_events) return check(p) != FSL_OK ? check(p) : FSL_E_INVAL;
     return attn_fwd_impl(q, k, v, out, p, ws, ws_bytes, nullptr, nullptr, nullptr, stage_events, stream);
+}
+
+size_t fsl_attn_bwd_workspace_bytes(const fsl_params *p) {
+    if (check(p) != FSL_OK) return 0;
+    return bwd_layout(kparams(p)).total;
+}
+
+int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, const fsl_params *p,
+                 const void *fwd_ws, size_t fwd_ws_bytes, void *ws, size_t ws_bytes, float *dq, float *dk,
+                 float *dv, float *dgamma, hipStream_t stream) {
+    int rc = check(p);
+    if (rc != FSL_OK) return rc;
+    if (!q || !k || !v || !dout || !fwd_ws || !ws || !dq || !dk || !dv || !dgamma) return FSL_E_INVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(fwd_ws) ||
+        !aligned16(ws) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(dgamma))
+        return FSL_E_INVAL;
+    const KParams kp = kparams(p);
+    const fsl_workspace_layout FL = layout(kp);
+    const BwdLayout BL = bwd_layout(kp);
+    if (fwd_ws_bytes < FL.total || ws_bytes < BL.total) return FSL_E_WORKSPACE;
+    const char *f = (const char *)fwd_ws;
+    char *b = (char *)ws;
+    BwdWork w;
+    w.rope = (float2 *)(b + BL.rope);
+    w.qr = (float *)(b + BL.qr);
+    w.kr = (float *)(b + BL.kr);
+    w.dO = (float *)(b + BL.dO);
+    w.do_l = (float *)(b + BL.do_l);
+    w.lse_w = (float *)(b + BL.lse_w);
+    w.D_w = (float *)(b + BL.D_w);
+    w.lse_l = (float *)(b + BL.lse_l);
+    w.D_l = (float *)(b + BL.D_l);
+    w.dg = (float *)(b + BL.dg);
+    w.crange = (int32_t *)(b + BL.crange);
+    w.status = (uint32_t *)(b + BL.status);
+    return hip_status(launch_attn_bwd(q, k, v, dout, (const int32_t *)(f + FL.sel), (const int32_t *)(f + FL.pool), w, dq, dk, dv, dgamma, kp, stream));
 }
 
 size_t fsl_decode_state_bytes(const fsl_params *p, int32_t n_seq) {

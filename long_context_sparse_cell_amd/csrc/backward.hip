@@ -1,0 +1,623 @@
+// Backward of the FS-L forward, for training (FreeSolo digest, method steps:
+// the two branches are trained while the hard top-P / top-K indices receive no
+// gradient; ai.info summary, training paragraph: the routing scalars sigma_h,
+// lambda_h stay fixed and the per-head mixing weight is learned).
+//
+// With the forward's selections held fixed, out = o_win + gamma * RMSNorm(o_long)
+// is differentiable in q, k, v and gamma. For a branch with output o and
+// upstream gradient dO, and D = dO . o, the softmax backward over its keys is
+//   P_j = exp(l_j - lse), dS_j = P_j (dO . v_j - D), dv_j += P_j dO,
+//   and l_j = scale a . b_j sends scale dS_j b_j to a and scale dS_j a to b_j.
+// Window: a = R(i) q_i, b_j = R(j) k_j, dO = dout_i; the rotated gradients go
+// back through R(t)^T. Long branch: a = q_i, b_j = k_j over the selected
+// cells' tokens, dO = RMSNorm's backward of gamma dout_i.
+//
+// Kernels, in launch order on the caller's stream (every one writes its own
+// outputs; nothing is accumulated with atomics, so results are reproducible):
+//   bwd_prep        fp32 rotated q, k and the upstream gradient
+//   bwd_win_dq      per 32 queries: a pass for the row's log-sum-exp and D, then dS
+//                   and dq (window part)
+//   bwd_win_dkv     per 32 keys: dk, dv of the window over the queries that see them
+//   bwd_long_q      per query (one wave): o_long, RMSNorm's backward, dq += long part
+//   bwd_cell_range  first / last block whose pool holds each cell (pruned variant)
+//   bwd_long_kv     per cell: dk, dv += long part over every query that selected it
+//   bwd_dgamma      per head: dgamma summed in a fixed order
+// Arithmetic is fp32 on the vector ALUs with the operand tiles staged in LDS.
+#include <climits>
+
+#include "fsl_internal.h"
+
+namespace fsl {
+
+namespace {
+
+constexpr int kBT = 32;        // queries (or keys) per work-group tile
+constexpr int kThreads = 256;  // 8 threads per tile row
+
+template <typename T>
+__device__ __forceinline__ float ld(const T *p, int64_t i) { return to_f32<T>(p[i]); }
+
+// (cos, sin) of angle pos * theta_m from the two-level table
+__device__ __forceinline__ float2 rope_cs(const float2 *tab, int nhi, int half, int64_t pos, int m) {
+    const float2 th = tab[(pos / kRopeSpan) * half + m];
+    const float2 tl = tab[(int64_t)(nhi + (int)(pos % kRopeSpan)) * half + m];
+    return make_float2(th.x * tl.x - th.y * tl.y, th.y * tl.x + th.x * tl.y);
+}
+
+// sum over the aligned group of G lanes (G a power of two, at most 64)
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+}  // namespace
+
+// ---- fp32 rotated q and k (R(t) x, rotate-half pairs) and the upstream gradient
+template <typename T, typename TO, int D>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                            const TO *__restrict__ dout, const float2 *__restrict__ tab,
+                                                            int nhi, float *__restrict__ qr, float *__restrict__ kr,
+                                                            float *__restrict__ dO, KParams p) {
+    constexpr int HALF = D / 2;
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // one rotation pair
+    const int64_t total = (int64_t)p.H * p.N * HALF;
+    if (e >= total) return;
+    const int64_t row = e / HALF;  // h * N + t
+    const int m = (int)(e % HALF);
+    const int64_t t = row % p.N;
+    const float2 cs = rope_cs(tab, nhi, HALF, t, m);
+    const int64_t a = row * D + m, b = a + HALF;
+    const float qa = ld(q, a), qb = ld(q, b), ka = ld(k, a), kb = ld(k, b);
+    qr[a] = qa * cs.x - qb * cs.y;
+    qr[b] = qb * cs.x + qa * cs.y;
+    kr[a] = ka * cs.x - kb * cs.y;
+    kr[b] = kb * cs.x + ka * cs.y;
+    dO[a] = ld(dout, a);
+    dO[b] = ld(dout, b);
+}
+
+// ---- window, query side. Work-group: 32 queries of one head. Thread t takes row
+// t / 8 and, in score phases, keys 4 (t % 8) .. +3 of the current 32-key tile; in
+// accumulation phases, dims (t % 8) + 8 k of its row.
+// D = dO . o_win is formed as sum_j P_j (dO . v_j), from this pass's own fp32
+// arithmetic: the forward's window output holds fp16-operand rounding that would
+// otherwise enter every dS.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_win_dq_kernel(const float *__restrict__ qr, const float *__restrict__ kr,
+                                                              const T *__restrict__ v, const float *__restrict__ dO,
+                                                              const float2 *__restrict__ tab, int nhi,
+                                                              float *__restrict__ dq, float *__restrict__ lse_w,
+                                                              float *__restrict__ D_w, KParams p) {
+    constexpr int LD = D + 1, HALF = D / 2, NK = D / 8;
+    __shared__ float s_q[kBT * LD], s_do[kBT * LD], s_k[kBT * LD], s_v[kBT * LD];
+    __shared__ float s_ds[kBT][kBT + 1];
+    const int ntile = (int)((p.N + kBT - 1) / kBT);
+    const int h = blockIdx.x / ntile;
+    const int64_t q0 = (int64_t)(blockIdx.x % ntile) * kBT;
+    const int64_t hN = (int64_t)h * p.N;
+    const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7, c4 = 4 * sub;
+    const int64_t i = q0 + r;
+    for (int e = tid; e < kBT * D; e += kThreads) {
+        const int rr = e / D, x = e % D;
+        const int64_t ii = q0 + rr;
+        s_q[rr * LD + x] = ii < p.N ? qr[(hN + ii) * D + x] : 0.0f;
+        s_do[rr * LD + x] = ii < p.N ? dO[(hN + ii) * D + x] : 0.0f;
+    }
+    const int64_t kmin = max((int64_t)0, q0 - p.w + 1);
+    const int64_t kmax = min(p.N, q0 + kBT) - 1;
+    const int64_t t0 = kmin / kBT * kBT;
+    auto load_tile = [&](float *dst, const float *src, int64_t ks0) {
+        for (int e = tid; e < kBT * D; e += kThreads) {
+            const int rr = e / D, x = e % D;
+            const int64_t j = ks0 + rr;
+            dst[rr * LD + x] = j < p.N ? src[(hN + j) * D + x] : 0.0f;
+        }
+    };
+    auto valid = [&](int64_t j) { return i < p.N && j <= i && j > i - p.w; };
+    auto load_v = [&](int64_t ks0) {
+        for (int e = tid; e < kBT * D; e += kThreads) {
+            const int rr = e / D, x = e % D;
+            const int64_t j = ks0 + rr;
+            s_v[rr * LD + x] = j < p.N ? ld(v, (hN + j) * D + x) : 0.0f;
+        }
+    };
+    // pass A: the row's log-sum-exp, and a = sum_j exp(l_j - m) (dO . v_j) with the
+    // same running maximum, so that D = a / sum_j exp(l_j - m)
+    float m = -INFINITY, l = 0.0f, a = 0.0f;
+    for (int64_t ks0 = t0; ks0 <= kmax; ks0 += kBT) {
+        __syncthreads();
+        load_tile(s_k, kr, ks0);
+        load_v(ks0);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = ks0 + c4 + u;
+            if (!valid(j)) continue;
+            float dot = 0.0f, dp = 0.0f;
+            for (int x = 0; x < D; ++x) {
+                dot += s_q[r * LD + x] * s_k[(c4 + u) * LD + x];
+                dp += s_do[r * LD + x] * s_v[(c4 + u) * LD + x];
+            }
+            const float sc = dot * p.scale;
+            const float mn = fmaxf(m, sc);
+            const float alpha = __expf(m - mn), e = __expf(sc - mn);
+            l = l * alpha + e;
+            a = a * alpha + e * dp;
+            m = mn;
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+        const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o), a2 = __shfl_xor(a, o);
+        const float mn = fmaxf(m, m2);
+        const float f1 = m == -INFINITY ? 0.0f : __expf(m - mn);
+        const float f2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mn);
+        l = l * f1 + l2 * f2;
+        a = a * f1 + a2 * f2;
+        m = mn;
+    }
+    const float lse = m + __logf(l);
+    const float Dr = l > 0.0f ? a / l : 0.0f;
+    // pass B: dS and the rotated query gradient
+    float acc[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) acc[kk] = 0.0f;
+    for (int64_t ks0 = t0; ks0 <= kmax; ks0 += kBT) {
+        __syncthreads();
+        load_tile(s_k, kr, ks0);
+        load_v(ks0);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = ks0 + c4 + u;
+            float ds = 0.0f;
+            if (valid(j)) {
+                float dot = 0.0f, dp = 0.0f;
+                for (int x = 0; x < D; ++x) {
+                    dot += s_q[r * LD + x] * s_k[(c4 + u) * LD + x];
+                    dp += s_do[r * LD + x] * s_v[(c4 + u) * LD + x];
+                }
+                const float P = __expf(dot * p.scale - lse);
+                ds = P * (dp - Dr);
+            }
+            s_ds[r][c4 + u] = ds;
+        }
+        __syncthreads();
+        for (int jj = 0; jj < kBT; ++jj) {
+            const float dsv = s_ds[r][jj];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) acc[kk] += dsv * s_k[jj * LD + sub + 8 * kk];
+        }
+    }
+    if (i >= p.N) return;
+    // dq = R(i)^T (scale acc): dims x = sub + 8 kk and x + D/2 are both this thread's
+#pragma unroll
+    for (int kk = 0; kk < NK / 2; ++kk) {
+        const int x = sub + 8 * kk;
+        const float2 cs = rope_cs(tab, nhi, HALF, i, x);
+        const float a = p.scale * acc[kk], b = p.scale * acc[kk + NK / 2];
+        dq[(hN + i) * D + x] = a * cs.x + b * cs.y;
+        dq[(hN + i) * D + x + HALF] = b * cs.x - a * cs.y;
+    }
+    if (sub == 0) {
+        lse_w[hN + i] = lse;
+        D_w[hN + i] = Dr;
+    }
+}
+
+// ---- window, key side. Work-group: 32 keys of one head, over every query tile
+// whose window holds one of them. Thread t takes key t / 8 and queries
+// 4 (t % 8) .. +3 of the current query tile, then dims (t % 8) + 8 k of its key.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_win_dkv_kernel(const float *__restrict__ qr,
+                                                               const float *__restrict__ kr, const T *__restrict__ v,
+                                                               const float *__restrict__ dO,
+                                                               const float *__restrict__ lse_w,
+                                                               const float *__restrict__ D_w,
+                                                               const float2 *__restrict__ tab, int nhi,
+                                                               float *__restrict__ dk, float *__restrict__ dv,
+                                                               KParams p) {
+    constexpr int LD = D + 1, HALF = D / 2, NK = D / 8;
+    __shared__ float s_k[kBT * LD], s_v[kBT * LD], s_q[kBT * LD], s_do[kBT * LD];
+    __shared__ float s_p[kBT][kBT + 1], s_ds[kBT][kBT + 1];
+    __shared__ float s_lse[kBT], s_D[kBT];
+    const int ntile = (int)((p.N + kBT - 1) / kBT);
+    const int h = blockIdx.x / ntile;
+    const int64_t k0 = (int64_t)(blockIdx.x % ntile) * kBT;
+    const int64_t hN = (int64_t)h * p.N;
+    const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7, c4 = 4 * sub;
+    const int64_t j = k0 + r;
+    for (int e = tid; e < kBT * D; e += kThreads) {
+        const int rr = e / D, x = e % D;
+        const int64_t jj = k0 + rr;
+        s_k[rr * LD + x] = jj < p.N ? kr[(hN + jj) * D + x] : 0.0f;
+        s_v[rr * LD + x] = jj < p.N ? ld(v, (hN + jj) * D + x) : 0.0f;
+    }
+    float acck[NK], accv[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) acck[kk] = accv[kk] = 0.0f;
+    const int64_t qmax = min(p.N - 1, k0 + kBT - 1 + (int64_t)p.w - 1);
+    for (int64_t qs0 = k0; qs0 <= qmax; qs0 += kBT) {
+        __syncthreads();
+        for (int e = tid; e < kBT * D; e += kThreads) {
+            const int rr = e / D, x = e % D;
+            const int64_t ii = qs0 + rr;
+            s_q[rr * LD + x] = ii < p.N ? qr[(hN + ii) * D + x] : 0.0f;
+            s_do[rr * LD + x] = ii < p.N ? dO[(hN + ii) * D + x] : 0.0f;
+        }
+        if (tid < kBT) {
+            const int64_t ii = qs0 + tid;
+            s_lse[tid] = ii < p.N ? lse_w[hN + ii] : 0.0f;
+            s_D[tid] = ii < p.N ? D_w[hN + ii] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = qs0 + c4 + u;
+            float P = 0.0f, ds = 0.0f;
+            if (j < p.N && i < p.N && j <= i && j > i - p.w) {
+                float dot = 0.0f, dp = 0.0f;
+                for (int x = 0; x < D; ++x) {
+                    dot += s_q[(c4 + u) * LD + x] * s_k[r * LD + x];
+                    dp += s_do[(c4 + u) * LD + x] * s_v[r * LD + x];
+                }
+                P = __expf(dot * p.scale - s_lse[c4 + u]);
+                ds = P * (dp - s_D[c4 + u]);
+            }
+            s_p[r][c4 + u] = P;
+            s_ds[r][c4 + u] = ds;
+        }
+        __syncthreads();
+        for (int ii = 0; ii < kBT; ++ii) {
+            const float pv = s_p[r][ii], dsv = s_ds[r][ii];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                acck[kk] += dsv * s_q[ii * LD + sub + 8 * kk];
+                accv[kk] += pv * s_do[ii * LD + sub + 8 * kk];
+            }
+        }
+    }
+    if (j >= p.N) return;
+#pragma unroll
+    for (int kk = 0; kk < NK / 2; ++kk) {
+        const int x = sub + 8 * kk;
+        const float2 cs = rope_cs(tab, nhi, HALF, j, x);
+        const float a = p.scale * acck[kk], b = p.scale * acck[kk + NK / 2];
+        dk[(hN + j) * D + x] = a * cs.x + b * cs.y;
+        dk[(hN + j) * D + x + HALF] = b * cs.x - a * cs.y;
+    }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) dv[(hN + j) * D + sub + 8 * kk] = accv[kk];
+}
+
+// ---- long branch, query side: one wave per query (4 per work-group). Recomputes the
+// branch's softmax over the selected cells' tokens, o_long and RMSNorm's backward;
+// writes the gradient reaching the softmax output (do_l), the row's lse and D, the
+// query's dgamma term, and adds the branch's part of dq.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                              const T *__restrict__ v, const float *__restrict__ dO,
+                                                              const int32_t *__restrict__ sel, float *__restrict__ dq,
+                                                              float *__restrict__ do_l, float *__restrict__ lse_l,
+                                                              float *__restrict__ D_l, float *__restrict__ dg,
+                                                              KParams p) {
+    constexpr int NX = D / 64;          // dims per lane
+    constexpr int MAXT = 8 * 64;        // K * s at most
+    __shared__ float s_q[4][D], s_d[4][D];
+    __shared__ float s_s[4][MAXT];
+    __shared__ int64_t s_tok[4][MAXT];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nqw = (int)((p.N + 3) / 4);
+    const int h = blockIdx.x / nqw;
+    const int64_t i = (int64_t)(blockIdx.x % nqw) * 4 + wave;
+    if (i >= p.N) return;  // this wave only: no work-group barrier below
+    const int64_t hN = (int64_t)h * p.N;
+    const int64_t row = (hN + i) * D;
+    int ntok = 0;
+    for (int u = 0; u < p.K; ++u) {
+        const int32_t c = sel[(hN + i) * p.K + u];
+        if (c < 0) continue;
+        for (int t = lane; t < p.s; t += 64) s_tok[wave][ntok + t] = (int64_t)c * p.s + t;
+        ntok += p.s;
+    }
+    if (ntok == 0) {
+        for (int x = lane; x < D; x += 64) do_l[row + x] = 0.0f;
+        if (lane == 0) { lse_l[hN + i] = 0.0f; D_l[hN + i] = 0.0f; dg[hN + i] = 0.0f; }
+        return;
+    }
+    for (int x = lane; x < D; x += 64) s_q[wave][x] = ld(q, row + x);
+    __builtin_amdgcn_wave_barrier();
+    // scores
+    float mx = -INFINITY;
+    for (int t = lane; t < ntok; t += 64) {
+        const int64_t kb = (hN + s_tok[wave][t]) * D;
+        float dot = 0.0f;
+        for (int x = 0; x < D; ++x) dot += s_q[wave][x] * ld(k, kb + x);
+        s_s[wave][t] = dot * p.scale;
+        mx = fmaxf(mx, dot * p.scale);
+    }
+    mx = wave_max(mx);
+    float sum = 0.0f;
+    for (int t = lane; t < ntok; t += 64) sum += __expf(s_s[wave][t] - mx);
+    sum = wave_sum(sum);
+    const float lse = mx + __logf(sum);
+    for (int t = lane; t < ntok; t += 64) s_s[wave][t] = __expf(s_s[wave][t] - lse);  // P_t
+    __builtin_amdgcn_wave_barrier();
+    // o_long, RMSNorm and its backward (lane: dims lane + 64 n)
+    float o[NX], dout_[NX], y[NX];
+#pragma unroll
+    for (int n = 0; n < NX; ++n) {
+        o[n] = 0.0f;
+        dout_[n] = dO[row + lane + 64 * n];
+    }
+    for (int t = 0; t < ntok; ++t) {
+        const float pt = s_s[wave][t];
+        const int64_t vb = (hN + s_tok[wave][t]) * D;
+#pragma unroll
+        for (int n = 0; n < NX; ++n) o[n] += pt * ld(v, vb + lane + 64 * n);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NX; ++n) ss += o[n] * o[n];
+    ss = wave_sum(ss);
+    const float rr = sqrtf(ss / (float)D + p.rms_eps);
+    const float gam = p.gamma[h];
+    float dy_y = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NX; ++n) {
+        y[n] = o[n] / rr;
+        dy_y += dout_[n] * y[n];
+    }
+    dy_y = wave_sum(dy_y);  // dout . y
+    float Dsum = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NX; ++n) {
+        const float d_o = (gam * dout_[n] - y[n] * (gam * dy_y) / (float)D) / rr;
+        s_d[wave][lane + 64 * n] = d_o;
+        do_l[row + lane + 64 * n] = d_o;
+        Dsum += d_o * o[n];
+    }
+    const float Dr = wave_sum(Dsum);
+    if (lane == 0) {
+        lse_l[hN + i] = lse;
+        D_l[hN + i] = Dr;
+        dg[hN + i] = dy_y;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // dS_t = P_t (do . v_t - D)
+    for (int t = lane; t < ntok; t += 64) {
+        const int64_t vb = (hN + s_tok[wave][t]) * D;
+        float dp = 0.0f;
+        for (int x = 0; x < D; ++x) dp += s_d[wave][x] * ld(v, vb + x);
+        s_s[wave][t] = s_s[wave][t] * (dp - Dr);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float acc[NX];
+#pragma unroll
+    for (int n = 0; n < NX; ++n) acc[n] = 0.0f;
+    for (int t = 0; t < ntok; ++t) {
+        const float dst = s_s[wave][t];
+        const int64_t kb = (hN + s_tok[wave][t]) * D;
+#pragma unroll
+        for (int n = 0; n < NX; ++n) acc[n] += dst * ld(k, kb + lane + 64 * n);
+    }
+#pragma unroll
+    for (int n = 0; n < NX; ++n) dq[row + lane + 64 * n] += p.scale * acc[n];
+}
+
+// ---- first and last block whose pool holds each cell (pools are ascending runs of
+// cells; a cell enters a block's pool and, once pushed out, never returns)
+__global__ void bwd_range_init_kernel(int32_t *__restrict__ crange, int64_t n) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n) return;
+    crange[2 * e] = INT_MAX;
+    crange[2 * e + 1] = -1;
+}
+
+__global__ void bwd_cell_range_kernel(const int32_t *__restrict__ pool, int32_t *__restrict__ crange, KParams p) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)p.H * p.nblk * p.PW) return;
+    const int32_t c = pool[e];
+    if (c < 0 || c >= p.C) return;
+    const int64_t hb = e / p.PW;
+    const int h = (int)(hb / p.nblk);
+    const int32_t b = (int32_t)(hb % p.nblk);
+    atomicMin(&crange[2 * ((int64_t)h * p.C + c)], b);
+    atomicMax(&crange[2 * ((int64_t)h * p.C + c) + 1], b);
+}
+
+// ---- long branch, key side: one work-group per (head, cell). Walks the blocks that
+// may select the cell (the blocks whose pool holds it; without pruning, every block
+// from the first one it is eligible for), lists in query order the queries that
+// selected it, and accumulates their dk, dv terms for the cell's S tokens. Thread t
+// takes token t / TPT and dims (t % TPT) + TPT k.
+template <typename T, int D, int S>
+__global__ __launch_bounds__(kThreads) void bwd_long_kv_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                               const T *__restrict__ v, const int32_t *__restrict__ sel,
+                                                               const float *__restrict__ do_l,
+                                                               const float *__restrict__ lse_l,
+                                                               const float *__restrict__ D_l,
+                                                               const int32_t *__restrict__ crange,
+                                                               float *__restrict__ dk, float *__restrict__ dv,
+                                                               KParams p) {
+    constexpr int TPT = kThreads / S;  // threads per token
+    constexpr int NK = D / TPT;        // dims per thread
+    constexpr int G = 8;               // selectors staged per round
+    __shared__ int32_t s_list[256];
+    __shared__ int s_n;
+    __shared__ float s_q[G][D], s_do[G][D];
+    __shared__ float s_lse[G], s_D[G];
+    const int h = (int)(blockIdx.x / p.C);
+    const int64_t c = blockIdx.x % p.C;
+    const int64_t hN = (int64_t)h * p.N;
+    const int tid = threadIdx.x, lane = tid & 63, sub = tid % TPT;
+    int64_t b0, b1;
+    if (p.P < 0) {
+        // first block b with floor((b B - w + 1) / s) > c
+        const int64_t need = (c + 1) * p.s + p.w - 1;
+        b0 = (need + p.B - 1) / p.B;
+        b1 = p.nblk - 1;
+    } else {
+        b0 = crange[2 * ((int64_t)h * p.C + c)];
+        b1 = crange[2 * ((int64_t)h * p.C + c) + 1];
+    }
+    if (b0 > b1) return;  // never selectable: nothing to add
+    const int64_t j = c * S + tid / TPT;
+    float kj[NK], vj[NK], acck[NK], accv[NK];
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+        kj[n] = ld(k, (hN + j) * D + sub + TPT * n);
+        vj[n] = ld(v, (hN + j) * D + sub + TPT * n);
+        acck[n] = accv[n] = 0.0f;
+    }
+    for (int64_t b = b0; b <= b1; ++b) {
+        const int64_t i0 = b * p.B;
+        const int nq = (int)min((int64_t)p.B, p.N - i0);
+        __syncthreads();
+        if (tid < 64) {
+            // ordered list of this block's queries that selected c (wave 0, ballots)
+            int base = 0;
+            for (int t0 = 0; t0 < nq; t0 += 64) {
+                const int t = t0 + lane;
+                bool hit = false;
+                if (t < nq)
+                    for (int u = 0; u < p.K; ++u) hit |= sel[(hN + i0 + t) * p.K + u] == (int32_t)c;
+                const uint64_t bal = __ballot(hit);
+                if (hit) s_list[base + __popcll(bal & ((1ull << lane) - 1ull))] = t;
+                base += __popcll(bal);
+            }
+            if (lane == 0) s_n = base;
+        }
+        __syncthreads();
+        const int n = s_n;
+        for (int g0 = 0; g0 < n; g0 += G) {
+            const int ng = min(G, n - g0);
+            __syncthreads();
+            for (int e = tid; e < ng * D; e += kThreads) {
+                const int gg = e / D, x = e % D;
+                const int64_t ii = i0 + s_list[g0 + gg];
+                s_q[gg][x] = ld(q, (hN + ii) * D + x);
+                s_do[gg][x] = do_l[(hN + ii) * D + x];
+            }
+            if (tid < ng) {
+                const int64_t ii = i0 + s_list[g0 + tid];
+                s_lse[tid] = lse_l[hN + ii];
+                s_D[tid] = D_l[hN + ii];
+            }
+            __syncthreads();
+            for (int gg = 0; gg < ng; ++gg) {
+                float dot = 0.0f, dp = 0.0f;
+#pragma unroll
+                for (int nn = 0; nn < NK; ++nn) {
+                    dot += s_q[gg][sub + TPT * nn] * kj[nn];
+                    dp += s_do[gg][sub + TPT * nn] * vj[nn];
+                }
+                dot = group_sum<TPT>(dot);
+                dp = group_sum<TPT>(dp);
+                const float P = __expf(dot * p.scale - s_lse[gg]);
+                const float ds = P * (dp - s_D[gg]);
+#pragma unroll
+                for (int nn = 0; nn < NK; ++nn) {
+                    acck[nn] += p.scale * ds * s_q[gg][sub + TPT * nn];
+                    accv[nn] += P * s_do[gg][sub + TPT * nn];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+        dk[(hN + j) * D + sub + TPT * n] += acck[n];
+        dv[(hN + j) * D + sub + TPT * n] += accv[n];
+    }
+}
+
+// ---- dgamma of each head: the per-query terms summed in a fixed order
+__global__ __launch_bounds__(kThreads) void bwd_dgamma_kernel(const float *__restrict__ dg, float *__restrict__ dgamma,
+                                                              KParams p) {
+    __shared__ float s_part[kThreads / 64];
+    const int h = blockIdx.x;
+    float acc = 0.0f;
+    for (int64_t t = threadIdx.x; t < p.N; t += kThreads) acc += dg[(int64_t)h * p.N + t];
+    acc = wave_sum(acc);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float s = 0.0f;
+        for (int w = 0; w < kThreads / 64; ++w) s += s_part[w];
+        dgamma[h] = s;
+    }
+}
+
+template <typename T, typename TO, int D, int S>
+static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v_, const void *dout_,
+                                   const int32_t *sel, const int32_t *pool, const BwdWork &w,
+                                   float *dq, float *dk, float *dv, float *dgamma, const KParams &p, hipStream_t st) {
+    const T *q = (const T *)q_, *k = (const T *)k_, *v = (const T *)v_;
+    const TO *dout = (const TO *)dout_;
+    const int nhi = rope_abs_rows_hi(p);
+    hipError_t e = launch_rope_abs_table(w.rope, w.status, p, st);
+    if (e != hipSuccess) return e;
+    const int64_t pairs = (int64_t)p.H * p.N * (D / 2);
+    hipLaunchKernelGGL((bwd_prep_kernel<T, TO, D>), dim3((unsigned)((pairs + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, st, q, k, dout, w.rope, nhi, w.qr, w.kr, w.dO, p);
+    const unsigned tiles = (unsigned)(((p.N + kBT - 1) / kBT) * p.H);
+    hipLaunchKernelGGL((bwd_win_dq_kernel<T, D>), dim3(tiles), dim3(kThreads), 0, st, w.qr, w.kr, v, w.dO,
+                       w.rope, nhi, dq, w.lse_w, w.D_w, p);
+    hipLaunchKernelGGL((bwd_win_dkv_kernel<T, D>), dim3(tiles), dim3(kThreads), 0, st, w.qr, w.kr, v, w.dO, w.lse_w,
+                       w.D_w, w.rope, nhi, dk, dv, p);
+    const unsigned qw = (unsigned)(((p.N + 3) / 4) * p.H);
+    hipLaunchKernelGGL((bwd_long_q_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, k, v, w.dO, sel, dq, w.do_l,
+                       w.lse_l, w.D_l, w.dg, p);
+    if (p.C > 0) {
+        if (p.P >= 0) {
+            const int64_t n = (int64_t)p.H * p.C;
+            hipLaunchKernelGGL(bwd_range_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w.crange, n);
+            const int64_t m = (int64_t)p.H * p.nblk * p.PW;
+            if (m > 0)
+                hipLaunchKernelGGL(bwd_cell_range_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, pool,
+                                   w.crange, p);
+        }
+        hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S>), dim3((unsigned)(p.H * p.C)), dim3(kThreads), 0, st, q, k, v,
+                           sel, w.do_l, w.lse_l, w.D_l, w.crange, dk, dv, p);
+    }
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((unsigned)p.H), dim3(kThreads), 0, st, w.dg, dgamma, p);
+    return hipGetLastError();
+}
+
+template <typename T, typename TO>
+static hipError_t launch_bwd_dt(const void *q, const void *k, const void *v, const void *dout, const int32_t *sel,
+                                const int32_t *pool, const BwdWork &w, float *dq, float *dk,
+                                float *dv, float *dgamma, const KParams &p, hipStream_t st) {
+#define FSL_BWD(DD, SS) \
+    launch_bwd_typed<T, TO, DD, SS>(q, k, v, dout, sel, pool, w, dq, dk, dv, dgamma, p, st)
+    if (p.d == 64) {
+        if (p.s == 16) return FSL_BWD(64, 16);
+        if (p.s == 32) return FSL_BWD(64, 32);
+        return FSL_BWD(64, 64);
+    }
+    if (p.s == 16) return FSL_BWD(128, 16);
+    if (p.s == 32) return FSL_BWD(128, 32);
+    return FSL_BWD(128, 64);
+#undef FSL_BWD
+}
+
+hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const void *dout, const int32_t *sel,
+                           const int32_t *pool, const BwdWork &w, float *dq, float *dk, float *dv,
+                           float *dgamma, const KParams &p, hipStream_t st) {
+    if (p.dtype == FSL_BF16)
+        return p.out_dtype == FSL_BF16
+                   ? launch_bwd_dt<uint16_t, uint16_t>(q, k, v, dout, sel, pool, w, dq, dk, dv, dgamma, p, st)
+                   : launch_bwd_dt<uint16_t, float>(q, k, v, dout, sel, pool, w, dq, dk, dv, dgamma, p, st);
+    return launch_bwd_dt<float, float>(q, k, v, dout, sel, pool, w, dq, dk, dv, dgamma, p, st);
+}
+
+}  // namespace fsl

@@ -411,6 +411,25 @@ hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const
                               const float *o_win, void *out, float *o_long_out, const KParams &p,
                               hipStream_t st);
 
+// the two-level absolute-position (cos, sin) table of kv_prep.hip (rows of 64a, then 64 rows of b);
+// also clears *status
+hipError_t launch_rope_abs_table(float2 *tab, uint32_t *status, const KParams &p, hipStream_t st);
+
+// backward (backward.hip): everything after the forward's selection
+struct BwdWork {
+    float2 *rope;     // absolute-position table
+    float *qr, *kr;   // [H][N][d] RoPE-rotated q and k, fp32
+    float *dO;        // [H][N][d] upstream gradient, fp32
+    float *do_l;      // [H][N][d] gradient reaching the long branch's softmax output
+    float *lse_w, *D_w, *lse_l, *D_l;  // [H][N] row statistics of both branches
+    float *dg;        // [H][N] per-query terms of dgamma
+    int32_t *crange;  // [H][C][2] first and last block whose pool holds the cell
+    uint32_t *status;
+};
+hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const void *dout, const int32_t *sel,
+                           const int32_t *pool, const BwdWork &w, float *dq, float *dk, float *dv,
+                           float *dgamma, const KParams &p, hipStream_t st);
+
 hipError_t launch_decode_init(void *state, const KParams &p, const DecodeLayout &L, int n_seq, hipStream_t st);
 hipError_t launch_decode_prefill(void *state, int seq, const void *kp, const void *vp, int64_t Lp, const Work &w,
                                  const KParams &p, const DecodeLayout &L, hipStream_t st);

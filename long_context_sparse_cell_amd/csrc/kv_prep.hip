@@ -37,6 +37,20 @@ union H8 {
     _Float16 f[8];
 };
 
+// Range tests on packed 16-bit halves (two per dword), OR-ed into an accumulator whose
+// bit 15 or 31 ends up set when some half's magnitude reaches the threshold: with the sign
+// cleared a half lies in [0, 0x7FFF], and adding 0x8000 - T leaves it below 0x8000 exactly
+// when it is below T (no carry crosses into the other half).
+//   bf16 bits >= 0x4780: |x| >= 65536, the first bf16 value past fp16's largest 65504
+//   (infinities and NaNs included);
+//   fp16 bits >= 0x7C00: an fp16 infinity or NaN (a rotated key that overflowed).
+__device__ __forceinline__ uint32_t range_bits(uint32_t w, uint32_t bias2) { return (w & 0x7FFF7FFFu) + bias2; }
+__device__ __forceinline__ uint32_t range_bits4(const uint4 u, uint32_t bias2) {
+    return range_bits(u.x, bias2) | range_bits(u.y, bias2) | range_bits(u.z, bias2) | range_bits(u.w, bias2);
+}
+constexpr uint32_t kBf16PastF16 = 0x38803880u;  // 0x8000 - 0x4780 in both halves
+constexpr uint32_t kF16NonFinite = 0x04000400u; // 0x8000 - 0x7C00 in both halves
+
 __device__ __forceinline__ void bf16x8_to_f32(const uint4 raw, float (&o)[8]) {
     const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -59,6 +73,13 @@ __global__ void rope_abs_kernel(float2 *__restrict__ tab, int nhi, uint32_t *__r
     const double theta = pow((double)p.rope_base, -2.0 * (double)m / (double)p.d);
     const double ang = pos * theta;
     tab[e] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+hipError_t launch_rope_abs_table(float2 *tab, uint32_t *status, const KParams &p, hipStream_t st) {
+    const int nhi = rope_abs_rows_hi(p);
+    const int64_t n = (int64_t)(nhi + kRopeSpan) * (p.d / 2);
+    hipLaunchKernelGGL(rope_abs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, nhi, status, p);
+    return hipGetLastError();
 }
 
 template <int D, bool STATS>
@@ -117,7 +138,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
     }
 
     // ---- rotated keys
-    bool out_of_range = false;  // an fp16 operand would not hold this thread's value
+    uint32_t range_acc = 0u;  // bit 15 or 31 set: an fp16 operand would not hold one of this thread's values
     const float2 *hi = rope + (int64_t)blockIdx.x * HALF;
 #pragma unroll
     for (int u = 0; u < KIT; ++u) {
@@ -134,11 +155,12 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
             const float2 th = hi[8 * pg + r], tl = lo[8 * pg + r];
             const float c = th.x * tl.x - th.y * tl.y;
             const float s = th.y * tl.x + th.x * tl.y;
-            const float xa = a[r] * c - b[r] * s, xb = b[r] * c + a[r] * s;
-            out_of_range |= ok && !(fabsf(xa) < 65504.0f && fabsf(xb) < 65504.0f);
-            ra.f[r] = ok ? (_Float16)xa : (_Float16)0.0f;
-            rb.f[r] = ok ? (_Float16)xb : (_Float16)0.0f;
+            ra.f[r] = ok ? (_Float16)(a[r] * c - b[r] * s) : (_Float16)0.0f;
+            rb.f[r] = ok ? (_Float16)(b[r] * c + a[r] * s) : (_Float16)0.0f;
         }
+        // rows past the end hold zeros here, and copies of the last row in ka / kb
+        range_acc |= range_bits4(ra.u, kF16NonFinite) | range_bits4(rb.u, kF16NonFinite) |
+                     range_bits4(ka[u], kBf16PastF16) | range_bits4(kb[u], kBf16PastF16);
         uint16_t *o = kt + h * kt_head_elems(p) + j * D;
         *reinterpret_cast<uint4 *>(o + 8 * pg) = ra.u;
         *reinterpret_cast<uint4 *>(o + HALF + 8 * pg) = rb.u;
@@ -152,27 +174,16 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
         float e0[8], e1[8];
         bf16x8_to_f32(va[u], e0);
         bf16x8_to_f32(vb[u], e1);
+        range_acc |= range_bits4(va[u], kBf16PastF16) | range_bits4(vb[u], kBf16PastF16);  // past the end: row N-1
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             union { _Float16 f[2]; uint32_t u; } pr;
-            out_of_range |= (j < p.N && !(fabsf(e0[r]) < 65504.0f)) || (j + 1 < p.N && !(fabsf(e1[r]) < 65504.0f));
             pr.f[0] = j < p.N ? (_Float16)e0[r] : (_Float16)0.0f;
             pr.f[1] = j + 1 < p.N ? (_Float16)e1[r] : (_Float16)0.0f;
             *reinterpret_cast<uint32_t *>(&s_t[(8 * c8 + r) * TLD + 2 * jp]) = pr.u;
         }
     }
-    // raw keys past fp16's range are caught too (a rotation can shrink a coordinate)
-#pragma unroll
-    for (int u = 0; u < KIT; ++u) {
-        const int jl = (tid + 256 * u) / PG;
-        float a[8], b[8];
-        bf16x8_to_f32(ka[u], a);
-        bf16x8_to_f32(kb[u], b);
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-            out_of_range |= j0 + jl < p.N && !(fabsf(a[r]) < 65504.0f && fabsf(b[r]) < 65504.0f);
-    }
-    if (__ballot(out_of_range) != 0ull && (tid & 63) == 0) atomicOr(status, FSL_STATUS_F16_RANGE);
+    if (__ballot((range_acc & 0x80008000u) != 0u) != 0ull && (tid & 63) == 0) atomicOr(status, FSL_STATUS_F16_RANGE);
     __syncthreads();
     if constexpr (STATS) {
         // cell statistics of the tile's complete cells (cells of s tokens, s | 64)

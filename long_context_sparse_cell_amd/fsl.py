@@ -67,6 +67,9 @@ def lib():
         L.fsl_prune_select.argtypes = [vp, vp, vp, vp, vp, pp, vp, sz, vp]
         L.fsl_attn_fwd.restype = i32
         L.fsl_attn_fwd.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, vp, vp, vp]
+        L.fsl_attn_bwd_workspace_bytes.restype = sz; L.fsl_attn_bwd_workspace_bytes.argtypes = [pp]
+        L.fsl_attn_bwd.restype = i32
+        L.fsl_attn_bwd.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, sz, vp, vp, vp, vp, vp]
         L.fsl_attn_fwd_noalloc.restype = i32
         L.fsl_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, pp, vp, vp, vp, vp]
         L.fsl_attn_fwd_timed.restype = i32
@@ -297,6 +300,37 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, out: 
             raise ValueError("fsl_attn_fwd: an element of k or v, or a rotated key, lies outside fp16's finite "
                              "range (|x| >= 65504 or not finite); the outputs of this call are undefined")
     return out
+
+
+def attn_bwd_workspace_bytes(p: Params) -> int:
+    return int(lib().fsl_attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, p: Params,
+             fwd_ws: torch.Tensor, ws: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             dgamma: Optional[torch.Tensor] = None, stream=None):
+    """Backward (fsl_attn_bwd): dq, dk, dv [H][N][d] float32 and dgamma [H] float32 for the upstream
+    gradient dout, with the selections of the forward whose workspace is fwd_ws held fixed."""
+    shp = _qkv_shape(p)
+    _check_fwd_operands(q, k, v, None, p)
+    _expect(dout, "dout", shp, _torch_dtype(p.out_dtype))
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, name, shp, torch.float32, optional=True)
+    _expect(dgamma, "dgamma", (p.H,), torch.float32, optional=True)
+    dev = _on_gpu(q=q, dout=dout, fwd_ws=fwd_ws, ws=ws, dq=dq, dk=dk, dv=dv, dgamma=dgamma)
+    _expect_ws(fwd_ws, workspace_bytes(p), dev, "fwd_ws")
+    need = attn_bwd_workspace_bytes(p)
+    ws = _empty(need, torch.uint8, dev, stream) if ws is None else ws
+    _expect_ws(ws, need, dev)
+    dq = _empty(shp, torch.float32, dev, stream) if dq is None else dq
+    dk = _empty(shp, torch.float32, dev, stream) if dk is None else dk
+    dv = _empty(shp, torch.float32, dev, stream) if dv is None else dv
+    dgamma = _empty((p.H,), torch.float32, dev, stream) if dgamma is None else dgamma
+    _check(lib().fsl_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), ctypes.byref(p), _ptr(fwd_ws), fwd_ws.numel(),
+                              _ptr(ws), ws.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgamma), _stream(stream)),
+           "fsl_attn_bwd")
+    return dq, dk, dv, dgamma
 
 
 NOALLOC_WORKSPACE_MAX = 256 << 20  # FSL_NOALLOC_WORKSPACE_MAX

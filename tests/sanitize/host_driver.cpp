@@ -47,6 +47,9 @@ static void forward_paths(const fsl_params &p) {
         CHECK(fsl_cell_stats(a, (float *)a, (float *)a, &p, nullptr) == rc);
         CHECK(fsl_prune_select(a, (float *)a, (float *)a, (int32_t *)a, (int32_t *)a, &p, a, (size_t)1 << 40, nullptr) == rc);
         CHECK(fsl_attn_fwd(a, a, a, a, &p, a, (size_t)1 << 40, nullptr, nullptr, nullptr, nullptr) == rc);
+        CHECK(fsl_attn_bwd_workspace_bytes(&p) == 0);
+        CHECK(fsl_attn_bwd(a, a, a, a, &p, a, (size_t)1 << 40, a, (size_t)1 << 40, (float *)a, (float *)a,
+                           (float *)a, (float *)a, nullptr) == rc);
         CHECK(fsl::g_launches == before);  // nothing launched on a rejected call
         return;
     }
@@ -77,6 +80,20 @@ static void forward_paths(const fsl_params &p) {
     CHECK(fsl_cell_stats(q, (float *)q, (float *)q, &p, nullptr) == FSL_OK);
     CHECK(fsl_cell_stats(q, nullptr, (float *)q, &p, nullptr) == FSL_E_INVAL);
     CHECK(fsl_attn_fwd_timed(q, q, q, q, &p, fake(ws), n, nullptr, nullptr) == FSL_E_INVAL);
+    // the backward: its own workspace checked by the stand-in, the forward's only by size
+    const size_t nb = fsl_attn_bwd_workspace_bytes(&p);
+    CHECK(nb > 0);
+    const uintptr_t bws = (uintptr_t)1 << 45;
+    fsl::g_ws_lo = (const char *)bws;
+    fsl::g_ws_hi = (const char *)(bws + nb);
+    float *g = (float *)fake(0x400000);
+    before = fsl::g_launches;
+    CHECK(fsl_attn_bwd(q, q, q, q, &p, fake(ws), n, fake(bws), nb, g, g, g, g, nullptr) == FSL_OK);
+    CHECK(fsl::g_launches == before + 1);
+    CHECK(fsl_attn_bwd(q, q, q, q, &p, fake(ws), n - 1, fake(bws), nb, g, g, g, g, nullptr) == FSL_E_WORKSPACE);
+    CHECK(fsl_attn_bwd(q, q, q, q, &p, fake(ws), n, fake(bws), nb - 1, g, g, g, g, nullptr) == FSL_E_WORKSPACE);
+    CHECK(fsl_attn_bwd(q, q, q, q, &p, fake(ws), n, fake(bws), nb, g, nullptr, g, g, nullptr) == FSL_E_INVAL);
+    fsl::g_ws_lo = fsl::g_ws_hi = nullptr;
 }
 
 static void decode_paths(const fsl_params &p, int32_t n_seq) {

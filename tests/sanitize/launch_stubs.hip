@@ -67,6 +67,18 @@ hipError_t launch_readout_mix(const void *, const void *, const void *, const in
                               float *, const KParams &, hipStream_t) {
     ++g_launches; inside(sel, "sel"); inside(o_win, "o_win"); return hipSuccess;
 }
+hipError_t launch_rope_abs_table(float2 *tab, uint32_t *status, const KParams &, hipStream_t) {
+    ++g_launches; inside(tab, "rope_abs"); inside(status, "status"); return hipSuccess;
+}
+hipError_t launch_attn_bwd(const void *, const void *, const void *, const void *, const int32_t *, const int32_t *,
+                           const BwdWork &w, float *, float *, float *, float *, const KParams &,
+                           hipStream_t) {
+    ++g_launches;
+    inside(w.rope, "bwd rope"); inside(w.qr, "qr"); inside(w.kr, "kr"); inside(w.dO, "dO"); inside(w.do_l, "do_l");
+    inside(w.lse_w, "lse_w"); inside(w.D_w, "D_w"); inside(w.lse_l, "lse_l"); inside(w.D_l, "D_l");
+    inside(w.dg, "dg"); inside(w.crange, "crange"); inside(w.status, "bwd status");
+    return hipSuccess;
+}
 hipError_t launch_decode_init(void *, const KParams &, const DecodeLayout &, int, hipStream_t) {
     ++g_launches; return hipSuccess;
 }

@@ -17,7 +17,8 @@ SRC = os.path.join(ROOT, "oracle", "fsl_oracle.c")
 
 MUTATIONS = {
     "rope_sign": ("out[m + half] = b * cs + a * sn;", "out[m + half] = b * cs - a * sn;"),
-    "rope_theta": ("-2.0 * (double)m / (double)p->d", "-1.0 * (double)m / (double)p->d"),
+    "rope_theta": ("-2.0 * (double)m / (double)p->d);\n        double ang = (double)t * theta;\n        double cs = cos(ang), sn = sin(ang);\n        double a = (double)x[m]",
+                   "-1.0 * (double)m / (double)p->d);\n        double ang = (double)t * theta;\n        double cs = cos(ang), sn = sin(ang);\n        double a = (double)x[m]"),
     "window_width": ("int64_t j0 = i - p->w + 1;\n    if (j0 < 0) j0 = 0;\n    const int64_t n",
                      "int64_t j0 = i - p->w;\n    if (j0 < 0) j0 = 0;\n    const int64_t n"),
     "eligible_edge": ("int64_t x = b * (int64_t)p->B - (int64_t)p->w + 1;",
