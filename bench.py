@@ -335,6 +335,44 @@ def time_forward(fsl, torch, sh, inp, q, k, v, dev, steps, warmup, with_work=Fal
     return res
 
 
+VALU_F32_PEAK_TFLOPS = 157.3  # fp32 vector
+
+
+def backward_bench(fsl, synth, torch, sh, inp, q, k, v, dev, steps, warmup):
+    """fsl_attn_bwd on one workload (after one forward whose selections it reuses): ms per call and
+    the rate of algorithmic work, 10 d flops per (query, key) pair of both branches (scores, dP, and
+    the dq, dk, dv products), against the fp32 vector peak (the backward runs on the vector ALUs)."""
+    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in (inp.sigma, inp.lam, inp.gamma))
+    p = fsl.make_params(sh.N, sh.H, sh.d, q.dtype, sig, lam, gam, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
+    fws = fsl.new_workspace(p, dev)
+    fsl.attn_fwd(q, k, v, p, ws=fws)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
+    bws = torch.empty(fsl.attn_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+    dg = torch.empty(sh.H, dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        fsl.attn_bwd(q, k, v, dout, p, fws, ws=bws, dq=grads[0], dk=grads[1], dv=grads[2], dgamma=dg)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fsl.attn_bwd(q, k, v, dout, p, fws, ws=bws, dq=grads[0], dk=grads[1], dv=grads[2], dgamma=dg)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    sel = fsl.workspace_views(fws, p)["sel"]
+    long_tokens = int((sel >= 0).sum().item()) * sh.s
+    i = np.arange(sh.N, dtype=np.float64)
+    pairs = sh.H * float(np.minimum(i + 1, sh.w).sum()) + long_tokens
+    flops = 10.0 * sh.d * pairs
+    tf = flops / el / 1e12
+    del fws, bws, grads, dout
+    torch.cuda.empty_cache()
+    return {"workload": sh.name, "ms_per_step": round(el * 1e3, 3), "tokens_per_s": round(sh.N / el, 1),
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": VALU_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4), "flops_per_launch": flops}}
+
+
 def other_workloads(fsl, synth, torch, dev, steps, warmup, skip):
     """The other forward workloads (4k fp32, 16k and 64k bf16), each timed on its own seeded inputs."""
     res = {}
@@ -389,6 +427,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     ap.add_argument("--no-fs", action="store_true", help="skip the unpruned (P = -1) forward measurement")
     ap.add_argument("--no-others", action="store_true", help="skip the 4k/16k/64k workloads and the O(N) check")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward (fsl_attn_bwd) measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, the reference kernel for scaling "
                          "profiler byte counters (FETCH_SIZE / WRITE_SIZE)")
@@ -421,10 +460,33 @@ def main():
     head = time_forward(fsl, torch, sh, inp, q, k, v, dev, args.steps, args.warmup, with_work=True)
     stages, roofline, work = head["stages"], head["roofline"], head["work"]
     t0, t1 = 0.0, head["elapsed_s"]
+    # the decode workload next, before the other measurements' large allocations come and go: a
+    # decode step reads about 190 MB spread over its 847 MiB state, and measured 5x slower on a
+    # state allocated after that churn
+    dec = None
+    if not args.no_decode:
+        log("[bench] streaming decode workload")
+        torch.cuda.empty_cache()
+        dec = decode_bench(fsl, synth, torch, dev)
+        log(f"[bench] decode {dec['tokens_per_s']:.0f} tokens/s, {dec['ms_per_step']:.3f} ms/step")
+
     others = lin = None
     if not args.no_others:
         others = other_workloads(fsl, synth, torch, dev, args.steps, args.warmup, args.workload)
         lin = linearity_check(fsl, synth, torch, dev, args.steps, args.warmup)
+
+    bwd = None
+    if not args.no_backward:
+        log("[bench] backward")
+        bwd = {sh.name: backward_bench(fsl, synth, torch, sh, inp, q, k, v, dev, max(1, args.steps // 4), 1)}
+        log(f"[bench] backward {sh.name}: {bwd[sh.name]['ms_per_step']} ms")
+        if not args.no_others:
+            sh2 = synth.CONFIGS["fwd_bf16_n16384"]
+            inp2 = synth.make_inputs(sh2)
+            q2, k2, v2 = upload(inp2, dev)
+            bwd[sh2.name] = backward_bench(fsl, synth, torch, sh2, inp2, q2, k2, v2, dev, args.steps, args.warmup)
+            log(f"[bench] backward {sh2.name}: {bwd[sh2.name]['ms_per_step']} ms")
+            del q2, k2, v2, inp2
 
     fs = None
     if not args.no_fs and sh.dtype == synth.BF16:
@@ -432,13 +494,6 @@ def main():
         torch.cuda.empty_cache()
         fs = fs_bench(fsl, synth, torch, inp, q, k, v, dev, args.steps, args.warmup)
         log(f"[bench] unpruned forward {fs['ms_per_step']:.3f} ms/step, stages {fs['stages']}")
-
-    dec = None
-    if not args.no_decode:
-        log("[bench] streaming decode workload")
-        torch.cuda.empty_cache()
-        dec = decode_bench(fsl, synth, torch, dev)
-        log(f"[bench] decode {dec['tokens_per_s']:.0f} tokens/s, {dec['ms_per_step']:.3f} ms/step")
 
     cpu = None
     if not args.no_cpu:
@@ -469,6 +524,7 @@ def main():
         "union_cells_per_block": round(work.get("_union_cells_per_block", 0.0), 2),
         "distinct_selected_cells": work.get("_distinct_cells"),
         "other_workloads": others,
+        "backward": bwd,
         "linearity": lin,
         "decode": dec,
         "noprune": fs,
