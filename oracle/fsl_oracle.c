@@ -559,3 +559,365 @@ int orc_backward_head(const float *q, const float *k, const float *v, const floa
     free(krot); free(dkrot); free(qrot); free(dqrot); free(back); free(dO); free(o); free(qd); free(idx);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* FS-B: beam search over two causal forests of balanced trees ([S]
+ * "Methodology in Plain English", FS-B paragraph: one tree over the full
+ * prefix and one over cells whose norm exceeds a threshold; each node keeps a
+ * mean key, a radius bounding its children, the largest cell norm and the
+ * earliest position; a beam of 16 nodes per level descends each tree under a
+ * provable upper bound of the cell score beneath a node; the union of both
+ * beams is reranked with token-level log-sum-exp scores and the top 4 cells
+ * are read. [D] method step 5 and novelty: two balanced forests, log depth,
+ * O(N log^2 N) including radix-sort construction; [S] key contributions 3:
+ * "causal forests").
+ *
+ * Readings where the pages leave the structure open:
+ *  - Lists: list 0 holds every complete cell, list 1 the cells with a_c > tau
+ *    (tau a per-head input; the pages set it once per checkpoint from data),
+ *    both in position order.
+ *  - Causal forest: every aligned segment [a 2^k, (a+1) 2^k) of a list holds a
+ *    perfect binary tree whose leaves are the segment's cells ordered by
+ *    (code asc, list index asc), code a 32-bit sign hash of kbar_c over 32
+ *    given projection rows (bit 31-b set iff proj_b . kbar_c > 0). A block whose
+ *    prefix holds m entries of a list searches the segments of m's binary
+ *    decomposition (largest first): O(log N) trees of depth O(log N).
+ *  - Node: mean key mu = float(sum of its leaves' kbar / count) (fp64 sum in
+ *    leaf order); radius r = max over children of |mu_child - mu| + r_child
+ *    (leaves 0), scaled by (1 + 2^-40) against rounding; amax and pmin the
+ *    largest a_c and smallest c s beneath.
+ *  - Bound (for rho, lambda, sigma >= 0): ub = fma(rho, fma(|q|, r, q . mu),
+ *    (lambda amax) erf(sigma (i - pmin) / (2 s))); at a leaf it is the cell score.
+ *  - Beam, per forest: start from the decomposition's roots; while the beam
+ *    holds an internal node, replace every internal node by its two children
+ *    and keep the `beam` best candidates under (ub desc, node key asc), the key
+ *    ordering forest, level, segment and heap index.
+ *  - Rerank: every distinct cell of the two final beams by
+ *    lse_c = log sum_j exp(scale q . k_j) over its s raw tokens (fp64); the K best
+ *    under (lse desc, cell asc), reported ascending and padded with -1.
+ */
+
+typedef struct {
+    const float *proj;  /* [32][d] projection rows of the code */
+    double tau;         /* list 1 holds the cells with a_c > tau */
+    int32_t beam;       /* nodes kept per level */
+    int32_t pad_;
+} orc_fsb;
+
+uint32_t orc_fsb_code(const float *x, const float *proj, int d)
+{
+    uint32_t code = 0;
+    for (int b = 0; b < 32; ++b) {
+        double dot = 0.0;
+        for (int t = 0; t < d; ++t) dot = fma((double)proj[b * d + t], (double)x[t], dot);
+        if (dot > 0.0) code |= 1u << (31 - b);
+    }
+    return code;
+}
+
+typedef struct {          /* one perfect tree: heap order, nodes 1 .. 2L-1, leaves L .. 2L-1 */
+    int64_t L;
+    int32_t *cell;        /* [L] leaf cells in leaf order */
+    float *mu;            /* [2L][d] */
+    double *rad;          /* [2L] */
+    float *amax;          /* [2L] */
+    int64_t *pmin;        /* [2L] */
+} orc_fsb_tree;
+
+typedef struct { uint32_t code; int64_t idx; int32_t cell; } orc_leafkey;
+
+static int cmp_leafkey(const void *pa, const void *pb)
+{
+    const orc_leafkey *a = (const orc_leafkey *)pa, *b = (const orc_leafkey *)pb;
+    if (a->code != b->code) return a->code < b->code ? -1 : 1;
+    return (a->idx > b->idx) - (a->idx < b->idx);
+}
+
+static double orc_dist(const float *a, const float *b, int d)
+{
+    double acc = 0.0;
+    for (int x = 0; x < d; ++x) {
+        double e = (double)a[x] - (double)b[x];
+        acc = fma(e, e, acc);
+    }
+    return sqrt(acc);
+}
+
+/* the tree of segment [a 2^k, (a+1) 2^k) of a list (list[] of cells, codes[] per cell) */
+void orc_fsb_build_tree(const int32_t *list, int64_t a, int k, const uint32_t *codes, const float *kbar,
+                        const float *amax, const orc_head *p, orc_fsb_tree *t)
+{
+    const int d = p->d;
+    const int64_t L = (int64_t)1 << k, base = a * L;
+    orc_leafkey *lk = (orc_leafkey *)malloc(sizeof(orc_leafkey) * (size_t)L);
+    for (int64_t u = 0; u < L; ++u) {
+        lk[u].idx = base + u;
+        lk[u].cell = list[base + u];
+        lk[u].code = codes[lk[u].cell];
+    }
+    qsort(lk, (size_t)L, sizeof(orc_leafkey), cmp_leafkey);
+    t->L = L;
+    t->cell = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
+    t->mu = (float *)malloc(sizeof(float) * (size_t)(2 * L) * d);
+    t->rad = (double *)calloc((size_t)(2 * L), sizeof(double));
+    t->amax = (float *)malloc(sizeof(float) * (size_t)(2 * L));
+    t->pmin = (int64_t *)malloc(sizeof(int64_t) * (size_t)(2 * L));
+    for (int64_t u = 0; u < L; ++u) t->cell[u] = lk[u].cell;
+    free(lk);
+    for (int64_t j = 1; j < 2 * L; ++j) {
+        int depth = 0;
+        while (((int64_t)1 << (depth + 1)) <= j) ++depth;
+        const int64_t n = L >> depth, first = (j - ((int64_t)1 << depth)) * n;
+        float am = -INFINITY;
+        int64_t pm = INT64_MAX;
+        for (int x = 0; x < d; ++x) {
+            double sum = 0.0;
+            for (int64_t u = first; u < first + n; ++u) sum = sum + (double)kbar[(int64_t)t->cell[u] * d + x];
+            t->mu[j * d + x] = (float)(sum / (double)n);
+        }
+        for (int64_t u = first; u < first + n; ++u) {
+            const int32_t c = t->cell[u];
+            if (amax[c] > am) am = amax[c];
+            if ((int64_t)c * p->s < pm) pm = (int64_t)c * p->s;
+        }
+        t->amax[j] = am;
+        t->pmin[j] = pm;
+    }
+    for (int64_t j = L - 1; j >= 1; --j) {
+        const double r0 = orc_dist(t->mu + 2 * j * d, t->mu + j * d, d) + t->rad[2 * j];
+        const double r1 = orc_dist(t->mu + (2 * j + 1) * d, t->mu + j * d, d) + t->rad[2 * j + 1];
+        t->rad[j] = (r0 > r1 ? r0 : r1) * (1.0 + 0x1p-40);
+    }
+}
+
+static void orc_fsb_free_tree(orc_fsb_tree *t)
+{
+    free(t->cell); free(t->mu); free(t->rad); free(t->amax); free(t->pmin);
+    t->L = 0;
+}
+
+/* the upper bound of node j of tree t for query q_i at position i (|q| given) */
+double orc_fsb_bound(const orc_fsb_tree *t, int64_t j, const float *q_i, double qn, int64_t i, const orc_head *p)
+{
+    double content = 0.0;
+    for (int x = 0; x < p->d; ++x) content = fma((double)q_i[x], (double)t->mu[j * p->d + x], content);
+    const double tt = fma(qn, t->rad[j], content);
+    const double arg = (p->sigma * (double)(i - t->pmin[j])) / (2.0 * (double)p->s);
+    const double g = arg >= 6.0 ? 1.0 : erf(arg);
+    return fma(p->rho, tt, (p->lambda * (double)t->amax[j]) * g);
+}
+
+typedef struct { double ub; int64_t key; const orc_fsb_tree *t; int64_t j; } orc_cand;
+
+static int cmp_cand(const void *pa, const void *pb)
+{
+    const orc_cand *a = (const orc_cand *)pa, *b = (const orc_cand *)pb;
+    if (a->ub > b->ub) return -1;
+    if (a->ub < b->ub) return 1;
+    return (a->key > b->key) - (a->key < b->key);
+}
+
+static int64_t orc_fsb_key(int T, int k, int64_t a, int64_t j)
+{
+    return ((int64_t)T << 40) | ((int64_t)k << 34) | (a << (k + 1)) | j;
+}
+
+/* FS-B selection for one head at the given query rows. q, k: [N][d]; sel: [nrows][K];
+ * lse_out (nullable): [nrows][K] the rerank scores of the selected cells, aligned
+ * with sel (NaN for padding). Returns 0, -1 for bad parameters. */
+int orc_fsb_select(const float *q, const float *k, const orc_head *p, const orc_fsb *fb,
+                   const int64_t *rows, int64_t nrows, int32_t *sel, double *lse_out)
+{
+    const int d = p->d, s = p->s, K = p->K;
+    const int64_t C = orc_num_cells(p);
+    if (d <= 0 || (d & 1) || s <= 0 || K <= 0 || fb->beam < 1 || p->rho < 0 || p->lambda < 0 || p->sigma < 0)
+        return -1;
+    float *kbar = (float *)malloc(sizeof(float) * (size_t)(C > 0 ? C : 1) * d);
+    float *amax = (float *)malloc(sizeof(float) * (size_t)(C > 0 ? C : 1));
+    orc_cell_stats(k, p, kbar, amax);
+    uint32_t *codes = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(C > 0 ? C : 1));
+    for (int64_t c = 0; c < C; ++c) codes[c] = orc_fsb_code(kbar + c * d, fb->proj, d);
+    int32_t *list[2];
+    int64_t len[2] = {0, 0};
+    list[0] = (int32_t *)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
+    list[1] = (int32_t *)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
+    for (int64_t c = 0; c < C; ++c) {
+        list[0][len[0]++] = (int32_t)c;
+        if ((double)amax[c] > fb->tau) list[1][len[1]++] = (int32_t)c;
+    }
+    /* every complete segment's tree, built once: trees[T][k][a] */
+    int kmax = 0;
+    while (((int64_t)1 << (kmax + 1)) <= C) ++kmax;
+    orc_fsb_tree **trees[2];
+    for (int T = 0; T < 2; ++T) {
+        trees[T] = (orc_fsb_tree **)calloc((size_t)kmax + 1, sizeof(orc_fsb_tree *));
+        for (int kk = 0; kk <= kmax; ++kk) {
+            const int64_t nseg = len[T] >> kk;
+            trees[T][kk] = (orc_fsb_tree *)calloc((size_t)(nseg > 0 ? nseg : 1), sizeof(orc_fsb_tree));
+            for (int64_t a = 0; a < nseg; ++a)
+                orc_fsb_build_tree(list[T], a, kk, codes, kbar, amax, p, &trees[T][kk][a]);
+        }
+    }
+    const int B = fb->beam;
+    orc_cand *cand = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)(2 * B + 64));
+    orc_cand *beam = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)(2 * B + 64));
+    int32_t *ucell = (int32_t *)malloc(sizeof(int32_t) * (size_t)(2 * B));
+    orc_skey *rk = (orc_skey *)malloc(sizeof(orc_skey) * (size_t)(2 * B));
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows[r];
+        const float *qi = q + i * d;
+        double qq = 0.0;
+        for (int x = 0; x < d; ++x) qq = fma((double)qi[x], (double)qi[x], qq);
+        const double qn = sqrt(qq);
+        const int64_t nb = orc_eligible(i / p->B, p);
+        int nu = 0;
+        for (int T = 0; T < 2; ++T) {
+            int64_t m = 0;
+            if (T == 0) m = nb;
+            else while (m < len[1] && list[1][m] < nb) ++m;
+            int nc = 0;
+            int64_t base = 0;
+            for (int kk = kmax; kk >= 0; --kk)
+                if ((m >> kk) & 1) {
+                    const int64_t a = base >> kk;
+                    const orc_fsb_tree *t = &trees[T][kk][a];
+                    cand[nc].t = t; cand[nc].j = 1; cand[nc].key = orc_fsb_key(T, kk, a, 1);
+                    cand[nc].ub = orc_fsb_bound(t, 1, qi, qn, i, p);
+                    ++nc;
+                    base += (int64_t)1 << kk;
+                }
+            qsort(cand, (size_t)nc, sizeof(orc_cand), cmp_cand);
+            int nbm = nc < B ? nc : B;
+            memcpy(beam, cand, sizeof(orc_cand) * (size_t)nbm);
+            for (;;) {
+                int internal = 0;
+                for (int u = 0; u < nbm; ++u) internal |= beam[u].j < beam[u].t->L;
+                if (!internal) break;
+                nc = 0;
+                for (int u = 0; u < nbm; ++u) {
+                    if (beam[u].j >= beam[u].t->L) { cand[nc++] = beam[u]; continue; }
+                    for (int ch = 0; ch < 2; ++ch) {
+                        const int64_t j = 2 * beam[u].j + ch;
+                        cand[nc] = beam[u];
+                        cand[nc].j = j;
+                        cand[nc].key = (beam[u].key & ~(((int64_t)1 << 34) - 1)) |
+                                       ((beam[u].key & (((int64_t)1 << 34) - 1)) - beam[u].j + j);
+                        cand[nc].ub = orc_fsb_bound(beam[u].t, j, qi, qn, i, p);
+                        ++nc;
+                    }
+                }
+                qsort(cand, (size_t)nc, sizeof(orc_cand), cmp_cand);
+                nbm = nc < B ? nc : B;
+                memcpy(beam, cand, sizeof(orc_cand) * (size_t)nbm);
+            }
+            for (int u = 0; u < nbm; ++u) {
+                const int32_t c = beam[u].t->cell[beam[u].j - beam[u].t->L];
+                int dup = 0;
+                for (int v2 = 0; v2 < nu; ++v2) dup |= ucell[v2] == c;
+                if (!dup) ucell[nu++] = c;
+            }
+        }
+        /* rerank by token-level log-sum-exp */
+        for (int u = 0; u < nu; ++u) {
+            const int32_t c = ucell[u];
+            double mx = -INFINITY;
+            double *l = (double *)malloc(sizeof(double) * (size_t)s);
+            for (int jt = 0; jt < s; ++jt) {
+                const float *kr = k + ((int64_t)c * s + jt) * d;
+                double dot = 0.0;
+                for (int x = 0; x < d; ++x) dot = fma((double)qi[x], (double)kr[x], dot);
+                l[jt] = p->scale * dot;
+                if (l[jt] > mx) mx = l[jt];
+            }
+            double sum = 0.0;
+            for (int jt = 0; jt < s; ++jt) sum = sum + exp(l[jt] - mx);
+            rk[u].sc = mx + log(sum);
+            rk[u].idx = c;
+            free(l);
+        }
+        qsort(rk, (size_t)nu, sizeof(orc_skey), cmp_skey);
+        const int nsel = nu < K ? nu : K;
+        int32_t *sl = sel + r * K;
+        for (int u = 0; u < nsel; ++u) sl[u] = rk[u].idx;
+        qsort(sl, (size_t)nsel, sizeof(int32_t), cmp_i32);
+        for (int u = nsel; u < K; ++u) sl[u] = -1;
+        if (lse_out)
+            for (int u = 0; u < K; ++u) {
+                double val = NAN;
+                for (int v2 = 0; v2 < nsel; ++v2)
+                    if (rk[v2].idx == sl[u]) val = rk[v2].sc;
+                lse_out[r * K + u] = u < nsel ? val : NAN;
+            }
+    }
+    for (int T = 0; T < 2; ++T) {
+        for (int kk = 0; kk <= kmax; ++kk) {
+            const int64_t nseg = len[T] >> kk;
+            for (int64_t a = 0; a < nseg; ++a) orc_fsb_free_tree(&trees[T][kk][a]);
+            free(trees[T][kk]);
+        }
+        free(trees[T]);
+        free(list[T]);
+    }
+    free(cand); free(beam); free(ucell); free(rk); free(codes); free(kbar); free(amax);
+    return 0;
+}
+
+/* the forward at the given rows with a given selection sel [nrows][K] (ascending,
+ * -1 padded): window, readout over the given cells, mix (for selections made by
+ * another rule, such as FS-B) */
+int orc_forward_rows_sel(const float *q, const float *k, const float *v, const orc_head *p,
+                         const int64_t *rows, int64_t nrows, const int32_t *sel, double *out,
+                         double *o_win, double *o_long)
+{
+    const int d = p->d;
+    const int64_t N = p->N;
+    if (d <= 0 || (d & 1) || p->s <= 0 || p->w <= 0 || p->K <= 0 || N <= 0) return -1;
+    double *krot = (double *)malloc(sizeof(double) * (size_t)N * d);
+    for (int64_t j = 0; j < N; ++j) orc_rope(k + j * d, j, p, krot + j * d);
+    double *qrot = (double *)malloc(sizeof(double) * d);
+    double *ow = (double *)malloc(sizeof(double) * d);
+    double *ol = (double *)malloc(sizeof(double) * d);
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows[r];
+        if (i < 0 || i >= N) { free(krot); free(qrot); free(ow); free(ol); return -2; }
+        orc_rope(q + i * d, i, p, qrot);
+        orc_window(qrot, krot, v, i, p, ow);
+        int32_t nsel = 0;
+        while (nsel < p->K && sel[r * p->K + nsel] >= 0) ++nsel;
+        orc_readout(q + i * d, k, v, sel + r * p->K, nsel, p, ol);
+        orc_mix(ow, ol, p, out + r * d);
+        if (o_win) memcpy(o_win + r * d, ow, sizeof(double) * d);
+        if (o_long) memcpy(o_long + r * d, ol, sizeof(double) * d);
+    }
+    free(krot); free(qrot); free(ow); free(ol);
+    return 0;
+}
+
+/* one segment tree, copied out (for the pins): cell [L], mu [2L][d], rad/amax/pmin [2L] */
+void orc_fsb_tree_dump(const int32_t *list, int64_t a, int k, const uint32_t *codes, const float *kbar,
+                       const float *amax, const orc_head *p, int32_t *cell, float *mu, double *rad, float *am,
+                       int64_t *pmin)
+{
+    orc_fsb_tree t;
+    orc_fsb_build_tree(list, a, k, codes, kbar, amax, p, &t);
+    const int64_t L = t.L;
+    memcpy(cell, t.cell, sizeof(int32_t) * (size_t)L);
+    memcpy(mu, t.mu, sizeof(float) * (size_t)(2 * L) * p->d);
+    memcpy(rad, t.rad, sizeof(double) * (size_t)(2 * L));
+    memcpy(am, t.amax, sizeof(float) * (size_t)(2 * L));
+    memcpy(pmin, t.pmin, sizeof(int64_t) * (size_t)(2 * L));
+    orc_fsb_free_tree(&t);
+}
+
+/* the bound of every node of one segment tree for query q_i at position i (for the pins): ub [2L] */
+void orc_fsb_tree_bounds(const int32_t *list, int64_t a, int k, const uint32_t *codes, const float *kbar,
+                         const float *amax, const orc_head *p, const float *q_i, int64_t i, double *ub)
+{
+    orc_fsb_tree t;
+    orc_fsb_build_tree(list, a, k, codes, kbar, amax, p, &t);
+    double qq = 0.0;
+    for (int x = 0; x < p->d; ++x) qq = fma((double)q_i[x], (double)q_i[x], qq);
+    const double qn = sqrt(qq);
+    for (int64_t j = 1; j < 2 * t.L; ++j) ub[j] = orc_fsb_bound(&t, j, q_i, qn, i, p);
+    orc_fsb_free_tree(&t);
+}

@@ -41,6 +41,11 @@ class Head(ctypes.Structure):
     ]
 
 
+class FsbParams(ctypes.Structure):
+    _fields_ = [("proj", ctypes.c_void_p), ("tau", ctypes.c_double), ("beam", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -73,6 +78,18 @@ def lib():
         L.orc_mix.restype = None; L.orc_mix.argtypes = [f64p, f64p, hp, f64p]
         L.orc_backward_head.restype = ctypes.c_int
         L.orc_backward_head.argtypes = [f32p, f32p, f32p, f32p, i32p, hp, f64p, f64p, f64p, f64p]
+        u32p = P(ctypes.c_uint32)
+        L.orc_fsb_code.restype = ctypes.c_uint32; L.orc_fsb_code.argtypes = [f32p, f32p, ctypes.c_int]
+        L.orc_fsb_select.restype = ctypes.c_int
+        L.orc_fsb_select.argtypes = [f32p, f32p, hp, P(FsbParams), i64p, ctypes.c_int64, i32p, f64p]
+        L.orc_forward_rows_sel.restype = ctypes.c_int
+        L.orc_forward_rows_sel.argtypes = [f32p, f32p, f32p, hp, i64p, ctypes.c_int64, i32p, f64p, f64p, f64p]
+        L.orc_fsb_tree_dump.restype = None
+        L.orc_fsb_tree_dump.argtypes = [i32p, ctypes.c_int64, ctypes.c_int, u32p, f32p, f32p, hp, i32p, f32p, f64p,
+                                        f32p, i64p]
+        L.orc_fsb_tree_bounds.restype = None
+        L.orc_fsb_tree_bounds.argtypes = [i32p, ctypes.c_int64, ctypes.c_int, u32p, f32p, f32p, hp, f32p,
+                                          ctypes.c_int64, f64p]
         L.orc_forward_head.restype = ctypes.c_int
         L.orc_forward_head.argtypes = [f32p, f32p, f32p, hp, i64p, ctypes.c_int64, f64p, f64p, f64p,
                                        i32p, f64p, i32p, ctypes.c_int32, f32p, f32p, ctypes.c_int]
@@ -279,3 +296,70 @@ def backward(inputs, dout, sels, heads=None, workers: int = 0, **overrides):
     n = workers or min(len(heads), len(os.sched_getaffinity(0)), 16)
     with ThreadPoolExecutor(max_workers=max(1, n)) as ex:
         return list(ex.map(one, heads))
+
+
+# ---------------------------------------------------------------------------
+# FS-B (beam search over two causal forests)
+
+def fsb_code(x, proj) -> int:
+    x = _f32(x); proj = _f32(proj)
+    return int(lib().orc_fsb_code(_p(x, ctypes.c_float), _p(proj, ctypes.c_float), x.shape[-1]))
+
+
+def fsb_select(q, k, p: Head, proj, tau: float, beam: int = 16, rows: Optional[Sequence[int]] = None):
+    """FS-B selections of one head at the given rows (default all): sel [R][K] and the rerank
+    log-sum-exp of each selected cell [R][K] (NaN for padding)."""
+    q = _f32(q); k = _f32(k); proj = _f32(proj)
+    assert proj.shape == (32, p.d)
+    rows = np.arange(p.N, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = len(rows)
+    sel = np.full((R, p.K), -1, np.int32)
+    lse = np.zeros((R, p.K), np.float64)
+    fb = FsbParams(proj=proj.ctypes.data, tau=float(tau), beam=int(beam), pad_=0)
+    rc = lib().orc_fsb_select(_p(q, ctypes.c_float), _p(k, ctypes.c_float), ctypes.byref(p), ctypes.byref(fb),
+                              _p(rows, ctypes.c_int64), R, _p(sel, ctypes.c_int32), _p(lse, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the parameters (code {rc})")
+    return sel, lse
+
+
+def forward_rows_sel(q, k, v, p: Head, rows, sel):
+    """Forward outputs (out, o_win, o_long) at the given rows for a given selection [R][K]."""
+    q = _f32(q); k = _f32(k); v = _f32(v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    R, d = len(rows), p.d
+    out = np.zeros((R, d)); ow = np.zeros((R, d)); ol = np.zeros((R, d))
+    rc = lib().orc_forward_rows_sel(_p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
+                                    ctypes.byref(p), _p(rows, ctypes.c_int64), R, _p(sel, ctypes.c_int32),
+                                    _p(out, ctypes.c_double), _p(ow, ctypes.c_double), _p(ol, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the parameters (code {rc})")
+    return out, ow, ol
+
+
+def fsb_tree(list_cells, a: int, k: int, codes, kbar, amax, p: Head):
+    """One segment tree of a list: leaf cells [L], mu [2L][d], rad, amax, pmin [2L] (heap order, index 0 unused)."""
+    lst = np.ascontiguousarray(list_cells, dtype=np.int32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    kbar = _f32(kbar); amax = _f32(amax)
+    L = 1 << k
+    cell = np.zeros(L, np.int32); mu = np.zeros((2 * L, p.d), np.float32); rad = np.zeros(2 * L)
+    am = np.zeros(2 * L, np.float32); pmin = np.zeros(2 * L, np.int64)
+    lib().orc_fsb_tree_dump(_p(lst, ctypes.c_int32), a, k, _p(codes, ctypes.c_uint32), _p(kbar, ctypes.c_float),
+                            _p(amax, ctypes.c_float), ctypes.byref(p), _p(cell, ctypes.c_int32),
+                            _p(mu, ctypes.c_float), _p(rad, ctypes.c_double), _p(am, ctypes.c_float),
+                            _p(pmin, ctypes.c_int64))
+    return dict(cell=cell, mu=mu, rad=rad, amax=am, pmin=pmin)
+
+
+def fsb_tree_bounds(list_cells, a: int, k: int, codes, kbar, amax, p: Head, q_i, i: int):
+    """Upper bound of every node of one segment tree for query q_i at position i ([2L], index 0 unused)."""
+    lst = np.ascontiguousarray(list_cells, dtype=np.int32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    kbar = _f32(kbar); amax = _f32(amax); q_i = _f32(q_i)
+    ub = np.zeros(2 << k)
+    lib().orc_fsb_tree_bounds(_p(lst, ctypes.c_int32), a, k, _p(codes, ctypes.c_uint32), _p(kbar, ctypes.c_float),
+                              _p(amax, ctypes.c_float), ctypes.byref(p), _p(q_i, ctypes.c_float), i,
+                              _p(ub, ctypes.c_double))
+    return ub

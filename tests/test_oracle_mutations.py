@@ -46,8 +46,15 @@ MUTATIONS = {
     "bwd_dgamma": ("dg += (double)dout[i * d + x] * y;", "dg += (double)dout[i * d + x] * o[x];"),
     "bwd_scale": ("da[x] += p->scale * dS * bx;", "da[x] += dS * bx;"),
     "bwd_dv_weight": ("K->dv[j * d + x] += l[t] * dO[x];", "K->dv[j * d + x] += dO[x];"),
+    # FS-B
+    "fsb_radius_dropped": ("const double tt = fma(qn, t->rad[j], content);", "const double tt = content;"),
+    "fsb_pmin": ("if ((int64_t)c * p->s < pm) pm = (int64_t)c * p->s;", "if ((int64_t)c * p->s > pm || pm == INT64_MAX) pm = (int64_t)c * p->s;"),
+    "fsb_code_bit": ("if (dot > 0.0) code |= 1u << (31 - b);", "if (dot > 0.0) code |= 1u << b;"),
+    "fsb_rerank_max": ("rk[u].sc = mx + log(sum);", "rk[u].sc = mx;"),
+    "fsb_beam_width": ("                nbm = nc < B ? nc : B;\n                memcpy(beam, cand",
+                       "                nbm = nc < 1 ? nc : 1;\n                memcpy(beam, cand"),
 }
-PIN_MODULES = ("test_oracle_pins.py", "test_oracle_backward_pins.py")
+PIN_MODULES = ("test_oracle_pins.py", "test_oracle_backward_pins.py", "test_oracle_fsb_pins.py")
 
 
 @pytest.mark.slow
