@@ -185,6 +185,46 @@ int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, 
                  const void *fwd_ws, size_t fwd_ws_bytes, void *ws, size_t ws_bytes, float *dq, float *dk,
                  float *dv, float *dgamma, hipStream_t stream);
 
+/* FS-B: selection by beam search over two causal forests instead of the norm
+ * prune (ai.info summary, "Methodology in Plain English", FS-B paragraph; digest,
+ * method step 5 and novelty: O(N log^2 N) including the radix-sort construction).
+ * Per head, list 0 holds every complete cell and list 1 the cells with
+ * a_c > tau_h, both in position order. Every aligned segment [a 2^k, (a+1) 2^k)
+ * of a list holds a balanced binary tree whose leaves are its cells ordered by
+ * (code asc, list index asc), code the 32-bit sign hash of kbar_c over the 32
+ * rows of proj (bit 31-b set iff proj_b . kbar_c > 0). Nodes keep the mean key
+ * mu (fp32 rounding of the fp64 mean of their leaves), a radius r bounding
+ * their children's balls, the largest a_c and the earliest position pmin
+ * beneath. Block b's queries search, in each forest, the segments of the binary
+ * decomposition of the list entries eligible for block b (as in fsl_prune_select),
+ * keeping `beam` nodes under the bound (rho, lambda_h, sigma_h >= 0)
+ *   ub = fma(rho, fma(|q|, r, q . mu), (lambda_h amax) erf(sigma_h (i - pmin) / (2 s))),
+ * ties by (forest, level, segment, heap index); the union of the two beams'
+ * cells is reranked by lse_c = log sum_j exp(scale q . k_j) over each cell's raw
+ * tokens and the K best (ties to the lower index) are read, ascending and
+ * padded with -1. p->P is ignored. */
+typedef struct fsl_fsb_params {
+    int32_t beam;       /* nodes kept per level in each forest (16); 1 .. 32 */
+    int32_t reserved;   /* 0 */
+    const float *tau;   /* device [H]: list 1 holds the cells with a_c > tau_h */
+    const float *proj;  /* device [32][d]: projection rows of the cell codes */
+} fsl_fsb_params;
+
+/* Workspace bytes of fsl_fsb_select and fsl_attn_fwd_fsb (0 if invalid). */
+size_t fsl_fsb_workspace_bytes(const fsl_params *p);
+
+/* FS-B selections only: sel device [H][N][K] int32 (ascending, padded -1); the
+ * cell statistics are computed into the workspace. q, k: device [H][N][d]. */
+int fsl_fsb_select(const void *q, const void *k, const fsl_params *p, const fsl_fsb_params *fb, int32_t *sel,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole forward with FS-B selections (window branch, readout over the
+ * selected cells, RMSNorm, mix as fsl_attn_fwd). sel_out (nullable) receives the
+ * selections. FSL_E_UNSUPPORTED for rho < 0 or beam outside 1 .. 32; lambda_h,
+ * sigma_h >= 0 is the caller's precondition (the bound assumes it). */
+int fsl_attn_fwd_fsb(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
+                     const fsl_fsb_params *fb, void *ws, size_t ws_bytes, int32_t *sel_out, hipStream_t stream);
+
 /* fsl_attn_fwd for callers that cannot allocate device memory (code under
  * stream capture, tight serving loops, hosts that forbid allocation calls):
  * the same arguments and results without ws / ws_bytes. The workspace is a

@@ -181,6 +181,55 @@ int32_t decode_capacity(const fsl_params *p, size_t state_bytes) {
     return (int32_t)((state_bytes - (size_t)L.off_rec) / ((size_t)p->H * (size_t)L.rec_bytes));
 }
 
+size_t fsb_workspace_extra(const KParams &p, size_t (*align)(size_t)) {
+    const int lv = fsb_levels(p);
+    const size_t nodes = (size_t)p.H * 2 * lv * 2 * p.C, leaves = (size_t)p.H * 2 * lv * p.C;
+    return align(p.H * p.C * sizeof(uint32_t)) + align(p.H * p.C * sizeof(int32_t)) +
+           align((size_t)p.H * (p.C + 1) * sizeof(int32_t)) + align(nodes * p.d * sizeof(float)) +
+           align(nodes * sizeof(double)) + align(nodes * sizeof(float)) + align(nodes * sizeof(int32_t)) +
+           align(leaves * sizeof(int32_t));
+}
+
+void fsb_carve(char *base, const KParams &p, size_t (*align)(size_t), FsbWork &w) {
+    const int lv = fsb_levels(p);
+    const size_t nodes = (size_t)p.H * 2 * lv * 2 * p.C, leaves = (size_t)p.H * 2 * lv * p.C;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { char *at = base + off; off += align(bytes); return at; };
+    w.codes = (uint32_t *)take(p.H * p.C * sizeof(uint32_t));
+    w.list1 = (int32_t *)take(p.H * p.C * sizeof(int32_t));
+    w.hcount = (int32_t *)take((size_t)p.H * (p.C + 1) * sizeof(int32_t));
+    w.mu = (float *)take(nodes * p.d * sizeof(float));
+    w.rad = (double *)take(nodes * sizeof(double));
+    w.amax = (float *)take(nodes * sizeof(float));
+    w.pmin = (int32_t *)take(nodes * sizeof(int32_t));
+    w.leaf = (int32_t *)take(leaves * sizeof(int32_t));
+}
+
+// FS-B runs the unpruned variant's forward (no pool, arbitrary selections in the
+// readout) with its own selection; its workspace is that forward's plus the forests
+size_t fsb_align(size_t x) { return align_up(x); }
+
+fsl_params fsb_base(const fsl_params *p) {
+    fsl_params q = *p;
+    q.P = -1;
+    return q;
+}
+
+int check_fsb(const fsl_params *p, const fsl_fsb_params *fb) {
+    int rc = check(p);
+    if (rc != FSL_OK) return rc;
+    if (!fb || !fb->tau || !fb->proj || fb->reserved != 0) return FSL_E_INVAL;
+    if (fb->beam < 1 || fb->beam > 32 || !(p->rho >= 0.0f)) return FSL_E_UNSUPPORTED;
+    if (!aligned4(fb->tau) || !aligned4(fb->proj)) return FSL_E_INVAL;
+    return FSL_OK;
+}
+
+size_t fsb_bytes(const fsl_params *p) {
+    const fsl_params b = fsb_base(p);
+    const KParams k = kparams(&b);
+    return layout(k).total + fsb_workspace_extra(k, fsb_align);
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +394,57 @@ int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, 
     w.crange = (int32_t *)(b + BL.crange);
     w.status = (uint32_t *)(b + BL.status);
     return hip_status(launch_attn_bwd(q, k, v, dout, (const int32_t *)(f + FL.sel), (const int32_t *)(f + FL.pool), w, dq, dk, dv, dgamma, kp, stream));
+}
+
+size_t fsl_fsb_workspace_bytes(const fsl_params *p) {
+    if (check(p) != FSL_OK) return 0;
+    return fsb_bytes(p);
+}
+
+static int fsb_run(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
+                   const fsl_fsb_params *fb, void *ws, size_t ws_bytes, int32_t *sel_dst, bool forward,
+                   hipStream_t stream) {
+    int rc = check_fsb(p, fb);
+    if (rc != FSL_OK) return rc;
+    if (!q || !k || !ws || (forward && (!v || !out)) || (!forward && !sel_dst)) return FSL_E_INVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(ws) || (v && !aligned16(v)) || (out && !aligned16(out)) ||
+        (sel_dst && !aligned4(sel_dst)))
+        return FSL_E_INVAL;
+    if (ws_bytes < fsb_bytes(p)) return FSL_E_WORKSPACE;
+    const fsl_params base = fsb_base(p);
+    const KParams kp = kparams(&base);
+    const fsl_workspace_layout L = layout(kp);
+    const Work w = carve(ws, L);
+    FsbWork fw;
+    fsb_carve((char *)ws + L.total, kp, fsb_align, fw);
+    const bool bf = kp.dtype == FSL_BF16;
+    hipError_t e = bf && forward ? launch_kv_prep(k, v, w.kt, w.vt, w.rope_abs, w.kbar, w.amax, w.status, kp, stream)
+                                 : launch_cell_stats(k, w.kbar, w.amax, kp, stream);
+    if (e == hipSuccess)
+        e = launch_fsb_select(q, k, w.kbar, w.amax, forward ? w.sel : sel_dst, fw, fb->tau, fb->proj, fb->beam, kp,
+                              stream);
+    if (!forward) return hip_status(e);
+    if (e == hipSuccess && !bf) e = launch_rope_table(w.rope, w.status, kp, stream);
+    if (e == hipSuccess)
+        e = bf ? launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.o_win, kp, stream)
+               : launch_window(q, k, v, w.rope, w.o_win, kp, stream);
+    if (e == hipSuccess)
+        e = bf ? launch_readout_flash(q, k, w.vt, w.sel, w.pool, w.o_win, out, nullptr, kp, stream)
+               : launch_readout_mix(q, k, v, w.sel, w.o_win, out, nullptr, kp, stream);
+    if (e == hipSuccess && sel_dst)
+        e = hipMemcpyAsync(sel_dst, w.sel, (size_t)kp.H * kp.N * kp.K * sizeof(int32_t), hipMemcpyDeviceToDevice,
+                           stream);
+    return hip_status(e);
+}
+
+int fsl_fsb_select(const void *q, const void *k, const fsl_params *p, const fsl_fsb_params *fb, int32_t *sel,
+                   void *ws, size_t ws_bytes, hipStream_t stream) {
+    return fsb_run(q, k, nullptr, nullptr, p, fb, ws, ws_bytes, sel, false, stream);
+}
+
+int fsl_attn_fwd_fsb(const void *q, const void *k, const void *v, void *out, const fsl_params *p,
+                     const fsl_fsb_params *fb, void *ws, size_t ws_bytes, int32_t *sel_out, hipStream_t stream) {
+    return fsb_run(q, k, v, out, p, fb, ws, ws_bytes, sel_out, true, stream);
 }
 
 size_t fsl_decode_state_bytes(const fsl_params *p, int32_t n_seq) {

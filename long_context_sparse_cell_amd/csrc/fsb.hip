@@ -1,0 +1,407 @@
+// FS-B selection: beam search over two causal forests of balanced trees
+// (ai.info summary, "Methodology in Plain English", FS-B paragraph: a tree over
+// the full prefix and one over the cells whose norm exceeds a threshold; nodes
+// keep a mean key, a radius bounding their children, the largest cell norm and
+// the earliest position; a beam of 16 nodes per level descends each tree under
+// a provable upper bound of the cell score beneath a node; the union of the two
+// beams is reranked by token-level log-sum-exp and the top K cells are read.
+// FreeSolo digest, method step 5 and novelty: O(N log^2 N) including the
+// radix-sort construction).
+//
+// Structure (the same readings as the oracle's FS-B):
+//  - list 0 holds every complete cell, list 1 the cells with a_c > tau_h, both in
+//    position order; every aligned segment [a 2^k, (a+1) 2^k) of a list holds a
+//    perfect binary tree (heap order, leaves 2^k .. 2^(k+1) - 1) over the
+//    segment's cells ordered by (code asc, list index asc), code a 32-bit sign
+//    hash of the mean key over 32 given projections;
+//  - a block whose prefix holds m entries of a list searches the segments of m's
+//    binary decomposition: O(log N) trees of depth O(log N).
+// Kernels: fsb_codes (one lane per projection, bits gathered by a ballot),
+// fsb_lists (per head: the high-norm list and the count of high cells below each
+// cell), fsb_tree (one launch per level k, one work-group per segment: the leaf
+// order as the merge of the two sorted halves of level k - 1, which is the sorted
+// order itself, then node means, norms, positions and radii) and fsb_search (one
+// wave per query: beam search over both forests, token-level rerank, top K).
+// Every decision is taken in fp64 with the oracle's operation order (explicit
+// fused multiply-adds, sums left to right), so selections match it exactly; the
+// rerank's exp and log may differ from the host's in the last place, which can
+// only reorder cells whose log-sum-exp agree to about 15 digits.
+#include <climits>
+
+#include "fsl_internal.h"
+
+namespace fsl {
+
+namespace {
+
+constexpr int kSearchWaves = 4;
+
+__device__ __forceinline__ int64_t fsb_key(int T, int k, int64_t a, int64_t j) {
+    return ((int64_t)T << 40) | ((int64_t)k << 34) | (a << (k + 1)) | j;
+}
+
+// "better" for beam candidates: larger bound, then smaller key
+__device__ __forceinline__ bool cand_better(double u1, int64_t k1, double u2, int64_t k2) {
+    return u1 > u2 || (u1 == u2 && k1 < k2);
+}
+
+}  // namespace
+
+// ---- codes: bit 31 - b set iff proj_b . kbar_c > 0 (fp64 fma chain over x). A wave takes
+// two cells, one lane per projection.
+template <int D>
+__global__ __launch_bounds__(256) void fsb_codes_kernel(const float *__restrict__ kbar, const float *__restrict__ proj,
+                                                        uint32_t *__restrict__ codes, KParams p) {
+    const int64_t cell2 = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;  // (head, cell) pair index
+    const int b = threadIdx.x & 31;
+    const bool ok = cell2 < (int64_t)p.H * p.C;
+    double dot = 0.0;
+    if (ok) {
+        const float *x = kbar + cell2 * D;
+        for (int t = 0; t < D; ++t) dot = __fma_rn((double)proj[b * D + t], (double)x[t], dot);
+    }
+    const uint64_t bal = __ballot(ok && dot > 0.0);
+    const uint32_t half = (threadIdx.x & 32) ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+    if (ok && b == 0) codes[cell2] = __builtin_bitreverse32(half);
+}
+
+// ---- list 1 (cells with a_c > tau_h, ascending) and hcount[c] = number of them below c
+__global__ __launch_bounds__(1024) void fsb_lists_kernel(const float *__restrict__ amax, const float *__restrict__ tau,
+                                                         int32_t *__restrict__ list1, int32_t *__restrict__ hcount,
+                                                         KParams p) {
+    __shared__ int s_wave[16];
+    __shared__ int s_base;
+    const int h = blockIdx.x;
+    const double th = (double)tau[h];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) s_base = 0;
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < p.C; c0 += 1024) {
+        const int64_t c = c0 + tid;
+        const bool hi = c < p.C && (double)amax[(int64_t)h * p.C + c] > th;
+        const uint64_t bal = __ballot(hi);
+        if (lane == 0) s_wave[wave] = __popcll(bal);
+        __syncthreads();
+        int before = s_base;
+        for (int w2 = 0; w2 < wave; ++w2) before += s_wave[w2];
+        const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
+        if (c < p.C) {
+            hcount[(int64_t)h * (p.C + 1) + c] = pos;
+            if (hi) list1[(int64_t)h * p.C + pos] = (int32_t)c;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int tot = 0;
+            for (int w2 = 0; w2 < 16; ++w2) tot += s_wave[w2];
+            s_base += tot;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) hcount[(int64_t)h * (p.C + 1) + p.C] = s_base;
+}
+
+// ---- trees of level k: one work-group per (head, forest, segment a)
+template <int D>
+__global__ __launch_bounds__(256) void fsb_tree_kernel(const float *__restrict__ kbar, const float *__restrict__ cam,
+                                                       const uint32_t *__restrict__ codes,
+                                                       const int32_t *__restrict__ list1,
+                                                       const int32_t *__restrict__ hcount, FsbWork w, int k,
+                                                       KParams p) {
+    const int64_t nseg = p.C >> k;
+    const int64_t g = blockIdx.x;
+    const int h = (int)(g / (2 * nseg));
+    const int T = (int)((g / nseg) % 2);
+    const int64_t a = g % nseg;
+    const int64_t len = T == 0 ? p.C : hcount[(int64_t)h * (p.C + 1) + p.C];
+    if ((a + 1) << k > len) return;  // incomplete segment: no tree
+    const int64_t L = (int64_t)1 << k;
+    const int tid = threadIdx.x;
+    auto cell_of = [&](int64_t idx) -> int32_t { return T == 0 ? (int32_t)idx : list1[(int64_t)h * p.C + idx]; };
+    int32_t *leaf = w.leaf + fsb_leaf(p, h, T, k, a, 0);
+    // leaf order: (code, list index) ascending
+    if (k == 0) {
+        if (tid == 0) leaf[0] = cell_of(a);
+    } else {
+        // merge the two sorted halves (the leaves of segments 2a and 2a + 1 of level k - 1)
+        const int32_t *lo = w.leaf + fsb_leaf(p, h, T, k - 1, 2 * a, 0);
+        const int32_t *hi = w.leaf + fsb_leaf(p, h, T, k - 1, 2 * a + 1, 0);
+        const int64_t half = L / 2;
+        const uint32_t *hc = codes + (int64_t)h * p.C;
+        // list index of a cell: the cell itself in list 0, its rank among high cells in list 1
+        auto lidx = [&](int32_t c) -> int64_t { return T == 0 ? (int64_t)c : (int64_t)hcount[(int64_t)h * (p.C + 1) + c]; };
+        for (int64_t u = tid; u < L; u += 256) {
+            const bool left = u < half;
+            const int32_t c = left ? lo[u] : hi[u - half];
+            const uint32_t cc = hc[c];
+            const int64_t ci = lidx(c);
+            const int32_t *other = left ? hi : lo;
+            // number of the other half's keys below this one (keys are distinct)
+            int64_t lo_i = 0, hi_i = half;
+            while (lo_i < hi_i) {
+                const int64_t mid = (lo_i + hi_i) >> 1;
+                const int32_t oc = other[mid];
+                const uint32_t ocode = hc[oc];
+                const bool below = ocode < cc || (ocode == cc && lidx(oc) < ci);
+                if (below) lo_i = mid + 1; else hi_i = mid;
+            }
+            leaf[(left ? u : u - half) + lo_i] = c;
+        }
+    }
+    __syncthreads();
+    // node means (fp64 sums over the node's leaves, left to right), largest norm, earliest position
+    const int64_t nodes = 2 * L;
+    float *mu = w.mu + fsb_node(p, h, T, k, a, 0) * D;
+    double *rad = w.rad + fsb_node(p, h, T, k, a, 0);
+    float *am = w.amax + fsb_node(p, h, T, k, a, 0);
+    int32_t *pm = w.pmin + fsb_node(p, h, T, k, a, 0);
+    for (int64_t e = tid; e < (nodes - 1) * D; e += 256) {
+        const int64_t j = 1 + e / D;
+        const int x = (int)(e % D);
+        const int depth = 63 - __builtin_clzll((uint64_t)j);
+        const int64_t n = L >> depth, first = (j - ((int64_t)1 << depth)) * n;
+        double sum = 0.0;
+        for (int64_t u = first; u < first + n; ++u) sum = __dadd_rn(sum, (double)kbar[((int64_t)h * p.C + leaf[u]) * D + x]);
+        mu[j * D + x] = (float)__ddiv_rn(sum, (double)n);
+    }
+    for (int64_t j = 1 + tid; j < nodes; j += 256) {
+        const int depth = 63 - __builtin_clzll((uint64_t)j);
+        const int64_t n = L >> depth, first = (j - ((int64_t)1 << depth)) * n;
+        float best = -INFINITY;
+        int32_t pmin = INT_MAX;
+        for (int64_t u = first; u < first + n; ++u) {
+            const int32_t c = leaf[u];
+            best = fmaxf(best, cam[(int64_t)h * p.C + c]);
+            pmin = min(pmin, c * p.s);
+        }
+        am[j] = best;
+        pm[j] = pmin;
+        if (j >= L) rad[j] = 0.0;
+    }
+    __syncthreads();
+    // radii, from the level above the leaves to the root
+    for (int depth = k - 1; depth >= 0; --depth) {
+        for (int64_t j = ((int64_t)1 << depth) + tid; j < ((int64_t)2 << depth); j += 256) {
+            double r2[2];
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                const int64_t cj = 2 * j + ch;
+                double acc = 0.0;
+                for (int x = 0; x < D; ++x) {
+                    const double e = __dsub_rn((double)mu[cj * D + x], (double)mu[j * D + x]);
+                    acc = __fma_rn(e, e, acc);
+                }
+                r2[ch] = __dadd_rn(__dsqrt_rn(acc), rad[cj]);
+            }
+            rad[j] = __dmul_rn(r2[0] > r2[1] ? r2[0] : r2[1], 1.0 + 0x1p-40);
+        }
+        __syncthreads();
+    }
+}
+
+// ---- search: one wave per query
+template <int D>
+__global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const float *__restrict__ q32,
+                                                                        const uint16_t *__restrict__ q16,
+                                                                        const float *__restrict__ k32,
+                                                                        const uint16_t *__restrict__ k16,
+                                                                        const int32_t *__restrict__ hcount,
+                                                                        FsbWork w, int beam, int32_t *__restrict__ sel,
+                                                                        KParams p) {
+    __shared__ double s_q[kSearchWaves][D];
+    __shared__ double s_lse[kSearchWaves][64];
+    __shared__ int32_t s_cell[kSearchWaves][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t nq = (p.N + kSearchWaves - 1) / kSearchWaves;
+    const int h = (int)(blockIdx.x / nq);
+    const int64_t i = (blockIdx.x % nq) * kSearchWaves + wave;
+    if (i >= p.N) return;  // per-wave exit: no work-group barrier below
+    const int64_t hN = (int64_t)h * p.N;
+    const bool bf = q16 != nullptr;
+    for (int x = lane; x < D; x += 64)
+        s_q[wave][x] = bf ? (double)bf16_to_f32(q16[(hN + i) * D + x]) : (double)q32[(hN + i) * D + x];
+    __builtin_amdgcn_wave_barrier();
+    double qq = 0.0;
+    for (int x = 0; x < D; ++x) qq = __fma_rn(s_q[wave][x], s_q[wave][x], qq);
+    const double qn = __dsqrt_rn(qq);
+    const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
+    const int64_t nb = eligible_cells(p, i / p.B);
+    const int lv = fsb_levels(p);
+    auto bound = [&](int T, int k, int64_t a, int64_t j) -> double {
+        const int64_t node = fsb_node(p, h, T, k, a, j);
+        const float *mu = w.mu + node * D;
+        double content = 0.0;
+        for (int x = 0; x < D; ++x) content = __fma_rn(s_q[wave][x], (double)mu[x], content);
+        const double tt = __fma_rn(qn, w.rad[node], content);
+        const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)w.pmin[node])), 2.0 * (double)p.s);
+        const double gg = arg >= 6.0 ? 1.0 : erf(arg);
+        return __fma_rn(rho, tt, __dmul_rn(__dmul_rn(lam, (double)w.amax[node]), gg));
+    };
+    int nu = 0;  // distinct cells collected from the two beams (in s_cell)
+    for (int T = 0; T < 2; ++T) {
+        const int64_t m = T == 0 ? nb : (int64_t)hcount[(int64_t)h * (p.C + 1) + nb];
+        // this lane's candidate: forest level k, segment a, heap index j (j = 0: none)
+        int ck = 0;
+        int64_t ca = 0, cj = 0;
+        {
+            // roots: the segments of m's binary decomposition, largest first; lane r takes the r-th
+            int64_t base = 0;
+            int r = 0;
+            for (int kk = lv - 1; kk >= 0; --kk)
+                if ((m >> kk) & 1) {
+                    if (r == lane) { ck = kk; ca = base >> kk; cj = 1; }
+                    base += (int64_t)1 << kk;
+                    ++r;
+                }
+        }
+        double cu = cj ? bound(T, ck, ca, cj) : -INFINITY;
+        int64_t ckey = cj ? fsb_key(T, ck, ca, cj) : INT64_MAX;
+        for (int iter = 0; iter < 64; ++iter) {
+            // keep the beam best: bitonic sort of the wave's candidates, best first
+#pragma unroll
+            for (int kk = 2; kk <= 64; kk <<= 1)
+#pragma unroll
+                for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+                    const double ou = __shfl_xor(cu, jj);
+                    const int64_t okey = __shfl_xor(ckey, jj);
+                    const int ok_ = __shfl_xor(ck, jj);
+                    const int64_t oa = __shfl_xor(ca, jj), oj = __shfl_xor(cj, jj);
+                    const bool lower = (lane & jj) == 0, up = (lane & kk) == 0;
+                    const bool ob = cand_better(ou, okey, cu, ckey);
+                    const bool take = (lower == up) ? ob : !ob;
+                    cu = take ? ou : cu;
+                    ckey = take ? okey : ckey;
+                    ck = take ? ok_ : ck;
+                    ca = take ? oa : ca;
+                    cj = take ? oj : cj;
+                }
+            if (lane >= beam) { cj = 0; cu = -INFINITY; ckey = INT64_MAX; }
+            const bool internal = cj != 0 && cj < ((int64_t)1 << ck);
+            if (__ballot(internal) == 0ull) break;
+            // expand: an internal beam node at lane r moves to its left child and its right child
+            // goes to lane beam + r (beam <= 32, so both fit the wave)
+            const int src = lane - beam;
+            const int64_t pj = __shfl(cj, src < 0 ? 0 : src);
+            const int pk = __shfl(ck, src < 0 ? 0 : src);
+            const int64_t pa = __shfl(ca, src < 0 ? 0 : src);
+            const bool p_int = __shfl((int)internal, src < 0 ? 0 : src) != 0;
+            if (lane < beam) {
+                if (internal) {
+                    cj = 2 * cj;
+                    cu = bound(T, ck, ca, cj);
+                    ckey = fsb_key(T, ck, ca, cj);
+                }
+            } else if (src < beam && p_int) {
+                ck = pk; ca = pa; cj = 2 * pj + 1;
+                cu = bound(T, ck, ca, cj);
+                ckey = fsb_key(T, ck, ca, cj);
+            } else {
+                cj = 0; cu = -INFINITY; ckey = INT64_MAX;
+            }
+        }
+        // this forest's leaves into the union
+        const int32_t mycell = cj ? w.leaf[fsb_leaf(p, h, T, ck, ca, cj - ((int64_t)1 << ck))] : -1;
+        for (int r = 0; r < beam; ++r) {
+            const int32_t c = __shfl(mycell, r);
+            if (c < 0) continue;
+            bool dup = false;
+            for (int u = 0; u < nu; ++u) dup |= s_cell[wave][u] == c;
+            if (!dup) {
+                if (lane == 0) s_cell[wave][nu] = c;
+                ++nu;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    // rerank: lse_c = log sum_j exp(scale q . k_j) over the cell's tokens (token dots one per lane)
+    const int S = p.s;
+    for (int u = 0; u < nu; ++u) {
+        const int32_t c = s_cell[wave][u];
+        double l = -INFINITY;
+        if (lane < S) {
+            const int64_t row = (hN + (int64_t)c * S + lane) * D;
+            double dot = 0.0;
+            for (int x = 0; x < D; ++x)
+                dot = __fma_rn(s_q[wave][x], bf ? (double)bf16_to_f32(k16[row + x]) : (double)k32[row + x], dot);
+            l = __dmul_rn((double)p.scale, dot);
+        }
+        double mx = l;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double ov = __shfl_xor(mx, o);
+            mx = ov > mx ? ov : mx;
+        }
+        const double e = lane < S ? exp(__dsub_rn(l, mx)) : 0.0;
+        // the sum in token order, as the oracle takes it
+        double sum = 0.0;
+        for (int t = 0; t < S; ++t) sum = __dadd_rn(sum, __shfl(e, t));
+        if (lane == 0) s_lse[wave][u] = __dadd_rn(mx, log(sum));
+    }
+    __builtin_amdgcn_wave_barrier();
+    // top K by (lse desc, cell asc), written ascending
+    double lu = lane < nu ? s_lse[wave][lane] : -INFINITY;
+    int32_t lc = lane < nu ? s_cell[wave][lane] : INT_MAX;
+#pragma unroll
+    for (int kk = 2; kk <= 64; kk <<= 1)
+#pragma unroll
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            const double ou = __shfl_xor(lu, jj);
+            const int32_t oc = __shfl_xor(lc, jj);
+            const bool lower = (lane & jj) == 0, up = (lane & kk) == 0;
+            const bool ob = ou > lu || (ou == lu && oc < lc);
+            const bool take = (lower == up) ? ob : !ob;
+            lu = take ? ou : lu;
+            lc = take ? oc : lc;
+        }
+    const int nsel = nu < p.K ? nu : p.K;
+    // ascending order of the K best: sort their cells
+    int32_t key = lane < nsel ? lc : INT_MAX;
+#pragma unroll
+    for (int kk = 2; kk <= 64; kk <<= 1)
+#pragma unroll
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            const int32_t ok2 = __shfl_xor(key, jj);
+            const bool lower = (lane & jj) == 0, up = (lane & kk) == 0;
+            const bool take = (lower == up) ? (ok2 < key) : !(ok2 < key);
+            key = take ? ok2 : key;
+        }
+    if (lane < p.K) sel[(hN + i) * p.K + lane] = lane < nsel ? key : -1;
+}
+
+hipError_t launch_fsb_select(const void *q, const void *k, const float *kbar, const float *amax, int32_t *sel,
+                             const FsbWork &w, const float *tau, const float *proj, int beam, const KParams &p,
+                             hipStream_t st) {
+    if (p.C > 0) {
+        const int64_t lanes = (int64_t)p.H * p.C * 32;
+        const unsigned g = (unsigned)((lanes + 255) / 256);
+        if (p.d == 64)
+            hipLaunchKernelGGL((fsb_codes_kernel<64>), dim3(g), dim3(256), 0, st, kbar, proj, w.codes, p);
+        else
+            hipLaunchKernelGGL((fsb_codes_kernel<128>), dim3(g), dim3(256), 0, st, kbar, proj, w.codes, p);
+        hipLaunchKernelGGL(fsb_lists_kernel, dim3((unsigned)p.H), dim3(1024), 0, st, amax, tau, w.list1, w.hcount, p);
+        const int lv = fsb_levels(p);
+        for (int kk = 0; kk < lv; ++kk) {
+            const unsigned grid = (unsigned)((int64_t)p.H * 2 * (p.C >> kk));
+            if (p.d == 64)
+                hipLaunchKernelGGL((fsb_tree_kernel<64>), dim3(grid), dim3(256), 0, st, kbar, amax, w.codes, w.list1,
+                                   w.hcount, w, kk, p);
+            else
+                hipLaunchKernelGGL((fsb_tree_kernel<128>), dim3(grid), dim3(256), 0, st, kbar, amax, w.codes, w.list1,
+                                   w.hcount, w, kk, p);
+        }
+    }
+    const bool bf = p.dtype == FSL_BF16;
+    const unsigned grid = (unsigned)(((p.N + kSearchWaves - 1) / kSearchWaves) * p.H);
+    const float *q32 = bf ? nullptr : (const float *)q;
+    const uint16_t *q16 = bf ? (const uint16_t *)q : nullptr;
+    const float *k32 = bf ? nullptr : (const float *)k;
+    const uint16_t *k16 = bf ? (const uint16_t *)k : nullptr;
+    if (p.d == 64)
+        hipLaunchKernelGGL((fsb_search_kernel<64>), dim3(grid), dim3(64 * kSearchWaves), 0, st, q32, q16, k32, k16,
+                           w.hcount, w, beam, sel, p);
+    else
+        hipLaunchKernelGGL((fsb_search_kernel<128>), dim3(grid), dim3(64 * kSearchWaves), 0, st, q32, q16, k32, k16,
+                           w.hcount, w, beam, sel, p);
+    return hipGetLastError();
+}
+
+}  // namespace fsl

@@ -430,6 +430,39 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const vo
                            const int32_t *pool, const BwdWork &w, float *dq, float *dk, float *dv,
                            float *dgamma, const KParams &p, hipStream_t st);
 
+// FS-B (fsb.hip): cell codes, the high-norm list, and every segment tree's nodes
+struct FsbWork {
+    uint32_t *codes;   // [H][C] sign hash of each mean key
+    int32_t *list1;    // [H][C] cells with a_c > tau, ascending
+    int32_t *hcount;   // [H][C+1] number of list-1 cells below each cell
+    float *mu;         // [node][d] node mean keys
+    double *rad;       // [node] radii
+    float *amax;       // [node] largest cell norm beneath
+    int32_t *pmin;     // [node] earliest position beneath
+    int32_t *leaf;     // leaf cells of every segment tree
+};
+// levels of the forests: kmax + 1, kmax = floor(log2 C)
+__host__ __device__ inline int fsb_levels(const KParams &p) {
+    int k = 0;
+    while (((int64_t)1 << (k + 1)) <= p.C) ++k;
+    return k + 1;
+}
+
+// node slots per (head, forest, level): 2 C, enough for (C >> k) trees of 2^(k+1) slots
+__host__ __device__ inline int64_t fsb_node(const KParams &p, int h, int T, int k, int64_t a, int64_t j) {
+    const int lv = fsb_levels(p);
+    return ((((int64_t)h * 2 + T) * lv + k) * 2 * p.C) + (a << (k + 1)) + j;
+}
+// leaf slots per (head, forest, level): C
+__host__ __device__ inline int64_t fsb_leaf(const KParams &p, int h, int T, int k, int64_t a, int64_t u) {
+    const int lv = fsb_levels(p);
+    return ((((int64_t)h * 2 + T) * lv + k) * p.C) + (a << k) + u;
+}
+
+hipError_t launch_fsb_select(const void *q, const void *k, const float *kbar, const float *amax, int32_t *sel,
+                             const FsbWork &w, const float *tau, const float *proj, int beam, const KParams &p,
+                             hipStream_t st);
+
 hipError_t launch_decode_init(void *state, const KParams &p, const DecodeLayout &L, int n_seq, hipStream_t st);
 hipError_t launch_decode_prefill(void *state, int seq, const void *kp, const void *vp, int64_t Lp, const Work &w,
                                  const KParams &p, const DecodeLayout &L, hipStream_t st);

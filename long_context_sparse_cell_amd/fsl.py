@@ -38,6 +38,11 @@ class Params(ctypes.Structure):
     ]
 
 
+class FsbParams(ctypes.Structure):
+    _fields_ = [("beam", ctypes.c_int32), ("reserved", ctypes.c_int32), ("tau", ctypes.c_void_p),
+                ("proj", ctypes.c_void_p)]
+
+
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win", "rope_abs", "kt", "vt",
@@ -70,6 +75,10 @@ def lib():
         L.fsl_attn_bwd_workspace_bytes.restype = sz; L.fsl_attn_bwd_workspace_bytes.argtypes = [pp]
         L.fsl_attn_bwd.restype = i32
         L.fsl_attn_bwd.argtypes = [vp, vp, vp, vp, pp, vp, sz, vp, sz, vp, vp, vp, vp, vp]
+        fp = ctypes.POINTER(FsbParams)
+        L.fsl_fsb_workspace_bytes.restype = sz; L.fsl_fsb_workspace_bytes.argtypes = [pp]
+        L.fsl_fsb_select.restype = i32; L.fsl_fsb_select.argtypes = [vp, vp, pp, fp, vp, vp, sz, vp]
+        L.fsl_attn_fwd_fsb.restype = i32; L.fsl_attn_fwd_fsb.argtypes = [vp, vp, vp, vp, pp, fp, vp, sz, vp, vp]
         L.fsl_attn_fwd_noalloc.restype = i32
         L.fsl_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, pp, vp, vp, vp, vp]
         L.fsl_attn_fwd_timed.restype = i32
@@ -299,6 +308,56 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, out: 
         if st & FSL_STATUS_F16_RANGE:
             raise ValueError("fsl_attn_fwd: an element of k or v, or a rotated key, lies outside fp16's finite "
                              "range (|x| >= 65504 or not finite); the outputs of this call are undefined")
+    return out
+
+
+def make_fsb_params(tau: torch.Tensor, proj: torch.Tensor, beam: int = 16) -> FsbParams:
+    """FS-B parameters: tau [H] and proj [32][d] device float32 tensors (kept alive by the block)."""
+    for name, t in (("tau", tau), ("proj", proj)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name}: a contiguous float32 tensor is required")
+    fb = FsbParams(beam=int(beam), reserved=0, tau=tau.data_ptr(), proj=proj.data_ptr())
+    fb._keep = (tau, proj)
+    return fb
+
+
+def fsb_workspace_bytes(p: Params) -> int:
+    return int(lib().fsl_fsb_workspace_bytes(ctypes.byref(p)))
+
+
+def fsb_select(q: torch.Tensor, k: torch.Tensor, p: Params, fb: FsbParams, ws: Optional[torch.Tensor] = None,
+               sel: Optional[torch.Tensor] = None, stream=None):
+    """FS-B selections [H][N][K] (fsl_fsb_select)."""
+    shp = _qkv_shape(p)
+    _expect(q, "q", shp, _torch_dtype(p.dtype))
+    _expect(k, "k", shp, _torch_dtype(p.dtype))
+    _expect(sel, "sel", (p.H, p.N, p.K), torch.int32, optional=True)
+    _expect(fb._keep[0], "tau", (p.H,), torch.float32)
+    _expect(fb._keep[1], "proj", (32, p.d), torch.float32)
+    dev = _on_gpu(q=q, k=k, sel=sel, ws=ws, tau=fb._keep[0], proj=fb._keep[1])
+    need = fsb_workspace_bytes(p)
+    ws = _empty(need, torch.uint8, dev, stream) if ws is None else ws
+    _expect_ws(ws, need, dev)
+    sel = _empty((p.H, p.N, p.K), torch.int32, dev, stream) if sel is None else sel
+    _check(lib().fsl_fsb_select(_ptr(q), _ptr(k), ctypes.byref(p), ctypes.byref(fb), _ptr(sel), _ptr(ws), ws.numel(),
+                                _stream(stream)), "fsl_fsb_select")
+    return sel
+
+
+def attn_fwd_fsb(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Params, fb: FsbParams,
+                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                 sel_out: Optional[torch.Tensor] = None, stream=None):
+    """The forward with FS-B selections (fsl_attn_fwd_fsb)."""
+    dev = _check_fwd_operands(q, k, v, out, p, sel_out, None, None, ws)
+    _expect(fb._keep[0], "tau", (p.H,), torch.float32)
+    _expect(fb._keep[1], "proj", (32, p.d), torch.float32)
+    _on_gpu(q=q, tau=fb._keep[0], proj=fb._keep[1])
+    out = _empty(q.shape, _torch_dtype(p.out_dtype), dev, stream) if out is None else out
+    need = fsb_workspace_bytes(p)
+    ws = _empty(need, torch.uint8, dev, stream) if ws is None else ws
+    _expect_ws(ws, need, dev)
+    _check(lib().fsl_attn_fwd_fsb(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(p), ctypes.byref(fb), _ptr(ws),
+                                  ws.numel(), _ptr(sel_out), _stream(stream)), "fsl_attn_fwd_fsb")
     return out
 
 

@@ -77,6 +77,26 @@ static void forward_paths(const fsl_params &p) {
     CHECK(fsl_prune_select(q, (float *)q, (float *)q, (int32_t *)q, (int32_t *)q, &p, fake(ws), n - 1, nullptr) ==
           FSL_E_WORKSPACE);
     fsl::g_ws_lo = fsl::g_ws_hi = nullptr;
+    // FS-B: its workspace (the unpruned forward's arrays, then the forests) checked by the stand-ins
+    {
+        const size_t nf = fsl_fsb_workspace_bytes(&p);
+        CHECK(nf > 0);
+        fsl_fsb_params fb{16, 0, g_param_arrays, g_param_arrays};
+        const uintptr_t fws = (uintptr_t)1 << 46;
+        fsl::g_ws_lo = (const char *)fws;
+        fsl::g_ws_hi = (const char *)(fws + nf);
+        int32_t *sel = (int32_t *)fake(0x500000);
+        CHECK(fsl_fsb_select(q, q, &p, &fb, sel, fake(fws), nf, nullptr) == (p.rho >= 0 ? FSL_OK : FSL_E_UNSUPPORTED));
+        CHECK(fsl_attn_fwd_fsb(q, q, q, q, &p, &fb, fake(fws), nf, nullptr, nullptr) == FSL_OK);
+        CHECK(fsl_attn_fwd_fsb(q, q, q, q, &p, &fb, fake(fws), nf - 1, nullptr, nullptr) == FSL_E_WORKSPACE);
+        fb.beam = 33;
+        CHECK(fsl_attn_fwd_fsb(q, q, q, q, &p, &fb, fake(fws), nf, nullptr, nullptr) == FSL_E_UNSUPPORTED);
+        fb.beam = 16;
+        fb.tau = nullptr;
+        CHECK(fsl_attn_fwd_fsb(q, q, q, q, &p, &fb, fake(fws), nf, nullptr, nullptr) == FSL_E_INVAL);
+        CHECK(fsl_attn_fwd_fsb(q, q, q, q, &p, nullptr, fake(fws), nf, nullptr, nullptr) == FSL_E_INVAL);
+        fsl::g_ws_lo = fsl::g_ws_hi = nullptr;
+    }
     CHECK(fsl_cell_stats(q, (float *)q, (float *)q, &p, nullptr) == FSL_OK);
     CHECK(fsl_cell_stats(q, nullptr, (float *)q, &p, nullptr) == FSL_E_INVAL);
     CHECK(fsl_attn_fwd_timed(q, q, q, q, &p, fake(ws), n, nullptr, nullptr) == FSL_E_INVAL);

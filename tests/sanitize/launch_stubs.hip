@@ -79,6 +79,15 @@ hipError_t launch_attn_bwd(const void *, const void *, const void *, const void 
     inside(w.dg, "dg"); inside(w.crange, "crange"); inside(w.status, "bwd status");
     return hipSuccess;
 }
+hipError_t launch_fsb_select(const void *, const void *, const float *kbar, const float *amax, int32_t *,
+                             const FsbWork &w, const float *, const float *, int, const KParams &p, hipStream_t) {
+    ++g_launches;
+    if (p.C == 0) return hipSuccess;  // no cells: every forest array is empty and none is touched
+    inside(kbar, "kbar"); inside(amax, "amax"); inside(w.codes, "codes"); inside(w.list1, "list1");
+    inside(w.hcount, "hcount"); inside(w.mu, "mu"); inside(w.rad, "rad"); inside(w.amax, "node amax");
+    inside(w.pmin, "pmin"); inside(w.leaf, "leaf");
+    return hipSuccess;
+}
 hipError_t launch_decode_init(void *, const KParams &, const DecodeLayout &, int, hipStream_t) {
     ++g_launches; return hipSuccess;
 }
