@@ -23,7 +23,8 @@ MUTATIONS = {
                      "int64_t j0 = i - p->w;\n    if (j0 < 0) j0 = 0;\n    const int64_t n"),
     "eligible_edge": ("int64_t x = b * (int64_t)p->B - (int64_t)p->w + 1;",
                       "int64_t x = b * (int64_t)p->B - (int64_t)p->w + 2;"),
-    "erf_width": ("/ (2.0 * (double)p->s);", "/ ((double)p->s);"),
+    "erf_width": ("double arg = (p->sigma * (double)(i - c * (int64_t)p->s)) / (2.0 * (double)p->s);",
+                  "double arg = (p->sigma * (double)(i - c * (int64_t)p->s)) / ((double)p->s);"),
     "erf_dropped": ("* erf(arg);", "* 1.0;"),
     "pool_tie": ("return (a->idx < b->idx) ? -1 : (a->idx > b->idx);\n}\n\nstatic int cmp_i32",
                  "return (a->idx > b->idx) ? -1 : (a->idx < b->idx);\n}\n\nstatic int cmp_i32"),
