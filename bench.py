@@ -109,9 +109,9 @@ def algorithmic_work(sh, sel_np=None):
 # factors read off a plain 1 GiB device copy in the same run), for the kernel source they were taken
 # on and the workload they were taken at; reported only for that workload while that source is unchanged.
 TRAFFIC = {
-    "readout_mix": {"bytes": 3188487861, "workload": "fwd_bf16_h8_n262144_d128",
+    "readout_mix": {"bytes": 3193598614, "workload": "fwd_bf16_h8_n262144_d128",
                     "source": "long_context_sparse_cell_amd/csrc/readout_flash.hip",
-                    "sha256": "db24c4bf584dee7774454ab46329c9d0fe7e22655b98ab2a622791ee6efd826f",
+                    "sha256": "1f0f5efc2f73ba2e2f9a2aa9fd48b86e314b1838759cc7256fd2c7e1347465d4",
                     "profile": "profiles/fwd_n262144_hbm_traffic.md"},
     "decode_step": {"bytes": 191697316, "workload": "decode_bf16_64seq_h16_d64_prefix131072",
                     "source": "long_context_sparse_cell_amd/csrc/decode.hip",
@@ -373,6 +373,40 @@ def backward_bench(fsl, synth, torch, sh, inp, q, k, v, dev, steps, warmup):
                          "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4), "flops_per_launch": flops}}
 
 
+def fsb_bench(fsl, synth, torch, sh, inp, q, k, v, dev, steps, warmup):
+    """The forward with FS-B selections (beam 16 over two causal forests): ms per step and tokens/s,
+    and the selection's own time (fsl_fsb_select, cell statistics and forests included)."""
+    sig, lam, gam = (torch.from_numpy(a).to(dev) for a in (inp.sigma, inp.lam, inp.gamma))
+    p = fsl.make_params(sh.N, sh.H, sh.d, q.dtype, sig, lam, gam, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
+    # tau: the median cell norm of each head's first 4096 tokens (a stand-in for the pages'
+    # per-checkpoint median over training windows); projections: seeded Gaussian rows
+    kb, am = fsl.cell_stats(k[:, :4096].contiguous(), fsl.make_params(4096, sh.H, sh.d, q.dtype, sig, lam, gam,
+                                                                        s=sh.s, B=sh.B))
+    tau = am.median(dim=1).values.contiguous()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    proj = torch.randn((32, sh.d), generator=gen, device=dev, dtype=torch.float32)
+    fb = fsl.make_fsb_params(tau, proj, 16)
+    ws = torch.empty(fsl.fsb_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    sel = torch.empty((sh.H, sh.N, sh.K), dtype=torch.int32, device=dev)
+    res = {"workload": sh.name + "_fsb", "beam": 16}
+    for name, fn in (("forward", lambda: fsl.attn_fwd_fsb(q, k, v, p, fb, out=out, ws=ws)),
+                     ("select", lambda: fsl.fsb_select(q, k, p, fb, ws=ws, sel=sel))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / steps
+        res[name] = {"ms_per_step": round(el * 1e3, 3), "tokens_per_s": round(sh.N / el, 1)}
+    del ws, out, sel
+    torch.cuda.empty_cache()
+    return res
+
+
 def other_workloads(fsl, synth, torch, dev, steps, warmup, skip):
     """The other forward workloads (4k fp32, 16k and 64k bf16), each timed on its own seeded inputs."""
     res = {}
@@ -428,6 +462,7 @@ def main():
     ap.add_argument("--no-fs", action="store_true", help="skip the unpruned (P = -1) forward measurement")
     ap.add_argument("--no-others", action="store_true", help="skip the 4k/16k/64k workloads and the O(N) check")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward (fsl_attn_bwd) measurement")
+    ap.add_argument("--no-fsb", action="store_true", help="skip the FS-B forward measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, the reference kernel for scaling "
                          "profiler byte counters (FETCH_SIZE / WRITE_SIZE)")
@@ -488,6 +523,19 @@ def main():
             log(f"[bench] backward {sh2.name}: {bwd[sh2.name]['ms_per_step']} ms")
             del q2, k2, v2, inp2
 
+    fsb = None
+    if not args.no_fsb:
+        log("[bench] FS-B forward")
+        fsb = {sh.name: fsb_bench(fsl, synth, torch, sh, inp, q, k, v, dev, max(1, args.steps // 4), 1)}
+        log(f"[bench] FS-B {sh.name}: {fsb[sh.name]}")
+        if not args.no_others:
+            sh2 = synth.CONFIGS["fwd_bf16_n16384"]
+            inp2 = synth.make_inputs(sh2)
+            q2, k2, v2 = upload(inp2, dev)
+            fsb[sh2.name] = fsb_bench(fsl, synth, torch, sh2, inp2, q2, k2, v2, dev, args.steps, args.warmup)
+            log(f"[bench] FS-B {sh2.name}: {fsb[sh2.name]}")
+            del q2, k2, v2, inp2
+
     fs = None
     if not args.no_fs and sh.dtype == synth.BF16:
         log("[bench] unpruned (P = -1) forward")
@@ -525,6 +573,7 @@ def main():
         "distinct_selected_cells": work.get("_distinct_cells"),
         "other_workloads": others,
         "backward": bwd,
+        "fsb": fsb,
         "linearity": lin,
         "decode": dec,
         "noprune": fs,
