@@ -85,9 +85,7 @@ def algorithmic_work(sh, sel_np=None):
         # the statistics roofline counts the statistics' own bytes (k read, kbar/amax written),
         # the fused pass's whole traffic is reported beside it
         work["_cell_stats_fused_pass"] = H * N * d * (2 * e + 2 * 2) + H * C * (d + 1) * 4
-    # q and o_win read, out written, plus the keys and values of every selected cell once
-    # per head (keys in the input dtype; values fp16 on the bf16 path, fp32 otherwise)
-    readout = H * N * d * (e + 4 + e)
+    pairs = H * N * K
     if sel_np is not None:
         union_cells = 0
         distinct = 0
@@ -98,10 +96,23 @@ def algorithmic_work(sh, sel_np=None):
             blocks = np.concatenate([sh_sel, np.full((pad, K), -1, sh_sel.dtype)]).reshape(nblk, B * K)
             srt = np.sort(blocks, axis=1)
             union_cells += int(((np.diff(srt, axis=1) != 0).sum(axis=1) + 1 - (srt[:, 0] < 0)).sum())
-        readout += distinct * s * d * (e + (2 if sh.dtype == "bf16" else 4))
+        pairs = int((sel_np >= 0).sum())
         work["_union_cells_per_block"] = union_cells / (H * nblk)
         work["_distinct_cells"] = distinct
-    work["readout_mix"] = ("hbm", readout)
+    else:
+        distinct = 0
+    # the keys and values of every selected cell once per head (keys in the input dtype;
+    # values fp16 on the bf16 path, fp32 otherwise)
+    cells = distinct * s * d * (e + (2 if sh.dtype == "bf16" else 4))
+    if sh.dtype == "bf16":
+        # long branch: q read, each selected cell's keys and values, and per (query, selected
+        # cell) the partial output it hands to the window kernel (fp16 d values and one float)
+        work["readout"] = ("hbm", H * N * d * e + cells + pairs * (2 * d + 4))
+        work["window_mix"] = work.pop("window")
+        work["_partials_bytes"] = pairs * (2 * d + 4)
+    else:
+        # q and o_win read, out written, plus the keys and values of every selected cell
+        work["readout_mix"] = ("hbm", H * N * d * (e + 4 + e) + cells)
     return work
 
 
@@ -248,7 +259,7 @@ def fs_bench(fsl, synth, torch, inp, q, k, v, dev, steps, warmup):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     stage_ms = {name: round(float(np.mean([ev.elapsed_ms(i * nst + j, i * nst + j + 1) for i in range(steps)])), 4)
-                for j, name in enumerate(fsl.STAGES)}
+                for j, name in enumerate(fsl.stage_names(p))}
     ev.close()
     nblk = (sh.N + sh.B - 1) // sh.B
     pairs = 0
@@ -297,7 +308,7 @@ def time_forward(fsl, torch, sh, inp, q, k, v, dev, steps, warmup, with_work=Fal
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     stage_ms = {name: float(np.mean([ev.elapsed_ms(i * nst + j, i * nst + j + 1) for i in range(steps)]))
-                for j, name in enumerate(fsl.STAGES)}
+                for j, name in enumerate(fsl.stage_names(p))}
     gpu_ms = float(np.mean([ev.elapsed_ms(i * nst, i * nst + nst - 1) for i in range(steps)]))
     ev.close()
     res = {"workload": sh.name, "tokens_per_s": round(sh.N * steps / el, 1), "ms_per_step": round(el * 1e3 / steps, 4),

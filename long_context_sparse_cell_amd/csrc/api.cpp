@@ -70,11 +70,15 @@ fsl_workspace_layout layout(const KParams &k, bool full = true) {
     L.rope = take(full ? (size_t)k.rope_n * (k.d / 2) * sizeof(float2) : 0);
     L.scan_a = take((size_t)scan_lists(k) * kChunk * sizeof(float));
     L.scan_i = take((size_t)scan_lists(k) * kChunk * sizeof(int32_t));
-    L.o_win = take(full ? (size_t)k.H * k.N * k.d * sizeof(float) : 0);
     const bool bf = full && k.dtype == FSL_BF16;  // prepared fp16 keys/values, near-tie list: bf16 forward only
+    // fp32 inputs: the window branch's output; bf16 inputs: each selected cell's partial readout
+    L.o_win = take(full && !bf ? (size_t)k.H * k.N * k.d * sizeof(float) : 0);
     L.rope_abs = take(bf ? (size_t)(rope_abs_rows_hi(k) + kRopeSpan) * (k.d / 2) * sizeof(float2) : 0);
     L.kt = take(bf ? (size_t)k.H * kt_head_elems(k) * sizeof(uint16_t) : 0);
     L.vt = take(bf ? (size_t)k.H * vt_head_elems(k) * sizeof(uint16_t) : 0);
+    L.plan = take(bf ? (size_t)plan_records(k) * kPlanRecBytes : 0);
+    L.part = take(bf ? (size_t)k.H * k.N * k.K * k.d * sizeof(uint16_t) : 0);
+    L.plse = take(bf ? (size_t)k.H * k.N * k.K * sizeof(float) : 0);
     const bool fs = k.P < 0;  // no pruning: a contender list per near-tie, and the split cell means
     L.fixups = take(bf ? (size_t)(fs ? fix_words_fs(k) : fix_words(k)) * sizeof(uint32_t) : 0);
     L.khi = take(bf && fs ? (size_t)k.H * k.C * k.d * sizeof(uint16_t) : 0);
@@ -99,6 +103,9 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
     w.rope_abs = (float2 *)(b + L.rope_abs);
     w.kt = (uint16_t *)(b + L.kt);
     w.vt = (uint16_t *)(b + L.vt);
+    w.plan = (uint32_t *)(b + L.plan);
+    w.part = (uint16_t *)(b + L.part);
+    w.plse = (float *)(b + L.plse);
     w.fix = L.khi > L.fixups ? (uint32_t *)(b + L.fixups) : nullptr;  // present iff it has bytes
     w.khi = L.klo > L.khi ? (uint16_t *)(b + L.khi) : nullptr;
     w.klo = L.kcf > L.klo ? (uint16_t *)(b + L.klo) : nullptr;
@@ -108,6 +115,7 @@ Work carve(void *ws, const fsl_workspace_layout &L) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FSL_OK : FSL_E_HIP; }
+
 
 constexpr int32_t kDecodeMaxW = 65536;  // bounds the ring of w + B + s tokens per (sequence, head)
 
@@ -334,16 +342,23 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
                             : hipErrorLaunchFailure)
                      : launch_select(q, w.kbar, w.amax, w.pool, w.sel, kp, stream));
     if (e == hipSuccess) e = mark(bf ? hipSuccess : launch_rope_table(w.rope, w.status, kp, stream));
-    if (e == hipSuccess)
-        e = mark(bf ? launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.o_win, kp, stream)
-                    : launch_window(q, k, v, w.rope, w.o_win, kp, stream));
-    if (e == hipSuccess)
-        e = mark(bf ? launch_readout_flash(q, k, w.vt, w.sel, w.pool, w.o_win, out, o_long_out, kp, stream)
-                    : launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
+    // bf16: the long branch first (a partial output per selected cell), then the window
+    // kernel, which merges the partials, applies RMSNorm and the mix, and writes out;
+    // fp32: the window branch, then the long branch with RMSNorm and the mix
+    if (bf) {
+        if (e == hipSuccess)
+            e = mark(launch_readout_units(q, k, w.vt, w.sel, w.plan, w.part, w.plse, kp, 0, kp.N, stream));
+        if (e == hipSuccess)
+            e = mark(launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.sel, w.part, w.plse, out, o_win_out,
+                                        o_long_out, kp, 0, kp.N, stream));
+    } else {
+        if (e == hipSuccess) e = mark(launch_window(q, k, v, w.rope, w.o_win, kp, stream));
+        if (e == hipSuccess) e = mark(launch_readout_mix(q, k, v, w.sel, w.o_win, out, o_long_out, kp, stream));
+    }
     if (e == hipSuccess && sel_out)
         e = hipMemcpyAsync(sel_out, w.sel, (size_t)kp.H * kp.N * kp.K * sizeof(int32_t), hipMemcpyDeviceToDevice,
                            stream);
-    if (e == hipSuccess && o_win_out)
+    if (e == hipSuccess && o_win_out && !bf)
         e = hipMemcpyAsync(o_win_out, w.o_win, (size_t)kp.H * kp.N * kp.d * sizeof(float), hipMemcpyDeviceToDevice,
                            stream);
     return hip_status(e);
@@ -425,12 +440,15 @@ static int fsb_run(const void *q, const void *k, const void *v, void *out, const
                               stream);
     if (!forward) return hip_status(e);
     if (e == hipSuccess && !bf) e = launch_rope_table(w.rope, w.status, kp, stream);
-    if (e == hipSuccess)
-        e = bf ? launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.o_win, kp, stream)
-               : launch_window(q, k, v, w.rope, w.o_win, kp, stream);
-    if (e == hipSuccess)
-        e = bf ? launch_readout_flash(q, k, w.vt, w.sel, w.pool, w.o_win, out, nullptr, kp, stream)
-               : launch_readout_mix(q, k, v, w.sel, w.o_win, out, nullptr, kp, stream);
+    if (bf) {
+        if (e == hipSuccess) e = launch_readout_units(q, k, w.vt, w.sel, w.plan, w.part, w.plse, kp, 0, kp.N, stream);
+        if (e == hipSuccess)
+            e = launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.sel, w.part, w.plse, out, nullptr, nullptr, kp, 0,
+                                   kp.N, stream);
+    } else {
+        if (e == hipSuccess) e = launch_window(q, k, v, w.rope, w.o_win, kp, stream);
+        if (e == hipSuccess) e = launch_readout_mix(q, k, v, w.sel, w.o_win, out, nullptr, kp, stream);
+    }
     if (e == hipSuccess && sel_dst)
         e = hipMemcpyAsync(sel_dst, w.sel, (size_t)kp.H * kp.N * kp.K * sizeof(int32_t), hipMemcpyDeviceToDevice,
                            stream);

@@ -34,11 +34,14 @@ struct Work {
     float *scan_a;     // prune scan lists, (a, index) pairs of 64 entries:
     int32_t *scan_i;   //   chunks [H][nchunk], local prefixes [H][nchunk+1],
                        //   group totals [H][nsg], group prefixes [H][nsg]
-    float *o_win;      // [H][N][d] window-branch output
+    float *o_win;      // [H][N][d] window-branch output (fp32 inputs)
     // bf16 inputs only (null otherwise): what kv_prep writes
     float2 *rope_abs;  // absolute-position (cos, sin): ceil(N/64) rows of 64a, then 64 rows of b
     uint16_t *kt;      // fp16 [H][Np][d] rotated keys, Np = 64 ceil(N/64)
     uint16_t *vt;      // fp16 [H][Np/32][d][32] values, transposed per 32-token group (vt_pos order)
+    uint32_t *plan;    // per (head, span) plan record of the long branch (kPlanRecBytes each)
+    uint16_t *part;    // fp16 [H][N][K][d] long-branch output of each selected cell, normalised
+    float *plse;       // [H][N][K] lambda = m + log2(l) of each selected cell (base-2 log-sum-exp)
     // queries whose certified filter left more than K contenders (bf16 scoring):
     // one region of kFixRegion entries per scoring work-group (fix_region), and
     // the number of entries each region holds at fix[0 .. fix_regions)
@@ -87,6 +90,25 @@ constexpr int kGroup = 16;    // chunks per prune-scan group
 constexpr int kQTile = 128;   // queries per window workgroup
 constexpr int kKTile = 64;    // keys per window LDS tile
 constexpr int kRopeSpan = 64; // positions per row of the coarse absolute RoPE table
+constexpr int kMaxK = 8;      // largest K (cells a query selects)
+
+// bf16 long branch: queries are read out in spans of span_queries(p) (at most
+// kSpanQ), at most kPlanMaxPairs (query, rank) pairs each. A span's plan record
+// (readout_units.hip) is kPlanRecBytes of 32-bit words: [0] tasks, [1] units,
+// [2] pairs, [3] unused; from kPlanTaskWord two words per task (cell, first unit
+// << 16 | units); from kPlanUnitWord one word per unit (first pair << 16 | pairs);
+// from kPlanPairWord 16-bit pairs (query in the span << 3 | rank).
+constexpr int kSpanQ = 256;
+constexpr int kPlanMaxPairs = 1024;
+constexpr int kPlanTaskWord = 4;
+constexpr int kPlanUnitWord = kPlanTaskWord + 2 * kPlanMaxPairs;
+constexpr int kPlanPairWord = kPlanUnitWord + kPlanMaxPairs + kPlanMaxPairs / 16;
+constexpr int kPlanRecBytes = 15 * 1024;
+static_assert(4 * kPlanPairWord + 2 * kPlanMaxPairs <= kPlanRecBytes, "plan record layout");
+__host__ __device__ inline int span_queries(const KParams &p) { return p.K <= kPlanMaxPairs / kSpanQ ? kSpanQ : kPlanMaxPairs / 8; }
+__host__ __device__ inline int64_t plan_records(const KParams &p) {
+    return (int64_t)p.H * ((p.N + span_queries(p) - 1) / span_queries(p));
+}
 
 // rows of the coarse absolute RoPE table (one per 64 positions)
 __host__ __device__ inline int rope_abs_rows_hi(const KParams &p) { return (int)((p.N + kRopeSpan - 1) / kRopeSpan); }
@@ -402,11 +424,14 @@ hipError_t launch_window(const void *q, const void *k, const void *v, const floa
                          const KParams &p, hipStream_t st);
 hipError_t launch_kv_prep(const void *k, const void *v, uint16_t *kt, uint16_t *vt, float2 *rope_abs, float *kbar,
                           float *amax, uint32_t *status, const KParams &p, hipStream_t st);
-hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs, float *o_win,
-                              const KParams &p, hipStream_t st);
-hipError_t launch_readout_flash(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
-                                const int32_t *pool, const float *o_win, void *out, float *o_long_out, const KParams &p,
-                                hipStream_t st);
+// the query range [qa, qb) of every head; qa a multiple of 256
+hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs,
+                              const int32_t *sel, const uint16_t *part, const float *plse, void *out,
+                              float *o_win_out, float *o_long_out, const KParams &p, int64_t qa, int64_t qb,
+                              hipStream_t st);
+hipError_t launch_readout_units(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
+                                uint32_t *plan, uint16_t *part, float *plse, const KParams &p, int64_t qa,
+                                int64_t qb, hipStream_t st);
 hipError_t launch_readout_mix(const void *q, const void *k, const void *v, const int32_t *sel,
                               const float *o_win, void *out, float *o_long_out, const KParams &p,
                               hipStream_t st);

@@ -21,8 +21,6 @@
 
 namespace fsl {
 
-constexpr int kMaxK = 8;
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void select_kernel(const T *__restrict__ q, const float *__restrict__ kbar,
                                                      const float *__restrict__ amax, const int32_t *__restrict__ pool,

@@ -29,6 +29,7 @@ namespace {
 
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 union P8 {
     uint4 u;
@@ -44,7 +45,12 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
                                                              const uint16_t *__restrict__ kt,
                                                              const uint16_t *__restrict__ vt,
                                                              const float2 *__restrict__ rope,
-                                                             float *__restrict__ o_win, KParams p) {
+                                                             const int32_t *__restrict__ sel,
+                                                             const uint16_t *__restrict__ part,
+                                                             const float *__restrict__ plse,
+                                                             void *__restrict__ out, float *__restrict__ o_win_out,
+                                                             float *__restrict__ o_long_out, KParams p,
+                                                             int tile0, int ntile) {
     constexpr int HALF = D / 2;
     constexpr int QS = D / 32;                  // MFMA k-steps over d
     constexpr int CPR = D / 8;                  // 16-byte chunks per key row
@@ -58,10 +64,10 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
-    const int ntile = (int)((p.N + kQTile - 1) / kQTile);
+    // query tiles tile0 .. tile0 + ntile - 1 of every head
     const int logical = xcd_remap((int)blockIdx.x, ntile * p.H);
     const int h = logical / ntile;
-    const int64_t q0 = (int64_t)(logical % ntile) * kQTile;
+    const int64_t q0 = (int64_t)(tile0 + logical % ntile) * kQTile;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
@@ -245,30 +251,106 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
         __syncthreads();
     }
 
+    // ---- the long branch: merge the query's cells (readout_units.hip wrote, per
+    // selected cell, its normalised output in fp16 and lambda = m + log2(l)) by
+    // weights 2^(lambda - max lambda), which is the softmax over the union of the
+    // cells' tokens; then RMSNorm over d and the mix with the per-head weight.
+    // Lane (col, g) holds dimensions 16 dt + 4 g + r of its query in both branches.
 #pragma unroll
     for (int qg = 0; qg < QT; ++qg) {
         const float l = colsum4(l_part[qg]);
         const int64_t i = qw + 16 * qg + col;
-        if (i >= p.N) continue;
+        const bool ok = i < p.N;
+        const int64_t ic = ok ? i : p.N - 1;
+        const int64_t row = (int64_t)h * p.N + ic;
         const float inv = 1.0f / l;
-        float *orow = o_win + ((int64_t)h * p.N + i) * D;
+        floatx4 ow[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) ow[dt] = oacc[qg][dt] * inv;
+        int sc[kMaxK];
+        float lam[kMaxK];
+        float lmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kMaxK; ++r) {
+            sc[r] = r < p.K ? sel[row * p.K + r] : -1;
+            lam[r] = sc[r] >= 0 ? plse[row * p.K + r] : -INFINITY;
+            lmax = fmaxf(lmax, lam[r]);
+        }
+        floatx4 ol[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) ol[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        float wsum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kMaxK; ++r) {
+            if (sc[r] < 0) continue;
+            const float wr = exp2_hw(lam[r] - lmax);
+            wsum += wr;
+            // element 32 (dt / 2) + 8 g + 4 (dt % 2) + x holds dimension 16 dt + 4 g + x
+            const uint16_t *src = part + (row * p.K + r) * D + 8 * g;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; dt += 2) {
+                union {
+                    u32x4 u;
+                    _Float16 h[8];
+                } c;
+                c.u = *reinterpret_cast<const u32x4 *>(src + 16 * dt);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    ol[dt][x] = fmaf(wr, (float)c.h[x], ol[dt][x]);
+                    ol[dt + 1][x] = fmaf(wr, (float)c.h[4 + x], ol[dt + 1][x]);
+                }
+            }
+        }
+        const float winv = wsum > 0.0f ? 1.0f / wsum : 0.0f;  // no selected cell: o_long = 0
+        float ss = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-            const floatx4 o = oacc[qg][dt] * inv;
-            *reinterpret_cast<float4 *>(orow + 16 * dt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+            ol[dt] *= winv;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ss += ol[dt][x] * ol[dt][x];
+        }
+        ss = colsum4(ss);
+        const float rs = 1.0f / sqrtf(ss / (float)D + p.rms_eps);
+        if (!ok) continue;
+        const float gam = p.gamma[h];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const int c0 = 16 * dt + 4 * g;
+            float val[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) val[x] = ow[dt][x] + gam * (ol[dt][x] * rs);
+            if (p.out_dtype == FSL_BF16) {
+                const uint32_t w0 = (uint32_t)f32_to_bf16(val[0]) | ((uint32_t)f32_to_bf16(val[1]) << 16);
+                const uint32_t w1 = (uint32_t)f32_to_bf16(val[2]) | ((uint32_t)f32_to_bf16(val[3]) << 16);
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + row * D + c0) = make_uint2(w0, w1);
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + row * D + c0) =
+                    make_float4(val[0], val[1], val[2], val[3]);
+            }
+            if (o_win_out)
+                *reinterpret_cast<float4 *>(o_win_out + row * D + c0) =
+                    make_float4(ow[dt][0], ow[dt][1], ow[dt][2], ow[dt][3]);
+            if (o_long_out)
+                *reinterpret_cast<float4 *>(o_long_out + row * D + c0) =
+                    make_float4(ol[dt][0], ol[dt][1], ol[dt][2], ol[dt][3]);
         }
     }
 }
 
 hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t *vt, const float2 *rope_abs,
-                              float *o_win, const KParams &p, hipStream_t st) {
-    dim3 grid((unsigned)(((p.N + kQTile - 1) / kQTile) * p.H));
+                              const int32_t *sel, const uint16_t *part, const float *plse, void *out,
+                              float *o_win_out, float *o_long_out, const KParams &p, int64_t qa, int64_t qb,
+                              hipStream_t st) {
+    const int tile0 = (int)(qa / kQTile);
+    const int ntile = (int)((qb + kQTile - 1) / kQTile) - tile0;
+    if (ntile <= 0) return hipSuccess;
+    dim3 grid((unsigned)(ntile * p.H));
     if (p.d == 64)
         hipLaunchKernelGGL((window_bf16_kernel<64>), grid, dim3(512), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
-                           o_win, p);
+                           sel, part, plse, out, o_win_out, o_long_out, p, tile0, ntile);
     else
         hipLaunchKernelGGL((window_bf16_kernel<128>), grid, dim3(512), 0, st, (const uint16_t *)q, kt, vt, rope_abs,
-                           o_win, p);
+                           sel, part, plse, out, o_win_out, o_long_out, p, tile0, ntile);
     return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ class FsbParams(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("kbar", "amax", "pool", "sel", "rope", "scan_a", "scan_i", "o_win", "rope_abs", "kt", "vt",
-                                      "fixups", "khi", "klo", "kcf", "status", "total")]
+                 "plan", "part", "plse", "fixups", "khi", "klo", "kcf", "status", "total")]
 
 
 _lib = None
@@ -408,7 +408,16 @@ def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: Param
 
 
 NUM_STAGES = 6
-STAGES = ("cell_stats", "prune", "select", "kv_prep", "window", "readout_mix")
+# Stages of fsl_attn_fwd_timed in launch order. fp32 inputs: the window branch, then the long
+# branch with RMSNorm and the mix. bf16 inputs: the long branch as per-cell partial outputs,
+# then the window kernel, which merges them and applies RMSNorm and the mix.
+STAGES_F32 = ("cell_stats", "prune", "select", "kv_prep", "window", "readout_mix")
+STAGES_BF16 = ("cell_stats", "prune", "select", "kv_prep", "readout", "window_mix")
+
+
+def stage_names(p: Params):
+    """Names of the NUM_STAGES stages fsl_attn_fwd_timed records for these parameters."""
+    return STAGES_BF16 if p.dtype == FSL_BF16 else STAGES_F32
 
 
 def attn_fwd_timed(q, k, v, p: Params, out: torch.Tensor, ws: torch.Tensor, events, stream=None):

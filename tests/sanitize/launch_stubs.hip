@@ -54,14 +54,18 @@ hipError_t launch_kv_prep(const void *, const void *, uint16_t *kt, uint16_t *vt
     ++g_launches; inside(kt, "kt"); inside(vt, "vt"); inside(rope_abs, "rope_abs"); inside(kbar, "kbar");
     inside(amax, "amax"); inside(status, "status"); return hipSuccess;
 }
-hipError_t launch_window_bf16(const void *, const uint16_t *kt, const uint16_t *vt, const float2 *rope, float *o_win,
-                              const KParams &, hipStream_t) {
-    ++g_launches; inside(kt, "kt"); inside(vt, "vt"); inside(rope, "rope_abs"); inside(o_win, "o_win");
+hipError_t launch_window_bf16(const void *, const uint16_t *kt, const uint16_t *vt, const float2 *rope,
+                              const int32_t *sel, const uint16_t *part, const float *plse, void *, float *, float *,
+                              const KParams &, int64_t, int64_t, hipStream_t) {
+    ++g_launches; inside(kt, "kt"); inside(vt, "vt"); inside(rope, "rope_abs"); inside(sel, "sel");
+    inside(part, "part"); inside(plse, "plse");
     return hipSuccess;
 }
-hipError_t launch_readout_flash(const void *, const void *, const uint16_t *vt, const int32_t *sel,
-                                const int32_t *, const float *o_win, void *, float *, const KParams &, hipStream_t) {
-    ++g_launches; inside(vt, "vt"); inside(sel, "sel"); inside(o_win, "o_win"); return hipSuccess;
+hipError_t launch_readout_units(const void *, const void *, const uint16_t *vt, const int32_t *sel, uint32_t *plan,
+                                uint16_t *part, float *plse, const KParams &, int64_t, int64_t, hipStream_t) {
+    ++g_launches; inside(vt, "vt"); inside(sel, "sel"); inside(plan, "plan"); inside(part, "part");
+    inside(plse, "plse");
+    return hipSuccess;
 }
 hipError_t launch_readout_mix(const void *, const void *, const void *, const int32_t *sel, const float *o_win, void *,
                               float *, const KParams &, hipStream_t) {

@@ -109,6 +109,21 @@ def test_prepared_key_value_arrays_cover_whole_tiles(fsl, N, d):
     assert L32.status == L32.vt == L32.kt
 
 
+@pytest.mark.parametrize("N,d,K", [(5000, 128, 4), (4096, 64, 8), (1, 64, 1)])
+def test_branch_arrays_by_input_dtype(fsl, N, d, K):
+    """fp32 inputs keep the window branch's fp32 output [H][N][d]; bf16 inputs keep instead,
+    per (query, rank), the selected cell's normalised long-branch output (fp16 [H][N][K][d])
+    and its base-2 log-sum-exp (float [H][N][K]), which the window kernel merges."""
+    H = 3
+    L = fsl.workspace_layout(params(fsl, N=N, d=d, H=H, K=K, dtype=1, out_dtype=1))
+    assert L.rope_abs == L.o_win  # no fp32 window output
+    assert L.plse - L.part >= H * N * K * d * 2 and L.fixups - L.plse >= H * N * K * 4
+    assert L.part % 256 == 0 and L.plse % 256 == 0
+    L32 = fsl.workspace_layout(params(fsl, N=N, d=d, H=H, K=K, dtype=0, out_dtype=0))
+    assert L32.rope_abs - L32.o_win >= H * N * d * 4
+    assert L32.part == L32.plse == L32.fixups  # no partial arrays
+
+
 @pytest.mark.parametrize("dtype", [0, 1])
 def test_unpruned_variant_workspace(fsl, dtype):
     """P = -1 (plain FS): no pool table; with bf16 inputs the workspace holds the split cell
