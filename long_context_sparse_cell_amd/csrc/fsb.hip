@@ -221,16 +221,30 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
         s_q[wave][x] = bf ? (double)bf16_to_f32(q16[(hN + i) * D + x]) : (double)q32[(hN + i) * D + x];
     __builtin_amdgcn_wave_barrier();
     double qq = 0.0;
+#pragma unroll 4
     for (int x = 0; x < D; ++x) qq = __fma_rn(s_q[wave][x], s_q[wave][x], qq);
     const double qn = __dsqrt_rn(qq);
     const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
     const int64_t nb = eligible_cells(p, i / p.B);
     const int lv = fsb_levels(p);
+    // upper bound of the cell score under a node: the mean key read 16 bytes at a time,
+    // the dot product still one fma per coordinate, left to right
     auto bound = [&](int T, int k, int64_t a, int64_t j) -> double {
         const int64_t node = fsb_node(p, h, T, k, a, j);
-        const float *mu = w.mu + node * D;
+        const float4 *mu = reinterpret_cast<const float4 *>(w.mu + node * D);
+        // the query stays in LDS (read at every use): held in registers it would take
+        // 2 D of them and leave room for one wave per SIMD
+        const double *qv = s_q[wave];
+        asm volatile("" : "+v"(qv));
         double content = 0.0;
-        for (int x = 0; x < D; ++x) content = __fma_rn(s_q[wave][x], (double)mu[x], content);
+#pragma unroll 4
+        for (int x4 = 0; x4 < D / 4; ++x4) {
+            const float4 m4 = mu[x4];
+            content = __fma_rn(qv[4 * x4], (double)m4.x, content);
+            content = __fma_rn(qv[4 * x4 + 1], (double)m4.y, content);
+            content = __fma_rn(qv[4 * x4 + 2], (double)m4.z, content);
+            content = __fma_rn(qv[4 * x4 + 3], (double)m4.w, content);
+        }
         const double tt = __fma_rn(qn, w.rad[node], content);
         const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)w.pmin[node])), 2.0 * (double)p.s);
         const double gg = arg >= 6.0 ? 1.0 : erf(arg);
@@ -239,7 +253,8 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     int nu = 0;  // distinct cells collected from the two beams (in s_cell)
     for (int T = 0; T < 2; ++T) {
         const int64_t m = T == 0 ? nb : (int64_t)hcount[(int64_t)h * (p.C + 1) + nb];
-        // this lane's candidate: forest level k, segment a, heap index j (j = 0: none)
+        // this lane's candidate: forest level k, segment a, heap index j (j = 0: none);
+        // fresh: its bound is still to be taken
         int ck = 0;
         int64_t ca = 0, cj = 0;
         {
@@ -253,13 +268,18 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
                     ++r;
                 }
         }
-        double cu = cj ? bound(T, ck, ca, cj) : -INFINITY;
-        int64_t ckey = cj ? fsb_key(T, ck, ca, cj) : INT64_MAX;
+        bool fresh = cj != 0;
+        double cu = -INFINITY;
+        int64_t ckey = INT64_MAX;
         for (int iter = 0; iter < 64; ++iter) {
+            if (fresh) {
+                cu = bound(T, ck, ca, cj);
+                ckey = fsb_key(T, ck, ca, cj);
+            }
             // keep the beam best: bitonic sort of the wave's candidates, best first
-#pragma unroll
+#pragma unroll 1
             for (int kk = 2; kk <= 64; kk <<= 1)
-#pragma unroll
+#pragma unroll 1
                 for (int jj = kk >> 1; jj > 0; jj >>= 1) {
                     const double ou = __shfl_xor(cu, jj);
                     const int64_t okey = __shfl_xor(ckey, jj);
@@ -284,16 +304,15 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
             const int pk = __shfl(ck, src < 0 ? 0 : src);
             const int64_t pa = __shfl(ca, src < 0 ? 0 : src);
             const bool p_int = __shfl((int)internal, src < 0 ? 0 : src) != 0;
+            fresh = false;
             if (lane < beam) {
                 if (internal) {
                     cj = 2 * cj;
-                    cu = bound(T, ck, ca, cj);
-                    ckey = fsb_key(T, ck, ca, cj);
+                    fresh = true;
                 }
             } else if (src < beam && p_int) {
                 ck = pk; ca = pa; cj = 2 * pj + 1;
-                cu = bound(T, ck, ca, cj);
-                ckey = fsb_key(T, ck, ca, cj);
+                fresh = true;
             } else {
                 cj = 0; cu = -INFINITY; ckey = INT64_MAX;
             }
@@ -318,10 +337,34 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
         const int32_t c = s_cell[wave][u];
         double l = -INFINITY;
         if (lane < S) {
+            // the token's key row 16 bytes at a time, one fma per coordinate, left to right
             const int64_t row = (hN + (int64_t)c * S + lane) * D;
+            const double *qv = s_q[wave];
+            asm volatile("" : "+v"(qv));
             double dot = 0.0;
-            for (int x = 0; x < D; ++x)
-                dot = __fma_rn(s_q[wave][x], bf ? (double)bf16_to_f32(k16[row + x]) : (double)k32[row + x], dot);
+            if (bf) {
+                const uint4 *kr = reinterpret_cast<const uint4 *>(k16 + row);
+#pragma unroll 2
+                for (int x8 = 0; x8 < D / 8; ++x8) {
+                    const uint4 r4 = kr[x8];
+                    const uint32_t w4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        dot = __fma_rn(qv[8 * x8 + 2 * t], (double)__uint_as_float(w4[t] << 16), dot);
+                        dot = __fma_rn(qv[8 * x8 + 2 * t + 1], (double)__uint_as_float(w4[t] & 0xFFFF0000u), dot);
+                    }
+                }
+            } else {
+                const float4 *kr = reinterpret_cast<const float4 *>(k32 + row);
+#pragma unroll 4
+                for (int x4 = 0; x4 < D / 4; ++x4) {
+                    const float4 f4 = kr[x4];
+                    dot = __fma_rn(qv[4 * x4], (double)f4.x, dot);
+                    dot = __fma_rn(qv[4 * x4 + 1], (double)f4.y, dot);
+                    dot = __fma_rn(qv[4 * x4 + 2], (double)f4.z, dot);
+                    dot = __fma_rn(qv[4 * x4 + 3], (double)f4.w, dot);
+                }
+            }
             l = __dmul_rn((double)p.scale, dot);
         }
         double mx = l;
