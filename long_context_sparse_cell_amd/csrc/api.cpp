@@ -159,8 +159,12 @@ size_t decode_bytes(const fsl_params *p, int32_t n_seq) {
 // backward workspace: the rotated q and k, the upstream gradient, the long branch's
 // softmax-output gradient, five row statistics and the cells' block ranges
 struct BwdLayout {
-    size_t rope, qr, kr, dO, do_l, lse_w, D_w, lse_l, D_l, dg, crange, status, total;
+    size_t rope, qr, kr, dO, do_l, lse_w, D_w, lse_l, D_l, dg, pkey, pval, pkey2, pval2, shist, stot, cseg, hcount,
+        hitems, hcells, hpart, status, total;
 };
+
+// the long branch's key side sorts the H N K (query, rank) pairs with 32-bit indices
+bool bwd_supported(const KParams &k) { return (int64_t)k.H * k.N * k.K < (int64_t(1) << 31); }
 
 BwdLayout bwd_layout(const KParams &k) {
     BwdLayout L;
@@ -177,7 +181,18 @@ BwdLayout bwd_layout(const KParams &k) {
     L.lse_l = take(rows * sizeof(float));
     L.D_l = take(rows * sizeof(float));
     L.dg = take(rows * sizeof(float));
-    L.crange = take((size_t)k.H * k.C * 2 * sizeof(int32_t));
+    const int64_t npair = (int64_t)k.H * k.N * k.K;
+    L.pkey = take((size_t)npair * sizeof(uint32_t));
+    L.pval = take((size_t)npair * sizeof(uint32_t));
+    L.pkey2 = take((size_t)npair * sizeof(uint32_t));
+    L.pval2 = take((size_t)npair * sizeof(uint32_t));
+    L.shist = take(sort_hist_words(npair) * sizeof(uint32_t));
+    L.stot = take(sort_total_words(npair) * sizeof(uint32_t));
+    L.cseg = take((size_t)k.H * k.C * 2 * sizeof(int32_t));
+    L.hcount = take(2 * sizeof(int32_t));
+    L.hitems = take((size_t)heavy_items_max(k) * 2 * sizeof(int32_t));
+    L.hcells = take((size_t)heavy_cells_max(k) * 3 * sizeof(int32_t));
+    L.hpart = take((size_t)heavy_items_max(k) * 2 * k.s * k.d * sizeof(float));
     L.status = take(sizeof(uint32_t));
     L.total = off;
     return L;
@@ -377,7 +392,9 @@ int fsl_attn_fwd_timed(const void *q, const void *k, const void *v, void *out, c
 
 size_t fsl_attn_bwd_workspace_bytes(const fsl_params *p) {
     if (check(p) != FSL_OK) return 0;
-    return bwd_layout(kparams(p)).total;
+    const KParams k = kparams(p);
+    if (!bwd_supported(k)) return 0;
+    return bwd_layout(k).total;
 }
 
 int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, const fsl_params *p,
@@ -390,6 +407,7 @@ int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, 
         !aligned16(ws) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(dgamma))
         return FSL_E_INVAL;
     const KParams kp = kparams(p);
+    if (!bwd_supported(kp)) return FSL_E_UNSUPPORTED;
     const fsl_workspace_layout FL = layout(kp);
     const BwdLayout BL = bwd_layout(kp);
     if (fwd_ws_bytes < FL.total || ws_bytes < BL.total) return FSL_E_WORKSPACE;
@@ -406,7 +424,17 @@ int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, 
     w.lse_l = (float *)(b + BL.lse_l);
     w.D_l = (float *)(b + BL.D_l);
     w.dg = (float *)(b + BL.dg);
-    w.crange = (int32_t *)(b + BL.crange);
+    w.pkey = (uint32_t *)(b + BL.pkey);
+    w.pval = (uint32_t *)(b + BL.pval);
+    w.pkey2 = (uint32_t *)(b + BL.pkey2);
+    w.pval2 = (uint32_t *)(b + BL.pval2);
+    w.shist = (uint32_t *)(b + BL.shist);
+    w.stot = (uint32_t *)(b + BL.stot);
+    w.cseg = (int32_t *)(b + BL.cseg);
+    w.hcount = (int32_t *)(b + BL.hcount);
+    w.hitems = (int32_t *)(b + BL.hitems);
+    w.hcells = (int32_t *)(b + BL.hcells);
+    w.hpart = (float *)(b + BL.hpart);
     w.status = (uint32_t *)(b + BL.status);
     return hip_status(launch_attn_bwd(q, k, v, dout, (const int32_t *)(f + FL.sel), (const int32_t *)(f + FL.pool), w, dq, dk, dv, dgamma, kp, stream));
 }

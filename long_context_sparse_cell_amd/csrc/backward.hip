@@ -19,8 +19,11 @@
 //                   and dq (window part)
 //   bwd_win_dkv     per 32 keys: dk, dv of the window over the queries that see them
 //   bwd_long_q      per query (one wave): o_long, RMSNorm's backward, dq += long part
-//   bwd_cell_range  first / last block whose pool holds each cell (pruned variant)
-//   bwd_long_kv     per cell: dk, dv += long part over every query that selected it
+//   bwd_pair_keys, a stable radix sort (sort.hip), bwd_seg_*: each cell's
+//                   selecting queries in query order
+//   bwd_long_kv     per cell: dk, dv += long part over every query that selected it;
+//                   cells chosen by more than kHeavyPairs queries in chunks whose
+//                   sums bwd_heavy_reduce adds in chunk order
 //   bwd_dgamma      per head: dgamma summed in a fixed order
 // Arithmetic is fp32 on the vector ALUs with the operand tiles staged in LDS.
 #include <climits>
@@ -414,63 +417,101 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     for (int n = 0; n < NX; ++n) dq[row + lane + 64 * n] += p.scale * acc[n];
 }
 
-// ---- first and last block whose pool holds each cell (pools are ascending runs of
-// cells; a cell enters a block's pool and, once pushed out, never returns)
-__global__ void bwd_range_init_kernel(int32_t *__restrict__ crange, int64_t n) {
+// ---- the (query, rank) pairs as sort keys: key = head * C + cell (or H * C when the
+// rank is empty, which sorts past every cell), value = the query
+__global__ void bwd_pair_keys_kernel(const int32_t *__restrict__ sel, uint32_t *__restrict__ key,
+                                     uint32_t *__restrict__ val, KParams p) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)p.H * p.N * p.K) return;
+    const int64_t hi = e / p.K;  // head * N + query
+    const int32_t c = sel[e];
+    const int64_t h = hi / p.N;
+    key[e] = c >= 0 ? (uint32_t)(h * p.C + c) : (uint32_t)(p.H * p.C);
+    val[e] = (uint32_t)(hi - h * p.N);
+}
+
+// ---- each cell's run [seg[2 c], seg[2 c + 1]) of the sorted pairs (empty: 0, 0); the
+// two work-list counters start at zero
+__global__ void bwd_seg_init_kernel(int32_t *__restrict__ seg, int64_t n, int32_t *__restrict__ counters) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < 2 * n) seg[e] = 0;
+    if (e < 2) counters[e] = 0;
+}
+
+// ---- cells chosen by more than kHeavyPairs queries (a planted needle is chosen by
+// nearly every later query) are split into chunks of kHeavyPairs pairs, one work-group
+// each: items[i] = (cell, chunk), heavy[h] = (cell, first item, chunks). The slots a
+// cell gets depend on the order of the atomics, but its chunks stay consecutive and
+// are summed in chunk order, so results do not.
+__global__ void bwd_heavy_list_kernel(const int32_t *__restrict__ seg, int64_t ncell, int32_t *__restrict__ counters,
+                                      int32_t *__restrict__ items, int32_t *__restrict__ heavy) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= ncell) return;
+    const int32_t cnt = seg[2 * c + 1] - seg[2 * c];
+    if (cnt <= kHeavyPairs) return;
+    const int32_t n = (cnt + kHeavyPairs - 1) / kHeavyPairs;
+    const int32_t base = atomicAdd(&counters[0], n);
+    const int32_t hc = atomicAdd(&counters[1], 1);
+    heavy[3 * hc] = (int32_t)c;
+    heavy[3 * hc + 1] = base;
+    heavy[3 * hc + 2] = n;
+    for (int32_t j = 0; j < n; ++j) {
+        items[2 * (base + j)] = (int32_t)c;
+        items[2 * (base + j) + 1] = j;
+    }
+}
+
+__global__ void bwd_seg_mark_kernel(const uint32_t *__restrict__ key, int64_t n, uint32_t ncell,
+                                    int32_t *__restrict__ seg) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= n) return;
-    crange[2 * e] = INT_MAX;
-    crange[2 * e + 1] = -1;
+    const uint32_t c = key[e];
+    if (c >= ncell) return;
+    if (e == 0 || key[e - 1] != c) seg[2 * (int64_t)c] = (int32_t)e;
+    if (e == n - 1 || key[e + 1] != c) seg[2 * (int64_t)c + 1] = (int32_t)(e + 1);
 }
 
-__global__ void bwd_cell_range_kernel(const int32_t *__restrict__ pool, int32_t *__restrict__ crange, KParams p) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (int64_t)p.H * p.nblk * p.PW) return;
-    const int32_t c = pool[e];
-    if (c < 0 || c >= p.C) return;
-    const int64_t hb = e / p.PW;
-    const int h = (int)(hb / p.nblk);
-    const int32_t b = (int32_t)(hb % p.nblk);
-    atomicMin(&crange[2 * ((int64_t)h * p.C + c)], b);
-    atomicMax(&crange[2 * ((int64_t)h * p.C + c) + 1], b);
-}
-
-// ---- long branch, key side: one work-group per (head, cell). Walks the blocks that
-// may select the cell (the blocks whose pool holds it; without pruning, every block
-// from the first one it is eligible for), lists in query order the queries that
-// selected it, and accumulates their dk, dv terms for the cell's S tokens. Thread t
-// takes token t / TPT and dims (t % TPT) + TPT k.
-template <typename T, int D, int S>
+// ---- long branch, key side. CHUNKS = false: one work-group per (head, cell) with at
+// most kHeavyPairs selectors, adding to dk, dv; CHUNKS = true: one work-group per
+// chunk of a heavier cell, writing its sums to part[item]. Walks the queries that
+// selected the cell, in query order (a stable sort of the pairs by cell), and
+// accumulates their dk, dv terms for the cell's S tokens. Thread t takes token
+// t / TPT and dims (t % TPT) + TPT k.
+template <typename T, int D, int S, bool CHUNKS>
 __global__ __launch_bounds__(kThreads) void bwd_long_kv_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                               const T *__restrict__ v, const int32_t *__restrict__ sel,
+                                                               const T *__restrict__ v, const uint32_t *__restrict__ sq,
+                                                               const int32_t *__restrict__ seg,
+                                                               const int32_t *__restrict__ items,
+                                                               const int32_t *__restrict__ counters,
                                                                const float *__restrict__ do_l,
                                                                const float *__restrict__ lse_l,
                                                                const float *__restrict__ D_l,
-                                                               const int32_t *__restrict__ crange,
                                                                float *__restrict__ dk, float *__restrict__ dv,
-                                                               KParams p) {
+                                                               float *__restrict__ part, KParams p) {
     constexpr int TPT = kThreads / S;  // threads per token
     constexpr int NK = D / TPT;        // dims per thread
     constexpr int G = 8;               // selectors staged per round
-    __shared__ int32_t s_list[256];
-    __shared__ int s_n;
     __shared__ float s_q[G][D], s_do[G][D];
     __shared__ float s_lse[G], s_D[G];
-    const int h = (int)(blockIdx.x / p.C);
-    const int64_t c = blockIdx.x % p.C;
-    const int64_t hN = (int64_t)h * p.N;
-    const int tid = threadIdx.x, lane = tid & 63, sub = tid % TPT;
-    int64_t b0, b1;
-    if (p.P < 0) {
-        // first block b with floor((b B - w + 1) / s) > c
-        const int64_t need = (c + 1) * p.s + p.w - 1;
-        b0 = (need + p.B - 1) / p.B;
-        b1 = p.nblk - 1;
+    int64_t cid;  // head * C + cell
+    int64_t e0, e1;
+    if constexpr (CHUNKS) {
+        if ((int)blockIdx.x >= counters[0]) return;
+        cid = items[2 * blockIdx.x];
+        const int64_t j = items[2 * blockIdx.x + 1];
+        const int64_t a = seg[2 * cid], z = seg[2 * cid + 1];
+        e0 = a + j * kHeavyPairs;
+        e1 = min(z, e0 + kHeavyPairs);
     } else {
-        b0 = crange[2 * ((int64_t)h * p.C + c)];
-        b1 = crange[2 * ((int64_t)h * p.C + c) + 1];
+        cid = blockIdx.x;
+        e0 = seg[2 * cid];
+        e1 = seg[2 * cid + 1];
+        if (e0 >= e1 || e1 - e0 > kHeavyPairs) return;  // never selected, or taken in chunks
     }
-    if (b0 > b1) return;  // never selectable: nothing to add
+    const int h = (int)(cid / p.C);
+    const int64_t c = cid % p.C;
+    const int64_t hN = (int64_t)h * p.N;
+    const int tid = threadIdx.x, sub = tid % TPT;
     const int64_t j = c * S + tid / TPT;
     float kj[NK], vj[NK], acck[NK], accv[NK];
 #pragma unroll
@@ -479,64 +520,79 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kv_kernel(const T *__restri
         vj[n] = ld(v, (hN + j) * D + sub + TPT * n);
         acck[n] = accv[n] = 0.0f;
     }
-    for (int64_t b = b0; b <= b1; ++b) {
-        const int64_t i0 = b * p.B;
-        const int nq = (int)min((int64_t)p.B, p.N - i0);
+    for (int64_t g0 = e0; g0 < e1; g0 += G) {
+        const int ng = (int)min((int64_t)G, e1 - g0);
         __syncthreads();
-        if (tid < 64) {
-            // ordered list of this block's queries that selected c (wave 0, ballots)
-            int base = 0;
-            for (int t0 = 0; t0 < nq; t0 += 64) {
-                const int t = t0 + lane;
-                bool hit = false;
-                if (t < nq)
-                    for (int u = 0; u < p.K; ++u) hit |= sel[(hN + i0 + t) * p.K + u] == (int32_t)c;
-                const uint64_t bal = __ballot(hit);
-                if (hit) s_list[base + __popcll(bal & ((1ull << lane) - 1ull))] = t;
-                base += __popcll(bal);
-            }
-            if (lane == 0) s_n = base;
+        for (int e = tid; e < ng * D; e += kThreads) {
+            const int gg = e / D, x = e % D;
+            const int64_t ii = sq[g0 + gg];
+            s_q[gg][x] = ld(q, (hN + ii) * D + x);
+            s_do[gg][x] = do_l[(hN + ii) * D + x];
+        }
+        if (tid < ng) {
+            const int64_t ii = sq[g0 + tid];
+            s_lse[tid] = lse_l[hN + ii];
+            s_D[tid] = D_l[hN + ii];
         }
         __syncthreads();
-        const int n = s_n;
-        for (int g0 = 0; g0 < n; g0 += G) {
-            const int ng = min(G, n - g0);
-            __syncthreads();
-            for (int e = tid; e < ng * D; e += kThreads) {
-                const int gg = e / D, x = e % D;
-                const int64_t ii = i0 + s_list[g0 + gg];
-                s_q[gg][x] = ld(q, (hN + ii) * D + x);
-                s_do[gg][x] = do_l[(hN + ii) * D + x];
-            }
-            if (tid < ng) {
-                const int64_t ii = i0 + s_list[g0 + tid];
-                s_lse[tid] = lse_l[hN + ii];
-                s_D[tid] = D_l[hN + ii];
-            }
-            __syncthreads();
-            for (int gg = 0; gg < ng; ++gg) {
-                float dot = 0.0f, dp = 0.0f;
+        for (int gg = 0; gg < ng; ++gg) {
+            float dot = 0.0f, dp = 0.0f;
 #pragma unroll
-                for (int nn = 0; nn < NK; ++nn) {
-                    dot += s_q[gg][sub + TPT * nn] * kj[nn];
-                    dp += s_do[gg][sub + TPT * nn] * vj[nn];
-                }
-                dot = group_sum<TPT>(dot);
-                dp = group_sum<TPT>(dp);
-                const float P = __expf(dot * p.scale - s_lse[gg]);
-                const float ds = P * (dp - s_D[gg]);
+            for (int nn = 0; nn < NK; ++nn) {
+                dot += s_q[gg][sub + TPT * nn] * kj[nn];
+                dp += s_do[gg][sub + TPT * nn] * vj[nn];
+            }
+            dot = group_sum<TPT>(dot);
+            dp = group_sum<TPT>(dp);
+            const float P = __expf(dot * p.scale - s_lse[gg]);
+            const float ds = P * (dp - s_D[gg]);
 #pragma unroll
-                for (int nn = 0; nn < NK; ++nn) {
-                    acck[nn] += p.scale * ds * s_q[gg][sub + TPT * nn];
-                    accv[nn] += P * s_do[gg][sub + TPT * nn];
-                }
+            for (int nn = 0; nn < NK; ++nn) {
+                acck[nn] += p.scale * ds * s_q[gg][sub + TPT * nn];
+                accv[nn] += P * s_do[gg][sub + TPT * nn];
             }
         }
     }
+    if constexpr (CHUNKS) {
+        // chunk sums: dk part then dv part, [S][D] each
+        float *dst = part + (int64_t)blockIdx.x * 2 * S * D;
 #pragma unroll
-    for (int n = 0; n < NK; ++n) {
-        dk[(hN + j) * D + sub + TPT * n] += acck[n];
-        dv[(hN + j) * D + sub + TPT * n] += accv[n];
+        for (int n = 0; n < NK; ++n) {
+            dst[(tid / TPT) * D + sub + TPT * n] = acck[n];
+            dst[S * D + (tid / TPT) * D + sub + TPT * n] = accv[n];
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < NK; ++n) {
+            dk[(hN + j) * D + sub + TPT * n] += acck[n];
+            dv[(hN + j) * D + sub + TPT * n] += accv[n];
+        }
+    }
+}
+
+// ---- a heavy cell's chunk sums added to dk, dv in chunk order
+template <int D, int S>
+__global__ __launch_bounds__(kThreads) void bwd_heavy_reduce_kernel(const int32_t *__restrict__ heavy,
+                                                                    const int32_t *__restrict__ counters,
+                                                                    const float *__restrict__ part,
+                                                                    float *__restrict__ dk, float *__restrict__ dv,
+                                                                    KParams p) {
+    if ((int)blockIdx.x >= counters[1]) return;
+    const int64_t cid = heavy[3 * blockIdx.x];
+    const int64_t base = heavy[3 * blockIdx.x + 1];
+    const int n = heavy[3 * blockIdx.x + 2];
+    const int h = (int)(cid / p.C);
+    const int64_t c = cid % p.C;
+    const int64_t t0 = (int64_t)h * p.N + c * S;  // the cell's first token row
+    for (int e = threadIdx.x; e < S * D; e += kThreads) {
+        float sk = 0.0f, sv = 0.0f;
+        for (int jj = 0; jj < n; ++jj) {
+            const float *src = part + (base + jj) * 2 * S * D;
+            sk += src[e];
+            sv += src[S * D + e];
+        }
+        dk[t0 * D + e] += sk;
+        dv[t0 * D + e] += sv;
     }
 }
 
@@ -578,16 +634,31 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
     hipLaunchKernelGGL((bwd_long_q_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, k, v, w.dO, sel, dq, w.do_l,
                        w.lse_l, w.D_l, w.dg, p);
     if (p.C > 0) {
-        if (p.P >= 0) {
-            const int64_t n = (int64_t)p.H * p.C;
-            hipLaunchKernelGGL(bwd_range_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w.crange, n);
-            const int64_t m = (int64_t)p.H * p.nblk * p.PW;
-            if (m > 0)
-                hipLaunchKernelGGL(bwd_cell_range_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, pool,
-                                   w.crange, p);
+        // each cell's selecting queries in query order: a stable sort of the pairs by cell
+        const int64_t npair = (int64_t)p.H * p.N * p.K;
+        const int64_t ncell = (int64_t)p.H * p.C;
+        hipLaunchKernelGGL(bwd_pair_keys_kernel, dim3((unsigned)((npair + 255) / 256)), dim3(256), 0, st, sel,
+                           w.pkey, w.pval, p);
+        bool in_tmp = false;
+        e = launch_sort_pairs(w.pkey, w.pval, w.pkey2, w.pval2, w.shist, w.stot, npair, pair_key_bits(p), &in_tmp,
+                              st);
+        if (e != hipSuccess) return e;
+        const uint32_t *skey = in_tmp ? w.pkey2 : w.pkey, *sval = in_tmp ? w.pval2 : w.pval;
+        hipLaunchKernelGGL(bwd_seg_init_kernel, dim3((unsigned)((2 * ncell + 255) / 256)), dim3(256), 0, st, w.cseg,
+                           ncell, w.hcount);
+        hipLaunchKernelGGL(bwd_seg_mark_kernel, dim3((unsigned)((npair + 255) / 256)), dim3(256), 0, st, skey, npair,
+                           (uint32_t)ncell, w.cseg);
+        hipLaunchKernelGGL(bwd_heavy_list_kernel, dim3((unsigned)((ncell + 255) / 256)), dim3(256), 0, st, w.cseg,
+                           ncell, w.hcount, w.hitems, w.hcells);
+        hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, false>), dim3((unsigned)ncell), dim3(kThreads), 0, st, q, k,
+                           v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, p);
+        const int64_t mi = heavy_items_max(p), mh = heavy_cells_max(p);
+        if (mi > 0) {
+            hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, true>), dim3((unsigned)mi), dim3(kThreads), 0, st, q, k,
+                               v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, p);
+            hipLaunchKernelGGL((bwd_heavy_reduce_kernel<D, S>), dim3((unsigned)mh), dim3(kThreads), 0, st, w.hcells,
+                               w.hcount, w.hpart, dk, dv, p);
         }
-        hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S>), dim3((unsigned)(p.H * p.C)), dim3(kThreads), 0, st, q, k, v,
-                           sel, w.do_l, w.lse_l, w.D_l, w.crange, dk, dv, p);
     }
     hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((unsigned)p.H), dim3(kThreads), 0, st, w.dg, dgamma, p);
     return hipGetLastError();

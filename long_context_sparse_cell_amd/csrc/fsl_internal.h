@@ -448,9 +448,52 @@ struct BwdWork {
     float *do_l;      // [H][N][d] gradient reaching the long branch's softmax output
     float *lse_w, *D_w, *lse_l, *D_l;  // [H][N] row statistics of both branches
     float *dg;        // [H][N] per-query terms of dgamma
-    int32_t *crange;  // [H][C][2] first and last block whose pool holds the cell
+    uint32_t *pkey, *pval, *pkey2, *pval2;  // [H][N][K] (cell, query) pairs and the sort's second buffers
+    uint32_t *shist, *stot;  // radix-sort digit counts and block totals (sort_hist_words, sort_total_words)
+    int32_t *cseg;    // [H][C][2] each cell's run of the pairs sorted by cell
+    int32_t *hcount;  // [2] chunks and cells of the heavy-cell work lists
+    int32_t *hitems;  // [heavy_items_max][2] (cell, chunk)
+    int32_t *hcells;  // [heavy_cells_max][3] (cell, first item, chunks)
+    float *hpart;     // [heavy_items_max][2][s][d] each chunk's dk and dv sums
     uint32_t *status;
 };
+// cells chosen by more than kHeavyPairs queries are processed in chunks of that many
+constexpr int kHeavyPairs = 2048;
+__host__ __device__ inline int64_t heavy_cells_max(const KParams &p) {
+    return (int64_t)p.H * p.N * p.K / (kHeavyPairs + 1);
+}
+__host__ __device__ inline int64_t heavy_items_max(const KParams &p) {
+    // ceil(cnt / kHeavyPairs) < cnt / kHeavyPairs + 1 per heavy cell
+    return (int64_t)p.H * p.N * p.K / kHeavyPairs + heavy_cells_max(p);
+}
+// the stable radix sort (sort.hip): 8-bit digits; chunk histograms stored digit-major
+// and scanned in blocks of kSortScanBlock, whose totals one work-group scans
+constexpr int kSortRadix = 256;
+constexpr int kSortScanBlock = 1024;
+constexpr int kSortScanTopMax = 8192;
+// chunk length (elements) and chunk count for n pairs
+inline void sort_plan(int64_t n, int &chunk, int &nch) {
+    const int64_t max_chunks = (int64_t)kSortScanTopMax * kSortScanBlock / kSortRadix;
+    int64_t c = 1024;
+    while ((n + c - 1) / c > max_chunks) c *= 2;
+    chunk = (int)c;
+    nch = (int)((n + c - 1) / c);
+    if (nch < 1) nch = 1;
+}
+inline size_t sort_hist_words(int64_t n) {
+    int chunk, nch;
+    sort_plan(n, chunk, nch);
+    return (size_t)kSortRadix * nch;
+}
+inline size_t sort_total_words(int64_t n) { return (sort_hist_words(n) + kSortScanBlock - 1) / kSortScanBlock; }
+hipError_t launch_sort_pairs(uint32_t *keys, uint32_t *vals, uint32_t *ktmp, uint32_t *vtmp, uint32_t *hist,
+                             uint32_t *totals, int64_t n, int bits, bool *in_tmp, hipStream_t st);
+// bits of the backward's pair keys, head * C + cell with the sentinel H * C
+__host__ __device__ inline int pair_key_bits(const KParams &p) {
+    int b = 1;
+    while (b < 32 && ((int64_t)1 << b) <= (int64_t)p.H * p.C) ++b;
+    return b;
+}
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const void *dout, const int32_t *sel,
                            const int32_t *pool, const BwdWork &w, float *dq, float *dk, float *dv,
                            float *dgamma, const KParams &p, hipStream_t st);

@@ -100,8 +100,15 @@ static void forward_paths(const fsl_params &p) {
     CHECK(fsl_cell_stats(q, (float *)q, (float *)q, &p, nullptr) == FSL_OK);
     CHECK(fsl_cell_stats(q, nullptr, (float *)q, &p, nullptr) == FSL_E_INVAL);
     CHECK(fsl_attn_fwd_timed(q, q, q, q, &p, fake(ws), n, nullptr, nullptr) == FSL_E_INVAL);
-    // the backward: its own workspace checked by the stand-in, the forward's only by size
+    // the backward: its own workspace checked by the stand-in, the forward's only by size;
+    // unsupported once the H N K (query, rank) pairs exceed 32-bit indices
     const size_t nb = fsl_attn_bwd_workspace_bytes(&p);
+    if ((int64_t)p.H * p.N * p.K >= (int64_t(1) << 31)) {
+        CHECK(nb == 0);
+        CHECK(fsl_attn_bwd(q, q, q, q, &p, fake(ws), n, fake(0x400000), (size_t)1 << 40, (float *)q, (float *)q,
+                           (float *)q, (float *)q, nullptr) == FSL_E_UNSUPPORTED);
+        return;
+    }
     CHECK(nb > 0);
     const uintptr_t bws = (uintptr_t)1 << 45;
     fsl::g_ws_lo = (const char *)bws;

@@ -80,7 +80,10 @@ hipError_t launch_attn_bwd(const void *, const void *, const void *, const void 
     ++g_launches;
     inside(w.rope, "bwd rope"); inside(w.qr, "qr"); inside(w.kr, "kr"); inside(w.dO, "dO"); inside(w.do_l, "do_l");
     inside(w.lse_w, "lse_w"); inside(w.D_w, "D_w"); inside(w.lse_l, "lse_l"); inside(w.D_l, "D_l");
-    inside(w.dg, "dg"); inside(w.crange, "crange"); inside(w.status, "bwd status");
+    inside(w.dg, "dg"); inside(w.pkey, "pkey"); inside(w.pval, "pval"); inside(w.pkey2, "pkey2");
+    inside(w.pval2, "pval2"); inside(w.shist, "shist"); inside(w.stot, "stot"); inside(w.cseg, "cseg");
+    inside(w.hcount, "hcount"); inside(w.hitems, "hitems"); inside(w.hcells, "hcells"); inside(w.hpart, "hpart");
+    inside(w.status, "bwd status");
     return hipSuccess;
 }
 hipError_t launch_fsb_select(const void *, const void *, const float *kbar, const float *amax, int32_t *,
