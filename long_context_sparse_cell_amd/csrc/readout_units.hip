@@ -7,9 +7,9 @@
 // the high-norm cells and all but four of the recent ones), so a span reads
 // each of its cells once for both blocks.
 //
-// readout_plan_kernel lists, per span, every selected cell (a "task") and the
-// (query, rank) pairs that chose it (rank = the cell's position in the query's
-// ascending selection), cut into units of at most 16 pairs. The list is written
+// readout_plan_kernel lists, per span, every selected cell (a "task", in no
+// particular order) and the (query, rank) pairs that chose it (rank = the cell's
+// position in the query's ascending selection), cut into units of at most 16 pairs. The list is written
 // as one record that readout_units_kernel copies into LDS.
 //
 // In readout_units_kernel each wave owns one LDS slot and walks its share of
@@ -31,7 +31,6 @@
 // cells' tokens, then applies RMSNorm and the mix. A query's result depends only
 // on its own cells, each computed the same way whatever the unit's other
 // queries, so the output is deterministic.
-#include <climits>
 
 #include "fsl_internal.h"
 
@@ -67,13 +66,18 @@ constexpr int ru_waves() {
 
 // One work-group per (head, span): the span's selected cells and their
 // (query, rank) pairs, grouped by cell and cut into units of at most 16 pairs.
-// The order of the pairs inside a cell's list does not change any result.
+// Cells are gathered in an LDS hash table (open addressing, at most half full);
+// the order of the tasks, and of the pairs inside a cell's list, depends on the
+// order of the atomics but changes no result: every (query, rank) partial is
+// computed the same way whichever unit or wave computes it.
 __global__ __launch_bounds__(kPlanThreads) void readout_plan_kernel(const int32_t *__restrict__ sel,
                                                                     uint32_t *__restrict__ plan, KParams p, int QR) {
-    __shared__ int s_sort[kPlanMaxPairs];   // selections, sorted; then the cells' pair counters
-    __shared__ int s_cell[kPlanMaxPairs];   // distinct selected cells, ascending
-    __shared__ int s_start[kPlanMaxPairs];  // first pair of each cell
-    __shared__ int s_ncell;
+    constexpr int TAB = 2 * kPlanMaxPairs;   // hash slots
+    constexpr int PER = kPlanMaxPairs / kPlanThreads;  // pairs per thread
+    __shared__ int s_key[TAB];     // cell in the slot, -1 when empty
+    __shared__ int s_cnt[TAB];     // pairs of the slot's cell, then the fill cursor
+    __shared__ int s_start[TAB];   // first pair of the slot's cell
+    __shared__ int s_wsum[kPlanThreads / 64][2];
     const int nspan = (int)((p.N + QR - 1) / QR);
     const int h = (int)blockIdx.x / nspan;
     const int64_t q0 = (int64_t)((int)blockIdx.x % nspan) * QR;
@@ -84,99 +88,102 @@ __global__ __launch_bounds__(kPlanThreads) void readout_plan_kernel(const int32_
     const int32_t *ssel = sel + ((int64_t)h * p.N + q0) * K;
     uint32_t *rec = plan + (int64_t)blockIdx.x * (kPlanRecBytes / 4);
     uint16_t *rpair = reinterpret_cast<uint16_t *>(rec + kPlanPairWord);
+    static_assert(kPlanMaxPairs % kPlanThreads == 0 && TAB % kPlanThreads == 0, "whole per-thread shares");
 
-    for (int t = tid; t < kPlanMaxPairs; t += kPlanThreads) {
-        const int c = t < nent ? ssel[t] : -1;
-        s_sort[t] = c < 0 ? INT_MAX : c;
-    }
-    __syncthreads();
-    for (int len = 2; len <= kPlanMaxPairs; len <<= 1)
-        for (int st = len >> 1; st > 0; st >>= 1) {
-            for (int t = tid; t < kPlanMaxPairs / 2; t += kPlanThreads) {
-                const int lo = 2 * st * (t / st) + (t % st), hi = lo + st;
-                const bool up = (lo & len) == 0;
-                const int a = s_sort[lo], c = s_sort[hi];
-                s_sort[lo] = up ? min(a, c) : max(a, c);
-                s_sort[hi] = up ? max(a, c) : min(a, c);
-            }
-            __syncthreads();
-        }
-    if (wave == 0) {
-        int base = 0;
-        for (int t0 = 0; t0 < kPlanMaxPairs; t0 += 64) {
-            const int t = t0 + lane;
-            const int c = s_sort[t];
-            const bool on = c != INT_MAX && (t == 0 || s_sort[t - 1] != c);
-            const uint64_t bal = __ballot(on);
-            if (on) s_cell[base + __popcll(bal & ((1ull << lane) - 1ull))] = c;
-            base += __popcll(bal);
-        }
-        if (lane == 0) s_ncell = base;
-    }
-    __syncthreads();
-    const int ncell = s_ncell;
-    int *s_cnt = s_sort;  // the sorted copy is no longer needed
-    for (int t = tid; t < ncell; t += kPlanThreads) s_cnt[t] = 0;
-    __syncthreads();
-    auto cell_pos = [&](int c) {
-        int lo = 0, hi = ncell - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (s_cell[mid] < c) lo = mid + 1; else hi = mid;
-        }
-        return lo;
-    };
-    for (int pr = tid; pr < nent; pr += kPlanThreads) {
-        const int c = ssel[pr];
-        if (c >= 0) atomicAdd(&s_cnt[cell_pos(c)], 1);
-    }
-    __syncthreads();
-    if (wave == 0) {
-        // exclusive scans of the pair counts and of the unit counts (ceil(count / 16));
-        // a task is a cell with its units
-        int base = 0, ubase = 0;
-        for (int t0 = 0; t0 < ncell; t0 += 64) {
-            const int t = t0 + lane;
-            const int c = t < ncell ? s_cnt[t] : 0;
-            const int nu = (c + 15) >> 4;
-            int inc = c, uinc = nu;
+    // this thread's pairs tid + kPlanThreads j (all loads in flight at once)
+    int cj[PER];
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int x = __shfl_up(inc, o), y = __shfl_up(uinc, o);
-                if (lane >= o) {
-                    inc += x;
-                    uinc += y;
-                }
-            }
-            const int start = base + inc - c, ustart = ubase + uinc - nu;
-            if (t < ncell) {
-                s_start[t] = start;
-                rec[kPlanTaskWord + 2 * t] = (uint32_t)s_cell[t];
-                rec[kPlanTaskWord + 2 * t + 1] = ((uint32_t)ustart << 16) | (uint32_t)nu;
-                for (int j = 0; j < nu; ++j)
-                    rec[kPlanUnitWord + ustart + j] =
-                        ((uint32_t)(start + 16 * j) << 16) | (uint32_t)min(16, c - 16 * j);
-            }
-            base += __shfl(inc, 63);
-            ubase += __shfl(uinc, 63);
-        }
-        if (lane == 0) {
-            rec[0] = (uint32_t)ncell;
-            rec[1] = (uint32_t)ubase;
-            rec[2] = (uint32_t)base;
-            rec[3] = 0u;
-        }
+    for (int j = 0; j < PER; ++j) {
+        const int pr = tid + kPlanThreads * j;
+        cj[j] = pr < nent ? ssel[pr] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < TAB / kPlanThreads; ++j) {
+        s_key[tid + kPlanThreads * j] = -1;
+        s_cnt[tid + kPlanThreads * j] = 0;
     }
     __syncthreads();
-    for (int t = tid; t < ncell; t += kPlanThreads) s_cnt[t] = 0;
-    __syncthreads();
-    for (int pr = tid; pr < nent; pr += kPlanThreads) {
-        const int c = ssel[pr];
-        if (c >= 0) {
-            const int pos = cell_pos(c);
-            const int at = s_start[pos] + atomicAdd(&s_cnt[pos], 1);
-            rpair[at] = (uint16_t)(((pr / K) << 3) | (pr % K));
+    int slot[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        slot[j] = -1;
+        if (cj[j] < 0) continue;
+        int sl = (int)(((uint32_t)cj[j] * 2654435761u) >> 21) & (TAB - 1);
+        while (true) {
+            const int old = atomicCAS(&s_key[sl], -1, cj[j]);
+            if (old == -1 || old == cj[j]) break;
+            sl = (sl + 1) & (TAB - 1);
         }
+        slot[j] = sl;
+        atomicAdd(&s_cnt[sl], 1);
+    }
+    __syncthreads();
+    // exclusive scans over the slots of (tasks, pairs, units); thread t owns slots
+    // TAB/kPlanThreads t .. + TAB/kPlanThreads - 1
+    constexpr int SPT = TAB / kPlanThreads;
+    int nt = 0, npair = 0, nunit = 0;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int c = s_cnt[SPT * tid + j];
+        nt += c > 0;
+        npair += c;
+        nunit += (c + 15) >> 4;
+    }
+    int it = nt, ip = npair, iu = nunit;  // inclusive scans within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int a = __shfl_up(it, o), b = __shfl_up(ip, o), u = __shfl_up(iu, o);
+        if (lane >= o) {
+            it += a;
+            ip += b;
+            iu += u;
+        }
+    }
+    __shared__ int s_wt[kPlanThreads / 64];
+    if (lane == 63) {
+        s_wt[wave] = it;
+        s_wsum[wave][0] = ip;
+        s_wsum[wave][1] = iu;
+    }
+    __syncthreads();
+    int bt = 0, bp = 0, bu = 0;
+    for (int w2 = 0; w2 < wave; ++w2) {
+        bt += s_wt[w2];
+        bp += s_wsum[w2][0];
+        bu += s_wsum[w2][1];
+    }
+    int tk = bt + it - nt, pk = bp + ip - npair, uk = bu + iu - nunit;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int sl = SPT * tid + j;
+        const int c = s_cnt[sl];
+        if (c == 0) continue;
+        const int nu = (c + 15) >> 4;
+        s_start[sl] = pk;
+        rec[kPlanTaskWord + 2 * tk] = (uint32_t)s_key[sl];
+        rec[kPlanTaskWord + 2 * tk + 1] = ((uint32_t)uk << 16) | (uint32_t)nu;
+        for (int u = 0; u < nu; ++u)
+            rec[kPlanUnitWord + uk + u] = ((uint32_t)(pk + 16 * u) << 16) | (uint32_t)min(16, c - 16 * u);
+        ++tk;
+        pk += c;
+        uk += nu;
+    }
+    if (tid == kPlanThreads - 1) {
+        rec[0] = (uint32_t)tk;
+        rec[1] = (uint32_t)uk;
+        rec[2] = (uint32_t)pk;
+        rec[3] = 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) s_cnt[SPT * tid + j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (slot[j] < 0) continue;
+        const int pr = tid + kPlanThreads * j;
+        const int at = s_start[slot[j]] + atomicAdd(&s_cnt[slot[j]], 1);
+        rpair[at] = (uint16_t)(((pr / K) << 3) | (pr % K));
     }
 }
 
