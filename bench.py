@@ -120,10 +120,14 @@ def algorithmic_work(sh, sel_np=None):
 # factors read off a plain 1 GiB device copy in the same run), for the kernel source they were taken
 # on and the workload they were taken at; reported only for that workload while that source is unchanged.
 TRAFFIC = {
-    "readout_mix": {"bytes": 3193598614, "workload": "fwd_bf16_h8_n262144_d128",
-                    "source": "long_context_sparse_cell_amd/csrc/readout_flash.hip",
-                    "sha256": "1f0f5efc2f73ba2e2f9a2aa9fd48b86e314b1838759cc7256fd2c7e1347465d4",
-                    "profile": "profiles/fwd_n262144_hbm_traffic.md"},
+    "readout": {"bytes": 4283625407, "workload": "fwd_bf16_h8_n262144_d128",
+                "source": "long_context_sparse_cell_amd/csrc/readout_units.hip",
+                "sha256": "67530fe0086f0ef45710561ad92adc5f4d8fd3ab111788e5d88f037858b604af",
+                "profile": "profiles/fwd_n262144_hbm_traffic.md"},
+    "window_mix": {"bytes": 4985320457, "workload": "fwd_bf16_h8_n262144_d128",
+                   "source": "long_context_sparse_cell_amd/csrc/window_bf16.hip",
+                   "sha256": "27b1d6235fc3f1b60f02f940b237fa58825a018a9196bcf2e4e388e368aa2a71",
+                   "profile": "profiles/fwd_n262144_hbm_traffic.md"},
     "decode_step": {"bytes": 191697316, "workload": "decode_bf16_64seq_h16_d64_prefix131072",
                     "source": "long_context_sparse_cell_amd/csrc/decode.hip",
                     "sha256": "f18958cf685d90b25e9ab85b33099e375a5c0adf61f23c1441ebe0535fa3f4b9",
