@@ -161,6 +161,10 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
         const int64_t ks0 = (int64_t)t * kKTile;
         const bool active = qw < p.N && ks0 <= qw + 16 * QT - 1 && ks0 + kKTile - 1 >= qw - p.w + 1;
         if (!active) return;
+        // The MFMA blocks run at raised wave priority, so that a wave which reaches its
+        // products issues them ahead of the other waves' softmax work and the matrix
+        // pipe idles less (measured: 1.23 -> 1.19 ms for the window with its merge).
+        __builtin_amdgcn_s_setprio(1);
         floatx4 sacc[4][QT];
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
@@ -176,6 +180,7 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
                     sacc[kg][qg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka.v, qreg[qg][ks], sacc[kg][qg], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // positions fit in int32 (N < 2^31)
         const int j0 = (int)ks0 + 4 * g;
         const bool edge = !(ks0 + kKTile - 1 <= qw && ks0 > qw + 16 * QT - 1 - p.w);
@@ -221,6 +226,7 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
             }
             l_part[qg] += lsum;
         }
+        __builtin_amdgcn_s_setprio(1);
         // value operand: dimension 16 dt + col, piece g of 32-token group kk
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -234,6 +240,7 @@ __global__ __launch_bounds__(512, 4) void window_bf16_kernel(const uint16_t *__r
                     oacc[qg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va.v, pb[kk][qg].v, oacc[qg][dt], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     issue(t_first, k_lds0, v_lds0);
