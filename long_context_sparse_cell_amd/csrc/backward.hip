@@ -14,10 +14,11 @@
 //
 // Kernels, in launch order on the caller's stream (every one writes its own
 // outputs; nothing is accumulated with atomics, so results are reproducible):
-//   bwd_prep        fp32 rotated q, k and the upstream gradient
-//   bwd_win_dq      per 32 queries: a pass for the row's log-sum-exp and D, then dS
-//                   and dq (window part)
-//   bwd_win_dkv     per 32 keys: dk, dv of the window over the queries that see them
+//   bwd_prep        fp32 rotated q, k, fp32 v and the upstream gradient
+//   bwd_win_dq      per 64 queries: a pass for the row's log-sum-exp and D, then dS
+//                   and dq (window part), on the fp32 matrix cores
+//   bwd_win_dkv     per 64 keys: dk, dv of the window over the queries that see them,
+//                   on the fp32 matrix cores
 //   bwd_long_q      per query (one wave): o_long, RMSNorm's backward, dq += long part
 //   bwd_pair_keys, a stable radix sort (sort.hip), bwd_seg_*: each cell's
 //                   selecting queries in query order
@@ -25,7 +26,8 @@
 //                   cells chosen by more than kHeavyPairs queries in chunks whose
 //                   sums bwd_heavy_reduce adds in chunk order
 //   bwd_dgamma      per head: dgamma summed in a fixed order
-// Arithmetic is fp32 on the vector ALUs with the operand tiles staged in LDS.
+// Arithmetic is fp32: the window's products on the matrix cores (fp32 MFMA), the long
+// branch's on the vector ALUs, operand tiles staged in LDS.
 #include <climits>
 
 #include "fsl_internal.h"
@@ -34,7 +36,7 @@ namespace fsl {
 
 namespace {
 
-constexpr int kBT = 32;        // queries (or keys) per work-group tile
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;  // 8 threads per tile row
 
 template <typename T>
@@ -64,12 +66,13 @@ __device__ __forceinline__ float wave_max(float x) {
 
 }  // namespace
 
-// ---- fp32 rotated q and k (R(t) x, rotate-half pairs) and the upstream gradient
+// ---- fp32 rotated q and k (R(t) x, rotate-half pairs), fp32 v and the upstream gradient
 template <typename T, typename TO, int D>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                            const TO *__restrict__ dout, const float2 *__restrict__ tab,
-                                                            int nhi, float *__restrict__ qr, float *__restrict__ kr,
-                                                            float *__restrict__ dO, KParams p) {
+                                                            const T *__restrict__ v, const TO *__restrict__ dout,
+                                                            const float2 *__restrict__ tab, int nhi,
+                                                            float *__restrict__ qr, float *__restrict__ kr,
+                                                            float *__restrict__ vf, float *__restrict__ dO, KParams p) {
     constexpr int HALF = D / 2;
     const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // one rotation pair
     const int64_t total = (int64_t)p.H * p.N * HALF;
@@ -84,82 +87,204 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const T *__restrict_
     qr[b] = qb * cs.x + qa * cs.y;
     kr[a] = ka * cs.x - kb * cs.y;
     kr[b] = kb * cs.x + ka * cs.y;
+    vf[a] = ld(v, a);
+    vf[b] = ld(v, b);
     dO[a] = ld(dout, a);
     dO[b] = ld(dout, b);
 }
 
-// ---- window, query side. Work-group: 32 queries of one head. Thread t takes row
-// t / 8 and, in score phases, keys 4 (t % 8) .. +3 of the current 32-key tile; in
-// accumulation phases, dims (t % 8) + 8 k of its row.
-// D = dO . o_win is formed as sum_j P_j (dO . v_j), from this pass's own fp32
-// arithmetic: the forward's window output holds fp16-operand rounding that would
-// otherwise enter every dS.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_win_dq_kernel(const float *__restrict__ qr, const float *__restrict__ kr,
-                                                              const T *__restrict__ v, const float *__restrict__ dO,
-                                                              const float2 *__restrict__ tab, int nhi,
-                                                              float *__restrict__ dq, float *__restrict__ lse_w,
-                                                              float *__restrict__ D_w, KParams p) {
-    constexpr int LD = D + 1, HALF = D / 2, NK = D / 8;
-    __shared__ float s_q[kBT * LD], s_do[kBT * LD], s_k[kBT * LD], s_v[kBT * LD];
-    __shared__ float s_ds[kBT][kBT + 1];
-    const int ntile = (int)((p.N + kBT - 1) / kBT);
-    const int h = blockIdx.x / ntile;
-    const int64_t q0 = (int64_t)(blockIdx.x % ntile) * kBT;
+// ---- window branch on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane (c, g)
+// holds A[c][g] and B[g][c]; accumulator element r holds D[4 g + r][c]). The d
+// dimensions of a product are summed in the order in which lane group g holds
+// dims (d/4) g .. (d/4) g + d/4 - 1, so that a lane's operands are one contiguous
+// quarter of a row. The other side's rows wait in LDS as fp32 tiles of kWinTile
+// rows whose 16-byte chunk c sits at c ^ (row & 15) (global_load_lds,
+// double-buffered); products whose k dimension is the tile row read one float per
+// lane from those tiles.
+namespace {
+constexpr int kWinWaves = 4;                 // waves per work-group, 16 rows each
+constexpr int kWinRows = 16 * kWinWaves;     // this side's rows per work-group
+constexpr int kWinTile = 32;                 // other side's rows per LDS tile
+
+template <int D>
+__device__ __forceinline__ int wtile_off(int row, int chunk) { return row * D + 4 * (chunk ^ (row & 15)); }
+
+// rows r0 .. r0 + kWinTile - 1 of one head's [N][D] fp32 array into a swizzled tile
+// (rows past N repeat row N - 1; every product they enter is masked)
+template <int D>
+__device__ __forceinline__ void wtile_issue(const float *src_head, int64_t r0, int64_t N, float *tile, int wave,
+                                            int lane) {
+    constexpr int CPR = D / 4;
+    constexpr int UNITS = kWinTile * D * 4 / 1024;
+    static_assert(UNITS % kWinWaves == 0, "whole copy units per wave");
+#pragma unroll
+    for (int i = 0; i < UNITS / kWinWaves; ++i) {
+        const int u = wave + kWinWaves * i;
+        const int c = 64 * u + lane;  // 16-byte chunk of the tile
+        const int row = c / CPR, phys = c % CPR;
+        const int64_t rr = min(r0 + row, N - 1);
+        lds_dma16(src_head + rr * D + 4 * (phys ^ (row & 15)), tile + 256 * u);
+    }
+}
+
+// acc (rows 4 g + r of a 16-row block, column c) += tile rows `rowbase` .. + 15 as A
+// times the lane's register operand b[] (its column's dims (d/4) g ..) over d
+template <int D>
+__device__ __forceinline__ floatx4 wtile_dot(const float *tile, int rowbase, int col, int g, const float *b) {
+    constexpr int KS = D / 4;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KS / 4; ++c) {
+        const float4 a = *reinterpret_cast<const float4 *>(&tile[wtile_off<D>(rowbase + col, KS / 4 * g + c)]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b[4 * c + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b[4 * c + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b[4 * c + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b[4 * c + 3], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// acc[dt] (dims 16 dt + 4 g + r, column c) += sum over tile rows rowbase .. + 15 of
+// tile[row][dim] w(row, c), with w(rowbase + 4 g + r, c) = w[r] held by lane (c, g)
+template <int D>
+__device__ __forceinline__ void wtile_tmul(const float *tile, int rowbase, int col, int g, const float *w,
+                                           floatx4 *acc) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = rowbase + 4 * g + r;
+            const float a = tile[wtile_off<D>(row, 4 * dt + (col >> 2)) + (col & 3)];
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, w[r], acc[dt], 0, 0, 0);
+        }
+}
+
+// a row's fp32 values at dims (d/4) g .. (d/4) g + d/4 - 1
+template <int D>
+__device__ __forceinline__ void wrow_quarter(const float *row, int g, float *dst) {
+    constexpr int KS = D / 4;
+#pragma unroll
+    for (int c = 0; c < KS / 4; ++c) {
+        const float4 x = *reinterpret_cast<const float4 *>(row + KS * g + 4 * c);
+        dst[4 * c] = x.x;
+        dst[4 * c + 1] = x.y;
+        dst[4 * c + 2] = x.z;
+        dst[4 * c + 3] = x.w;
+    }
+}
+
+// x = R(t)^T scale acc for the lane's dims 16 dt + 4 g + r (rotate-half pairs dt and
+// dt + D/32 are both the lane's), written as float4 rows
+template <int D>
+__device__ __forceinline__ void wstore_rotated(float *dst_row, const floatx4 *acc, const float2 *tab, int nhi,
+                                               int64_t t, int g, float scale) {
+    constexpr int HALF = D / 2;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        float lo[4], hi[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int x = 16 * dt + 4 * g + r;
+            const float2 cs = rope_cs(tab, nhi, HALF, t, x);
+            const float a = scale * acc[dt][r], b = scale * acc[dt + D / 32][r];
+            lo[r] = a * cs.x + b * cs.y;
+            hi[r] = b * cs.x - a * cs.y;
+        }
+        *reinterpret_cast<float4 *>(dst_row + 16 * dt + 4 * g) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<float4 *>(dst_row + HALF + 16 * dt + 4 * g) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+    }
+}
+}  // namespace
+
+// ---- window, query side. Work-group: 64 queries of one head, 16 per wave (one per
+// lane column), over 32-key tiles. S^T = K Q^T and dP^T = V dO^T put keys 4 g + r of
+// query c in lane (c, g). Pass A: the row's log-sum-exp and D = sum_j P_j (dO . v_j)
+// (from this pass's own fp32 arithmetic: the forward's window output holds
+// fp16-operand rounding that would otherwise enter every dS). Pass B: dS, and
+// dq^T += K^T dS^T with dS^T straight from the accumulator layout.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_win_dq_kernel(const float *__restrict__ qr,
+                                                            const float *__restrict__ kr,
+                                                            const float *__restrict__ vf,
+                                                            const float *__restrict__ dO,
+                                                            const float2 *__restrict__ tab, int nhi,
+                                                            float *__restrict__ dq, float *__restrict__ lse_w,
+                                                            float *__restrict__ D_w, KParams p) {
+    constexpr int KS = D / 4;
+    __shared__ __attribute__((aligned(1024))) float s_k0[kWinTile * D];
+    __shared__ __attribute__((aligned(1024))) float s_k1[kWinTile * D];
+    __shared__ __attribute__((aligned(1024))) float s_v0[kWinTile * D];
+    __shared__ __attribute__((aligned(1024))) float s_v1[kWinTile * D];
+    const int ntile = (int)((p.N + kWinRows - 1) / kWinRows);
+    const int logical = xcd_remap((int)blockIdx.x, ntile * p.H);
+    const int h = logical / ntile;
+    const int64_t q0 = (int64_t)(logical % ntile) * kWinRows;
     const int64_t hN = (int64_t)h * p.N;
-    const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7, c4 = 4 * sub;
-    const int64_t i = q0 + r;
-    for (int e = tid; e < kBT * D; e += kThreads) {
-        const int rr = e / D, x = e % D;
-        const int64_t ii = q0 + rr;
-        s_q[rr * LD + x] = ii < p.N ? qr[(hN + ii) * D + x] : 0.0f;
-        s_do[rr * LD + x] = ii < p.N ? dO[(hN + ii) * D + x] : 0.0f;
+    const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t qw = q0 + 16 * wave;
+    const int64_t i = qw + col;
+    float qb[KS], ob[KS];
+    {
+        const int64_t ic = min(i, p.N - 1);
+        wrow_quarter<D>(qr + (hN + ic) * D, g, qb);
+        wrow_quarter<D>(dO + (hN + ic) * D, g, ob);
     }
     const int64_t kmin = max((int64_t)0, q0 - p.w + 1);
-    const int64_t kmax = min(p.N, q0 + kBT) - 1;
-    const int64_t t0 = kmin / kBT * kBT;
-    auto load_tile = [&](float *dst, const float *src, int64_t ks0) {
-        for (int e = tid; e < kBT * D; e += kThreads) {
-            const int rr = e / D, x = e % D;
-            const int64_t j = ks0 + rr;
-            dst[rr * LD + x] = j < p.N ? src[(hN + j) * D + x] : 0.0f;
+    const int64_t kmax = min(p.N, q0 + kWinRows) - 1;
+    const int t_first = (int)(kmin / kWinTile), t_last = (int)(kmax / kWinTile);
+    const float *kh = kr + hN * D, *vh = vf + hN * D;
+    auto issue = [&](int t, float *kb, float *vb) __attribute__((always_inline)) {
+        wtile_issue<D>(kh, (int64_t)t * kWinTile, p.N, kb, wave, lane);
+        wtile_issue<D>(vh, (int64_t)t * kWinTile, p.N, vb, wave, lane);
+    };
+    // a 16-key block holds a key of one of this wave's windows
+    auto block_live = [&](int64_t kb0) __attribute__((always_inline)) {
+        return qw < p.N && kb0 <= qw + 15 && kb0 + 15 > qw - p.w;
+    };
+    auto valid = [&](int64_t j) __attribute__((always_inline)) { return i < p.N && j <= i && j > i - p.w; };
+    // every tile, double-buffered; body(t, keys, values)
+    auto sweep = [&](auto &&body) __attribute__((always_inline)) {
+        issue(t_first, s_k0, s_v0);
+        wait_vmem();
+        __syncthreads();
+        for (int t = t_first; t <= t_last; t += 2) {
+            if (t + 1 <= t_last) issue(t + 1, s_k1, s_v1);
+            body(t, s_k0, s_v0);
+            wait_vmem();
+            __syncthreads();
+            if (t + 1 > t_last) break;
+            if (t + 2 <= t_last) issue(t + 2, s_k0, s_v0);
+            body(t + 1, s_k1, s_v1);
+            wait_vmem();
+            __syncthreads();
         }
     };
-    auto valid = [&](int64_t j) { return i < p.N && j <= i && j > i - p.w; };
-    auto load_v = [&](int64_t ks0) {
-        for (int e = tid; e < kBT * D; e += kThreads) {
-            const int rr = e / D, x = e % D;
-            const int64_t j = ks0 + rr;
-            s_v[rr * LD + x] = j < p.N ? ld(v, (hN + j) * D + x) : 0.0f;
-        }
-    };
-    // pass A: the row's log-sum-exp, and a = sum_j exp(l_j - m) (dO . v_j) with the
-    // same running maximum, so that D = a / sum_j exp(l_j - m)
+
+    // pass A: each lane runs (max, sum, weighted dP) over its keys, then the four
+    // lanes of a query merge theirs
     float m = -INFINITY, l = 0.0f, a = 0.0f;
-    for (int64_t ks0 = t0; ks0 <= kmax; ks0 += kBT) {
-        __syncthreads();
-        load_tile(s_k, kr, ks0);
-        load_v(ks0);
-        __syncthreads();
+    sweep([&](int t, const float *kb, const float *vb) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t j = ks0 + c4 + u;
-            if (!valid(j)) continue;
-            float dot = 0.0f, dp = 0.0f;
-            for (int x = 0; x < D; ++x) {
-                dot += s_q[r * LD + x] * s_k[(c4 + u) * LD + x];
-                dp += s_do[r * LD + x] * s_v[(c4 + u) * LD + x];
+        for (int kk = 0; kk < kWinTile / 16; ++kk) {
+            const int64_t kb0 = (int64_t)t * kWinTile + 16 * kk;
+            if (!block_live(kb0)) continue;
+            const floatx4 sv = wtile_dot<D>(kb, 16 * kk, col, g, qb);
+            const floatx4 dp = wtile_dot<D>(vb, 16 * kk, col, g, ob);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (!valid(kb0 + 4 * g + r)) continue;
+                const float sc = sv[r] * p.scale;
+                const float mn = fmaxf(m, sc);
+                const float alpha = __expf(m - mn), e = __expf(sc - mn);
+                l = l * alpha + e;
+                a = a * alpha + e * dp[r];
+                m = mn;
             }
-            const float sc = dot * p.scale;
-            const float mn = fmaxf(m, sc);
-            const float alpha = __expf(m - mn), e = __expf(sc - mn);
-            l = l * alpha + e;
-            a = a * alpha + e * dp;
-            m = mn;
         }
-    }
+    });
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
+    for (int o = 16; o < 64; o <<= 1) {
         const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o), a2 = __shfl_xor(a, o);
         const float mn = fmaxf(m, m2);
         const float f1 = m == -INFINITY ? 0.0f : __expf(m - mn);
@@ -170,136 +295,126 @@ __global__ __launch_bounds__(kThreads) void bwd_win_dq_kernel(const float *__res
     }
     const float lse = m + __logf(l);
     const float Dr = l > 0.0f ? a / l : 0.0f;
-    // pass B: dS and the rotated query gradient
-    float acc[NK];
+
+    // pass B: dS^T and dq^T += K^T dS^T
+    floatx4 acc[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) acc[kk] = 0.0f;
-    for (int64_t ks0 = t0; ks0 <= kmax; ks0 += kBT) {
-        __syncthreads();
-        load_tile(s_k, kr, ks0);
-        load_v(ks0);
-        __syncthreads();
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    sweep([&](int t, const float *kb, const float *vb) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t j = ks0 + c4 + u;
-            float ds = 0.0f;
-            if (valid(j)) {
-                float dot = 0.0f, dp = 0.0f;
-                for (int x = 0; x < D; ++x) {
-                    dot += s_q[r * LD + x] * s_k[(c4 + u) * LD + x];
-                    dp += s_do[r * LD + x] * s_v[(c4 + u) * LD + x];
-                }
-                const float P = __expf(dot * p.scale - lse);
-                ds = P * (dp - Dr);
+        for (int kk = 0; kk < kWinTile / 16; ++kk) {
+            const int64_t kb0 = (int64_t)t * kWinTile + 16 * kk;
+            if (!block_live(kb0)) continue;
+            const floatx4 sv = wtile_dot<D>(kb, 16 * kk, col, g, qb);
+            const floatx4 dp = wtile_dot<D>(vb, 16 * kk, col, g, ob);
+            float ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float P = valid(kb0 + 4 * g + r) ? __expf(sv[r] * p.scale - lse) : 0.0f;
+                ds[r] = P * (dp[r] - Dr);
             }
-            s_ds[r][c4 + u] = ds;
+            wtile_tmul<D>(kb, 16 * kk, col, g, ds, acc);
         }
-        __syncthreads();
-        for (int jj = 0; jj < kBT; ++jj) {
-            const float dsv = s_ds[r][jj];
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) acc[kk] += dsv * s_k[jj * LD + sub + 8 * kk];
-        }
-    }
+    });
     if (i >= p.N) return;
-    // dq = R(i)^T (scale acc): dims x = sub + 8 kk and x + D/2 are both this thread's
-#pragma unroll
-    for (int kk = 0; kk < NK / 2; ++kk) {
-        const int x = sub + 8 * kk;
-        const float2 cs = rope_cs(tab, nhi, HALF, i, x);
-        const float a = p.scale * acc[kk], b = p.scale * acc[kk + NK / 2];
-        dq[(hN + i) * D + x] = a * cs.x + b * cs.y;
-        dq[(hN + i) * D + x + HALF] = b * cs.x - a * cs.y;
-    }
-    if (sub == 0) {
+    // dq = R(i)^T (scale acc)
+    wstore_rotated<D>(dq + (hN + i) * D, acc, tab, nhi, i, g, p.scale);
+    if (g == 0) {
         lse_w[hN + i] = lse;
         D_w[hN + i] = Dr;
     }
 }
 
-// ---- window, key side. Work-group: 32 keys of one head, over every query tile
-// whose window holds one of them. Thread t takes key t / 8 and queries
-// 4 (t % 8) .. +3 of the current query tile, then dims (t % 8) + 8 k of its key.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_win_dkv_kernel(const float *__restrict__ qr,
-                                                               const float *__restrict__ kr, const T *__restrict__ v,
-                                                               const float *__restrict__ dO,
-                                                               const float *__restrict__ lse_w,
-                                                               const float *__restrict__ D_w,
-                                                               const float2 *__restrict__ tab, int nhi,
-                                                               float *__restrict__ dk, float *__restrict__ dv,
-                                                               KParams p) {
-    constexpr int LD = D + 1, HALF = D / 2, NK = D / 8;
-    __shared__ float s_k[kBT * LD], s_v[kBT * LD], s_q[kBT * LD], s_do[kBT * LD];
-    __shared__ float s_p[kBT][kBT + 1], s_ds[kBT][kBT + 1];
-    __shared__ float s_lse[kBT], s_D[kBT];
-    const int ntile = (int)((p.N + kBT - 1) / kBT);
-    const int h = blockIdx.x / ntile;
-    const int64_t k0 = (int64_t)(blockIdx.x % ntile) * kBT;
+// ---- window, key side. Work-group: 64 keys of one head, 16 per wave (one per lane
+// column), over the 32-query tiles whose windows hold them. S = Q K^T and
+// dP = dO V^T put queries 4 g + r of key c in lane (c, g); dv^T += dO^T P and
+// dk^T += Q^T dS take P and dS straight from the accumulator layout.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_win_dkv_kernel(const float *__restrict__ qr,
+                                                             const float *__restrict__ kr,
+                                                             const float *__restrict__ vf,
+                                                             const float *__restrict__ dO,
+                                                             const float *__restrict__ lse_w,
+                                                             const float *__restrict__ D_w,
+                                                             const float2 *__restrict__ tab, int nhi,
+                                                             float *__restrict__ dk, float *__restrict__ dv,
+                                                             KParams p) {
+    constexpr int KS = D / 4;
+    __shared__ __attribute__((aligned(1024))) float s_q0[kWinTile * D];
+    __shared__ __attribute__((aligned(1024))) float s_q1[kWinTile * D];
+    __shared__ __attribute__((aligned(1024))) float s_o0[kWinTile * D];
+    __shared__ __attribute__((aligned(1024))) float s_o1[kWinTile * D];
+    const int ntile = (int)((p.N + kWinRows - 1) / kWinRows);
+    const int logical = xcd_remap((int)blockIdx.x, ntile * p.H);
+    const int h = logical / ntile;
+    const int64_t k0 = (int64_t)(logical % ntile) * kWinRows;
     const int64_t hN = (int64_t)h * p.N;
-    const int tid = threadIdx.x, r = tid >> 3, sub = tid & 7, c4 = 4 * sub;
-    const int64_t j = k0 + r;
-    for (int e = tid; e < kBT * D; e += kThreads) {
-        const int rr = e / D, x = e % D;
-        const int64_t jj = k0 + rr;
-        s_k[rr * LD + x] = jj < p.N ? kr[(hN + jj) * D + x] : 0.0f;
-        s_v[rr * LD + x] = jj < p.N ? ld(v, (hN + jj) * D + x) : 0.0f;
+    const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t kw = k0 + 16 * wave;
+    const int64_t j = kw + col;
+    float kb[KS], vb[KS];
+    {
+        const int64_t jc = min(j, p.N - 1);
+        wrow_quarter<D>(kr + (hN + jc) * D, g, kb);
+        wrow_quarter<D>(vf + (hN + jc) * D, g, vb);
     }
-    float acck[NK], accv[NK];
+    // queries whose windows hold one of these keys: k0 .. k0 + 63 + w - 1
+    const int64_t qmax = min(p.N, k0 + kWinRows + (int64_t)p.w - 1) - 1;
+    const int t_first = (int)(k0 / kWinTile), t_last = (int)(qmax / kWinTile);
+    const float *qh = qr + hN * D, *oh = dO + hN * D;
+    auto issue = [&](int t, float *qt, float *ot) __attribute__((always_inline)) {
+        wtile_issue<D>(qh, (int64_t)t * kWinTile, p.N, qt, wave, lane);
+        wtile_issue<D>(oh, (int64_t)t * kWinTile, p.N, ot, wave, lane);
+    };
+    // a 16-query block holds a query whose window holds one of this wave's keys
+    auto block_live = [&](int64_t qb0) __attribute__((always_inline)) {
+        return kw < p.N && qb0 < p.N && qb0 + 15 >= kw && qb0 <= kw + 15 + p.w - 1;
+    };
+    floatx4 acck[D / 16], accv[D / 16];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) acck[kk] = accv[kk] = 0.0f;
-    const int64_t qmax = min(p.N - 1, k0 + kBT - 1 + (int64_t)p.w - 1);
-    for (int64_t qs0 = k0; qs0 <= qmax; qs0 += kBT) {
-        __syncthreads();
-        for (int e = tid; e < kBT * D; e += kThreads) {
-            const int rr = e / D, x = e % D;
-            const int64_t ii = qs0 + rr;
-            s_q[rr * LD + x] = ii < p.N ? qr[(hN + ii) * D + x] : 0.0f;
-            s_do[rr * LD + x] = ii < p.N ? dO[(hN + ii) * D + x] : 0.0f;
-        }
-        if (tid < kBT) {
-            const int64_t ii = qs0 + tid;
-            s_lse[tid] = ii < p.N ? lse_w[hN + ii] : 0.0f;
-            s_D[tid] = ii < p.N ? D_w[hN + ii] : 0.0f;
-        }
-        __syncthreads();
+    for (int dt = 0; dt < D / 16; ++dt) acck[dt] = accv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto body = [&](int t, const float *qt, const float *ot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t i = qs0 + c4 + u;
-            float P = 0.0f, ds = 0.0f;
-            if (j < p.N && i < p.N && j <= i && j > i - p.w) {
-                float dot = 0.0f, dp = 0.0f;
-                for (int x = 0; x < D; ++x) {
-                    dot += s_q[(c4 + u) * LD + x] * s_k[r * LD + x];
-                    dp += s_do[(c4 + u) * LD + x] * s_v[r * LD + x];
-                }
-                P = __expf(dot * p.scale - s_lse[c4 + u]);
-                ds = P * (dp - s_D[c4 + u]);
+        for (int qq = 0; qq < kWinTile / 16; ++qq) {
+            const int64_t qb0 = (int64_t)t * kWinTile + 16 * qq;
+            if (!block_live(qb0)) continue;
+            const floatx4 sv = wtile_dot<D>(qt, 16 * qq, col, g, kb);
+            const floatx4 dp = wtile_dot<D>(ot, 16 * qq, col, g, vb);
+            float P[4], ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t ii = qb0 + 4 * g + r;
+                const bool ok = j < p.N && ii < p.N && j <= ii && j > ii - p.w;
+                const int64_t ic = min(ii, p.N - 1);
+                const float pr = ok ? __expf(sv[r] * p.scale - lse_w[hN + ic]) : 0.0f;
+                P[r] = pr;
+                ds[r] = ok ? pr * (dp[r] - D_w[hN + ic]) : 0.0f;
             }
-            s_p[r][c4 + u] = P;
-            s_ds[r][c4 + u] = ds;
+            wtile_tmul<D>(ot, 16 * qq, col, g, P, accv);
+            wtile_tmul<D>(qt, 16 * qq, col, g, ds, acck);
         }
+    };
+    issue(t_first, s_q0, s_o0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = t_first; t <= t_last; t += 2) {
+        if (t + 1 <= t_last) issue(t + 1, s_q1, s_o1);
+        body(t, s_q0, s_o0);
+        wait_vmem();
         __syncthreads();
-        for (int ii = 0; ii < kBT; ++ii) {
-            const float pv = s_p[r][ii], dsv = s_ds[r][ii];
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                acck[kk] += dsv * s_q[ii * LD + sub + 8 * kk];
-                accv[kk] += pv * s_do[ii * LD + sub + 8 * kk];
-            }
-        }
+        if (t + 1 > t_last) break;
+        if (t + 2 <= t_last) issue(t + 2, s_q0, s_o0);
+        body(t + 1, s_q1, s_o1);
+        wait_vmem();
+        __syncthreads();
     }
     if (j >= p.N) return;
+    wstore_rotated<D>(dk + (hN + j) * D, acck, tab, nhi, j, g, p.scale);
 #pragma unroll
-    for (int kk = 0; kk < NK / 2; ++kk) {
-        const int x = sub + 8 * kk;
-        const float2 cs = rope_cs(tab, nhi, HALF, j, x);
-        const float a = p.scale * acck[kk], b = p.scale * acck[kk + NK / 2];
-        dk[(hN + j) * D + x] = a * cs.x + b * cs.y;
-        dk[(hN + j) * D + x + HALF] = b * cs.x - a * cs.y;
-    }
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) dv[(hN + j) * D + sub + 8 * kk] = accv[kk];
+    for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<float4 *>(dv + (hN + j) * D + 16 * dt + 4 * g) =
+            make_float4(accv[dt][0], accv[dt][1], accv[dt][2], accv[dt][3]);
 }
 
 // ---- long branch, query side: one wave per query (4 per work-group). Recomputes the
@@ -623,13 +738,16 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
     hipError_t e = launch_rope_abs_table(w.rope, w.status, p, st);
     if (e != hipSuccess) return e;
     const int64_t pairs = (int64_t)p.H * p.N * (D / 2);
+    // the window kernels read fp32 values from do_l's storage, which the long branch's
+    // query kernel fills only after them
+    float *vf = w.do_l;
     hipLaunchKernelGGL((bwd_prep_kernel<T, TO, D>), dim3((unsigned)((pairs + kThreads - 1) / kThreads)), dim3(kThreads),
-                       0, st, q, k, dout, w.rope, nhi, w.qr, w.kr, w.dO, p);
-    const unsigned tiles = (unsigned)(((p.N + kBT - 1) / kBT) * p.H);
-    hipLaunchKernelGGL((bwd_win_dq_kernel<T, D>), dim3(tiles), dim3(kThreads), 0, st, w.qr, w.kr, v, w.dO,
-                       w.rope, nhi, dq, w.lse_w, w.D_w, p);
-    hipLaunchKernelGGL((bwd_win_dkv_kernel<T, D>), dim3(tiles), dim3(kThreads), 0, st, w.qr, w.kr, v, w.dO, w.lse_w,
-                       w.D_w, w.rope, nhi, dk, dv, p);
+                       0, st, q, k, v, dout, w.rope, nhi, w.qr, w.kr, vf, w.dO, p);
+    const unsigned tiles = (unsigned)(((p.N + kWinRows - 1) / kWinRows) * p.H);
+    hipLaunchKernelGGL((bwd_win_dq_kernel<D>), dim3(tiles), dim3(256), 0, st, w.qr, w.kr, vf, w.dO, w.rope, nhi, dq,
+                       w.lse_w, w.D_w, p);
+    hipLaunchKernelGGL((bwd_win_dkv_kernel<D>), dim3(tiles), dim3(256), 0, st, w.qr, w.kr, vf, w.dO, w.lse_w, w.D_w,
+                       w.rope, nhi, dk, dv, p);
     const unsigned qw = (unsigned)(((p.N + 3) / 4) * p.H);
     hipLaunchKernelGGL((bwd_long_q_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, k, v, w.dO, sel, dq, w.do_l,
                        w.lse_l, w.D_l, w.dg, p);
