@@ -420,7 +420,42 @@ __global__ __launch_bounds__(256, 2) void bwd_win_dkv_kernel(const float *__rest
 // ---- long branch, query side: one wave per query (4 per work-group). Recomputes the
 // branch's softmax over the selected cells' tokens, o_long and RMSNorm's backward;
 // writes the gradient reaching the softmax output (do_l), the row's lse and D, the
-// query's dgamma term, and adds the branch's part of dq.
+// query's dgamma term, and adds the branch's part of dq. Dot products with token
+// rows (scores, dO . v_t) read whole rows per instruction: 16 bytes per lane, the
+// lanes of one row summing their parts; sums over tokens (o, dq) give each lane
+// NX = d/64 consecutive dims.
+namespace {
+// the 16 bytes at p as floats (8 bf16 or 4 fp32)
+template <typename T> __device__ __forceinline__ void ld16f(const T *p, float *dst);
+template <> __device__ __forceinline__ void ld16f<uint16_t>(const uint16_t *p, float *dst) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = __uint_as_float(w[e] << 16);
+        dst[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+}
+template <> __device__ __forceinline__ void ld16f<float>(const float *p, float *dst) {
+    const float4 f = *reinterpret_cast<const float4 *>(p);
+    dst[0] = f.x; dst[1] = f.y; dst[2] = f.z; dst[3] = f.w;
+}
+// NX (1 or 2) consecutive elements at p as floats
+template <typename T, int NX> __device__ __forceinline__ void ldnx(const T *p, float *dst) {
+    if constexpr (NX == 2 && sizeof(T) == 2) {
+        const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+        dst[0] = __uint_as_float(u << 16);
+        dst[1] = __uint_as_float(u & 0xFFFF0000u);
+    } else if constexpr (NX == 2) {
+        const float2 f = *reinterpret_cast<const float2 *>(p);
+        dst[0] = f.x;
+        dst[1] = f.y;
+    } else {
+        dst[0] = to_f32<T>(p[0]);
+    }
+}
+}  // namespace
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                               const T *__restrict__ v, const float *__restrict__ dO,
@@ -428,9 +463,12 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
                                                               float *__restrict__ do_l, float *__restrict__ lse_l,
                                                               float *__restrict__ D_l, float *__restrict__ dg,
                                                               KParams p) {
-    constexpr int NX = D / 64;          // dims per lane
-    constexpr int MAXT = 8 * 64;        // K * s at most
-    __shared__ float s_q[4][D], s_d[4][D];
+    constexpr int NX = D / 64;             // consecutive dims per lane in sums over tokens
+    constexpr int VEC = 16 / sizeof(T);    // elements per lane in row dot products
+    constexpr int LPR = D / VEC;           // lanes per row
+    constexpr int RPI = 64 / LPR;          // rows per wave instruction
+    constexpr int MAXT = 8 * 64;           // K * s at most
+    __shared__ float s_d[4][D];
     __shared__ float s_s[4][MAXT];
     __shared__ int64_t s_tok[4][MAXT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -444,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     for (int u = 0; u < p.K; ++u) {
         const int32_t c = sel[(hN + i) * p.K + u];
         if (c < 0) continue;
-        for (int t = lane; t < p.s; t += 64) s_tok[wave][ntok + t] = (int64_t)c * p.s + t;
+        for (int t = lane; t < p.s; t += 64) s_tok[wave][ntok + t] = hN + (int64_t)c * p.s + t;
         ntok += p.s;
     }
     if (ntok == 0) {
@@ -452,36 +490,49 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
         if (lane == 0) { lse_l[hN + i] = 0.0f; D_l[hN + i] = 0.0f; dg[hN + i] = 0.0f; }
         return;
     }
-    for (int x = lane; x < D; x += 64) s_q[wave][x] = ld(q, row + x);
     __builtin_amdgcn_wave_barrier();
-    // scores
+    const int rsub = lane / LPR, rpart = lane % LPR;  // row of the instruction, 16-byte part of it
+    // scores: row dot products, the LPR lanes of a row summing their VEC products
+    float qv[VEC];
+    ld16f<T>(q + row + VEC * rpart, qv);
     float mx = -INFINITY;
-    for (int t = lane; t < ntok; t += 64) {
-        const int64_t kb = (hN + s_tok[wave][t]) * D;
+#pragma unroll 8
+    for (int t0 = 0; t0 < ntok; t0 += RPI) {
+        const int t = t0 + rsub;
+        const int64_t tok = s_tok[wave][min(t, ntok - 1)];
+        float kv[VEC];
+        ld16f<T>(k + tok * D + VEC * rpart, kv);
         float dot = 0.0f;
-        for (int x = 0; x < D; ++x) dot += s_q[wave][x] * ld(k, kb + x);
-        s_s[wave][t] = dot * p.scale;
-        mx = fmaxf(mx, dot * p.scale);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dot += qv[e] * kv[e];
+        dot = group_sum<LPR>(dot);
+        if (t < ntok) {
+            if (rpart == 0) s_s[wave][t] = dot * p.scale;
+            mx = fmaxf(mx, dot * p.scale);
+        }
     }
     mx = wave_max(mx);
+    __builtin_amdgcn_wave_barrier();
     float sum = 0.0f;
     for (int t = lane; t < ntok; t += 64) sum += __expf(s_s[wave][t] - mx);
     sum = wave_sum(sum);
     const float lse = mx + __logf(sum);
     for (int t = lane; t < ntok; t += 64) s_s[wave][t] = __expf(s_s[wave][t] - lse);  // P_t
     __builtin_amdgcn_wave_barrier();
-    // o_long, RMSNorm and its backward (lane: dims lane + 64 n)
+    // o_long, RMSNorm and its backward (lane: dims NX lane .. NX lane + NX - 1)
     float o[NX], dout_[NX], y[NX];
 #pragma unroll
     for (int n = 0; n < NX; ++n) {
         o[n] = 0.0f;
-        dout_[n] = dO[row + lane + 64 * n];
+        dout_[n] = dO[row + NX * lane + n];
     }
+#pragma unroll 8
     for (int t = 0; t < ntok; ++t) {
         const float pt = s_s[wave][t];
-        const int64_t vb = (hN + s_tok[wave][t]) * D;
+        float vv[NX];
+        ldnx<T, NX>(v + s_tok[wave][t] * D + NX * lane, vv);
 #pragma unroll
-        for (int n = 0; n < NX; ++n) o[n] += pt * ld(v, vb + lane + 64 * n);
+        for (int n = 0; n < NX; ++n) o[n] += pt * vv[n];
     }
     float ss = 0.0f;
 #pragma unroll
@@ -500,8 +551,8 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
 #pragma unroll
     for (int n = 0; n < NX; ++n) {
         const float d_o = (gam * dout_[n] - y[n] * (gam * dy_y) / (float)D) / rr;
-        s_d[wave][lane + 64 * n] = d_o;
-        do_l[row + lane + 64 * n] = d_o;
+        s_d[wave][NX * lane + n] = d_o;
+        do_l[row + NX * lane + n] = d_o;
         Dsum += d_o * o[n];
     }
     const float Dr = wave_sum(Dsum);
@@ -511,25 +562,36 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
         dg[hN + i] = dy_y;
     }
     __builtin_amdgcn_wave_barrier();
-    // dS_t = P_t (do . v_t - D)
-    for (int t = lane; t < ntok; t += 64) {
-        const int64_t vb = (hN + s_tok[wave][t]) * D;
+    // dS_t = P_t (do . v_t - D): row dot products again
+    float dv[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dv[e] = s_d[wave][VEC * rpart + e];
+#pragma unroll 8
+    for (int t0 = 0; t0 < ntok; t0 += RPI) {
+        const int t = t0 + rsub;
+        const int64_t tok = s_tok[wave][min(t, ntok - 1)];
+        float vv[VEC];
+        ld16f<T>(v + tok * D + VEC * rpart, vv);
         float dp = 0.0f;
-        for (int x = 0; x < D; ++x) dp += s_d[wave][x] * ld(v, vb + x);
-        s_s[wave][t] = s_s[wave][t] * (dp - Dr);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dp += dv[e] * vv[e];
+        dp = group_sum<LPR>(dp);
+        if (t < ntok && rpart == 0) s_s[wave][t] = s_s[wave][t] * (dp - Dr);
     }
     __builtin_amdgcn_wave_barrier();
     float acc[NX];
 #pragma unroll
     for (int n = 0; n < NX; ++n) acc[n] = 0.0f;
+#pragma unroll 8
     for (int t = 0; t < ntok; ++t) {
         const float dst = s_s[wave][t];
-        const int64_t kb = (hN + s_tok[wave][t]) * D;
+        float kk[NX];
+        ldnx<T, NX>(k + s_tok[wave][t] * D + NX * lane, kk);
 #pragma unroll
-        for (int n = 0; n < NX; ++n) acc[n] += dst * ld(k, kb + lane + 64 * n);
+        for (int n = 0; n < NX; ++n) acc[n] += dst * kk[n];
     }
 #pragma unroll
-    for (int n = 0; n < NX; ++n) dq[row + lane + 64 * n] += p.scale * acc[n];
+    for (int n = 0; n < NX; ++n) dq[row + NX * lane + n] += p.scale * acc[n];
 }
 
 // ---- the (query, rank) pairs as sort keys: key = head * C + cell (or H * C when the
