@@ -253,7 +253,7 @@ typedef struct fsl_workspace_layout {
     size_t rope_abs;/* float2 (cos, sin) by absolute position, two levels (bf16 only) */
     size_t kt;      /* fp16 [H][Np][d] RoPE-rotated keys, Np = 64 ceil(N/64) (bf16 only) */
     size_t vt;      /* fp16 [H][Np/32][d][32] values transposed per 32 tokens (bf16 only) */
-    size_t plan;    /* per (head, 256-query span) list of the span's selected cells and their queries (bf16 only) */
+    size_t plan;    /* long branch work lists: per (head, 256-query span) cells and queries, or per-cell (query, rank) lists without pruning (bf16 only) */
     size_t part;    /* fp16 [H][N][K][d] each selected cell's normalised long-branch output (bf16 only) */
     size_t plse;    /* float [H][N][K] each selected cell's base-2 log-sum-exp of scaled scores (bf16 only) */
     size_t fixups;  /* uint32 near-tie query list of the bf16 scoring (bf16 only) */

@@ -76,7 +76,7 @@ fsl_workspace_layout layout(const KParams &k, bool full = true) {
     L.rope_abs = take(bf ? (size_t)(rope_abs_rows_hi(k) + kRopeSpan) * (k.d / 2) * sizeof(float2) : 0);
     L.kt = take(bf ? (size_t)k.H * kt_head_elems(k) * sizeof(uint16_t) : 0);
     L.vt = take(bf ? (size_t)k.H * vt_head_elems(k) * sizeof(uint16_t) : 0);
-    L.plan = take(bf ? (size_t)plan_records(k) * kPlanRecBytes : 0);
+    L.plan = take(bf ? (size_t)plan_bytes(k) : 0);
     L.part = take(bf ? (size_t)k.H * k.N * k.K * k.d * sizeof(uint16_t) : 0);
     L.plse = take(bf ? (size_t)k.H * k.N * k.K * sizeof(float) : 0);
     const bool fs = k.P < 0;  // no pruning: a contender list per near-tie, and the split cell means
@@ -332,6 +332,7 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
     const KParams kp = kparams(p);
     const fsl_workspace_layout L = layout(kp);
     if (ws_bytes < L.total) return FSL_E_WORKSPACE;
+    if (kp.dtype == FSL_BF16 && kp.P < 0 && !ro_supported(kp)) return FSL_E_UNSUPPORTED;  // 32-bit list indices
     const Work w = carve(ws, L);
     int stage = 0;
     auto mark = [&](hipError_t e) {
@@ -362,7 +363,8 @@ static int attn_fwd_impl(const void *q, const void *k, const void *v, void *out,
     // fp32: the window branch, then the long branch with RMSNorm and the mix
     if (bf) {
         if (e == hipSuccess)
-            e = mark(launch_readout_units(q, k, w.vt, w.sel, w.plan, w.part, w.plse, kp, 0, kp.N, stream));
+            e = mark(kp.P < 0 ? launch_readout_cells(q, k, w.vt, w.sel, w.plan, w.part, w.plse, kp, stream)
+                              : launch_readout_units(q, k, w.vt, w.sel, w.plan, w.part, w.plse, kp, 0, kp.N, stream));
         if (e == hipSuccess)
             e = mark(launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.sel, w.part, w.plse, out, o_win_out,
                                         o_long_out, kp, 0, kp.N, stream));
@@ -456,6 +458,7 @@ static int fsb_run(const void *q, const void *k, const void *v, void *out, const
     if (ws_bytes < fsb_bytes(p)) return FSL_E_WORKSPACE;
     const fsl_params base = fsb_base(p);
     const KParams kp = kparams(&base);
+    if (forward && kp.dtype == FSL_BF16 && !ro_supported(kp)) return FSL_E_UNSUPPORTED;  // 32-bit list indices
     const fsl_workspace_layout L = layout(kp);
     const Work w = carve(ws, L);
     FsbWork fw;
@@ -469,7 +472,7 @@ static int fsb_run(const void *q, const void *k, const void *v, void *out, const
     if (!forward) return hip_status(e);
     if (e == hipSuccess && !bf) e = launch_rope_table(w.rope, w.status, kp, stream);
     if (bf) {
-        if (e == hipSuccess) e = launch_readout_units(q, k, w.vt, w.sel, w.plan, w.part, w.plse, kp, 0, kp.N, stream);
+        if (e == hipSuccess) e = launch_readout_cells(q, k, w.vt, w.sel, w.plan, w.part, w.plse, kp, stream);
         if (e == hipSuccess)
             e = launch_window_bf16(q, w.kt, w.vt, w.rope_abs, w.sel, w.part, w.plse, out, nullptr, nullptr, kp, 0,
                                    kp.N, stream);

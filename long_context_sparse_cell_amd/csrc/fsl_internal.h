@@ -39,7 +39,8 @@ struct Work {
     float2 *rope_abs;  // absolute-position (cos, sin): ceil(N/64) rows of 64a, then 64 rows of b
     uint16_t *kt;      // fp16 [H][Np][d] rotated keys, Np = 64 ceil(N/64)
     uint16_t *vt;      // fp16 [H][Np/32][d][32] values, transposed per 32-token group (vt_pos order)
-    uint32_t *plan;    // per (head, span) plan record of the long branch (kPlanRecBytes each)
+    uint32_t *plan;    // long branch: per (head, span) plan records (kPlanRecBytes each), or without
+                       // pruning the per-cell counters and pair lists (ro_* layout)
     uint16_t *part;    // fp16 [H][N][K][d] long-branch output of each selected cell, normalised
     float *plse;       // [H][N][K] lambda = m + log2(l) of each selected cell (base-2 log-sum-exp)
     // queries whose certified filter left more than K contenders (bf16 scoring):
@@ -108,6 +109,45 @@ static_assert(4 * kPlanPairWord + 2 * kPlanMaxPairs <= kPlanRecBytes, "plan reco
 __host__ __device__ inline int span_queries(const KParams &p) { return p.K <= kPlanMaxPairs / kSpanQ ? kSpanQ : kPlanMaxPairs / 8; }
 __host__ __device__ inline int64_t plan_records(const KParams &p) {
     return (int64_t)p.H * ((p.N + span_queries(p) - 1) / span_queries(p));
+}
+
+// bf16 long branch without pruning (readout_cells.hip): the (query, rank) pairs
+// of every head are listed by super-span (a run of ro_spans_per_super(p)
+// consecutive spans, 8192 queries at most unless the counters would outgrow
+// kRoMaxCounters) and, inside it, by cell, so that a stretch of the list reads
+// the queries of one super-span while each cell is read once per super-span.
+// The lists are built from the same spans as the plan records. The plan region
+// then holds, in 32-bit words: one pair counter per (head, super-span, cell) plus
+// a sentinel (scanned in place into list offsets), the scan's block totals, then
+// the list itself, one (counter index, pair index) word pair per entry; the
+// kernel walks the list in items of kRoItem entries.
+constexpr int kRoItem = 256;
+constexpr int kRoSuperQ = 8192;
+constexpr int64_t kRoMaxCounters = (int64_t)1 << 22;
+__host__ __device__ inline int64_t ro_spans(const KParams &p) { return (p.N + span_queries(p) - 1) / span_queries(p); }
+__host__ __device__ inline int64_t ro_spans_per_super(const KParams &p) {
+    const int64_t nspan = ro_spans(p);
+    const int64_t hc = (int64_t)p.H * p.C > 0 ? (int64_t)p.H * p.C : 1;
+    int64_t nsup = (p.N + kRoSuperQ - 1) / kRoSuperQ;
+    if (nsup > kRoMaxCounters / hc) nsup = kRoMaxCounters / hc;
+    if (nsup < 1) nsup = 1;
+    return (nspan + nsup - 1) / nsup;
+}
+__host__ __device__ inline int64_t ro_supers(const KParams &p) {
+    return (ro_spans(p) + ro_spans_per_super(p) - 1) / ro_spans_per_super(p);
+}
+__host__ __device__ inline int64_t ro_count_words(const KParams &p) { return (int64_t)p.H * ro_supers(p) * p.C + 1; }
+__host__ __device__ inline int64_t ro_total_words(const KParams &p) { return (ro_count_words(p) + 1023) / 1024; }
+// word offset of the list (8-byte aligned)
+__host__ __device__ inline int64_t ro_list_word(const KParams &p) { return (ro_count_words(p) + ro_total_words(p) + 1) & ~(int64_t)1; }
+__host__ __device__ inline int64_t ro_plan_words(const KParams &p) { return ro_list_word(p) + 2 * (int64_t)p.H * p.N * p.K; }
+// the list's pair indices (head * N + query) * K + rank and counter indices are 32-bit
+__host__ __device__ inline bool ro_supported(const KParams &p) {
+    return (int64_t)p.H * p.N * p.K < ((int64_t)1 << 31) && ro_count_words(p) < ((int64_t)1 << 31);
+}
+// bytes of the plan region: span records with pruning, cell lists without
+__host__ __device__ inline int64_t plan_bytes(const KParams &p) {
+    return p.P < 0 ? ro_plan_words(p) * 4 : plan_records(p) * kPlanRecBytes;
 }
 
 // rows of the coarse absolute RoPE table (one per 64 positions)
@@ -429,6 +469,8 @@ hipError_t launch_window_bf16(const void *q, const uint16_t *kt, const uint16_t 
                               const int32_t *sel, const uint16_t *part, const float *plse, void *out,
                               float *o_win_out, float *o_long_out, const KParams &p, int64_t qa, int64_t qb,
                               hipStream_t st);
+hipError_t launch_readout_cells(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
+                                uint32_t *plan, uint16_t *part, float *plse, const KParams &p, hipStream_t st);
 hipError_t launch_readout_units(const void *q, const void *k, const uint16_t *vt, const int32_t *sel,
                                 uint32_t *plan, uint16_t *part, float *plse, const KParams &p, int64_t qa,
                                 int64_t qb, hipStream_t st);
@@ -471,6 +513,7 @@ __host__ __device__ inline int64_t heavy_items_max(const KParams &p) {
 constexpr int kSortRadix = 256;
 constexpr int kSortScanBlock = 1024;
 constexpr int kSortScanTopMax = 8192;
+static_assert(kSortScanBlock == 1024, "ro_total_words counts 1024-word scan blocks");
 // chunk length (elements) and chunk count for n pairs
 inline void sort_plan(int64_t n, int &chunk, int &nch) {
     const int64_t max_chunks = (int64_t)kSortScanTopMax * kSortScanBlock / kSortRadix;
@@ -488,6 +531,9 @@ inline size_t sort_hist_words(int64_t n) {
 inline size_t sort_total_words(int64_t n) { return (sort_hist_words(n) + kSortScanBlock - 1) / kSortScanBlock; }
 hipError_t launch_sort_pairs(uint32_t *keys, uint32_t *vals, uint32_t *ktmp, uint32_t *vtmp, uint32_t *hist,
                              uint32_t *totals, int64_t n, int bits, bool *in_tmp, hipStream_t st);
+// exclusive scan of m words in place in blocks of kSortScanBlock; prefix of i =
+// data[i] + totals[i / kSortScanBlock]
+hipError_t launch_scan_u32(uint32_t *data, int64_t m, uint32_t *totals, hipStream_t st);
 // bits of the backward's pair keys, head * C + cell with the sentinel H * C
 __host__ __device__ inline int pair_key_bits(const KParams &p) {
     int b = 1;

@@ -10,6 +10,7 @@
 //   sort_scan_kernel     exclusive scan of each 1024-entry block of hist, with the
 //                        block's total
 //   sort_scan_top_kernel exclusive scan of the block totals (one work-group)
+// launch_scan_u32 runs the last two on their own for other users of a block scan.
 //   sort_scatter_kernel  one wave per chunk walks it 64 elements at a time; a lane's
 //                        slot is its digit's first slot, plus the chunk's elements of
 //                        that digit already placed, plus the lanes below it with the
@@ -67,33 +68,45 @@ __global__ __launch_bounds__(256) void sort_scan_kernel(uint32_t *__restrict__ h
     if (tid == 255) totals[blockIdx.x] = wbase + inc;
 }
 
-// exclusive scan of the block totals in place (at most kScanTopMax of them)
+// exclusive scan of the block totals in place, kScanTopMax at a time with the
+// running sum carried from one piece to the next
 __global__ __launch_bounds__(1024) void sort_scan_top_kernel(uint32_t *__restrict__ totals, int nb) {
     __shared__ uint32_t s_w[16];
+    __shared__ uint32_t s_carry;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int PER = kScanTopMax / 1024;
-    uint32_t x[PER], sum = 0u;
+    if (tid == 0) s_carry = 0u;
+    for (int base = 0; base < nb; base += kScanTopMax) {
+        uint32_t x[PER], sum = 0u;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int e = PER * tid + j;
-        x[j] = e < nb ? totals[e] : 0u;
-        sum += x[j];
-    }
-    uint32_t inc = sum;
+        for (int j = 0; j < PER; ++j) {
+            const int e = base + PER * tid + j;
+            x[j] = e < nb ? totals[e] : 0u;
+            sum += x[j];
+        }
+        uint32_t inc = sum;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-    }
-    if (lane == 63) s_w[wave] = inc;
-    __syncthreads();
-    uint32_t run = inc - sum;
-    for (int w2 = 0; w2 < wave; ++w2) run += s_w[w2];
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(inc, o);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) s_w[wave] = inc;
+        __syncthreads();
+        uint32_t run = s_carry + inc - sum;
+        uint32_t all = 0u;
+        for (int w2 = 0; w2 < 16; ++w2) {
+            if (w2 < wave) run += s_w[w2];
+            all += s_w[w2];
+        }
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int e = PER * tid + j;
-        if (e < nb) totals[e] = run;
-        run += x[j];
+        for (int j = 0; j < PER; ++j) {
+            const int e = base + PER * tid + j;
+            if (e < nb) totals[e] = run;
+            run += x[j];
+        }
+        __syncthreads();  // every thread has read s_w and s_carry
+        if (tid == 0) s_carry += all;
+        __syncthreads();
     }
 }
 
@@ -134,6 +147,16 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(const uint32_t *__rest
         if (ok && (same >> lane) == 1ull) placed[dg] += (uint32_t)__popcll(same);
         __builtin_amdgcn_wave_barrier();
     }
+}
+
+// Exclusive scan of m words in place, in blocks of kScanBlock: afterwards the
+// prefix of element i is data[i] + totals[i / kScanBlock].
+hipError_t launch_scan_u32(uint32_t *data, int64_t m, uint32_t *totals, hipStream_t st) {
+    if (m <= 0) return hipSuccess;
+    const int64_t nb = (m + kScanBlock - 1) / kScanBlock;
+    hipLaunchKernelGGL(sort_scan_kernel, dim3((unsigned)nb), dim3(256), 0, st, data, m, totals);
+    hipLaunchKernelGGL(sort_scan_top_kernel, dim3(1), dim3(1024), 0, st, totals, (int)nb);
+    return hipGetLastError();
 }
 
 // Sorts (keys, vals) by the low `bits` bits of the keys, stably; the result ends in

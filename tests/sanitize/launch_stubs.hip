@@ -62,9 +62,15 @@ hipError_t launch_window_bf16(const void *, const uint16_t *kt, const uint16_t *
     return hipSuccess;
 }
 hipError_t launch_readout_units(const void *, const void *, const uint16_t *vt, const int32_t *sel, uint32_t *plan,
-                                uint16_t *part, float *plse, const KParams &, int64_t, int64_t, hipStream_t) {
+                                uint16_t *part, float *plse, const KParams &k, int64_t, int64_t, hipStream_t) {
     ++g_launches; inside(vt, "vt"); inside(sel, "sel"); inside(plan, "plan"); inside(part, "part");
-    inside(plse, "plse");
+    inside(plse, "plse"); inside((const char *)plan + plan_records(k) * kPlanRecBytes - 1, "plan (last byte)");
+    return hipSuccess;
+}
+hipError_t launch_readout_cells(const void *, const void *, const uint16_t *vt, const int32_t *sel, uint32_t *plan,
+                                uint16_t *part, float *plse, const KParams &k, hipStream_t) {
+    ++g_launches; inside(vt, "vt"); inside(sel, "sel"); inside(plan, "plan"); inside(part, "part");
+    inside(plse, "plse"); inside(plan + ro_plan_words(k) - 1, "plan (last word)");
     return hipSuccess;
 }
 hipError_t launch_readout_mix(const void *, const void *, const void *, const int32_t *sel, const float *o_win, void *,
