@@ -13,7 +13,8 @@
 //  1. fs_prep_kernel splits every float32 kbar_c once into bf16 head + tail
 //     (hi, lo) and stores the per-cell constants of the error bound.
 //  2. select_fs_kernel streams the block's cells through LDS in chunks of 64
-//     (double buffered) and computes content~ = q.(hi + lo) on
+//     (copied straight into LDS, double buffered, 16-byte pieces of a row
+//     permuted against bank conflicts) and computes content~ = q.(hi + lo) on
 //     v_mfma_f32_16x16x32_bf16, with the bound |s - s~| <= eps of the pool
 //     scoring kernel (select_mfma.hip). Each lane (one query, four cells of
 //     every 16-cell tile) keeps the K_L + 1 cells of largest upper bound (K_L =
@@ -55,21 +56,10 @@ __host__ __device__ constexpr float fs_eps_content(int d) {
     return 1.001f * (7.62939453125e-06f + (float)(4 * d + 8) * 5.9604644775390625e-08f);
 }
 
-// One 16-byte piece u (row u / (D/8), piece u % (D/8)) of a chunk's split means:
-// rows past the block's last cell read that cell again (they are never scored).
-template <int D>
-__device__ __forceinline__ void fs_load_piece(const uint16_t *__restrict__ khi, const uint16_t *__restrict__ klo,
-                                              int64_t hC, int64_t c0, int64_t clast, int u, uint4 &h, uint4 &l) {
-    const int64_t c = min(c0 + u / (D / 8), clast);
-    const int64_t off = (hC + c) * D + 8 * (u % (D / 8));
-    h = *reinterpret_cast<const uint4 *>(khi + off);
-    l = *reinterpret_cast<const uint4 *>(klo + off);
-}
-template <int D, int HLD>
-__device__ __forceinline__ void fs_store_piece(uint16_t *s_hi, uint16_t *s_lo, int u, const uint4 &h, const uint4 &l) {
-    *reinterpret_cast<uint4 *>(&s_hi[(u / (D / 8)) * HLD + 8 * (u % (D / 8))]) = h;
-    *reinterpret_cast<uint4 *>(&s_lo[(u / (D / 8)) * HLD + 8 * (u % (D / 8))]) = l;
-}
+// LDS position of 16-byte piece c of chunk row r (of CPR pieces): c ^ (r mod CPR),
+// so that the 16 rows of a score tile read by one lane group hit distinct banks
+template <int CPR>
+__device__ __forceinline__ int fs_piece(int r, int c) { return c ^ (r & (CPR - 1)); }
 
 }  // namespace
 
@@ -122,17 +112,23 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
                                                         const uint16_t *__restrict__ klo,
                                                         const float4 *__restrict__ kcf, int32_t *__restrict__ sel,
                                                         uint32_t *__restrict__ fix, KParams p, int QW) {
-    constexpr int HLD = D + 8;     // bf16 row stride in LDS (272 B for d = 128)
     constexpr int QS = D / 32;
     constexpr int CH = kFsChunk;
-    constexpr int VPR = D / 8;     // 16-byte pieces per row
-    constexpr int VPT = CH * VPR / 512;  // pieces per thread per array and chunk
+    constexpr int CPR = D / 8;     // 16-byte pieces per row
+    constexpr int ROWU = CH * D * 2 / 1024;  // 1 KB copy units of a chunk's hi (and of its lo) rows
+    constexpr int NCOPY = 2 * ROWU + 1;      // and one unit of per-cell constants (64 x 16 bytes)
+    static_assert(CH == 64, "one copy unit of per-cell constants per chunk");
     // listed cells per lane: one more than the largest K of this instance, so a list
     // overflows only when a single lane holds K + 1 cells whose bounds reach theta
     constexpr int kFsCap = KL + 1;
-    __shared__ __attribute__((aligned(16))) uint16_t s_hi[2][CH * HLD];
-    __shared__ __attribute__((aligned(16))) uint16_t s_lo[2][CH * HLD];
-    __shared__ float4 s_cf[2][CH];
+    // two named buffers of each kind, so that the compiler can tell a chunk's copy from
+    // the reads of the other buffer and does not wait for the copy before them
+    __shared__ __attribute__((aligned(1024))) uint16_t s_hi0[CH * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_hi1[CH * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_lo0[CH * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t s_lo1[CH * D];
+    __shared__ __attribute__((aligned(1024))) float4 s_cf0[CH];
+    __shared__ __attribute__((aligned(1024))) float4 s_cf1[CH];
     __shared__ int s_nfix;
 
     const int nqb = (int)((p.N + QW - 1) / QW);
@@ -159,21 +155,25 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
     for (int ks = 0; ks < QS; ++ks) bq[ks].u = *reinterpret_cast<const uint4 *>(q + (hN + i) * D + 32 * ks + 8 * g);
     if (tid == 0) s_nfix = 0;
 
-    // ---- chunk staging in registers: every load of a chunk is issued before any is
-    // stored. Plain variables, not arrays, so that nothing of it lives in scratch.
-    static_assert(VPT == 1 || VPT == 2, "one or two 16-byte pieces per thread and array");
-    uint4 rh0, rl0, rh1, rl1;
-    float4 rcf = make_float4(0.f, 0.f, 0.f, 0.f);
+    // ---- chunk copies straight into LDS (global_load_lds), 1 KB per wave instruction:
+    // rows past the block's last cell repeat that cell (they are never scored)
     const int64_t nlast = (int64_t)n - 1;
-    auto load = [&](int t) __attribute__((always_inline)) {
-        fs_load_piece<D>(khi, klo, hC, (int64_t)t * CH, nlast, tid, rh0, rl0);
-        if constexpr (VPT > 1) fs_load_piece<D>(khi, klo, hC, (int64_t)t * CH, nlast, tid + 512, rh1, rl1);
-        if (tid < CH) rcf = kcf[hC + min((int64_t)t * CH + tid, nlast)];
-    };
-    auto store = [&](int buf) __attribute__((always_inline)) {
-        fs_store_piece<D, HLD>(s_hi[buf], s_lo[buf], tid, rh0, rl0);
-        if constexpr (VPT > 1) fs_store_piece<D, HLD>(s_hi[buf], s_lo[buf], tid + 512, rh1, rl1);
-        if (tid < CH) s_cf[buf][tid] = rcf;
+    auto issue = [&](int t, uint16_t *bhi, uint16_t *blo, float4 *bcf) __attribute__((always_inline)) {
+        const int64_t c0 = (int64_t)t * CH;
+        for (int u = __builtin_amdgcn_readfirstlane(wave); u < NCOPY; u += 8) {
+            if (u < 2 * ROWU) {
+                const int uu = u % ROWU;
+                const int pc = 64 * uu + lane;  // 16-byte piece of the chunk
+                const int r = pc / CPR, phys = pc % CPR;
+                const int64_t off = (hC + min(c0 + r, nlast)) * D + 8 * fs_piece<CPR>(r, phys);
+                if (u < ROWU)
+                    lds_dma16(khi + off, bhi + 512 * uu);
+                else
+                    lds_dma16(klo + off, blo + 512 * uu);
+            } else {
+                lds_dma16(kcf + hC + min(c0 + lane, nlast), bcf);
+            }
+        }
     };
 
     float qss = 0.0f;
@@ -193,14 +193,7 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
     for (int r = 0; r < kFsCap; ++r) { lu[r] = -INFINITY; ll[r] = -INFINITY; li[r] = INT_MAX; }
     float thr = -INFINITY;  // a score that K cells are known to beat: skip cells whose ub is below it
 
-    if (nch > 0) {
-        load(0);
-        store(0);
-        if (nch > 1) load(1);
-    }
-    __syncthreads();
-    for (int t = 0; t < nch; ++t) {
-        const int buf = t & 1;
+    auto chunk = [&](int t, const uint16_t *bhi, const uint16_t *blo, const float4 *bcf) __attribute__((always_inline)) {
         const int c0 = t * CH;
         // erf is 1 (in fp32 and fp64) once its argument reaches 6; cells are ascending
         // and every query is at or after q0, so the chunk's last cell decides for all
@@ -213,8 +206,8 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
 #pragma unroll
             for (int ks = 0; ks < QS; ++ks) {
                 U16x8f hi, lo;
-                hi.u = *reinterpret_cast<const uint4 *>(&s_hi[buf][rowc * HLD + 32 * ks + 8 * g]);
-                lo.u = *reinterpret_cast<const uint4 *>(&s_lo[buf][rowc * HLD + 32 * ks + 8 * g]);
+                hi.u = *reinterpret_cast<const uint4 *>(&bhi[rowc * D + 8 * fs_piece<CPR>(rowc, 4 * ks + g)]);
+                lo.u = *reinterpret_cast<const uint4 *>(&blo[rowc * D + 8 * fs_piece<CPR>(rowc, 4 * ks + g)]);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi.b, bq[ks].b, acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.b, bq[ks].b, acc, 0, 0, 0);
             }
@@ -230,7 +223,7 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
             for (int e = 0; e < 4; ++e) {
                 const int loc = 16 * ct + 4 * g + e;
                 const int c = c0 + loc;
-                const float4 cf = s_cf[buf][loc];
+                const float4 cf = bcf[loc];
                 float bf = cf.x;  // lambda a_c times the erf factor 1
                 if (need_erf) {
                     const float argf = (float)((int)i - __float_as_int(cf.w)) * karg;
@@ -269,10 +262,19 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
             // when the entries that certified them are evicted later
             thr = colmax4(thr);
         }
-        if (t + 1 < nch) {
-            store(buf ^ 1);
-            if (t + 2 < nch) load(t + 2);
-        }
+    };
+    if (nch > 0) issue(0, s_hi0, s_lo0, s_cf0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nch; t += 2) {
+        if (t + 1 < nch) issue(t + 1, s_hi1, s_lo1, s_cf1);
+        chunk(t, s_hi0, s_lo0, s_cf0);
+        wait_vmem();  // the next chunk has landed, and every wave is done with this one
+        __syncthreads();
+        if (t + 1 >= nch) break;
+        if (t + 2 < nch) issue(t + 2, s_hi0, s_lo0, s_cf0);
+        chunk(t + 1, s_hi1, s_lo1, s_cf1);
+        wait_vmem();
         __syncthreads();
     }
 
