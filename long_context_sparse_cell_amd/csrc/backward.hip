@@ -22,12 +22,12 @@
 //   bwd_long_q      per query (one wave): o_long, RMSNorm's backward, dq += long part
 //   bwd_pair_keys, a stable radix sort (sort.hip), bwd_seg_*: each cell's
 //                   selecting queries in query order
-//   bwd_long_kv     per cell: dk, dv += long part over every query that selected it;
-//                   cells chosen by more than kHeavyPairs queries in chunks whose
-//                   sums bwd_heavy_reduce adds in chunk order
+//   bwd_long_kv     per cell: dk, dv += long part over every query that selected it,
+//                   on the fp32 matrix cores; cells chosen by more than kHeavyPairs
+//                   queries in chunks whose sums bwd_heavy_reduce adds in chunk order
 //   bwd_dgamma      per head: dgamma summed in a fixed order
-// Arithmetic is fp32: the window's products on the matrix cores (fp32 MFMA), the long
-// branch's on the vector ALUs, operand tiles staged in LDS.
+// Arithmetic is fp32: the window's and the long branch's key-side products on the
+// matrix cores (fp32 MFMA), the long branch's query side on the vector ALUs.
 #include <climits>
 
 #include "fsl_internal.h"
@@ -420,7 +420,8 @@ __global__ __launch_bounds__(256, 2) void bwd_win_dkv_kernel(const float *__rest
 // ---- long branch, query side: one wave per query (4 per work-group). Recomputes the
 // branch's softmax over the selected cells' tokens, o_long and RMSNorm's backward;
 // writes the gradient reaching the softmax output (do_l), the row's lse and D, the
-// query's dgamma term, and adds the branch's part of dq. Dot products with token
+// query's dgamma term and the query in fp32 (for the key side), and adds the branch's
+// part of dq. Dot products with token
 // rows (scores, dO . v_t) read whole rows per instruction: 16 bytes per lane, the
 // lanes of one row summing their parts; sums over tokens (o, dq) give each lane
 // NX = d/64 consecutive dims.
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
                                                               const int32_t *__restrict__ sel, float *__restrict__ dq,
                                                               float *__restrict__ do_l, float *__restrict__ lse_l,
                                                               float *__restrict__ D_l, float *__restrict__ dg,
-                                                              KParams p) {
+                                                              float *__restrict__ q32, KParams p) {
     constexpr int NX = D / 64;             // consecutive dims per lane in sums over tokens
     constexpr int VEC = 16 / sizeof(T);    // elements per lane in row dot products
     constexpr int LPR = D / VEC;           // lanes per row
@@ -486,7 +487,10 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
         ntok += p.s;
     }
     if (ntok == 0) {
-        for (int x = lane; x < D; x += 64) do_l[row + x] = 0.0f;
+        for (int x = lane; x < D; x += 64) {
+            do_l[row + x] = 0.0f;
+            q32[row + x] = ld(q, row + x);
+        }
         if (lane == 0) { lse_l[hN + i] = 0.0f; D_l[hN + i] = 0.0f; dg[hN + i] = 0.0f; }
         return;
     }
@@ -495,6 +499,11 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     // scores: row dot products, the LPR lanes of a row summing their VEC products
     float qv[VEC];
     ld16f<T>(q + row + VEC * rpart, qv);
+    // the query as fp32 for the key side (bwd_long_kv)
+    if (rsub == 0)
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+            *reinterpret_cast<float4 *>(q32 + row + VEC * rpart + e) = make_float4(qv[e], qv[e + 1], qv[e + 2], qv[e + 3]);
     float mx = -INFINITY;
 #pragma unroll 8
     for (int t0 = 0; t0 < ntok; t0 += RPI) {
@@ -650,26 +659,144 @@ __global__ void bwd_seg_mark_kernel(const uint32_t *__restrict__ key, int64_t n,
 
 // ---- long branch, key side. CHUNKS = false: one work-group per (head, cell) with at
 // most kHeavyPairs selectors, adding to dk, dv; CHUNKS = true: one work-group per
-// chunk of a heavier cell, writing its sums to part[item]. Walks the queries that
-// selected the cell, in query order (a stable sort of the pairs by cell), and
-// accumulates their dk, dv terms for the cell's S tokens. Thread t takes token
-// t / TPT and dims (t % TPT) + TPT k.
+// chunk of a heavier cell, writing its sums to part[item]. One wave per 16 of the
+// cell's tokens holds their keys and values as B operands of the fp32 matrix cores
+// (dims (d/4) g .. of token c in lane (c, g)); the queries that selected the cell,
+// in query order (a stable sort of the pairs by cell), are gathered 16 at a time into
+// LDS (q as fp32 and unrotated, written by bwd_long_q: the long branch has no RoPE;
+// and the gradient reaching the softmax output). S = Q K^T and dP = do V^T put queries 4 g + r of token c in
+// lane (c, g); P = exp(scale S - lse), dS = P (dP - D), then dv^T += do^T P and
+// dk^T += Q^T dS (times the scale) take P and dS straight from that layout.
+namespace {
+// 16 bytes of T at p as four floats (4 fp32, or 4 bf16 from 8 bytes)
+template <typename T> __device__ __forceinline__ float4 ld4f(const T *p);
+template <> __device__ __forceinline__ float4 ld4f<float>(const float *p) {
+    return *reinterpret_cast<const float4 *>(p);
+}
+template <> __device__ __forceinline__ float4 ld4f<uint16_t>(const uint16_t *p) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xFFFF0000u));
+}
+// LDS tiles of 16 rows of D elements of T, 16-byte chunk c of row r at c ^ (r mod chunks per row)
+template <typename T, int D>
+struct GTile {
+    static constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+    static constexpr int CPR = D / EPC;              // chunks per row
+    static constexpr int ELEMS = 16 * D;
+    static constexpr int UNITS = ELEMS * (int)sizeof(T) / 1024;  // 1 KB copy units
+    __device__ static int off(int row, int chunk) { return (row * CPR + (chunk ^ (row & (CPR - 1)))) * EPC; }
+};
+// the 16 bytes at an LDS chunk as floats
+template <typename T> __device__ __forceinline__ void chunkf(const T *p, float *dst);
+template <> __device__ __forceinline__ void chunkf<float>(const float *p, float *dst) {
+    const float4 f = *reinterpret_cast<const float4 *>(p);
+    dst[0] = f.x; dst[1] = f.y; dst[2] = f.z; dst[3] = f.w;
+}
+template <> __device__ __forceinline__ void chunkf<uint16_t>(const uint16_t *p, float *dst) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = __uint_as_float(w[e] << 16);
+        dst[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+}
+// acc (rows 4 g + r of the 16 tile rows, column c) += tile rows as A (row c for this
+// lane) times the lane's register operand b[] (dims (d/4) g .. of its column)
+template <typename T, int D, typename BV>
+__device__ __forceinline__ floatx4 gtile_dot(const T *tile, int col, int g, BV b) {
+    using G = GTile<T, D>;
+    constexpr int KS = D / 4;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < KS / G::EPC; ++cc) {
+        float a[G::EPC];
+        chunkf<T>(tile + G::off(col, KS / G::EPC * g + cc), a);
+#pragma unroll
+        for (int e = 0; e < G::EPC; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b(G::EPC * cc + e), acc, 0, 0, 0);
+    }
+    return acc;
+}
+// a token's d/4 values (dims (d/4) g ..) as MFMA B operands: fp32 as they are, bf16
+// packed two to a register and widened at each use
+template <typename T, int KS>
+struct BRow;
+template <int KS>
+struct BRow<float, KS> {
+    float x[KS];
+    __device__ void load(const float *src) {
+#pragma unroll
+        for (int i = 0; i < KS / 4; ++i) {
+            const float4 f = *reinterpret_cast<const float4 *>(src + 4 * i);
+            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+        }
+    }
+    __device__ float operator()(int i) const { return x[i]; }
+};
+template <int KS>
+struct BRow<uint16_t, KS> {
+    uint32_t w[KS / 2];
+    __device__ void load(const uint16_t *src) {
+#pragma unroll
+        for (int i = 0; i < KS / 8; ++i) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(src + 8 * i);
+            w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+        }
+    }
+    __device__ float operator()(int i) const {
+        return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+    }
+};
+// acc[dt] (dims 16 dt + 4 g + r, column c) += sum over the tile rows of tile[row][dim]
+// w(row, c), with w(4 g + r, c) = w[r] held by lane (c, g)
+template <typename T, int D>
+__device__ __forceinline__ void gtile_tmul(const T *tile, int col, int g, const float *w, floatx4 *acc) {
+    using G = GTile<T, D>;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * dt + col;
+            const float a = to_f32<T>(tile[G::off(4 * g + r, d / G::EPC) + d % G::EPC]);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, w[r], acc[dt], 0, 0, 0);
+        }
+}
+// rows src_rows[r] (r < 16) of a [rows][D] array of T into a tile, by the NWV waves
+template <typename T, int D, int NWV>
+__device__ __forceinline__ void gtile_issue(const T *base, const int64_t *rows, T *tile, int wave, int lane) {
+    using G = GTile<T, D>;
+    for (int u = __builtin_amdgcn_readfirstlane(wave); u < G::UNITS; u += NWV) {
+        const int pc = 64 * u + lane;  // chunk of the tile
+        const int r = pc / G::CPR, phys = pc % G::CPR;
+        lds_dma16(base + rows[r] * D + G::EPC * (phys ^ (r & (G::CPR - 1))), tile + 64 * G::EPC * u);
+    }
+}
+}  // namespace
+
 template <typename T, int D, int S, bool CHUNKS>
-__global__ __launch_bounds__(kThreads) void bwd_long_kv_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                               const T *__restrict__ v, const uint32_t *__restrict__ sq,
-                                                               const int32_t *__restrict__ seg,
-                                                               const int32_t *__restrict__ items,
-                                                               const int32_t *__restrict__ counters,
-                                                               const float *__restrict__ do_l,
-                                                               const float *__restrict__ lse_l,
-                                                               const float *__restrict__ D_l,
-                                                               float *__restrict__ dk, float *__restrict__ dv,
-                                                               float *__restrict__ part, KParams p) {
-    constexpr int TPT = kThreads / S;  // threads per token
-    constexpr int NK = D / TPT;        // dims per thread
-    constexpr int G = 8;               // selectors staged per round
-    __shared__ float s_q[G][D], s_do[G][D];
-    __shared__ float s_lse[G], s_D[G];
+__global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const float *__restrict__ q, const T *__restrict__ k,
+                                                                    const T *__restrict__ v,
+                                                                    const uint32_t *__restrict__ sq,
+                                                                    const int32_t *__restrict__ seg,
+                                                                    const int32_t *__restrict__ items,
+                                                                    const int32_t *__restrict__ counters,
+                                                                    const float *__restrict__ do_l,
+                                                                    const float *__restrict__ lse_l,
+                                                                    const float *__restrict__ D_l,
+                                                                    float *__restrict__ dk, float *__restrict__ dv,
+                                                                    float *__restrict__ part, KParams p) {
+    constexpr int NWV = S / 16;          // waves, 16 tokens each
+    constexpr int KS = D / 4;
+    constexpr int QT = 16;               // selectors per tile
+    // two named buffers of each kind, so that the compiler can tell a tile's copy from
+    // the reads of the other buffer
+    __shared__ __attribute__((aligned(1024))) float s_q0[QT * D];
+    __shared__ __attribute__((aligned(1024))) float s_q1[QT * D];
+    __shared__ __attribute__((aligned(1024))) float s_o0[QT * D];
+    __shared__ __attribute__((aligned(1024))) float s_o1[QT * D];
+    __shared__ int64_t s_rows[2][QT];              // the gathered rows of two tiles
     int64_t cid;  // head * C + cell
     int64_t e0, e1;
     if constexpr (CHUNKS) {
@@ -688,61 +815,93 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kv_kernel(const T *__restri
     const int h = (int)(cid / p.C);
     const int64_t c = cid % p.C;
     const int64_t hN = (int64_t)h * p.N;
-    const int tid = threadIdx.x, sub = tid % TPT;
-    const int64_t j = c * S + tid / TPT;
-    float kj[NK], vj[NK], acck[NK], accv[NK];
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    const int wave = tid >> 6;
+    const int tok = 16 * wave + col;                  // this lane's token within the cell
+    const int64_t jrow = hN + c * S + tok;
+    // this lane's token as B operands: dims KS g .. KS g + KS - 1
+    BRow<T, KS> kb, vb;
+    kb.load(k + jrow * D + KS * g);
+    vb.load(v + jrow * D + KS * g);
+    floatx4 acck[D / 16], accv[D / 16];
 #pragma unroll
-    for (int n = 0; n < NK; ++n) {
-        kj[n] = ld(k, (hN + j) * D + sub + TPT * n);
-        vj[n] = ld(v, (hN + j) * D + sub + TPT * n);
-        acck[n] = accv[n] = 0.0f;
-    }
-    for (int64_t g0 = e0; g0 < e1; g0 += G) {
-        const int ng = (int)min((int64_t)G, e1 - g0);
+    for (int dt = 0; dt < D / 16; ++dt) acck[dt] = accv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Tile t: selectors e0 + 16 t + r, their rows in s_rows[t % 2] (past e1: the last
+    // selector again, masked). Per tile: the lse and D loads and the row prefetch for
+    // tile t + 2 go out before the copies of tile t + 1, which are issued every tile
+    // (a repeat past the end), so that waiting for those loads never waits for a copy.
+    const int ntile = (int)((e1 - e0 + QT - 1) / QT);
+    auto sel_row = [&](int t) __attribute__((always_inline)) {
+        return hN + (int64_t)sq[min(e0 + (int64_t)QT * t + (tid & (QT - 1)), e1 - 1)];
+    };
+    auto issue = [&](int slot, float *bq, float *bo) __attribute__((always_inline)) {
+        gtile_issue<float, D, NWV>(q, s_rows[slot], bq, wave, lane);
+        gtile_issue<float, D, NWV>(do_l, s_rows[slot], bo, wave, lane);
+    };
+    auto step = [&](int t, const float *bq, const float *bo, float *nq, float *no) __attribute__((always_inline)) {
+        const int slot = t & 1;
+        float lv[4], dd[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t ii = s_rows[slot][4 * g + r];
+            lv[r] = lse_l[ii];
+            dd[r] = D_l[ii];
+        }
+        const int64_t nrow = sel_row(t + 2);
+        issue(slot ^ 1, nq, no);  // tile t + 1
+        const floatx4 sv = gtile_dot<float, D>(bq, col, g, kb);
+        const floatx4 dp = gtile_dot<float, D>(bo, col, g, vb);
+        float P[4], ds[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool ok = e0 + (int64_t)QT * t + 4 * g + r < e1;
+            const float pr = ok ? __expf(sv[r] * p.scale - lv[r]) : 0.0f;
+            P[r] = pr;
+            ds[r] = ok ? pr * (dp[r] - dd[r]) : 0.0f;
+        }
+        gtile_tmul<float, D>(bo, col, g, P, accv);
+        gtile_tmul<float, D>(bq, col, g, ds, acck);
+        wait_vmem();
+        __syncthreads();  // tile t + 1 has landed; every wave is done with this tile and its rows
+        if (tid < QT) s_rows[slot][tid] = nrow;
         __syncthreads();
-        for (int e = tid; e < ng * D; e += kThreads) {
-            const int gg = e / D, x = e % D;
-            const int64_t ii = sq[g0 + gg];
-            s_q[gg][x] = ld(q, (hN + ii) * D + x);
-            s_do[gg][x] = do_l[(hN + ii) * D + x];
-        }
-        if (tid < ng) {
-            const int64_t ii = sq[g0 + tid];
-            s_lse[tid] = lse_l[hN + ii];
-            s_D[tid] = D_l[hN + ii];
-        }
-        __syncthreads();
-        for (int gg = 0; gg < ng; ++gg) {
-            float dot = 0.0f, dp = 0.0f;
-#pragma unroll
-            for (int nn = 0; nn < NK; ++nn) {
-                dot += s_q[gg][sub + TPT * nn] * kj[nn];
-                dp += s_do[gg][sub + TPT * nn] * vj[nn];
-            }
-            dot = group_sum<TPT>(dot);
-            dp = group_sum<TPT>(dp);
-            const float P = __expf(dot * p.scale - s_lse[gg]);
-            const float ds = P * (dp - s_D[gg]);
-#pragma unroll
-            for (int nn = 0; nn < NK; ++nn) {
-                acck[nn] += p.scale * ds * s_q[gg][sub + TPT * nn];
-                accv[nn] += P * s_do[gg][sub + TPT * nn];
-            }
-        }
+    };
+    if (tid < QT) {
+        s_rows[0][tid] = sel_row(0);
+        s_rows[1][tid] = sel_row(1);
     }
+    __syncthreads();
+    issue(0, s_q0, s_o0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < ntile; t += 2) {
+        step(t, s_q0, s_o0, s_q1, s_o1);
+        if (t + 1 >= ntile) break;
+        step(t + 1, s_q1, s_o1, s_q0, s_o0);
+    }
+    // dims 16 dt + 4 g + r of token tok
     if constexpr (CHUNKS) {
         // chunk sums: dk part then dv part, [S][D] each
-        float *dst = part + (int64_t)blockIdx.x * 2 * S * D;
+        float *dst = part + (int64_t)blockIdx.x * 2 * S * D + (int64_t)tok * D;
 #pragma unroll
-        for (int n = 0; n < NK; ++n) {
-            dst[(tid / TPT) * D + sub + TPT * n] = acck[n];
-            dst[S * D + (tid / TPT) * D + sub + TPT * n] = accv[n];
+        for (int dt = 0; dt < D / 16; ++dt) {
+            *reinterpret_cast<float4 *>(dst + 16 * dt + 4 * g) =
+                make_float4(p.scale * acck[dt][0], p.scale * acck[dt][1], p.scale * acck[dt][2], p.scale * acck[dt][3]);
+            *reinterpret_cast<float4 *>(dst + S * D + 16 * dt + 4 * g) =
+                make_float4(accv[dt][0], accv[dt][1], accv[dt][2], accv[dt][3]);
         }
     } else {
 #pragma unroll
-        for (int n = 0; n < NK; ++n) {
-            dk[(hN + j) * D + sub + TPT * n] += acck[n];
-            dv[(hN + j) * D + sub + TPT * n] += accv[n];
+        for (int dt = 0; dt < D / 16; ++dt) {
+            float4 *pk = reinterpret_cast<float4 *>(dk + jrow * D + 16 * dt + 4 * g);
+            float4 *pv = reinterpret_cast<float4 *>(dv + jrow * D + 16 * dt + 4 * g);
+            float4 a4 = *pk, b4 = *pv;
+            a4.x += p.scale * acck[dt][0]; a4.y += p.scale * acck[dt][1];
+            a4.z += p.scale * acck[dt][2]; a4.w += p.scale * acck[dt][3];
+            b4.x += accv[dt][0]; b4.y += accv[dt][1]; b4.z += accv[dt][2]; b4.w += accv[dt][3];
+            *pk = a4;
+            *pv = b4;
         }
     }
 }
@@ -811,8 +970,11 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
     hipLaunchKernelGGL((bwd_win_dkv_kernel<D>), dim3(tiles), dim3(256), 0, st, w.qr, w.kr, vf, w.dO, w.lse_w, w.D_w,
                        w.rope, nhi, dk, dv, p);
     const unsigned qw = (unsigned)(((p.N + 3) / 4) * p.H);
+    // the long branch's query side also leaves the queries in fp32, unrotated, in qr's
+    // storage, which the window kernels no longer need
+    float *q32 = w.qr;
     hipLaunchKernelGGL((bwd_long_q_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, k, v, w.dO, sel, dq, w.do_l,
-                       w.lse_l, w.D_l, w.dg, p);
+                       w.lse_l, w.D_l, w.dg, q32, p);
     if (p.C > 0) {
         // each cell's selecting queries in query order: a stable sort of the pairs by cell
         const int64_t npair = (int64_t)p.H * p.N * p.K;
@@ -830,11 +992,11 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
                            (uint32_t)ncell, w.cseg);
         hipLaunchKernelGGL(bwd_heavy_list_kernel, dim3((unsigned)((ncell + 255) / 256)), dim3(256), 0, st, w.cseg,
                            ncell, w.hcount, w.hitems, w.hcells);
-        hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, false>), dim3((unsigned)ncell), dim3(kThreads), 0, st, q, k,
+        hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, false>), dim3((unsigned)ncell), dim3(64 * (S / 16)), 0, st, q32, k,
                            v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, p);
         const int64_t mi = heavy_items_max(p), mh = heavy_cells_max(p);
         if (mi > 0) {
-            hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, true>), dim3((unsigned)mi), dim3(kThreads), 0, st, q, k,
+            hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, true>), dim3((unsigned)mi), dim3(64 * (S / 16)), 0, st, q32, k,
                                v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, p);
             hipLaunchKernelGGL((bwd_heavy_reduce_kernel<D, S>), dim3((unsigned)mh), dim3(kThreads), 0, st, w.hcells,
                                w.hcount, w.hpart, dk, dv, p);
