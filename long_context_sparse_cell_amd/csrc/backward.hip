@@ -19,15 +19,18 @@
 //                   and dq (window part), on the fp32 matrix cores
 //   bwd_win_dkv     per 64 keys: dk, dv of the window over the queries that see them,
 //                   on the fp32 matrix cores
-//   bwd_long_q      per query (one wave): o_long, RMSNorm's backward, dq += long part
+//   bwd_long_q      per query (one wave): o_long and RMSNorm's backward
 //   bwd_pair_keys, a stable radix sort (sort.hip), bwd_seg_*: each cell's
 //                   selecting queries in query order
 //   bwd_long_kv     per cell: dk, dv += long part over every query that selected it,
-//                   on the fp32 matrix cores; cells chosen by more than kHeavyPairs
-//                   queries in chunks whose sums bwd_heavy_reduce adds in chunk order
+//                   and each (query, rank) pair's dq, on the fp32 matrix cores; cells
+//                   chosen by more than kHeavyPairs queries in chunks whose dk, dv sums
+//                   bwd_heavy_reduce adds in chunk order
+//   bwd_dq_long_sum per query: dq += its pairs' dq in rank order
 //   bwd_dgamma      per head: dgamma summed in a fixed order
-// Arithmetic is fp32: the window's and the long branch's key-side products on the
-// matrix cores (fp32 MFMA), the long branch's query side on the vector ALUs.
+// Arithmetic is fp32: the window's products and the long branch's gradient products
+// on the matrix cores (fp32 MFMA), the long branch's forward recompute on the vector
+// ALUs.
 #include <climits>
 
 #include "fsl_internal.h"
@@ -420,11 +423,10 @@ __global__ __launch_bounds__(256, 2) void bwd_win_dkv_kernel(const float *__rest
 // ---- long branch, query side: one wave per query (4 per work-group). Recomputes the
 // branch's softmax over the selected cells' tokens, o_long and RMSNorm's backward;
 // writes the gradient reaching the softmax output (do_l), the row's lse and D, the
-// query's dgamma term and the query in fp32 (for the key side), and adds the branch's
-// part of dq. Dot products with token
-// rows (scores, dO . v_t) read whole rows per instruction: 16 bytes per lane, the
-// lanes of one row summing their parts; sums over tokens (o, dq) give each lane
-// NX = d/64 consecutive dims.
+// query's dgamma term and the query in fp32 (for the key side, which also forms the
+// branch's dq). The score dot products read whole token rows per instruction: 16
+// bytes per lane, the lanes of one row summing their parts; the sum over tokens (o)
+// gives each lane NX = d/64 consecutive dims.
 namespace {
 // the 16 bytes at p as floats (8 bf16 or 4 fp32)
 template <typename T> __device__ __forceinline__ void ld16f(const T *p, float *dst);
@@ -460,7 +462,7 @@ template <typename T, int NX> __device__ __forceinline__ void ldnx(const T *p, f
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                               const T *__restrict__ v, const float *__restrict__ dO,
-                                                              const int32_t *__restrict__ sel, float *__restrict__ dq,
+                                                              const int32_t *__restrict__ sel,
                                                               float *__restrict__ do_l, float *__restrict__ lse_l,
                                                               float *__restrict__ D_l, float *__restrict__ dg,
                                                               float *__restrict__ q32, KParams p) {
@@ -469,7 +471,6 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     constexpr int LPR = D / VEC;           // lanes per row
     constexpr int RPI = 64 / LPR;          // rows per wave instruction
     constexpr int MAXT = 8 * 64;           // K * s at most
-    __shared__ float s_d[4][D];
     __shared__ float s_s[4][MAXT];
     __shared__ int64_t s_tok[4][MAXT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -560,7 +561,6 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
 #pragma unroll
     for (int n = 0; n < NX; ++n) {
         const float d_o = (gam * dout_[n] - y[n] * (gam * dy_y) / (float)D) / rr;
-        s_d[wave][NX * lane + n] = d_o;
         do_l[row + NX * lane + n] = d_o;
         Dsum += d_o * o[n];
     }
@@ -570,50 +570,19 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
         D_l[hN + i] = Dr;
         dg[hN + i] = dy_y;
     }
-    __builtin_amdgcn_wave_barrier();
-    // dS_t = P_t (do . v_t - D): row dot products again
-    float dv[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) dv[e] = s_d[wave][VEC * rpart + e];
-#pragma unroll 8
-    for (int t0 = 0; t0 < ntok; t0 += RPI) {
-        const int t = t0 + rsub;
-        const int64_t tok = s_tok[wave][min(t, ntok - 1)];
-        float vv[VEC];
-        ld16f<T>(v + tok * D + VEC * rpart, vv);
-        float dp = 0.0f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) dp += dv[e] * vv[e];
-        dp = group_sum<LPR>(dp);
-        if (t < ntok && rpart == 0) s_s[wave][t] = s_s[wave][t] * (dp - Dr);
-    }
-    __builtin_amdgcn_wave_barrier();
-    float acc[NX];
-#pragma unroll
-    for (int n = 0; n < NX; ++n) acc[n] = 0.0f;
-#pragma unroll 8
-    for (int t = 0; t < ntok; ++t) {
-        const float dst = s_s[wave][t];
-        float kk[NX];
-        ldnx<T, NX>(k + s_tok[wave][t] * D + NX * lane, kk);
-#pragma unroll
-        for (int n = 0; n < NX; ++n) acc[n] += dst * kk[n];
-    }
-#pragma unroll
-    for (int n = 0; n < NX; ++n) dq[row + NX * lane + n] += p.scale * acc[n];
 }
 
 // ---- the (query, rank) pairs as sort keys: key = head * C + cell (or H * C when the
-// rank is empty, which sorts past every cell), value = the query
+// rank is empty, which sorts past every cell), value = the pair's index within its
+// head, query * K + rank
 __global__ void bwd_pair_keys_kernel(const int32_t *__restrict__ sel, uint32_t *__restrict__ key,
                                      uint32_t *__restrict__ val, KParams p) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= (int64_t)p.H * p.N * p.K) return;
-    const int64_t hi = e / p.K;  // head * N + query
+    const int64_t h = e / ((int64_t)p.N * p.K);
     const int32_t c = sel[e];
-    const int64_t h = hi / p.N;
     key[e] = c >= 0 ? (uint32_t)(h * p.C + c) : (uint32_t)(p.H * p.C);
-    val[e] = (uint32_t)(hi - h * p.N);
+    val[e] = (uint32_t)(e - h * p.N * p.K);
 }
 
 // ---- each cell's run [seg[2 c], seg[2 c + 1]) of the sorted pairs (empty: 0, 0); the
@@ -659,14 +628,18 @@ __global__ void bwd_seg_mark_kernel(const uint32_t *__restrict__ key, int64_t n,
 
 // ---- long branch, key side. CHUNKS = false: one work-group per (head, cell) with at
 // most kHeavyPairs selectors, adding to dk, dv; CHUNKS = true: one work-group per
-// chunk of a heavier cell, writing its sums to part[item]. One wave per 16 of the
-// cell's tokens holds their keys and values as B operands of the fp32 matrix cores
-// (dims (d/4) g .. of token c in lane (c, g)); the queries that selected the cell,
+// chunk of a heavier cell, writing its sums to part[item]. The cell's keys and values
+// wait in LDS; one wave per 16 of the cell's tokens takes them as B operands of the
+// fp32 matrix cores (dims (d/4) g .. of token c in lane (c, g)); the queries that selected the cell,
 // in query order (a stable sort of the pairs by cell), are gathered 16 at a time into
 // LDS (q as fp32 and unrotated, written by bwd_long_q: the long branch has no RoPE;
 // and the gradient reaching the softmax output). S = Q K^T and dP = do V^T put queries 4 g + r of token c in
 // lane (c, g); P = exp(scale S - lse), dS = P (dP - D), then dv^T += do^T P and
-// dk^T += Q^T dS (times the scale) take P and dS straight from that layout.
+// dk^T += Q^T dS (times the scale) take P and dS straight from that layout. dS also
+// goes to LDS transposed, where dq^T = K^T dS^T (times the scale) over all the cell's
+// tokens gives each selector's dq from this cell: wave w forms dims (d / waves) w ..
+// from the cell's keys in LDS and writes them to the selector's (query, rank) row of
+// dqp, which bwd_dq_long_sum adds to dq in rank order.
 namespace {
 // 16 bytes of T at p as four floats (4 fp32, or 4 bf16 from 8 bytes)
 template <typename T> __device__ __forceinline__ float4 ld4f(const T *p);
@@ -733,6 +706,15 @@ struct BRow<float, KS> {
             x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
         }
     }
+    // the same dims of row `row` of a GTile
+    template <int D> __device__ void load_tile(const float *tile, int row, int g) {
+        using G = GTile<float, D>;
+#pragma unroll
+        for (int i = 0; i < KS / 4; ++i) {
+            const float4 f = *reinterpret_cast<const float4 *>(tile + G::off(row, KS / 4 * g + i));
+            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+        }
+    }
     __device__ float operator()(int i) const { return x[i]; }
 };
 template <int KS>
@@ -742,6 +724,14 @@ struct BRow<uint16_t, KS> {
 #pragma unroll
         for (int i = 0; i < KS / 8; ++i) {
             const uint4 u = *reinterpret_cast<const uint4 *>(src + 8 * i);
+            w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+        }
+    }
+    template <int D> __device__ void load_tile(const uint16_t *tile, int row, int g) {
+        using G = GTile<uint16_t, D>;
+#pragma unroll
+        for (int i = 0; i < KS / 8; ++i) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(tile + G::off(row, KS / 8 * g + i));
             w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
         }
     }
@@ -759,6 +749,20 @@ __device__ __forceinline__ void gtile_tmul(const T *tile, int col, int g, const 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int d = 16 * dt + col;
+            const float a = to_f32<T>(tile[G::off(4 * g + r, d / G::EPC) + d % G::EPC]);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, w[r], acc[dt], 0, 0, 0);
+        }
+}
+// acc[dt] (dims 16 (dt0 + dt) + 4 g + r, column c) += sum over the tile rows of
+// tile[row][dim] w(row, c), as gtile_tmul for NDT of the D / 16 dim tiles
+template <typename T, int D, int NDT>
+__device__ __forceinline__ void gtile_tmul_part(const T *tile, int dt0, int col, int g, const float *w, floatx4 *acc) {
+    using G = GTile<T, D>;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * (dt0 + dt) + col;
             const float a = to_f32<T>(tile[G::off(4 * g + r, d / G::EPC) + d % G::EPC]);
             acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, w[r], acc[dt], 0, 0, 0);
         }
@@ -786,10 +790,15 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
                                                                     const float *__restrict__ lse_l,
                                                                     const float *__restrict__ D_l,
                                                                     float *__restrict__ dk, float *__restrict__ dv,
-                                                                    float *__restrict__ part, KParams p) {
+                                                                    float *__restrict__ part, float *__restrict__ dqp,
+                                                                    KParams p) {
     constexpr int NWV = S / 16;          // waves, 16 tokens each
     constexpr int KS = D / 4;
     constexpr int QT = 16;               // selectors per tile
+    constexpr int DQT = D / 16 / NWV;    // 16-dim tiles of dq per wave
+    constexpr int DSLD = QT + 1;         // row stride of the transposed dS
+    using G = GTile<T, D>;
+    static_assert(DQT >= 1 && DQT * NWV * 16 == D, "whole dq dim tiles per wave");
     // two named buffers of each kind, so that the compiler can tell a tile's copy from
     // the reads of the other buffer
     __shared__ __attribute__((aligned(1024))) float s_q0[QT * D];
@@ -797,6 +806,10 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
     __shared__ __attribute__((aligned(1024))) float s_o0[QT * D];
     __shared__ __attribute__((aligned(1024))) float s_o1[QT * D];
     __shared__ int64_t s_rows[2][QT];              // the gathered rows of two tiles
+    __shared__ int32_t s_pair[2][QT];              // their (query, rank) rows of dqp
+    __shared__ __attribute__((aligned(16))) T s_k[S * D];  // the cell's keys, 16-token tiles
+    __shared__ __attribute__((aligned(16))) T s_v[S * D];  // and values
+    __shared__ float s_ds[S * DSLD];               // dS of the current tile, [token][selector]
     int64_t cid;  // head * C + cell
     int64_t e0, e1;
     if constexpr (CHUNKS) {
@@ -819,10 +832,16 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
     const int wave = tid >> 6;
     const int tok = 16 * wave + col;                  // this lane's token within the cell
     const int64_t jrow = hN + c * S + tok;
-    // this lane's token as B operands: dims KS g .. KS g + KS - 1
-    BRow<T, KS> kb, vb;
-    kb.load(k + jrow * D + KS * g);
-    vb.load(v + jrow * D + KS * g);
+    const int64_t hNK = hN * p.K;
+    // the cell's keys and values into LDS, one GTile per 16 tokens (read after the first
+    // barrier below)
+    for (int pc = tid; pc < S * G::CPR; pc += 64 * NWV) {
+        const int tk = pc / G::CPR, ch = pc % G::CPR;
+        const int at = (tk / 16) * G::ELEMS + G::off(tk % 16, ch);
+        const int64_t src = (hN + c * S + tk) * D + G::EPC * ch;
+        *reinterpret_cast<uint4 *>(s_k + at) = *reinterpret_cast<const uint4 *>(k + src);
+        *reinterpret_cast<uint4 *>(s_v + at) = *reinterpret_cast<const uint4 *>(v + src);
+    }
     floatx4 acck[D / 16], accv[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acck[dt] = accv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -832,8 +851,9 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
     // tile t + 2 go out before the copies of tile t + 1, which are issued every tile
     // (a repeat past the end), so that waiting for those loads never waits for a copy.
     const int ntile = (int)((e1 - e0 + QT - 1) / QT);
-    auto sel_row = [&](int t) __attribute__((always_inline)) {
-        return hN + (int64_t)sq[min(e0 + (int64_t)QT * t + (tid & (QT - 1)), e1 - 1)];
+    // the sorted pairs hold query * K + rank
+    auto sel_val = [&](int t) __attribute__((always_inline)) {
+        return (int64_t)sq[min(e0 + (int64_t)QT * t + (tid & (QT - 1)), e1 - 1)];
     };
     auto issue = [&](int slot, float *bq, float *bo) __attribute__((always_inline)) {
         gtile_issue<float, D, NWV>(q, s_rows[slot], bq, wave, lane);
@@ -848,9 +868,13 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
             lv[r] = lse_l[ii];
             dd[r] = D_l[ii];
         }
-        const int64_t nrow = sel_row(t + 2);
+        const int64_t nval = sel_val(t + 2);
         issue(slot ^ 1, nq, no);  // tile t + 1
+        // this lane's token as B operands: dims KS g .. KS g + KS - 1
+        BRow<T, KS> kb, vb;
+        kb.template load_tile<D>(s_k + wave * G::ELEMS, col, g);
         const floatx4 sv = gtile_dot<float, D>(bq, col, g, kb);
+        vb.template load_tile<D>(s_v + wave * G::ELEMS, col, g);
         const floatx4 dp = gtile_dot<float, D>(bo, col, g, vb);
         float P[4], ds[4];
 #pragma unroll
@@ -862,14 +886,40 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
         }
         gtile_tmul<float, D>(bo, col, g, P, accv);
         gtile_tmul<float, D>(bq, col, g, ds, acck);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_ds[tok * DSLD + 4 * g + r] = ds[r];
+        const int64_t prow = hNK + s_pair[slot][col];  // this lane's column of the dq tile
+        const bool pok = e0 + (int64_t)QT * t + col < e1;
         wait_vmem();
         __syncthreads();  // tile t + 1 has landed; every wave is done with this tile and its rows
-        if (tid < QT) s_rows[slot][tid] = nrow;
+        float w[NWV][4];
+#pragma unroll
+        for (int j = 0; j < NWV; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[j][r] = s_ds[(16 * j + 4 * g + r) * DSLD + col];
+        // one 16-dim tile at a time, each stored before the next, to keep few registers live
+#pragma unroll 1
+        for (int dt = 0; dt < DQT; ++dt) {
+            floatx4 accq = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NWV; ++j)
+                gtile_tmul_part<T, D, 1>(s_k + j * G::ELEMS, DQT * wave + dt, col, g, w[j], &accq);
+            if (pok)
+                *reinterpret_cast<float4 *>(dqp + prow * D + 16 * (DQT * wave + dt) + 4 * g) =
+                    make_float4(p.scale * accq[0], p.scale * accq[1], p.scale * accq[2], p.scale * accq[3]);
+        }
+        if (tid < QT) {
+            s_rows[slot][tid] = hN + nval / p.K;
+            s_pair[slot][tid] = (int32_t)nval;
+        }
         __syncthreads();
     };
     if (tid < QT) {
-        s_rows[0][tid] = sel_row(0);
-        s_rows[1][tid] = sel_row(1);
+        const int64_t v0 = sel_val(0), v1 = sel_val(1);
+        s_rows[0][tid] = hN + v0 / p.K;
+        s_rows[1][tid] = hN + v1 / p.K;
+        s_pair[0][tid] = (int32_t)v0;
+        s_pair[1][tid] = (int32_t)v1;
     }
     __syncthreads();
     issue(0, s_q0, s_o0);
@@ -932,6 +982,28 @@ __global__ __launch_bounds__(kThreads) void bwd_heavy_reduce_kernel(const int32_
     }
 }
 
+// ---- the long branch's dq: each query's (query, rank) rows of dqp added to dq in rank
+// order (ranks without a cell have no row); one thread per 4 dims
+__global__ __launch_bounds__(kThreads) void bwd_dq_long_sum_kernel(const int32_t *__restrict__ sel,
+                                                                   const float *__restrict__ dqp,
+                                                                   float *__restrict__ dq, KParams p) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int d4 = p.d / 4;
+    if (e >= (int64_t)p.H * p.N * d4) return;
+    const int64_t row = e / d4;  // head * N + query
+    const int x = 4 * (int)(e % d4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < p.K; ++r) {
+        if (sel[row * p.K + r] < 0) continue;
+        const float4 v = *reinterpret_cast<const float4 *>(dqp + (row * p.K + r) * p.d + x);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    float4 *o = reinterpret_cast<float4 *>(dq + row * p.d + x);
+    float4 a = *o;
+    a.x += acc.x; a.y += acc.y; a.z += acc.z; a.w += acc.w;
+    *o = a;
+}
+
 // ---- dgamma of each head: the per-query terms summed in a fixed order
 __global__ __launch_bounds__(kThreads) void bwd_dgamma_kernel(const float *__restrict__ dg, float *__restrict__ dgamma,
                                                               KParams p) {
@@ -973,7 +1045,7 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
     // the long branch's query side also leaves the queries in fp32, unrotated, in qr's
     // storage, which the window kernels no longer need
     float *q32 = w.qr;
-    hipLaunchKernelGGL((bwd_long_q_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, k, v, w.dO, sel, dq, w.do_l,
+    hipLaunchKernelGGL((bwd_long_q_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, k, v, w.dO, sel, w.do_l,
                        w.lse_l, w.D_l, w.dg, q32, p);
     if (p.C > 0) {
         // each cell's selecting queries in query order: a stable sort of the pairs by cell
@@ -993,14 +1065,17 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
         hipLaunchKernelGGL(bwd_heavy_list_kernel, dim3((unsigned)((ncell + 255) / 256)), dim3(256), 0, st, w.cseg,
                            ncell, w.hcount, w.hitems, w.hcells);
         hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, false>), dim3((unsigned)ncell), dim3(64 * (S / 16)), 0, st, q32, k,
-                           v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, p);
+                           v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, w.dqp, p);
         const int64_t mi = heavy_items_max(p), mh = heavy_cells_max(p);
         if (mi > 0) {
             hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, true>), dim3((unsigned)mi), dim3(64 * (S / 16)), 0, st, q32, k,
-                               v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, p);
+                               v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, w.dqp, p);
             hipLaunchKernelGGL((bwd_heavy_reduce_kernel<D, S>), dim3((unsigned)mh), dim3(kThreads), 0, st, w.hcells,
                                w.hcount, w.hpart, dk, dv, p);
         }
+        const int64_t n4 = (int64_t)p.H * p.N * (p.d / 4);
+        hipLaunchKernelGGL(bwd_dq_long_sum_kernel, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                           st, sel, w.dqp, dq, p);
     }
     hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((unsigned)p.H), dim3(kThreads), 0, st, w.dg, dgamma, p);
     return hipGetLastError();
