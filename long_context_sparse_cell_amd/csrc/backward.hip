@@ -61,6 +61,32 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+// sum over the lanes that share lane % G (G = 8, 16 or 32)
+template <int G>
+__device__ __forceinline__ float rows_sum(float x) {
+    if constexpr (G <= 8) x += __shfl_xor(x, 8);
+    if constexpr (G <= 16) {
+        const uint32_t u = __float_as_uint(x);
+        const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    const uint32_t u = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// a . b over 8 bf16 (two per dword), on the packed dot-product instruction: the
+// products are exact in fp32, the sum is fp32
+__device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b) {
+    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x),
+                                                0.0f, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc,
+                                          false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc,
+                                          false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc,
+                                           false);
+}
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -424,9 +450,10 @@ __global__ __launch_bounds__(256, 2) void bwd_win_dkv_kernel(const float *__rest
 // branch's softmax over the selected cells' tokens, o_long and RMSNorm's backward;
 // writes the gradient reaching the softmax output (do_l), the row's lse and D, the
 // query's dgamma term and the query in fp32 (for the key side, which also forms the
-// branch's dq). The score dot products read whole token rows per instruction: 16
-// bytes per lane, the lanes of one row summing their parts; the sum over tokens (o)
-// gives each lane NX = d/64 consecutive dims.
+// branch's dq). Both passes over the tokens read whole rows, 16 bytes per lane: the
+// scores with the lanes of one row summing their parts (bf16 rows on the packed
+// dot-product instruction), o_long with each group of lanes summing its share of the
+// tokens over the same 16-byte dims, then the groups added.
 namespace {
 // the 16 bytes at p as floats (8 bf16 or 4 fp32)
 template <typename T> __device__ __forceinline__ void ld16f(const T *p, float *dst);
@@ -443,20 +470,6 @@ template <> __device__ __forceinline__ void ld16f<float>(const float *p, float *
     const float4 f = *reinterpret_cast<const float4 *>(p);
     dst[0] = f.x; dst[1] = f.y; dst[2] = f.z; dst[3] = f.w;
 }
-// NX (1 or 2) consecutive elements at p as floats
-template <typename T, int NX> __device__ __forceinline__ void ldnx(const T *p, float *dst) {
-    if constexpr (NX == 2 && sizeof(T) == 2) {
-        const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
-        dst[0] = __uint_as_float(u << 16);
-        dst[1] = __uint_as_float(u & 0xFFFF0000u);
-    } else if constexpr (NX == 2) {
-        const float2 f = *reinterpret_cast<const float2 *>(p);
-        dst[0] = f.x;
-        dst[1] = f.y;
-    } else {
-        dst[0] = to_f32<T>(p[0]);
-    }
-}
 }  // namespace
 
 template <typename T, int D>
@@ -466,13 +479,12 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
                                                               float *__restrict__ do_l, float *__restrict__ lse_l,
                                                               float *__restrict__ D_l, float *__restrict__ dg,
                                                               float *__restrict__ q32, KParams p) {
-    constexpr int NX = D / 64;             // consecutive dims per lane in sums over tokens
-    constexpr int VEC = 16 / sizeof(T);    // elements per lane in row dot products
+    constexpr int VEC = 16 / sizeof(T);    // elements per lane in a row read
     constexpr int LPR = D / VEC;           // lanes per row
     constexpr int RPI = 64 / LPR;          // rows per wave instruction
     constexpr int MAXT = 8 * 64;           // K * s at most
     __shared__ float s_s[4][MAXT];
-    __shared__ int64_t s_tok[4][MAXT];
+    __shared__ int32_t s_tok[4][MAXT];  // token rows head * N + j (below 2^31: H N K < 2^31)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nqw = (int)((p.N + 3) / 4);
     const int h = blockIdx.x / nqw;
@@ -484,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     for (int u = 0; u < p.K; ++u) {
         const int32_t c = sel[(hN + i) * p.K + u];
         if (c < 0) continue;
-        for (int t = lane; t < p.s; t += 64) s_tok[wave][ntok + t] = hN + (int64_t)c * p.s + t;
+        for (int t = lane; t < p.s; t += 64) s_tok[wave][ntok + t] = (int32_t)(hN + (int64_t)c * p.s + t);
         ntok += p.s;
     }
     if (ntok == 0) {
@@ -498,6 +510,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     __builtin_amdgcn_wave_barrier();
     const int rsub = lane / LPR, rpart = lane % LPR;  // row of the instruction, 16-byte part of it
     // scores: row dot products, the LPR lanes of a row summing their VEC products
+    const uint4 qraw = *reinterpret_cast<const uint4 *>(q + row + VEC * rpart);
     float qv[VEC];
     ld16f<T>(q + row + VEC * rpart, qv);
     // the query as fp32 for the key side (bwd_long_kv)
@@ -510,11 +523,15 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     for (int t0 = 0; t0 < ntok; t0 += RPI) {
         const int t = t0 + rsub;
         const int64_t tok = s_tok[wave][min(t, ntok - 1)];
-        float kv[VEC];
-        ld16f<T>(k + tok * D + VEC * rpart, kv);
         float dot = 0.0f;
+        if constexpr (sizeof(T) == 2) {
+            dot = dot8_bf16(qraw, *reinterpret_cast<const uint4 *>(k + tok * D + VEC * rpart));
+        } else {
+            float kv[VEC];
+            ld16f<T>(k + tok * D + VEC * rpart, kv);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) dot += qv[e] * kv[e];
+            for (int e = 0; e < VEC; ++e) dot += qv[e] * kv[e];
+        }
         dot = group_sum<LPR>(dot);
         if (t < ntok) {
             if (rpart == 0) s_s[wave][t] = dot * p.scale;
@@ -529,42 +546,53 @@ __global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restric
     const float lse = mx + __logf(sum);
     for (int t = lane; t < ntok; t += 64) s_s[wave][t] = __expf(s_s[wave][t] - lse);  // P_t
     __builtin_amdgcn_wave_barrier();
-    // o_long, RMSNorm and its backward (lane: dims NX lane .. NX lane + NX - 1)
-    float o[NX], dout_[NX], y[NX];
+    // o_long: lanes of row group rsub take tokens rsub, rsub + RPI, ... over dims VEC rpart ..,
+    // then the groups are added (every lane ends with its dims' sums)
+    float o[VEC];
 #pragma unroll
-    for (int n = 0; n < NX; ++n) {
-        o[n] = 0.0f;
-        dout_[n] = dO[row + NX * lane + n];
-    }
-#pragma unroll 8
-    for (int t = 0; t < ntok; ++t) {
-        const float pt = s_s[wave][t];
-        float vv[NX];
-        ldnx<T, NX>(v + s_tok[wave][t] * D + NX * lane, vv);
+    for (int e = 0; e < VEC; ++e) o[e] = 0.0f;
+#pragma unroll 4
+    for (int t0 = 0; t0 < ntok; t0 += RPI) {
+        const int t = t0 + rsub;
+        const int tc = min(t, ntok - 1);
+        const float pt = t < ntok ? s_s[wave][tc] : 0.0f;
+        float vv[VEC];
+        ld16f<T>(v + (int64_t)s_tok[wave][tc] * D + VEC * rpart, vv);
 #pragma unroll
-        for (int n = 0; n < NX; ++n) o[n] += pt * vv[n];
+        for (int e = 0; e < VEC; ++e) o[e] += pt * vv[e];
     }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = rows_sum<LPR>(o[e]);
+    // RMSNorm and its backward over dims VEC rpart .. (the lanes of row group 0 count
+    // in the sums over dims and store)
+    const bool lead = rsub == 0;
+    float dout_[VEC], y[VEC];
+    ld16f<float>(dO + row + VEC * rpart, dout_);
+    if constexpr (VEC == 8) ld16f<float>(dO + row + VEC * rpart + 4, dout_ + 4);
     float ss = 0.0f;
 #pragma unroll
-    for (int n = 0; n < NX; ++n) ss += o[n] * o[n];
-    ss = wave_sum(ss);
+    for (int e = 0; e < VEC; ++e) ss += o[e] * o[e];
+    ss = wave_sum(lead ? ss : 0.0f);
     const float rr = sqrtf(ss / (float)D + p.rms_eps);
     const float gam = p.gamma[h];
     float dy_y = 0.0f;
 #pragma unroll
-    for (int n = 0; n < NX; ++n) {
-        y[n] = o[n] / rr;
-        dy_y += dout_[n] * y[n];
+    for (int e = 0; e < VEC; ++e) {
+        y[e] = o[e] / rr;
+        dy_y += dout_[e] * y[e];
     }
-    dy_y = wave_sum(dy_y);  // dout . y
-    float Dsum = 0.0f;
+    dy_y = wave_sum(lead ? dy_y : 0.0f);  // dout . y
+    float Dsum = 0.0f, d_o[VEC];
 #pragma unroll
-    for (int n = 0; n < NX; ++n) {
-        const float d_o = (gam * dout_[n] - y[n] * (gam * dy_y) / (float)D) / rr;
-        do_l[row + NX * lane + n] = d_o;
-        Dsum += d_o * o[n];
+    for (int e = 0; e < VEC; ++e) {
+        d_o[e] = (gam * dout_[e] - y[e] * (gam * dy_y) / (float)D) / rr;
+        Dsum += d_o[e] * o[e];
     }
-    const float Dr = wave_sum(Dsum);
+    if (lead)
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+            *reinterpret_cast<float4 *>(do_l + row + VEC * rpart + e) = make_float4(d_o[e], d_o[e + 1], d_o[e + 2], d_o[e + 3]);
+    const float Dr = wave_sum(lead ? Dsum : 0.0f);
     if (lane == 0) {
         lse_l[hN + i] = lse;
         D_l[hN + i] = Dr;
