@@ -161,7 +161,7 @@ size_t decode_bytes(const fsl_params *p, int32_t n_seq) {
 // runs and heavy-cell chunk sums, and the long branch's dq of every (query, rank) pair
 struct BwdLayout {
     size_t rope, qr, kr, dO, do_l, lse_w, D_w, lse_l, D_l, dg, pkey, pval, pkey2, pval2, shist, stot, cseg, hcount,
-        hitems, hcells, hpart, dqp, status, total;
+        hitems, hcells, hpart, dqp, pml, status, total;
 };
 
 // the long branch's key side sorts the H N K (query, rank) pairs with 32-bit indices
@@ -195,6 +195,7 @@ BwdLayout bwd_layout(const KParams &k) {
     L.hcells = take((size_t)heavy_cells_max(k) * 3 * sizeof(int32_t));
     L.hpart = take((size_t)heavy_items_max(k) * 2 * k.s * k.d * sizeof(float));
     L.dqp = take((size_t)npair * k.d * sizeof(float));
+    L.pml = take((size_t)npair * sizeof(float2));
     L.status = take(sizeof(uint32_t));
     L.total = off;
     return L;
@@ -440,6 +441,7 @@ int fsl_attn_bwd(const void *q, const void *k, const void *v, const void *dout, 
     w.hcells = (int32_t *)(b + BL.hcells);
     w.hpart = (float *)(b + BL.hpart);
     w.dqp = (float *)(b + BL.dqp);
+    w.pml = (float2 *)(b + BL.pml);
     w.status = (uint32_t *)(b + BL.status);
     return hip_status(launch_attn_bwd(q, k, v, dout, (const int32_t *)(f + FL.sel), (const int32_t *)(f + FL.pool), w, dq, dk, dv, dgamma, kp, stream));
 }

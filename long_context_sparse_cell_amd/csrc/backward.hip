@@ -19,18 +19,19 @@
 //                   and dq (window part), on the fp32 matrix cores
 //   bwd_win_dkv     per 64 keys: dk, dv of the window over the queries that see them,
 //                   on the fp32 matrix cores
-//   bwd_long_q      per query (one wave): o_long and RMSNorm's backward
 //   bwd_pair_keys, a stable radix sort (sort.hip), bwd_seg_*: each cell's
 //                   selecting queries in query order
+//   bwd_long_fwd    per cell: the branch's softmax over the cell's tokens for every query
+//                   that selected it (max, sum, weighted values), on the fp32 matrix cores
+//   bwd_long_merge  per query (one wave): its cells combined in rank order into o_long,
+//                   lse; RMSNorm's backward
 //   bwd_long_kv     per cell: dk, dv += long part over every query that selected it,
 //                   and each (query, rank) pair's dq, on the fp32 matrix cores; cells
 //                   chosen by more than kHeavyPairs queries in chunks whose dk, dv sums
 //                   bwd_heavy_reduce adds in chunk order
 //   bwd_dq_long_sum per query: dq += its pairs' dq in rank order
 //   bwd_dgamma      per head: dgamma summed in a fixed order
-// Arithmetic is fp32: the window's products and the long branch's gradient products
-// on the matrix cores (fp32 MFMA), the long branch's forward recompute on the vector
-// ALUs.
+// Arithmetic is fp32, every product on the matrix cores (fp32 MFMA).
 #include <climits>
 
 #include "fsl_internal.h"
@@ -61,32 +62,6 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
-// sum over the lanes that share lane % G (G = 8, 16 or 32)
-template <int G>
-__device__ __forceinline__ float rows_sum(float x) {
-    if constexpr (G <= 8) x += __shfl_xor(x, 8);
-    if constexpr (G <= 16) {
-        const uint32_t u = __float_as_uint(x);
-        const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    }
-    const uint32_t u = __float_as_uint(x);
-    const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// a . b over 8 bf16 (two per dword), on the packed dot-product instruction: the
-// products are exact in fp32, the sum is fp32
-__device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b) {
-    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x),
-                                                0.0f, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc,
-                                          false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc,
-                                          false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc,
-                                           false);
-}
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -446,160 +421,6 @@ __global__ __launch_bounds__(256, 2) void bwd_win_dkv_kernel(const float *__rest
             make_float4(accv[dt][0], accv[dt][1], accv[dt][2], accv[dt][3]);
 }
 
-// ---- long branch, query side: one wave per query (4 per work-group). Recomputes the
-// branch's softmax over the selected cells' tokens, o_long and RMSNorm's backward;
-// writes the gradient reaching the softmax output (do_l), the row's lse and D, the
-// query's dgamma term and the query in fp32 (for the key side, which also forms the
-// branch's dq). Both passes over the tokens read whole rows, 16 bytes per lane: the
-// scores with the lanes of one row summing their parts (bf16 rows on the packed
-// dot-product instruction), o_long with each group of lanes summing its share of the
-// tokens over the same 16-byte dims, then the groups added.
-namespace {
-// the 16 bytes at p as floats (8 bf16 or 4 fp32)
-template <typename T> __device__ __forceinline__ void ld16f(const T *p, float *dst);
-template <> __device__ __forceinline__ void ld16f<uint16_t>(const uint16_t *p, float *dst) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        dst[2 * e] = __uint_as_float(w[e] << 16);
-        dst[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-    }
-}
-template <> __device__ __forceinline__ void ld16f<float>(const float *p, float *dst) {
-    const float4 f = *reinterpret_cast<const float4 *>(p);
-    dst[0] = f.x; dst[1] = f.y; dst[2] = f.z; dst[3] = f.w;
-}
-}  // namespace
-
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bwd_long_q_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                              const T *__restrict__ v, const float *__restrict__ dO,
-                                                              const int32_t *__restrict__ sel,
-                                                              float *__restrict__ do_l, float *__restrict__ lse_l,
-                                                              float *__restrict__ D_l, float *__restrict__ dg,
-                                                              float *__restrict__ q32, KParams p) {
-    constexpr int VEC = 16 / sizeof(T);    // elements per lane in a row read
-    constexpr int LPR = D / VEC;           // lanes per row
-    constexpr int RPI = 64 / LPR;          // rows per wave instruction
-    constexpr int MAXT = 8 * 64;           // K * s at most
-    __shared__ float s_s[4][MAXT];
-    __shared__ int32_t s_tok[4][MAXT];  // token rows head * N + j (below 2^31: H N K < 2^31)
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nqw = (int)((p.N + 3) / 4);
-    const int h = blockIdx.x / nqw;
-    const int64_t i = (int64_t)(blockIdx.x % nqw) * 4 + wave;
-    if (i >= p.N) return;  // this wave only: no work-group barrier below
-    const int64_t hN = (int64_t)h * p.N;
-    const int64_t row = (hN + i) * D;
-    int ntok = 0;
-    for (int u = 0; u < p.K; ++u) {
-        const int32_t c = sel[(hN + i) * p.K + u];
-        if (c < 0) continue;
-        for (int t = lane; t < p.s; t += 64) s_tok[wave][ntok + t] = (int32_t)(hN + (int64_t)c * p.s + t);
-        ntok += p.s;
-    }
-    if (ntok == 0) {
-        for (int x = lane; x < D; x += 64) {
-            do_l[row + x] = 0.0f;
-            q32[row + x] = ld(q, row + x);
-        }
-        if (lane == 0) { lse_l[hN + i] = 0.0f; D_l[hN + i] = 0.0f; dg[hN + i] = 0.0f; }
-        return;
-    }
-    __builtin_amdgcn_wave_barrier();
-    const int rsub = lane / LPR, rpart = lane % LPR;  // row of the instruction, 16-byte part of it
-    // scores: row dot products, the LPR lanes of a row summing their VEC products
-    const uint4 qraw = *reinterpret_cast<const uint4 *>(q + row + VEC * rpart);
-    float qv[VEC];
-    ld16f<T>(q + row + VEC * rpart, qv);
-    // the query as fp32 for the key side (bwd_long_kv)
-    if (rsub == 0)
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4)
-            *reinterpret_cast<float4 *>(q32 + row + VEC * rpart + e) = make_float4(qv[e], qv[e + 1], qv[e + 2], qv[e + 3]);
-    float mx = -INFINITY;
-#pragma unroll 8
-    for (int t0 = 0; t0 < ntok; t0 += RPI) {
-        const int t = t0 + rsub;
-        const int64_t tok = s_tok[wave][min(t, ntok - 1)];
-        float dot = 0.0f;
-        if constexpr (sizeof(T) == 2) {
-            dot = dot8_bf16(qraw, *reinterpret_cast<const uint4 *>(k + tok * D + VEC * rpart));
-        } else {
-            float kv[VEC];
-            ld16f<T>(k + tok * D + VEC * rpart, kv);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) dot += qv[e] * kv[e];
-        }
-        dot = group_sum<LPR>(dot);
-        if (t < ntok) {
-            if (rpart == 0) s_s[wave][t] = dot * p.scale;
-            mx = fmaxf(mx, dot * p.scale);
-        }
-    }
-    mx = wave_max(mx);
-    __builtin_amdgcn_wave_barrier();
-    float sum = 0.0f;
-    for (int t = lane; t < ntok; t += 64) sum += __expf(s_s[wave][t] - mx);
-    sum = wave_sum(sum);
-    const float lse = mx + __logf(sum);
-    for (int t = lane; t < ntok; t += 64) s_s[wave][t] = __expf(s_s[wave][t] - lse);  // P_t
-    __builtin_amdgcn_wave_barrier();
-    // o_long: lanes of row group rsub take tokens rsub, rsub + RPI, ... over dims VEC rpart ..,
-    // then the groups are added (every lane ends with its dims' sums)
-    float o[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) o[e] = 0.0f;
-#pragma unroll 4
-    for (int t0 = 0; t0 < ntok; t0 += RPI) {
-        const int t = t0 + rsub;
-        const int tc = min(t, ntok - 1);
-        const float pt = t < ntok ? s_s[wave][tc] : 0.0f;
-        float vv[VEC];
-        ld16f<T>(v + (int64_t)s_tok[wave][tc] * D + VEC * rpart, vv);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] += pt * vv[e];
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) o[e] = rows_sum<LPR>(o[e]);
-    // RMSNorm and its backward over dims VEC rpart .. (the lanes of row group 0 count
-    // in the sums over dims and store)
-    const bool lead = rsub == 0;
-    float dout_[VEC], y[VEC];
-    ld16f<float>(dO + row + VEC * rpart, dout_);
-    if constexpr (VEC == 8) ld16f<float>(dO + row + VEC * rpart + 4, dout_ + 4);
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) ss += o[e] * o[e];
-    ss = wave_sum(lead ? ss : 0.0f);
-    const float rr = sqrtf(ss / (float)D + p.rms_eps);
-    const float gam = p.gamma[h];
-    float dy_y = 0.0f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        y[e] = o[e] / rr;
-        dy_y += dout_[e] * y[e];
-    }
-    dy_y = wave_sum(lead ? dy_y : 0.0f);  // dout . y
-    float Dsum = 0.0f, d_o[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        d_o[e] = (gam * dout_[e] - y[e] * (gam * dy_y) / (float)D) / rr;
-        Dsum += d_o[e] * o[e];
-    }
-    if (lead)
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4)
-            *reinterpret_cast<float4 *>(do_l + row + VEC * rpart + e) = make_float4(d_o[e], d_o[e + 1], d_o[e + 2], d_o[e + 3]);
-    const float Dr = wave_sum(lead ? Dsum : 0.0f);
-    if (lane == 0) {
-        lse_l[hN + i] = lse;
-        D_l[hN + i] = Dr;
-        dg[hN + i] = dy_y;
-    }
-}
-
 // ---- the (query, rank) pairs as sort keys: key = head * C + cell (or H * C when the
 // rank is empty, which sorts past every cell), value = the pair's index within its
 // head, query * K + rank
@@ -660,8 +481,8 @@ __global__ void bwd_seg_mark_kernel(const uint32_t *__restrict__ key, int64_t n,
 // wait in LDS; one wave per 16 of the cell's tokens takes them as B operands of the
 // fp32 matrix cores (dims (d/4) g .. of token c in lane (c, g)); the queries that selected the cell,
 // in query order (a stable sort of the pairs by cell), are gathered 16 at a time into
-// LDS (q as fp32 and unrotated, written by bwd_long_q: the long branch has no RoPE;
-// and the gradient reaching the softmax output). S = Q K^T and dP = do V^T put queries 4 g + r of token c in
+// LDS (q as fp32 and unrotated, written by bwd_long_merge: the long branch has no
+// RoPE; and the gradient reaching the softmax output). S = Q K^T and dP = do V^T put queries 4 g + r of token c in
 // lane (c, g); P = exp(scale S - lse), dS = P (dP - D), then dv^T += do^T P and
 // dk^T += Q^T dS (times the scale) take P and dS straight from that layout. dS also
 // goes to LDS transposed, where dq^T = K^T dS^T (times the scale) over all the cell's
@@ -805,7 +626,204 @@ __device__ __forceinline__ void gtile_issue(const T *base, const int64_t *rows, 
         lds_dma16(base + rows[r] * D + G::EPC * (phys ^ (r & (G::CPR - 1))), tile + 64 * G::EPC * u);
     }
 }
+
+// the selectors e0 .. e1 - 1 (sorted pairs) of a light cell, or of one chunk of a heavy one
+template <bool CHUNKS>
+__device__ __forceinline__ bool cell_run(const int32_t *seg, const int32_t *items, const int32_t *counters,
+                                         int64_t &cid, int64_t &e0, int64_t &e1) {
+    if constexpr (CHUNKS) {
+        if ((int)blockIdx.x >= counters[0]) return false;
+        cid = items[2 * blockIdx.x];
+        const int64_t j = items[2 * blockIdx.x + 1];
+        const int64_t a = seg[2 * cid], z = seg[2 * cid + 1];
+        e0 = a + j * kHeavyPairs;
+        e1 = min(z, e0 + kHeavyPairs);
+        return true;
+    } else {
+        cid = blockIdx.x;
+        e0 = seg[2 * cid];
+        e1 = seg[2 * cid + 1];
+        return e0 < e1 && e1 - e0 <= kHeavyPairs;  // never selected, or taken in chunks
+    }
+}
+// the S tokens' rows of a [rows][D] array of T from row r0, one GTile per 16 tokens
+template <typename T, int D, int S, int NTH>
+__device__ __forceinline__ void cell_tiles(const T *src, int64_t r0, T *dst) {
+    using G = GTile<T, D>;
+    for (int pc = threadIdx.x; pc < S * G::CPR; pc += NTH) {
+        const int tk = pc / G::CPR, ch = pc % G::CPR;
+        *reinterpret_cast<uint4 *>(dst + (tk / 16) * G::ELEMS + G::off(tk % 16, ch)) =
+            *reinterpret_cast<const uint4 *>(src + (r0 + tk) * D + G::EPC * ch);
+    }
+}
 }  // namespace
+
+// ---- long branch, forward recompute, per cell: for each selector of the cell (light
+// cells whole, heavy ones in chunks), the cell's share of the selector's softmax:
+// m = the largest scaled score over the cell's tokens, l = sum_j exp(scale s_j - m),
+// o = sum_j exp(scale s_j - m) v_j, written to the selector's (query, rank) row (o to
+// po, (m, l) to pml); bwd_long_merge combines a query's rows. The cell's keys and values
+// wait in LDS; each wave takes 16 selectors at a time, their queries as B operands
+// (dims (d/4) g .. of selector c in lane (c, g)), so that S^T = K Q^T puts tokens
+// 4 g + r of selector c in lane (c, g) and P^T feeds o^T = V^T P^T from that layout.
+template <typename T, int D, int S, bool CHUNKS>
+__global__ __launch_bounds__(256) void bwd_long_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                           const T *__restrict__ v, const uint32_t *__restrict__ sq,
+                                                           const int32_t *__restrict__ seg,
+                                                           const int32_t *__restrict__ items,
+                                                           const int32_t *__restrict__ counters,
+                                                           float *__restrict__ po, float2 *__restrict__ pml,
+                                                           KParams p) {
+    constexpr int NW = 4;       // waves
+    constexpr int KS = D / 4;
+    constexpr int NT = S / 16;  // 16-token tiles of the cell
+    using G = GTile<T, D>;
+    __shared__ __attribute__((aligned(16))) T s_k[S * D];
+    __shared__ __attribute__((aligned(16))) T s_v[S * D];
+    int64_t cid, e0, e1;
+    if (!cell_run<CHUNKS>(seg, items, counters, cid, e0, e1)) return;
+    const int h = (int)(cid / p.C);
+    const int64_t c = cid % p.C;
+    const int64_t hN = (int64_t)h * p.N, hNK = hN * p.K;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    cell_tiles<T, D, S, 64 * NW>(k, hN + c * S, s_k);
+    cell_tiles<T, D, S, 64 * NW>(v, hN + c * S, s_v);
+    __syncthreads();
+    const int ntile = (int)((e1 - e0 + 15) / 16);
+    for (int t = wave; t < ntile; t += NW) {
+        const int64_t e = e0 + 16 * (int64_t)t + col;
+        const bool ok = e < e1;
+        const int64_t val = sq[min(e, e1 - 1)];  // query * K + rank
+        const int64_t pair = hNK + val;
+        BRow<T, KS> qb;
+        qb.load(q + (hN + val / p.K) * D + KS * g);
+        floatx4 sv[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) sv[j] = gtile_dot<T, D>(s_k + j * G::ELEMS, col, g, qb);
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, sv[j][r] * p.scale);
+        m = colmax4(m);
+        float P[NT][4], l = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                P[j][r] = __expf(sv[j][r] * p.scale - m);
+                l += P[j][r];
+            }
+        l = colsum4(l);
+        floatx4 acc[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) gtile_tmul<T, D>(s_v + j * G::ELEMS, col, g, P[j], acc);
+        if (ok) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                *reinterpret_cast<float4 *>(po + pair * D + 16 * dt + 4 * g) =
+                    make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+            if (g == 0) pml[pair] = make_float2(m, l);
+        }
+    }
+}
+
+// ---- long branch, per query (one wave, 4 per work-group): its cells' rows combined in
+// rank order, M = max m_r, L = sum_r exp(m_r - M) l_r, o_long = sum_r exp(m_r - M) o_r / L,
+// lse = M + log L; then RMSNorm's backward. Writes the gradient reaching the softmax
+// output (do_l), the row's lse and D = do_l . o_long, the query's dgamma term, and the
+// query in fp32 for the key side. Lane: dims NX lane .. NX lane + NX - 1.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_long_merge_kernel(const T *__restrict__ q, const int32_t *__restrict__ sel,
+                                                                  const float *__restrict__ po,
+                                                                  const float2 *__restrict__ pml,
+                                                                  const float *__restrict__ dO,
+                                                                  float *__restrict__ do_l, float *__restrict__ lse_l,
+                                                                  float *__restrict__ D_l, float *__restrict__ dg,
+                                                                  float *__restrict__ q32, KParams p) {
+    constexpr int NX = D / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nqw = (int)((p.N + 3) / 4);
+    const int h = blockIdx.x / nqw;
+    const int64_t i = (int64_t)(blockIdx.x % nqw) * 4 + wave;
+    if (i >= p.N) return;
+    const int64_t hi = (int64_t)h * p.N + i;
+    const int64_t row = hi * D;
+    float qf[NX];
+#pragma unroll
+    for (int n = 0; n < NX; ++n) qf[n] = to_f32<T>(q[row + NX * lane + n]);
+    // every rank's row is read at once; a rank without a cell has no row (its words are
+    // whatever the workspace held) and is dropped by selects, never multiplied in
+    bool ok[kMaxK];
+    float2 ml[kMaxK];
+    float src[kMaxK][NX], dout_[NX], y[NX];
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r) {
+        if (r >= p.K) break;
+        ok[r] = sel[hi * p.K + r] >= 0;
+        ml[r] = pml[hi * p.K + r];
+#pragma unroll
+        for (int n = 0; n < NX; ++n) src[r][n] = po[(hi * p.K + r) * D + NX * lane + n];
+    }
+#pragma unroll
+    for (int n = 0; n < NX; ++n) dout_[n] = dO[row + NX * lane + n];
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r) {
+        if (r >= p.K) break;
+        M = ok[r] ? fmaxf(M, ml[r].x) : M;
+    }
+#pragma unroll
+    for (int n = 0; n < NX; ++n) q32[row + NX * lane + n] = qf[n];
+    if (M == -INFINITY) {  // no cell: o_long = 0
+        for (int x = lane; x < D; x += 64) do_l[row + x] = 0.0f;
+        if (lane == 0) { lse_l[hi] = 0.0f; D_l[hi] = 0.0f; dg[hi] = 0.0f; }
+        return;
+    }
+    float L = 0.0f, o[NX];
+#pragma unroll
+    for (int n = 0; n < NX; ++n) o[n] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kMaxK; ++r) {
+        if (r >= p.K) break;
+        const float wr = ok[r] ? __expf(ml[r].x - M) : 0.0f;
+        L += ok[r] ? wr * ml[r].y : 0.0f;
+#pragma unroll
+        for (int n = 0; n < NX; ++n) o[n] += ok[r] ? wr * src[r][n] : 0.0f;
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int n = 0; n < NX; ++n) o[n] *= inv;
+    float ss = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NX; ++n) ss += o[n] * o[n];
+    ss = wave_sum(ss);
+    const float rr = sqrtf(ss / (float)D + p.rms_eps);
+    const float gam = p.gamma[h];
+    float dy_y = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NX; ++n) {
+        y[n] = o[n] / rr;
+        dy_y += dout_[n] * y[n];
+    }
+    dy_y = wave_sum(dy_y);  // dout . y
+    float Dsum = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NX; ++n) {
+        const float d_o = (gam * dout_[n] - y[n] * (gam * dy_y) / (float)D) / rr;
+        do_l[row + NX * lane + n] = d_o;
+        Dsum += d_o * o[n];
+    }
+    const float Dr = wave_sum(Dsum);
+    if (lane == 0) {
+        lse_l[hi] = M + __logf(L);
+        D_l[hi] = Dr;
+        dg[hi] = dy_y;
+    }
+}
 
 template <typename T, int D, int S, bool CHUNKS>
 __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const float *__restrict__ q, const T *__restrict__ k,
@@ -838,21 +856,8 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
     __shared__ __attribute__((aligned(16))) T s_k[S * D];  // the cell's keys, 16-token tiles
     __shared__ __attribute__((aligned(16))) T s_v[S * D];  // and values
     __shared__ float s_ds[S * DSLD];               // dS of the current tile, [token][selector]
-    int64_t cid;  // head * C + cell
-    int64_t e0, e1;
-    if constexpr (CHUNKS) {
-        if ((int)blockIdx.x >= counters[0]) return;
-        cid = items[2 * blockIdx.x];
-        const int64_t j = items[2 * blockIdx.x + 1];
-        const int64_t a = seg[2 * cid], z = seg[2 * cid + 1];
-        e0 = a + j * kHeavyPairs;
-        e1 = min(z, e0 + kHeavyPairs);
-    } else {
-        cid = blockIdx.x;
-        e0 = seg[2 * cid];
-        e1 = seg[2 * cid + 1];
-        if (e0 >= e1 || e1 - e0 > kHeavyPairs) return;  // never selected, or taken in chunks
-    }
+    int64_t cid, e0, e1;  // head * C + cell, its selectors
+    if (!cell_run<CHUNKS>(seg, items, counters, cid, e0, e1)) return;
     const int h = (int)(cid / p.C);
     const int64_t c = cid % p.C;
     const int64_t hN = (int64_t)h * p.N;
@@ -861,15 +866,9 @@ __global__ __launch_bounds__(64 * (S / 16), 2) void bwd_long_kv_kernel(const flo
     const int tok = 16 * wave + col;                  // this lane's token within the cell
     const int64_t jrow = hN + c * S + tok;
     const int64_t hNK = hN * p.K;
-    // the cell's keys and values into LDS, one GTile per 16 tokens (read after the first
-    // barrier below)
-    for (int pc = tid; pc < S * G::CPR; pc += 64 * NWV) {
-        const int tk = pc / G::CPR, ch = pc % G::CPR;
-        const int at = (tk / 16) * G::ELEMS + G::off(tk % 16, ch);
-        const int64_t src = (hN + c * S + tk) * D + G::EPC * ch;
-        *reinterpret_cast<uint4 *>(s_k + at) = *reinterpret_cast<const uint4 *>(k + src);
-        *reinterpret_cast<uint4 *>(s_v + at) = *reinterpret_cast<const uint4 *>(v + src);
-    }
+    // the cell's keys and values into LDS (read after the first barrier below)
+    cell_tiles<T, D, S, 64 * NWV>(k, hN + c * S, s_k);
+    cell_tiles<T, D, S, 64 * NWV>(v, hN + c * S, s_v);
     floatx4 acck[D / 16], accv[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acck[dt] = accv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1060,7 +1059,7 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
     if (e != hipSuccess) return e;
     const int64_t pairs = (int64_t)p.H * p.N * (D / 2);
     // the window kernels read fp32 values from do_l's storage, which the long branch's
-    // query kernel fills only after them
+    // merge kernel fills only after them
     float *vf = w.do_l;
     hipLaunchKernelGGL((bwd_prep_kernel<T, TO, D>), dim3((unsigned)((pairs + kThreads - 1) / kThreads)), dim3(kThreads),
                        0, st, q, k, v, dout, w.rope, nhi, w.qr, w.kr, vf, w.dO, p);
@@ -1070,31 +1069,42 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
     hipLaunchKernelGGL((bwd_win_dkv_kernel<D>), dim3(tiles), dim3(256), 0, st, w.qr, w.kr, vf, w.dO, w.lse_w, w.D_w,
                        w.rope, nhi, dk, dv, p);
     const unsigned qw = (unsigned)(((p.N + 3) / 4) * p.H);
-    // the long branch's query side also leaves the queries in fp32, unrotated, in qr's
-    // storage, which the window kernels no longer need
-    float *q32 = w.qr;
-    hipLaunchKernelGGL((bwd_long_q_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, k, v, w.dO, sel, w.do_l,
-                       w.lse_l, w.D_l, w.dg, q32, p);
+    const int64_t npair = (int64_t)p.H * p.N * p.K;
+    const int64_t ncell = (int64_t)p.H * p.C;
+    const int64_t mi = heavy_items_max(p), mh = heavy_cells_max(p);
+    const uint32_t *sval = nullptr;
+    // the long branch's per-pair rows: first the forward recompute's o (then its dq) in dqp
+    float *po = w.dqp;
     if (p.C > 0) {
         // each cell's selecting queries in query order: a stable sort of the pairs by cell
-        const int64_t npair = (int64_t)p.H * p.N * p.K;
-        const int64_t ncell = (int64_t)p.H * p.C;
         hipLaunchKernelGGL(bwd_pair_keys_kernel, dim3((unsigned)((npair + 255) / 256)), dim3(256), 0, st, sel,
                            w.pkey, w.pval, p);
         bool in_tmp = false;
         e = launch_sort_pairs(w.pkey, w.pval, w.pkey2, w.pval2, w.shist, w.stot, npair, pair_key_bits(p), &in_tmp,
                               st);
         if (e != hipSuccess) return e;
-        const uint32_t *skey = in_tmp ? w.pkey2 : w.pkey, *sval = in_tmp ? w.pval2 : w.pval;
+        const uint32_t *skey = in_tmp ? w.pkey2 : w.pkey;
+        sval = in_tmp ? w.pval2 : w.pval;
         hipLaunchKernelGGL(bwd_seg_init_kernel, dim3((unsigned)((2 * ncell + 255) / 256)), dim3(256), 0, st, w.cseg,
                            ncell, w.hcount);
         hipLaunchKernelGGL(bwd_seg_mark_kernel, dim3((unsigned)((npair + 255) / 256)), dim3(256), 0, st, skey, npair,
                            (uint32_t)ncell, w.cseg);
         hipLaunchKernelGGL(bwd_heavy_list_kernel, dim3((unsigned)((ncell + 255) / 256)), dim3(256), 0, st, w.cseg,
                            ncell, w.hcount, w.hitems, w.hcells);
+        hipLaunchKernelGGL((bwd_long_fwd_kernel<T, D, S, false>), dim3((unsigned)ncell), dim3(256), 0, st, q, k, v,
+                           sval, w.cseg, w.hitems, w.hcount, po, w.pml, p);
+        if (mi > 0)
+            hipLaunchKernelGGL((bwd_long_fwd_kernel<T, D, S, true>), dim3((unsigned)mi), dim3(256), 0, st, q, k, v,
+                               sval, w.cseg, w.hitems, w.hcount, po, w.pml, p);
+    }
+    // the merge also leaves the queries in fp32, unrotated, in qr's storage, which the
+    // window kernels no longer need
+    float *q32 = w.qr;
+    hipLaunchKernelGGL((bwd_long_merge_kernel<T, D>), dim3(qw), dim3(kThreads), 0, st, q, sel, po, w.pml, w.dO, w.do_l,
+                       w.lse_l, w.D_l, w.dg, q32, p);
+    if (p.C > 0) {
         hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, false>), dim3((unsigned)ncell), dim3(64 * (S / 16)), 0, st, q32, k,
                            v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, w.dqp, p);
-        const int64_t mi = heavy_items_max(p), mh = heavy_cells_max(p);
         if (mi > 0) {
             hipLaunchKernelGGL((bwd_long_kv_kernel<T, D, S, true>), dim3((unsigned)mi), dim3(64 * (S / 16)), 0, st, q32, k,
                                v, sval, w.cseg, w.hitems, w.hcount, w.do_l, w.lse_l, w.D_l, dk, dv, w.hpart, w.dqp, p);

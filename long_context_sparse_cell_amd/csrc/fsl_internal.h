@@ -497,7 +497,9 @@ struct BwdWork {
     int32_t *hitems;  // [heavy_items_max][2] (cell, chunk)
     int32_t *hcells;  // [heavy_cells_max][3] (cell, first item, chunks)
     float *hpart;     // [heavy_items_max][2][s][d] each chunk's dk and dv sums
-    float *dqp;       // [H][N][K][d] the long branch's dq of each (query, rank) pair, scaled
+    float *dqp;       // [H][N][K][d] per (query, rank) pair: the long branch's weighted values
+                      // of the cell, then its dq (scaled)
+    float2 *pml;      // [H][N][K] per pair: the largest scaled score over the cell and the sum of weights
     uint32_t *status;
 };
 // cells chosen by more than kHeavyPairs queries are processed in chunks of that many

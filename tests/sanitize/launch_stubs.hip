@@ -88,7 +88,7 @@ hipError_t launch_attn_bwd(const void *, const void *, const void *, const void 
     inside(w.lse_w, "lse_w"); inside(w.D_w, "D_w"); inside(w.lse_l, "lse_l"); inside(w.D_l, "D_l");
     inside(w.dg, "dg"); inside(w.pkey, "pkey"); inside(w.pval, "pval"); inside(w.pkey2, "pkey2");
     inside(w.pval2, "pval2"); inside(w.shist, "shist"); inside(w.stot, "stot"); inside(w.cseg, "cseg");
-    inside(w.hcount, "hcount"); inside(w.hitems, "hitems"); inside(w.hcells, "hcells"); inside(w.hpart, "hpart"); inside(w.dqp, "dqp");
+    inside(w.hcount, "hcount"); inside(w.hitems, "hitems"); inside(w.hcells, "hcells"); inside(w.hpart, "hpart"); inside(w.dqp, "dqp"); inside(w.pml, "pml");
     inside(w.status, "bwd status");
     return hipSuccess;
 }
