@@ -350,14 +350,15 @@ def time_forward(fsl, torch, sh, inp, q, k, v, dev, steps, warmup, with_work=Fal
     return res
 
 
-VALU_F32_PEAK_TFLOPS = 157.3  # fp32 vector
+F32_PEAK_TFLOPS = 157.3  # fp32, on the matrix cores (dense) as on the vector ALUs
 
 
 def backward_bench(fsl, synth, torch, sh, inp, q, k, v, dev, steps, warmup):
     """fsl_attn_bwd on one workload (after one forward whose selections it reuses): ms per call and
     the rate of algorithmic work, 10 d flops per (query, key) pair of both branches (scores, dP, and
-    the dq, dk, dv products), against the fp32 peak: the window's products run on the fp32 matrix
-    cores and the long branch's on the vector ALUs, both 157.3 TFLOP/s on MI355X."""
+    the dq, dk, dv products), against the fp32 peak (157.3 TFLOP/s on MI355X): every product of both
+    branches runs on the fp32 matrix cores. The long branch's recomputed forward (scores and the
+    weighted values once more) is not counted."""
     sig, lam, gam = (torch.from_numpy(a).to(dev) for a in (inp.sigma, inp.lam, inp.gamma))
     p = fsl.make_params(sh.N, sh.H, sh.d, q.dtype, sig, lam, gam, w=sh.w, s=sh.s, P=sh.P, W=sh.W, K=sh.K, B=sh.B)
     fws = fsl.new_workspace(p, dev)
@@ -385,9 +386,9 @@ def backward_bench(fsl, synth, torch, sh, inp, q, k, v, dev, steps, warmup):
     del fws, bws, grads, dout
     torch.cuda.empty_cache()
     return {"workload": sh.name, "ms_per_step": round(el * 1e3, 3), "tokens_per_s": round(sh.N / el, 1),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": VALU_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4), "flops_per_launch": flops,
-                         "note": "fp32: window on the matrix cores, long branch on the vector ALUs"}}
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / F32_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+                         "note": "fp32 on the matrix cores, both branches"}}
 
 
 def fsb_bench(fsl, synth, torch, sh, inp, q, k, v, dev, steps, warmup):
