@@ -170,9 +170,11 @@ def cpu_baseline(inp, sample_rows):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{sample_rows} query rows (the last {sample_rows // sh.B} blocks) x {sh.H} heads of the "
-                   f"{sh.name} workload, plus per-head cell statistics; rows time scaled by N/{sample_rows}; "
-                   f"measured {t_fixed + t_rows:.1f} s of oracle work"),
+        "sample": ((f"all {sh.N} query rows x {sh.H} heads of the {sh.name} workload (the whole step)"
+                    if sample_rows == sh.N else
+                    f"{sample_rows} query rows (the last {sample_rows // sh.B} blocks) x {sh.H} heads of the "
+                    f"{sh.name} workload, plus per-head cell statistics; rows time scaled by N/{sample_rows}")
+                   + f"; measured {t_fixed + t_rows:.1f} s of oracle work"),
     }
 
 
@@ -475,7 +477,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fwd_bf16_n262144", help="a forward workload of synth.CONFIGS (default fwd_bf16_n262144: N=262144, H=8, d=128, bf16)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-rows", type=int, default=131072)
+    ap.add_argument("--cpu-rows", type=int, default=262144)
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     ap.add_argument("--no-fs", action="store_true", help="skip the unpruned (P = -1) forward measurement")
     ap.add_argument("--no-others", action="store_true", help="skip the 4k/16k/64k workloads and the O(N) check")
