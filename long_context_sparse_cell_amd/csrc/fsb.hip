@@ -210,7 +210,9 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     __shared__ double s_q[kSearchWaves][D];
     __shared__ double s_lse[kSearchWaves][64];
     __shared__ int32_t s_cell[kSearchWaves][64];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // per wave: 32 node means (fp32), or 64 bf16 key rows, copied in before their dot products
+    __shared__ __attribute__((aligned(16))) float s_stage[kSearchWaves][32 * D];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t nq = (p.N + kSearchWaves - 1) / kSearchWaves;
     const int h = (int)(blockIdx.x / nq);
     const int64_t i = (blockIdx.x % nq) * kSearchWaves + wave;
@@ -223,36 +225,43 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     double qq = 0.0;
 #pragma unroll 4
     for (int x = 0; x < D; ++x) qq = __fma_rn(s_q[wave][x], s_q[wave][x], qq);
+    // the query stays in LDS (read at every use): held in registers it would take 2 D of them
+    const double *qg = s_q[wave];
     const double qn = __dsqrt_rn(qq);
     const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
     const int64_t nb = eligible_cells(p, i / p.B);
     const int lv = fsb_levels(p);
-    // upper bound of the cell score under a node: the mean key read 16 bytes at a time,
-    // the dot product still one fma per coordinate, left to right
-    auto bound = [&](int T, int k, int64_t a, int64_t j) -> double {
-        const int64_t node = fsb_node(p, h, T, k, a, j);
-        const float4 *mu = reinterpret_cast<const float4 *>(w.mu + node * D);
-        // the query stays in LDS (read at every use): held in registers it would take
-        // 2 D of them and leave room for one wave per SIMD
-        const double *qv = s_q[wave];
+    float *st = s_stage[wave];
+    // upper bound of the cell score under a node whose mean key waits in the stage (dims
+    // 8 c .. 8 c + 3 at st[256 c + 4 l], 8 c + 4 .. at st[256 c + 128 + 4 l] for the l-th
+    // lane of its round): the dot product one fma per coordinate, left to right
+    auto bound = [&](int l, double rd, int32_t pm, float am) -> double {
+        const double *qv = qg;
         asm volatile("" : "+v"(qv));
         double content = 0.0;
-#pragma unroll 4
-        for (int x4 = 0; x4 < D / 4; ++x4) {
-            const float4 m4 = mu[x4];
-            content = __fma_rn(qv[4 * x4], (double)m4.x, content);
-            content = __fma_rn(qv[4 * x4 + 1], (double)m4.y, content);
-            content = __fma_rn(qv[4 * x4 + 2], (double)m4.z, content);
-            content = __fma_rn(qv[4 * x4 + 3], (double)m4.w, content);
+#pragma unroll 2
+        for (int c = 0; c < D / 8; ++c) {
+            const float4 m0 = *reinterpret_cast<const float4 *>(st + 256 * c + 4 * l);
+            const float4 m1 = *reinterpret_cast<const float4 *>(st + 256 * c + 128 + 4 * l);
+            content = __fma_rn(qv[8 * c], (double)m0.x, content);
+            content = __fma_rn(qv[8 * c + 1], (double)m0.y, content);
+            content = __fma_rn(qv[8 * c + 2], (double)m0.z, content);
+            content = __fma_rn(qv[8 * c + 3], (double)m0.w, content);
+            content = __fma_rn(qv[8 * c + 4], (double)m1.x, content);
+            content = __fma_rn(qv[8 * c + 5], (double)m1.y, content);
+            content = __fma_rn(qv[8 * c + 6], (double)m1.z, content);
+            content = __fma_rn(qv[8 * c + 7], (double)m1.w, content);
         }
-        const double tt = __fma_rn(qn, w.rad[node], content);
-        const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)w.pmin[node])), 2.0 * (double)p.s);
+        const double tt = __fma_rn(qn, rd, content);
+        const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)pm)), 2.0 * (double)p.s);
         const double gg = arg >= 6.0 ? 1.0 : erf(arg);
-        return __fma_rn(rho, tt, __dmul_rn(__dmul_rn(lam, (double)w.amax[node]), gg));
+        return __fma_rn(rho, tt, __dmul_rn(__dmul_rn(lam, (double)am), gg));
     };
     int nu = 0;  // distinct cells collected from the two beams (in s_cell)
     for (int T = 0; T < 2; ++T) {
-        const int64_t m = T == 0 ? nb : (int64_t)hcount[(int64_t)h * (p.C + 1) + nb];
+        // forest 1 covers the list-1 cells below nb (none below cell 0; with no cells at all
+        // the counts are never computed, so they are not read then)
+        const int64_t m = T == 0 ? nb : nb == 0 ? 0 : (int64_t)hcount[(int64_t)h * (p.C + 1) + nb];
         // this lane's candidate: forest level k, segment a, heap index j (j = 0: none);
         // fresh: its bound is still to be taken
         int ck = 0;
@@ -272,9 +281,29 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
         double cu = -INFINITY;
         int64_t ckey = INT64_MAX;
         for (int iter = 0; iter < 64; ++iter) {
-            if (fresh) {
-                cu = bound(T, ck, ca, cj);
-                ckey = fsb_key(T, ck, ca, cj);
+            if (__ballot(fresh) != 0ull) {
+                // the fresh lanes' node means into the stage, 32 lanes a round (one copy of
+                // 32 x 16 bytes per instruction pair), their radii, norms and positions
+                // requested with them; other lanes name a valid slot they do not use
+                const int64_t mynode = fsb_node(p, h, T, fresh ? ck : 0, fresh ? ca : 0, fresh ? cj : 1);
+                const double rd = w.rad[mynode];
+                const int32_t pm = w.pmin[mynode];
+                const float am = w.amax[mynode];
+                const int rounds = __ballot(fresh) >> 32 ? 2 : 1;
+                for (int rn = 0; rn < rounds; ++rn) {
+                    const int64_t src_node = __shfl(mynode, 32 * rn + (lane & 31));
+                    const float *src = w.mu + src_node * D + 4 * (lane >> 5);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
+#pragma unroll
+                    for (int c = 0; c < D / 8; ++c) lds_dma16(src + 8 * c, st + 256 * c);
+                    wait_vmem();
+                    __builtin_amdgcn_wave_barrier();
+                    if (fresh && (lane >> 5) == rn) {
+                        cu = bound(lane & 31, rd, pm, am);
+                        ckey = fsb_key(T, ck, ca, cj);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                }
             }
             // keep the beam best: bitonic sort of the wave's candidates, best first
 #pragma unroll 1
@@ -333,13 +362,61 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     }
     // rerank: lse_c = log sum_j exp(scale q . k_j) over the cell's tokens (token dots one per lane)
     const int S = p.s;
-    for (int u = 0; u < nu; ++u) {
+    if (bf) {
+        // 64 / S cells at a time: their key rows copied into the stage (16-byte piece c of
+        // row r at c ^ (r mod pieces per row)), then one row per lane
+        constexpr int CPR = D / 8;
+        constexpr int RPI = 64 / CPR;  // rows per copy instruction
+        uint16_t *st16 = reinterpret_cast<uint16_t *>(st);
+        const int cps = 64 / S;
+        for (int u0 = 0; u0 < nu; u0 += cps) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
+#pragma unroll
+            for (int ii = 0; ii < 64 / RPI; ++ii) {
+                const int row = RPI * ii + lane / CPR, pos = lane % CPR;
+                const int uu = min(u0 + row / S, nu - 1);
+                const int64_t tok = hN + (int64_t)s_cell[wave][uu] * S + row % S;
+                lds_dma16(k16 + tok * D + 8 * (pos ^ (row & (CPR - 1))), st16 + 512 * ii);
+            }
+            wait_vmem();
+            __builtin_amdgcn_wave_barrier();
+            const int uu = u0 + lane / S;
+            double l = -INFINITY;
+            if (uu < nu) {
+                const double *qv = qg;
+                asm volatile("" : "+v"(qv));
+                double dot = 0.0;
+#pragma unroll 2
+                for (int c = 0; c < CPR; ++c) {
+                    const uint4 r4 = *reinterpret_cast<const uint4 *>(st16 + lane * D + 8 * (c ^ (lane & (CPR - 1))));
+                    const uint32_t w4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        dot = __fma_rn(qv[8 * c + 2 * t], (double)__uint_as_float(w4[t] << 16), dot);
+                        dot = __fma_rn(qv[8 * c + 2 * t + 1], (double)__uint_as_float(w4[t] & 0xFFFF0000u), dot);
+                    }
+                }
+                l = __dmul_rn((double)p.scale, dot);
+            }
+            double mx = l;
+            for (int o = 1; o < S; o <<= 1) {
+                const double ov = __shfl_xor(mx, o);
+                mx = ov > mx ? ov : mx;
+            }
+            const double e = uu < nu ? exp(__dsub_rn(l, mx)) : 0.0;
+            // the sum in token order, as the oracle takes it
+            double sum = 0.0;
+            for (int t = 0; t < S; ++t) sum = __dadd_rn(sum, __shfl(e, (lane / S) * S + t));
+            if (uu < nu && lane % S == 0) s_lse[wave][uu] = __dadd_rn(mx, log(sum));
+        }
+    }
+    for (int u = 0; u < (bf ? 0 : nu); ++u) {
         const int32_t c = s_cell[wave][u];
         double l = -INFINITY;
         if (lane < S) {
             // the token's key row 16 bytes at a time, one fma per coordinate, left to right
             const int64_t row = (hN + (int64_t)c * S + lane) * D;
-            const double *qv = s_q[wave];
+            const double *qv = qg;
             asm volatile("" : "+v"(qv));
             double dot = 0.0;
             if (bf) {

@@ -123,3 +123,21 @@ def test_fsb_262144_workload_stripe(oracle):
         for row in inp.probes[h]:
             assert pos // sh.s in sel[h][row], (h, pos, row)
     torch.cuda.empty_cache()
+
+
+def test_fsb_no_cells_ignores_stale_workspace(oracle):
+    """With fewer than s tokens there are no cells and nothing is selected, whatever bytes the
+    workspace held before: the per-cell list counts are not computed then, so the search must not
+    read them (a regression test for exactly that read)."""
+    from long_context_sparse_cell_amd import fsl
+    for n in (1, 20):
+        print(f"\n[case] fsb no cells N={n}, workspace filled with 0x7F", flush=True)
+        sh = synth.Shape(f"fsb_nocells_n{n}", H=2, N=n, d=64, dtype=synth.BF16, seed=54)
+        inp = synth.random_inputs(sh)
+        tau, proj = fsb_inputs(sh, inp, oracle)
+        run = GpuRun(inp, want_internals=False)
+        fb = fsl.make_fsb_params(torch.from_numpy(tau).cuda(), torch.from_numpy(proj).cuda(), 16)
+        ws = torch.full((fsl.fsb_workspace_bytes(run.p),), 0x7F, dtype=torch.uint8, device="cuda")
+        sel = fsl.fsb_select(run.q, run.k, run.p, fb, ws=ws)
+        torch.cuda.synchronize()
+        assert (sel.cpu().numpy() == -1).all(), n
