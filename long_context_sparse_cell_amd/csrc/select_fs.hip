@@ -15,10 +15,10 @@
 //  2. select_fs_kernel streams the block's cells through LDS in chunks of 64
 //     (copied straight into LDS, double buffered, 16-byte pieces of a row
 //     permuted against bank conflicts) and computes content~ = q.(hi + lo) on
-//     v_mfma_f32_16x16x32_bf16, with the bound |s - s~| <= eps of the pool
-//     scoring kernel (select_mfma.hip). Each lane (one query, four cells of
-//     every 16-cell tile) keeps the K_L + 1 cells of largest upper bound (K_L =
-//     4 or 8, at least K)
+//     v_mfma_f32_16x16x32_bf16, with the pool scoring kernel's bound |s - s~| <=
+//     eps (select_mfma.hip) itself bounded by ||q|| A_c + B_c (fs_prep_kernel).
+//     Each lane (one query, four cells of every 16-cell tile) keeps the K_L + 1
+//     cells of largest upper bound (K_L = 4 or 8, at least K)
 //     ub = s~ + eps, with lb = s~ - eps. A cell whose ub is below the smallest
 //     lb of some lane's K leading entries (at any earlier time, shared by the
 //     query's four lanes) is beaten by those K cells and is not inserted. At
@@ -64,7 +64,14 @@ __device__ __forceinline__ int fs_piece(int r, int c) { return c ^ (r & (CPR - 1
 }  // namespace
 
 // kbar -> khi, klo (bf16 head and tail, round to nearest even) and
-// kcf = (lambda a_c, |rho| ||kbar_c|| eps, |lambda a_c| 2e-6, c s as int bits).
+// kcf = (lambda a_c, A_c, B_c, c s as int bits), the constants of the per-pair bound
+// eps = ||q|| A_c + B_c. The pool kernel's bound (select_mfma.hip) is
+//   2 (||q|| |rho| ||kbar_c|| e_d + |lambda a_c| 2e-6 + (|rc| + |b|) 2^-22 + 1e-30)
+// with rc = rho q.(hi + lo) in fp32 and b the bias. Here |rc| <= 1.01 |rho| ||q|| ||kbar_c||
+// (Cauchy-Schwarz; the split and the fp32 sum add far less than 1%) and |b| <= |lambda a_c|
+// (|erf| <= 1), so
+//   A_c = 2 |rho| ||kbar_c|| (e_d + 1.01 2^-22),  B_c = 2 (|lambda a_c| (2e-6 + 2^-22) + 1e-30)
+// bound it from above with one fma per pair.
 // Row r by 8 consecutive threads, 64 rows per work-group.
 template <int D>
 __global__ __launch_bounds__(512) void fs_prep_kernel(const float *__restrict__ kbar, const float *__restrict__ amax,
@@ -102,8 +109,10 @@ __global__ __launch_bounds__(512) void fs_prep_kernel(const float *__restrict__ 
     ss = sum8_dpp(ss);  // all 8 threads of the row take part
     if (ok && part == 0) {
         const float la = p.lambda[h] * amax[(int64_t)h * p.C + r];
-        kcf[(int64_t)h * p.C + r] = make_float4(la, fabsf(p.rho) * sqrtf(ss) * fs_eps_content(D), fabsf(la) * 2e-6f,
-                                                __int_as_float((int)(r * p.s)));
+        const float ka = fabsf(p.rho) * sqrtf(ss);
+        kcf[(int64_t)h * p.C + r] =
+            make_float4(la, 2.0f * ka * (fs_eps_content(D) + 1.01f * 2.384185791015625e-07f),
+                        2.0f * (fabsf(la) * (2e-6f + 2.384185791015625e-07f) + 1e-30f), __int_as_float((int)(r * p.s)));
     }
 }
 
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
             // was seen taking the accumulator before the MFMA had written it)
             float rcv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rcv[e] = rhof * acc[e];
+            for (int e = 0; e < 4; ++e) rcv[e] = acc[e];
             asm volatile("" : "+v"(rcv[0]), "+v"(rcv[1]), "+v"(rcv[2]), "+v"(rcv[3]));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -229,10 +238,8 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
                     const float argf = (float)((int)i - __float_as_int(cf.w)) * karg;
                     if (argf < 6.0f) bf = cf.x * erff(argf);
                 }
-                const float rc = rcv[e];
-                const float sv = rc + bf;
-                const float ev =
-                    2.0f * (fmaf(qn, cf.y, cf.z) + (fabsf(rc) + fabsf(bf)) * 2.384185791015625e-07f + 1e-30f);
+                const float sv = fmaf(rhof, rcv[e], bf);
+                const float ev = fmaf(qn, cf.y, cf.z);  // eps = ||q|| A_c + B_c
                 float cu = c < n ? sv + ev : -INFINITY;
                 if (cu >= thr && cu > lu[kFsCap - 1]) {
                     float cl = sv - ev;
