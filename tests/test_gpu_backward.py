@@ -77,6 +77,7 @@ SMALL = [
     ("bf16_d64_n700_w1", dict(H=2, N=700, d=64, dtype=synth.BF16, w=1, s=16, B=16, P=4, W=1, K=2)),
     ("bf16_d64_n1", dict(H=1, N=1, d=64, dtype=synth.BF16)),
     ("bf16_d128_b256", dict(H=1, N=4000, d=128, dtype=synth.BF16, B=256, P=20, K=5)),
+    ("bf16_d64_k8", dict(H=2, N=3000, d=64, dtype=synth.BF16, P=16, K=8)),
 ]
 
 
