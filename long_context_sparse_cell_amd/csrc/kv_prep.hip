@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
     constexpr int PG = HALF / 8;               // groups of 8 rotation pairs per row
     constexpr int KIT = kRopeSpan * PG / 256;  // key items per thread
     constexpr int VIT = kRopeSpan * D / 8 / 2 / 256;  // value items (token pair x 8 dims) per thread
-    constexpr int TLD = kRopeSpan + 8;         // transposed tile row stride
+    constexpr int TLD = kRopeSpan + 2;         // transposed tile row stride (4 TLD = 8 mod 64 dwords)
     static_assert(KIT >= 1 && VIT >= 1, "tile work must cover every thread");
     __shared__ __attribute__((aligned(16))) uint16_t s_t[D * TLD];  // fp16 bits, [dim][token]
     // raw key rows for the statistics: a row stride of D + 2 bf16 (an odd number of
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
     }
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
-        const int it = tid + 256 * u, jp = it % (kRopeSpan / 2), c8 = it / (kRopeSpan / 2);
+        const int it = tid + 256 * u, c8 = it % (D / 8), jp = it / (D / 8);
         const int64_t j = j0 + 2 * jp;
         va[u] = *reinterpret_cast<const uint4 *>(v + (hN + min(j, p.N - 1)) * D + 8 * c8);
         vb[u] = *reinterpret_cast<const uint4 *>(v + (hN + min(j + 1, p.N - 1)) * D + 8 * c8);
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
     // ---- values: fp16, transposed through LDS (token pairs per 32-bit store)
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
-        const int it = tid + 256 * u, jp = it % (kRopeSpan / 2), c8 = it / (kRopeSpan / 2);
+        const int it = tid + 256 * u, c8 = it % (D / 8), jp = it / (D / 8);
         const int64_t j = j0 + 2 * jp;
         float e0[8], e1[8];
         bf16x8_to_f32(va[u], e0);
@@ -219,11 +219,9 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(const uint16_t *__restrict
         const int pi = tid + 256 * u;
         const int grp = pi / (4 * D), rem = pi % (4 * D);
         const int dim = rem >> 2, pg = rem & 3;
-        const uint16_t *src = &s_t[dim * TLD + 32 * grp + 4 * pg];
-        const uint2 lo = *reinterpret_cast<const uint2 *>(src);
-        const uint2 hi2 = *reinterpret_cast<const uint2 *>(src + 16);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(&s_t[dim * TLD + 32 * grp + 4 * pg]);
         *reinterpret_cast<uint4 *>(vt + h * vt_head_elems(p) + ((2 * (int64_t)blockIdx.x + grp) * D + dim) * 32 + 8 * pg) =
-            make_uint4(lo.x, lo.y, hi2.x, hi2.y);
+            make_uint4(src[0], src[1], src[8], src[9]);
     }
     if constexpr (STATS) {
         __syncthreads();
