@@ -57,7 +57,7 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
     // reads (after the static arrays below, whose size is not a multiple of 16)
     extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
     __shared__ int s_pool[kSelPool];
-    // per pool cell: lambda a_c, |rho| ||kbar_c|| epsc, |lambda a_c| 2e-6, and c s (int bits)
+    // per pool cell: lambda a_c, A_c, B_c (the bound eps = ||q|| A_c + B_c, below) and c s (int bits)
     __shared__ float4 s_cf[kSelPool];
     __shared__ int s_nfix;  // near-tie queries of this work-group
 
@@ -142,7 +142,13 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
         if (crow[j] >= 0 && part == 0) {
             const float la = lamf * am[j];
             s_pool[r] = crow[j];
-            s_cf[r] = make_float4(la, fabsf(rhof) * sqrtf(ss) * epsc, fabsf(la) * 2e-6f, __int_as_float(crow[j] * p.s));
+            // the bound 2 (||q|| |rho| ||kbar_c|| epsc + |lambda a_c| 2e-6 + (|rc| + |b|) 2^-22 + 1e-30) of
+            // the header, with |rc| <= 1.01 |rho| ||q|| ||kbar_c|| (Cauchy-Schwarz; the split and the fp32
+            // sum add far less than 1%) and |b| <= |lambda a_c| (|erf| <= 1): ||q|| A_c + B_c bounds it
+            const float ka = fabsf(rhof) * sqrtf(ss);
+            s_cf[r] = make_float4(la, 2.0f * ka * (epsc + 1.01f * 2.384185791015625e-07f),
+                                  2.0f * (fabsf(la) * (2e-6f + 2.384185791015625e-07f) + 1e-30f),
+                                  __int_as_float(crow[j] * p.s));
         }
     }
     __syncthreads();
@@ -191,10 +197,8 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
                         const float argf = (float)((int)i - __float_as_int(cf.w)) * karg;
                         if (argf < 6.0f) bf = cf.x * erff(argf);
                     }
-                    const float rc = rhof * acc[e];
-                    const float sv = rc + bf;
-                    const float ev =
-                        2.0f * (fmaf(qn, cf.y, cf.z) + (fabsf(rc) + fabsf(bf)) * 2.384185791015625e-07f + 1e-30f);
+                    const float sv = fmaf(rhof, acc[e], bf);
+                    const float ev = fmaf(qn, cf.y, cf.z);  // eps = ||q|| A_c + B_c
                     sub[ct][e] = sv + ev;
                     float x = sv - ev;
 #pragma unroll
