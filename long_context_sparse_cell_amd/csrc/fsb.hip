@@ -100,13 +100,21 @@ __global__ __launch_bounds__(1024) void fsb_lists_kernel(const float *__restrict
     if (tid == 0) hcount[(int64_t)h * (p.C + 1) + p.C] = s_base;
 }
 
-// ---- trees of level k: one work-group per (head, forest, segment a)
+// ---- trees of level k: one work-group per (head, forest, segment a). The leaf order is
+// the merge of the two halves' orders (keys (code, list index) staged in LDS for segments of
+// up to kTreeLds leaves, read from global memory beyond); the node means come from one pass
+// over the merged leaves that keeps, per dimension, a running fp64 sum for each depth (the
+// node of that depth holding the current leaf), so every sum still runs over its node's
+// leaves left to right; largest norms and earliest positions, exact under any order, are
+// taken bottom-up from the children.
+constexpr int kTreeLds = 8192;
 template <int D>
 __global__ __launch_bounds__(256) void fsb_tree_kernel(const float *__restrict__ kbar, const float *__restrict__ cam,
                                                        const uint32_t *__restrict__ codes,
                                                        const int32_t *__restrict__ list1,
                                                        const int32_t *__restrict__ hcount, FsbWork w, int k,
                                                        KParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_key[];  // [L] keys, then [L] merged leaves
     const int64_t nseg = p.C >> k;
     const int64_t g = blockIdx.x;
     const int h = (int)(g / (2 * nseg));
@@ -115,12 +123,17 @@ __global__ __launch_bounds__(256) void fsb_tree_kernel(const float *__restrict__
     const int64_t len = T == 0 ? p.C : hcount[(int64_t)h * (p.C + 1) + p.C];
     if ((a + 1) << k > len) return;  // incomplete segment: no tree
     const int64_t L = (int64_t)1 << k;
+    const bool in_lds = L <= kTreeLds;
+    int32_t *s_leaf = reinterpret_cast<int32_t *>(s_key + (in_lds ? L : 0));
     const int tid = threadIdx.x;
     auto cell_of = [&](int64_t idx) -> int32_t { return T == 0 ? (int32_t)idx : list1[(int64_t)h * p.C + idx]; };
     int32_t *leaf = w.leaf + fsb_leaf(p, h, T, k, a, 0);
     // leaf order: (code, list index) ascending
     if (k == 0) {
-        if (tid == 0) leaf[0] = cell_of(a);
+        if (tid == 0) {
+            leaf[0] = cell_of(a);
+            if (in_lds) s_leaf[0] = leaf[0];
+        }
     } else {
         // merge the two sorted halves (the leaves of segments 2a and 2a + 1 of level k - 1)
         const int32_t *lo = w.leaf + fsb_leaf(p, h, T, k - 1, 2 * a, 0);
@@ -129,55 +142,102 @@ __global__ __launch_bounds__(256) void fsb_tree_kernel(const float *__restrict__
         const uint32_t *hc = codes + (int64_t)h * p.C;
         // list index of a cell: the cell itself in list 0, its rank among high cells in list 1
         auto lidx = [&](int32_t c) -> int64_t { return T == 0 ? (int64_t)c : (int64_t)hcount[(int64_t)h * (p.C + 1) + c]; };
+        if (in_lds) {
+            // (code, list index) as one 64-bit key: list indices are below C < 2^31
+            for (int64_t u = tid; u < L; u += 256) {
+                const int32_t c = u < half ? lo[u] : hi[u - half];
+                s_key[u] = ((uint64_t)hc[c] << 32) | (uint64_t)(uint32_t)lidx(c);
+            }
+            __syncthreads();
+        }
         for (int64_t u = tid; u < L; u += 256) {
             const bool left = u < half;
             const int32_t c = left ? lo[u] : hi[u - half];
-            const uint32_t cc = hc[c];
-            const int64_t ci = lidx(c);
-            const int32_t *other = left ? hi : lo;
-            // number of the other half's keys below this one (keys are distinct)
             int64_t lo_i = 0, hi_i = half;
-            while (lo_i < hi_i) {
-                const int64_t mid = (lo_i + hi_i) >> 1;
-                const int32_t oc = other[mid];
-                const uint32_t ocode = hc[oc];
-                const bool below = ocode < cc || (ocode == cc && lidx(oc) < ci);
-                if (below) lo_i = mid + 1; else hi_i = mid;
+            if (in_lds) {
+                const uint64_t key = s_key[u];
+                const uint64_t *other = s_key + (left ? half : 0);
+                while (lo_i < hi_i) {
+                    const int64_t mid = (lo_i + hi_i) >> 1;
+                    if (other[mid] < key) lo_i = mid + 1; else hi_i = mid;
+                }
+            } else {
+                const uint32_t cc = hc[c];
+                const int64_t ci = lidx(c);
+                const int32_t *other = left ? hi : lo;
+                // number of the other half's keys below this one (keys are distinct)
+                while (lo_i < hi_i) {
+                    const int64_t mid = (lo_i + hi_i) >> 1;
+                    const int32_t oc = other[mid];
+                    const uint32_t ocode = hc[oc];
+                    const bool below = ocode < cc || (ocode == cc && lidx(oc) < ci);
+                    if (below) lo_i = mid + 1; else hi_i = mid;
+                }
             }
-            leaf[(left ? u : u - half) + lo_i] = c;
+            const int64_t at = (left ? u : u - half) + lo_i;
+            leaf[at] = c;
+            if (in_lds) s_leaf[at] = c;
         }
     }
     __syncthreads();
-    // node means (fp64 sums over the node's leaves, left to right), largest norm, earliest position
+    const int32_t *lf = in_lds ? s_leaf : leaf;
     const int64_t nodes = 2 * L;
     float *mu = w.mu + fsb_node(p, h, T, k, a, 0) * D;
     double *rad = w.rad + fsb_node(p, h, T, k, a, 0);
     float *am = w.amax + fsb_node(p, h, T, k, a, 0);
     int32_t *pm = w.pmin + fsb_node(p, h, T, k, a, 0);
-    for (int64_t e = tid; e < (nodes - 1) * D; e += 256) {
-        const int64_t j = 1 + e / D;
-        const int x = (int)(e % D);
-        const int depth = 63 - __builtin_clzll((uint64_t)j);
-        const int64_t n = L >> depth, first = (j - ((int64_t)1 << depth)) * n;
-        double sum = 0.0;
-        for (int64_t u = first; u < first + n; ++u) sum = __dadd_rn(sum, (double)kbar[((int64_t)h * p.C + leaf[u]) * D + x]);
-        mu[j * D + x] = (float)__ddiv_rn(sum, (double)n);
-    }
-    for (int64_t j = 1 + tid; j < nodes; j += 256) {
-        const int depth = 63 - __builtin_clzll((uint64_t)j);
-        const int64_t n = L >> depth, first = (j - ((int64_t)1 << depth)) * n;
-        float best = -INFINITY;
-        int32_t pmin = INT_MAX;
-        for (int64_t u = first; u < first + n; ++u) {
-            const int32_t c = leaf[u];
-            best = fmaxf(best, cam[(int64_t)h * p.C + c]);
-            pmin = min(pmin, c * p.s);
+    // node means: thread (group gi, dim x) keeps the sums of depths gi, gi + NG, ... (node
+    // j = 2^d + (u >> (k - d)) of depth d holds leaf u; it ends after leaf u when the
+    // 2^(k - d) leaves of the node are in)
+    {
+        constexpr int NG = 256 / D;        // thread groups, one dimension per thread
+        constexpr int kMaxDepth = 31;      // C < 2^31
+        constexpr int DPT = (kMaxDepth + NG) / NG;  // depths per thread at most
+        const int x = tid % D, gi = tid / D;
+        double acc[DPT];
+#pragma unroll
+        for (int t = 0; t < DPT; ++t) acc[t] = 0.0;
+        const float *kb = kbar + (int64_t)h * p.C * D + x;
+        constexpr int UB = 8;  // leaves whose values are requested together
+        for (int64_t u0 = 0; u0 < L; u0 += UB) {
+            float vb[UB];
+#pragma unroll
+            for (int e = 0; e < UB; ++e) vb[e] = kb[(int64_t)lf[min(u0 + e, L - 1)] * D];
+#pragma unroll
+            for (int e = 0; e < UB; ++e) {
+                const int64_t u = u0 + e;
+                if (u >= L) break;
+                const double v = (double)vb[e];
+#pragma unroll
+                for (int t = 0; t < DPT; ++t) {
+                    const int d = gi + NG * t;
+                    if (d > k) break;
+                    acc[t] = __dadd_rn(acc[t], v);
+                    const int64_t n = L >> d;
+                    if (((u + 1) & (n - 1)) == 0) {
+                        const int64_t j = ((int64_t)1 << d) + (u >> (k - d));
+                        mu[j * D + x] = (float)__ddiv_rn(acc[t], (double)n);
+                        acc[t] = 0.0;
+                    }
+                }
+            }
         }
-        am[j] = best;
-        pm[j] = pmin;
-        if (j >= L) rad[j] = 0.0;
+    }
+    // largest norm and earliest position: the leaves, then each level from its children
+    for (int64_t u = tid; u < L; u += 256) {
+        const int32_t c = lf[u];
+        am[L + u] = cam[(int64_t)h * p.C + c];
+        pm[L + u] = c * p.s;
+        rad[L + u] = 0.0;
     }
     __syncthreads();
+    for (int depth = k - 1; depth >= 0; --depth) {
+        for (int64_t j = ((int64_t)1 << depth) + tid; j < ((int64_t)2 << depth); j += 256) {
+            am[j] = fmaxf(am[2 * j], am[2 * j + 1]);
+            pm[j] = min(pm[2 * j], pm[2 * j + 1]);
+        }
+        __syncthreads();
+    }
     // radii, from the level above the leaves to the root
     for (int depth = k - 1; depth >= 0; --depth) {
         for (int64_t j = ((int64_t)1 << depth) + tid; j < ((int64_t)2 << depth); j += 256) {
@@ -501,11 +561,13 @@ hipError_t launch_fsb_select(const void *q, const void *k, const float *kbar, co
         const int lv = fsb_levels(p);
         for (int kk = 0; kk < lv; ++kk) {
             const unsigned grid = (unsigned)((int64_t)p.H * 2 * (p.C >> kk));
+            const int64_t lk = (int64_t)1 << kk;
+            const size_t lds = lk <= kTreeLds ? (size_t)lk * (sizeof(uint64_t) + sizeof(int32_t)) : 0;
             if (p.d == 64)
-                hipLaunchKernelGGL((fsb_tree_kernel<64>), dim3(grid), dim3(256), 0, st, kbar, amax, w.codes, w.list1,
+                hipLaunchKernelGGL((fsb_tree_kernel<64>), dim3(grid), dim3(256), lds, st, kbar, amax, w.codes, w.list1,
                                    w.hcount, w, kk, p);
             else
-                hipLaunchKernelGGL((fsb_tree_kernel<128>), dim3(grid), dim3(256), 0, st, kbar, amax, w.codes, w.list1,
+                hipLaunchKernelGGL((fsb_tree_kernel<128>), dim3(grid), dim3(256), lds, st, kbar, amax, w.codes, w.list1,
                                    w.hcount, w, kk, p);
         }
     }
