@@ -291,6 +291,9 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     const double sig = (double)p.sigma[h], lam = (double)p.lambda[h], rho = (double)p.rho;
     const int64_t nb = eligible_cells(p, i / p.B);
     const int lv = fsb_levels(p);
+    // lanes sorted: a power of two covering the roots (at most lv) and a beam's children
+    int sortw = 2;
+    while (sortw < 64 && (sortw < 2 * beam || sortw < lv)) sortw <<= 1;
     float *st = s_stage[wave];
     // upper bound of the cell score under a node whose mean key waits in the stage (dims
     // 8 c .. 8 c + 3 at st[256 c + 4 l], 8 c + 4 .. at st[256 c + 128 + 4 l] for the l-th
@@ -365,24 +368,38 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
                     __builtin_amdgcn_wave_barrier();
                 }
             }
-            // keep the beam best: bitonic sort of the wave's candidates, best first
+            // keep the beam best: bitonic sort of the lanes that can hold a candidate (the
+            // roots, then a beam's children), best first, on (bound, key) alone; the key
+            // names the node, which is read back from it after the sort
+            auto stage = [&](int kk, int jj) __attribute__((always_inline)) {
+                const double ou = __shfl_xor(cu, jj);
+                const int64_t okey = __shfl_xor(ckey, jj);
+                const bool lower = (lane & jj) == 0, up = (lane & kk) == 0;
+                const bool ob = cand_better(ou, okey, cu, ckey);
+                const bool take = (lower == up) ? ob : !ob;
+                cu = take ? ou : cu;
+                ckey = take ? okey : ckey;
+            };
+            if (sortw <= 32) {  // the usual width (beam <= 16): stages unrolled
+#pragma unroll
+                for (int kk = 2; kk <= 32; kk <<= 1)
+#pragma unroll
+                    for (int jj = kk >> 1; jj > 0; jj >>= 1)
+                        if (kk <= sortw) stage(kk, jj);
+            } else {
 #pragma unroll 1
-            for (int kk = 2; kk <= 64; kk <<= 1)
+                for (int kk = 2; kk <= 64; kk <<= 1)
 #pragma unroll 1
-                for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-                    const double ou = __shfl_xor(cu, jj);
-                    const int64_t okey = __shfl_xor(ckey, jj);
-                    const int ok_ = __shfl_xor(ck, jj);
-                    const int64_t oa = __shfl_xor(ca, jj), oj = __shfl_xor(cj, jj);
-                    const bool lower = (lane & jj) == 0, up = (lane & kk) == 0;
-                    const bool ob = cand_better(ou, okey, cu, ckey);
-                    const bool take = (lower == up) ? ob : !ob;
-                    cu = take ? ou : cu;
-                    ckey = take ? okey : ckey;
-                    ck = take ? ok_ : ck;
-                    ca = take ? oa : ca;
-                    cj = take ? oj : cj;
-                }
+                    for (int jj = kk >> 1; jj > 0; jj >>= 1) stage(kk, jj);
+            }
+            if (ckey == INT64_MAX) {
+                cj = 0;
+            } else {
+                ck = (int)((ckey >> 34) & 63);
+                const int64_t low = ckey & (((int64_t)1 << 34) - 1);
+                ca = low >> (ck + 1);
+                cj = low & (((int64_t)1 << (ck + 1)) - 1);
+            }
             if (lane >= beam) { cj = 0; cu = -INFINITY; ckey = INT64_MAX; }
             const bool internal = cj != 0 && cj < ((int64_t)1 << ck);
             if (__ballot(internal) == 0ull) break;
@@ -407,18 +424,16 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
             }
         }
         // this forest's leaves into the union
+        // (the beam ends on leaves; within one forest they are distinct cells, so a lane's
+        // cell is checked only against the cells already collected, all lanes at once, and
+        // the new ones are appended in lane order)
         const int32_t mycell = cj ? w.leaf[fsb_leaf(p, h, T, ck, ca, cj - ((int64_t)1 << ck))] : -1;
-        for (int r = 0; r < beam; ++r) {
-            const int32_t c = __shfl(mycell, r);
-            if (c < 0) continue;
-            bool dup = false;
-            for (int u = 0; u < nu; ++u) dup |= s_cell[wave][u] == c;
-            if (!dup) {
-                if (lane == 0) s_cell[wave][nu] = c;
-                ++nu;
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
+        bool dup = mycell < 0;
+        for (int u = 0; u < nu; ++u) dup |= s_cell[wave][u] == mycell;
+        const uint64_t keep = __ballot(!dup);
+        if (!dup) s_cell[wave][nu + __popcll(keep & ((1ull << lane) - 1))] = mycell;
+        nu += __popcll(keep);
+        __builtin_amdgcn_wave_barrier();
     }
     // rerank: lse_c = log sum_j exp(scale q . k_j) over the cell's tokens (token dots one per lane)
     const int S = p.s;
