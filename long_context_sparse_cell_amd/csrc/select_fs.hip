@@ -17,20 +17,29 @@
 //     permuted against bank conflicts) and computes content~ = q.(hi + lo) on
 //     v_mfma_f32_16x16x32_bf16, with the pool scoring kernel's bound |s - s~| <=
 //     eps (select_mfma.hip) itself bounded by ||q|| A_c + B_c (fs_prep_kernel).
-//     Each lane (one query, four cells of every 16-cell tile) keeps the K_L + 1
-//     cells of largest upper bound (K_L = 4 or 8, at least K)
-//     ub = s~ + eps, with lb = s~ - eps. A cell whose ub is below the smallest
-//     lb of some lane's K leading entries (at any earlier time, shared by the
-//     query's four lanes) is beaten by those K cells and is not inserted. At
-//     the end theta = the K-th largest lb over the query's four
-//     lists; the contenders are the listed cells with ub >= theta. Every true
-//     top-K cell has ub >= its score >= theta, so it is a contender unless a
-//     full list dropped it, which needs that list's smallest ub to reach theta
-//     (an overflow). Without overflow, at most K contenders are the top-K set.
+//     Each lane holds one query and four cells of every 16-cell tile.
+//     A first pass over every 8th chunk scores q.hi alone (its bound widened by
+//     the tail's share) and keeps each lane's largest lower bound: the query's
+//     four lanes hold distinct cells, so the smallest of their four maxima (of
+//     eight, two per lane, for K > 4) is a score that K cells reach, the
+//     starting threshold. The second pass visits every chunk; each lane keeps
+//     the K_L + 1 cells of largest upper bound ub = s~ + eps (K_L = 4 or 8, at
+//     least K) among those whose ub reaches the threshold, which rises with the
+//     lists (the smallest over the four lanes of their leading lower bounds).
+//     Insertions go in rounds, each lane carrying its largest pending cell down
+//     its list with selects. A listed cell's lower bound is ub - 2 emax (emax the
+//     largest eps the lane has listed), less a rounding margin. At the end
+//     theta = the K-th largest lower bound over the query's four lists; the
+//     contenders are the listed cells with ub >= theta. Every true top-K cell
+//     has ub >= its score >= theta, so it is a contender unless a full list
+//     dropped it, which needs that list's smallest ub to reach theta (an
+//     overflow). Without overflow, at most K contenders are the top-K set.
 //  3. Near-ties (more than K contenders) and overflows go to a per-work-group
 //     list; select_fs_fixup_kernel re-scores the contenders (or, after an
 //     overflow, every eligible cell) exactly as the oracle does.
+#include <cfloat>
 #include <climits>
+#include <cstdlib>
 
 #include "fsl_internal.h"
 
@@ -44,6 +53,7 @@ namespace {
 constexpr int kFsChunk = 64;  // cells per LDS chunk
 constexpr int kFsK = 8;       // largest K
 constexpr int kFsMaxCont = kFixWordsFs - 4;  // contender cells a near-tie entry lists
+constexpr int kFsPass1Stride = 8;  // the scorer's first pass visits every 8th chunk
 
 union U16x8f {
     uint4 u;
@@ -63,15 +73,29 @@ __device__ __forceinline__ int fs_piece(int r, int c) { return c ^ (r & (CPR - 1
 
 }  // namespace
 
+// B_c = 2 (|lambda a_c| (2e-6 + 2^-22) + 1e-30), the part of the per-pair bound that
+// does not scale with ||q|| (computed the same way wherever it is needed)
+__device__ __forceinline__ float fs_bconst(float la) {
+    return 2.0f * (fabsf(la) * (2e-6f + 2.384185791015625e-07f) + 1e-30f);
+}
+
+// a lower bound of the score of a cell with upper bound u and eps at most e2 / 2:
+// u - e2, less a margin for the fp32 rounding of u and of this difference
+__device__ __forceinline__ float fs_lbound(float u, float e2) {
+    return (u - e2) - (fabsf(u) + e2) * 4.76837158203125e-07f;
+}
+
 // kbar -> khi, klo (bf16 head and tail, round to nearest even) and
-// kcf = (lambda a_c, A_c, B_c, c s as int bits), the constants of the per-pair bound
-// eps = ||q|| A_c + B_c. The pool kernel's bound (select_mfma.hip) is
+// kcf = (A_c, lambda a_c + B_c, lambda a_c - B_c, lambda a_c), the constants of the
+// per-pair bound eps = ||q|| A_c + B_c. The pool kernel's bound (select_mfma.hip) is
 //   2 (||q|| |rho| ||kbar_c|| e_d + |lambda a_c| 2e-6 + (|rc| + |b|) 2^-22 + 1e-30)
 // with rc = rho q.(hi + lo) in fp32 and b the bias. Here |rc| <= 1.01 |rho| ||q|| ||kbar_c||
 // (Cauchy-Schwarz; the split and the fp32 sum add far less than 1%) and |b| <= |lambda a_c|
 // (|erf| <= 1), so
-//   A_c = 2 |rho| ||kbar_c|| (e_d + 1.01 2^-22),  B_c = 2 (|lambda a_c| (2e-6 + 2^-22) + 1e-30)
-// bound it from above with one fma per pair.
+//   A_c = 2 |rho| ||kbar_c|| (e_d + 1.01 2^-22),  B_c = fs_bconst(lambda a_c)
+// bound it from above. Where the erf factor is 1 (every cell far enough before the
+// query) a cell's upper bound is one fma on lambda a_c + B_c and its lower bound one on
+// lambda a_c - B_c; the roundings of these sums are of the size the 2^-22 terms cover.
 // Row r by 8 consecutive threads, 64 rows per work-group.
 template <int D>
 __global__ __launch_bounds__(512) void fs_prep_kernel(const float *__restrict__ kbar, const float *__restrict__ amax,
@@ -110,9 +134,9 @@ __global__ __launch_bounds__(512) void fs_prep_kernel(const float *__restrict__ 
     if (ok && part == 0) {
         const float la = p.lambda[h] * amax[(int64_t)h * p.C + r];
         const float ka = fabsf(p.rho) * sqrtf(ss);
+        const float bc = fs_bconst(la);
         kcf[(int64_t)h * p.C + r] =
-            make_float4(la, 2.0f * ka * (fs_eps_content(D) + 1.01f * 2.384185791015625e-07f),
-                        2.0f * (fabsf(la) * (2e-6f + 2.384185791015625e-07f) + 1e-30f), __int_as_float((int)(r * p.s)));
+            make_float4(2.0f * ka * (fs_eps_content(D) + 1.01f * 2.384185791015625e-07f), la + bc, la - bc, la);
     }
 }
 
@@ -120,12 +144,11 @@ template <int D, int KL>
 __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ khi,
                                                         const uint16_t *__restrict__ klo,
                                                         const float4 *__restrict__ kcf, int32_t *__restrict__ sel,
-                                                        uint32_t *__restrict__ fix, KParams p, int QW) {
+                                                        uint32_t *__restrict__ fix, KParams p, int QW, int S1) {
     constexpr int QS = D / 32;
     constexpr int CH = kFsChunk;
     constexpr int CPR = D / 8;     // 16-byte pieces per row
     constexpr int ROWU = CH * D * 2 / 1024;  // 1 KB copy units of a chunk's hi (and of its lo) rows
-    constexpr int NCOPY = 2 * ROWU + 1;      // and one unit of per-cell constants (64 x 16 bytes)
     static_assert(CH == 64, "one copy unit of per-cell constants per chunk");
     // listed cells per lane: one more than the largest K of this instance, so a list
     // overflows only when a single lane holds K + 1 cells whose bounds reach theta
@@ -165,23 +188,46 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
     if (tid == 0) s_nfix = 0;
 
     // ---- chunk copies straight into LDS (global_load_lds), 1 KB per wave instruction:
-    // rows past the block's last cell repeat that cell (they are never scored)
-    const int64_t nlast = (int64_t)n - 1;
-    auto issue = [&](int t, uint16_t *bhi, uint16_t *blo, float4 *bcf) __attribute__((always_inline)) {
-        const int64_t c0 = (int64_t)t * CH;
-        for (int u = __builtin_amdgcn_readfirstlane(wave); u < NCOPY; u += 8) {
-            if (u < 2 * ROWU) {
+    // rows past the block's last cell repeat that cell (they are never scored); the
+    // first pass copies the hi rows and the constants only
+    // (offsets are 32-bit, from the head's base: rows below C, C * D below 2^31)
+    const uint16_t *khi_h = khi + hC * D;
+    const uint16_t *klo_h = klo + hC * D;
+    const float4 *kcf_h = kcf + hC;
+    const int prow = lane / CPR, pphys = lane % CPR;  // a copy unit's lane: row offset and piece
+    auto issue = [&](int t, uint16_t *bhi, uint16_t *blo, float4 *bcf, bool with_lo) __attribute__((always_inline)) {
+        const int c0 = t * CH;
+        const int ncopy = with_lo ? 2 * ROWU + 1 : ROWU + 1;
+        for (int u = __builtin_amdgcn_readfirstlane(wave); u < ncopy; u += 8) {
+            if (u < ROWU || (with_lo && u < 2 * ROWU)) {
                 const int uu = u % ROWU;
-                const int pc = 64 * uu + lane;  // 16-byte piece of the chunk
-                const int r = pc / CPR, phys = pc % CPR;
-                const int64_t off = (hC + min(c0 + r, nlast)) * D + 8 * fs_piece<CPR>(r, phys);
+                const int r = uu * (64 / CPR) + prow;  // chunk row of this lane's 16-byte piece
+                const uint32_t off = (uint32_t)min(c0 + r, n - 1) * D + 8 * fs_piece<CPR>(r, pphys);
                 if (u < ROWU)
-                    lds_dma16(khi + off, bhi + 512 * uu);
+                    lds_dma16(khi_h + off, bhi + 512 * uu);
                 else
-                    lds_dma16(klo + off, blo + 512 * uu);
+                    lds_dma16(klo_h + off, blo + 512 * uu);
             } else {
-                lds_dma16(kcf + hC + min(c0 + lane, nlast), bcf);
+                lds_dma16(kcf_h + min(c0 + lane, n - 1), bcf);
             }
+        }
+    };
+    // the chunks first, first + step, ... below nch, double buffered; body(t, hi, lo, cf)
+    auto stream = [&](int first, int step, bool with_lo, auto &&body) __attribute__((always_inline)) {
+        if (first >= nch) return;
+        issue(first, s_hi0, s_lo0, s_cf0, with_lo);
+        wait_vmem();
+        __syncthreads();
+        for (int t = first; t < nch; t += 2 * step) {
+            if (t + step < nch) issue(t + step, s_hi1, s_lo1, s_cf1, with_lo);
+            body(t, s_hi0, s_lo0, s_cf0);
+            wait_vmem();  // the next chunk has landed, and every wave is done with this one
+            __syncthreads();
+            if (t + step >= nch) break;
+            if (t + 2 * step < nch) issue(t + 2 * step, s_hi0, s_lo0, s_cf0, with_lo);
+            body(t + step, s_hi1, s_lo1, s_cf1);
+            wait_vmem();
+            __syncthreads();
         }
     };
 
@@ -194,20 +240,93 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
             qss += f * f;
         }
     const float qn = sqrtf(colsum4(qss));  // the four lanes of a query hold all its d elements
+    // the first pass scores q.hi alone: |q.lo| <= 2^-9 ||q|| ||kbar_c|| adds 2^-8 |rho| ||q||
+    // ||kbar_c|| (with a factor 2 to spare) to eps, i.e. ||q|| A_c grows by the factor below
+    const float qn_hi =
+        qn * (1.0f + 3.90625e-3f / (2.0f * (fs_eps_content(D) + 1.01f * 2.384185791015625e-07f))) * 1.0001f;
 
-    // this lane's list: the kFsCap cells of largest upper bound, descending
-    float lu[kFsCap], ll[kFsCap];
+    // erf is 1 (in fp32 and fp64) once its argument reaches 6; cells are ascending
+    // and every query is at or after q0, so the chunk's last cell decides for all
+    auto chunk_needs_erf = [&](int c0) __attribute__((always_inline)) {
+        const int clast = min(c0 + CH, n) - 1;
+        return !((float)((int)q0 - clast * p.s) * karg >= 6.0f);
+    };
+    // the erf-weighted bias of cell c for this lane's query
+    auto bias_erf = [&](float la, int c) __attribute__((always_inline)) {
+        const float argf = (float)((int)i - c * p.s) * karg;
+        return argf < 6.0f ? la * erff(argf) : la;
+    };
+
+    // ---- first pass: a threshold. Each lane keeps the largest lower bound of its cells
+    // (two for K > 4: cells e < 2 and e >= 2 of each group of four); the query's four lanes
+    // hold distinct cells, so at least 4 (or 8) cells score above the smallest of them.
+    // S1 > 1 visits every S1-th chunk only.
+    float lbm0 = -INFINITY, lbm1 = -INFINITY;
+    stream(0, S1, false, [&](int t, const uint16_t *bhi, const uint16_t *, const float4 *bcf)
+                             __attribute__((always_inline)) {
+        const int c0 = t * CH;
+        const bool need_erf = chunk_needs_erf(c0);
+        const bool tail = c0 + CH > n;
+#pragma unroll
+        for (int ct = 0; ct < CH / 16; ++ct) {
+            const int rowc = 16 * ct + col;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < QS; ++ks) {
+                U16x8f hi;
+                hi.u = *reinterpret_cast<const uint4 *>(&bhi[rowc * D + 8 * fs_piece<CPR>(rowc, 4 * ks + g)]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi.b, bq[ks].b, acc, 0, 0, 0);
+            }
+            // the accumulators read in straight-line code right after the MFMAs (the empty
+            // asm keeps these reads ahead of the branches below)
+            float rcv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rcv[e] = acc[e];
+            asm volatile("" : "+v"(rcv[0]), "+v"(rcv[1]), "+v"(rcv[2]), "+v"(rcv[3]));
+            const int cbase = c0 + 16 * ct + 4 * g;
+            float lb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float4 cf = bcf[16 * ct + 4 * g + e];
+                lb[e] = fmaf(rhof, rcv[e], fmaf(-qn_hi, cf.x, cf.z));
+            }
+            if (need_erf) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float4 cf = bcf[16 * ct + 4 * g + e];
+                    lb[e] = fmaf(rhof, rcv[e], bias_erf(cf.w, cbase + e) - fmaf(qn_hi, cf.x, fs_bconst(cf.w)));
+                }
+            }
+            if (tail) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lb[e] = cbase + e < n ? lb[e] : -INFINITY;
+            }
+            if (KL > 4) {
+                lbm0 = fmaxf(lbm0, fmaxf(lb[0], lb[1]));
+                lbm1 = fmaxf(lbm1, fmaxf(lb[2], lb[3]));
+            } else {
+                lbm0 = fmaxf(lbm0, fmaxf(fmaxf(lb[0], lb[1]), fmaxf(lb[2], lb[3])));
+            }
+        }
+    });
+    // a score that K cells are known to reach: cells whose ub is below it are skipped
+    // (never below the lowest finite float, so an empty slot's -inf never passes)
+    float thr = fmaxf(-colmax4(-(KL > 4 ? fminf(lbm0, lbm1) : lbm0)), -FLT_MAX);
+
+    // ---- second pass: this lane's list, the kFsCap cells of largest upper bound
+    // (descending) among those that reach the threshold; a listed cell's lower bound is
+    // taken as fs_lbound(ub, 2 emax), emax the largest eps of the cells listed so far
+    float lu[kFsCap];
     int li[kFsCap];
 #pragma unroll
-    for (int r = 0; r < kFsCap; ++r) { lu[r] = -INFINITY; ll[r] = -INFINITY; li[r] = INT_MAX; }
-    float thr = -INFINITY;  // a score that K cells are known to beat: skip cells whose ub is below it
-
-    auto chunk = [&](int t, const uint16_t *bhi, const uint16_t *blo, const float4 *bcf) __attribute__((always_inline)) {
+    for (int r = 0; r < kFsCap; ++r) { lu[r] = -INFINITY; li[r] = INT_MAX; }
+    float emax = 0.0f;
+    float floor_u = thr;  // max(thr, lu[kFsCap - 1]): a cell is listed if its ub reaches this
+    stream(0, 1, true, [&](int t, const uint16_t *bhi, const uint16_t *blo, const float4 *bcf)
+                           __attribute__((always_inline)) {
         const int c0 = t * CH;
-        // erf is 1 (in fp32 and fp64) once its argument reaches 6; cells are ascending
-        // and every query is at or after q0, so the chunk's last cell decides for all
-        const int clast = min(c0 + CH, n) - 1;
-        const bool need_erf = !((float)((int)q0 - clast * p.s) * karg >= 6.0f);
+        const bool need_erf = chunk_needs_erf(c0);
+        const bool tail = c0 + CH > n;
 #pragma unroll
         for (int ct = 0; ct < CH / 16; ++ct) {
             const int rowc = 16 * ct + col;
@@ -220,79 +339,81 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi.b, bq[ks].b, acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo.b, bq[ks].b, acc, 0, 0, 0);
             }
-            // read the accumulators in straight-line code right after the MFMAs, where the
-            // compiler pads the MFMA-to-VALU dependency with wait states; the empty asm keeps
-            // these reads here, ahead of the branches below (a read placed after a branch
-            // was seen taking the accumulator before the MFMA had written it)
             float rcv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) rcv[e] = acc[e];
             asm volatile("" : "+v"(rcv[0]), "+v"(rcv[1]), "+v"(rcv[2]), "+v"(rcv[3]));
+            const int cbase = c0 + 16 * ct + 4 * g;
+            float pc[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int loc = 16 * ct + 4 * g + e;
-                const int c = c0 + loc;
-                const float4 cf = bcf[loc];
-                float bf = cf.x;  // lambda a_c times the erf factor 1
-                if (need_erf) {
-                    const float argf = (float)((int)i - __float_as_int(cf.w)) * karg;
-                    if (argf < 6.0f) bf = cf.x * erff(argf);
+                const float2 cf = *reinterpret_cast<const float2 *>(&bcf[16 * ct + 4 * g + e]);
+                pc[e] = fmaf(rhof, rcv[e], fmaf(qn, cf.x, cf.y));
+            }
+            if (need_erf) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float4 cf = bcf[16 * ct + 4 * g + e];
+                    pc[e] = fmaf(rhof, rcv[e], bias_erf(cf.w, cbase + e) + fmaf(qn, cf.x, fs_bconst(cf.w)));
                 }
-                const float sv = fmaf(rhof, rcv[e], bf);
-                const float ev = fmaf(qn, cf.y, cf.z);  // eps = ||q|| A_c + B_c
-                float cu = c < n ? sv + ev : -INFINITY;
-                if (cu >= thr && cu > lu[kFsCap - 1]) {
-                    float cl = sv - ev;
-                    int ci = c;
-                    // carry the cell down the list (selects only)
+            }
+            if (tail) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pc[e] = cbase + e < n ? pc[e] : -INFINITY;
+            }
+            // insertion rounds: each lane carries its largest pending cell down its list
+            // (selects only), so one round serves every lane that still has one; a lane
+            // has at most four, and a round is skipped unless some lane has one (each round
+            // updates the list in place: no loop-carried copies of it)
+            float m = fmaxf(fmaxf(pc[0], pc[1]), fmaxf(pc[2], pc[3]));
+#pragma unroll
+            for (int round = 0; round < 4; ++round) {
+                if (__ballot(m >= floor_u) == 0ull) break;
+                if (m >= floor_u) {
+                    // the first of the four holding m (selects, no branches)
+                    int e = 3;
+                    e = m == pc[2] ? 2 : e;
+                    e = m == pc[1] ? 1 : e;
+                    e = m == pc[0] ? 0 : e;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) pc[x] = x == e ? -INFINITY : pc[x];
+                    const float4 cf = bcf[16 * ct + 4 * g + e];
+                    emax = fmaxf(emax, fmaf(qn, cf.x, fs_bconst(cf.w)));
+                    float cu = m;
+                    int ci = cbase + e;
 #pragma unroll
                     for (int r = 0; r < kFsCap; ++r) {
                         const bool bt = cu > lu[r];
-                        const float tu = lu[r], tl = ll[r];
+                        const float tu = lu[r];
                         const int ti = li[r];
                         lu[r] = bt ? cu : tu;
-                        ll[r] = bt ? cl : tl;
                         li[r] = bt ? ci : ti;
                         cu = bt ? tu : cu;
-                        cl = bt ? tl : cl;
                         ci = bt ? ti : ci;
                     }
-                    float m = INFINITY;
-#pragma unroll
-                    for (int r = 0; r < kFsK; ++r)
-                        if (r < K) m = fminf(m, ll[r]);
-                    thr = fmaxf(thr, m);
+                    floor_u = fmaxf(thr, lu[kFsCap - 1]);
                 }
+                m = fmaxf(fmaxf(pc[0], pc[1]), fmaxf(pc[2], pc[3]));
             }
-            // a lane's threshold holds for the whole query (K cells beat anything below it),
-            // so the four lanes of the query column take the largest; thresholds stay valid
-            // when the entries that certified them are evicted later
-            thr = colmax4(thr);
         }
-    };
-    if (nch > 0) issue(0, s_hi0, s_lo0, s_cf0);
-    wait_vmem();
-    __syncthreads();
-    for (int t = 0; t < nch; t += 2) {
-        if (t + 1 < nch) issue(t + 1, s_hi1, s_lo1, s_cf1);
-        chunk(t, s_hi0, s_lo0, s_cf0);
-        wait_vmem();  // the next chunk has landed, and every wave is done with this one
-        __syncthreads();
-        if (t + 1 >= nch) break;
-        if (t + 2 < nch) issue(t + 2, s_hi0, s_lo0, s_cf0);
-        chunk(t + 1, s_hi1, s_lo1, s_cf1);
-        wait_vmem();
-        __syncthreads();
-    }
+        // the threshold rises with the lists: the smallest over the query's four lanes of
+        // the lower bounds of their first ceil(K/4) entries (4 ceil(K/4) >= K distinct
+        // cells); it stays valid when those entries are evicted later
+        const float e2 = 2.0f * emax;
+        const float v = KL > 4 && K > 4 ? fminf(fs_lbound(lu[0], e2), fs_lbound(lu[1], e2)) : fs_lbound(lu[0], e2);
+        thr = fmaxf(thr, -colmax4(-v));
+        floor_u = fmaxf(thr, lu[kFsCap - 1]);
+    });
 
     // ---- theta = K-th largest lb over the query's four lists: each lane sorts its
     // lbs (descending, KL kept), then the lists of the query column are merged
     float lbk[KL];
 #pragma unroll
     for (int r = 0; r < KL; ++r) lbk[r] = -INFINITY;
+    const float e2f = 2.0f * emax;
 #pragma unroll
     for (int s2 = 0; s2 < kFsCap; ++s2) {
-        float x = ll[s2];
+        float x = fs_lbound(lu[s2], e2f);
 #pragma unroll
         for (int r = 0; r < KL; ++r) {
             const float hi = fmaxf(lbk[r], x);
@@ -495,6 +616,8 @@ __global__ __launch_bounds__(256) void select_fs_fixup_kernel(const uint16_t *__
 
 hipError_t launch_select_fs(const void *q, const float *kbar, const float *amax, int32_t *sel, const Work &w,
                             const KParams &p, hipStream_t st) {
+    // the scorer addresses a head's split cell means with 32-bit element offsets
+    if ((int64_t)p.C * p.d >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     if (p.C > 0) {
         const dim3 pg((unsigned)((p.C + 63) / 64), (unsigned)p.H);
         if (p.d == 64)
@@ -508,7 +631,7 @@ hipError_t launch_select_fs(const void *q, const float *kbar, const float *amax,
     const dim3 grid((unsigned)(((p.N + QW - 1) / QW) * p.H));
 #define FSL_SFS(DD, KK)                                                                                            \
     hipLaunchKernelGGL((select_fs_kernel<DD, KK>), grid, dim3(512), 0, st, (const uint16_t *)q, w.khi, w.klo, w.kcf, \
-                       sel, w.fix, p, QW)
+                       sel, w.fix, p, QW, kFsPass1Stride)
     if (p.d == 64) {
         if (p.K <= 4) FSL_SFS(64, 4); else FSL_SFS(64, 8);
     } else {
