@@ -21,7 +21,9 @@
 // cell), fsb_tree (one launch per level k, one work-group per segment: the leaf
 // order as the merge of the two sorted halves of level k - 1, which is the sorted
 // order itself, then node means, norms, positions and radii) and fsb_search (one
-// wave per query: beam search over both forests, token-level rerank, top K).
+// wave per query: beam search over both forests, token-level rerank, top K; with a
+// beam of at most 16 both forests are searched at once, one per half of the wave,
+// and the fresh candidates' node means reach LDS half their dimensions at a time).
 // Every decision is taken in fp64 with the oracle's operation order (explicit
 // fused multiply-adds, sums left to right), so selections match it exactly; the
 // rerank's exp and log may differ from the host's in the last place, which can
@@ -298,14 +300,15 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     // upper bound of the cell score under a node whose mean key waits in the stage (dims
     // 8 c .. 8 c + 3 at st[256 c + 4 l], 8 c + 4 .. at st[256 c + 128 + 4 l] for the l-th
     // lane of its round): the dot product one fma per coordinate, left to right
-    auto bound = [&](int l, double rd, int32_t pm, float am) -> double {
+    // (dims 8 c .. 8 c + 7 of the chunks c0 .. c1 - 1 at st[g (c - c0) + 4 l] and
+    // st[g (c - c0) + g / 2 + 4 l], g = 8 x the lanes of the round)
+    auto dot_part = [&](double content, int c0, int c1, int g, int l) -> double {
         const double *qv = qg;
         asm volatile("" : "+v"(qv));
-        double content = 0.0;
 #pragma unroll 2
-        for (int c = 0; c < D / 8; ++c) {
-            const float4 m0 = *reinterpret_cast<const float4 *>(st + 256 * c + 4 * l);
-            const float4 m1 = *reinterpret_cast<const float4 *>(st + 256 * c + 128 + 4 * l);
+        for (int c = c0; c < c1; ++c) {
+            const float4 m0 = *reinterpret_cast<const float4 *>(st + g * (c - c0) + 4 * l);
+            const float4 m1 = *reinterpret_cast<const float4 *>(st + g * (c - c0) + g / 2 + 4 * l);
             content = __fma_rn(qv[8 * c], (double)m0.x, content);
             content = __fma_rn(qv[8 * c + 1], (double)m0.y, content);
             content = __fma_rn(qv[8 * c + 2], (double)m0.z, content);
@@ -315,13 +318,23 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
             content = __fma_rn(qv[8 * c + 6], (double)m1.z, content);
             content = __fma_rn(qv[8 * c + 7], (double)m1.w, content);
         }
+        return content;
+    };
+    auto bound_of = [&](double content, double rd, int32_t pm, float am) -> double {
         const double tt = __fma_rn(qn, rd, content);
         const double arg = __ddiv_rn(__dmul_rn(sig, (double)(i - (int64_t)pm)), 2.0 * (double)p.s);
         const double gg = arg >= 6.0 ? 1.0 : erf(arg);
         return __fma_rn(rho, tt, __dmul_rn(__dmul_rn(lam, (double)am), gg));
     };
     int nu = 0;  // distinct cells collected from the two beams (in s_cell)
-    for (int T = 0; T < 2; ++T) {
+    // a beam of up to 16 sorts within 32 lanes: then both forests are searched at once,
+    // forest 0 in lanes 0..31 and forest 1 in lanes 32..63 (every shuffle of the sort
+    // stays inside a half); wider beams search the forests one after the other
+    const bool dual = sortw <= 32;
+    const int hl = dual ? (lane & 31) : lane;  // the lane's place in its forest's group
+    const int hbase = dual ? (lane & 32) : 0;  // the group's first lane
+    for (int T0 = 0; T0 < (dual ? 1 : 2); ++T0) {
+        const int T = dual ? (lane >> 5) : T0;
         // forest 1 covers the list-1 cells below nb (none below cell 0; with no cells at all
         // the counts are never computed, so they are not read then)
         const int64_t m = T == 0 ? nb : nb == 0 ? 0 : (int64_t)hcount[(int64_t)h * (p.C + 1) + nb];
@@ -335,7 +348,7 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
             int r = 0;
             for (int kk = lv - 1; kk >= 0; --kk)
                 if ((m >> kk) & 1) {
-                    if (r == lane) { ck = kk; ca = base >> kk; cj = 1; }
+                    if (r == hl) { ck = kk; ca = base >> kk; cj = 1; }
                     base += (int64_t)1 << kk;
                     ++r;
                 }
@@ -352,20 +365,42 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
                 const double rd = w.rad[mynode];
                 const int32_t pm = w.pmin[mynode];
                 const float am = w.amax[mynode];
-                const int rounds = __ballot(fresh) >> 32 ? 2 : 1;
-                for (int rn = 0; rn < rounds; ++rn) {
-                    const int64_t src_node = __shfl(mynode, 32 * rn + (lane & 31));
+                if ((__ballot(fresh) >> 32) == 0ull) {
+                    // lanes 0..31 only: one round, all dims
+                    const int64_t src_node = __shfl(mynode, lane & 31);
                     const float *src = w.mu + src_node * D + 4 * (lane >> 5);
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
 #pragma unroll
                     for (int c = 0; c < D / 8; ++c) lds_dma16(src + 8 * c, st + 256 * c);
                     wait_vmem();
                     __builtin_amdgcn_wave_barrier();
-                    if (fresh && (lane >> 5) == rn) {
-                        cu = bound(lane & 31, rd, pm, am);
+                    if (fresh) {
+                        cu = bound_of(dot_part(0.0, 0, D / 8, 256, lane & 31), rd, pm, am);
                         ckey = fsb_key(T, ck, ca, cj);
                     }
                     __builtin_amdgcn_wave_barrier();
+                } else {
+                    // every lane: two rounds of half the dims (64 node rows of 64 dims each), the
+                    // dot product carried from the first half to the second in coordinate order
+                    const float *src = w.mu + mynode * D;
+                    double content = 0.0;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
+#pragma unroll
+                        for (int c = 0; c < D / 16; ++c) {
+                            lds_dma16(src + D / 2 * half + 8 * c, st + 512 * c);
+                            lds_dma16(src + D / 2 * half + 8 * c + 4, st + 512 * c + 256);
+                        }
+                        wait_vmem();
+                        __builtin_amdgcn_wave_barrier();
+                        if (fresh) content = dot_part(content, D / 16 * half, D / 16 * (half + 1), 512, lane);
+                        __builtin_amdgcn_wave_barrier();
+                    }
+                    if (fresh) {
+                        cu = bound_of(content, rd, pm, am);
+                        ckey = fsb_key(T, ck, ca, cj);
+                    }
                 }
             }
             // keep the beam best: bitonic sort of the lanes that can hold a candidate (the
@@ -374,7 +409,7 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
             auto stage = [&](int kk, int jj) __attribute__((always_inline)) {
                 const double ou = __shfl_xor(cu, jj);
                 const int64_t okey = __shfl_xor(ckey, jj);
-                const bool lower = (lane & jj) == 0, up = (lane & kk) == 0;
+                const bool lower = (lane & jj) == 0, up = (hl & kk) == 0;
                 const bool ob = cand_better(ou, okey, cu, ckey);
                 const bool take = (lower == up) ? ob : !ob;
                 cu = take ? ou : cu;
@@ -400,18 +435,19 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
                 ca = low >> (ck + 1);
                 cj = low & (((int64_t)1 << (ck + 1)) - 1);
             }
-            if (lane >= beam) { cj = 0; cu = -INFINITY; ckey = INT64_MAX; }
+            if (hl >= beam) { cj = 0; cu = -INFINITY; ckey = INT64_MAX; }
             const bool internal = cj != 0 && cj < ((int64_t)1 << ck);
             if (__ballot(internal) == 0ull) break;
-            // expand: an internal beam node at lane r moves to its left child and its right child
-            // goes to lane beam + r (beam <= 32, so both fit the wave)
-            const int src = lane - beam;
-            const int64_t pj = __shfl(cj, src < 0 ? 0 : src);
-            const int pk = __shfl(ck, src < 0 ? 0 : src);
-            const int64_t pa = __shfl(ca, src < 0 ? 0 : src);
-            const bool p_int = __shfl((int)internal, src < 0 ? 0 : src) != 0;
+            // expand: an internal beam node at place r of its group moves to its left child and
+            // its right child goes to place beam + r (2 beam fits the group)
+            const int src = hl - beam;
+            const int srcl = hbase + (src < 0 ? 0 : src);
+            const int64_t pj = __shfl(cj, srcl);
+            const int pk = __shfl(ck, srcl);
+            const int64_t pa = __shfl(ca, srcl);
+            const bool p_int = __shfl((int)internal, srcl) != 0;
             fresh = false;
-            if (lane < beam) {
+            if (hl < beam) {
                 if (internal) {
                     cj = 2 * cj;
                     fresh = true;
@@ -428,12 +464,15 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
         // cell is checked only against the cells already collected, all lanes at once, and
         // the new ones are appended in lane order)
         const int32_t mycell = cj ? w.leaf[fsb_leaf(p, h, T, ck, ca, cj - ((int64_t)1 << ck))] : -1;
-        bool dup = mycell < 0;
-        for (int u = 0; u < nu; ++u) dup |= s_cell[wave][u] == mycell;
-        const uint64_t keep = __ballot(!dup);
-        if (!dup) s_cell[wave][nu + __popcll(keep & ((1ull << lane) - 1))] = mycell;
-        nu += __popcll(keep);
-        __builtin_amdgcn_wave_barrier();
+        // forest 0's leaves first, then forest 1's (both at once when searched together)
+        for (int part = 0; part < (dual ? 2 : 1); ++part) {
+            bool dup = mycell < 0 || (dual && (lane >> 5) != part);
+            for (int u = 0; u < nu; ++u) dup |= s_cell[wave][u] == mycell;
+            const uint64_t keep = __ballot(!dup);
+            if (!dup) s_cell[wave][nu + __popcll(keep & ((1ull << lane) - 1))] = mycell;
+            nu += __popcll(keep);
+            __builtin_amdgcn_wave_barrier();
+        }
     }
     // rerank: lse_c = log sum_j exp(scale q . k_j) over the cell's tokens (token dots one per lane)
     const int S = p.s;
