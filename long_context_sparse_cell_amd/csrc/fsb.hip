@@ -22,8 +22,9 @@
 // order as the merge of the two sorted halves of level k - 1, which is the sorted
 // order itself, then node means, norms, positions and radii) and fsb_search (one
 // wave per query: beam search over both forests, token-level rerank, top K; with a
-// beam of at most 16 both forests are searched at once, one per half of the wave,
-// and the fresh candidates' node means reach LDS half their dimensions at a time).
+// beam of at most 16 both forests are searched at once, one per half of the wave;
+// node means and key rows reach LDS a part of their dimensions at a time, through an
+// 8 KB stage per wave, and the sort's lane exchanges within 16 lanes are DPP moves).
 // Every decision is taken in fp64 with the oracle's operation order (explicit
 // fused multiply-adds, sums left to right), so selections match it exactly; the
 // rerank's exp and log may differ from the host's in the last place, which can
@@ -260,6 +261,30 @@ __global__ __launch_bounds__(256) void fsb_tree_kernel(const float *__restrict__
     }
 }
 
+// The value of lane (this lane xor j), for j = 1, 2, 4, 8 by DPP moves inside rows of 16
+// lanes (quad permutes; xor 4 = half-row mirror then quad reverse; xor 8 = row mirror
+// then half-row mirror), otherwise by a shuffle through LDS.
+__device__ __forceinline__ int dpp_xor32(int x, int j) {
+    if (j == 1) return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    if (j == 2) return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    if (j == 4) {
+        const int y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        return __builtin_amdgcn_update_dpp(0, y, 0x1B, 0xF, 0xF, false);          // quad_perm 3,2,1,0
+    }
+    if (j == 8) {
+        const int y = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+        return __builtin_amdgcn_update_dpp(0, y, 0x141, 0xF, 0xF, false);         // row_half_mirror
+    }
+    return __shfl_xor(x, j);
+}
+__device__ __forceinline__ int64_t lane_xor(int64_t x, int j) {
+    const int lo = dpp_xor32((int)(uint32_t)x, j), hi = dpp_xor32((int)(x >> 32), j);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double lane_xor(double x, int j) {
+    return __longlong_as_double(lane_xor((int64_t)__double_as_longlong(x), j));
+}
+
 // ---- search: one wave per query
 template <int D>
 __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const float *__restrict__ q32,
@@ -272,8 +297,9 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     __shared__ double s_q[kSearchWaves][D];
     __shared__ double s_lse[kSearchWaves][64];
     __shared__ int32_t s_cell[kSearchWaves][64];
-    // per wave: 32 node means (fp32), or 64 bf16 key rows, copied in before their dot products
-    __shared__ __attribute__((aligned(16))) float s_stage[kSearchWaves][32 * D];
+    // per wave (8 KB at d = 128, so that four work-groups fit a CU): node means (fp32) or
+    // bf16 key rows, a part of their dimensions at a time, copied in before their dot products
+    __shared__ __attribute__((aligned(16))) float s_stage[kSearchWaves][16 * D];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t nq = (p.N + kSearchWaves - 1) / kSearchWaves;
     const int h = (int)(blockIdx.x / nq);
@@ -358,57 +384,58 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
         int64_t ckey = INT64_MAX;
         for (int iter = 0; iter < 64; ++iter) {
             if (__ballot(fresh) != 0ull) {
-                // the fresh lanes' node means into the stage, 32 lanes a round (one copy of
-                // 32 x 16 bytes per instruction pair), their radii, norms and positions
-                // requested with them; other lanes name a valid slot they do not use
+                // the fresh lanes' node means into the stage a part of their dims at a time,
+                // their radii, norms and positions requested with them; other lanes name a
+                // valid slot they do not use
                 const int64_t mynode = fsb_node(p, h, T, fresh ? ck : 0, fresh ? ca : 0, fresh ? cj : 1);
                 const double rd = w.rad[mynode];
                 const int32_t pm = w.pmin[mynode];
                 const float am = w.amax[mynode];
+                double content = 0.0;
                 if ((__ballot(fresh) >> 32) == 0ull) {
-                    // lanes 0..31 only: one round, all dims
+                    // lanes 0..31 only: two rounds of half the dims (32 node rows each)
                     const int64_t src_node = __shfl(mynode, lane & 31);
                     const float *src = w.mu + src_node * D + 4 * (lane >> 5);
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
-#pragma unroll
-                    for (int c = 0; c < D / 8; ++c) lds_dma16(src + 8 * c, st + 256 * c);
-                    wait_vmem();
-                    __builtin_amdgcn_wave_barrier();
-                    if (fresh) {
-                        cu = bound_of(dot_part(0.0, 0, D / 8, 256, lane & 31), rd, pm, am);
-                        ckey = fsb_key(T, ck, ca, cj);
-                    }
-                    __builtin_amdgcn_wave_barrier();
-                } else {
-                    // every lane: two rounds of half the dims (64 node rows of 64 dims each), the
-                    // dot product carried from the first half to the second in coordinate order
-                    const float *src = w.mu + mynode * D;
-                    double content = 0.0;
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
 #pragma unroll
-                        for (int c = 0; c < D / 16; ++c) {
-                            lds_dma16(src + D / 2 * half + 8 * c, st + 512 * c);
-                            lds_dma16(src + D / 2 * half + 8 * c + 4, st + 512 * c + 256);
+                        for (int c = 0; c < D / 16; ++c) lds_dma16(src + D / 2 * half + 8 * c, st + 256 * c);
+                        wait_vmem();
+                        __builtin_amdgcn_wave_barrier();
+                        if (fresh) content = dot_part(content, D / 16 * half, D / 16 * (half + 1), 256, lane & 31);
+                        __builtin_amdgcn_wave_barrier();
+                    }
+                } else {
+                    // every lane: four rounds of a quarter of the dims (64 node rows of D / 4
+                    // dims each), the dot product carried from round to round in coordinate order
+                    constexpr int RC = D / 32;  // 8-dim chunks per round
+                    const float *src = w.mu + mynode * D;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
+#pragma unroll
+                        for (int c = 0; c < RC; ++c) {
+                            lds_dma16(src + 8 * (RC * r + c), st + 512 * c);
+                            lds_dma16(src + 8 * (RC * r + c) + 4, st + 512 * c + 256);
                         }
                         wait_vmem();
                         __builtin_amdgcn_wave_barrier();
-                        if (fresh) content = dot_part(content, D / 16 * half, D / 16 * (half + 1), 512, lane);
+                        if (fresh) content = dot_part(content, RC * r, RC * r + RC, 512, lane);
                         __builtin_amdgcn_wave_barrier();
                     }
-                    if (fresh) {
-                        cu = bound_of(content, rd, pm, am);
-                        ckey = fsb_key(T, ck, ca, cj);
-                    }
+                }
+                if (fresh) {
+                    cu = bound_of(content, rd, pm, am);
+                    ckey = fsb_key(T, ck, ca, cj);
                 }
             }
             // keep the beam best: bitonic sort of the lanes that can hold a candidate (the
             // roots, then a beam's children), best first, on (bound, key) alone; the key
             // names the node, which is read back from it after the sort
             auto stage = [&](int kk, int jj) __attribute__((always_inline)) {
-                const double ou = __shfl_xor(cu, jj);
-                const int64_t okey = __shfl_xor(ckey, jj);
+                const double ou = lane_xor(cu, jj);
+                const int64_t okey = lane_xor(ckey, jj);
                 const bool lower = (lane & jj) == 0, up = (hl & kk) == 0;
                 const bool ob = cand_better(ou, okey, cu, ckey);
                 const bool take = (lower == up) ? ob : !ob;
@@ -477,41 +504,46 @@ __global__ __launch_bounds__(64 * kSearchWaves) void fsb_search_kernel(const flo
     // rerank: lse_c = log sum_j exp(scale q . k_j) over the cell's tokens (token dots one per lane)
     const int S = p.s;
     if (bf) {
-        // 64 / S cells at a time: their key rows copied into the stage (16-byte piece c of
-        // row r at c ^ (r mod pieces per row)), then one row per lane
-        constexpr int CPR = D / 8;
-        constexpr int RPI = 64 / CPR;  // rows per copy instruction
+        // 64 / S cells at a time: their key rows copied into the stage half the dims at a time
+        // (16-byte piece c of a round's row r at c ^ (r mod pieces per round row)), then one
+        // row per lane, the dot product carried from the first half to the second
+        constexpr int HP = D / 16;     // 16-byte pieces of a row per round
+        constexpr int RPI = 64 / HP;   // rows per copy instruction
         uint16_t *st16 = reinterpret_cast<uint16_t *>(st);
         const int cps = 64 / S;
         for (int u0 = 0; u0 < nu; u0 += cps) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
-#pragma unroll
-            for (int ii = 0; ii < 64 / RPI; ++ii) {
-                const int row = RPI * ii + lane / CPR, pos = lane % CPR;
-                const int uu = min(u0 + row / S, nu - 1);
-                const int64_t tok = hN + (int64_t)s_cell[wave][uu] * S + row % S;
-                lds_dma16(k16 + tok * D + 8 * (pos ^ (row & (CPR - 1))), st16 + 512 * ii);
-            }
-            wait_vmem();
-            __builtin_amdgcn_wave_barrier();
             const int uu = u0 + lane / S;
-            double l = -INFINITY;
-            if (uu < nu) {
-                const double *qv = qg;
-                asm volatile("" : "+v"(qv));
-                double dot = 0.0;
-#pragma unroll 2
-                for (int c = 0; c < CPR; ++c) {
-                    const uint4 r4 = *reinterpret_cast<const uint4 *>(st16 + lane * D + 8 * (c ^ (lane & (CPR - 1))));
-                    const uint32_t w4[4] = {r4.x, r4.y, r4.z, r4.w};
+            double dot = 0.0;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        dot = __fma_rn(qv[8 * c + 2 * t], (double)__uint_as_float(w4[t] << 16), dot);
-                        dot = __fma_rn(qv[8 * c + 2 * t + 1], (double)__uint_as_float(w4[t] & 0xFFFF0000u), dot);
+            for (int half = 0; half < 2; ++half) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the stage are done
+#pragma unroll
+                for (int ii = 0; ii < 64 / RPI; ++ii) {
+                    const int row = RPI * ii + lane / HP, pos = lane % HP;
+                    const int uc = min(u0 + row / S, nu - 1);
+                    const int64_t tok = hN + (int64_t)s_cell[wave][uc] * S + row % S;
+                    lds_dma16(k16 + tok * D + 8 * (HP * half + (pos ^ (row & (HP - 1)))), st16 + 512 * ii);
+                }
+                wait_vmem();
+                __builtin_amdgcn_wave_barrier();
+                if (uu < nu) {
+                    const double *qv = qg + D / 2 * half;
+                    asm volatile("" : "+v"(qv));
+#pragma unroll 2
+                    for (int c = 0; c < HP; ++c) {
+                        const uint4 r4 =
+                            *reinterpret_cast<const uint4 *>(st16 + lane * (D / 2) + 8 * (c ^ (lane & (HP - 1))));
+                        const uint32_t w4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            dot = __fma_rn(qv[8 * c + 2 * t], (double)__uint_as_float(w4[t] << 16), dot);
+                            dot = __fma_rn(qv[8 * c + 2 * t + 1], (double)__uint_as_float(w4[t] & 0xFFFF0000u), dot);
+                        }
                     }
                 }
-                l = __dmul_rn((double)p.scale, dot);
+                __builtin_amdgcn_wave_barrier();
             }
+            const double l = uu < nu ? __dmul_rn((double)p.scale, dot) : -INFINITY;
             double mx = l;
             for (int o = 1; o < S; o <<= 1) {
                 const double ov = __shfl_xor(mx, o);
