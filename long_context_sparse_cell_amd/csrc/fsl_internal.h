@@ -113,16 +113,20 @@ __host__ __device__ inline int64_t plan_records(const KParams &p) {
 
 // bf16 long branch without pruning (readout_cells.hip): the (query, rank) pairs
 // of every head are listed by super-span (a run of ro_spans_per_super(p)
-// consecutive spans, 8192 queries at most unless the counters would outgrow
+// consecutive spans, 65536 queries at most unless the counters would outgrow
 // kRoMaxCounters) and, inside it, by cell, so that a stretch of the list reads
 // the queries of one super-span while each cell is read once per super-span.
+// Without the prune a super-span's queries spread over most cells, so the longer
+// the super-span, the more pairs share one read of a cell's keys and values: at
+// N = 262144 the readout took 4.23 ms with 8192-query super-spans and 2.53 ms with
+// 65536 (the re-read query rows cost less than the re-read cells).
 // The lists are built from the same spans as the plan records. The plan region
 // then holds, in 32-bit words: one pair counter per (head, super-span, cell) plus
 // a sentinel (scanned in place into list offsets), the scan's block totals, then
 // the list itself, one (counter index, pair index) word pair per entry; the
 // kernel walks the list in items of kRoItem entries.
 constexpr int kRoItem = 256;
-constexpr int kRoSuperQ = 8192;
+constexpr int kRoSuperQ = 65536;
 constexpr int64_t kRoMaxCounters = (int64_t)1 << 22;
 __host__ __device__ inline int64_t ro_spans(const KParams &p) { return (p.N + span_queries(p) - 1) / span_queries(p); }
 __host__ __device__ inline int64_t ro_spans_per_super(const KParams &p) {
