@@ -1032,18 +1032,30 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_long_sum_kernel(const int32_t
 }
 
 // ---- dgamma of each head: the per-query terms summed in a fixed order
-__global__ __launch_bounds__(kThreads) void bwd_dgamma_kernel(const float *__restrict__ dg, float *__restrict__ dgamma,
-                                                              KParams p) {
-    __shared__ float s_part[kThreads / 64];
+constexpr int kDgThreads = 1024;
+__global__ __launch_bounds__(kDgThreads) void bwd_dgamma_kernel(const float *__restrict__ dg, float *__restrict__ dgamma,
+                                                                KParams p) {
+    // one work-group per head: each thread adds its strided share in order (eight loads
+    // in flight per step), then the waves' sums are added in a fixed order
+    __shared__ float s_part[kDgThreads / 64];
     const int h = blockIdx.x;
+    const float *src = dg + (int64_t)h * p.N;
     float acc = 0.0f;
-    for (int64_t t = threadIdx.x; t < p.N; t += kThreads) acc += dg[(int64_t)h * p.N + t];
+    int64_t t = threadIdx.x;
+    for (; t + 7 * kDgThreads < p.N; t += 8 * kDgThreads) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[t + u * kDgThreads];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; t < p.N; t += kDgThreads) acc += src[t];
     acc = wave_sum(acc);
     if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
         float s = 0.0f;
-        for (int w = 0; w < kThreads / 64; ++w) s += s_part[w];
+        for (int w = 0; w < kDgThreads / 64; ++w) s += s_part[w];
         dgamma[h] = s;
     }
 }
@@ -1115,7 +1127,7 @@ static hipError_t launch_bwd_typed(const void *q_, const void *k_, const void *v
         hipLaunchKernelGGL(bwd_dq_long_sum_kernel, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                            st, sel, w.dqp, dq, p);
     }
-    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((unsigned)p.H), dim3(kThreads), 0, st, w.dg, dgamma, p);
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((unsigned)p.H), dim3(kDgThreads), 0, st, w.dg, dgamma, p);
     return hipGetLastError();
 }
 
