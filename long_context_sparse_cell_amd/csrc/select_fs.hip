@@ -506,27 +506,28 @@ __global__ __launch_bounds__(512) void select_fs_kernel(const uint16_t *__restri
 }
 
 // Exact re-scoring of the near-tie and overflow queries listed by
-// select_fs_kernel: one work-group of four waves per scoring work-group's
-// region, wave w taking entries w, w + 4, ... Each lane scores its share of the
+// select_fs_kernel: one work-group of two waves per scoring work-group's
+// region (regions hold about three entries; two waves per work-group measured
+// faster than one or four), wave w taking entries w, w + 2, ... Each lane scores its share of the
 // candidates (the listed contenders, or every eligible cell after an overflow)
 // with the oracle's fp64 fma chain and keeps its K best under (score desc,
 // cell asc); K rounds of a wave-wide maximum then take the K best overall,
 // written in ascending cell order. Comparisons are written as selects.
 template <int D>
-__global__ __launch_bounds__(256) void select_fs_fixup_kernel(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(128) void select_fs_fixup_kernel(const uint16_t *__restrict__ q,
                                                               const float *__restrict__ kbar,
                                                               const float *__restrict__ amax,
                                                               int32_t *__restrict__ sel,
                                                               const uint32_t *__restrict__ fix, KParams p) {
     // each wave's current query row in fp32 (written and read by that wave only: a wave's LDS
     // operations complete in issue order)
-    __shared__ __attribute__((aligned(16))) float s_qf[4][D];
+    __shared__ __attribute__((aligned(16))) float s_qf[2][D];
     const int64_t region = blockIdx.x;
     const uint32_t nfix = fix[region];
     const int lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
     const int K = p.K;
-    for (uint32_t j = wave; j < nfix; j += 4) {
+    for (uint32_t j = wave; j < nfix; j += 2) {
         const uint32_t *e = fix_region_fs(fix, p, region) + (size_t)j * kFixWordsFs;
         const int h = (int)e[0];
         const int64_t i = (int64_t)e[1];
@@ -641,10 +642,10 @@ hipError_t launch_select_fs(const void *q, const float *kbar, const float *amax,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.d == 64)
-        hipLaunchKernelGGL((select_fs_fixup_kernel<64>), grid, dim3(256), 0, st, (const uint16_t *)q, kbar, amax, sel,
+        hipLaunchKernelGGL((select_fs_fixup_kernel<64>), grid, dim3(128), 0, st, (const uint16_t *)q, kbar, amax, sel,
                            w.fix, p);
     else
-        hipLaunchKernelGGL((select_fs_fixup_kernel<128>), grid, dim3(256), 0, st, (const uint16_t *)q, kbar, amax, sel,
+        hipLaunchKernelGGL((select_fs_fixup_kernel<128>), grid, dim3(128), 0, st, (const uint16_t *)q, kbar, amax, sel,
                            w.fix, p);
     return hipGetLastError();
 }

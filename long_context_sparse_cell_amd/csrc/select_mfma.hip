@@ -297,16 +297,17 @@ __global__ __launch_bounds__(512) void select_mfma_kernel(const uint16_t *__rest
 }
 
 // Exact re-scoring of the near-tie queries listed by select_mfma_kernel: one
-// work-group of four waves per scoring work-group's region, wave w taking its
-// near-ties w, w + 4, ...; lane l scores the contenders at pool positions l and
-// 64 + l with the fp64 fma chain of the oracle, then ranks each of its
+// work-group of two waves per scoring work-group's region (faster than four: more
+// work-groups fit a CU), wave w taking its near-ties w, w + 2, ...; lane l scores
+// the contenders at pool positions l and 64 + l with the fp64 fma chain of the
+// oracle, then ranks each of its
 // contenders against all of the query's contenders (read lane by lane), keeps
 // the K best by (score desc, cell asc) and writes them in cell order.
 // Comparisons are written as selects: a conditional-swap list insert with
 // double keys was compiled into wrong code (equal keys lost the index
 // tie-break) by this toolchain at -O3.
 template <int D>
-__global__ __launch_bounds__(256) void select_fixup_kernel(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(128) void select_fixup_kernel(const uint16_t *__restrict__ q,
                                                            const float *__restrict__ kbar,
                                                            const float *__restrict__ amax,
                                                            const int32_t *__restrict__ pool, int32_t *__restrict__ sel,
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(256) void select_fixup_kernel(const uint16_t *__res
     const uint32_t n = fix[region];
     const int lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
-    for (uint32_t j = wave; j < n; j += 4) {
+    for (uint32_t j = wave; j < n; j += 2) {
         const uint32_t *e = fix_region(fix, p, region) + (size_t)j * kFixWords;
         const int h = (int)e[0];
         const int64_t i = (int64_t)e[1];
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(256) void select_fixup_kernel(const uint16_t *__res
 
 hipError_t launch_select_fixup(const void *q, const float *kbar, const float *amax, const int32_t *pool,
                                int32_t *sel, const uint32_t *fix, const KParams &p, hipStream_t st) {
-    const dim3 grid((unsigned)fix_regions(p)), block(256);
+    const dim3 grid((unsigned)fix_regions(p)), block(128);
     if (p.d == 64)
         hipLaunchKernelGGL((select_fixup_kernel<64>), grid, block, 0, st, (const uint16_t *)q, kbar, amax, pool, sel,
                            fix, p);
